@@ -1,0 +1,109 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that the pins
+catch every one of them. A mutant that no pin rejects would mean the oracle
+could carry that mistake unnoticed."""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.moe_oracle as mo
+import test_oracle_dispatch as tdisp
+import test_oracle_experts as texp
+import test_oracle_routing as trout
+
+F64 = np.float64
+
+
+def _topk_ties_high(logits, k):
+    l = np.asarray(logits, F64)
+    E = l.shape[1]
+    order = np.argsort(-l[:, ::-1], axis=1, kind="stable")
+    return (E - 1 - order)[:, :k]
+
+
+def _gates_not_renormalised(logits, idx):
+    return np.take_along_axis(mo.softmax_full(logits), np.asarray(idx), 1)
+
+
+def _silu_wrong_sign(a):
+    a = np.asarray(a, F64)
+    return a / (1.0 + np.exp(a))
+
+
+def _ffn_drop_lora_up(x_rows, w_gate, w_up, w_down, lora=None, return_parts=False):
+    if lora is not None:
+        lora = dict(lora)
+        lora["b_up"] = np.zeros_like(np.asarray(lora["b_up"], F64))
+    return ORIG["expert_ffn"](x_rows, w_gate, w_up, w_down, lora, return_parts)
+
+
+def _ffn_gate_up_swapped(x_rows, w_gate, w_up, w_down, lora=None, return_parts=False):
+    return ORIG["expert_ffn"](x_rows, w_up, w_gate, w_down, lora, return_parts)
+
+
+def _capacity_keeps_lowest(idx, gate, E, e_lo=0, e_hi=None, capacity=0):
+    return ORIG["dispatch"](idx, -np.asarray(gate, F64), E, e_lo, e_hi, capacity)
+
+
+def _bwd_no_gate(dy, x_perm, offsets, row_src, row_gate, G, H, w_down, lora):
+    return ORIG["lora_backward"](dy, x_perm, offsets, row_src, np.ones_like(np.asarray(row_gate, F64)),
+                                 G, H, w_down, lora)
+
+
+def _bwd_wrong_sign_lora_dh(dy, x_perm, offsets, row_src, row_gate, G, H, w_down, lora):
+    lo = dict(lora)
+    lo["a_down"] = -np.asarray(lora["a_down"], F64)
+    out = ORIG["lora_backward"](dy, x_perm, offsets, row_src, row_gate, G, H, w_down, lo)
+    out["da_down"] = -out["da_down"]
+    return out
+
+
+def _aux_wrong_norm(counts, prob_sum, T, k, coef):
+    return ORIG["aux_loss"](counts, prob_sum, T, 1, coef)
+
+
+ORIG = {n: getattr(mo, n) for n in ("topk_experts", "topk_gates", "silu", "expert_ffn",
+                                     "dispatch", "lora_backward", "aux_loss")}
+
+MUTANTS = {
+    "ties_to_higher_id": ("topk_experts", _topk_ties_high),
+    "gates_not_renormalised": ("topk_gates", _gates_not_renormalised),
+    "silu_wrong_sign": ("silu", _silu_wrong_sign),
+    "lora_up_term_dropped": ("expert_ffn", _ffn_drop_lora_up),
+    "gate_and_up_swapped": ("expert_ffn", _ffn_gate_up_swapped),
+    "capacity_keeps_lowest_gates": ("dispatch", _capacity_keeps_lowest),
+    "backward_ignores_gate": ("lora_backward", _bwd_no_gate),
+    "backward_lora_dh_sign": ("lora_backward", _bwd_wrong_sign_lora_dh),
+    "aux_loss_drops_k": ("aux_loss", _aux_wrong_norm),
+}
+
+PINS = [
+    trout.test_topk_matches_brute_force_with_ties, trout.test_topk_signed_zero_ties_to_lower_id,
+    trout.test_hand_computed_gates, trout.test_gates_sum_to_one_and_k1_is_one,
+    trout.test_gates_equal_renormalised_full_softmax,
+    tdisp.test_capacity_keeps_largest_gates_ties_to_lower_token,
+    tdisp.test_capacity_threshold_property,
+    texp.test_silu_constants_are_the_closed_forms, texp.test_expert_ffn_hand_case,
+    texp.test_hand_moe_layer_one_token, texp.test_k_equals_E_with_identical_experts_is_dense_ffn,
+    texp.test_layer_equals_per_token_sum_over_selected_experts,
+    texp.test_aux_loss_uniform_and_hand_case, texp.test_lora_forward_equals_merged_weights,
+    texp.test_lora_backward_matches_central_differences,
+]
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_some_pin_rejects_mutant(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(mo, attr, fn)
+    monkeypatch.setattr(oracle, attr, fn)
+    caught = []
+    for pin in PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError, TypeError) as exc:
+            caught.append((pin.__name__, type(exc).__name__))
+    assert caught, f"mutant {name} passed every pin"
+
+
+def test_pins_pass_unmutated():
+    for pin in PINS:
+        pin()
