@@ -1,0 +1,256 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) sparse MoE layer library.
+ *
+ * The layer is y = sum_{i in TopK(x)} g_i(x) * E_i(x) ("Adapting Trillion-
+ * Parameter MoE Models for LoRA Fine-Tuning: A Full-Stack Engineering Guide",
+ * §2.1), with E routed experts of which each token uses k (896 and 16 on "Day-
+ * Level Adaptation and LoRA Fine-Tuning of Ultra-Large-Scale Sparse MoE
+ * Models", §2.1), computed in four calls that mirror the permute -> grouped
+ * GEMM -> unpermute pipeline of "Trillion-Parameter MoE Model Training
+ * Adaptation: Full-Stack Optimization Practices", §4.3:
+ *
+ *   moe_route        router GEMM, softmax, top-k, renormalised gates
+ *   moe_dispatch     expert histogram, scan, stable scatter, capacity, row gather
+ *   moe_expert_gemm  grouped SwiGLU expert FFN over ragged per-expert row blocks
+ *   moe_combine      gate-weighted sum of each token's expert rows
+ *
+ * plus moe_aux_loss (load-balance loss) and moe_lora_bwd (gradients of the
+ * LoRA adapters on the up and down projections).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers are DEVICE pointers unless marked [host]. Matrices are dense and
+ *   row-major with no padding; "[a,b]" gives the shape.
+ * - Floating tensors use the dtype of moe_shape_t.dtype (fp32 or bf16) unless
+ *   stated as f32; indices are int32.
+ * - Every call enqueues kernels on `stream` and returns without waiting for
+ *   them; nothing synchronises with the host and nothing is allocated or freed
+ *   on the device. The caller owns every buffer; the library keeps no pointer
+ *   after the call returns.
+ * - Sizes that depend on the routing (the number R of dispatched rows) stay on
+ *   the device: R = offsets[L]. Buffers sized by moe_max_rows() hold R valid
+ *   rows; the rows after R are not written.
+ * - `ws` is scratch memory of at least moe_workspace_bytes() bytes, 256-byte
+ *   aligned, used by one call at a time; its contents on entry do not matter.
+ * - Errors: arguments are validated on the host before anything is enqueued;
+ *   a bad argument returns MOE_ERR_INVALID_ARG or MOE_ERR_UNSUPPORTED and
+ *   enqueues nothing. A failed launch returns MOE_ERR_HIP. The library never
+ *   aborts or prints; moe_last_error() gives the message of the calling
+ *   thread's last failure.
+ * - Device preconditions (not checked): inputs are finite; topk_idx entries
+ *   are in [0, E). Results are deterministic: the same inputs give bitwise the
+ *   same outputs on every call.
+ * - T == 0 is a valid empty batch: every call returns MOE_OK and does nothing.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* moe_stream_t; /* a hipStream_t; NULL = the null stream */
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* null pointer, inconsistent or out-of-range sizes */
+  MOE_ERR_UNSUPPORTED = 2, /* valid but outside what the kernels implement    */
+  MOE_ERR_WORKSPACE = 3,   /* ws smaller than moe_workspace_bytes()           */
+  MOE_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed      */
+} moe_status_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+
+/* Problem shape. Local experts are [e_lo, e_hi): the expert weights passed to
+ * the library hold L = e_hi - e_lo experts (local expert le is global expert
+ * e_lo + le), as one expert-parallel rank holds E/EP of them ("Fine-Tuning
+ * Trillion-Parameter Sparse MoE Models: Challenges and Engineering Practices",
+ * §4: 896 / 64 = 14 per rank). Assignments to other experts are not computed.
+ *
+ * capacity > 0 caps the rows kept per expert ("Adapting Ultra-Large MoE
+ * Models: Engineering Practices and Optimization Pathways", §3.3): an expert
+ * chosen more than `capacity` times keeps the assignments with the largest
+ * gate, equal gates going to the lower token; the rest are dropped.
+ *
+ * Limits: 1 <= k <= E <= 1024, k <= 32, 0 <= e_lo < e_hi <= E, T*k < 2^31.
+ * bf16 additionally needs d % 64 == 0 and f % 64 == 0 (MFMA tiles). */
+typedef struct {
+  int32_t T;        /* tokens                          */
+  int32_t d;        /* hidden size                     */
+  int32_t E;        /* routed experts                  */
+  int32_t k;        /* experts per token               */
+  int32_t f;        /* expert FFN width                */
+  int32_t e_lo;     /* first local expert              */
+  int32_t e_hi;     /* one past the last local expert  */
+  int32_t capacity; /* rows kept per expert, <= 0: all */
+  int32_t dtype;    /* moe_dtype_t                     */
+} moe_shape_t;
+
+/* LoRA adapters on the up and down projections of every local expert:
+ * W' = W0 + (alpha/r) B A ("Adapting Trillion-Parameter MoE Models for LoRA
+ * Fine-Tuning: A Full-Stack Engineering Guide", §3). bf16 only, 1 <= r <= 64.
+ *   a_up   [L, r, d]   b_up   [L, f, r]     (U  += s (X A_up^T) B_up^T)
+ *   a_down [L, r, f]   b_down [L, d, r]     (O  += s (H A_down^T) B_down^T)
+ * with s = alpha / r. */
+typedef struct {
+  int32_t r;
+  float alpha;
+  const void* a_up;
+  const void* b_up;
+  const void* a_down;
+  const void* b_down;
+} moe_lora_t;
+
+/* [host] Scratch bytes every entry point below needs for this shape
+ * (lora_r = 0 when no adapters are used). Returns 0 for an invalid shape. */
+size_t moe_workspace_bytes(const moe_shape_t* shape, int32_t lora_r);
+
+/* [host] Upper bound on the dispatched rows R: T*min(k, L), or, with a
+ * capacity, min(T*min(k, L), L*capacity). Buffers indexed by row (row_src,
+ * row_gate, x_perm, act_save, y_perm) need this many rows. -1 if invalid. */
+int64_t moe_max_rows(const moe_shape_t* shape);
+
+/* [host] Message of the calling thread's last failed call ("" if none). */
+const char* moe_last_error(void);
+
+/* Routing ("Day-Level Adaptation ...", §2.1 and §3.3: routing score, Top-16
+ * selection; "Full-Stack Engineering Guide", §2.1: gate score g_i).
+ *   x         [T, d]          tokens
+ *   w_router  [E, d]          router weight (out x in)
+ *   bias      [E] f32 | NULL  per-expert logit bias, added before the softmax
+ *   topk_idx  [T, k] int32    OUT: selected experts, descending logit, ties
+ *                             to the lower expert id (-0.0 equals +0.0)
+ *   topk_gate [T, k] f32      OUT: softmax of the selected logits (the full
+ *                             softmax renormalised over the selection)
+ *   logits    [T, E] f32|NULL OUT (optional): x w_router^T + bias, fp32
+ *                             accumulation; NULL keeps them in ws
+ *   prob_sum  [E] f32 | NULL  OUT (optional): sum over tokens of the full
+ *                             softmax, for moe_aux_loss
+ * Logits are fp32 (bf16 inputs, fp32 accumulation); selection compares the
+ * fp32 logits exactly. */
+moe_status_t moe_route(const moe_shape_t* shape, const void* x, const void* w_router,
+                       const float* bias, int32_t* topk_idx, float* topk_gate,
+                       float* logits, float* prob_sum, void* ws, size_t ws_bytes,
+                       moe_stream_t stream);
+
+/* Dispatch ("Trillion-Parameter ... Full-Stack Optimization Practices", §3
+ * and §4.3: permute tokens by routing result).
+ *   topk_idx, topk_gate       from moe_route
+ *   x         [T, d]          tokens
+ *   counts    [E] int32       OUT: assignments per expert over all T*k,
+ *                             before capacity
+ *   offsets   [L+1] int32     OUT: row block of local expert le is
+ *                             [offsets[le], offsets[le+1]); R = offsets[L]
+ *   slot      [T, k] int32    OUT: row of assignment (t, j), or -1 when its
+ *                             expert is not local or it was dropped
+ *   row_src   [Rmax] int32    OUT: token of each row
+ *   row_gate  [Rmax] f32      OUT: gate of each row
+ *   x_perm    [Rmax, d]       OUT: x_perm[p] = x[row_src[p]] (bitwise copy)
+ *   dropped   [1] int32|NULL  OUT (optional): local assignments dropped by
+ *                             the capacity rule
+ * Rows are grouped by local expert ascending and, within an expert, by token
+ * ascending; the order never depends on thread timing. */
+moe_status_t moe_dispatch(const moe_shape_t* shape, const int32_t* topk_idx,
+                          const float* topk_gate, const void* x, int32_t* counts,
+                          int32_t* offsets, int32_t* slot, int32_t* row_src, float* row_gate,
+                          void* x_perm, int32_t* dropped, void* ws, size_t ws_bytes,
+                          moe_stream_t stream);
+
+/* Grouped expert FFN ("Trillion-Parameter ... Full-Stack Optimization
+ * Practices", §3: experts compute in grouped matrix multiplications; SwiGLU
+ * expert network). For the rows of local expert le:
+ *   G = X w_gate[le]^T, U = X w_up[le]^T (+ LoRA), H = silu(G) * U,
+ *   O = H w_down[le]^T (+ LoRA),  silu(a) = a / (1 + exp(-a)).
+ *   x_perm   [Rmax, d]        rows from moe_dispatch
+ *   offsets  [L+1] int32      from moe_dispatch
+ *   w_gate   [L, f, d]        w_up [L, f, d]        w_down [L, d, f]
+ *   lora     [host] | NULL    adapters (bf16 only)
+ *   act_save [Rmax, 2f]|NULL  OUT (optional): per row G (columns 0..f-1) and
+ *                             the H fed to the down projection (f..2f-1);
+ *                             moe_lora_bwd needs it
+ *   y_perm   [Rmax, d]        OUT: O per row (not gate-scaled)
+ * Accumulation is fp32; in bf16 mode H is rounded to bf16 before the down
+ * projection and O is stored as bf16. */
+moe_status_t moe_expert_gemm(const moe_shape_t* shape, const void* x_perm,
+                             const int32_t* offsets, const void* w_gate, const void* w_up,
+                             const void* w_down, const moe_lora_t* lora, void* act_save,
+                             void* y_perm, void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* Combine ("Full-Stack Engineering Guide", §2.1: results are gathered back
+ * and weighted by g_i).
+ *   y_perm    [Rmax, d]        from moe_expert_gemm
+ *   slot      [T, k] int32     from moe_dispatch
+ *   topk_gate [T, k] f32       from moe_route
+ *   y         [T, d]           OUT: y[t] = sum_j g[t,j] y_perm[slot[t,j]] over
+ *                              slot >= 0, in j order, fp32 accumulation;
+ *                              tokens with no slot get zeros */
+moe_status_t moe_combine(const moe_shape_t* shape, const void* y_perm, const int32_t* slot,
+                         const float* topk_gate, void* y, moe_stream_t stream);
+
+/* Load-balance loss ("Full-Stack Engineering Guide", §2.1 and "Engineering
+ * Practices and Optimization Pathways", §3.3: auxiliary loss that encourages
+ * uniform routing), in the Switch form:
+ *   out[1] = E * sum_e (counts[e] / (T k)) * (prob_sum[e] / T),
+ *   out[0] = coef * out[1].
+ *   counts [E] int32 (moe_dispatch), prob_sum [E] f32 (moe_route), out [2] f32. */
+moe_status_t moe_aux_loss(const moe_shape_t* shape, const int32_t* counts,
+                          const float* prob_sum, float coef, float* out, moe_stream_t stream);
+
+/* Gradients of the four LoRA adapters for the loss sum(y * dy), with the
+ * router, the gates and the base weights frozen ("Full-Stack Engineering
+ * Guide", §3; the routing of the forward is reused, never recomputed, as
+ * "Day-Level Adaptation ...", §5 advises). With s = alpha/r, for the rows of
+ * local expert le, dO[p] = row_gate[p] dy[row_src[p]], Z_u = X A_up^T,
+ * Z_d = H A_down^T:
+ *   db_down = s dO^T Z_d                 da_down = s (dO B_down)^T H
+ *   dH = dO w_down + s (dO B_down) A_down,  dU = dH * silu(G)
+ *   db_up   = s dU^T Z_u                 da_up   = s (dU B_up)^T X
+ *   dy          [T, d]            upstream gradient of y
+ *   offsets, row_src, row_gate    from moe_dispatch
+ *   x_perm      [Rmax, d]         from moe_dispatch
+ *   act_save    [Rmax, 2f]        from moe_expert_gemm (G and H)
+ *   w_down      [L, d, f]
+ *   da_up [L,r,d], db_up [L,f,r], da_down [L,r,f], db_down [L,d,r]   OUT, f32
+ * bf16 only. Every gradient element is written (zero for experts with no
+ * rows). */
+moe_status_t moe_lora_bwd(const moe_shape_t* shape, const moe_lora_t* lora, const void* dy,
+                          const int32_t* offsets, const int32_t* row_src, const float* row_gate,
+                          const void* x_perm, const void* act_save, const void* w_down,
+                          float* da_up, float* db_up, float* da_down, float* db_down, void* ws,
+                          size_t ws_bytes, moe_stream_t stream);
+
+/* ---- kernel timing (profiling aid) -------------------------------------
+ * When enabled, the library records a pair of HIP events on the launch
+ * stream around every kernel it enqueues, per kernel kind. moe_timing_read
+ * waits for the recorded events and returns the summed duration and the
+ * launch count of one kind since the last reset. [host] */
+typedef enum {
+  MOE_K_ROUTER_GEMM = 0,
+  MOE_K_TOPK = 1,
+  MOE_K_PROB_REDUCE = 2,
+  MOE_K_HIST = 3,
+  MOE_K_SCAN = 4,
+  MOE_K_SCATTER = 5,
+  MOE_K_CAPACITY = 6,
+  MOE_K_GATHER = 7,
+  MOE_K_TILES = 8,
+  MOE_K_GATE_UP = 9,
+  MOE_K_DOWN = 10,
+  MOE_K_COMBINE = 11,
+  MOE_K_AUX = 12,
+  MOE_K_LORA_PROJ = 13,
+  MOE_K_LORA_DH = 14,
+  MOE_K_LORA_GRAD = 15,
+  MOE_K_COUNT = 16
+} moe_kernel_t;
+
+moe_status_t moe_timing_enable(int32_t on);  /* also resets the totals */
+moe_status_t moe_timing_read(int32_t kernel, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,182 @@
+"""ctypes binding of libmoe_mi355x.so, one Python function per C entry point.
+
+Argument marshalling only: each function checks that the tensors it is given
+are contiguous, on the GPU and of the expected dtype, then passes their device
+pointers and torch's current HIP stream to the C function of the same name.
+Every computation runs in the library's HIP kernels; if the library is not
+built, loading fails with an error instead of falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_mi355x.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_F32, MOE_BF16 = 0, 1
+
+KERNELS = ["router_gemm", "topk", "prob_reduce", "hist", "scan", "scatter", "capacity",
+           "gather", "tiles", "gate_up", "down", "combine", "aux", "lora_proj", "lora_dh",
+           "lora_grad"]
+
+EXPORTED = ["moe_workspace_bytes", "moe_max_rows", "moe_last_error", "moe_route",
+            "moe_dispatch", "moe_expert_gemm", "moe_combine", "moe_aux_loss", "moe_lora_bwd",
+            "moe_timing_enable", "moe_timing_read"]
+
+
+class MoeShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("T", "d", "E", "k", "f", "e_lo", "e_hi", "capacity", "dtype")]
+
+
+class MoeLora(ctypes.Structure):
+    _fields_ = [("r", ctypes.c_int32), ("alpha", ctypes.c_float), ("a_up", ctypes.c_void_p),
+                ("b_up", ctypes.c_void_p), ("a_down", ctypes.c_void_p), ("b_down", ctypes.c_void_p)]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"status {status}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the library once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m sparse_mixture_experts_top_amd._build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    shp, lor = ctypes.POINTER(MoeShape), ctypes.POINTER(MoeLora)
+    L.moe_workspace_bytes.argtypes, L.moe_workspace_bytes.restype = [shp, i32], sz
+    L.moe_max_rows.argtypes, L.moe_max_rows.restype = [shp], i64
+    L.moe_last_error.argtypes, L.moe_last_error.restype = [], ctypes.c_char_p
+    L.moe_route.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_dispatch.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_expert_gemm.argtypes = [shp, vp, vp, vp, vp, vp, lor, vp, vp, vp, sz, vp]
+    L.moe_combine.argtypes = [shp, vp, vp, vp, vp, vp]
+    L.moe_aux_loss.argtypes = [shp, vp, vp, f32, vp, vp]
+    L.moe_lora_bwd.argtypes = [shp, lor, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_timing_enable.argtypes = [i32]
+    L.moe_timing_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+    for fn in ("moe_route", "moe_dispatch", "moe_expert_gemm", "moe_combine", "moe_aux_loss",
+               "moe_lora_bwd", "moe_timing_enable", "moe_timing_read"):
+        getattr(L, fn).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(status: int) -> None:
+    if status != MOE_OK:
+        raise MoeError(status, lib().moe_last_error().decode())
+
+
+def make_shape(T, d, E, k, f, e_lo=0, e_hi=None, capacity=0, dtype=MOE_BF16) -> MoeShape:
+    return MoeShape(T, d, E, k, f, e_lo, E if e_hi is None else e_hi, capacity, dtype)
+
+
+def make_lora(r: int, alpha: float, a_up, b_up, a_down, b_down) -> MoeLora:
+    for t in (a_up, b_up, a_down, b_down):
+        _dev(t, torch.bfloat16)
+    return MoeLora(r, alpha, a_up.data_ptr(), b_up.data_ptr(), a_down.data_ptr(), b_down.data_ptr())
+
+
+def _dev(t: Optional[torch.Tensor], dtype=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"expected {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _fdt(shape: MoeShape):
+    return torch.bfloat16 if shape.dtype == MOE_BF16 else torch.float32
+
+
+def _stream(stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def moe_workspace_bytes(shape: MoeShape, lora_r: int = 0) -> int:
+    return int(lib().moe_workspace_bytes(ctypes.byref(shape), lora_r))
+
+
+def moe_max_rows(shape: MoeShape) -> int:
+    return int(lib().moe_max_rows(ctypes.byref(shape)))
+
+
+def moe_route(shape, x, w_router, bias, topk_idx, topk_gate, logits, prob_sum, ws, stream=None):
+    dt = _fdt(shape)
+    _check(lib().moe_route(ctypes.byref(shape), _dev(x, dt), _dev(w_router, dt),
+                           _dev(bias, torch.float32), _dev(topk_idx, torch.int32),
+                           _dev(topk_gate, torch.float32), _dev(logits, torch.float32),
+                           _dev(prob_sum, torch.float32), _dev(ws, torch.uint8), ws.numel(),
+                           _stream(stream)))
+
+
+def moe_dispatch(shape, topk_idx, topk_gate, x, counts, offsets, slot, row_src, row_gate, x_perm,
+                 dropped, ws, stream=None):
+    dt, i32 = _fdt(shape), torch.int32
+    _check(lib().moe_dispatch(ctypes.byref(shape), _dev(topk_idx, i32), _dev(topk_gate, torch.float32),
+                              _dev(x, dt), _dev(counts, i32), _dev(offsets, i32), _dev(slot, i32),
+                              _dev(row_src, i32), _dev(row_gate, torch.float32), _dev(x_perm, dt),
+                              _dev(dropped, i32), _dev(ws, torch.uint8), ws.numel(), _stream(stream)))
+
+
+def moe_expert_gemm(shape, x_perm, offsets, w_gate, w_up, w_down, lora, act_save, y_perm, ws,
+                    stream=None):
+    dt = _fdt(shape)
+    _check(lib().moe_expert_gemm(ctypes.byref(shape), _dev(x_perm, dt), _dev(offsets, torch.int32),
+                                 _dev(w_gate, dt), _dev(w_up, dt), _dev(w_down, dt),
+                                 ctypes.byref(lora) if lora is not None else None,
+                                 _dev(act_save, dt), _dev(y_perm, dt), _dev(ws, torch.uint8),
+                                 ws.numel(), _stream(stream)))
+
+
+def moe_combine(shape, y_perm, slot, topk_gate, y, stream=None):
+    dt = _fdt(shape)
+    _check(lib().moe_combine(ctypes.byref(shape), _dev(y_perm, dt), _dev(slot, torch.int32),
+                             _dev(topk_gate, torch.float32), _dev(y, dt), _stream(stream)))
+
+
+def moe_aux_loss(shape, counts, prob_sum, coef, out, stream=None):
+    _check(lib().moe_aux_loss(ctypes.byref(shape), _dev(counts, torch.int32),
+                              _dev(prob_sum, torch.float32), float(coef), _dev(out, torch.float32),
+                              _stream(stream)))
+
+
+def moe_lora_bwd(shape, lora, dy, offsets, row_src, row_gate, x_perm, act_save, w_down, da_up,
+                 db_up, da_down, db_down, ws, stream=None):
+    bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
+    _check(lib().moe_lora_bwd(ctypes.byref(shape), ctypes.byref(lora), _dev(dy, bf), _dev(offsets, i32),
+                              _dev(row_src, i32), _dev(row_gate, f32), _dev(x_perm, bf),
+                              _dev(act_save, bf), _dev(w_down, bf), _dev(da_up, f32),
+                              _dev(db_up, f32), _dev(da_down, f32), _dev(db_down, f32),
+                              _dev(ws, torch.uint8), ws.numel(), _stream(stream)))
+
+
+def moe_timing_enable(on: bool) -> None:
+    _check(lib().moe_timing_enable(1 if on else 0))
+
+
+def moe_timing_read(kernel: str):
+    """(total milliseconds, launches) of one kernel kind since the last enable."""
+    ms, n = ctypes.c_double(0.0), ctypes.c_int64(0)
+    _check(lib().moe_timing_read(KERNELS.index(kernel), ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value

@@ -1,0 +1,393 @@
+// Host side of the C ABI declared in include/moe.h: argument validation,
+// workspace layout, per-device launch context, kernel timing, error text.
+#include <algorithm>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "common.h"
+
+namespace moe {
+
+static thread_local std::string g_error;
+
+static moe_status_t fail(moe_status_t st, const std::string& msg) {
+  g_error = msg;
+  return st;
+}
+
+static int64_t align256(int64_t b) { return (b + 255) & ~int64_t(255); }
+
+int64_t max_rows(const moe_shape_t& s) {
+  const int64_t L = s.e_hi - s.e_lo;
+  int64_t r = (int64_t)s.T * std::min<int64_t>(s.k, L);
+  if (s.capacity > 0) r = std::min<int64_t>(r, L * (int64_t)s.capacity);
+  return r;
+}
+
+int gemm_max_tiles(const moe_shape_t& s) {
+  return (int)((max_rows(s) + kGemmBM - 1) / kGemmBM + (s.e_hi - s.e_lo));
+}
+
+Workspace carve_workspace(const moe_shape_t& s, int lora_r, void* base) {
+  Workspace w{};
+  char* p = static_cast<char*>(base);
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) -> void* {
+    void* q = p ? static_cast<void*>(p + off) : nullptr;
+    off += align256(bytes > 0 ? bytes : 1);
+    return q;
+  };
+  const int64_t L = s.e_hi - s.e_lo;
+  const int64_t ntok_tiles = (s.T + kTokTile - 1) / kTokTile;
+  const int64_t rmax = max_rows(s);
+  const int64_t elt = s.dtype == MOE_BF16 ? 2 : 4;
+  w.tile_counts = static_cast<int32_t*>(take(ntok_tiles * s.E * 4));
+  w.tile_base = static_cast<int32_t*>(take(ntok_tiles * s.E * 4));
+  w.cseg = static_cast<int32_t*>(take((L + 1) * 4));
+  if (s.capacity > 0) {
+    w.cand_key = static_cast<uint32_t*>(take((int64_t)s.T * s.k * 4));
+    w.cand_idx = static_cast<int32_t*>(take((int64_t)s.T * s.k * 4));
+  }
+  w.gemm_tiles = static_cast<int32_t*>(take((2 * (int64_t)gemm_max_tiles(s) + 1) * 4));
+  w.hbuf = take(rmax * s.f * elt);
+  if (lora_r > 0) {
+    w.zu = static_cast<float*>(take(rmax * lora_r * 4));
+    w.zd = static_cast<float*>(take(rmax * lora_r * 4));
+    w.wproj = static_cast<float*>(take(rmax * lora_r * 4));
+    w.vproj = static_cast<float*>(take(rmax * lora_r * 4));
+    w.du = static_cast<float*>(take(rmax * s.f * 4));
+  }
+  w.logits = static_cast<float*>(take((int64_t)s.T * s.E * 4));
+  w.prob_part = static_cast<float*>(take(((int64_t)s.T + kTopkTokPerBlock - 1) / kTopkTokPerBlock * s.E * 4));
+  w.bytes = off;
+  return w;
+}
+
+// ------------------------------------------------------------ validation ---
+
+static moe_status_t check_shape(const moe_shape_t* s) {
+  if (!s) return fail(MOE_ERR_INVALID_ARG, "shape is NULL");
+  if (s->T < 0) return fail(MOE_ERR_INVALID_ARG, "T < 0");
+  if (s->d < 1 || s->E < 1 || s->f < 1) return fail(MOE_ERR_INVALID_ARG, "d, E and f must be >= 1");
+  if (s->k < 1 || s->k > s->E) return fail(MOE_ERR_INVALID_ARG, "k must be in [1, E]");
+  if (s->e_lo < 0 || s->e_hi > s->E || s->e_lo >= s->e_hi)
+    return fail(MOE_ERR_INVALID_ARG, "local experts [e_lo, e_hi) must be a non-empty range inside [0, E)");
+  if (s->dtype != MOE_F32 && s->dtype != MOE_BF16) return fail(MOE_ERR_INVALID_ARG, "dtype must be MOE_F32 or MOE_BF16");
+  if ((int64_t)s->T * s->k >= (int64_t(1) << 31)) return fail(MOE_ERR_INVALID_ARG, "T*k must be < 2^31");
+  if (s->E > 1024) return fail(MOE_ERR_UNSUPPORTED, "E > 1024");
+  if (s->k > 32) return fail(MOE_ERR_UNSUPPORTED, "k > 32");
+  if (s->dtype == MOE_BF16 && (s->d % 64 != 0 || s->f % 64 != 0))
+    return fail(MOE_ERR_UNSUPPORTED, "bf16 needs d % 64 == 0 and f % 64 == 0");
+  return MOE_OK;
+}
+
+static moe_status_t check_lora(const moe_shape_t& s, const moe_lora_t* lo) {
+  if (!lo) return MOE_OK;
+  if (lo->r < 1) return fail(MOE_ERR_INVALID_ARG, "LoRA rank must be >= 1");
+  if (!lo->a_up || !lo->b_up || !lo->a_down || !lo->b_down)
+    return fail(MOE_ERR_INVALID_ARG, "LoRA adapter pointer is NULL");
+  if (lo->r > 64) return fail(MOE_ERR_UNSUPPORTED, "LoRA rank > 64");
+  if (s.dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "LoRA needs dtype MOE_BF16");
+  return MOE_OK;
+}
+
+#define MOE_REQUIRE(ptr, name) \
+  if (!(ptr)) return fail(MOE_ERR_INVALID_ARG, std::string(name) + " is NULL")
+// Buffers sized by T (or by the row bound) may be NULL when that size is 0.
+#define MOE_REQUIRE_IF(cond, ptr, name) \
+  if ((cond) && !(ptr)) return fail(MOE_ERR_INVALID_ARG, std::string(name) + " is NULL")
+
+static moe_status_t check_ws(const moe_shape_t& s, int lora_r, const void* ws, size_t ws_bytes) {
+  const int64_t need = carve_workspace(s, lora_r, nullptr).bytes;
+  if (!ws) return fail(MOE_ERR_INVALID_ARG, "ws is NULL");
+  if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return fail(MOE_ERR_INVALID_ARG, "ws must be 256-byte aligned");
+  if ((int64_t)ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "ws has " + std::to_string(ws_bytes) + " bytes, needs " + std::to_string(need));
+  return MOE_OK;
+}
+
+// ----------------------------------------------------------- device info ---
+
+static moe_status_t make_ctx(moe_stream_t stream, Ctx* c) {
+  static std::mutex mu;
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+    return fail(MOE_ERR_HIP, "hipGetDevice failed (no HIP device?)");
+  {
+    std::lock_guard<std::mutex> g(mu);
+    if (cus[dev] == 0) {
+      int n = 0;
+      if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        return fail(MOE_ERR_HIP, "hipDeviceGetAttribute(MultiprocessorCount) failed");
+      cus[dev] = (n + 3) & ~3;  // persistent grids of 2 per CU stay a multiple of 8
+    }
+    c->num_cus = cus[dev];
+  }
+  c->stream = reinterpret_cast<hipStream_t>(stream);
+  return MOE_OK;
+}
+
+static moe_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MOE_OK;
+  return fail(MOE_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// ---------------------------------------------------------------- timing ---
+
+namespace {
+struct Timing {
+  std::mutex mu;
+  bool on = false;
+  std::vector<hipEvent_t> pool;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pending[MOE_K_COUNT];
+  double total_ms[MOE_K_COUNT] = {};
+  int64_t launches[MOE_K_COUNT] = {};
+};
+Timing& timing() {
+  static Timing t;
+  return t;
+}
+thread_local hipEvent_t t_open[MOE_K_COUNT] = {};
+
+hipEvent_t take_event(Timing& t) {
+  if (t.pool.empty()) {
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+  hipEvent_t e = t.pool.back();
+  t.pool.pop_back();
+  return e;
+}
+
+void drain(Timing& t, int kid) {
+  for (auto& pr : t.pending[kid]) {
+    float ms = 0.f;
+    if (hipEventSynchronize(pr.second) == hipSuccess &&
+        hipEventElapsedTime(&ms, pr.first, pr.second) == hipSuccess) {
+      t.total_ms[kid] += ms;
+      t.launches[kid] += 1;
+    }
+    t.pool.push_back(pr.first);
+    t.pool.push_back(pr.second);
+  }
+  t.pending[kid].clear();
+}
+}  // namespace
+
+void timing_begin(int kid, hipStream_t s) {
+  Timing& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  if (!t.on) return;
+  hipEvent_t e = take_event(t);
+  if (e && hipEventRecord(e, s) == hipSuccess) t_open[kid] = e;
+}
+
+void timing_end(int kid, hipStream_t s) {
+  Timing& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  hipEvent_t start = t_open[kid];
+  t_open[kid] = nullptr;
+  if (!t.on || !start) return;
+  hipEvent_t e = take_event(t);
+  if (e && hipEventRecord(e, s) == hipSuccess) t.pending[kid].push_back({start, e});
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+// ============================================================== C ABI ======
+
+extern "C" {
+
+size_t moe_workspace_bytes(const moe_shape_t* shape, int32_t lora_r) {
+  if (check_shape(shape) != MOE_OK || lora_r < 0 || lora_r > 64) return 0;
+  return (size_t)carve_workspace(*shape, lora_r, nullptr).bytes;
+}
+
+int64_t moe_max_rows(const moe_shape_t* shape) {
+  if (check_shape(shape) != MOE_OK) return -1;
+  return max_rows(*shape);
+}
+
+const char* moe_last_error(void) { return g_error.c_str(); }
+
+moe_status_t moe_route(const moe_shape_t* shape, const void* x, const void* w_router,
+                       const float* bias, int32_t* topk_idx, float* topk_gate, float* logits,
+                       float* prob_sum, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  moe_status_t st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape_t& s = *shape;
+  MOE_REQUIRE_IF(s.T > 0, x, "x");
+  MOE_REQUIRE(w_router, "w_router");
+  MOE_REQUIRE_IF(s.T > 0, topk_idx, "topk_idx");
+  MOE_REQUIRE_IF(s.T > 0, topk_gate, "topk_gate");
+  if ((st = check_ws(s, 0, ws, ws_bytes)) != MOE_OK) return st;
+  Ctx c;
+  if ((st = make_ctx(stream, &c)) != MOE_OK) return st;
+  const Workspace w = carve_workspace(s, 0, ws);
+  float* lg = logits ? logits : w.logits;
+  if (s.T > 0) {
+    if ((st = hip_status(launch_router(c, s, x, w_router, bias, lg), "router GEMM")) != MOE_OK) return st;
+  }
+  return hip_status(launch_topk(c, s, lg, topk_idx, topk_gate, w.prob_part, prob_sum), "top-k");
+}
+
+moe_status_t moe_dispatch(const moe_shape_t* shape, const int32_t* topk_idx,
+                          const float* topk_gate, const void* x, int32_t* counts,
+                          int32_t* offsets, int32_t* slot, int32_t* row_src, float* row_gate,
+                          void* x_perm, int32_t* dropped, void* ws, size_t ws_bytes,
+                          moe_stream_t stream) {
+  moe_status_t st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape_t& s = *shape;
+  const bool rows = max_rows(s) > 0;
+  MOE_REQUIRE_IF(s.T > 0, topk_idx, "topk_idx");
+  MOE_REQUIRE_IF(s.T > 0, topk_gate, "topk_gate");
+  MOE_REQUIRE_IF(s.T > 0, x, "x");
+  MOE_REQUIRE(counts, "counts");
+  MOE_REQUIRE(offsets, "offsets");
+  MOE_REQUIRE_IF(s.T > 0, slot, "slot");
+  MOE_REQUIRE_IF(rows, row_src, "row_src");
+  MOE_REQUIRE_IF(rows, row_gate, "row_gate");
+  MOE_REQUIRE_IF(rows, x_perm, "x_perm");
+  if ((st = check_ws(s, 0, ws, ws_bytes)) != MOE_OK) return st;
+  Ctx c;
+  if ((st = make_ctx(stream, &c)) != MOE_OK) return st;
+  const Workspace w = carve_workspace(s, 0, ws);
+  return hip_status(launch_dispatch(c, s, w, topk_idx, topk_gate, x, counts, offsets, slot, row_src,
+                                    row_gate, x_perm, dropped),
+                    "dispatch");
+}
+
+moe_status_t moe_expert_gemm(const moe_shape_t* shape, const void* x_perm,
+                             const int32_t* offsets, const void* w_gate, const void* w_up,
+                             const void* w_down, const moe_lora_t* lora, void* act_save,
+                             void* y_perm, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  moe_status_t st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape_t& s = *shape;
+  const bool rows = max_rows(s) > 0;
+  MOE_REQUIRE_IF(rows, x_perm, "x_perm");
+  MOE_REQUIRE(offsets, "offsets");
+  MOE_REQUIRE(w_gate, "w_gate");
+  MOE_REQUIRE(w_up, "w_up");
+  MOE_REQUIRE(w_down, "w_down");
+  MOE_REQUIRE_IF(rows, y_perm, "y_perm");
+  if ((st = check_lora(s, lora)) != MOE_OK) return st;
+  const int r = lora ? lora->r : 0;
+  if ((st = check_ws(s, r, ws, ws_bytes)) != MOE_OK) return st;
+  Ctx c;
+  if ((st = make_ctx(stream, &c)) != MOE_OK) return st;
+  const Workspace w = carve_workspace(s, r, ws);
+  LoraArgs la{};
+  if (lora) {
+    la.r = lora->r;
+    la.scale = lora->alpha / (float)lora->r;
+    la.a_up = static_cast<const bf16_t*>(lora->a_up);
+    la.b_up = static_cast<const bf16_t*>(lora->b_up);
+    la.a_down = static_cast<const bf16_t*>(lora->a_down);
+    la.b_down = static_cast<const bf16_t*>(lora->b_down);
+  }
+  return hip_status(launch_expert_gemm(c, s, w, x_perm, offsets, w_gate, w_up, w_down,
+                                       lora ? &la : nullptr, act_save, y_perm),
+                    "expert GEMM");
+}
+
+moe_status_t moe_combine(const moe_shape_t* shape, const void* y_perm, const int32_t* slot,
+                         const float* topk_gate, void* y, moe_stream_t stream) {
+  moe_status_t st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape_t& s = *shape;
+  if (s.T == 0) return MOE_OK;
+  MOE_REQUIRE_IF(max_rows(s) > 0, y_perm, "y_perm");
+  MOE_REQUIRE(slot, "slot");
+  MOE_REQUIRE(topk_gate, "topk_gate");
+  MOE_REQUIRE(y, "y");
+  Ctx c;
+  if ((st = make_ctx(stream, &c)) != MOE_OK) return st;
+  return hip_status(launch_combine(c, s, y_perm, slot, topk_gate, y), "combine");
+}
+
+moe_status_t moe_aux_loss(const moe_shape_t* shape, const int32_t* counts,
+                          const float* prob_sum, float coef, float* out, moe_stream_t stream) {
+  moe_status_t st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  MOE_REQUIRE(counts, "counts");
+  MOE_REQUIRE(prob_sum, "prob_sum");
+  MOE_REQUIRE(out, "out");
+  Ctx c;
+  if ((st = make_ctx(stream, &c)) != MOE_OK) return st;
+  return hip_status(launch_aux(c, *shape, counts, prob_sum, coef, out), "aux loss");
+}
+
+moe_status_t moe_lora_bwd(const moe_shape_t* shape, const moe_lora_t* lora, const void* dy,
+                          const int32_t* offsets, const int32_t* row_src, const float* row_gate,
+                          const void* x_perm, const void* act_save, const void* w_down,
+                          float* da_up, float* db_up, float* da_down, float* db_down, void* ws,
+                          size_t ws_bytes, moe_stream_t stream) {
+  moe_status_t st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape_t& s = *shape;
+  MOE_REQUIRE(lora, "lora");
+  if ((st = check_lora(s, lora)) != MOE_OK) return st;
+  const bool rows = max_rows(s) > 0;
+  MOE_REQUIRE_IF(s.T > 0, dy, "dy");
+  MOE_REQUIRE(offsets, "offsets");
+  MOE_REQUIRE_IF(rows, row_src, "row_src");
+  MOE_REQUIRE_IF(rows, row_gate, "row_gate");
+  MOE_REQUIRE_IF(rows, x_perm, "x_perm");
+  MOE_REQUIRE_IF(rows, act_save, "act_save");
+  MOE_REQUIRE(w_down, "w_down");
+  MOE_REQUIRE(da_up, "da_up");
+  MOE_REQUIRE(db_up, "db_up");
+  MOE_REQUIRE(da_down, "da_down");
+  MOE_REQUIRE(db_down, "db_down");
+  if ((st = check_ws(s, lora->r, ws, ws_bytes)) != MOE_OK) return st;
+  Ctx c;
+  if ((st = make_ctx(stream, &c)) != MOE_OK) return st;
+  const Workspace w = carve_workspace(s, lora->r, ws);
+  LoraArgs la{lora->r, lora->alpha / (float)lora->r, static_cast<const bf16_t*>(lora->a_up),
+              static_cast<const bf16_t*>(lora->b_up), static_cast<const bf16_t*>(lora->a_down),
+              static_cast<const bf16_t*>(lora->b_down)};
+  return hip_status(
+      launch_lora_bwd(c, s, w, la, static_cast<const bf16_t*>(dy), offsets, row_src, row_gate,
+                      static_cast<const bf16_t*>(x_perm), static_cast<const bf16_t*>(act_save),
+                      static_cast<const bf16_t*>(w_down), da_up, db_up, da_down, db_down),
+      "LoRA backward");
+}
+
+moe_status_t moe_timing_enable(int32_t on) {
+  Timing& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  for (int k = 0; k < MOE_K_COUNT; ++k) {
+    drain(t, k);
+    t.total_ms[k] = 0.0;
+    t.launches[k] = 0;
+  }
+  if (on && t.pool.size() < 512) {
+    for (int i = 0; i < 512; ++i) {
+      hipEvent_t e = nullptr;
+      if (hipEventCreate(&e) != hipSuccess) return fail(MOE_ERR_HIP, "hipEventCreate failed");
+      t.pool.push_back(e);
+    }
+  }
+  t.on = on != 0;
+  return MOE_OK;
+}
+
+moe_status_t moe_timing_read(int32_t kernel, double* total_ms, int64_t* launches) {
+  if (kernel < 0 || kernel >= MOE_K_COUNT) return fail(MOE_ERR_INVALID_ARG, "unknown kernel id");
+  if (!total_ms || !launches) return fail(MOE_ERR_INVALID_ARG, "output pointer is NULL");
+  Timing& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  drain(t, kernel);
+  *total_ms = t.total_ms[kernel];
+  *launches = t.launches[kernel];
+  return MOE_OK;
+}
+
+}  // extern "C"

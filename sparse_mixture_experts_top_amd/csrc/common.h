@@ -1,0 +1,156 @@
+// Internal declarations shared by the kernels and the host entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+#include <algorithm>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+typedef uint16_t bf16_t;  // bfloat16 bit pattern in memory
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- numbers ---
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round to nearest, ties to even (NaN stays NaN).
+__device__ __forceinline__ bf16_t f32_to_bf16(float v) {
+  uint32_t u = __float_as_uint(v);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return static_cast<bf16_t>((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+template <class T> __device__ __forceinline__ float load_f(const T* p);
+template <> __device__ __forceinline__ float load_f<float>(const float* p) { return *p; }
+template <> __device__ __forceinline__ float load_f<bf16_t>(const bf16_t* p) { return bf16_to_f32(*p); }
+
+template <class T> __device__ __forceinline__ void store_f(T* p, float v);
+template <> __device__ __forceinline__ void store_f<float>(float* p, float v) { *p = v; }
+template <> __device__ __forceinline__ void store_f<bf16_t>(bf16_t* p, float v) { *p = f32_to_bf16(v); }
+
+__device__ __forceinline__ float silu_f(float a) { return a / (1.0f + expf(-a)); }
+
+// Index of the row block containing row p: largest le with off[le] <= p
+// (off has L+1 non-decreasing entries, off[0] = 0, p < off[L]).
+__device__ __forceinline__ int segment_of(const int32_t* off, int L, int p) {
+  int lo = 0, hi = L;  // invariant: off[lo] <= p < off[hi]
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (off[mid] <= p) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+// ------------------------------------------------------------- host side ---
+
+struct Ctx {
+  hipStream_t stream;
+  int num_cus;
+};
+
+// Kernel timing hooks (api.cpp). begin/end bracket one launch.
+void timing_begin(int kid, hipStream_t s);
+void timing_end(int kid, hipStream_t s);
+
+struct TimedLaunch {
+  int kid;
+  hipStream_t s;
+  TimedLaunch(int k, hipStream_t st) : kid(k), s(st) { timing_begin(kid, s); }
+  ~TimedLaunch() { timing_end(kid, s); }
+};
+
+// Workspace carve-up (api.cpp).
+struct Workspace {
+  int32_t* tile_counts;  // [ntok_tiles, E]
+  int32_t* tile_base;    // [ntok_tiles, E]
+  int32_t* cseg;         // [L+1]   candidate segment offsets (capacity)
+  uint32_t* cand_key;    // [T*k]   gate bits of candidates (capacity)
+  int32_t* cand_idx;     // [T*k]   assignment index t*k+j (capacity)
+  int32_t* gemm_tiles;   // [max_tiles*2 + 1] (expert, row0) pairs + count at the end
+  void* hbuf;            // [Rmax, f] H in the shape's dtype
+  float* zu;             // [Rmax, rmax] LoRA X A_up^T
+  float* zd;             // [Rmax, rmax] LoRA H A_down^T
+  float* wproj;          // [Rmax, rmax] LoRA dO B_down
+  float* vproj;          // [Rmax, rmax] LoRA dU B_up
+  float* du;             // [Rmax, f]   LoRA backward dU (f32)
+  float* logits;         // [T, E]
+  float* prob_part;      // [prob_blocks, E]
+  int64_t bytes;
+};
+
+constexpr int kTokTile = 256;      // tokens per dispatch tile
+constexpr int kTopkTokPerBlock = 16;  // tokens per top-k block (4 waves x 4)
+constexpr int kGemmBM = 128;       // grouped GEMM row tile
+
+Workspace carve_workspace(const moe_shape_t& s, int lora_r, void* base);
+int64_t max_rows(const moe_shape_t& s);
+int gemm_max_tiles(const moe_shape_t& s);
+
+// ------------------------------------------------------ kernel launchers ---
+// Each returns hipSuccess or the launch error.
+
+hipError_t launch_router(const Ctx& c, const moe_shape_t& s, const void* x, const void* w,
+                         const float* bias, float* logits);
+hipError_t launch_topk(const Ctx& c, const moe_shape_t& s, const float* logits, int32_t* idx,
+                       float* gate, float* prob_part, float* prob_sum);
+hipError_t launch_aux(const Ctx& c, const moe_shape_t& s, const int32_t* counts,
+                      const float* prob_sum, float coef, float* out);
+
+hipError_t launch_dispatch(const Ctx& c, const moe_shape_t& s, const Workspace& ws,
+                           const int32_t* idx, const float* gate, const void* x, int32_t* counts,
+                           int32_t* offsets, int32_t* slot, int32_t* row_src, float* row_gate,
+                           void* x_perm, int32_t* dropped);
+
+struct LoraArgs {
+  int r;
+  float scale;
+  const bf16_t* a_up;
+  const bf16_t* b_up;
+  const bf16_t* a_down;
+  const bf16_t* b_down;
+};
+
+hipError_t launch_expert_gemm(const Ctx& c, const moe_shape_t& s, const Workspace& ws,
+                              const void* x_perm, const int32_t* offsets, const void* w_gate,
+                              const void* w_up, const void* w_down, const LoraArgs* lora,
+                              void* act_save, void* y_perm);
+
+hipError_t launch_row_tiles(const Ctx& c, const int32_t* offsets, int L, int max_tiles,
+                            int32_t* tiles);
+
+hipError_t launch_combine(const Ctx& c, const moe_shape_t& s, const void* y_perm,
+                          const int32_t* slot, const float* gate, void* y);
+
+hipError_t launch_lora_bwd(const Ctx& c, const moe_shape_t& s, const Workspace& ws,
+                           const LoraArgs& lo, const bf16_t* dy, const int32_t* offsets,
+                           const int32_t* row_src, const float* row_gate, const bf16_t* x_perm,
+                           const bf16_t* act_save, const bf16_t* w_down, float* da_up,
+                           float* db_up, float* da_down, float* db_down);
+
+// LoRA building blocks shared by the forward (expert_gemm) and the backward.
+// out[p, q] = scale_p * sum_i in[src(p), i] * M(le(p), q, i) for rows p < R.
+//   m_qk: M stored [L, r, K] (true) or [L, K, r] (false)
+template <class TIn>
+hipError_t launch_lora_rowproj(const Ctx& c, int L, const int32_t* offsets, int64_t rmax_rows,
+                               const TIn* in, int64_t in_stride, const int32_t* src,
+                               const float* row_scale, int K, const bf16_t* M, bool m_qk, int r,
+                               float* out);
+
+}  // namespace moe

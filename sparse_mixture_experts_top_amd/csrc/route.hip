@@ -1,0 +1,272 @@
+// Routing: router GEMM, softmax + top-k + renormalised gates, load-balance loss.
+//
+// The router scores every expert for every token (logits = x W_r^T + b), each
+// token keeps its k best experts, and the gate is the softmax restricted to
+// them ("Adapting Trillion-Parameter MoE Models for LoRA Fine-Tuning: A
+// Full-Stack Engineering Guide", §2.1: g_i is the routing gate score; "Day-
+// Level Adaptation and LoRA Fine-Tuning of Ultra-Large-Scale Sparse MoE
+// Models", §2.1: Top-16 selection and the auxiliary load-balancing loss).
+#include "common.h"
+#include "mfma_tile.h"
+
+namespace moe {
+
+// ------------------------------------------------------------ router GEMM ---
+
+// bf16: logits[T, E] (f32) = x[T, d] * w[E, d]^T + bias. One 128 x 128 (or
+// 64 x 128) tile per workgroup, tiles visited in XCD-aware order.
+template <class Cfg>
+__global__ __launch_bounds__(256) void router_gemm_bf16(const bf16_t* __restrict__ x,
+                                                        const bf16_t* __restrict__ w,
+                                                        const float* __restrict__ bias,
+                                                        float* __restrict__ logits, int T, int d,
+                                                        int E, int mt, int nt) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  bf16_t* smem = reinterpret_cast<bf16_t*>(smem_raw);
+  const XcdSplit sp = xcd_split(mt * nt);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lrow = tid / Cfg::CHUNKS_PER_ROW, lcol = (tid % Cfg::CHUNKS_PER_ROW) * 8;
+  for (int item = sp.first; item < sp.end; item += sp.stride) {
+    const int m0 = (item / nt) * Cfg::BM, n0 = (item % nt) * Cfg::BN;
+    const bf16_t* a_rows[Cfg::A_LOADS];
+    const bf16_t* b_rows[Cfg::B_LOADS];
+#pragma unroll
+    for (int i = 0; i < Cfg::A_LOADS; ++i)
+      a_rows[i] = x + (int64_t)min(m0 + lrow + i * Cfg::ROWS_PER_PASS, T - 1) * d + lcol;
+#pragma unroll
+    for (int i = 0; i < Cfg::B_LOADS; ++i)
+      b_rows[i] = w + (int64_t)min(n0 + lrow + i * Cfg::ROWS_PER_PASS, E - 1) * d + lcol;
+    Acc<Cfg> acc;
+    acc.zero();
+    mainloop_nt<Cfg>(a_rows, b_rows, d, acc, smem);
+#pragma unroll
+    for (int j = 0; j < Cfg::FN; ++j) {
+      const int n = n0 + frag_col<Cfg>(wn, j, lane);
+      if (n >= E) continue;
+      const float b = bias ? bias[n] : 0.f;
+#pragma unroll
+      for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = m0 + frag_row<Cfg>(wm, i, lane, r);
+          if (m < T) logits[(int64_t)m * E + n] = acc.v[i][j][r] + b;
+        }
+    }
+  }
+}
+
+// fp32: one thread per logit, plain dot product (small parity workloads).
+__global__ __launch_bounds__(256) void router_gemm_f32(const float* __restrict__ x,
+                                                       const float* __restrict__ w,
+                                                       const float* __restrict__ bias,
+                                                       float* __restrict__ logits, int T, int d,
+                                                       int E) {
+  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (id >= (int64_t)T * E) return;
+  const int t = (int)(id / E), e = (int)(id % E);
+  const float* xr = x + (int64_t)t * d;
+  const float* wr = w + (int64_t)e * d;
+  float acc = 0.f;
+  for (int i = 0; i < d; ++i) acc = fmaf(xr[i], wr[i], acc);
+  logits[id] = acc + (bias ? bias[e] : 0.f);
+}
+
+template <class Cfg>
+static hipError_t launch_router_bf16(const Ctx& c, const moe_shape_t& s, const bf16_t* x,
+                                     const bf16_t* w, const float* bias, float* logits) {
+  const int mt = (s.T + Cfg::BM - 1) / Cfg::BM, nt = (s.E + Cfg::BN - 1) / Cfg::BN;
+  const int items = mt * nt;
+  int grid = ((items + 7) / 8) * 8;
+  TimedLaunch tl(MOE_K_ROUTER_GEMM, c.stream);
+  hipLaunchKernelGGL(router_gemm_bf16<Cfg>, dim3(grid), dim3(256), Cfg::SMEM_BYTES, c.stream, x,
+                     w, bias, logits, s.T, s.d, s.E, mt, nt);
+  return hipGetLastError();
+}
+
+hipError_t launch_router(const Ctx& c, const moe_shape_t& s, const void* x, const void* w,
+                         const float* bias, float* logits) {
+  if (s.dtype == MOE_BF16) {
+    const int tiles128 = ((s.T + 127) / 128) * ((s.E + 127) / 128);
+    if (tiles128 >= 2 * c.num_cus)
+      return launch_router_bf16<TileCfg<128, 128>>(c, s, (const bf16_t*)x, (const bf16_t*)w, bias, logits);
+    return launch_router_bf16<TileCfg<64, 128>>(c, s, (const bf16_t*)x, (const bf16_t*)w, bias, logits);
+  }
+  const int64_t n = (int64_t)s.T * s.E;
+  TimedLaunch tl(MOE_K_ROUTER_GEMM, c.stream);
+  hipLaunchKernelGGL(router_gemm_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, c.stream,
+                     (const float*)x, (const float*)w, bias, logits, s.T, s.d, s.E);
+  return hipGetLastError();
+}
+
+// --------------------------------------------------------- top-k + gates ---
+
+// Order-preserving map of an fp32 value to uint32 (larger value -> larger
+// code); -0.0 is mapped like +0.0 so the two compare equal.
+__device__ __forceinline__ uint32_t ordered_bits(float v) {
+  uint32_t u = __float_as_uint(v);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float from_ordered(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, m, kWave);
+    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, kWave);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// One wave per token. Lane l holds the logits of experts l, l+64, ... as
+// 64-bit keys (ordered logit bits << 32 | ~expert) so that the largest key is
+// the largest logit and, among equal logits, the lowest expert id. k rounds of
+// "lane maximum, then wave maximum" pick the experts in order; lane j keeps
+// the j-th pick. Gates: exp(l_j - l_0) / sum over the picks. With prob_part,
+// the wave also accumulates the full softmax of its tokens per expert; the
+// block's four waves are summed in a fixed order into prob_part[block, E].
+template <int EPL>
+__global__ __launch_bounds__(256) void topk_softmax(const float* __restrict__ logits, int T, int E,
+                                                    int k, int32_t* __restrict__ idx_out,
+                                                    float* __restrict__ gate_out,
+                                                    float* __restrict__ prob_part) {
+  __shared__ float red[4][EPL * 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float psum[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) psum[i] = 0.f;
+  constexpr int kTokPerWave = kTopkTokPerBlock / 4;
+  for (int q = 0; q < kTokPerWave; ++q) {
+    const int t = blockIdx.x * kTopkTokPerBlock + wave * kTokPerWave + q;
+    if (t >= T) break;
+    const float* row = logits + (int64_t)t * E;
+    uint64_t key[EPL];
+    float val[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = lane + 64 * i;
+      if (e < E) {
+        val[i] = row[e];
+        key[i] = ((uint64_t)ordered_bits(val[i]) << 32) | (uint32_t)(0xffffffffu - (uint32_t)e);
+      } else {
+        val[i] = 0.f;
+        key[i] = 0;
+      }
+    }
+    int my_idx = 0;
+    float my_logit = 0.f, top = 0.f;
+    for (int j = 0; j < k; ++j) {
+      uint64_t best = 0;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) best = key[i] > best ? key[i] : best;
+      const uint64_t win = wave_max_u64(best);
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (key[i] == win) key[i] = 0;  // keys are unique: only the owner matches
+      const float v = from_ordered((uint32_t)(win >> 32));
+      if (j == 0) top = v;
+      if (lane == j) {
+        my_idx = (int)(0xffffffffu - (uint32_t)win);
+        my_logit = v;
+      }
+    }
+    const float ex = lane < k ? expf(my_logit - top) : 0.f;
+    const float den = wave_sum(ex);
+    if (lane < k) {
+      idx_out[(int64_t)t * k + lane] = my_idx;
+      gate_out[(int64_t)t * k + lane] = ex / den;
+    }
+    if (prob_part) {
+      float z[EPL], zs = 0.f;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        z[i] = (lane + 64 * i < E) ? expf(val[i] - top) : 0.f;
+        zs += z[i];
+      }
+      const float Z = wave_sum(zs);
+      const float inv = 1.0f / Z;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) psum[i] += z[i] * inv;
+    }
+  }
+  if (!prob_part) return;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) red[wave][lane + 64 * i] = psum[i];
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256)
+    prob_part[(int64_t)blockIdx.x * E + e] = ((red[0][e] + red[1][e]) + red[2][e]) + red[3][e];
+}
+
+// prob_sum[e] = sum over blocks of prob_part[b, e], blocks in order.
+__global__ __launch_bounds__(256) void prob_reduce(const float* __restrict__ part, int nblk, int E,
+                                                   float* __restrict__ out) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= E) return;
+  float acc = 0.f;
+  for (int b = 0; b < nblk; ++b) acc += part[(int64_t)b * E + e];
+  out[e] = acc;
+}
+
+hipError_t launch_topk(const Ctx& c, const moe_shape_t& s, const float* logits, int32_t* idx,
+                       float* gate, float* prob_part, float* prob_sum) {
+  const int nblk = (s.T + kTopkTokPerBlock - 1) / kTopkTokPerBlock;
+  const int epl = (s.E + 63) / 64;
+  float* part = prob_sum ? prob_part : nullptr;
+  if (nblk > 0) {
+    TimedLaunch tl(MOE_K_TOPK, c.stream);
+#define MOE_TOPK(N) \
+  hipLaunchKernelGGL(topk_softmax<N>, dim3(nblk), dim3(256), 0, c.stream, logits, s.T, s.E, s.k, idx, gate, part)
+    if (epl <= 1) MOE_TOPK(1);
+    else if (epl <= 2) MOE_TOPK(2);
+    else if (epl <= 4) MOE_TOPK(4);
+    else if (epl <= 8) MOE_TOPK(8);
+    else MOE_TOPK(16);
+#undef MOE_TOPK
+  }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || !prob_sum) return err;
+  TimedLaunch tl(MOE_K_PROB_REDUCE, c.stream);
+  hipLaunchKernelGGL(prob_reduce, dim3((s.E + 255) / 256), dim3(256), 0, c.stream, part, nblk, s.E,
+                     prob_sum);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------ load-balance loss ---
+
+// out[1] = E * sum_e (counts[e] / (T k)) (prob_sum[e] / T); out[0] = coef out[1].
+// One block; fixed-shape tree reduction in double.
+__global__ __launch_bounds__(1024) void aux_loss_kernel(const int32_t* __restrict__ counts,
+                                                        const float* __restrict__ prob_sum, int T,
+                                                        int k, int E, float coef,
+                                                        float* __restrict__ out) {
+  __shared__ double red[1024];
+  const int e = threadIdx.x;
+  double v = 0.0;
+  if (e < E && T > 0) v = ((double)counts[e] / ((double)T * k)) * ((double)prob_sum[e] / T);
+  red[e] = v;
+  __syncthreads();
+  for (int h = 512; h >= 1; h >>= 1) {
+    if (e < h) red[e] += red[e + h];
+    __syncthreads();
+  }
+  if (e == 0) {
+    const double raw = (double)E * red[0];
+    out[1] = (float)raw;
+    out[0] = (float)(coef * raw);
+  }
+}
+
+hipError_t launch_aux(const Ctx& c, const moe_shape_t& s, const int32_t* counts,
+                      const float* prob_sum, float coef, float* out) {
+  TimedLaunch tl(MOE_K_AUX, c.stream);
+  hipLaunchKernelGGL(aux_loss_kernel, dim3(1), dim3(1024), 0, c.stream, counts, prob_sum, s.T, s.k,
+                     s.E, coef, out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

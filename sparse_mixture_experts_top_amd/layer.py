@@ -1,0 +1,83 @@
+"""Buffers and the four-call forward of the MoE layer on top of the binding.
+
+This module only allocates device tensors (through torch) and calls the C
+entry points in order: route -> dispatch -> expert GEMM -> combine. It holds
+no arithmetic of its own.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import binding as B
+from .workloads import Workload
+
+
+def shape_of(w: Workload) -> B.MoeShape:
+    return B.make_shape(w.T, w.d, w.E, w.k, w.f, w.e_lo, w.local_hi, w.capacity,
+                        B.MOE_BF16 if w.dtype == "bf16" else B.MOE_F32)
+
+
+@dataclass
+class Buffers:
+    shape: B.MoeShape
+    topk_idx: torch.Tensor
+    topk_gate: torch.Tensor
+    logits: Optional[torch.Tensor]
+    prob_sum: Optional[torch.Tensor]
+    counts: torch.Tensor
+    offsets: torch.Tensor
+    slot: torch.Tensor
+    row_src: torch.Tensor
+    row_gate: torch.Tensor
+    x_perm: torch.Tensor
+    y_perm: torch.Tensor
+    act_save: Optional[torch.Tensor]
+    y: torch.Tensor
+    dropped: torch.Tensor
+    aux: torch.Tensor
+    ws: torch.Tensor
+
+
+def alloc(shape: B.MoeShape, lora_r: int = 0, logits: bool = False, prob: bool = False,
+          act_save: bool = False, device: str = "cuda") -> Buffers:
+    T, d, E, k, f = shape.T, shape.d, shape.E, shape.k, shape.f
+    L = shape.e_hi - shape.e_lo
+    rmax = B.moe_max_rows(shape)
+    if rmax < 0:
+        raise ValueError("invalid shape")
+    dt = torch.bfloat16 if shape.dtype == B.MOE_BF16 else torch.float32
+    kw = {"device": device}
+    ws_bytes = B.moe_workspace_bytes(shape, lora_r)
+    return Buffers(
+        shape=shape,
+        topk_idx=torch.empty((T, k), dtype=torch.int32, **kw),
+        topk_gate=torch.empty((T, k), dtype=torch.float32, **kw),
+        logits=torch.empty((T, E), dtype=torch.float32, **kw) if logits else None,
+        prob_sum=torch.empty((E,), dtype=torch.float32, **kw) if prob else None,
+        counts=torch.empty((E,), dtype=torch.int32, **kw),
+        offsets=torch.empty((L + 1,), dtype=torch.int32, **kw),
+        slot=torch.empty((T, k), dtype=torch.int32, **kw),
+        row_src=torch.empty((max(rmax, 1),), dtype=torch.int32, **kw),
+        row_gate=torch.empty((max(rmax, 1),), dtype=torch.float32, **kw),
+        x_perm=torch.empty((max(rmax, 1), d), dtype=dt, **kw),
+        y_perm=torch.empty((max(rmax, 1), d), dtype=dt, **kw),
+        act_save=torch.empty((max(rmax, 1), 2 * f), dtype=dt, **kw) if act_save else None,
+        y=torch.empty((T, d), dtype=dt, **kw),
+        dropped=torch.zeros((1,), dtype=torch.int32, **kw),
+        aux=torch.zeros((2,), dtype=torch.float32, **kw),
+        ws=torch.empty((max(ws_bytes, 256),), dtype=torch.uint8, **kw),
+    )
+
+
+def forward(b: Buffers, x, w_router, bias, w_gate, w_up, w_down, lora=None, stream=None) -> None:
+    """route -> dispatch -> expert GEMM -> combine; results stay in ``b``."""
+    s = b.shape
+    B.moe_route(s, x, w_router, bias, b.topk_idx, b.topk_gate, b.logits, b.prob_sum, b.ws, stream)
+    B.moe_dispatch(s, b.topk_idx, b.topk_gate, x, b.counts, b.offsets, b.slot, b.row_src,
+                   b.row_gate, b.x_perm, b.dropped, b.ws, stream)
+    B.moe_expert_gemm(s, b.x_perm, b.offsets, w_gate, w_up, w_down, lora, b.act_save, b.y_perm,
+                      b.ws, stream)
+    B.moe_combine(s, b.y_perm, b.slot, b.topk_gate, b.y, stream)

@@ -1,0 +1,149 @@
+"""Helpers for the GPU parity tests: run the layer through the C ABI and
+compare each stage with the oracle fed the GPU's own upstream outputs."""
+from __future__ import annotations
+
+import sys
+from typing import Dict, Optional
+
+import numpy as np
+import torch
+
+import oracle
+from sparse_mixture_experts_top_amd import binding as B
+from sparse_mixture_experts_top_amd import layer, workloads
+from sparse_mixture_experts_top_amd.workloads import Workload, to_f64
+
+# floating-point tolerances: bf16 storage with fp32 accumulation, or fp32
+TOL = {"bf16": (2e-2, 1e-2), "f32": (1e-5, 1e-5)}
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def upload(inp: Dict[str, torch.Tensor]) -> Dict[str, torch.Tensor]:
+    return {k: v.to("cuda").contiguous() for k, v in inp.items()}
+
+
+def lora_of(w: Workload, dev: Dict[str, torch.Tensor]):
+    if w.lora_r <= 0:
+        return None
+    return B.make_lora(w.lora_r, w.lora_alpha, dev["a_up"], dev["b_up"], dev["a_down"], dev["b_down"])
+
+
+def run_forward(w: Workload, dev: Dict[str, torch.Tensor], logits=True, prob=False,
+                act_save=False) -> layer.Buffers:
+    shape = layer.shape_of(w)
+    buf = layer.alloc(shape, lora_r=w.lora_r, logits=logits, prob=prob, act_save=act_save)
+    layer.forward(buf, dev["x"], dev["w_router"], dev.get("bias"), dev["w_gate"], dev["w_up"],
+                  dev["w_down"], lora_of(w, dev))
+    torch.cuda.synchronize()
+    return buf
+
+
+def host(t: Optional[torch.Tensor]) -> Optional[np.ndarray]:
+    if t is None:
+        return None
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        t = t.to(torch.float64)
+    return t.numpy()
+
+
+def assert_close(got, ref, dtype: str, what: str, stored_bf16: bool = False) -> dict:
+    """max-abs <= atol and relative Frobenius <= rtol (TOL[dtype]).
+
+    stored_bf16: ``got`` is an intermediate kept in bf16 storage (the expert
+    rows y_perm). Its representation alone is off by up to half a bf16 ulp,
+    i.e. 2^-8 |v|, which exceeds 2e-2 once |v| > 5; the element-wise bound is
+    then atol + 2^-8 |ref|. The layer output y is always held to plain atol.
+    """
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    atol, rtol = TOL[dtype]
+    err = np.abs(got - ref)
+    if stored_bf16 and dtype == "bf16":
+        err = np.maximum(err - 2.0 ** -8 * np.abs(ref), 0.0)
+    max_abs = float(err.max()) if err.size else 0.0
+    denom = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(got - ref) / denom) if denom > 0 else float(np.linalg.norm(got - ref))
+    info = {"what": what, "max_abs": max_abs, "rel_frob": rel,
+            "ref_inf": float(np.abs(ref).max()) if ref.size else 0.0}
+    say(f"  {what}: max_abs={max_abs:.3e} rel_frob={rel:.3e} |ref|inf={info['ref_inf']:.3e}")
+    assert max_abs <= atol, f"{what}: max-abs {max_abs} > {atol}"
+    assert rel <= rtol, f"{what}: rel-Frobenius {rel} > {rtol}"
+    return info
+
+
+def logit_bound(x64: np.ndarray, w64: np.ndarray, bias=None) -> np.ndarray:
+    """Per-element bound of an fp32-accumulated dot product of exact products
+    plus the bias: gamma_d * sum_i |x_i| |w_i| with gamma_d = d u / (1 - d u),
+    u = 2^-24, plus one rounding of the result."""
+    d = x64.shape[1]
+    u = 2.0 ** -24
+    gamma = (d + 1) * u / (1 - (d + 1) * u)
+    ref = x64 @ w64.T + (0.0 if bias is None else bias[None, :])
+    return gamma * (np.abs(x64) @ np.abs(w64).T) + 2 * u * np.abs(ref) + 1e-30
+
+
+def check_route(w: Workload, inp, buf: layer.Buffers, sample_tokens: Optional[np.ndarray] = None):
+    """Logits within the fp32 bound on sampled tokens; ids bit-exact and gates
+    within 1e-5 against the oracle applied to the GPU's own logits."""
+    lg = host(buf.logits)
+    x64, wr64 = to_f64(inp["x"]), to_f64(inp["w_router"])
+    bias = to_f64(inp.get("bias"))
+    ts = np.arange(w.T) if sample_tokens is None else sample_tokens
+    ref = oracle.router_logits(x64[ts], wr64, bias)
+    bound = logit_bound(x64[ts], wr64, bias)
+    diff = np.abs(lg[ts] - ref)
+    say(f"  logits: max |d|={diff.max():.3e} max bound={bound.max():.3e} "
+        f"rel_frob={np.linalg.norm(lg[ts] - ref) / np.linalg.norm(ref):.3e}")
+    assert np.all(diff <= bound), "logit outside the fp32 accumulation bound"
+    assert np.linalg.norm(lg[ts] - ref) / np.linalg.norm(ref) <= 1e-5
+    idx_ref = oracle.topk_experts(lg, w.k)
+    idx = host(buf.topk_idx)
+    bad = int((idx != idx_ref).sum())
+    assert bad == 0, f"{bad} top-k ids differ from the oracle on the GPU logits"
+    g_ref = oracle.topk_gates(lg, idx)
+    g = host(buf.topk_gate)
+    say(f"  gates: max |d|={np.abs(g - g_ref).max():.3e}")
+    assert np.abs(g - g_ref).max() <= 1e-5
+    return lg, idx, g
+
+
+def check_dispatch(w: Workload, dev, buf: layer.Buffers, idx, gate):
+    """counts, offsets, slot, row_src bit-exact; row_gate and x_perm bitwise."""
+    ref = oracle.dispatch(idx, gate.astype(np.float32), w.E, w.e_lo, w.local_hi, w.capacity)
+    counts, offsets, slot = host(buf.counts), host(buf.offsets), host(buf.slot)
+    assert (counts == ref["counts"]).all(), "counts differ"
+    assert (offsets == ref["offsets"]).all(), "offsets differ"
+    assert (slot == ref["slot"]).all(), f"slot differs at {int((slot != ref['slot']).sum())} places"
+    R = int(offsets[-1])
+    row_src = host(buf.row_src)[:R]
+    assert (row_src == ref["row_src"]).all(), "row_src differs"
+    row_gate = buf.row_gate[:R].cpu().numpy()
+    assert (row_gate == ref["row_gate"].astype(np.float32)).all(), "row_gate differs"
+    if w.capacity > 0:
+        assert int(buf.dropped.item()) == ref["dropped"]
+    xp = buf.x_perm[:R]
+    src = buf.row_src[:R].long()
+    assert torch.equal(xp, dev["x"][src]), "x_perm is not x[row_src]"
+    say(f"  dispatch: R={R} dropped={ref['dropped']} bit-exact")
+    return ref, R
+
+
+def expert_ref_rows(w: Workload, inp, buf: layer.Buffers, rows: np.ndarray, lora=None):
+    """Oracle expert output for the given dispatched rows, from the GPU x_perm."""
+    offsets = host(buf.offsets)
+    xp = host(buf.x_perm[torch.as_tensor(rows, device="cuda").long()]) if len(rows) else np.zeros((0, w.d))
+    out = np.zeros((len(rows), w.d))
+    les = np.searchsorted(offsets, rows, side="right") - 1
+    for le in np.unique(les):
+        m = les == le
+        lo = None
+        if lora is not None:
+            lo = {"scale": lora["scale"], **{n: to_f64(inp[n][le]) for n in ("a_up", "b_up", "a_down", "b_down")}}
+        out[m] = oracle.expert_ffn(xp[m], to_f64(inp["w_gate"][le]), to_f64(inp["w_up"][le]),
+                                   to_f64(inp["w_down"][le]), lo)
+    return out

@@ -1,0 +1,86 @@
+"""The C ABI on the CPU: the library loads, exports what include/moe.h declares,
+and rejects bad arguments on the host before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_mixture_experts_top_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    lib = B.lib()
+    names = declared_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(B.EXPORTED) == names
+
+
+def shape(**kw):
+    base = dict(T=64, d=128, E=16, k=4, f=64, e_lo=0, e_hi=16, capacity=0, dtype=B.MOE_F32)
+    base.update(kw)
+    return B.MoeShape(*[base[n] for n, _ in B.MoeShape._fields_])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=0), B.MOE_ERR_INVALID_ARG), (dict(k=17), B.MOE_ERR_INVALID_ARG),
+    (dict(T=-1), B.MOE_ERR_INVALID_ARG), (dict(e_lo=5, e_hi=5), B.MOE_ERR_INVALID_ARG),
+    (dict(e_hi=17), B.MOE_ERR_INVALID_ARG), (dict(dtype=7), B.MOE_ERR_INVALID_ARG),
+    (dict(d=0), B.MOE_ERR_INVALID_ARG),
+    (dict(E=1025, e_hi=1025), B.MOE_ERR_UNSUPPORTED), (dict(E=64, e_hi=64, k=33), B.MOE_ERR_UNSUPPORTED),
+    (dict(dtype=B.MOE_BF16, d=96), B.MOE_ERR_UNSUPPORTED),
+    (dict(dtype=B.MOE_BF16, d=128, f=96), B.MOE_ERR_UNSUPPORTED),
+])
+def test_bad_shapes_are_rejected_on_the_host(kw, status):
+    lib = B.lib()
+    s = shape(**kw)
+    st = lib.moe_route(ctypes.byref(s), None, None, None, None, None, None, None, None, 0, None)
+    assert st == status
+    assert lib.moe_last_error()
+    assert lib.moe_workspace_bytes(ctypes.byref(s), 0) == 0
+    assert lib.moe_max_rows(ctypes.byref(s)) == -1
+
+
+def test_null_pointers_and_small_workspace_are_rejected():
+    lib = B.lib()
+    s = shape()
+    assert lib.moe_route(ctypes.byref(s), None, None, None, None, None, None, None, None, 0,
+                         None) == B.MOE_ERR_INVALID_ARG
+    assert b"x is NULL" in lib.moe_last_error()
+    fake = ctypes.c_void_p(0x100000)      # never dereferenced: validation fails first
+    assert lib.moe_route(ctypes.byref(s), fake, fake, None, fake, fake, None, None, fake, 16,
+                         None) == B.MOE_ERR_WORKSPACE
+    assert lib.moe_combine(ctypes.byref(s), fake, None, fake, fake, None) == B.MOE_ERR_INVALID_ARG
+    lo = B.MoeLora(16, 32.0, None, None, None, None)
+    assert lib.moe_expert_gemm(ctypes.byref(s), fake, fake, fake, fake, fake, ctypes.byref(lo),
+                               None, fake, fake, 1 << 30, None) == B.MOE_ERR_INVALID_ARG
+    lo = B.MoeLora(16, 32.0, fake, fake, fake, fake)
+    assert lib.moe_expert_gemm(ctypes.byref(s), fake, fake, fake, fake, fake, ctypes.byref(lo),
+                               None, fake, fake, 1 << 30, None) == B.MOE_ERR_UNSUPPORTED  # fp32 LoRA
+    assert lib.moe_timing_read(99, None, None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_max_rows_and_workspace_sizes():
+    full = B.make_shape(4096, 2048, 896, 16, 256)
+    assert B.moe_max_rows(full) == 4096 * 16
+    ep = B.make_shape(16384, 4096, 896, 16, 1024, 0, 14)
+    assert B.moe_max_rows(ep) == 16384 * 14
+    cap = B.make_shape(8192, 2048, 896, 16, 256, capacity=183)
+    assert B.moe_max_rows(cap) == min(8192 * 16, 896 * 183)
+    assert B.moe_max_rows(B.make_shape(8192, 2048, 896, 16, 256, capacity=100)) == 896 * 100
+    for s in (full, ep, cap):
+        ws0, ws16 = B.moe_workspace_bytes(s, 0), B.moe_workspace_bytes(s, 16)
+        assert 0 < ws0 < ws16
+        assert ws0 % 256 == 0
+    # the logits scratch alone is T*E fp32
+    assert B.moe_workspace_bytes(full, 0) > 4096 * 896 * 4
