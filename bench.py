@@ -1,0 +1,213 @@
+#!/usr/bin/env python3
+"""MoE-layer throughput on one MI355X.
+
+One step = route + dispatch + expert GEMM + combine over one batch of the
+full-router workload (T=4096 tokens, d=2048, E=896 experts, top-16, SwiGLU
+f=256, bf16, all experts on this GPU), inputs resident in HBM before timing.
+
+Prints ONE JSON line: tokens/s, ms per step, the roofline of the dominant
+kernel (the gate/up grouped GEMM, which streams 1.9 GB of expert weights per
+step) from HIP events recorded around it on its launch stream, and the CPU
+oracle timed on a bounded token sample of the same workload.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                  [--no-cpu-baseline] [--calibrate-copy]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/sec (route+dispatch+experts+combine); % bf16 MFMA/HBM peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
+PMC_FILE = os.path.join(ROOT, "profiles", "gate_up_full_router_pmc.txt")
+KERNEL_SOURCES = ["expert_gemm.hip", "mfma_tile.h", "common.h"]
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for n in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "sparse_mixture_experts_top_amd", "csrc", n), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per gate/up launch from the committed rocprofv3 counter runs,
+    or None when they are missing or the kernel source changed since."""
+    if not os.path.exists(PMC_FILE):
+        return None
+    vals = {}
+    with open(PMC_FILE) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_hash") != kernel_source_hash() or vals.get("workload") != workload:
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class LazyExperts:
+    """Per-expert float64 view of a bf16 CPU tensor, converted on access."""
+
+    def __init__(self, t):
+        self.t = t
+        self.shape = tuple(t.shape)
+
+    def __getitem__(self, i):
+        import torch
+        return self.t[i].to(torch.float64).numpy()
+
+
+def cpu_baseline(w, inp):
+    """The oracle, untouched, on the first S tokens of the same workload."""
+    import numpy as np
+    import torch
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    wr = inp["w_router"].to(torch.float64).numpy()
+    wg, wu, wd = LazyExperts(inp["w_gate"]), LazyExperts(inp["w_up"]), LazyExperts(inp["w_down"])
+    bias = inp["bias"].numpy() if "bias" in inp else None
+    S = min(64, w.T)          # about 15-20 s of float64 NumPy on 8-16 cores
+    x = inp["x"][:S].to(torch.float64).numpy()
+    t0 = time.perf_counter()
+    oracle.moe_layer(x, wr, wg, wu, wd, w.k, bias=bias, e_lo=w.e_lo, e_hi=w.local_hi,
+                     capacity=0)
+    spent, total_tok = time.perf_counter() - t0, S
+    log(f"[cpu_baseline] oracle on {S} tokens: {spent:.2f} s")
+    return {"value": total_tok / spent, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {total_tok} of {w.T} tokens of {w.name} (route over all {w.E} experts, "
+                      f"dispatch, SwiGLU experts, combine; float64 NumPy), {spent:.1f} s"}
+
+
+def calibrate_copy(nbytes: int = 1 << 30, reps: int = 5) -> None:
+    """A plain elementwise copy of known size, for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    n = nbytes // 4
+    a = torch.randn(n, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        torch.mul(a, 1.0, out=b)
+    torch.cuda.synchronize()
+    log(f"[calibrate] {reps} copies of {nbytes} bytes read + {nbytes} bytes written")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="full_router")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the expert-parallel all-to-all is design only). Run with --gpus 1.",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from sparse_mixture_experts_top_amd import binding as B
+    from sparse_mixture_experts_top_amd import layer
+    from sparse_mixture_experts_top_amd.workloads import WORKLOADS, generate
+
+    if args.calibrate_copy:
+        calibrate_copy()
+        return 0
+
+    w = WORKLOADS[args.workload]
+    if w.lora_r:
+        raise SystemExit("bench.py times the forward layer; pick a workload without LoRA")
+    log(f"[bench] generating {w.name}: T={w.T} d={w.d} E={w.E} k={w.k} f={w.f} L={w.L}")
+    t0 = time.time()
+    inp = generate(w, seed=0)
+    dev = {k: v.to("cuda") for k, v in inp.items()}
+    torch.cuda.synchronize()
+    log(f"[bench] inputs ready in {time.time() - t0:.1f} s")
+    shape = layer.shape_of(w)
+    buf = layer.alloc(shape)
+    args_fw = (dev["x"], dev["w_router"], dev.get("bias"), dev["w_gate"], dev["w_up"], dev["w_down"])
+
+    for _ in range(args.warmup):
+        layer.forward(buf, *args_fw)
+    torch.cuda.synchronize()
+
+    B.moe_timing_enable(True)
+    stream = torch.cuda.current_stream()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        layer.forward(buf, *args_fw)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    elapsed_ms = start.elapsed_time(stop)
+    kernels = {}
+    for name in B.KERNELS:
+        ms, n = B.moe_timing_read(name)
+        if n:
+            kernels[name] = {"avg_us": 1000.0 * ms / n, "launches": n}
+    B.moe_timing_enable(False)
+    log(f"[bench] {args.steps} steps in {elapsed_ms:.3f} ms")
+
+    ms_step = elapsed_ms / args.steps
+    tok_s = w.T / (ms_step / 1000.0)
+
+    # algorithmic bytes of one gate/up launch: the gate and up weights of every
+    # expert that received a row, the dispatched rows read once, H written once
+    counts = buf.offsets.diff().cpu().numpy()
+    R = int(buf.offsets[-1].item())
+    active = int((counts > 0).sum())
+    gu_bytes = 2 * active * w.f * w.d * 2 + R * w.d * 2 + R * w.f * 2
+    gu_us = kernels["gate_up"]["avg_us"]
+    achieved = gu_bytes / (gu_us * 1e-6) / 1e9
+    traffic = recorded_traffic(w.name)
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic, "kernel": "gate_up_bf16", "algorithmic_bytes": gu_bytes,
+            "avg_us": round(gu_us, 2)}
+    # layer-level figures for context
+    flops = 2 * w.T * w.d * w.E + 6 * R * w.d * w.f
+    out = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) tokens, N(0,1/fan_in) weights)",
+        "config": {"workload": w.name, "T": w.T, "d": w.d, "E": w.E, "k": w.k, "f": w.f,
+                   "local_experts": w.L, "capacity": w.capacity, "rows": R,
+                   "active_experts": active},
+        "roofline": roof,
+        "layer_tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "kernels_us": {k: round(v["avg_us"], 2) for k, v in kernels.items()},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inp)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -85,10 +85,32 @@ __device__ __forceinline__ void mfma_step(const bf16_t* As, const bf16_t* Bs, Ac
   }
 }
 
+// 16 bytes as a native vector (HIP's uint4 is a struct, which keeps arrays of
+// it from being promoted to registers).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Global -> register staging of one K step (16-byte loads).
+template <int N>
+__device__ __forceinline__ void gload_rows(u32x4 (&r)[N], const bf16_t* const (&rows)[N], int k0) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) r[i] = *reinterpret_cast<const u32x4*>(rows[i] + k0);
+}
+
+// Register -> LDS store of one K step; `lds` is the buffer base, rows of the
+// tile are ROWS_PER_PASS apart for consecutive loads.
+template <class Cfg, int N>
+__device__ __forceinline__ void sstore_rows(bf16_t* lds, const u32x4 (&r)[N], int lrow, int lcol) {
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    *reinterpret_cast<u32x4*>(&lds[(lrow + i * Cfg::ROWS_PER_PASS) * Cfg::LDS_STRIDE + lcol]) = r[i];
+}
+
 // Main loop with both operands K-contiguous ("NT"): a_rows[i] / b_rows[i] are
 // the row starts (already offset by this thread's 8-element column chunk) of
 // the rows this thread loads; rows past the valid range must point at some
 // valid row (their results are discarded by the caller). K % 64 == 0.
+// LDS holds [A0 | A1 | B0 | B1]; buffers are addressed by integer offsets so
+// every access stays an LDS (ds_*) instruction.
 template <class Cfg>
 __device__ __forceinline__ void mainloop_nt(const bf16_t* const (&a_rows)[Cfg::A_LOADS],
                                             const bf16_t* const (&b_rows)[Cfg::B_LOADS], int K,
@@ -98,36 +120,63 @@ __device__ __forceinline__ void mainloop_nt(const bf16_t* const (&a_rows)[Cfg::A
   const int wm = wave >> 1, wn = wave & 1;
   const int lrow = tid / Cfg::CHUNKS_PER_ROW;
   const int lcol = (tid % Cfg::CHUNKS_PER_ROW) * 8;
-  bf16_t* As[2] = {smem, smem + Cfg::A_ELEMS};
-  bf16_t* Bs[2] = {smem + 2 * Cfg::A_ELEMS, smem + 2 * Cfg::A_ELEMS + Cfg::B_ELEMS};
-  uint4 ra[Cfg::A_LOADS], rb[Cfg::B_LOADS];
+  bf16_t* const A0 = smem;
+  bf16_t* const B0 = smem + 2 * Cfg::A_ELEMS;
+  u32x4 ra[Cfg::A_LOADS], rb[Cfg::B_LOADS];
   const int nk = K / Cfg::BK;
 
-  auto gload = [&](int kt) {
-    const int k0 = kt * Cfg::BK;
-#pragma unroll
-    for (int i = 0; i < Cfg::A_LOADS; ++i) ra[i] = *reinterpret_cast<const uint4*>(a_rows[i] + k0);
-#pragma unroll
-    for (int i = 0; i < Cfg::B_LOADS; ++i) rb[i] = *reinterpret_cast<const uint4*>(b_rows[i] + k0);
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < Cfg::A_LOADS; ++i)
-      *reinterpret_cast<uint4*>(&As[buf][(lrow + i * Cfg::ROWS_PER_PASS) * Cfg::LDS_STRIDE + lcol]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < Cfg::B_LOADS; ++i)
-      *reinterpret_cast<uint4*>(&Bs[buf][(lrow + i * Cfg::ROWS_PER_PASS) * Cfg::LDS_STRIDE + lcol]) = rb[i];
-  };
-
-  gload(0);
-  sstore(0);
+  gload_rows(ra, a_rows, 0);
+  gload_rows(rb, b_rows, 0);
+  sstore_rows<Cfg>(A0, ra, lrow, lcol);
+  sstore_rows<Cfg>(B0, rb, lrow, lcol);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    mfma_step<Cfg>(As[cur], Bs[cur], acc, wm, wn, lane);
-    if (kt + 1 < nk) sstore(cur ^ 1);
+    const bool more = kt + 1 < nk;
+    if (more) {
+      gload_rows(ra, a_rows, (kt + 1) * Cfg::BK);
+      gload_rows(rb, b_rows, (kt + 1) * Cfg::BK);
+    }
+    mfma_step<Cfg>(A0 + cur * Cfg::A_ELEMS, B0 + cur * Cfg::B_ELEMS, acc, wm, wn, lane);
+    if (more) {
+      sstore_rows<Cfg>(A0 + (cur ^ 1) * Cfg::A_ELEMS, ra, lrow, lcol);
+      sstore_rows<Cfg>(B0 + (cur ^ 1) * Cfg::B_ELEMS, rb, lrow, lcol);
+    }
     __syncthreads();
+  }
+}
+
+// B stored [K][N] ("NN"): load 8 consecutive n of one k per 16-byte chunk;
+// columns at or past n_valid are clamped to the last valid column.
+template <class Cfg>
+__device__ __forceinline__ void gload_nn(u32x4 (&r)[Cfg::NN_B_LOADS], const bf16_t* b_base,
+                                         int64_t ldb, int k0, int nk_row, int nn_col, int n_valid,
+                                         bool chunk_ok) {
+#pragma unroll
+  for (int i = 0; i < Cfg::NN_B_LOADS; ++i) {
+    const bf16_t* src = b_base + (int64_t)(k0 + nk_row + i * Cfg::NN_K_PER_PASS) * ldb;
+    if (chunk_ok) {
+      r[i] = *reinterpret_cast<const u32x4*>(src + nn_col);
+    } else {
+      uint32_t t[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) t[u] = src[min(nn_col + u, n_valid - 1)];
+      r[i] = u32x4{t[0] | t[1] << 16, t[2] | t[3] << 16, t[4] | t[5] << 16, t[6] | t[7] << 16};
+    }
+  }
+}
+
+// Transposing store: element (k, n) of the chunk goes to LDS row n, column k.
+template <class Cfg>
+__device__ __forceinline__ void sstore_nn(bf16_t* lds, const u32x4 (&r)[Cfg::NN_B_LOADS],
+                                          int nk_row, int nn_col) {
+#pragma unroll
+  for (int i = 0; i < Cfg::NN_B_LOADS; ++i) {
+    const int kr = nk_row + i * Cfg::NN_K_PER_PASS;
+    const uint32_t w[4] = {r[i][0], r[i][1], r[i][2], r[i][3]};
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      lds[(nn_col + u) * Cfg::LDS_STRIDE + kr] = static_cast<bf16_t>(w[u >> 1] >> ((u & 1) * 16));
   }
 }
 
@@ -143,55 +192,31 @@ __device__ __forceinline__ void mainloop_nn(const bf16_t* const (&a_rows)[Cfg::A
   const int wm = wave >> 1, wn = wave & 1;
   const int lrow = tid / Cfg::CHUNKS_PER_ROW;
   const int lcol = (tid % Cfg::CHUNKS_PER_ROW) * 8;
-  const int nk_row = tid / Cfg::NN_CHUNKS_PER_K;           // k row within a pass
-  const int nn_col = (tid % Cfg::NN_CHUNKS_PER_K) * 8;     // first n of the chunk
-  bf16_t* As[2] = {smem, smem + Cfg::A_ELEMS};
-  bf16_t* Bs[2] = {smem + 2 * Cfg::A_ELEMS, smem + 2 * Cfg::A_ELEMS + Cfg::B_ELEMS};
-  uint4 ra[Cfg::A_LOADS], rb[Cfg::NN_B_LOADS];
-  const int nk = K / Cfg::BK;
-  // full 8-wide chunks only when the chunk is entirely valid; else per element
+  const int nk_row = tid / Cfg::NN_CHUNKS_PER_K;
+  const int nn_col = (tid % Cfg::NN_CHUNKS_PER_K) * 8;
   const bool chunk_ok = nn_col + 8 <= n_valid;
+  bf16_t* const A0 = smem;
+  bf16_t* const B0 = smem + 2 * Cfg::A_ELEMS;
+  u32x4 ra[Cfg::A_LOADS], rb[Cfg::NN_B_LOADS];
+  const int nk = K / Cfg::BK;
 
-  auto gload = [&](int kt) {
-    const int k0 = kt * Cfg::BK;
-#pragma unroll
-    for (int i = 0; i < Cfg::A_LOADS; ++i) ra[i] = *reinterpret_cast<const uint4*>(a_rows[i] + k0);
-#pragma unroll
-    for (int i = 0; i < Cfg::NN_B_LOADS; ++i) {
-      const bf16_t* src = b_base + (int64_t)(k0 + nk_row + i * Cfg::NN_K_PER_PASS) * ldb;
-      if (chunk_ok) {
-        rb[i] = *reinterpret_cast<const uint4*>(src + nn_col);
-      } else {
-        uint16_t t[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) t[u] = src[min(nn_col + u, n_valid - 1)];
-        rb[i] = make_uint4(t[0] | (uint32_t)t[1] << 16, t[2] | (uint32_t)t[3] << 16,
-                           t[4] | (uint32_t)t[5] << 16, t[6] | (uint32_t)t[7] << 16);
-      }
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < Cfg::A_LOADS; ++i)
-      *reinterpret_cast<uint4*>(&As[buf][(lrow + i * Cfg::ROWS_PER_PASS) * Cfg::LDS_STRIDE + lcol]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < Cfg::NN_B_LOADS; ++i) {
-      const int kr = nk_row + i * Cfg::NN_K_PER_PASS;
-      const uint32_t w[4] = {rb[i].x, rb[i].y, rb[i].z, rb[i].w};
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        Bs[buf][(nn_col + u) * Cfg::LDS_STRIDE + kr] = static_cast<bf16_t>(w[u >> 1] >> ((u & 1) * 16));
-    }
-  };
-
-  gload(0);
-  sstore(0);
+  gload_rows(ra, a_rows, 0);
+  gload_nn<Cfg>(rb, b_base, ldb, 0, nk_row, nn_col, n_valid, chunk_ok);
+  sstore_rows<Cfg>(A0, ra, lrow, lcol);
+  sstore_nn<Cfg>(B0, rb, nk_row, nn_col);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    mfma_step<Cfg>(As[cur], Bs[cur], acc, wm, wn, lane);
-    if (kt + 1 < nk) sstore(cur ^ 1);
+    const bool more = kt + 1 < nk;
+    if (more) {
+      gload_rows(ra, a_rows, (kt + 1) * Cfg::BK);
+      gload_nn<Cfg>(rb, b_base, ldb, (kt + 1) * Cfg::BK, nk_row, nn_col, n_valid, chunk_ok);
+    }
+    mfma_step<Cfg>(A0 + cur * Cfg::A_ELEMS, B0 + cur * Cfg::B_ELEMS, acc, wm, wn, lane);
+    if (more) {
+      sstore_rows<Cfg>(A0 + (cur ^ 1) * Cfg::A_ELEMS, ra, lrow, lcol);
+      sstore_nn<Cfg>(B0 + (cur ^ 1) * Cfg::B_ELEMS, rb, nk_row, nn_col);
+    }
     __syncthreads();
   }
 }
