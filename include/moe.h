@@ -40,7 +40,8 @@
  * - Device preconditions (not checked): inputs are finite; topk_idx entries
  *   are in [0, E). Results are deterministic: the same inputs give bitwise the
  *   same outputs on every call.
- * - T == 0 is a valid empty batch: every call returns MOE_OK and does nothing.
+ * - T == 0 is a valid empty batch: buffers sized by T may be NULL; counts,
+ *   offsets, prob_sum and the LoRA gradients are still written (as zeros).
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -148,7 +149,9 @@ moe_status_t moe_route(const moe_shape_t* shape, const void* x, const void* w_ro
  *                             expert is not local or it was dropped
  *   row_src   [Rmax] int32    OUT: token of each row
  *   row_gate  [Rmax] f32      OUT: gate of each row
- *   x_perm    [Rmax, d]       OUT: x_perm[p] = x[row_src[p]] (bitwise copy)
+ *   x_perm    [Rmax, d]|NULL  OUT (optional): x_perm[p] = x[row_src[p]]
+ *                             (bitwise copy); NULL skips the copy, x may
+ *                             then be NULL too
  *   dropped   [1] int32|NULL  OUT (optional): local assignments dropped by
  *                             the capacity rule
  * Rows are grouped by local expert ascending and, within an expert, by token
@@ -164,8 +167,11 @@ moe_status_t moe_dispatch(const moe_shape_t* shape, const int32_t* topk_idx,
  * expert network). For the rows of local expert le:
  *   G = X w_gate[le]^T, U = X w_up[le]^T (+ LoRA), H = silu(G) * U,
  *   O = H w_down[le]^T (+ LoRA),  silu(a) = a / (1 + exp(-a)).
- *   x_perm   [Rmax, d]        rows from moe_dispatch
- *   offsets  [L+1] int32      from moe_dispatch
+ *   x        input rows: with row_src, the tokens [T, d] and row p reads
+ *            x[row_src[p]] (the dispatch gather happens inside the GEMM's
+ *            loads); with row_src == NULL, the permuted rows x_perm [Rmax, d]
+ *   row_src  [Rmax] int32 | NULL   from moe_dispatch
+ *   offsets  [L+1] int32           from moe_dispatch
  *   w_gate   [L, f, d]        w_up [L, f, d]        w_down [L, d, f]
  *   lora     [host] | NULL    adapters (bf16 only)
  *   act_save [Rmax, 2f]|NULL  OUT (optional): per row G (columns 0..f-1) and
@@ -174,7 +180,7 @@ moe_status_t moe_dispatch(const moe_shape_t* shape, const int32_t* topk_idx,
  *   y_perm   [Rmax, d]        OUT: O per row (not gate-scaled)
  * Accumulation is fp32; in bf16 mode H is rounded to bf16 before the down
  * projection and O is stored as bf16. */
-moe_status_t moe_expert_gemm(const moe_shape_t* shape, const void* x_perm,
+moe_status_t moe_expert_gemm(const moe_shape_t* shape, const void* x, const int32_t* row_src,
                              const int32_t* offsets, const void* w_gate, const void* w_up,
                              const void* w_down, const moe_lora_t* lora, void* act_save,
                              void* y_perm, void* ws, size_t ws_bytes, moe_stream_t stream);
@@ -210,7 +216,9 @@ moe_status_t moe_aux_loss(const moe_shape_t* shape, const int32_t* counts,
  *   db_up   = s dU^T Z_u                 da_up   = s (dU B_up)^T X
  *   dy          [T, d]            upstream gradient of y
  *   offsets, row_src, row_gate    from moe_dispatch
- *   x_perm      [Rmax, d]         from moe_dispatch
+ *   x, x_src                      input rows as for moe_expert_gemm: the
+ *                                 tokens [T, d] with x_src = row_src, or
+ *                                 x_perm [Rmax, d] with x_src = NULL
  *   act_save    [Rmax, 2f]        from moe_expert_gemm (G and H)
  *   w_down      [L, d, f]
  *   da_up [L,r,d], db_up [L,f,r], da_down [L,r,f], db_down [L,d,r]   OUT, f32
@@ -218,9 +226,9 @@ moe_status_t moe_aux_loss(const moe_shape_t* shape, const int32_t* counts,
  * rows). */
 moe_status_t moe_lora_bwd(const moe_shape_t* shape, const moe_lora_t* lora, const void* dy,
                           const int32_t* offsets, const int32_t* row_src, const float* row_gate,
-                          const void* x_perm, const void* act_save, const void* w_down,
-                          float* da_up, float* db_up, float* da_down, float* db_down, void* ws,
-                          size_t ws_bytes, moe_stream_t stream);
+                          const void* x, const int32_t* x_src, const void* act_save,
+                          const void* w_down, float* da_up, float* db_up, float* da_down,
+                          float* db_down, void* ws, size_t ws_bytes, moe_stream_t stream);
 
 /* ---- kernel timing (profiling aid) -------------------------------------
  * When enabled, the library records a pair of HIP events on the launch

@@ -64,10 +64,10 @@ def lib() -> ctypes.CDLL:
     L.moe_last_error.argtypes, L.moe_last_error.restype = [], ctypes.c_char_p
     L.moe_route.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_dispatch.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    L.moe_expert_gemm.argtypes = [shp, vp, vp, vp, vp, vp, lor, vp, vp, vp, sz, vp]
+    L.moe_expert_gemm.argtypes = [shp, vp, vp, vp, vp, vp, vp, lor, vp, vp, vp, sz, vp]
     L.moe_combine.argtypes = [shp, vp, vp, vp, vp, vp]
     L.moe_aux_loss.argtypes = [shp, vp, vp, f32, vp, vp]
-    L.moe_lora_bwd.argtypes = [shp, lor, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_lora_bwd.argtypes = [shp, lor, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_timing_enable.argtypes = [i32]
     L.moe_timing_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     for fn in ("moe_route", "moe_dispatch", "moe_expert_gemm", "moe_combine", "moe_aux_loss",
@@ -139,12 +139,13 @@ def moe_dispatch(shape, topk_idx, topk_gate, x, counts, offsets, slot, row_src, 
                               _dev(dropped, i32), _dev(ws, torch.uint8), ws.numel(), _stream(stream)))
 
 
-def moe_expert_gemm(shape, x_perm, offsets, w_gate, w_up, w_down, lora, act_save, y_perm, ws,
+def moe_expert_gemm(shape, x, row_src, offsets, w_gate, w_up, w_down, lora, act_save, y_perm, ws,
                     stream=None):
+    """x: tokens [T, d] read through row_src, or x_perm [Rmax, d] with row_src=None."""
     dt = _fdt(shape)
-    _check(lib().moe_expert_gemm(ctypes.byref(shape), _dev(x_perm, dt), _dev(offsets, torch.int32),
-                                 _dev(w_gate, dt), _dev(w_up, dt), _dev(w_down, dt),
-                                 ctypes.byref(lora) if lora is not None else None,
+    _check(lib().moe_expert_gemm(ctypes.byref(shape), _dev(x, dt), _dev(row_src, torch.int32),
+                                 _dev(offsets, torch.int32), _dev(w_gate, dt), _dev(w_up, dt),
+                                 _dev(w_down, dt), ctypes.byref(lora) if lora is not None else None,
                                  _dev(act_save, dt), _dev(y_perm, dt), _dev(ws, torch.uint8),
                                  ws.numel(), _stream(stream)))
 
@@ -161,11 +162,12 @@ def moe_aux_loss(shape, counts, prob_sum, coef, out, stream=None):
                               _stream(stream)))
 
 
-def moe_lora_bwd(shape, lora, dy, offsets, row_src, row_gate, x_perm, act_save, w_down, da_up,
+def moe_lora_bwd(shape, lora, dy, offsets, row_src, row_gate, x, x_src, act_save, w_down, da_up,
                  db_up, da_down, db_down, ws, stream=None):
+    """x, x_src: as for moe_expert_gemm (tokens + row_src, or x_perm + None)."""
     bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
     _check(lib().moe_lora_bwd(ctypes.byref(shape), ctypes.byref(lora), _dev(dy, bf), _dev(offsets, i32),
-                              _dev(row_src, i32), _dev(row_gate, f32), _dev(x_perm, bf),
+                              _dev(row_src, i32), _dev(row_gate, f32), _dev(x, bf), _dev(x_src, i32),
                               _dev(act_save, bf), _dev(w_down, bf), _dev(da_up, f32),
                               _dev(db_up, f32), _dev(da_down, f32), _dev(db_down, f32),
                               _dev(ws, torch.uint8), ws.numel(), _stream(stream)))

@@ -247,13 +247,12 @@ moe_status_t moe_dispatch(const moe_shape_t* shape, const int32_t* topk_idx,
   const bool rows = max_rows(s) > 0;
   MOE_REQUIRE_IF(s.T > 0, topk_idx, "topk_idx");
   MOE_REQUIRE_IF(s.T > 0, topk_gate, "topk_gate");
-  MOE_REQUIRE_IF(s.T > 0, x, "x");
+  MOE_REQUIRE_IF(s.T > 0 && x_perm, x, "x");
   MOE_REQUIRE(counts, "counts");
   MOE_REQUIRE(offsets, "offsets");
   MOE_REQUIRE_IF(s.T > 0, slot, "slot");
   MOE_REQUIRE_IF(rows, row_src, "row_src");
   MOE_REQUIRE_IF(rows, row_gate, "row_gate");
-  MOE_REQUIRE_IF(rows, x_perm, "x_perm");
   if ((st = check_ws(s, 0, ws, ws_bytes)) != MOE_OK) return st;
   Ctx c;
   if ((st = make_ctx(stream, &c)) != MOE_OK) return st;
@@ -263,7 +262,7 @@ moe_status_t moe_dispatch(const moe_shape_t* shape, const int32_t* topk_idx,
                     "dispatch");
 }
 
-moe_status_t moe_expert_gemm(const moe_shape_t* shape, const void* x_perm,
+moe_status_t moe_expert_gemm(const moe_shape_t* shape, const void* x, const int32_t* row_src,
                              const int32_t* offsets, const void* w_gate, const void* w_up,
                              const void* w_down, const moe_lora_t* lora, void* act_save,
                              void* y_perm, void* ws, size_t ws_bytes, moe_stream_t stream) {
@@ -271,7 +270,7 @@ moe_status_t moe_expert_gemm(const moe_shape_t* shape, const void* x_perm,
   if (st != MOE_OK) return st;
   const moe_shape_t& s = *shape;
   const bool rows = max_rows(s) > 0;
-  MOE_REQUIRE_IF(rows, x_perm, "x_perm");
+  MOE_REQUIRE_IF(rows, x, "x");
   MOE_REQUIRE(offsets, "offsets");
   MOE_REQUIRE(w_gate, "w_gate");
   MOE_REQUIRE(w_up, "w_up");
@@ -292,7 +291,7 @@ moe_status_t moe_expert_gemm(const moe_shape_t* shape, const void* x_perm,
     la.a_down = static_cast<const bf16_t*>(lora->a_down);
     la.b_down = static_cast<const bf16_t*>(lora->b_down);
   }
-  return hip_status(launch_expert_gemm(c, s, w, x_perm, offsets, w_gate, w_up, w_down,
+  return hip_status(launch_expert_gemm(c, s, w, x, row_src, offsets, w_gate, w_up, w_down,
                                        lora ? &la : nullptr, act_save, y_perm),
                     "expert GEMM");
 }
@@ -326,8 +325,8 @@ moe_status_t moe_aux_loss(const moe_shape_t* shape, const int32_t* counts,
 
 moe_status_t moe_lora_bwd(const moe_shape_t* shape, const moe_lora_t* lora, const void* dy,
                           const int32_t* offsets, const int32_t* row_src, const float* row_gate,
-                          const void* x_perm, const void* act_save, const void* w_down,
-                          float* da_up, float* db_up, float* da_down, float* db_down, void* ws,
+                          const void* x, const int32_t* x_src, const void* act_save,
+                          const void* w_down, float* da_up, float* db_up, float* da_down, float* db_down, void* ws,
                           size_t ws_bytes, moe_stream_t stream) {
   moe_status_t st = check_shape(shape);
   if (st != MOE_OK) return st;
@@ -339,7 +338,7 @@ moe_status_t moe_lora_bwd(const moe_shape_t* shape, const moe_lora_t* lora, cons
   MOE_REQUIRE(offsets, "offsets");
   MOE_REQUIRE_IF(rows, row_src, "row_src");
   MOE_REQUIRE_IF(rows, row_gate, "row_gate");
-  MOE_REQUIRE_IF(rows, x_perm, "x_perm");
+  MOE_REQUIRE_IF(rows, x, "x");
   MOE_REQUIRE_IF(rows, act_save, "act_save");
   MOE_REQUIRE(w_down, "w_down");
   MOE_REQUIRE(da_up, "da_up");
@@ -355,7 +354,7 @@ moe_status_t moe_lora_bwd(const moe_shape_t* shape, const moe_lora_t* lora, cons
               static_cast<const bf16_t*>(lora->b_down)};
   return hip_status(
       launch_lora_bwd(c, s, w, la, static_cast<const bf16_t*>(dy), offsets, row_src, row_gate,
-                      static_cast<const bf16_t*>(x_perm), static_cast<const bf16_t*>(act_save),
+                      static_cast<const bf16_t*>(x), x_src, static_cast<const bf16_t*>(act_save),
                       static_cast<const bf16_t*>(w_down), da_up, db_up, da_down, db_down),
       "LoRA backward");
 }

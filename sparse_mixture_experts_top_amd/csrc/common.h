@@ -52,6 +52,14 @@ __device__ __forceinline__ int segment_of(const int32_t* off, int L, int p) {
   return lo;
 }
 
+// Wave-uniform read of data no kernel writes while this one runs (written by
+// an earlier kernel on the stream): through the constant address space with a
+// uniform index, so it becomes a scalar load and never waits on vector memory.
+typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr_t;
+__device__ __forceinline__ int ld_uniform(const int32_t* p, int idx) {
+  return ((const_i32_ptr_t)p)[__builtin_amdgcn_readfirstlane(idx)];
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
@@ -128,7 +136,8 @@ struct LoraArgs {
 };
 
 hipError_t launch_expert_gemm(const Ctx& c, const moe_shape_t& s, const Workspace& ws,
-                              const void* x_perm, const int32_t* offsets, const void* w_gate,
+                              const void* x_rows, const int32_t* row_src, const int32_t* offsets,
+                              const void* w_gate,
                               const void* w_up, const void* w_down, const LoraArgs* lora,
                               void* act_save, void* y_perm);
 
@@ -140,7 +149,8 @@ hipError_t launch_combine(const Ctx& c, const moe_shape_t& s, const void* y_perm
 
 hipError_t launch_lora_bwd(const Ctx& c, const moe_shape_t& s, const Workspace& ws,
                            const LoraArgs& lo, const bf16_t* dy, const int32_t* offsets,
-                           const int32_t* row_src, const float* row_gate, const bf16_t* x_perm,
+                           const int32_t* row_src, const float* row_gate, const bf16_t* x_rows,
+                           const int32_t* x_src,
                            const bf16_t* act_save, const bf16_t* w_down, float* da_up,
                            float* db_up, float* da_down, float* db_down);
 

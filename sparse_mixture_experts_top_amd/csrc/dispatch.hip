@@ -20,6 +20,7 @@
 //   K5 capacity  per over-capacity expert: C-th largest (gate, -token) key by
 //                radix select, then kept candidates in token order -> rows
 //   K7 gather    x_perm[p] = x[row_src[p]] with 16-byte loads and stores
+//                (optional: the grouped GEMM can read x through row_src)
 #include "common.h"
 
 namespace moe {
@@ -284,6 +285,7 @@ hipError_t launch_dispatch(const Ctx& c, const moe_shape_t& s, const Workspace& 
                        row_src, row_gate);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
+  if (!x_perm) return hipSuccess;  // the grouped GEMM gathers through row_src itself
   const int64_t rmax = max_rows(s);
   const int grid = (int)std::min<int64_t>(rmax > 0 ? rmax : 1, (int64_t)c.num_cus * 8);
   const size_t row_bytes = (size_t)s.d * (s.dtype == MOE_BF16 ? 2 : 4);

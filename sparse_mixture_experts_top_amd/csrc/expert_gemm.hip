@@ -12,20 +12,23 @@
 //   K-tiles   one block turns offsets into the list of (expert, first row)
 //             row tiles of 128 rows; the GEMMs walk that list on the device,
 //             so no row count ever travels to the host.
-//   K8 gate_up  per (row tile, 64 FFN columns): the B tile interleaves 16 rows
+//   K8 gate_up  per (row tile, 64 FFN columns), reading token rows through
+//             row_src (the dispatch gather fused into the A loader, so the
+//             permuted copy of x never has to exist); the B tile interleaves 16 rows
 //             of W_g and the same 16 rows of W_u, so each lane ends up holding
 //             G and U of the same (row, column) and applies silu(G) * U in
 //             registers; H is rounded to bf16.
 //   K9 down   per (row tile, 128 output columns): O = H W_d^T (+ LoRA).
-// Both are persistent: a grid of 2 workgroups per CU walks the items, each
-// XCD taking a contiguous range so row tiles that share A or B stay in one L2.
+// Both run on the persistent pipelined driver of mfma_tile.h: a grid of 2
+// workgroups per CU walks the items, each XCD taking a contiguous range so
+// row tiles that share A or B stay in one L2.
 // fp32 path (small parity shapes): one thread per output element.
 #include "common.h"
 #include "mfma_tile.h"
 
 namespace moe {
 
-using GemmCfg = TileCfg<kGemmBM, 128>;
+using GemmCfg = DmaCfg<kGemmBM, 128>;
 
 __global__ __launch_bounds__(1024) void build_row_tiles(const int32_t* __restrict__ offsets, int L,
                                                         int bm, int max_tiles,
@@ -57,44 +60,66 @@ __global__ __launch_bounds__(1024) void build_row_tiles(const int32_t* __restric
   if (le == 0) tiles[2 * max_tiles] = total;
 }
 
+// Row-tile item of a grouped GEMM: expert, first row of the tile, rows valid.
+struct RowTile {
+  int le, r0, valid;
+  int64_t row0;  // first dispatched row of the tile
+};
+template <int BM>
+__device__ __forceinline__ RowTile row_tile(const int32_t* tiles, const int32_t* offsets, int ti) {
+  RowTile t;
+  t.le = ld_uniform(tiles, 2 * ti);
+  t.r0 = ld_uniform(tiles, 2 * ti + 1);
+  const int seg = ld_uniform(offsets, t.le);
+  t.valid = min(BM, ld_uniform(offsets, t.le + 1) - seg - t.r0);
+  t.row0 = (int64_t)seg + t.r0;
+  return t;
+}
+
+// K8: H = silu(X W_g^T) * (X W_u^T [+ s Z_u B_u^T]) for one (row tile, 64
+// FFN columns) item. Rows of X are x[row_src[p]] (gather fused into the A
+// loader) or, with row_src == NULL, x[p] of an already gathered matrix.
 template <class Cfg>
-__global__ __launch_bounds__(256) void gate_up_bf16(
-    const bf16_t* __restrict__ x_perm, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ tiles, int max_tiles, const bf16_t* __restrict__ w_gate,
-    const bf16_t* __restrict__ w_up, int d, int f, const float* __restrict__ zu,
-    const bf16_t* __restrict__ b_up, int r, float lora_scale, bf16_t* __restrict__ hbuf,
-    bf16_t* __restrict__ act_save) {
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  bf16_t* smem = reinterpret_cast<bf16_t*>(smem_raw);
-  constexpr int HALF = Cfg::BN / 2;  // FFN columns per item
-  const int nt = f / HALF;
-  const int ntiles = tiles[2 * max_tiles];
-  const XcdSplit sp = xcd_split(ntiles * nt);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int lrow = tid / Cfg::CHUNKS_PER_ROW, lcol = (tid % Cfg::CHUNKS_PER_ROW) * 8;
-  for (int item = sp.first; item < sp.end; item += sp.stride) {
-    const int ti = item / nt, ni = item % nt;
-    const int le = tiles[2 * ti], r0 = tiles[2 * ti + 1];
-    const int seg = offsets[le];
-    const int valid = min(Cfg::BM, offsets[le + 1] - seg - r0);
-    const int64_t row0 = (int64_t)seg + r0;
-    const bf16_t* a_rows[Cfg::A_LOADS];
-    const bf16_t* b_rows[Cfg::B_LOADS];
+struct GateUpProb {
+  const bf16_t* x;
+  const int32_t* row_src;
+  const int32_t* offsets;
+  const int32_t* tiles;
+  const bf16_t* w_gate;
+  const bf16_t* w_up;
+  int d, f, nt;
+  const float* zu;
+  const bf16_t* b_up;
+  int r;
+  float scale;
+  bf16_t* hbuf;
+  bf16_t* act_save;
+  static constexpr int HALF = Cfg::BN / 2;  // FFN columns per item
+
+  __device__ __forceinline__ void setup(int item, DmaLoader<Cfg>& ld) const {
+    const RowTile t = row_tile<Cfg::BM>(tiles, offsets, item / nt);
+    const int ni = item % nt;
+    const int ce = dma_chunk_elem();
 #pragma unroll
-    for (int i = 0; i < Cfg::A_LOADS; ++i)
-      a_rows[i] = x_perm + (row0 + min(lrow + i * Cfg::ROWS_PER_PASS, valid - 1)) * d + lcol;
+    for (int i = 0; i < Cfg::A_DMA; ++i) {
+      const int64_t row = t.row0 + min(dma_row(Cfg::A_DMA, i), t.valid - 1);
+      const int64_t src = row_src ? (int64_t)row_src[row] : row;
+      ld.a[i] = x + src * d + ce;
+    }
 #pragma unroll
-    for (int i = 0; i < Cfg::B_LOADS; ++i) {
-      const int jb = lrow + i * Cfg::ROWS_PER_PASS;
+    for (int i = 0; i < Cfg::B_DMA; ++i) {
+      const int jb = dma_row(Cfg::B_DMA, i);
       const int frag = jb >> 4;
       const int fcol = ni * HALF + (frag >> 1) * 16 + (jb & 15);
-      const bf16_t* w = (frag & 1) ? w_up : w_gate;
-      b_rows[i] = w + ((int64_t)le * f + fcol) * d + lcol;
+      ld.b[i] = ((frag & 1) ? w_up : w_gate) + ((int64_t)t.le * f + fcol) * d + ce;
     }
-    Acc<Cfg> acc;
-    acc.zero();
-    mainloop_nt<Cfg>(a_rows, b_rows, d, acc, smem);
+  }
+
+  __device__ __forceinline__ void epilogue(int item, Acc<Cfg>& acc) const {
+    const RowTile t = row_tile<Cfg::BM>(tiles, offsets, item / nt);
+    const int ni = item % nt;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
     for (int jj = 0; jj < Cfg::FN; jj += 2) {
       const int jg = wn * Cfg::FN + jj;  // even: G fragment, jg + 1: U fragment
@@ -104,16 +129,16 @@ __global__ __launch_bounds__(256) void gate_up_bf16(
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int rin = frag_row<Cfg>(wm, i, lane, q);
-          if (rin >= valid) continue;
-          const int64_t row = row0 + rin;
+          if (rin >= t.valid) continue;
+          const int64_t row = t.row0 + rin;
           const float g = acc.v[i][jj][q];
           float u = acc.v[i][jj + 1][q];
           if (zu) {
             const float* z = zu + row * r;
-            const bf16_t* bu = b_up + ((int64_t)le * f + fcol) * r;
-            float t = 0.f;
-            for (int c = 0; c < r; ++c) t = fmaf(z[c], bf16_to_f32(bu[c]), t);
-            u = fmaf(lora_scale, t, u);
+            const bf16_t* bu = b_up + ((int64_t)t.le * f + fcol) * r;
+            float s = 0.f;
+            for (int c = 0; c < r; ++c) s = fmaf(z[c], bf16_to_f32(bu[c]), s);
+            u = fmaf(scale, s, u);
           }
           const bf16_t h = f32_to_bf16(silu_f(g) * u);
           hbuf[row * f + fcol] = h;
@@ -124,40 +149,45 @@ __global__ __launch_bounds__(256) void gate_up_bf16(
         }
     }
   }
-}
+};
 
 template <class Cfg>
-__global__ __launch_bounds__(256) void down_bf16(
-    const bf16_t* __restrict__ hbuf, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ tiles, int max_tiles, const bf16_t* __restrict__ w_down, int d,
-    int f, const float* __restrict__ zd, const bf16_t* __restrict__ b_down, int r,
-    float lora_scale, bf16_t* __restrict__ y_perm) {
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  bf16_t* smem = reinterpret_cast<bf16_t*>(smem_raw);
-  const int nt = (d + Cfg::BN - 1) / Cfg::BN;
-  const int ntiles = tiles[2 * max_tiles];
-  const XcdSplit sp = xcd_split(ntiles * nt);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int lrow = tid / Cfg::CHUNKS_PER_ROW, lcol = (tid % Cfg::CHUNKS_PER_ROW) * 8;
-  for (int item = sp.first; item < sp.end; item += sp.stride) {
-    const int ti = item / nt, ni = item % nt;
-    const int le = tiles[2 * ti], r0 = tiles[2 * ti + 1];
-    const int seg = offsets[le];
-    const int valid = min(Cfg::BM, offsets[le + 1] - seg - r0);
-    const int64_t row0 = (int64_t)seg + r0;
-    const int n0 = ni * Cfg::BN;
-    const bf16_t* a_rows[Cfg::A_LOADS];
-    const bf16_t* b_rows[Cfg::B_LOADS];
+__global__ __launch_bounds__(256, 2) void gate_up_bf16(GateUpProb<Cfg> pb, int max_tiles) {
+  const int items = ld_uniform(pb.tiles, 2 * max_tiles) * pb.nt;
+  persistent_gemm_dma<Cfg>(pb, items, pb.d / Cfg::BK);
+}
+
+// K9: O = H W_d^T [+ s Z_d B_d^T] for one (row tile, 128 output columns) item.
+template <class Cfg>
+struct DownProb {
+  const bf16_t* hbuf;
+  const int32_t* offsets;
+  const int32_t* tiles;
+  const bf16_t* w_down;
+  int d, f, nt;
+  const float* zd;
+  const bf16_t* b_down;
+  int r;
+  float scale;
+  bf16_t* y_perm;
+
+  __device__ __forceinline__ void setup(int item, DmaLoader<Cfg>& ld) const {
+    const RowTile t = row_tile<Cfg::BM>(tiles, offsets, item / nt);
+    const int n0 = (item % nt) * Cfg::BN;
+    const int ce = dma_chunk_elem();
 #pragma unroll
-    for (int i = 0; i < Cfg::A_LOADS; ++i)
-      a_rows[i] = hbuf + (row0 + min(lrow + i * Cfg::ROWS_PER_PASS, valid - 1)) * f + lcol;
+    for (int i = 0; i < Cfg::A_DMA; ++i)
+      ld.a[i] = hbuf + (t.row0 + min(dma_row(Cfg::A_DMA, i), t.valid - 1)) * f + ce;
 #pragma unroll
-    for (int i = 0; i < Cfg::B_LOADS; ++i)
-      b_rows[i] = w_down + ((int64_t)le * d + min(n0 + lrow + i * Cfg::ROWS_PER_PASS, d - 1)) * f + lcol;
-    Acc<Cfg> acc;
-    acc.zero();
-    mainloop_nt<Cfg>(a_rows, b_rows, f, acc, smem);
+    for (int i = 0; i < Cfg::B_DMA; ++i)
+      ld.b[i] = w_down + ((int64_t)t.le * d + min(n0 + dma_row(Cfg::B_DMA, i), d - 1)) * f + ce;
+  }
+
+  __device__ __forceinline__ void epilogue(int item, Acc<Cfg>& acc) const {
+    const RowTile t = row_tile<Cfg::BM>(tiles, offsets, item / nt);
+    const int n0 = (item % nt) * Cfg::BN;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
     for (int j = 0; j < Cfg::FN; ++j) {
       const int n = n0 + frag_col<Cfg>(wn, j, lane);
@@ -167,25 +197,32 @@ __global__ __launch_bounds__(256) void down_bf16(
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int rin = frag_row<Cfg>(wm, i, lane, q);
-          if (rin >= valid) continue;
-          const int64_t row = row0 + rin;
+          if (rin >= t.valid) continue;
+          const int64_t row = t.row0 + rin;
           float o = acc.v[i][j][q];
           if (zd) {
             const float* z = zd + row * r;
-            const bf16_t* bd = b_down + ((int64_t)le * d + n) * r;
-            float t = 0.f;
-            for (int c = 0; c < r; ++c) t = fmaf(z[c], bf16_to_f32(bd[c]), t);
-            o = fmaf(lora_scale, t, o);
+            const bf16_t* bd = b_down + ((int64_t)t.le * d + n) * r;
+            float s = 0.f;
+            for (int c = 0; c < r; ++c) s = fmaf(z[c], bf16_to_f32(bd[c]), s);
+            o = fmaf(scale, s, o);
           }
           y_perm[row * d + n] = f32_to_bf16(o);
         }
     }
   }
+};
+
+template <class Cfg>
+__global__ __launch_bounds__(256, 2) void down_bf16(DownProb<Cfg> pb, int max_tiles) {
+  const int items = ld_uniform(pb.tiles, 2 * max_tiles) * pb.nt;
+  persistent_gemm_dma<Cfg>(pb, items, pb.f / Cfg::BK);
 }
 
 // ------------------------------------------------------------- fp32 path ---
 
-__global__ __launch_bounds__(256) void gate_up_f32(const float* __restrict__ x_perm,
+__global__ __launch_bounds__(256) void gate_up_f32(const float* __restrict__ x_rows,
+                                                   const int32_t* __restrict__ row_src,
                                                    const int32_t* __restrict__ offsets, int L,
                                                    int64_t rmax, const float* __restrict__ w_gate,
                                                    const float* __restrict__ w_up, int d, int f,
@@ -196,7 +233,7 @@ __global__ __launch_bounds__(256) void gate_up_f32(const float* __restrict__ x_p
        id += (int64_t)gridDim.x * blockDim.x) {
     const int p = (int)(id / f), c = (int)(id % f);
     const int le = segment_of(offsets, L, p);
-    const float* xr = x_perm + (int64_t)p * d;
+    const float* xr = x_rows + (int64_t)(row_src ? row_src[p] : p) * d;
     const float* wg = w_gate + ((int64_t)le * f + c) * d;
     const float* wu = w_up + ((int64_t)le * f + c) * d;
     float g = 0.f, u = 0.f;
@@ -241,7 +278,8 @@ hipError_t launch_row_tiles(const Ctx& c, const int32_t* offsets, int L, int max
 }
 
 hipError_t launch_expert_gemm(const Ctx& c, const moe_shape_t& s, const Workspace& ws,
-                              const void* x_perm, const int32_t* offsets, const void* w_gate,
+                              const void* x_rows, const int32_t* row_src, const int32_t* offsets,
+                              const void* w_gate,
                               const void* w_up, const void* w_down, const LoraArgs* lora,
                               void* act_save, void* y_perm) {
   const int L = s.e_hi - s.e_lo;
@@ -251,8 +289,8 @@ hipError_t launch_expert_gemm(const Ctx& c, const moe_shape_t& s, const Workspac
     const int grid = c.num_cus * 4;
     {
       TimedLaunch tl(MOE_K_GATE_UP, c.stream);
-      hipLaunchKernelGGL(gate_up_f32, dim3(grid), dim3(256), 0, c.stream, (const float*)x_perm,
-                         offsets, L, rmax, (const float*)w_gate, (const float*)w_up, s.d, s.f,
+      hipLaunchKernelGGL(gate_up_f32, dim3(grid), dim3(256), 0, c.stream, (const float*)x_rows,
+                         row_src, offsets, L, rmax, (const float*)w_gate, (const float*)w_up, s.d, s.f,
                          (float*)ws.hbuf, (float*)act_save);
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
@@ -263,20 +301,20 @@ hipError_t launch_expert_gemm(const Ctx& c, const moe_shape_t& s, const Workspac
   }
   const int max_tiles = gemm_max_tiles(s);
   if ((err = launch_row_tiles(c, offsets, L, max_tiles, ws.gemm_tiles)) != hipSuccess) return err;
-  const bf16_t* xp = (const bf16_t*)x_perm;
+  const bf16_t* xr = (const bf16_t*)x_rows;
   if (lora) {
-    err = launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, xp, s.d, nullptr, nullptr, s.d,
+    err = launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, xr, s.d, row_src, nullptr, s.d,
                                       lora->a_up, true, lora->r, ws.zu);
     if (err != hipSuccess) return err;
   }
-  const int grid = c.num_cus * 2;  // two 72 KB-LDS workgroups fit one CU
+  const int grid = c.num_cus * 2;  // two 64 KB-LDS workgroups fit one CU
   {
+    GateUpProb<GemmCfg> pb{xr, row_src, offsets, ws.gemm_tiles, (const bf16_t*)w_gate,
+                           (const bf16_t*)w_up, s.d, s.f, s.f / GateUpProb<GemmCfg>::HALF,
+                           lora ? ws.zu : nullptr, lora ? lora->b_up : nullptr, lora ? lora->r : 0,
+                           lora ? lora->scale : 0.f, (bf16_t*)ws.hbuf, (bf16_t*)act_save};
     TimedLaunch tl(MOE_K_GATE_UP, c.stream);
-    hipLaunchKernelGGL(gate_up_bf16<GemmCfg>, dim3(grid), dim3(256), GemmCfg::SMEM_BYTES, c.stream,
-                       xp, offsets, ws.gemm_tiles, max_tiles, (const bf16_t*)w_gate,
-                       (const bf16_t*)w_up, s.d, s.f, lora ? ws.zu : nullptr,
-                       lora ? lora->b_up : nullptr, lora ? lora->r : 0,
-                       lora ? lora->scale : 0.f, (bf16_t*)ws.hbuf, (bf16_t*)act_save);
+    hipLaunchKernelGGL(gate_up_bf16<GemmCfg>, dim3(grid), dim3(256), 0, c.stream, pb, max_tiles);
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (lora) {
@@ -284,12 +322,12 @@ hipError_t launch_expert_gemm(const Ctx& c, const moe_shape_t& s, const Workspac
                                       nullptr, s.f, lora->a_down, true, lora->r, ws.zd);
     if (err != hipSuccess) return err;
   }
+  DownProb<GemmCfg> pb{(const bf16_t*)ws.hbuf, offsets, ws.gemm_tiles, (const bf16_t*)w_down, s.d, s.f,
+                       (s.d + GemmCfg::BN - 1) / GemmCfg::BN, lora ? ws.zd : nullptr,
+                       lora ? lora->b_down : nullptr, lora ? lora->r : 0, lora ? lora->scale : 0.f,
+                       (bf16_t*)y_perm};
   TimedLaunch tl(MOE_K_DOWN, c.stream);
-  hipLaunchKernelGGL(down_bf16<GemmCfg>, dim3(grid), dim3(256), GemmCfg::SMEM_BYTES, c.stream,
-                     (const bf16_t*)ws.hbuf, offsets, ws.gemm_tiles, max_tiles,
-                     (const bf16_t*)w_down, s.d, s.f, lora ? ws.zd : nullptr,
-                     lora ? lora->b_down : nullptr, lora ? lora->r : 0, lora ? lora->scale : 0.f,
-                     (bf16_t*)y_perm);
+  hipLaunchKernelGGL(down_bf16<GemmCfg>, dim3(grid), dim3(256), 0, c.stream, pb, max_tiles);
   return hipGetLastError();
 }
 

@@ -181,38 +181,47 @@ static hipError_t launch_seg_outer(const Ctx& c, int L, const int32_t* offsets, 
 }
 
 // dU[row, n] = (g_row * (dY[src_row] . W_d[:, n]) + s * wproj[row] . A_d[:, n])
-//              * silu(G[row, n]), per (row tile, 128 FFN columns).
+//              * silu(G[row, n]), per (row tile, 128 FFN columns) item.
 template <class Cfg>
-__global__ __launch_bounds__(256) void lora_dh_bf16(
-    const bf16_t* __restrict__ dy, const int32_t* __restrict__ row_src,
-    const float* __restrict__ row_gate, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ tiles, int max_tiles, const bf16_t* __restrict__ w_down, int d,
-    int f, const float* __restrict__ wproj, const bf16_t* __restrict__ a_down, int r, float s,
-    const bf16_t* __restrict__ act_save, float* __restrict__ du) {
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  bf16_t* smem = reinterpret_cast<bf16_t*>(smem_raw);
-  const int nt = (f + Cfg::BN - 1) / Cfg::BN;
-  const int ntiles = tiles[2 * max_tiles];
-  const XcdSplit sp = xcd_split(ntiles * nt);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int lrow = tid / Cfg::CHUNKS_PER_ROW, lcol = (tid % Cfg::CHUNKS_PER_ROW) * 8;
-  for (int item = sp.first; item < sp.end; item += sp.stride) {
-    const int ti = item / nt, ni = item % nt;
-    const int le = tiles[2 * ti], r0 = tiles[2 * ti + 1];
-    const int seg = offsets[le];
-    const int valid = min(Cfg::BM, offsets[le + 1] - seg - r0);
-    const int64_t row0 = (int64_t)seg + r0;
-    const int n0 = ni * Cfg::BN;
-    const bf16_t* a_rows[Cfg::A_LOADS];
+struct DhProb {
+  const bf16_t* dy;
+  const int32_t* row_src;
+  const float* row_gate;
+  const int32_t* offsets;
+  const int32_t* tiles;
+  const bf16_t* w_down;
+  int d, f, nt;
+  const float* wproj;
+  const bf16_t* a_down;
+  int r;
+  float s;
+  const bf16_t* act_save;
+  float* du;
+
+  __device__ __forceinline__ void setup(int item, LoaderNN<Cfg>& ld) const {
+    const int ti = item / nt, n0 = (item % nt) * Cfg::BN;
+    const int le = ld_uniform(tiles, 2 * ti), r0 = ld_uniform(tiles, 2 * ti + 1);
+    const int seg = ld_uniform(offsets, le);
+    const int valid = min(Cfg::BM, ld_uniform(offsets, le + 1) - seg - r0);
+    const int lrow = threadIdx.x / Cfg::CHUNKS_PER_ROW, lcol = (threadIdx.x % Cfg::CHUNKS_PER_ROW) * 8;
 #pragma unroll
     for (int i = 0; i < Cfg::A_LOADS; ++i) {
-      const int64_t row = row0 + min(lrow + i * Cfg::ROWS_PER_PASS, valid - 1);
-      a_rows[i] = dy + (int64_t)row_src[row] * d + lcol;
+      const int64_t row = (int64_t)seg + r0 + min(lrow + i * Cfg::ROWS_PER_PASS, valid - 1);
+      ld.a[i] = dy + (int64_t)row_src[row] * d + lcol;
     }
-    Acc<Cfg> acc;
-    acc.zero();
-    mainloop_nn<Cfg>(a_rows, w_down + (int64_t)le * d * f + n0, f, min(Cfg::BN, f - n0), d, acc, smem);
+    ld.b_base = w_down + (int64_t)le * d * f + n0;
+    ld.ldb = f;
+    ld.n_valid = min(Cfg::BN, f - n0);
+  }
+
+  __device__ __forceinline__ void epilogue(int item, Acc<Cfg>& acc) const {
+    const int ti = item / nt, n0 = (item % nt) * Cfg::BN;
+    const int le = ld_uniform(tiles, 2 * ti), r0 = ld_uniform(tiles, 2 * ti + 1);
+    const int seg = ld_uniform(offsets, le);
+    const int valid = min(Cfg::BM, ld_uniform(offsets, le + 1) - seg - r0);
+    const int64_t row0 = (int64_t)seg + r0;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
     for (int j = 0; j < Cfg::FN; ++j) {
       const int n = n0 + frag_col<Cfg>(wn, j, lane);
@@ -234,12 +243,19 @@ __global__ __launch_bounds__(256) void lora_dh_bf16(
         }
     }
   }
+};
+
+template <class Cfg>
+__global__ __launch_bounds__(256, 2) void lora_dh_bf16(DhProb<Cfg> pb, int max_tiles) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  const int items = ld_uniform(pb.tiles, 2 * max_tiles) * pb.nt;
+  persistent_gemm<Cfg, LoaderNN<Cfg>>(pb, items, pb.d / Cfg::BK, reinterpret_cast<bf16_t*>(smem_raw));
 }
 
 hipError_t launch_lora_bwd(const Ctx& c, const moe_shape_t& sh, const Workspace& ws,
                            const LoraArgs& lo, const bf16_t* dy, const int32_t* offsets,
-                           const int32_t* row_src, const float* row_gate, const bf16_t* x_perm,
-                           const bf16_t* act_save, const bf16_t* w_down, float* da_up,
+                           const int32_t* row_src, const float* row_gate, const bf16_t* x_rows,
+                           const int32_t* x_src, const bf16_t* act_save, const bf16_t* w_down, float* da_up,
                            float* db_up, float* da_down, float* db_down) {
   using Cfg = TileCfg<kGemmBM, 128>;
   const int L = sh.e_hi - sh.e_lo;
@@ -251,21 +267,22 @@ hipError_t launch_lora_bwd(const Ctx& c, const moe_shape_t& sh, const Workspace&
 #define MOE_TRY(x) \
   if ((err = (x)) != hipSuccess) return err
   MOE_TRY(launch_row_tiles(c, offsets, L, max_tiles, ws.gemm_tiles));
-  MOE_TRY(launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, x_perm, d, nullptr, nullptr, d, lo.a_up, true, r, ws.zu));
+  MOE_TRY(launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, x_rows, d, x_src, nullptr, d, lo.a_up, true, r, ws.zu));
   MOE_TRY(launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, H, 2 * f, nullptr, nullptr, f, lo.a_down, true, r, ws.zd));
   MOE_TRY(launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, dy, d, row_src, row_gate, d, lo.b_down, false, r, ws.wproj));
   {
     TimedLaunch tl(MOE_K_LORA_DH, c.stream);
-    hipLaunchKernelGGL(lora_dh_bf16<Cfg>, dim3(c.num_cus * 2), dim3(256), Cfg::SMEM_BYTES, c.stream, dy,
-                       row_src, row_gate, offsets, ws.gemm_tiles, max_tiles, w_down, d, f, ws.wproj,
-                       lo.a_down, r, lo.scale, act_save, ws.du);
+    DhProb<Cfg> pb{dy, row_src, row_gate, offsets, ws.gemm_tiles, w_down, d, f, (f + Cfg::BN - 1) / Cfg::BN,
+                   ws.wproj, lo.a_down, r, lo.scale, act_save, ws.du};
+    hipLaunchKernelGGL(lora_dh_bf16<Cfg>, dim3(c.num_cus * 2), dim3(256), Cfg::SMEM_BYTES, c.stream, pb,
+                       max_tiles);
     MOE_TRY(hipGetLastError());
   }
   MOE_TRY(launch_lora_rowproj<float>(c, L, offsets, rmax, ws.du, f, nullptr, nullptr, f, lo.b_up, false, r, ws.vproj));
   MOE_TRY(launch_seg_outer<bf16_t>(c, L, offsets, ws.zd, r, dy, d, row_src, row_gate, d, lo.scale, false, db_down));
   MOE_TRY(launch_seg_outer<bf16_t>(c, L, offsets, ws.wproj, r, H, 2 * f, nullptr, nullptr, f, lo.scale, true, da_down));
   MOE_TRY(launch_seg_outer<float>(c, L, offsets, ws.zu, r, ws.du, f, nullptr, nullptr, f, lo.scale, false, db_up));
-  MOE_TRY(launch_seg_outer<bf16_t>(c, L, offsets, ws.vproj, r, x_perm, d, nullptr, nullptr, d, lo.scale, true, da_up));
+  MOE_TRY(launch_seg_outer<bf16_t>(c, L, offsets, ws.vproj, r, x_rows, d, x_src, nullptr, d, lo.scale, true, da_up));
 #undef MOE_TRY
   return hipSuccess;
 }

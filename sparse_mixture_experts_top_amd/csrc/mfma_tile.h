@@ -2,9 +2,9 @@
 //
 // One workgroup = 4 waves in a 2 x 2 grid; each wave owns a (BM/2) x (BN/2)
 // sub-tile made of 16 x 16 fragments computed with v_mfma_f32_16x16x32_bf16.
-// K advances in steps of 64: each step stages A and B through LDS (double
-// buffered: the next step's global loads are in flight while the current
-// step's MFMAs run), rows padded by 16 bytes to spread LDS banks.
+// K advances in steps of 64: each step stages A and B through LDS (two
+// buffers, plus two register stages of global loads in flight), rows padded
+// by 16 bytes to spread LDS banks.
 //
 // Fragment layout of the 16x16x32 bf16 MFMA: lane l supplies row (l % 16) of
 // the A fragment and row (l % 16) of the B fragment (= column of B^T), each
@@ -105,49 +105,37 @@ __device__ __forceinline__ void sstore_rows(bf16_t* lds, const u32x4 (&r)[N], in
     *reinterpret_cast<u32x4*>(&lds[(lrow + i * Cfg::ROWS_PER_PASS) * Cfg::LDS_STRIDE + lcol]) = r[i];
 }
 
-// Main loop with both operands K-contiguous ("NT"): a_rows[i] / b_rows[i] are
-// the row starts (already offset by this thread's 8-element column chunk) of
-// the rows this thread loads; rows past the valid range must point at some
-// valid row (their results are discarded by the caller). K % 64 == 0.
-// LDS holds [A0 | A1 | B0 | B1]; buffers are addressed by integer offsets so
-// every access stays an LDS (ds_*) instruction.
+// Staging registers and loaders for one K step of A (K-contiguous rows) and
+// of B, either K-contiguous rows ("NT") or stored [K][N] ("NN", transposed
+// into the same LDS layout while it is stored).
 template <class Cfg>
-__device__ __forceinline__ void mainloop_nt(const bf16_t* const (&a_rows)[Cfg::A_LOADS],
-                                            const bf16_t* const (&b_rows)[Cfg::B_LOADS], int K,
-                                            Acc<Cfg>& acc, bf16_t* smem) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int lrow = tid / Cfg::CHUNKS_PER_ROW;
-  const int lcol = (tid % Cfg::CHUNKS_PER_ROW) * 8;
-  bf16_t* const A0 = smem;
-  bf16_t* const B0 = smem + 2 * Cfg::A_ELEMS;
-  u32x4 ra[Cfg::A_LOADS], rb[Cfg::B_LOADS];
-  const int nk = K / Cfg::BK;
+struct RegsNT {
+  u32x4 a[Cfg::A_LOADS];
+  u32x4 b[Cfg::B_LOADS];
+};
 
-  gload_rows(ra, a_rows, 0);
-  gload_rows(rb, b_rows, 0);
-  sstore_rows<Cfg>(A0, ra, lrow, lcol);
-  sstore_rows<Cfg>(B0, rb, lrow, lcol);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      gload_rows(ra, a_rows, (kt + 1) * Cfg::BK);
-      gload_rows(rb, b_rows, (kt + 1) * Cfg::BK);
-    }
-    mfma_step<Cfg>(A0 + cur * Cfg::A_ELEMS, B0 + cur * Cfg::B_ELEMS, acc, wm, wn, lane);
-    if (more) {
-      sstore_rows<Cfg>(A0 + (cur ^ 1) * Cfg::A_ELEMS, ra, lrow, lcol);
-      sstore_rows<Cfg>(B0 + (cur ^ 1) * Cfg::B_ELEMS, rb, lrow, lcol);
-    }
-    __syncthreads();
+// a[i] / b[i]: start (already offset by this thread's 8-element column chunk)
+// of the i-th row this thread loads; rows past the valid range point at some
+// valid row, their results are discarded by the epilogue.
+template <class Cfg>
+struct LoaderNT {
+  typedef RegsNT<Cfg> Regs;
+  const bf16_t* a[Cfg::A_LOADS];
+  const bf16_t* b[Cfg::B_LOADS];
+  __device__ __forceinline__ void load(Regs& r, int kt) const {
+    const int k0 = kt * Cfg::BK;
+    gload_rows(r.a, a, k0);
+    gload_rows(r.b, b, k0);
   }
-}
+  __device__ __forceinline__ void store(bf16_t* As, bf16_t* Bs, const Regs& r) const {
+    const int lrow = threadIdx.x / Cfg::CHUNKS_PER_ROW, lcol = (threadIdx.x % Cfg::CHUNKS_PER_ROW) * 8;
+    sstore_rows<Cfg>(As, r.a, lrow, lcol);
+    sstore_rows<Cfg>(Bs, r.b, lrow, lcol);
+  }
+};
 
-// B stored [K][N] ("NN"): load 8 consecutive n of one k per 16-byte chunk;
-// columns at or past n_valid are clamped to the last valid column.
+// B stored [K][N]: load 8 consecutive n of one k per 16-byte chunk; columns
+// at or past n_valid are clamped to the last valid column.
 template <class Cfg>
 __device__ __forceinline__ void gload_nn(u32x4 (&r)[Cfg::NN_B_LOADS], const bf16_t* b_base,
                                          int64_t ldb, int k0, int nk_row, int nn_col, int n_valid,
@@ -180,46 +168,32 @@ __device__ __forceinline__ void sstore_nn(bf16_t* lds, const u32x4 (&r)[Cfg::NN_
   }
 }
 
-// Main loop with A K-contiguous and B stored [K][N] ("NN"): b_base points at
-// B[0][n0] (row stride ldb); columns n0 + c for c >= n_valid are clamped to
-// column n0 + n_valid - 1. B is transposed into the same LDS layout as NT.
 template <class Cfg>
-__device__ __forceinline__ void mainloop_nn(const bf16_t* const (&a_rows)[Cfg::A_LOADS],
-                                            const bf16_t* b_base, int64_t ldb, int n_valid,
-                                            int K, Acc<Cfg>& acc, bf16_t* smem) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int lrow = tid / Cfg::CHUNKS_PER_ROW;
-  const int lcol = (tid % Cfg::CHUNKS_PER_ROW) * 8;
-  const int nk_row = tid / Cfg::NN_CHUNKS_PER_K;
-  const int nn_col = (tid % Cfg::NN_CHUNKS_PER_K) * 8;
-  const bool chunk_ok = nn_col + 8 <= n_valid;
-  bf16_t* const A0 = smem;
-  bf16_t* const B0 = smem + 2 * Cfg::A_ELEMS;
-  u32x4 ra[Cfg::A_LOADS], rb[Cfg::NN_B_LOADS];
-  const int nk = K / Cfg::BK;
+struct RegsNN {
+  u32x4 a[Cfg::A_LOADS];
+  u32x4 b[Cfg::NN_B_LOADS];
+};
 
-  gload_rows(ra, a_rows, 0);
-  gload_nn<Cfg>(rb, b_base, ldb, 0, nk_row, nn_col, n_valid, chunk_ok);
-  sstore_rows<Cfg>(A0, ra, lrow, lcol);
-  sstore_nn<Cfg>(B0, rb, nk_row, nn_col);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      gload_rows(ra, a_rows, (kt + 1) * Cfg::BK);
-      gload_nn<Cfg>(rb, b_base, ldb, (kt + 1) * Cfg::BK, nk_row, nn_col, n_valid, chunk_ok);
-    }
-    mfma_step<Cfg>(A0 + cur * Cfg::A_ELEMS, B0 + cur * Cfg::B_ELEMS, acc, wm, wn, lane);
-    if (more) {
-      sstore_rows<Cfg>(A0 + (cur ^ 1) * Cfg::A_ELEMS, ra, lrow, lcol);
-      sstore_nn<Cfg>(B0 + (cur ^ 1) * Cfg::B_ELEMS, rb, nk_row, nn_col);
-    }
-    __syncthreads();
+template <class Cfg>
+struct LoaderNN {
+  typedef RegsNN<Cfg> Regs;
+  const bf16_t* a[Cfg::A_LOADS];
+  const bf16_t* b_base;  // B[0][n0]
+  int64_t ldb;
+  int n_valid;
+  __device__ __forceinline__ void load(Regs& r, int kt) const {
+    const int k0 = kt * Cfg::BK;
+    const int nk_row = threadIdx.x / Cfg::NN_CHUNKS_PER_K;
+    const int nn_col = (threadIdx.x % Cfg::NN_CHUNKS_PER_K) * 8;
+    gload_rows(r.a, a, k0);
+    gload_nn<Cfg>(r.b, b_base, ldb, k0, nk_row, nn_col, n_valid, nn_col + 8 <= n_valid);
   }
-}
+  __device__ __forceinline__ void store(bf16_t* As, bf16_t* Bs, const Regs& r) const {
+    const int lrow = threadIdx.x / Cfg::CHUNKS_PER_ROW, lcol = (threadIdx.x % Cfg::CHUNKS_PER_ROW) * 8;
+    sstore_rows<Cfg>(As, r.a, lrow, lcol);
+    sstore_nn<Cfg>(Bs, r.b, threadIdx.x / Cfg::NN_CHUNKS_PER_K, (threadIdx.x % Cfg::NN_CHUNKS_PER_K) * 8);
+  }
+};
 
 // Workgroup -> work item with the XCD-aware order: the hardware hands
 // consecutive workgroup ids to the 8 XCDs in turn, so id b runs on XCD b % 8.
@@ -240,6 +214,236 @@ __device__ __forceinline__ XcdSplit xcd_split(int items) {
   s.end = min(items, (xcd + 1) * chunk);
   s.stride = per_xcd;
   return s;
+}
+
+// Persistent GEMM driver with register-staged loads (used where B must be
+// transposed on its way into LDS). The workgroup's items (XCD-aware split,
+// see xcd_split) are walked as one flat sequence of K steps, so the pipeline
+// never drains between items: while the MFMAs of step g run from one LDS
+// buffer, step g+1 is in flight into registers; when step g closes an item,
+// its epilogue runs while the next item's first step is loading.
+//   Prob::setup(item, loader)   row pointers of an item
+//   Prob::epilogue(item, acc)   consume one finished tile
+template <class Cfg, class Loader, class Prob>
+__device__ __forceinline__ void persistent_gemm(Prob& pb, int items, int nk, bf16_t* smem) {
+  const XcdSplit sp = xcd_split(items);
+  if (sp.first >= sp.end || nk <= 0) return;
+  const int n_mine = (sp.end - sp.first + sp.stride - 1) / sp.stride;
+  const int total = n_mine * nk;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  bf16_t* const A0 = smem;
+  bf16_t* const B0 = smem + 2 * Cfg::A_ELEMS;
+  Loader ld;
+  typename Loader::Regs r0;
+  int l_ord = 0, l_kt = 0;  // load cursor: item ordinal and K step
+  pb.setup(sp.first, ld);
+  ld.load(r0, 0);
+  ld.store(A0, B0, r0);
+  if (++l_kt == nk) {
+    l_kt = 0;
+    if (++l_ord < n_mine) pb.setup(sp.first + l_ord * sp.stride, ld);
+  }
+  __syncthreads();
+  Acc<Cfg> acc;
+  acc.zero();
+  int c_kt = 0, c_ord = 0;  // compute cursor
+  for (int g = 0; g < total; ++g) {
+    const int cur = g & 1;
+    const bool more = g + 1 < total;
+    if (more) ld.load(r0, l_kt);
+    mfma_step<Cfg>(A0 + cur * Cfg::A_ELEMS, B0 + cur * Cfg::B_ELEMS, acc, wm, wn, lane);
+    if (more) {
+      ld.store(A0 + (cur ^ 1) * Cfg::A_ELEMS, B0 + (cur ^ 1) * Cfg::B_ELEMS, r0);
+      if (++l_kt == nk) {
+        l_kt = 0;
+        if (++l_ord < n_mine) pb.setup(sp.first + l_ord * sp.stride, ld);
+      }
+    }
+    __syncthreads();
+    if (++c_kt == nk) {
+      pb.epilogue(sp.first + c_ord * sp.stride, acc);
+      acc.zero();
+      c_kt = 0;
+      ++c_ord;
+    }
+  }
+}
+
+// ===================================================== LDS-DMA pipeline ===
+//
+// For operands that are K-contiguous rows (A and B "NT"), global memory is
+// copied straight into LDS with global_load_lds_dwordx4 (each lane moves 16
+// bytes; the 64 lanes of one instruction fill 1 KB of LDS in lane order), so
+// no registers hold tiles in transit and several K steps can be in flight.
+//
+// K step = 32. A stage holds A [BM][32] and B [BN][32] bf16 (64-byte rows,
+// 16 rows per DMA instruction). To keep the MFMA fragment reads free of bank
+// conflicts, the 16-byte chunk c of row r is stored at slot c ^ ((r >> 2) & 3):
+// the 16 rows one fragment read touches then cover 16 distinct bank groups.
+// Four stages form a ring; stage g's slot is g % 4 and three stages are in
+// flight while one is consumed. Each slot is its own __shared__ array so the
+// compiler can tell the DMA into one slot from the reads of another.
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+template <int BM_, int BN_>
+struct DmaCfg {
+  static constexpr int BM = BM_;
+  static constexpr int BN = BN_;
+  static constexpr int BK = 32;
+  static constexpr int STAGES = 4;
+  static constexpr int FM = BM / 32;  // fragments per wave along M (2 x 2 waves)
+  static constexpr int FN = BN / 32;
+  static constexpr int A_DMA = BM / 64;  // DMA instructions per wave per stage (16 rows each, 4 waves)
+  static constexpr int B_DMA = BN / 64;
+  static constexpr int DMA_PER_STAGE = A_DMA + B_DMA;
+  static constexpr int A_ELEMS = BM * BK;
+  static constexpr int B_ELEMS = BN * BK;
+  static_assert(BM % 64 == 0 && BN % 64 == 0, "DMA tiles are multiples of 64 rows");
+};
+
+// Per-thread source rows of one item: a[i] / b[i] point at the logical chunk
+// this lane fetches ((lane & 3) ^ (lane >> 4)) of row 16 * (wave * X_DMA + i)
+// + lane / 4 of the tile; set by Prob::setup.
+template <class Cfg>
+struct DmaLoader {
+  const bf16_t* a[Cfg::A_DMA];
+  const bf16_t* b[Cfg::B_DMA];
+};
+
+// Row of the tile whose chunk this thread fetches in DMA instruction i, and
+// the element offset of that chunk inside the row.
+__device__ __forceinline__ int dma_row(int x_dma, int i) {
+  return 16 * ((int)(threadIdx.x >> 6) * x_dma + i) + ((threadIdx.x & 63) >> 2);
+}
+__device__ __forceinline__ int dma_chunk_elem() {
+  const int lane = threadIdx.x & 63;
+  return (((lane & 3) ^ (lane >> 4)) & 3) * 8;
+}
+
+// One 16-byte-per-lane DMA: global -> LDS at lds + 16 * lane. Issued as
+// inline assembly so the compiler's wait-count pass does not treat it as an
+// LDS store: with many DMAs in flight it would otherwise make every LDS read
+// wait for all of them. Completion is tracked explicitly instead
+// (dma_wait_younger + barrier before a stage is read). M0 carries the LDS
+// base; nothing else in these kernels uses M0.
+__device__ __forceinline__ void dma16(const void* g, const bf16_t* lds) {
+  const uint32_t a = (uint32_t)(uintptr_t)(lds_void_t*)lds;
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(a) : "memory");
+}
+
+template <class Cfg>
+__device__ __forceinline__ void dma_issue(const DmaLoader<Cfg>& ld, int kt, bf16_t* As, bf16_t* Bs) {
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int k0 = kt * Cfg::BK;
+#pragma unroll
+  for (int i = 0; i < Cfg::A_DMA; ++i) dma16(ld.a[i] + k0, As + 16 * (wave * Cfg::A_DMA + i) * Cfg::BK);
+#pragma unroll
+  for (int i = 0; i < Cfg::B_DMA; ++i) dma16(ld.b[i] + k0, Bs + 16 * (wave * Cfg::B_DMA + i) * Cfg::BK);
+}
+
+// One K step of 32 from a swizzled stage.
+template <class Cfg>
+__device__ __forceinline__ void dma_mfma(const bf16_t* As, const bf16_t* Bs, Acc<Cfg>& acc, int wm,
+                                         int wn, int lane) {
+  const int r = lane & 15;
+  const int slot = ((lane >> 4) ^ (r >> 2)) & 3;
+  bf16x8 a[Cfg::FM], b[Cfg::FN];
+#pragma unroll
+  for (int i = 0; i < Cfg::FM; ++i)
+    a[i] = *reinterpret_cast<const bf16x8*>(&As[(wm * (Cfg::BM / 2) + i * 16 + r) * Cfg::BK + slot * 8]);
+#pragma unroll
+  for (int j = 0; j < Cfg::FN; ++j)
+    b[j] = *reinterpret_cast<const bf16x8*>(&Bs[(wn * (Cfg::BN / 2) + j * 16 + r) * Cfg::BK + slot * 8]);
+#pragma unroll
+  for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < Cfg::FN; ++j)
+      acc.v[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc.v[i][j], 0, 0, 0);
+}
+
+// Wait until at most n of this thread's vector-memory operations are
+// outstanding (n a multiple of DMA_PER_STAGE, at most 2 stages).
+template <class Cfg>
+__device__ __forceinline__ void dma_wait_younger(int younger_stages) {
+  // s_waitcnt immediate: vmcnt in bits [3:0] and [15:14], expcnt [6:4] and
+  // lgkmcnt [11:8] left at their "no wait" maxima.
+  constexpr int n1 = Cfg::DMA_PER_STAGE, n2 = 2 * Cfg::DMA_PER_STAGE;
+  static_assert(n2 < 64, "vmcnt field");
+  if (younger_stages >= 2)
+    __builtin_amdgcn_s_waitcnt((n2 & 15) | ((n2 >> 4) << 14) | (7 << 4) | (15 << 8));
+  else if (younger_stages == 1)
+    __builtin_amdgcn_s_waitcnt((n1 & 15) | ((n1 >> 4) << 14) | (7 << 4) | (15 << 8));
+  else
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+}
+
+// Persistent driver on the DMA ring. Same contract as persistent_gemm, with
+// Prob::setup filling a DmaLoader. Step g:
+//   wait for own DMAs of stage g, barrier (everyone's DMAs of g landed, and
+//   everyone finished reading slot (g-1) % 4), issue stage g+3 into that slot,
+//   MFMAs of stage g, epilogue if g closes an item.
+// The barrier is a bare s_barrier: the explicit vmcnt wait before it already
+// orders this wave's DMA writes, and a fenced barrier would wait for every
+// stage in flight.
+template <class Cfg, class Prob>
+__device__ __forceinline__ void persistent_gemm_dma(Prob& pb, int items, int nk) {
+  __shared__ __align__(16) bf16_t sA0[Cfg::A_ELEMS], sA1[Cfg::A_ELEMS], sA2[Cfg::A_ELEMS], sA3[Cfg::A_ELEMS];
+  __shared__ __align__(16) bf16_t sB0[Cfg::B_ELEMS], sB1[Cfg::B_ELEMS], sB2[Cfg::B_ELEMS], sB3[Cfg::B_ELEMS];
+  const XcdSplit sp = xcd_split(items);
+  if (sp.first >= sp.end || nk <= 0) return;
+  const int n_mine = (sp.end - sp.first + sp.stride - 1) / sp.stride;
+  const int total = n_mine * nk;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  DmaLoader<Cfg> ld;
+  int l_ord = 0, l_kt = 0;
+  pb.setup(sp.first, ld);
+
+#define MOE_DMA_NEXT(As, Bs)                                               \
+  {                                                                        \
+    dma_issue<Cfg>(ld, l_kt, As, Bs);                                      \
+    if (++l_kt == nk) {                                                    \
+      l_kt = 0;                                                            \
+      if (++l_ord < n_mine) pb.setup(sp.first + l_ord * sp.stride, ld);    \
+    }                                                                      \
+  }
+
+  // prologue: stages 0, 1, 2 in flight
+  MOE_DMA_NEXT(sA0, sB0);
+  if (total > 1) MOE_DMA_NEXT(sA1, sB1);
+  if (total > 2) MOE_DMA_NEXT(sA2, sB2);
+  Acc<Cfg> acc;
+  acc.zero();
+  int c_kt = 0, c_ord = 0;
+
+#define MOE_DMA_STEP(g, As, Bs, NA, NB)                                        \
+  {                                                                            \
+    dma_wait_younger<Cfg>(min(2, total - 1 - (g)));                            \
+    __builtin_amdgcn_s_barrier();                                              \
+    if ((g) + 3 < total) MOE_DMA_NEXT(NA, NB);                                 \
+    dma_mfma<Cfg>(As, Bs, acc, wm, wn, lane);                                  \
+    if (++c_kt == nk) {                                                        \
+      pb.epilogue(sp.first + c_ord * sp.stride, acc);                          \
+      acc.zero();                                                              \
+      c_kt = 0;                                                                \
+      ++c_ord;                                                                 \
+    }                                                                          \
+  }
+
+  for (int g = 0; g < total; g += 4) {
+    MOE_DMA_STEP(g, sA0, sB0, sA3, sB3);
+    if (g + 1 >= total) break;
+    MOE_DMA_STEP(g + 1, sA1, sB1, sA0, sB0);
+    if (g + 2 >= total) break;
+    MOE_DMA_STEP(g + 2, sA2, sB2, sA1, sB1);
+    if (g + 3 >= total) break;
+    MOE_DMA_STEP(g + 3, sA3, sB3, sA2, sB2);
+  }
+#undef MOE_DMA_STEP
+#undef MOE_DMA_NEXT
 }
 
 }  // namespace moe

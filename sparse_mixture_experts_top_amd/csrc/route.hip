@@ -13,33 +13,31 @@ namespace moe {
 
 // ------------------------------------------------------------ router GEMM ---
 
-// bf16: logits[T, E] (f32) = x[T, d] * w[E, d]^T + bias. One 128 x 128 (or
-// 64 x 128) tile per workgroup, tiles visited in XCD-aware order.
+// bf16: logits[T, E] (f32) = x[T, d] * w[E, d]^T + bias, one 128 x 128 (or
+// 64 x 128) tile per item on the persistent pipelined driver.
 template <class Cfg>
-__global__ __launch_bounds__(256) void router_gemm_bf16(const bf16_t* __restrict__ x,
-                                                        const bf16_t* __restrict__ w,
-                                                        const float* __restrict__ bias,
-                                                        float* __restrict__ logits, int T, int d,
-                                                        int E, int mt, int nt) {
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  bf16_t* smem = reinterpret_cast<bf16_t*>(smem_raw);
-  const XcdSplit sp = xcd_split(mt * nt);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int lrow = tid / Cfg::CHUNKS_PER_ROW, lcol = (tid % Cfg::CHUNKS_PER_ROW) * 8;
-  for (int item = sp.first; item < sp.end; item += sp.stride) {
+struct RouterProb {
+  const bf16_t* x;
+  const bf16_t* w;
+  const float* bias;
+  float* logits;
+  int T, d, E, nt;
+
+  __device__ __forceinline__ void setup(int item, DmaLoader<Cfg>& ld) const {
     const int m0 = (item / nt) * Cfg::BM, n0 = (item % nt) * Cfg::BN;
-    const bf16_t* a_rows[Cfg::A_LOADS];
-    const bf16_t* b_rows[Cfg::B_LOADS];
+    const int ce = dma_chunk_elem();
 #pragma unroll
-    for (int i = 0; i < Cfg::A_LOADS; ++i)
-      a_rows[i] = x + (int64_t)min(m0 + lrow + i * Cfg::ROWS_PER_PASS, T - 1) * d + lcol;
+    for (int i = 0; i < Cfg::A_DMA; ++i)
+      ld.a[i] = x + (int64_t)min(m0 + dma_row(Cfg::A_DMA, i), T - 1) * d + ce;
 #pragma unroll
-    for (int i = 0; i < Cfg::B_LOADS; ++i)
-      b_rows[i] = w + (int64_t)min(n0 + lrow + i * Cfg::ROWS_PER_PASS, E - 1) * d + lcol;
-    Acc<Cfg> acc;
-    acc.zero();
-    mainloop_nt<Cfg>(a_rows, b_rows, d, acc, smem);
+    for (int i = 0; i < Cfg::B_DMA; ++i)
+      ld.b[i] = w + (int64_t)min(n0 + dma_row(Cfg::B_DMA, i), E - 1) * d + ce;
+  }
+
+  __device__ __forceinline__ void epilogue(int item, Acc<Cfg>& acc) const {
+    const int m0 = (item / nt) * Cfg::BM, n0 = (item % nt) * Cfg::BN;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
     for (int j = 0; j < Cfg::FN; ++j) {
       const int n = n0 + frag_col<Cfg>(wn, j, lane);
@@ -54,6 +52,11 @@ __global__ __launch_bounds__(256) void router_gemm_bf16(const bf16_t* __restrict
         }
     }
   }
+};
+
+template <class Cfg>
+__global__ __launch_bounds__(256, 2) void router_gemm_bf16(RouterProb<Cfg> pb, int items) {
+  persistent_gemm_dma<Cfg>(pb, items, pb.d / Cfg::BK);
 }
 
 // fp32: one thread per logit, plain dot product (small parity workloads).
@@ -77,10 +80,10 @@ static hipError_t launch_router_bf16(const Ctx& c, const moe_shape_t& s, const b
                                      const bf16_t* w, const float* bias, float* logits) {
   const int mt = (s.T + Cfg::BM - 1) / Cfg::BM, nt = (s.E + Cfg::BN - 1) / Cfg::BN;
   const int items = mt * nt;
-  int grid = ((items + 7) / 8) * 8;
+  const int grid = std::min(((items + 7) / 8) * 8, c.num_cus * 2);
+  RouterProb<Cfg> pb{x, w, bias, logits, s.T, s.d, s.E, nt};
   TimedLaunch tl(MOE_K_ROUTER_GEMM, c.stream);
-  hipLaunchKernelGGL(router_gemm_bf16<Cfg>, dim3(grid), dim3(256), Cfg::SMEM_BYTES, c.stream, x,
-                     w, bias, logits, s.T, s.d, s.E, mt, nt);
+  hipLaunchKernelGGL(router_gemm_bf16<Cfg>, dim3(grid), dim3(256), 0, c.stream, pb, items);
   return hipGetLastError();
 }
 
@@ -89,8 +92,8 @@ hipError_t launch_router(const Ctx& c, const moe_shape_t& s, const void* x, cons
   if (s.dtype == MOE_BF16) {
     const int tiles128 = ((s.T + 127) / 128) * ((s.E + 127) / 128);
     if (tiles128 >= 2 * c.num_cus)
-      return launch_router_bf16<TileCfg<128, 128>>(c, s, (const bf16_t*)x, (const bf16_t*)w, bias, logits);
-    return launch_router_bf16<TileCfg<64, 128>>(c, s, (const bf16_t*)x, (const bf16_t*)w, bias, logits);
+      return launch_router_bf16<DmaCfg<128, 128>>(c, s, (const bf16_t*)x, (const bf16_t*)w, bias, logits);
+    return launch_router_bf16<DmaCfg<64, 128>>(c, s, (const bf16_t*)x, (const bf16_t*)w, bias, logits);
   }
   const int64_t n = (int64_t)s.T * s.E;
   TimedLaunch tl(MOE_K_ROUTER_GEMM, c.stream);

@@ -32,7 +32,7 @@ class Buffers:
     slot: torch.Tensor
     row_src: torch.Tensor
     row_gate: torch.Tensor
-    x_perm: torch.Tensor
+    x_perm: Optional[torch.Tensor]   # None: the expert GEMM gathers x through row_src
     y_perm: torch.Tensor
     act_save: Optional[torch.Tensor]
     y: torch.Tensor
@@ -42,7 +42,7 @@ class Buffers:
 
 
 def alloc(shape: B.MoeShape, lora_r: int = 0, logits: bool = False, prob: bool = False,
-          act_save: bool = False, device: str = "cuda") -> Buffers:
+          act_save: bool = False, x_perm: bool = False, device: str = "cuda") -> Buffers:
     T, d, E, k, f = shape.T, shape.d, shape.E, shape.k, shape.f
     L = shape.e_hi - shape.e_lo
     rmax = B.moe_max_rows(shape)
@@ -62,7 +62,7 @@ def alloc(shape: B.MoeShape, lora_r: int = 0, logits: bool = False, prob: bool =
         slot=torch.empty((T, k), dtype=torch.int32, **kw),
         row_src=torch.empty((max(rmax, 1),), dtype=torch.int32, **kw),
         row_gate=torch.empty((max(rmax, 1),), dtype=torch.float32, **kw),
-        x_perm=torch.empty((max(rmax, 1), d), dtype=dt, **kw),
+        x_perm=torch.empty((max(rmax, 1), d), dtype=dt, **kw) if x_perm else None,
         y_perm=torch.empty((max(rmax, 1), d), dtype=dt, **kw),
         act_save=torch.empty((max(rmax, 1), 2 * f), dtype=dt, **kw) if act_save else None,
         y=torch.empty((T, d), dtype=dt, **kw),
@@ -72,12 +72,19 @@ def alloc(shape: B.MoeShape, lora_r: int = 0, logits: bool = False, prob: bool =
     )
 
 
+def x_rows(b: Buffers, x):
+    """(rows, row index) the expert GEMM reads: the gathered copy, or x itself
+    through row_src."""
+    return (b.x_perm, None) if b.x_perm is not None else (x, b.row_src)
+
+
 def forward(b: Buffers, x, w_router, bias, w_gate, w_up, w_down, lora=None, stream=None) -> None:
     """route -> dispatch -> expert GEMM -> combine; results stay in ``b``."""
     s = b.shape
     B.moe_route(s, x, w_router, bias, b.topk_idx, b.topk_gate, b.logits, b.prob_sum, b.ws, stream)
     B.moe_dispatch(s, b.topk_idx, b.topk_gate, x, b.counts, b.offsets, b.slot, b.row_src,
                    b.row_gate, b.x_perm, b.dropped, b.ws, stream)
-    B.moe_expert_gemm(s, b.x_perm, b.offsets, w_gate, w_up, w_down, lora, b.act_save, b.y_perm,
+    xr, src = x_rows(b, x)
+    B.moe_expert_gemm(s, xr, src, b.offsets, w_gate, w_up, w_down, lora, b.act_save, b.y_perm,
                       b.ws, stream)
     B.moe_combine(s, b.y_perm, b.slot, b.topk_gate, b.y, stream)

@@ -33,9 +33,12 @@ def lora_of(w: Workload, dev: Dict[str, torch.Tensor]):
 
 
 def run_forward(w: Workload, dev: Dict[str, torch.Tensor], logits=True, prob=False,
-                act_save=False) -> layer.Buffers:
+                act_save=False, x_perm=True) -> layer.Buffers:
+    """x_perm=True materialises the dispatched rows (and checks the copy);
+    False runs the fused path the benchmark times (gather inside the GEMM)."""
     shape = layer.shape_of(w)
-    buf = layer.alloc(shape, lora_r=w.lora_r, logits=logits, prob=prob, act_save=act_save)
+    buf = layer.alloc(shape, lora_r=w.lora_r, logits=logits, prob=prob, act_save=act_save,
+                      x_perm=x_perm)
     layer.forward(buf, dev["x"], dev["w_router"], dev.get("bias"), dev["w_gate"], dev["w_up"],
                   dev["w_down"], lora_of(w, dev))
     torch.cuda.synchronize()
@@ -126,17 +129,26 @@ def check_dispatch(w: Workload, dev, buf: layer.Buffers, idx, gate):
     assert (row_gate == ref["row_gate"].astype(np.float32)).all(), "row_gate differs"
     if w.capacity > 0:
         assert int(buf.dropped.item()) == ref["dropped"]
-    xp = buf.x_perm[:R]
-    src = buf.row_src[:R].long()
-    assert torch.equal(xp, dev["x"][src]), "x_perm is not x[row_src]"
+    if buf.x_perm is not None:
+        assert torch.equal(buf.x_perm[:R], dev["x"][buf.row_src[:R].long()]), "x_perm is not x[row_src]"
     say(f"  dispatch: R={R} dropped={ref['dropped']} bit-exact")
     return ref, R
 
 
+def rows_x(w: Workload, inp, buf: layer.Buffers, rows: np.ndarray) -> np.ndarray:
+    """The expert input rows the GPU used: the gathered copy, or x[row_src]."""
+    if len(rows) == 0:
+        return np.zeros((0, w.d))
+    idx = torch.as_tensor(rows, device="cuda").long()
+    if buf.x_perm is not None:
+        return host(buf.x_perm[idx])
+    return to_f64(inp["x"])[host(buf.row_src[idx])]
+
+
 def expert_ref_rows(w: Workload, inp, buf: layer.Buffers, rows: np.ndarray, lora=None):
-    """Oracle expert output for the given dispatched rows, from the GPU x_perm."""
+    """Oracle expert output for the given dispatched rows."""
     offsets = host(buf.offsets)
-    xp = host(buf.x_perm[torch.as_tensor(rows, device="cuda").long()]) if len(rows) else np.zeros((0, w.d))
+    xp = rows_x(w, inp, buf, rows)
     out = np.zeros((len(rows), w.d))
     les = np.searchsorted(offsets, rows, side="right") - 1
     for le in np.unique(les):

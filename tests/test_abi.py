@@ -62,10 +62,10 @@ def test_null_pointers_and_small_workspace_are_rejected():
                          None) == B.MOE_ERR_WORKSPACE
     assert lib.moe_combine(ctypes.byref(s), fake, None, fake, fake, None) == B.MOE_ERR_INVALID_ARG
     lo = B.MoeLora(16, 32.0, None, None, None, None)
-    assert lib.moe_expert_gemm(ctypes.byref(s), fake, fake, fake, fake, fake, ctypes.byref(lo),
+    assert lib.moe_expert_gemm(ctypes.byref(s), fake, None, fake, fake, fake, fake, ctypes.byref(lo),
                                None, fake, fake, 1 << 30, None) == B.MOE_ERR_INVALID_ARG
     lo = B.MoeLora(16, 32.0, fake, fake, fake, fake)
-    assert lib.moe_expert_gemm(ctypes.byref(s), fake, fake, fake, fake, fake, ctypes.byref(lo),
+    assert lib.moe_expert_gemm(ctypes.byref(s), fake, None, fake, fake, fake, fake, ctypes.byref(lo),
                                None, fake, fake, 1 << 30, None) == B.MOE_ERR_UNSUPPORTED  # fp32 LoRA
     assert lib.moe_timing_read(99, None, None) == B.MOE_ERR_INVALID_ARG
 

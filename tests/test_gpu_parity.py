@@ -6,8 +6,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import (assert_close, check_dispatch, check_route, expert_ref_rows, host, run_forward,
-                      say, upload)
+from gpu_util import (assert_close, check_dispatch, check_route, expert_ref_rows, host, rows_x,
+                      run_forward, say, upload)
 from sparse_mixture_experts_top_amd import binding as B
 from sparse_mixture_experts_top_amd import layer
 from sparse_mixture_experts_top_amd.workloads import WORKLOADS, Workload, generate, to_f64
@@ -32,12 +32,12 @@ SMALL = {
 }
 
 
-def run_and_check(w, seed=0):
+def run_and_check(w, seed=0, x_perm=True):
     say(f"[case {w.name}] T={w.T} d={w.d} E={w.E} k={w.k} f={w.f} local=[{w.e_lo},{w.local_hi}) "
-        f"cap={w.capacity} dtype={w.dtype}")
+        f"cap={w.capacity} dtype={w.dtype} x_perm={x_perm}")
     inp = generate(w, seed=seed)
     dev = upload(inp)
-    buf = run_forward(w, dev)
+    buf = run_forward(w, dev, x_perm=x_perm)
     lg, idx, gate = check_route(w, inp, buf)
     ref, R = check_dispatch(w, dev, buf, idx, gate)
     rows = np.arange(R)
@@ -53,6 +53,12 @@ def run_and_check(w, seed=0):
 @pytest.mark.parametrize("name", sorted(SMALL))
 def test_stagewise_parity(name):
     run_and_check(SMALL[name])
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "ragged_bf16", "local_bf16", "rows_bf16", "capacity_bf16"])
+def test_stagewise_parity_fused_gather(name):
+    """The expert GEMM reading x through row_src (no x_perm copy)."""
+    run_and_check(SMALL[name], seed=7, x_perm=False)
 
 
 @pytest.mark.parametrize("name", ["tiny_f32", "ragged_bf16", "capacity_bf16"])
@@ -145,44 +151,45 @@ def test_capacity_one_everywhere():
     assert R == int((ref["counts"] > 0).sum())
 
 
-def test_lora_forward_backward_and_aux():
-    for b_init in ("normal", "zero"):
-        w = W("lora_small", T=256, d=128, E=12, k=4, f=128, e_lo=2, e_hi=9, lora_r=16,
-              lora_alpha=32.0, lora_b=b_init, aux_coef=0.01)
-        say(f"[case lora_small b={b_init}]")
-        inp = generate(w, seed=6)
-        dev = upload(inp)
-        buf = run_forward(w, dev, prob=True, act_save=True)
-        lg, idx, gate = check_route(w, inp, buf)
-        ref, R = check_dispatch(w, dev, buf, idx, gate)
-        lo64 = {"scale": w.lora_alpha / w.lora_r}
-        o_ref = expert_ref_rows(w, inp, buf, np.arange(R), lora=lo64)
-        assert_close(host(buf.y_perm[:R]), o_ref, "bf16", "expert rows (LoRA)", stored_bf16=True)
-        # aux loss from the GPU counts and probabilities
-        B.moe_aux_loss(buf.shape, buf.counts, buf.prob_sum, w.aux_coef, buf.aux)
-        p_ref = oracle.softmax_full(lg).sum(0)
-        assert np.abs(host(buf.prob_sum) - p_ref).max() <= 1e-5 * np.abs(p_ref).max()
-        a_ref = oracle.aux_loss(host(buf.counts), p_ref, w.T, w.k, w.aux_coef)
-        assert abs(buf.aux[0].item() - a_ref[0]) <= 1e-5 * abs(a_ref[0]) + 1e-9
-        assert abs(buf.aux[1].item() - a_ref[1]) <= 1e-5 * abs(a_ref[1])
-        # adapter gradients, oracle fed the GPU's saved G and H
-        L, r = w.L, w.lora_r
-        grads = {n: torch.empty(s, dtype=torch.float32, device="cuda") for n, s in
-                 [("da_up", (L, r, w.d)), ("db_up", (L, w.f, r)), ("da_down", (L, r, w.f)),
-                  ("db_down", (L, w.d, r))]}
-        lora = B.make_lora(r, w.lora_alpha, dev["a_up"], dev["b_up"], dev["a_down"], dev["b_down"])
-        B.moe_lora_bwd(buf.shape, lora, dev["dy"], buf.offsets, buf.row_src, buf.row_gate,
-                       buf.x_perm, buf.act_save, dev["w_down"], grads["da_up"], grads["db_up"],
-                       grads["da_down"], grads["db_down"], buf.ws)
-        torch.cuda.synchronize()
-        act = host(buf.act_save[:R])
-        lo = {"scale": w.lora_alpha / w.lora_r, **{n: to_f64(inp[n]) for n in ("a_up", "b_up", "a_down", "b_down")}}
-        g_ref = oracle.lora_backward(to_f64(inp["dy"]), host(buf.x_perm[:R]), host(buf.offsets),
-                                     host(buf.row_src[:R]), buf.row_gate[:R].cpu().numpy(),
-                                     act[:, :w.f], act[:, w.f:], to_f64(inp["w_down"]), lo)
-        for n in grads:
-            assert_close(host(grads[n]), g_ref[n], "bf16", n)
-        if b_init == "zero":
-            assert (grads["da_up"] == 0).all() and (grads["da_down"] == 0).all()
-            frozen = run_forward(w.replace(lora_r=0), dev)
-            assert torch.equal(frozen.y, buf.y)
+@pytest.mark.parametrize("b_init,x_perm", [("normal", True), ("normal", False), ("zero", False)])
+def test_lora_forward_backward_and_aux(b_init, x_perm):
+    w = W("lora_small", T=256, d=128, E=12, k=4, f=128, e_lo=2, e_hi=9, lora_r=16,
+          lora_alpha=32.0, lora_b=b_init, aux_coef=0.01)
+    say(f"[case lora_small b={b_init} x_perm={x_perm}]")
+    inp = generate(w, seed=6)
+    dev = upload(inp)
+    buf = run_forward(w, dev, prob=True, act_save=True, x_perm=x_perm)
+    lg, idx, gate = check_route(w, inp, buf)
+    ref, R = check_dispatch(w, dev, buf, idx, gate)
+    lo64 = {"scale": w.lora_alpha / w.lora_r}
+    o_ref = expert_ref_rows(w, inp, buf, np.arange(R), lora=lo64)
+    assert_close(host(buf.y_perm[:R]), o_ref, "bf16", "expert rows (LoRA)", stored_bf16=True)
+    # aux loss from the GPU counts and probabilities
+    B.moe_aux_loss(buf.shape, buf.counts, buf.prob_sum, w.aux_coef, buf.aux)
+    p_ref = oracle.softmax_full(lg).sum(0)
+    assert np.abs(host(buf.prob_sum) - p_ref).max() <= 1e-5 * np.abs(p_ref).max()
+    a_ref = oracle.aux_loss(host(buf.counts), p_ref, w.T, w.k, w.aux_coef)
+    assert abs(buf.aux[0].item() - a_ref[0]) <= 1e-5 * abs(a_ref[0]) + 1e-9
+    assert abs(buf.aux[1].item() - a_ref[1]) <= 1e-5 * abs(a_ref[1])
+    # adapter gradients, oracle fed the GPU's saved G and H
+    L, r = w.L, w.lora_r
+    grads = {n: torch.empty(s, dtype=torch.float32, device="cuda") for n, s in
+             [("da_up", (L, r, w.d)), ("db_up", (L, w.f, r)), ("da_down", (L, r, w.f)),
+              ("db_down", (L, w.d, r))]}
+    lora = B.make_lora(r, w.lora_alpha, dev["a_up"], dev["b_up"], dev["a_down"], dev["b_down"])
+    xr, xs = layer.x_rows(buf, dev["x"])
+    B.moe_lora_bwd(buf.shape, lora, dev["dy"], buf.offsets, buf.row_src, buf.row_gate, xr, xs,
+                   buf.act_save, dev["w_down"], grads["da_up"], grads["db_up"], grads["da_down"],
+                   grads["db_down"], buf.ws)
+    torch.cuda.synchronize()
+    act = host(buf.act_save[:R])
+    lo = {"scale": w.lora_alpha / w.lora_r, **{n: to_f64(inp[n]) for n in ("a_up", "b_up", "a_down", "b_down")}}
+    g_ref = oracle.lora_backward(to_f64(inp["dy"]), rows_x(w, inp, buf, np.arange(R)), host(buf.offsets),
+                                 host(buf.row_src[:R]), buf.row_gate[:R].cpu().numpy(),
+                                 act[:, :w.f], act[:, w.f:], to_f64(inp["w_down"]), lo)
+    for n in grads:
+        assert_close(host(grads[n]), g_ref[n], "bf16", n)
+    if b_init == "zero":
+        assert (grads["da_up"] == 0).all() and (grads["da_down"] == 0).all()
+        frozen = run_forward(w.replace(lora_r=0), dev, x_perm=x_perm)
+        assert torch.equal(frozen.y, buf.y)

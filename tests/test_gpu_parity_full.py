@@ -7,8 +7,9 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import (assert_close, check_dispatch, check_route, expert_ref_rows, host, run_forward,
-                      say, upload)
+from gpu_util import (assert_close, check_dispatch, check_route, expert_ref_rows, host, rows_x,
+                      run_forward, say, upload)
+from sparse_mixture_experts_top_amd import layer
 from sparse_mixture_experts_top_amd import binding as B
 from sparse_mixture_experts_top_amd.workloads import WORKLOADS, generate, to_f64
 
@@ -31,7 +32,8 @@ def full_case(name, prob=False, act_save=False):
     say(f"[case {name}] T={w.T} d={w.d} E={w.E} k={w.k} f={w.f} L={w.L} cap={w.capacity}")
     inp = generate(w, seed=0)
     dev = upload(inp)
-    buf = run_forward(w, dev, prob=prob, act_save=act_save)
+    # the fused-gather path, as bench.py runs it
+    buf = run_forward(w, dev, prob=prob, act_save=act_save, x_perm=False)
     rng = np.random.default_rng(123)
     ts = np.sort(rng.choice(w.T, 48, replace=False))
     lg, idx, gate = check_route(w, inp, buf, sample_tokens=ts)
@@ -64,7 +66,8 @@ def test_lora_step_full():
     grads = {n: torch.empty(s, dtype=torch.float32, device="cuda") for n, s in
              [("da_up", (L, r, d)), ("db_up", (L, f, r)), ("da_down", (L, r, f)), ("db_down", (L, d, r))]}
     lora = B.make_lora(r, w.lora_alpha, dev["a_up"], dev["b_up"], dev["a_down"], dev["b_down"])
-    B.moe_lora_bwd(buf.shape, lora, dev["dy"], buf.offsets, buf.row_src, buf.row_gate, buf.x_perm,
+    xr, xs = layer.x_rows(buf, dev["x"])
+    B.moe_lora_bwd(buf.shape, lora, dev["dy"], buf.offsets, buf.row_src, buf.row_gate, xr, xs,
                    buf.act_save, dev["w_down"], grads["da_up"], grads["db_up"], grads["da_down"],
                    grads["db_down"], buf.ws)
     torch.cuda.synchronize()
@@ -76,7 +79,7 @@ def test_lora_step_full():
         act = host(buf.act_save[sl])
         lo = {"scale": w.lora_alpha / r,
               **{n: to_f64(inp[n][le:le + 1]) for n in ("a_up", "b_up", "a_down", "b_down")}}
-        g_ref = oracle.lora_backward(dy64, host(buf.x_perm[sl]), np.array([0, b - a]),
+        g_ref = oracle.lora_backward(dy64, rows_x(w, inp, buf, np.arange(a, b)), np.array([0, b - a]),
                                      host(buf.row_src[sl]), buf.row_gate[sl].cpu().numpy(),
                                      act[:, :f], act[:, f:], to_f64(inp["w_down"][le:le + 1]), lo)
         say(f"  expert {le}: {b - a} rows")
