@@ -101,15 +101,22 @@ def cpu_baseline(w, inp):
 
 
 def calibrate_copy(nbytes: int = 1 << 30, reps: int = 5) -> None:
-    """A plain elementwise copy of known size, for scaling FETCH_SIZE / WRITE_SIZE."""
+    """A plain elementwise copy of known size, for scaling FETCH_SIZE / WRITE_SIZE;
+    also prints the copy's own bandwidth (a practical HBM ceiling on this machine)."""
     import torch
     n = nbytes // 4
     a = torch.randn(n, device="cuda")
     b = torch.empty_like(a)
-    for _ in range(reps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for i in range(reps):
+        if i == reps - 1:
+            ev[0].record()
         torch.mul(a, 1.0, out=b)
+    ev[1].record()
     torch.cuda.synchronize()
-    log(f"[calibrate] {reps} copies of {nbytes} bytes read + {nbytes} bytes written")
+    ms = ev[0].elapsed_time(ev[1])
+    log(f"[calibrate] {reps} copies of {nbytes} bytes read + {nbytes} bytes written; "
+        f"last copy {ms:.3f} ms = {2 * nbytes / ms / 1e6:.0f} GB/s")
 
 
 def main() -> int:

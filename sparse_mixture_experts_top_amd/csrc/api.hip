@@ -59,7 +59,8 @@ Workspace carve_workspace(const moe_shape_t& s, int lora_r, void* base) {
     w.du = static_cast<float*>(take(rmax * s.f * 4));
   }
   w.logits = static_cast<float*>(take((int64_t)s.T * s.E * 4));
-  w.prob_part = static_cast<float*>(take(((int64_t)s.T + kTopkTokPerBlock - 1) / kTopkTokPerBlock * s.E * 4));
+  const int64_t tok_per_blk = 4 * kTopkTokPerWaveProb;
+  w.prob_part = static_cast<float*>(take(((int64_t)s.T + tok_per_blk - 1) / tok_per_blk * s.E * 4));
   w.bytes = off;
   return w;
 }

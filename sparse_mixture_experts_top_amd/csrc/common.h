@@ -104,7 +104,7 @@ struct Workspace {
 };
 
 constexpr int kTokTile = 256;      // tokens per dispatch tile
-constexpr int kTopkTokPerBlock = 16;  // tokens per top-k block (4 waves x 4)
+constexpr int kTopkTokPerWaveProb = 4;  // tokens per top-k wave when softmax sums are kept
 constexpr int kGemmBM = 128;       // grouped GEMM row tile
 
 Workspace carve_workspace(const moe_shape_t& s, int lora_r, void* base);

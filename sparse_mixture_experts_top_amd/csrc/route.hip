@@ -126,30 +126,61 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
+// Bitonic sort of one 64-bit key per lane across the wave, descending by
+// lane (lane 0 ends with the largest key).
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+    for (int j = size >> 1; j >= 1; j >>= 1) {
+      const uint32_t lo = __shfl_xor((uint32_t)v, j, kWave);
+      const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), j, kWave);
+      const uint64_t o = ((uint64_t)hi << 32) | lo;
+      // descending overall: blocks with (lane & size) == 0 sort descending
+      const bool desc = (lane & size) == 0;
+      const bool lower = (lane & j) == 0;
+      const bool take_max = (desc == lower);
+      const uint64_t mx = o > v ? o : v, mn = o > v ? v : o;
+      v = take_max ? mx : mn;
+    }
+  }
+  return v;
+}
+
 // One wave per token. Lane l holds the logits of experts l, l+64, ... as
-// 64-bit keys (ordered logit bits << 32 | ~expert) so that the largest key is
-// the largest logit and, among equal logits, the lowest expert id. k rounds of
-// "lane maximum, then wave maximum" pick the experts in order; lane j keeps
-// the j-th pick. Gates: exp(l_j - l_0) / sum over the picks. With prob_part,
-// the wave also accumulates the full softmax of its tokens per expert; the
-// block's four waves are summed in a fixed order into prob_part[block, E].
-template <int EPL>
+// 64-bit keys (ordered logit bits << 32 | ~expert): the largest key is the
+// largest logit and, among equal logits, the lowest expert id; keys are
+// unique. The k largest keys are found exactly in three steps:
+//   1. tau = k-th largest of the 64 lane maxima (bitwise search with ballot
+//      counts, no cross-lane shuffles). At least k keys (those maxima) are
+//      >= tau, so every one of the k largest keys is >= tau.
+//   2. keys >= tau are compacted through LDS (ballot + popcount positions).
+//   3. if at most 64 survive, one bitonic sort across the wave orders them
+//      and lanes 0..k-1 hold the answer; otherwise (many equal logits) k
+//      rounds of "wave maximum, remove it" over all keys.
+// Gates: exp(l_j - l_0) / sum over the picks. With prob_part, the wave also
+// sums the full softmax of its tokens per expert; the block's waves are added
+// in a fixed order into prob_part[block, E].
+template <int EPL, int TPW>
 __global__ __launch_bounds__(256) void topk_softmax(const float* __restrict__ logits, int T, int E,
                                                     int k, int32_t* __restrict__ idx_out,
                                                     float* __restrict__ gate_out,
                                                     float* __restrict__ prob_part) {
+  __shared__ uint64_t cand[4][64];
   __shared__ float red[4][EPL * 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));  // lanes < this one
   float psum[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) psum[i] = 0.f;
-  constexpr int kTokPerWave = kTopkTokPerBlock / 4;
-  for (int q = 0; q < kTokPerWave; ++q) {
-    const int t = blockIdx.x * kTopkTokPerBlock + wave * kTokPerWave + q;
+  for (int q = 0; q < TPW; ++q) {
+    const int t = (blockIdx.x * 4 + wave) * TPW + q;
     if (t >= T) break;
     const float* row = logits + (int64_t)t * E;
     uint64_t key[EPL];
     float val[EPL];
+    uint64_t lmax = 0;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       const int e = lane + 64 * i;
@@ -160,24 +191,51 @@ __global__ __launch_bounds__(256) void topk_softmax(const float* __restrict__ lo
         val[i] = 0.f;
         key[i] = 0;
       }
+      lmax = key[i] > lmax ? key[i] : lmax;
     }
-    int my_idx = 0;
-    float my_logit = 0.f, top = 0.f;
-    for (int j = 0; j < k; ++j) {
-      uint64_t best = 0;
+    // 1. tau: largest value with at least k lane maxima >= it (a key value)
+    uint64_t tau = 0;
+    for (int b = 63; b >= 0; --b) {
+      const uint64_t c = tau | (1ull << b);
+      if (__popcll(__ballot(lmax >= c)) >= k) tau = c;
+    }
+    // 2. candidates
+    int n = 0;
 #pragma unroll
-      for (int i = 0; i < EPL; ++i) best = key[i] > best ? key[i] : best;
-      const uint64_t win = wave_max_u64(best);
+    for (int i = 0; i < EPL; ++i) n += __popcll(__ballot(key[i] >= tau));
+    uint64_t mine = 0;  // this lane's key after selection (lanes 0..k-1)
+    if (n <= 64) {
+      int base = 0;
 #pragma unroll
-      for (int i = 0; i < EPL; ++i)
-        if (key[i] == win) key[i] = 0;  // keys are unique: only the owner matches
-      const float v = from_ordered((uint32_t)(win >> 32));
-      if (j == 0) top = v;
-      if (lane == j) {
-        my_idx = (int)(0xffffffffu - (uint32_t)win);
-        my_logit = v;
+      for (int i = 0; i < EPL; ++i) {
+        const bool in = key[i] >= tau;
+        const uint64_t bal = __ballot(in);
+        if (in) cand[wave][base + __popcll(bal & below)] = key[i];
+        base += __popcll(bal);
+      }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      const uint64_t v = lane < n ? cand[wave][lane] : 0ull;
+      __builtin_amdgcn_wave_barrier();
+      mine = wave_sort_desc(v);
+    } else {
+      uint64_t kk[EPL];
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) kk[i] = key[i];
+      for (int j = 0; j < k; ++j) {
+        uint64_t best = 0;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) best = kk[i] > best ? kk[i] : best;
+        const uint64_t win = wave_max_u64(best);
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+          if (kk[i] == win) kk[i] = 0;
+        if (lane == j) mine = win;
       }
     }
+    const float top = from_ordered((uint32_t)(__shfl(mine, 0, kWave) >> 32));
+    const float my_logit = from_ordered((uint32_t)(mine >> 32));
+    const int my_idx = (int)(0xffffffffu - (uint32_t)mine);
     const float ex = lane < k ? expf(my_logit - top) : 0.f;
     const float den = wave_sum(ex);
     if (lane < k) {
@@ -217,17 +275,26 @@ __global__ __launch_bounds__(256) void prob_reduce(const float* __restrict__ par
 
 hipError_t launch_topk(const Ctx& c, const moe_shape_t& s, const float* logits, int32_t* idx,
                        float* gate, float* prob_part, float* prob_sum) {
-  const int nblk = (s.T + kTopkTokPerBlock - 1) / kTopkTokPerBlock;
+  // one token per wave; with the softmax sums requested, four tokens per wave
+  // so the per-block partial sums stay small
+  const int tpw = prob_sum ? kTopkTokPerWaveProb : 1;
+  const int nblk = (s.T + 4 * tpw - 1) / (4 * tpw);
   const int epl = (s.E + 63) / 64;
   float* part = prob_sum ? prob_part : nullptr;
   if (nblk > 0) {
     TimedLaunch tl(MOE_K_TOPK, c.stream);
-#define MOE_TOPK(N) \
-  hipLaunchKernelGGL(topk_softmax<N>, dim3(nblk), dim3(256), 0, c.stream, logits, s.T, s.E, s.k, idx, gate, part)
+#define MOE_TOPK(N)                                                                                  \
+  if (prob_sum)                                                                                      \
+    hipLaunchKernelGGL((topk_softmax<N, kTopkTokPerWaveProb>), dim3(nblk), dim3(256), 0, c.stream,    \
+                       logits, s.T, s.E, s.k, idx, gate, part);                                      \
+  else                                                                                               \
+    hipLaunchKernelGGL((topk_softmax<N, 1>), dim3(nblk), dim3(256), 0, c.stream, logits, s.T, s.E,    \
+                       s.k, idx, gate, part)
     if (epl <= 1) MOE_TOPK(1);
     else if (epl <= 2) MOE_TOPK(2);
     else if (epl <= 4) MOE_TOPK(4);
     else if (epl <= 8) MOE_TOPK(8);
+    else if (epl <= 14) MOE_TOPK(14);
     else MOE_TOPK(16);
 #undef MOE_TOPK
   }
