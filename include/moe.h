@@ -185,6 +185,32 @@ moe_status_t moe_expert_gemm(const moe_shape_t* shape, const void* x, const int3
                              const void* w_down, const moe_lora_t* lora, void* act_save,
                              void* y_perm, void* ws, size_t ws_bytes, moe_stream_t stream);
 
+/* Packed expert weights. The expert weights are frozen, so they can be stored
+ * once in the order the grouped GEMM streams them: every weight tile one
+ * GEMM step reads (128 rows x 32 K values, bf16) becomes one contiguous 8 KB
+ * block laid out exactly as it sits in LDS. Packing is a pure permutation
+ * (bitwise equal values); packed buffers have the sizes of the originals.
+ *   gu_packed   [L, 2f, d] elements: tile (le, b, kt) for b < f/64, kt < d/32
+ *               holds rows 16q..16q+15 of w_gate[le] block b and the same
+ *               rows of w_up[le], interleaved per 16 (q = 0..3), K values
+ *               32kt..32kt+31
+ *   down_packed [L, d, f]  elements: tile (le, b, kt) for b < d/128, kt < f/32
+ *               holds rows 128b..128b+127 of w_down[le], K values 32kt..32kt+31
+ * Within a tile, row r's 16-byte chunk c (K values 8c..8c+7) is stored at
+ * chunk position c ^ ((r >> 2) & 3) of the row.
+ * bf16 only, d % 128 == 0. Either output may be NULL (that input is then
+ * not read). */
+moe_status_t moe_pack_expert_weights(const moe_shape_t* shape, const void* w_gate, const void* w_up,
+                                     const void* w_down, void* gu_packed, void* down_packed,
+                                     moe_stream_t stream);
+
+/* moe_expert_gemm with packed weights (same results, bitwise): the weight
+ * tiles are read as contiguous blocks. */
+moe_status_t moe_expert_gemm_packed(const moe_shape_t* shape, const void* x, const int32_t* row_src,
+                                    const int32_t* offsets, const void* gu_packed,
+                                    const void* down_packed, const moe_lora_t* lora, void* act_save,
+                                    void* y_perm, void* ws, size_t ws_bytes, moe_stream_t stream);
+
 /* Combine ("Full-Stack Engineering Guide", §2.1: results are gathered back
  * and weighted by g_i).
  *   y_perm    [Rmax, d]        from moe_expert_gemm

@@ -15,7 +15,8 @@ from typing import Optional
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmoe_mi355x.so")
+# MOE_MI355X_LIB selects another build of the same library (e.g. a tuning variant)
+LIB_PATH = os.environ.get("MOE_MI355X_LIB") or os.path.join(_PKG, "libmoe_mi355x.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
@@ -25,8 +26,8 @@ KERNELS = ["router_gemm", "topk", "prob_reduce", "hist", "scan", "scatter", "cap
            "lora_grad"]
 
 EXPORTED = ["moe_workspace_bytes", "moe_max_rows", "moe_last_error", "moe_route",
-            "moe_dispatch", "moe_expert_gemm", "moe_combine", "moe_aux_loss", "moe_lora_bwd",
-            "moe_timing_enable", "moe_timing_read"]
+            "moe_dispatch", "moe_expert_gemm", "moe_pack_expert_weights", "moe_expert_gemm_packed",
+            "moe_combine", "moe_aux_loss", "moe_lora_bwd", "moe_timing_enable", "moe_timing_read"]
 
 
 class MoeShape(ctypes.Structure):
@@ -65,13 +66,16 @@ def lib() -> ctypes.CDLL:
     L.moe_route.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_dispatch.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_expert_gemm.argtypes = [shp, vp, vp, vp, vp, vp, vp, lor, vp, vp, vp, sz, vp]
+    L.moe_pack_expert_weights.argtypes = [shp, vp, vp, vp, vp, vp, vp]
+    L.moe_expert_gemm_packed.argtypes = [shp, vp, vp, vp, vp, vp, lor, vp, vp, vp, sz, vp]
     L.moe_combine.argtypes = [shp, vp, vp, vp, vp, vp]
     L.moe_aux_loss.argtypes = [shp, vp, vp, f32, vp, vp]
     L.moe_lora_bwd.argtypes = [shp, lor, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_timing_enable.argtypes = [i32]
     L.moe_timing_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
-    for fn in ("moe_route", "moe_dispatch", "moe_expert_gemm", "moe_combine", "moe_aux_loss",
-               "moe_lora_bwd", "moe_timing_enable", "moe_timing_read"):
+    for fn in ("moe_route", "moe_dispatch", "moe_expert_gemm", "moe_pack_expert_weights",
+               "moe_expert_gemm_packed", "moe_combine", "moe_aux_loss", "moe_lora_bwd",
+               "moe_timing_enable", "moe_timing_read"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
     return L
@@ -148,6 +152,24 @@ def moe_expert_gemm(shape, x, row_src, offsets, w_gate, w_up, w_down, lora, act_
                                  _dev(w_down, dt), ctypes.byref(lora) if lora is not None else None,
                                  _dev(act_save, dt), _dev(y_perm, dt), _dev(ws, torch.uint8),
                                  ws.numel(), _stream(stream)))
+
+
+def moe_pack_expert_weights(shape, w_gate, w_up, w_down, gu_packed, down_packed, stream=None):
+    bf = torch.bfloat16
+    _check(lib().moe_pack_expert_weights(ctypes.byref(shape), _dev(w_gate, bf), _dev(w_up, bf),
+                                         _dev(w_down, bf), _dev(gu_packed, bf), _dev(down_packed, bf),
+                                         _stream(stream)))
+
+
+def moe_expert_gemm_packed(shape, x, row_src, offsets, gu_packed, down_packed, lora, act_save, y_perm,
+                           ws, stream=None):
+    bf = torch.bfloat16
+    _check(lib().moe_expert_gemm_packed(ctypes.byref(shape), _dev(x, bf), _dev(row_src, torch.int32),
+                                        _dev(offsets, torch.int32), _dev(gu_packed, bf),
+                                        _dev(down_packed, bf),
+                                        ctypes.byref(lora) if lora is not None else None,
+                                        _dev(act_save, bf), _dev(y_perm, bf), _dev(ws, torch.uint8),
+                                        ws.numel(), _stream(stream)))
 
 
 def moe_combine(shape, y_perm, slot, topk_gate, y, stream=None):

@@ -292,9 +292,65 @@ moe_status_t moe_expert_gemm(const moe_shape_t* shape, const void* x, const int3
     la.a_down = static_cast<const bf16_t*>(lora->a_down);
     la.b_down = static_cast<const bf16_t*>(lora->b_down);
   }
-  return hip_status(launch_expert_gemm(c, s, w, x, row_src, offsets, w_gate, w_up, w_down,
+  return hip_status(launch_expert_gemm(c, s, w, x, row_src, offsets, nullptr, nullptr, w_gate, w_up, w_down,
                                        lora ? &la : nullptr, act_save, y_perm),
                     "expert GEMM");
+}
+
+static moe_status_t check_packable(const moe_shape_t& s) {
+  if (s.dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "packed weights need dtype MOE_BF16");
+  if (s.d % 128 != 0) return fail(MOE_ERR_UNSUPPORTED, "packed weights need d % 128 == 0");
+  return MOE_OK;
+}
+
+moe_status_t moe_pack_expert_weights(const moe_shape_t* shape, const void* w_gate, const void* w_up,
+                                     const void* w_down, void* gu_packed, void* down_packed,
+                                     moe_stream_t stream) {
+  moe_status_t st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape_t& s = *shape;
+  if ((st = check_packable(s)) != MOE_OK) return st;
+  if (!gu_packed && !down_packed) return fail(MOE_ERR_INVALID_ARG, "no output requested");
+  MOE_REQUIRE_IF(gu_packed, w_gate, "w_gate");
+  MOE_REQUIRE_IF(gu_packed, w_up, "w_up");
+  MOE_REQUIRE_IF(down_packed, w_down, "w_down");
+  Ctx c;
+  if ((st = make_ctx(stream, &c)) != MOE_OK) return st;
+  return hip_status(launch_pack(c, s, w_gate, w_up, w_down, gu_packed, down_packed), "pack");
+}
+
+moe_status_t moe_expert_gemm_packed(const moe_shape_t* shape, const void* x, const int32_t* row_src,
+                                    const int32_t* offsets, const void* gu_packed,
+                                    const void* down_packed, const moe_lora_t* lora, void* act_save,
+                                    void* y_perm, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  moe_status_t st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape_t& s = *shape;
+  if ((st = check_packable(s)) != MOE_OK) return st;
+  const bool rows = max_rows(s) > 0;
+  MOE_REQUIRE_IF(rows, x, "x");
+  MOE_REQUIRE(offsets, "offsets");
+  MOE_REQUIRE(gu_packed, "gu_packed");
+  MOE_REQUIRE(down_packed, "down_packed");
+  MOE_REQUIRE_IF(rows, y_perm, "y_perm");
+  if ((st = check_lora(s, lora)) != MOE_OK) return st;
+  const int r = lora ? lora->r : 0;
+  if ((st = check_ws(s, r, ws, ws_bytes)) != MOE_OK) return st;
+  Ctx c;
+  if ((st = make_ctx(stream, &c)) != MOE_OK) return st;
+  const Workspace w = carve_workspace(s, r, ws);
+  LoraArgs la{};
+  if (lora) {
+    la.r = lora->r;
+    la.scale = lora->alpha / (float)lora->r;
+    la.a_up = static_cast<const bf16_t*>(lora->a_up);
+    la.b_up = static_cast<const bf16_t*>(lora->b_up);
+    la.a_down = static_cast<const bf16_t*>(lora->a_down);
+    la.b_down = static_cast<const bf16_t*>(lora->b_down);
+  }
+  return hip_status(launch_expert_gemm(c, s, w, x, row_src, offsets, gu_packed, down_packed, nullptr,
+                                       nullptr, nullptr, lora ? &la : nullptr, act_save, y_perm),
+                    "expert GEMM (packed)");
 }
 
 moe_status_t moe_combine(const moe_shape_t* shape, const void* y_perm, const int32_t* slot,

@@ -39,8 +39,7 @@ __global__ __launch_bounds__(256) void combine_bf16(const bf16_t* __restrict__ y
       }
       uint32_t o[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        o[u] = (uint32_t)f32_to_bf16(acc[2 * u]) | ((uint32_t)f32_to_bf16(acc[2 * u + 1]) << 16);
+      for (int u = 0; u < 4; ++u) o[u] = f32x2_to_bf16x2(acc[2 * u], acc[2 * u + 1]);
       *reinterpret_cast<uint4*>(y + (int64_t)t * d + v * 8) = make_uint4(o[0], o[1], o[2], o[3]);
     }
     __syncthreads();

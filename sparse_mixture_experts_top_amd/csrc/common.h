@@ -7,13 +7,16 @@
 #include <algorithm>
 #include <stdint.h>
 
-#include "../../include/moe.h"
+#include "moe.h"
 
 namespace moe {
 
 typedef uint16_t bf16_t;  // bfloat16 bit pattern in memory
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// 16 bytes as a native vector (HIP's uint4 is a struct, which keeps arrays of
+// it from being promoted to registers).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
@@ -23,12 +26,17 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-// Round to nearest, ties to even (NaN stays NaN).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Round to nearest, ties to even: gfx950's packed convert instruction
+// (v_cvt_pk_bf16_f32), which rounds exactly like the textbook bit
+// manipulation (u + 0x7fff + lsb) >> 16 for every finite value and infinity.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), bf16x2_t));
+}
 __device__ __forceinline__ bf16_t f32_to_bf16(float v) {
-  uint32_t u = __float_as_uint(v);
-  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return static_cast<bf16_t>((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<bf16_t>(u >> 16);
+  return static_cast<bf16_t>(f32x2_to_bf16x2(v, 0.f));
 }
 
 template <class T> __device__ __forceinline__ float load_f(const T* p);
@@ -40,6 +48,11 @@ template <> __device__ __forceinline__ void store_f<float>(float* p, float v) { 
 template <> __device__ __forceinline__ void store_f<bf16_t>(bf16_t* p, float v) { *p = f32_to_bf16(v); }
 
 __device__ __forceinline__ float silu_f(float a) { return a / (1.0f + expf(-a)); }
+
+// Four floats -> four bf16 (round to nearest even) packed in 8 bytes.
+__device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) {
+  return make_uint2(f32x2_to_bf16x2(a, b), f32x2_to_bf16x2(c, d));
+}
 
 // Index of the row block containing row p: largest le with off[le] <= p
 // (off has L+1 non-decreasing entries, off[0] = 0, p < off[L]).
@@ -137,9 +150,12 @@ struct LoraArgs {
 
 hipError_t launch_expert_gemm(const Ctx& c, const moe_shape_t& s, const Workspace& ws,
                               const void* x_rows, const int32_t* row_src, const int32_t* offsets,
-                              const void* w_gate,
+                              const void* gu_packed, const void* d_packed, const void* w_gate,
                               const void* w_up, const void* w_down, const LoraArgs* lora,
                               void* act_save, void* y_perm);
+
+hipError_t launch_pack(const Ctx& c, const moe_shape_t& s, const void* w_gate, const void* w_up,
+                       const void* w_down, void* gu_packed, void* d_packed);
 
 hipError_t launch_row_tiles(const Ctx& c, const int32_t* offsets, int L, int max_tiles,
                             int32_t* tiles);

@@ -87,6 +87,7 @@ struct GateUpProb {
   const int32_t* tiles;
   const bf16_t* w_gate;
   const bf16_t* w_up;
+  const bf16_t* w_packed;  // packed gate/up tiles, or NULL for row-major w_gate / w_up
   int d, f, nt;
   const float* zu;
   const bf16_t* b_up;
@@ -106,6 +107,13 @@ struct GateUpProb {
       const int64_t src = row_src ? (int64_t)row_src[row] : row;
       ld.a[i] = x + src * d + ce;
     }
+    if (w_packed) {
+      const bf16_t* tile0 = w_packed + ((int64_t)t.le * nt + ni) * (d / Cfg::BK) * kPackTileElems;
+#pragma unroll
+      for (int i = 0; i < Cfg::B_DMA; ++i) ld.b[i] = packed_b_ptr<Cfg>(tile0, i);
+      ld.b_kstep = kPackTileElems;
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < Cfg::B_DMA; ++i) {
       const int jb = dma_row(Cfg::B_DMA, i);
@@ -115,39 +123,54 @@ struct GateUpProb {
     }
   }
 
-  __device__ __forceinline__ void epilogue(int item, Acc<Cfg>& acc) const {
+  // Returns the store instructions this wave issued: one per (fragment pair,
+  // fragment row block with a valid row) and stored tensor, or -1 with LoRA
+  // (the epilogue then also loads).
+  __device__ __forceinline__ int epilogue(int item, Acc<Cfg>& acc) const {
     const RowTile t = row_tile<Cfg::BM>(tiles, offsets, item / nt);
     const int ni = item % nt;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave >> 1, wn = wave & 1;
+    int nfrag = 0;
 #pragma unroll
-    for (int jj = 0; jj < Cfg::FN; jj += 2) {
-      const int jg = wn * Cfg::FN + jj;  // even: G fragment, jg + 1: U fragment
-      const int fcol = ni * HALF + (jg >> 1) * 16 + (lane & 15);
+    for (int i = 0; i < Cfg::FM; ++i) {
+      const int base = wm * (Cfg::BM / 2) + i * 16;  // wave-uniform
+      if (base >= t.valid) continue;
+      ++nfrag;
+      const int rin = base + (lane & 15);
+      const bool ok = rin < t.valid;
+      const int64_t row = t.row0 + rin;
 #pragma unroll
-      for (int i = 0; i < Cfg::FM; ++i)
+      for (int jj = 0; jj < Cfg::FN; jj += 2) {
+        // fragment jg (even) holds G, jg + 1 holds U, for the same 16 FFN columns
+        const int jg = wn * Cfg::FN + jj;
+        const int fcol = ni * HALF + (jg >> 1) * 16 + (lane >> 4) * 4;
+        float h[4], g[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int rin = frag_row<Cfg>(wm, i, lane, q);
-          if (rin >= t.valid) continue;
-          const int64_t row = t.row0 + rin;
-          const float g = acc.v[i][jj][q];
+          g[q] = acc.v[i][jj][q];
           float u = acc.v[i][jj + 1][q];
-          if (zu) {
+          if (zu && ok) {
             const float* z = zu + row * r;
-            const bf16_t* bu = b_up + ((int64_t)t.le * f + fcol) * r;
+            const bf16_t* bu = b_up + ((int64_t)t.le * f + fcol + q) * r;
             float s = 0.f;
             for (int c = 0; c < r; ++c) s = fmaf(z[c], bf16_to_f32(bu[c]), s);
             u = fmaf(scale, s, u);
           }
-          const bf16_t h = f32_to_bf16(silu_f(g) * u);
-          hbuf[row * f + fcol] = h;
+          h[q] = silu_f(g[q]) * u;
+        }
+        if (ok) {
+          const uint2 hv = pack4_bf16(h[0], h[1], h[2], h[3]);
+          *reinterpret_cast<uint2*>(hbuf + row * f + fcol) = hv;
           if (act_save) {
-            act_save[row * 2 * f + fcol] = f32_to_bf16(g);
-            act_save[row * 2 * f + f + fcol] = h;
+            *reinterpret_cast<uint2*>(act_save + row * 2 * f + fcol) = pack4_bf16(g[0], g[1], g[2], g[3]);
+            *reinterpret_cast<uint2*>(act_save + row * 2 * f + f + fcol) = hv;
           }
         }
+      }
     }
+    if (zu) return -1;
+    return nfrag * (Cfg::FN / 2) * (act_save ? 3 : 1);
   }
 };
 
@@ -164,6 +187,7 @@ struct DownProb {
   const int32_t* offsets;
   const int32_t* tiles;
   const bf16_t* w_down;
+  const bf16_t* w_packed;  // packed down tiles, or NULL for row-major w_down
   int d, f, nt;
   const float* zd;
   const bf16_t* b_down;
@@ -178,38 +202,55 @@ struct DownProb {
 #pragma unroll
     for (int i = 0; i < Cfg::A_DMA; ++i)
       ld.a[i] = hbuf + (t.row0 + min(dma_row(Cfg::A_DMA, i), t.valid - 1)) * f + ce;
+    if (w_packed) {
+      const bf16_t* tile0 = w_packed + ((int64_t)t.le * nt + item % nt) * (f / Cfg::BK) * kPackTileElems;
+#pragma unroll
+      for (int i = 0; i < Cfg::B_DMA; ++i) ld.b[i] = packed_b_ptr<Cfg>(tile0, i);
+      ld.b_kstep = kPackTileElems;
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < Cfg::B_DMA; ++i)
       ld.b[i] = w_down + ((int64_t)t.le * d + min(n0 + dma_row(Cfg::B_DMA, i), d - 1)) * f + ce;
   }
 
-  __device__ __forceinline__ void epilogue(int item, Acc<Cfg>& acc) const {
+  // Returns the store instructions this wave issued (one per fragment with a
+  // valid row and valid columns), or -1 with LoRA (the epilogue then loads).
+  __device__ __forceinline__ int epilogue(int item, Acc<Cfg>& acc) const {
     const RowTile t = row_tile<Cfg::BM>(tiles, offsets, item / nt);
     const int n0 = (item % nt) * Cfg::BN;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave >> 1, wn = wave & 1;
+    int nst = 0;
 #pragma unroll
-    for (int j = 0; j < Cfg::FN; ++j) {
-      const int n = n0 + frag_col<Cfg>(wn, j, lane);
-      if (n >= d) continue;
+    for (int i = 0; i < Cfg::FM; ++i) {
+      const int base = wm * (Cfg::BM / 2) + i * 16;  // wave-uniform
+      if (base >= t.valid) continue;
+      const int rin = base + (lane & 15);
+      const bool ok = rin < t.valid;
+      const int64_t row = t.row0 + rin;
 #pragma unroll
-      for (int i = 0; i < Cfg::FM; ++i)
+      for (int j = 0; j < Cfg::FN; ++j) {
+        // d % 64 == 0: a wave's 16-column fragment is all valid or all not
+        if (n0 + wn * (Cfg::BN / 2) + j * 16 >= d) continue;
+        ++nst;
+        const int n = n0 + dma_out_col<Cfg>(wn, j, lane);
+        float o[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int rin = frag_row<Cfg>(wm, i, lane, q);
-          if (rin >= t.valid) continue;
-          const int64_t row = t.row0 + rin;
-          float o = acc.v[i][j][q];
-          if (zd) {
+          o[q] = acc.v[i][j][q];
+          if (zd && ok) {
             const float* z = zd + row * r;
-            const bf16_t* bd = b_down + ((int64_t)t.le * d + n) * r;
+            const bf16_t* bd = b_down + ((int64_t)t.le * d + n + q) * r;
             float s = 0.f;
             for (int c = 0; c < r; ++c) s = fmaf(z[c], bf16_to_f32(bd[c]), s);
-            o = fmaf(scale, s, o);
+            o[q] = fmaf(scale, s, o[q]);
           }
-          y_perm[row * d + n] = f32_to_bf16(o);
         }
+        if (ok) *reinterpret_cast<uint2*>(y_perm + row * d + n) = pack4_bf16(o[0], o[1], o[2], o[3]);
+      }
     }
+    return zd ? -1 : nst;
   }
 };
 
@@ -217,6 +258,66 @@ template <class Cfg>
 __global__ __launch_bounds__(256, 2) void down_bf16(DownProb<Cfg> pb, int max_tiles) {
   const int items = ld_uniform(pb.tiles, 2 * max_tiles) * pb.nt;
   persistent_gemm_dma<Cfg>(pb, items, pb.f / Cfg::BK);
+}
+
+// ------------------------------------------------------------ packing ---
+//
+// Frozen weights rearranged once so that every weight tile the grouped GEMMs
+// stream is one contiguous 8 KB block holding the exact LDS image of a B
+// stage (128 rows x 32 K values, 16-byte chunk c of row r at slot
+// c ^ ((r >> 2) & 3)). gate/up: tile (le, n block of 64 FFN columns, K step)
+// with rows interleaving 16 W_g rows and the same 16 W_u rows; down: tile
+// (le, n block of 128 output columns, K step).
+__global__ __launch_bounds__(256) void pack_gate_up(const bf16_t* __restrict__ w_gate,
+                                                    const bf16_t* __restrict__ w_up, int L, int d,
+                                                    int f, u32x4* __restrict__ out) {
+  const int nk = d / 32, nt = f / 64;
+  const int64_t total = (int64_t)L * nt * nk * 512;
+  for (int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; id < total;
+       id += (int64_t)gridDim.x * blockDim.x) {
+    const int slot = (int)(id & 3), jb = (int)((id >> 2) & 127);
+    const int64_t tile = id >> 9;
+    const int kt = (int)(tile % nk);
+    const int64_t rest = tile / nk;
+    const int ni = (int)(rest % nt), le = (int)(rest / nt);
+    const int frag = jb >> 4;
+    const int fcol = ni * 64 + (frag >> 1) * 16 + (jb & 15);
+    const int c = slot ^ ((jb >> 2) & 3);
+    const bf16_t* src = ((frag & 1) ? w_up : w_gate) + ((int64_t)le * f + fcol) * d + kt * 32 + c * 8;
+    out[id] = *reinterpret_cast<const u32x4*>(src);
+  }
+}
+
+__global__ __launch_bounds__(256) void pack_down(const bf16_t* __restrict__ w_down, int L, int d,
+                                                 int f, u32x4* __restrict__ out) {
+  const int nk = f / 32, nt = d / 128;
+  const int64_t total = (int64_t)L * nt * nk * 512;
+  for (int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; id < total;
+       id += (int64_t)gridDim.x * blockDim.x) {
+    const int slot = (int)(id & 3), jb = (int)((id >> 2) & 127);
+    const int64_t tile = id >> 9;
+    const int kt = (int)(tile % nk);
+    const int64_t rest = tile / nk;
+    const int ni = (int)(rest % nt), le = (int)(rest / nt);
+    const int c = slot ^ ((jb >> 2) & 3);
+    out[id] = *reinterpret_cast<const u32x4*>(w_down + ((int64_t)le * d + ni * 128 + jb) * f + kt * 32 + c * 8);
+  }
+}
+
+hipError_t launch_pack(const Ctx& c, const moe_shape_t& s, const void* w_gate, const void* w_up,
+                       const void* w_down, void* gu_packed, void* d_packed) {
+  const int L = s.e_hi - s.e_lo;
+  const int grid = c.num_cus * 8;
+  if (gu_packed) {
+    hipLaunchKernelGGL(pack_gate_up, dim3(grid), dim3(256), 0, c.stream, (const bf16_t*)w_gate,
+                       (const bf16_t*)w_up, L, s.d, s.f, (u32x4*)gu_packed);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (d_packed)
+    hipLaunchKernelGGL(pack_down, dim3(grid), dim3(256), 0, c.stream, (const bf16_t*)w_down, L, s.d,
+                       s.f, (u32x4*)d_packed);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------- fp32 path ---
@@ -279,7 +380,7 @@ hipError_t launch_row_tiles(const Ctx& c, const int32_t* offsets, int L, int max
 
 hipError_t launch_expert_gemm(const Ctx& c, const moe_shape_t& s, const Workspace& ws,
                               const void* x_rows, const int32_t* row_src, const int32_t* offsets,
-                              const void* w_gate,
+                              const void* gu_packed, const void* d_packed, const void* w_gate,
                               const void* w_up, const void* w_down, const LoraArgs* lora,
                               void* act_save, void* y_perm) {
   const int L = s.e_hi - s.e_lo;
@@ -310,7 +411,8 @@ hipError_t launch_expert_gemm(const Ctx& c, const moe_shape_t& s, const Workspac
   const int grid = c.num_cus * 2;  // two 64 KB-LDS workgroups fit one CU
   {
     GateUpProb<GemmCfg> pb{xr, row_src, offsets, ws.gemm_tiles, (const bf16_t*)w_gate,
-                           (const bf16_t*)w_up, s.d, s.f, s.f / GateUpProb<GemmCfg>::HALF,
+                           (const bf16_t*)w_up, (const bf16_t*)gu_packed, s.d, s.f,
+                           s.f / GateUpProb<GemmCfg>::HALF,
                            lora ? ws.zu : nullptr, lora ? lora->b_up : nullptr, lora ? lora->r : 0,
                            lora ? lora->scale : 0.f, (bf16_t*)ws.hbuf, (bf16_t*)act_save};
     TimedLaunch tl(MOE_K_GATE_UP, c.stream);
@@ -322,7 +424,8 @@ hipError_t launch_expert_gemm(const Ctx& c, const moe_shape_t& s, const Workspac
                                       nullptr, s.f, lora->a_down, true, lora->r, ws.zd);
     if (err != hipSuccess) return err;
   }
-  DownProb<GemmCfg> pb{(const bf16_t*)ws.hbuf, offsets, ws.gemm_tiles, (const bf16_t*)w_down, s.d, s.f,
+  DownProb<GemmCfg> pb{(const bf16_t*)ws.hbuf, offsets, ws.gemm_tiles, (const bf16_t*)w_down,
+                       (const bf16_t*)d_packed, s.d, s.f,
                        (s.d + GemmCfg::BN - 1) / GemmCfg::BN, lora ? ws.zd : nullptr,
                        lora ? lora->b_down : nullptr, lora ? lora->r : 0, lora ? lora->scale : 0.f,
                        (bf16_t*)y_perm};

@@ -85,10 +85,6 @@ __device__ __forceinline__ void mfma_step(const bf16_t* As, const bf16_t* Bs, Ac
   }
 }
 
-// 16 bytes as a native vector (HIP's uint4 is a struct, which keeps arrays of
-// it from being promoted to registers).
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
 // Global -> register staging of one K step (16-byte loads).
 template <int N>
 __device__ __forceinline__ void gload_rows(u32x4 (&r)[N], const bf16_t* const (&rows)[N], int k0) {
@@ -307,10 +303,14 @@ struct DmaCfg {
 // Per-thread source rows of one item: a[i] / b[i] point at the logical chunk
 // this lane fetches ((lane & 3) ^ (lane >> 4)) of row 16 * (wave * X_DMA + i)
 // + lane / 4 of the tile; set by Prob::setup.
+// a_kstep / b_kstep: elements between consecutive K steps of one operand
+// (32 for a row-major operand; one whole 8 KB tile for a packed one).
 template <class Cfg>
 struct DmaLoader {
   const bf16_t* a[Cfg::A_DMA];
   const bf16_t* b[Cfg::B_DMA];
+  int a_kstep = Cfg::BK;
+  int b_kstep = Cfg::BK;
 };
 
 // Row of the tile whose chunk this thread fetches in DMA instruction i, and
@@ -327,7 +327,7 @@ __device__ __forceinline__ int dma_chunk_elem() {
 // inline assembly so the compiler's wait-count pass does not treat it as an
 // LDS store: with many DMAs in flight it would otherwise make every LDS read
 // wait for all of them. Completion is tracked explicitly instead
-// (dma_wait_younger + barrier before a stage is read). M0 carries the LDS
+// (dma_wait_stage + barrier before a stage is read). M0 carries the LDS
 // base; nothing else in these kernels uses M0.
 __device__ __forceinline__ void dma16(const void* g, const bf16_t* lds) {
   const uint32_t a = (uint32_t)(uintptr_t)(lds_void_t*)lds;
@@ -337,14 +337,29 @@ __device__ __forceinline__ void dma16(const void* g, const bf16_t* lds) {
 template <class Cfg>
 __device__ __forceinline__ void dma_issue(const DmaLoader<Cfg>& ld, int kt, bf16_t* As, bf16_t* Bs) {
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int k0 = kt * Cfg::BK;
+  const int64_t ka = (int64_t)kt * ld.a_kstep, kb = (int64_t)kt * ld.b_kstep;
 #pragma unroll
-  for (int i = 0; i < Cfg::A_DMA; ++i) dma16(ld.a[i] + k0, As + 16 * (wave * Cfg::A_DMA + i) * Cfg::BK);
+  for (int i = 0; i < Cfg::A_DMA; ++i) dma16(ld.a[i] + ka, As + 16 * (wave * Cfg::A_DMA + i) * Cfg::BK);
 #pragma unroll
-  for (int i = 0; i < Cfg::B_DMA; ++i) dma16(ld.b[i] + k0, Bs + 16 * (wave * Cfg::B_DMA + i) * Cfg::BK);
+  for (int i = 0; i < Cfg::B_DMA; ++i) dma16(ld.b[i] + kb, Bs + 16 * (wave * Cfg::B_DMA + i) * Cfg::BK);
 }
 
-// One K step of 32 from a swizzled stage.
+// Packed B operand: the weight tile of one (n block, K step) stored as the
+// exact image of its LDS stage (BN rows x 32, chunks swizzled as above), so
+// a DMA instruction copies 1 KB of contiguous memory. Pointer for this lane's
+// chunk of DMA instruction i, K step 0, given the tile's base.
+template <class Cfg>
+__device__ __forceinline__ const bf16_t* packed_b_ptr(const bf16_t* tile0, int i) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  return tile0 + (int64_t)(wave * Cfg::B_DMA + i) * 16 * Cfg::BK + lane * 8;
+}
+constexpr int kPackTileElems = 128 * 32;  // one packed weight tile: 128 rows x 32 (8 KB)
+
+// One K step of 32 from a swizzled stage. The MFMA is fed (B, A) so that it
+// produces C^T fragments: lane l then holds output row (l % 16) and the four
+// consecutive output columns 4 * (l / 16) .. +3 of a 16 x 16 fragment, which
+// the epilogues write as one 8- or 16-byte store instead of four scattered
+// 2-byte ones (see dma_out_row / dma_out_col).
 template <class Cfg>
 __device__ __forceinline__ void dma_mfma(const bf16_t* As, const bf16_t* Bs, Acc<Cfg>& acc, int wm,
                                          int wn, int lane) {
@@ -361,27 +376,64 @@ __device__ __forceinline__ void dma_mfma(const bf16_t* As, const bf16_t* Bs, Acc
   for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
     for (int j = 0; j < Cfg::FN; ++j)
-      acc.v[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc.v[i][j], 0, 0, 0);
+      acc.v[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[j], a[i], acc.v[i][j], 0, 0, 0);
 }
 
-// Wait until at most n of this thread's vector-memory operations are
-// outstanding (n a multiple of DMA_PER_STAGE, at most 2 stages).
+// Output coordinates (within the tile) of acc.v[i][j][r] for the DMA driver:
+// row dma_out_row(i), column dma_out_col(j) + r, r = 0..3.
 template <class Cfg>
-__device__ __forceinline__ void dma_wait_younger(int younger_stages) {
-  // s_waitcnt immediate: vmcnt in bits [3:0] and [15:14], expcnt [6:4] and
-  // lgkmcnt [11:8] left at their "no wait" maxima.
-  constexpr int n1 = Cfg::DMA_PER_STAGE, n2 = 2 * Cfg::DMA_PER_STAGE;
-  static_assert(n2 < 64, "vmcnt field");
-  if (younger_stages >= 2)
-    __builtin_amdgcn_s_waitcnt((n2 & 15) | ((n2 >> 4) << 14) | (7 << 4) | (15 << 8));
-  else if (younger_stages == 1)
-    __builtin_amdgcn_s_waitcnt((n1 & 15) | ((n1 >> 4) << 14) | (7 << 4) | (15 << 8));
-  else
-    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+__device__ __forceinline__ int dma_out_row(int wm, int i, int lane) {
+  return wm * (Cfg::BM / 2) + i * 16 + (lane & 15);
+}
+template <class Cfg>
+__device__ __forceinline__ int dma_out_col(int wn, int j, int lane) {
+  return wn * (Cfg::BN / 2) + j * 16 + (lane >> 4) * 4;
+}
+
+// s_waitcnt with vmcnt = 4 * q (q < 16) and the other counters left alone:
+// vmcnt lives in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
+#define MOE_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+__device__ __forceinline__ void wait_vmcnt_x4(int q) {
+  switch (q) {
+    case 0: MOE_VMCNT(0); break;
+    case 1: MOE_VMCNT(4); break;
+    case 2: MOE_VMCNT(8); break;
+    case 3: MOE_VMCNT(12); break;
+    case 4: MOE_VMCNT(16); break;
+    case 5: MOE_VMCNT(20); break;
+    case 6: MOE_VMCNT(24); break;
+    case 7: MOE_VMCNT(28); break;
+    case 8: MOE_VMCNT(32); break;
+    case 9: MOE_VMCNT(36); break;
+    case 10: MOE_VMCNT(40); break;
+    case 11: MOE_VMCNT(44); break;
+    case 12: MOE_VMCNT(48); break;
+    case 13: MOE_VMCNT(52); break;
+    case 14: MOE_VMCNT(56); break;
+    default: MOE_VMCNT(60); break;
+  }
+}
+#undef MOE_VMCNT
+
+// Before reading stage g: wait until this wave's DMAs of stage g have landed.
+// Vector-memory operations complete in order for the counter's purposes only
+// among loads; the operations issued after stage g's DMAs are the DMAs of the
+// younger stages in flight plus the epilogue stores of the last three steps
+// (stores share the counter on this GPU). Allowing exactly that many keeps the
+// stores from draining the pipeline; any count that is not exactly known
+// (younger_stores < 0) or does not fit the counter falls back to counting the
+// DMAs only, which waits longer and is always safe.
+template <class Cfg>
+__device__ __forceinline__ void dma_wait_stage(int younger_stages, int younger_stores) {
+  int n = younger_stages * Cfg::DMA_PER_STAGE;
+  if (younger_stores > 0 && n + younger_stores <= 60) n += younger_stores;
+  wait_vmcnt_x4(n >> 2);
 }
 
 // Persistent driver on the DMA ring. Same contract as persistent_gemm, with
-// Prob::setup filling a DmaLoader. Step g:
+// Prob::setup filling a DmaLoader and Prob::epilogue returning the number of
+// vector-memory store instructions the calling wave issued (-1 if not exactly
+// known, e.g. when the epilogue also loads). Step g:
 //   wait for own DMAs of stage g, barrier (everyone's DMAs of g landed, and
 //   everyone finished reading slot (g-1) % 4), issue stage g+3 into that slot,
 //   MFMAs of stage g, epilogue if g closes an item.
@@ -418,15 +470,22 @@ __device__ __forceinline__ void persistent_gemm_dma(Prob& pb, int items, int nk)
   Acc<Cfg> acc;
   acc.zero();
   int c_kt = 0, c_ord = 0;
+  // store instructions issued by the epilogues of the last three steps (-1:
+  // not exactly known); they were issued after the DMAs of the stage awaited
+  int st1 = 0, st2 = 0, st3 = 0;
 
 #define MOE_DMA_STEP(g, As, Bs, NA, NB)                                        \
   {                                                                            \
-    dma_wait_younger<Cfg>(min(2, total - 1 - (g)));                            \
+    const int ys = (st1 < 0 || st2 < 0 || st3 < 0) ? -1 : st1 + st2 + st3;     \
+    dma_wait_stage<Cfg>(min(2, total - 1 - (g)), ys);                          \
     __builtin_amdgcn_s_barrier();                                              \
     if ((g) + 3 < total) MOE_DMA_NEXT(NA, NB);                                 \
     dma_mfma<Cfg>(As, Bs, acc, wm, wn, lane);                                  \
+    st3 = st2;                                                                 \
+    st2 = st1;                                                                 \
+    st1 = 0;                                                                   \
     if (++c_kt == nk) {                                                        \
-      pb.epilogue(sp.first + c_ord * sp.stride, acc);                          \
+      st1 = pb.epilogue(sp.first + c_ord * sp.stride, acc);                    \
       acc.zero();                                                              \
       c_kt = 0;                                                                \
       ++c_ord;                                                                 \

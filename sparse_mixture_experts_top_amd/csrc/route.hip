@@ -34,23 +34,34 @@ struct RouterProb {
       ld.b[i] = w + (int64_t)min(n0 + dma_row(Cfg::B_DMA, i), E - 1) * d + ce;
   }
 
-  __device__ __forceinline__ void epilogue(int item, Acc<Cfg>& acc) const {
+  // Store count not tracked (-1): the router's tiles end rarely.
+  __device__ __forceinline__ int epilogue(int item, Acc<Cfg>& acc) const {
     const int m0 = (item / nt) * Cfg::BM, n0 = (item % nt) * Cfg::BN;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
     for (int j = 0; j < Cfg::FN; ++j) {
-      const int n = n0 + frag_col<Cfg>(wn, j, lane);
+      const int n = n0 + dma_out_col<Cfg>(wn, j, lane);
       if (n >= E) continue;
-      const float b = bias ? bias[n] : 0.f;
+      float b[4];
 #pragma unroll
-      for (int i = 0; i < Cfg::FM; ++i)
+      for (int q = 0; q < 4; ++q) b[q] = (bias && n + q < E) ? bias[n + q] : 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = m0 + frag_row<Cfg>(wm, i, lane, r);
-          if (m < T) logits[(int64_t)m * E + n] = acc.v[i][j][r] + b;
+      for (int i = 0; i < Cfg::FM; ++i) {
+        const int m = m0 + dma_out_row<Cfg>(wm, i, lane);
+        if (m >= T) continue;
+        float* dst = logits + (int64_t)m * E + n;
+        if (n + 4 <= E && (E & 3) == 0) {
+          *reinterpret_cast<float4*>(dst) = make_float4(acc.v[i][j][0] + b[0], acc.v[i][j][1] + b[1],
+                                                        acc.v[i][j][2] + b[2], acc.v[i][j][3] + b[3]);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (n + q < E) dst[q] = acc.v[i][j][q] + b[q];
         }
+      }
     }
+    return -1;
   }
 };
 

@@ -78,13 +78,29 @@ def x_rows(b: Buffers, x):
     return (b.x_perm, None) if b.x_perm is not None else (x, b.row_src)
 
 
-def forward(b: Buffers, x, w_router, bias, w_gate, w_up, w_down, lora=None, stream=None) -> None:
-    """route -> dispatch -> expert GEMM -> combine; results stay in ``b``."""
+def pack_weights(shape: B.MoeShape, w_gate, w_up, w_down, stream=None):
+    """Packed copies (gate/up, down) of frozen expert weights (bitwise equal values)."""
+    L, f, d = w_gate.shape
+    gu = torch.empty((L, 2 * f, d), dtype=w_gate.dtype, device=w_gate.device)
+    dn = torch.empty_like(w_down)
+    B.moe_pack_expert_weights(shape, w_gate, w_up, w_down, gu, dn, stream)
+    return gu, dn
+
+
+def forward(b: Buffers, x, w_router, bias, w_gate, w_up, w_down, lora=None, stream=None,
+            packed=None) -> None:
+    """route -> dispatch -> expert GEMM -> combine; results stay in ``b``.
+    packed: (gu_packed, down_packed) from pack_weights, used instead of the
+    row-major expert weights."""
     s = b.shape
     B.moe_route(s, x, w_router, bias, b.topk_idx, b.topk_gate, b.logits, b.prob_sum, b.ws, stream)
     B.moe_dispatch(s, b.topk_idx, b.topk_gate, x, b.counts, b.offsets, b.slot, b.row_src,
                    b.row_gate, b.x_perm, b.dropped, b.ws, stream)
     xr, src = x_rows(b, x)
-    B.moe_expert_gemm(s, xr, src, b.offsets, w_gate, w_up, w_down, lora, b.act_save, b.y_perm,
-                      b.ws, stream)
+    if packed is not None:
+        B.moe_expert_gemm_packed(s, xr, src, b.offsets, packed[0], packed[1], lora, b.act_save,
+                                 b.y_perm, b.ws, stream)
+    else:
+        B.moe_expert_gemm(s, xr, src, b.offsets, w_gate, w_up, w_down, lora, b.act_save, b.y_perm,
+                          b.ws, stream)
     B.moe_combine(s, b.y_perm, b.slot, b.topk_gate, b.y, stream)

@@ -33,14 +33,17 @@ def lora_of(w: Workload, dev: Dict[str, torch.Tensor]):
 
 
 def run_forward(w: Workload, dev: Dict[str, torch.Tensor], logits=True, prob=False,
-                act_save=False, x_perm=True) -> layer.Buffers:
+                act_save=False, x_perm=True, packed=False) -> layer.Buffers:
     """x_perm=True materialises the dispatched rows (and checks the copy);
-    False runs the fused path the benchmark times (gather inside the GEMM)."""
+    False runs the fused path the benchmark times (gather inside the GEMM).
+    packed=True streams the expert weights from their packed copies, as the
+    benchmark does."""
     shape = layer.shape_of(w)
     buf = layer.alloc(shape, lora_r=w.lora_r, logits=logits, prob=prob, act_save=act_save,
                       x_perm=x_perm)
+    pk = layer.pack_weights(shape, dev["w_gate"], dev["w_up"], dev["w_down"]) if packed else None
     layer.forward(buf, dev["x"], dev["w_router"], dev.get("bias"), dev["w_gate"], dev["w_up"],
-                  dev["w_down"], lora_of(w, dev))
+                  dev["w_down"], lora_of(w, dev), packed=pk)
     torch.cuda.synchronize()
     return buf
 

@@ -32,12 +32,12 @@ SMALL = {
 }
 
 
-def run_and_check(w, seed=0, x_perm=True):
+def run_and_check(w, seed=0, x_perm=True, packed=False):
     say(f"[case {w.name}] T={w.T} d={w.d} E={w.E} k={w.k} f={w.f} local=[{w.e_lo},{w.local_hi}) "
-        f"cap={w.capacity} dtype={w.dtype} x_perm={x_perm}")
+        f"cap={w.capacity} dtype={w.dtype} x_perm={x_perm} packed={packed}")
     inp = generate(w, seed=seed)
     dev = upload(inp)
-    buf = run_forward(w, dev, x_perm=x_perm)
+    buf = run_forward(w, dev, x_perm=x_perm, packed=packed)
     lg, idx, gate = check_route(w, inp, buf)
     ref, R = check_dispatch(w, dev, buf, idx, gate)
     rows = np.arange(R)
@@ -149,6 +149,39 @@ def test_capacity_one_everywhere():
     lg, idx, gate = check_route(w, inp, buf)
     ref, R = check_dispatch(w, dev, buf, idx, gate)
     assert R == int((ref["counts"] > 0).sum())
+
+
+@pytest.mark.parametrize("name", ["ragged_bf16", "rows_bf16", "capacity_bf16", "k1_bf16"])
+def test_stagewise_parity_packed_weights(name):
+    """Expert weights streamed from their packed copies (fused gather too)."""
+    run_and_check(SMALL[name], seed=8, x_perm=False, packed=True)
+
+
+def test_packed_weights_bitwise_equal_and_permutation():
+    """Packing only moves values: the packed buffers hold the same multiset of
+    bf16 values, and the packed GEMM reproduces the row-major one bitwise."""
+    w = SMALL["rows_bf16"]
+    inp = generate(w, seed=9)
+    dev = upload(inp)
+    shape = layer.shape_of(w)
+    gu, dn = layer.pack_weights(shape, dev["w_gate"], dev["w_up"], dev["w_down"])
+    srt = lambda t: torch.sort(t.float().flatten())[0]
+    assert torch.equal(srt(gu), srt(torch.cat([dev["w_gate"], dev["w_up"]], 1)))
+    assert torch.equal(srt(dn), srt(dev["w_down"]))
+    a = run_forward(w, dev, x_perm=False, packed=False)
+    b = run_forward(w, dev, x_perm=False, packed=True)
+    R = int(a.offsets[-1].item())
+    assert torch.equal(a.y_perm[:R], b.y_perm[:R]) and torch.equal(a.y, b.y)
+
+
+def test_packed_weights_need_d_multiple_of_128():
+    w = SMALL["local_bf16"]            # d = 192
+    shape = layer.shape_of(w)
+    z = lambda *s: torch.zeros(s, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(B.MoeError) as e:
+        B.moe_pack_expert_weights(shape, z(w.L, w.f, w.d), z(w.L, w.f, w.d), z(w.L, w.d, w.f),
+                                  z(w.L, 2 * w.f, w.d), z(w.L, w.d, w.f))
+    assert e.value.status == B.MOE_ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("b_init,x_perm", [("normal", True), ("normal", False), ("zero", False)])

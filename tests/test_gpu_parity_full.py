@@ -32,8 +32,8 @@ def full_case(name, prob=False, act_save=False):
     say(f"[case {name}] T={w.T} d={w.d} E={w.E} k={w.k} f={w.f} L={w.L} cap={w.capacity}")
     inp = generate(w, seed=0)
     dev = upload(inp)
-    # the fused-gather path, as bench.py runs it
-    buf = run_forward(w, dev, prob=prob, act_save=act_save, x_perm=False)
+    # fused gather and packed weights, as bench.py runs it
+    buf = run_forward(w, dev, prob=prob, act_save=act_save, x_perm=False, packed=True)
     rng = np.random.default_rng(123)
     ts = np.sort(rng.choice(w.T, 48, replace=False))
     lg, idx, gate = check_route(w, inp, buf, sample_tokens=ts)
