@@ -28,7 +28,11 @@
 
 namespace moe {
 
-using GemmCfg = DmaCfg<kGemmBM, 128>;
+// Ring depth of the grouped GEMMs (4 slots of 16 KB: two workgroups per CU).
+#ifndef MOE_GEMM_STAGES
+#define MOE_GEMM_STAGES 4
+#endif
+using GemmCfg = DmaCfg<kGemmBM, 128, MOE_GEMM_STAGES>;
 
 __global__ __launch_bounds__(1024) void build_row_tiles(const int32_t* __restrict__ offsets, int L,
                                                         int bm, int max_tiles,

@@ -277,19 +277,18 @@ __device__ __forceinline__ void persistent_gemm(Prob& pb, int items, int nk, bf1
 // 16 rows per DMA instruction). To keep the MFMA fragment reads free of bank
 // conflicts, the 16-byte chunk c of row r is stored at slot c ^ ((r >> 2) & 3):
 // the 16 rows one fragment read touches then cover 16 distinct bank groups.
-// Four stages form a ring; stage g's slot is g % 4 and three stages are in
-// flight while one is consumed. Each slot is its own __shared__ array so the
-// compiler can tell the DMA into one slot from the reads of another.
+// STAGES stages form a ring in one LDS array; stage g's slot is g % STAGES and
+// STAGES - 1 stages are in flight while one is consumed.
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
-template <int BM_, int BN_>
+template <int BM_, int BN_, int STAGES_ = 4>
 struct DmaCfg {
   static constexpr int BM = BM_;
   static constexpr int BN = BN_;
   static constexpr int BK = 32;
-  static constexpr int STAGES = 4;
+  static constexpr int STAGES = STAGES_;  // ring slots; STAGES - 1 stages in flight
   static constexpr int FM = BM / 32;  // fragments per wave along M (2 x 2 waves)
   static constexpr int FN = BN / 32;
   static constexpr int A_DMA = BM / 64;  // DMA instructions per wave per stage (16 rows each, 4 waves)
@@ -297,7 +296,9 @@ struct DmaCfg {
   static constexpr int DMA_PER_STAGE = A_DMA + B_DMA;
   static constexpr int A_ELEMS = BM * BK;
   static constexpr int B_ELEMS = BN * BK;
+  static constexpr int STAGE_ELEMS = A_ELEMS + B_ELEMS;
   static_assert(BM % 64 == 0 && BN % 64 == 0, "DMA tiles are multiples of 64 rows");
+  static_assert(STAGES >= 3 && (STAGES - 2) * DMA_PER_STAGE <= 63, "ring depth vs vmcnt");
 };
 
 // Per-thread source rows of one item: a[i] / b[i] point at the logical chunk
@@ -390,29 +391,21 @@ __device__ __forceinline__ int dma_out_col(int wn, int j, int lane) {
   return wn * (Cfg::BN / 2) + j * 16 + (lane >> 4) * 4;
 }
 
-// s_waitcnt with vmcnt = 4 * q (q < 16) and the other counters left alone:
-// vmcnt lives in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
-#define MOE_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
-__device__ __forceinline__ void wait_vmcnt_x4(int q) {
-  switch (q) {
-    case 0: MOE_VMCNT(0); break;
-    case 1: MOE_VMCNT(4); break;
-    case 2: MOE_VMCNT(8); break;
-    case 3: MOE_VMCNT(12); break;
-    case 4: MOE_VMCNT(16); break;
-    case 5: MOE_VMCNT(20); break;
-    case 6: MOE_VMCNT(24); break;
-    case 7: MOE_VMCNT(28); break;
-    case 8: MOE_VMCNT(32); break;
-    case 9: MOE_VMCNT(36); break;
-    case 10: MOE_VMCNT(40); break;
-    case 11: MOE_VMCNT(44); break;
-    case 12: MOE_VMCNT(48); break;
-    case 13: MOE_VMCNT(52); break;
-    case 14: MOE_VMCNT(56); break;
-    default: MOE_VMCNT(60); break;
+// s_waitcnt with vmcnt = n (n < 64) and the other counters left alone: vmcnt
+// lives in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]. The count
+// must be an immediate, hence the table.
+#define MOE_VMCNT(n) \
+  case n: __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8)); break;
+#define MOE_VMCNT8(b) MOE_VMCNT(b) MOE_VMCNT(b + 1) MOE_VMCNT(b + 2) MOE_VMCNT(b + 3) \
+  MOE_VMCNT(b + 4) MOE_VMCNT(b + 5) MOE_VMCNT(b + 6) MOE_VMCNT(b + 7)
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  switch (n) {
+    MOE_VMCNT8(0) MOE_VMCNT8(8) MOE_VMCNT8(16) MOE_VMCNT8(24)
+    MOE_VMCNT8(32) MOE_VMCNT8(40) MOE_VMCNT8(48) MOE_VMCNT8(56)
+    default: __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); break;  // vmcnt(0)
   }
 }
+#undef MOE_VMCNT8
 #undef MOE_VMCNT
 
 // Before reading stage g: wait until this wave's DMAs of stage g have landed.
@@ -426,24 +419,26 @@ __device__ __forceinline__ void wait_vmcnt_x4(int q) {
 template <class Cfg>
 __device__ __forceinline__ void dma_wait_stage(int younger_stages, int younger_stores) {
   int n = younger_stages * Cfg::DMA_PER_STAGE;
-  if (younger_stores > 0 && n + younger_stores <= 60) n += younger_stores;
-  wait_vmcnt_x4(n >> 2);
+  if (younger_stores > 0 && n + younger_stores <= 63) n += younger_stores;
+  wait_vmcnt(n);
 }
 
 // Persistent driver on the DMA ring. Same contract as persistent_gemm, with
 // Prob::setup filling a DmaLoader and Prob::epilogue returning the number of
 // vector-memory store instructions the calling wave issued (-1 if not exactly
-// known, e.g. when the epilogue also loads). Step g:
+// known, e.g. when the epilogue also loads). The ring has STAGES slots in one
+// LDS array; stage g lives in slot g % STAGES. Step g:
 //   wait for own DMAs of stage g, barrier (everyone's DMAs of g landed, and
-//   everyone finished reading slot (g-1) % 4), issue stage g+3 into that slot,
-//   MFMAs of stage g, epilogue if g closes an item.
+//   everyone finished reading slot (g-1) % STAGES), issue stage
+//   g + STAGES - 1 into that slot, MFMAs of stage g, epilogue if g closes an
+//   item.
 // The barrier is a bare s_barrier: the explicit vmcnt wait before it already
 // orders this wave's DMA writes, and a fenced barrier would wait for every
 // stage in flight.
 template <class Cfg, class Prob>
 __device__ __forceinline__ void persistent_gemm_dma(Prob& pb, int items, int nk) {
-  __shared__ __align__(16) bf16_t sA0[Cfg::A_ELEMS], sA1[Cfg::A_ELEMS], sA2[Cfg::A_ELEMS], sA3[Cfg::A_ELEMS];
-  __shared__ __align__(16) bf16_t sB0[Cfg::B_ELEMS], sB1[Cfg::B_ELEMS], sB2[Cfg::B_ELEMS], sB3[Cfg::B_ELEMS];
+  constexpr int S = Cfg::STAGES;
+  __shared__ __align__(16) bf16_t ring[S * Cfg::STAGE_ELEMS];
   const XcdSplit sp = xcd_split(items);
   if (sp.first >= sp.end || nk <= 0) return;
   const int n_mine = (sp.end - sp.first + sp.stride - 1) / sp.stride;
@@ -451,57 +446,51 @@ __device__ __forceinline__ void persistent_gemm_dma(Prob& pb, int items, int nk)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   DmaLoader<Cfg> ld;
-  int l_ord = 0, l_kt = 0;
+  int l_ord = 0, l_kt = 0;  // load cursor
+  int l_slot = 0;           // ring slot of the next stage to load
   pb.setup(sp.first, ld);
 
-#define MOE_DMA_NEXT(As, Bs)                                               \
-  {                                                                        \
-    dma_issue<Cfg>(ld, l_kt, As, Bs);                                      \
-    if (++l_kt == nk) {                                                    \
-      l_kt = 0;                                                            \
-      if (++l_ord < n_mine) pb.setup(sp.first + l_ord * sp.stride, ld);    \
-    }                                                                      \
-  }
-
-  // prologue: stages 0, 1, 2 in flight
-  MOE_DMA_NEXT(sA0, sB0);
-  if (total > 1) MOE_DMA_NEXT(sA1, sB1);
-  if (total > 2) MOE_DMA_NEXT(sA2, sB2);
-  Acc<Cfg> acc;
-  acc.zero();
-  int c_kt = 0, c_ord = 0;
-  // store instructions issued by the epilogues of the last three steps (-1:
-  // not exactly known); they were issued after the DMAs of the stage awaited
-  int st1 = 0, st2 = 0, st3 = 0;
-
-#define MOE_DMA_STEP(g, As, Bs, NA, NB)                                        \
+#define MOE_DMA_NEXT()                                                         \
   {                                                                            \
-    const int ys = (st1 < 0 || st2 < 0 || st3 < 0) ? -1 : st1 + st2 + st3;     \
-    dma_wait_stage<Cfg>(min(2, total - 1 - (g)), ys);                          \
-    __builtin_amdgcn_s_barrier();                                              \
-    if ((g) + 3 < total) MOE_DMA_NEXT(NA, NB);                                 \
-    dma_mfma<Cfg>(As, Bs, acc, wm, wn, lane);                                  \
-    st3 = st2;                                                                 \
-    st2 = st1;                                                                 \
-    st1 = 0;                                                                   \
-    if (++c_kt == nk) {                                                        \
-      st1 = pb.epilogue(sp.first + c_ord * sp.stride, acc);                    \
-      acc.zero();                                                              \
-      c_kt = 0;                                                                \
-      ++c_ord;                                                                 \
+    bf16_t* st_ = ring + l_slot * Cfg::STAGE_ELEMS;                            \
+    dma_issue<Cfg>(ld, l_kt, st_, st_ + Cfg::A_ELEMS);                         \
+    l_slot = (l_slot + 1 == S) ? 0 : l_slot + 1;                               \
+    if (++l_kt == nk) {                                                        \
+      l_kt = 0;                                                                \
+      if (++l_ord < n_mine) pb.setup(sp.first + l_ord * sp.stride, ld);        \
     }                                                                          \
   }
 
-  for (int g = 0; g < total; g += 4) {
-    MOE_DMA_STEP(g, sA0, sB0, sA3, sB3);
-    if (g + 1 >= total) break;
-    MOE_DMA_STEP(g + 1, sA1, sB1, sA0, sB0);
-    if (g + 2 >= total) break;
-    MOE_DMA_STEP(g + 2, sA2, sB2, sA1, sB1);
-    if (g + 3 >= total) break;
-    MOE_DMA_STEP(g + 3, sA3, sB3, sA2, sB2);
+  // prologue: stages 0 .. S-2 in flight
+  for (int p = 0; p < S - 1 && p < total; ++p) MOE_DMA_NEXT();
+  Acc<Cfg> acc;
+  acc.zero();
+  int c_kt = 0, c_ord = 0, c_slot = 0;
+  // store instructions issued by the epilogues of the last S-1 steps (< 0:
+  // not exactly known); they were issued after the DMAs of the stage awaited
+  int st_hist[S - 1];
+#pragma unroll
+  for (int i = 0; i < S - 1; ++i) st_hist[i] = 0;
+  for (int g = 0; g < total; ++g) {
+    int ys = 0;
+#pragma unroll
+    for (int i = 0; i < S - 1; ++i) ys = (ys < 0 || st_hist[i] < 0) ? -1 : ys + st_hist[i];
+    dma_wait_stage<Cfg>(min(S - 2, total - 1 - g), ys);
+    __builtin_amdgcn_s_barrier();
+    if (g + S - 1 < total) MOE_DMA_NEXT();
+    const bf16_t* st = ring + c_slot * Cfg::STAGE_ELEMS;
+    dma_mfma<Cfg>(st, st + Cfg::A_ELEMS, acc, wm, wn, lane);
+    c_slot = (c_slot + 1 == S) ? 0 : c_slot + 1;
+#pragma unroll
+    for (int i = S - 2; i > 0; --i) st_hist[i] = st_hist[i - 1];
+    st_hist[0] = 0;
+    if (++c_kt == nk) {
+      st_hist[0] = pb.epilogue(sp.first + c_ord * sp.stride, acc);
+      acc.zero();
+      c_kt = 0;
+      ++c_ord;
+    }
   }
-#undef MOE_DMA_STEP
 #undef MOE_DMA_NEXT
 }
 

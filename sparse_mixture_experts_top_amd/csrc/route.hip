@@ -98,13 +98,24 @@ static hipError_t launch_router_bf16(const Ctx& c, const moe_shape_t& s, const b
   return hipGetLastError();
 }
 
+// Ring depths: the router's operands come from L2 / MALL, so each K step is
+// short and the ring has to cover the cache latency.
+#ifndef MOE_ROUTER_STAGES_128
+#define MOE_ROUTER_STAGES_128 4
+#endif
+#ifndef MOE_ROUTER_STAGES_64
+#define MOE_ROUTER_STAGES_64 6
+#endif
+
 hipError_t launch_router(const Ctx& c, const moe_shape_t& s, const void* x, const void* w,
                          const float* bias, float* logits) {
   if (s.dtype == MOE_BF16) {
     const int tiles128 = ((s.T + 127) / 128) * ((s.E + 127) / 128);
     if (tiles128 >= 2 * c.num_cus)
-      return launch_router_bf16<DmaCfg<128, 128>>(c, s, (const bf16_t*)x, (const bf16_t*)w, bias, logits);
-    return launch_router_bf16<DmaCfg<64, 128>>(c, s, (const bf16_t*)x, (const bf16_t*)w, bias, logits);
+      return launch_router_bf16<DmaCfg<128, 128, MOE_ROUTER_STAGES_128>>(c, s, (const bf16_t*)x,
+                                                                          (const bf16_t*)w, bias, logits);
+    return launch_router_bf16<DmaCfg<64, 128, MOE_ROUTER_STAGES_64>>(c, s, (const bf16_t*)x,
+                                                                      (const bf16_t*)w, bias, logits);
   }
   const int64_t n = (int64_t)s.T * s.E;
   TimedLaunch tl(MOE_K_ROUTER_GEMM, c.stream);
