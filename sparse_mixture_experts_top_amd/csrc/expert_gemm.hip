@@ -80,6 +80,26 @@ __device__ __forceinline__ RowTile row_tile(const int32_t* tiles, const int32_t*
   return t;
 }
 
+// Source row of this lane's chunk in DMA instruction i of an A tile gathered
+// through row_src: the 16 rows of one instruction are read with scalar loads
+// (clamped to the tile's valid rows) and lane l takes row l / 4. Scalar loads
+// count on the LGKM counter, so a new item's gather does not drain the DMA
+// stages still in flight the way a vector load's vmcnt(0) wait would.
+template <class Cfg>
+__device__ __forceinline__ int64_t gathered_row(const int32_t* row_src, const RowTile& t, int i) {
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int first = 16 * (wave * Cfg::A_DMA + i);
+  const int q = (threadIdx.x & 63) >> 2;
+  const int32_t* seg = row_src + t.row0;
+  int src = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int v = ld_uniform(seg, min(first + j, t.valid - 1));
+    src = (q == j) ? v : src;
+  }
+  return src;
+}
+
 // K8: H = silu(X W_g^T) * (X W_u^T [+ s Z_u B_u^T]) for one (row tile, 64
 // FFN columns) item. Rows of X are x[row_src[p]] (gather fused into the A
 // loader) or, with row_src == NULL, x[p] of an already gathered matrix.
@@ -107,8 +127,8 @@ struct GateUpProb {
     const int ce = dma_chunk_elem();
 #pragma unroll
     for (int i = 0; i < Cfg::A_DMA; ++i) {
-      const int64_t row = t.row0 + min(dma_row(Cfg::A_DMA, i), t.valid - 1);
-      const int64_t src = row_src ? (int64_t)row_src[row] : row;
+      const int64_t src = row_src ? gathered_row<Cfg>(row_src, t, i)
+                                  : t.row0 + min(dma_row(Cfg::A_DMA, i), t.valid - 1);
       ld.a[i] = x + src * d + ce;
     }
     if (w_packed) {
@@ -269,7 +289,7 @@ __global__ __launch_bounds__(256, 2) void down_bf16(DownProb<Cfg> pb, int max_ti
 // Frozen weights rearranged once so that every weight tile the grouped GEMMs
 // stream is one contiguous 8 KB block holding the exact LDS image of a B
 // stage (128 rows x 32 K values, 16-byte chunk c of row r at slot
-// c ^ ((r >> 2) & 3)). gate/up: tile (le, n block of 64 FFN columns, K step)
+// c ^ chunk_key(r)). gate/up: tile (le, n block of 64 FFN columns, K step)
 // with rows interleaving 16 W_g rows and the same 16 W_u rows; down: tile
 // (le, n block of 128 output columns, K step).
 __global__ __launch_bounds__(256) void pack_gate_up(const bf16_t* __restrict__ w_gate,
@@ -286,7 +306,7 @@ __global__ __launch_bounds__(256) void pack_gate_up(const bf16_t* __restrict__ w
     const int ni = (int)(rest % nt), le = (int)(rest / nt);
     const int frag = jb >> 4;
     const int fcol = ni * 64 + (frag >> 1) * 16 + (jb & 15);
-    const int c = slot ^ ((jb >> 2) & 3);
+    const int c = slot ^ chunk_key(jb);
     const bf16_t* src = ((frag & 1) ? w_up : w_gate) + ((int64_t)le * f + fcol) * d + kt * 32 + c * 8;
     out[id] = *reinterpret_cast<const u32x4*>(src);
   }
@@ -303,7 +323,7 @@ __global__ __launch_bounds__(256) void pack_down(const bf16_t* __restrict__ w_do
     const int kt = (int)(tile % nk);
     const int64_t rest = tile / nk;
     const int ni = (int)(rest % nt), le = (int)(rest / nt);
-    const int c = slot ^ ((jb >> 2) & 3);
+    const int c = slot ^ chunk_key(jb);
     out[id] = *reinterpret_cast<const u32x4*>(w_down + ((int64_t)le * d + ni * 128 + jb) * f + kt * 32 + c * 8);
   }
 }

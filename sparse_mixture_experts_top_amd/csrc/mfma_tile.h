@@ -274,9 +274,13 @@ __device__ __forceinline__ void persistent_gemm(Prob& pb, int items, int nk, bf1
 // no registers hold tiles in transit and several K steps can be in flight.
 //
 // K step = 32. A stage holds A [BM][32] and B [BN][32] bf16 (64-byte rows,
-// 16 rows per DMA instruction). To keep the MFMA fragment reads free of bank
-// conflicts, the 16-byte chunk c of row r is stored at slot c ^ ((r >> 2) & 3):
-// the 16 rows one fragment read touches then cover 16 distinct bank groups.
+// 16 rows per DMA instruction). To keep the MFMA fragment reads (16 rows x one
+// 16-byte chunk per instruction) free of bank conflicts, the 16-byte chunk c
+// of row r is stored at slot c ^ chunk_key(r): among any 8 consecutive rows
+// (one 128-byte bank line holds two rows) the (row parity, slot) pairs are
+// all distinct, and among any 16 consecutive rows the (row mod 4, slot)
+// pairs are, so the read is conflict-free whether the LDS serves 8 or 16
+// lanes of a 16-byte read per cycle.
 // STAGES stages form a ring in one LDS array; stage g's slot is g % STAGES and
 // STAGES - 1 stages are in flight while one is consumed.
 
@@ -302,7 +306,7 @@ struct DmaCfg {
 };
 
 // Per-thread source rows of one item: a[i] / b[i] point at the logical chunk
-// this lane fetches ((lane & 3) ^ (lane >> 4)) of row 16 * (wave * X_DMA + i)
+// this lane fetches ((lane & 3) ^ chunk_key(lane / 4)) of row 16 * (wave * X_DMA + i)
 // + lane / 4 of the tile; set by Prob::setup.
 // a_kstep / b_kstep: elements between consecutive K steps of one operand
 // (32 for a row-major operand; one whole 8 KB tile for a packed one).
@@ -314,14 +318,21 @@ struct DmaLoader {
   int b_kstep = Cfg::BK;
 };
 
+// Swizzle key of tile row r (only r mod 16 matters): bit 0 = bit 2 of r,
+// bit 1 = bit 1 ^ bit 3 of r. XOR with it maps chunk -> slot and back.
+__host__ __device__ __forceinline__ int chunk_key(int r) {
+  return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1);
+}
+
 // Row of the tile whose chunk this thread fetches in DMA instruction i, and
-// the element offset of that chunk inside the row.
+// the element offset of that chunk inside the row: lane l writes slot l % 4
+// of row l / 4 of its 16-row group, so it fetches chunk (l % 4) ^ key.
 __device__ __forceinline__ int dma_row(int x_dma, int i) {
   return 16 * ((int)(threadIdx.x >> 6) * x_dma + i) + ((threadIdx.x & 63) >> 2);
 }
 __device__ __forceinline__ int dma_chunk_elem() {
   const int lane = threadIdx.x & 63;
-  return (((lane & 3) ^ (lane >> 4)) & 3) * 8;
+  return ((lane & 3) ^ chunk_key(lane >> 2)) * 8;
 }
 
 // One 16-byte-per-lane DMA: global -> LDS at lds + 16 * lane. Issued as
@@ -365,7 +376,7 @@ template <class Cfg>
 __device__ __forceinline__ void dma_mfma(const bf16_t* As, const bf16_t* Bs, Acc<Cfg>& acc, int wm,
                                          int wn, int lane) {
   const int r = lane & 15;
-  const int slot = ((lane >> 4) ^ (r >> 2)) & 3;
+  const int slot = (lane >> 4) ^ chunk_key(r);
   bf16x8 a[Cfg::FM], b[Cfg::FN];
 #pragma unroll
   for (int i = 0; i < Cfg::FM; ++i)
@@ -407,6 +418,11 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 }
 #undef MOE_VMCNT8
 #undef MOE_VMCNT
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_imm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 // Before reading stage g: wait until this wave's DMAs of stage g have landed.
 // Vector-memory operations complete in order for the counter's purposes only
@@ -415,9 +431,15 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 // (stores share the counter on this GPU). Allowing exactly that many keeps the
 // stores from draining the pipeline; any count that is not exactly known
 // (younger_stores < 0) or does not fit the counter falls back to counting the
-// DMAs only, which waits longer and is always safe.
+// DMAs only, which waits longer and is always safe. Both arguments are
+// wave-uniform; the steady state (full ring, no recent stores) takes one
+// immediate wait, the rest a scalar branch table.
 template <class Cfg>
 __device__ __forceinline__ void dma_wait_stage(int younger_stages, int younger_stores) {
+  if (younger_stages == Cfg::STAGES - 2 && younger_stores == 0) {
+    wait_vmcnt_imm<(Cfg::STAGES - 2) * Cfg::DMA_PER_STAGE>();
+    return;
+  }
   int n = younger_stages * Cfg::DMA_PER_STAGE;
   if (younger_stores > 0 && n + younger_stores <= 63) n += younger_stores;
   wait_vmcnt(n);
@@ -485,7 +507,8 @@ __device__ __forceinline__ void persistent_gemm_dma(Prob& pb, int items, int nk)
     for (int i = S - 2; i > 0; --i) st_hist[i] = st_hist[i - 1];
     st_hist[0] = 0;
     if (++c_kt == nk) {
-      st_hist[0] = pb.epilogue(sp.first + c_ord * sp.stride, acc);
+      // the count is wave-uniform; keep it (and the wait it selects) scalar
+      st_hist[0] = __builtin_amdgcn_readfirstlane(pb.epilogue(sp.first + c_ord * sp.stride, acc));
       acc.zero();
       c_kt = 0;
       ++c_ord;

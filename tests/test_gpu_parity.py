@@ -174,6 +174,47 @@ def test_packed_weights_bitwise_equal_and_permutation():
     assert torch.equal(a.y_perm[:R], b.y_perm[:R]) and torch.equal(a.y, b.y)
 
 
+def _chunk_key(r):
+    return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1)
+
+
+def test_packed_weights_documented_layout():
+    """The packed buffers follow the tile layout the header documents: 8 KB
+    tiles of 128 rows x 32 K values, gate/up rows interleaved per 16, chunk c
+    of row r at position c ^ key(r). The expected buffers are built on the
+    host by index arithmetic from that description."""
+    w = SMALL["rows_bf16"]
+    dev = upload(generate(w, seed=10))
+    shape = layer.shape_of(w)
+    gu, dn = layer.pack_weights(shape, dev["w_gate"], dev["w_up"], dev["w_down"])
+    wg, wu, wd = (dev[n].cpu() for n in ("w_gate", "w_up", "w_down"))
+    L, f, d = wg.shape
+    jb = torch.arange(128)
+    key = _chunk_key(jb)
+    c = torch.arange(4)[None, :] ^ key[:, None]                      # [128 rows, 4 slots]
+    kk = c[:, :, None] * 8 + torch.arange(8)[None, None, :]          # [128, 4, 8] K offset in step
+    # gate/up: tile (le, b, kt); row jb -> 16-row block q = jb // 32, gate if (jb // 16) even
+    frag = jb >> 4
+    col = (frag >> 1) * 16 + (jb & 15)
+    both = torch.stack([wg, wu])                                     # [2, L, f, d]
+    nt, nk = f // 64, d // 32
+    le = torch.arange(L)[:, None, None, None, None, None]
+    b = torch.arange(nt)[None, :, None, None, None, None]
+    kt = torch.arange(nk)[None, None, :, None, None, None]
+    src = (frag & 1)[None, None, None, :, None, None]
+    row = b * 64 + col[None, None, None, :, None, None]
+    kidx = kt * 32 + kk[None, None, None]
+    exp_gu = both[src, le, row, kidx].reshape(-1)
+    assert torch.equal(gu.cpu().reshape(-1), exp_gu)
+    # down: tile (le, b < d/128, kt < f/32), rows 128b + jb
+    nt, nk = d // 128, f // 32
+    b = torch.arange(nt)[None, :, None, None, None, None]
+    kt = torch.arange(nk)[None, None, :, None, None, None]
+    row = b * 128 + jb[None, None, None, :, None, None]
+    exp_dn = wd[le, row, kt * 32 + kk[None, None, None]].reshape(-1)
+    assert torch.equal(dn.cpu().reshape(-1), exp_dn)
+
+
 def test_packed_weights_need_d_multiple_of_128():
     w = SMALL["local_bf16"]            # d = 192
     shape = layer.shape_of(w)
