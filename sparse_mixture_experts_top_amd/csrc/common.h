@@ -69,6 +69,8 @@ __device__ __forceinline__ int segment_of(const int32_t* off, int L, int p) {
 // an earlier kernel on the stream): through the constant address space with a
 // uniform index, so it becomes a scalar load and never waits on vector memory.
 typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr_t;
+typedef int32_t i32x16_t __attribute__((ext_vector_type(16), aligned(4)));
+typedef const __attribute__((address_space(4))) i32x16_t* const_i32x16_ptr_t;
 __device__ __forceinline__ int ld_uniform(const int32_t* p, int idx) {
   return ((const_i32_ptr_t)p)[__builtin_amdgcn_readfirstlane(idx)];
 }

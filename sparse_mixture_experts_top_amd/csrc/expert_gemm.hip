@@ -32,7 +32,10 @@ namespace moe {
 #ifndef MOE_GEMM_STAGES
 #define MOE_GEMM_STAGES 4
 #endif
-using GemmCfg = DmaCfg<kGemmBM, 128, MOE_GEMM_STAGES>;
+// The 4 waves split the 128 columns (WM = 1): every wave holds all row
+// fragments, so the fragments of a partly filled row tile that are pure
+// padding are skipped by all four waves alike.
+using GemmCfg = DmaCfg<kGemmBM, 128, MOE_GEMM_STAGES, 1>;
 
 __global__ __launch_bounds__(1024) void build_row_tiles(const int32_t* __restrict__ offsets, int L,
                                                         int bm, int max_tiles,
@@ -81,23 +84,32 @@ __device__ __forceinline__ RowTile row_tile(const int32_t* tiles, const int32_t*
 }
 
 // Source row of this lane's chunk in DMA instruction i of an A tile gathered
-// through row_src: the 16 rows of one instruction are read with scalar loads
-// (clamped to the tile's valid rows) and lane l takes row l / 4. Scalar loads
-// count on the LGKM counter, so a new item's gather does not drain the DMA
-// stages still in flight the way a vector load's vmcnt(0) wait would.
+// through row_src (first = 16 i). Lane l needs entry row0 + min(first + l / 4, valid - 1)
+// of row_src; the 16 entries of one instruction's rows are fetched with one
+// 16-dword scalar load from a window [base, base + 16) inside the R written
+// entries, and each lane picks its entry with a 4-level select on the bits of
+// its offset in the window. Scalar loads count on the LGKM counter, so a new
+// item's gather does not drain the DMA stages still in flight the way a
+// vector load's vmcnt(0) wait would. With fewer than 16 rows in all, a plain
+// vector load is used.
 template <class Cfg>
-__device__ __forceinline__ int64_t gathered_row(const int32_t* row_src, const RowTile& t, int i) {
-  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int first = 16 * (wave * Cfg::A_DMA + i);
-  const int q = (threadIdx.x & 63) >> 2;
-  const int32_t* seg = row_src + t.row0;
-  int src = 0;
+__device__ __forceinline__ int64_t gathered_row(const int32_t* row_src, const RowTile& t, int i, int R) {
+  const int first = 16 * i;
+  const int64_t gr = t.row0 + min(first + (int)((threadIdx.x & 63) >> 2), t.valid - 1);
+  if (R < 16) return row_src[gr];
+  const int64_t base = min(t.row0 + min(first, t.valid - 1), (int64_t)R - 16);  // wave-uniform
+  const i32x16_t v = *(const_i32x16_ptr_t)(row_src + base);
+  const int e = (int)(gr - base);  // 0 .. 15
+  // bitwise selects (not an indexed array, which would live in scratch)
+  const int m0 = -(e & 1), m1 = -((e >> 1) & 1), m2 = -((e >> 2) & 1), m3 = -((e >> 3) & 1);
+  int l1[8], l2[4], l3[2];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int v = ld_uniform(seg, min(first + j, t.valid - 1));
-    src = (q == j) ? v : src;
-  }
-  return src;
+  for (int k = 0; k < 8; ++k) l1[k] = (v[2 * k + 1] & m0) | (v[2 * k] & ~m0);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) l2[k] = (l1[2 * k + 1] & m1) | (l1[2 * k] & ~m1);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) l3[k] = (l2[2 * k + 1] & m2) | (l2[2 * k] & ~m2);
+  return (l3[1] & m3) | (l3[0] & ~m3);
 }
 
 // K8: H = silu(X W_g^T) * (X W_u^T [+ s Z_u B_u^T]) for one (row tile, 64
@@ -112,7 +124,7 @@ struct GateUpProb {
   const bf16_t* w_gate;
   const bf16_t* w_up;
   const bf16_t* w_packed;  // packed gate/up tiles, or NULL for row-major w_gate / w_up
-  int d, f, nt;
+  int d, f, nt, L;
   const float* zu;
   const bf16_t* b_up;
   int r;
@@ -121,46 +133,47 @@ struct GateUpProb {
   bf16_t* act_save;
   static constexpr int HALF = Cfg::BN / 2;  // FFN columns per item
 
-  __device__ __forceinline__ void setup(int item, DmaLoader<Cfg>& ld) const {
+  __device__ __forceinline__ int rows(int item) const {
+    return row_tile<Cfg::BM>(tiles, offsets, item / nt).valid;
+  }
+
+  __device__ __forceinline__ void setup(int item, DmaLoader<Cfg>& ld, int part) const {
     const RowTile t = row_tile<Cfg::BM>(tiles, offsets, item / nt);
     const int ni = item % nt;
     const int ce = dma_chunk_elem();
 #pragma unroll
-    for (int i = 0; i < Cfg::A_DMA; ++i) {
-      const int64_t src = row_src ? gathered_row<Cfg>(row_src, t, i)
-                                  : t.row0 + min(dma_row(Cfg::A_DMA, i), t.valid - 1);
-      ld.a[i] = x + src * d + ce;
+    for (int q = 0; q < Cfg::A_DMA / kProducers; ++q) {
+      const int i = q * kProducers + part;
+      const int64_t src = row_src ? gathered_row<Cfg>(row_src, t, i, ld_uniform(offsets, L))
+                                  : t.row0 + min(dma_row(i), t.valid - 1);
+      ld.a[q] = x + src * d + ce;
     }
     if (w_packed) {
       const bf16_t* tile0 = w_packed + ((int64_t)t.le * nt + ni) * (d / Cfg::BK) * kPackTileElems;
 #pragma unroll
-      for (int i = 0; i < Cfg::B_DMA; ++i) ld.b[i] = packed_b_ptr<Cfg>(tile0, i);
+      for (int q = 0; q < Cfg::B_DMA / kProducers; ++q)
+        ld.b[q] = packed_b_ptr<Cfg>(tile0, q * kProducers + part);
       ld.b_kstep = kPackTileElems;
       return;
     }
 #pragma unroll
-    for (int i = 0; i < Cfg::B_DMA; ++i) {
-      const int jb = dma_row(Cfg::B_DMA, i);
+    for (int q = 0; q < Cfg::B_DMA / kProducers; ++q) {
+      const int jb = dma_row(q * kProducers + part);
       const int frag = jb >> 4;
       const int fcol = ni * HALF + (frag >> 1) * 16 + (jb & 15);
-      ld.b[i] = ((frag & 1) ? w_up : w_gate) + ((int64_t)t.le * f + fcol) * d + ce;
+      ld.b[q] = ((frag & 1) ? w_up : w_gate) + ((int64_t)t.le * f + fcol) * d + ce;
     }
   }
 
-  // Returns the store instructions this wave issued: one per (fragment pair,
-  // fragment row block with a valid row) and stored tensor, or -1 with LoRA
-  // (the epilogue then also loads).
-  __device__ __forceinline__ int epilogue(int item, Acc<Cfg>& acc) const {
+  __device__ __forceinline__ void epilogue(int item, Acc<Cfg>& acc) const {
     const RowTile t = row_tile<Cfg::BM>(tiles, offsets, item / nt);
     const int ni = item % nt;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    int nfrag = 0;
+    const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i) {
-      const int base = wm * (Cfg::BM / 2) + i * 16;  // wave-uniform
+      const int base = wm * (Cfg::BM / Cfg::WM) + i * 16;  // wave-uniform
       if (base >= t.valid) continue;
-      ++nfrag;
       const int rin = base + (lane & 15);
       const bool ok = rin < t.valid;
       const int64_t row = t.row0 + rin;
@@ -193,13 +206,11 @@ struct GateUpProb {
         }
       }
     }
-    if (zu) return -1;
-    return nfrag * (Cfg::FN / 2) * (act_save ? 3 : 1);
   }
 };
 
 template <class Cfg>
-__global__ __launch_bounds__(256, 2) void gate_up_bf16(GateUpProb<Cfg> pb, int max_tiles) {
+__global__ __launch_bounds__(kDmaThreads, 2) void gate_up_bf16(GateUpProb<Cfg> pb, int max_tiles) {
   const int items = ld_uniform(pb.tiles, 2 * max_tiles) * pb.nt;
   persistent_gemm_dma<Cfg>(pb, items, pb.d / Cfg::BK);
 }
@@ -219,36 +230,38 @@ struct DownProb {
   float scale;
   bf16_t* y_perm;
 
-  __device__ __forceinline__ void setup(int item, DmaLoader<Cfg>& ld) const {
+  __device__ __forceinline__ int rows(int item) const {
+    return row_tile<Cfg::BM>(tiles, offsets, item / nt).valid;
+  }
+
+  __device__ __forceinline__ void setup(int item, DmaLoader<Cfg>& ld, int part) const {
     const RowTile t = row_tile<Cfg::BM>(tiles, offsets, item / nt);
     const int n0 = (item % nt) * Cfg::BN;
     const int ce = dma_chunk_elem();
 #pragma unroll
-    for (int i = 0; i < Cfg::A_DMA; ++i)
-      ld.a[i] = hbuf + (t.row0 + min(dma_row(Cfg::A_DMA, i), t.valid - 1)) * f + ce;
+    for (int q = 0; q < Cfg::A_DMA / kProducers; ++q)
+      ld.a[q] = hbuf + (t.row0 + min(dma_row(q * kProducers + part), t.valid - 1)) * f + ce;
     if (w_packed) {
       const bf16_t* tile0 = w_packed + ((int64_t)t.le * nt + item % nt) * (f / Cfg::BK) * kPackTileElems;
 #pragma unroll
-      for (int i = 0; i < Cfg::B_DMA; ++i) ld.b[i] = packed_b_ptr<Cfg>(tile0, i);
+      for (int q = 0; q < Cfg::B_DMA / kProducers; ++q)
+        ld.b[q] = packed_b_ptr<Cfg>(tile0, q * kProducers + part);
       ld.b_kstep = kPackTileElems;
       return;
     }
 #pragma unroll
-    for (int i = 0; i < Cfg::B_DMA; ++i)
-      ld.b[i] = w_down + ((int64_t)t.le * d + min(n0 + dma_row(Cfg::B_DMA, i), d - 1)) * f + ce;
+    for (int q = 0; q < Cfg::B_DMA / kProducers; ++q)
+      ld.b[q] = w_down + ((int64_t)t.le * d + min(n0 + dma_row(q * kProducers + part), d - 1)) * f + ce;
   }
 
-  // Returns the store instructions this wave issued (one per fragment with a
-  // valid row and valid columns), or -1 with LoRA (the epilogue then loads).
-  __device__ __forceinline__ int epilogue(int item, Acc<Cfg>& acc) const {
+  __device__ __forceinline__ void epilogue(int item, Acc<Cfg>& acc) const {
     const RowTile t = row_tile<Cfg::BM>(tiles, offsets, item / nt);
     const int n0 = (item % nt) * Cfg::BN;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    int nst = 0;
+    const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i) {
-      const int base = wm * (Cfg::BM / 2) + i * 16;  // wave-uniform
+      const int base = wm * (Cfg::BM / Cfg::WM) + i * 16;  // wave-uniform
       if (base >= t.valid) continue;
       const int rin = base + (lane & 15);
       const bool ok = rin < t.valid;
@@ -256,8 +269,7 @@ struct DownProb {
 #pragma unroll
       for (int j = 0; j < Cfg::FN; ++j) {
         // d % 64 == 0: a wave's 16-column fragment is all valid or all not
-        if (n0 + wn * (Cfg::BN / 2) + j * 16 >= d) continue;
-        ++nst;
+        if (n0 + wn * (Cfg::BN / Cfg::WN) + j * 16 >= d) continue;
         const int n = n0 + dma_out_col<Cfg>(wn, j, lane);
         float o[4];
 #pragma unroll
@@ -274,12 +286,11 @@ struct DownProb {
         if (ok) *reinterpret_cast<uint2*>(y_perm + row * d + n) = pack4_bf16(o[0], o[1], o[2], o[3]);
       }
     }
-    return zd ? -1 : nst;
   }
 };
 
 template <class Cfg>
-__global__ __launch_bounds__(256, 2) void down_bf16(DownProb<Cfg> pb, int max_tiles) {
+__global__ __launch_bounds__(kDmaThreads, 2) void down_bf16(DownProb<Cfg> pb, int max_tiles) {
   const int items = ld_uniform(pb.tiles, 2 * max_tiles) * pb.nt;
   persistent_gemm_dma<Cfg>(pb, items, pb.f / Cfg::BK);
 }
@@ -436,11 +447,11 @@ hipError_t launch_expert_gemm(const Ctx& c, const moe_shape_t& s, const Workspac
   {
     GateUpProb<GemmCfg> pb{xr, row_src, offsets, ws.gemm_tiles, (const bf16_t*)w_gate,
                            (const bf16_t*)w_up, (const bf16_t*)gu_packed, s.d, s.f,
-                           s.f / GateUpProb<GemmCfg>::HALF,
+                           s.f / GateUpProb<GemmCfg>::HALF, s.e_hi - s.e_lo,
                            lora ? ws.zu : nullptr, lora ? lora->b_up : nullptr, lora ? lora->r : 0,
                            lora ? lora->scale : 0.f, (bf16_t*)ws.hbuf, (bf16_t*)act_save};
     TimedLaunch tl(MOE_K_GATE_UP, c.stream);
-    hipLaunchKernelGGL(gate_up_bf16<GemmCfg>, dim3(grid), dim3(256), 0, c.stream, pb, max_tiles);
+    hipLaunchKernelGGL(gate_up_bf16<GemmCfg>, dim3(grid), dim3(kDmaThreads), 0, c.stream, pb, max_tiles);
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (lora) {
@@ -454,7 +465,7 @@ hipError_t launch_expert_gemm(const Ctx& c, const moe_shape_t& s, const Workspac
                        lora ? lora->b_down : nullptr, lora ? lora->r : 0, lora ? lora->scale : 0.f,
                        (bf16_t*)y_perm};
   TimedLaunch tl(MOE_K_DOWN, c.stream);
-  hipLaunchKernelGGL(down_bf16<GemmCfg>, dim3(grid), dim3(256), 0, c.stream, pb, max_tiles);
+  hipLaunchKernelGGL(down_bf16<GemmCfg>, dim3(grid), dim3(kDmaThreads), 0, c.stream, pb, max_tiles);
   return hipGetLastError();
 }
 

@@ -273,6 +273,18 @@ __device__ __forceinline__ void persistent_gemm(Prob& pb, int items, int nk, bf1
 // bytes; the 64 lanes of one instruction fill 1 KB of LDS in lane order), so
 // no registers hold tiles in transit and several K steps can be in flight.
 //
+// Wave roles. A workgroup has 4 compute waves and 2 producer waves. The
+// producers issue every DMA of the ring and never store; the compute waves
+// read LDS, run the MFMAs and write the results. On this GPU stores share
+// the vector-memory counter with loads and the counter retires in issue
+// order, so in a wave that both loads and stores, every load issued after an
+// epilogue's stores could only be waited for once those stores were
+// acknowledged - a bubble of a full write latency after every output tile.
+// With the roles split, a producer's waits count its own DMAs only (a
+// constant in the steady state) and the compute waves never wait on memory
+// counters. Two producers share each stage's DMAs: one wave alone issues
+// them too slowly to keep the memory system busy.
+//
 // K step = 32. A stage holds A [BM][32] and B [BN][32] bf16 (64-byte rows,
 // 16 rows per DMA instruction). To keep the MFMA fragment reads (16 rows x one
 // 16-byte chunk per instruction) free of bank conflicts, the 16-byte chunk c
@@ -287,33 +299,45 @@ __device__ __forceinline__ void persistent_gemm(Prob& pb, int items, int nk, bf1
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
-template <int BM_, int BN_, int STAGES_ = 4>
+constexpr int kComputeWaves = 4;  // waves 0..3
+constexpr int kProducers = 2;     // waves 4..5; producer p issues the DMAs i with i % kProducers == p
+constexpr int kDmaThreads = 64 * (kComputeWaves + kProducers);  // workgroup size of the DMA GEMMs
+
+template <int BM_, int BN_, int STAGES_ = 4, int WM_ = 2>
 struct DmaCfg {
   static constexpr int BM = BM_;
   static constexpr int BN = BN_;
   static constexpr int BK = 32;
   static constexpr int STAGES = STAGES_;  // ring slots; STAGES - 1 stages in flight
-  static constexpr int FM = BM / 32;  // fragments per wave along M (2 x 2 waves)
-  static constexpr int FN = BN / 32;
-  static constexpr int A_DMA = BM / 64;  // DMA instructions per wave per stage (16 rows each, 4 waves)
-  static constexpr int B_DMA = BN / 64;
+  static constexpr int WM = WM_;          // the compute waves form a WM x WN grid over the tile
+  static constexpr int WN = kComputeWaves / WM_;
+  static constexpr int FM = BM / (16 * WM);  // 16 x 16 fragments per wave along M
+  static constexpr int FN = BN / (16 * WN);
+  static constexpr int A_DMA = BM / 16;  // producer DMA instructions per stage (16 rows each)
+  static constexpr int B_DMA = BN / 16;
   static constexpr int DMA_PER_STAGE = A_DMA + B_DMA;
   static constexpr int A_ELEMS = BM * BK;
   static constexpr int B_ELEMS = BN * BK;
   static constexpr int STAGE_ELEMS = A_ELEMS + B_ELEMS;
-  static_assert(BM % 64 == 0 && BN % 64 == 0, "DMA tiles are multiples of 64 rows");
-  static_assert(STAGES >= 3 && (STAGES - 2) * DMA_PER_STAGE <= 63, "ring depth vs vmcnt");
+  static_assert(WM == 1 || WM == 2 || WM == 4, "wave grid");
+  static_assert(FM >= 1 && FN >= 1 && FM * 16 * WM == BM && FN * 16 * WN == BN, "fragments");
+  static_assert(BM % 16 == 0 && BN % 16 == 0, "DMA tiles are multiples of 16 rows");
+  static constexpr int DMA_PER_PRODUCER = DMA_PER_STAGE / kProducers;  // per stage
+  static_assert(A_DMA % kProducers == 0 && B_DMA % kProducers == 0, "DMA split");
+  static_assert(STAGES >= 3 && (STAGES - 2) * DMA_PER_PRODUCER <= 63, "ring depth vs vmcnt");
 };
 
-// Per-thread source rows of one item: a[i] / b[i] point at the logical chunk
-// this lane fetches ((lane & 3) ^ chunk_key(lane / 4)) of row 16 * (wave * X_DMA + i)
-// + lane / 4 of the tile; set by Prob::setup.
+// Lane pointers of one producer for one item: a[q] / b[q] belong to the
+// producer's q-th DMA instruction of each operand, i = q * kProducers + part,
+// and point at the logical chunk this lane fetches ((lane & 3) ^
+// chunk_key(lane / 4)) of tile row 16 i + lane / 4; set by
+// Prob::setup(item, ld, part).
 // a_kstep / b_kstep: elements between consecutive K steps of one operand
-// (32 for a row-major operand; one whole 8 KB tile for a packed one).
+// (32 for a row-major operand; one whole packed tile for a packed one).
 template <class Cfg>
 struct DmaLoader {
-  const bf16_t* a[Cfg::A_DMA];
-  const bf16_t* b[Cfg::B_DMA];
+  const bf16_t* a[Cfg::A_DMA / kProducers];
+  const bf16_t* b[Cfg::B_DMA / kProducers];
   int a_kstep = Cfg::BK;
   int b_kstep = Cfg::BK;
 };
@@ -324,12 +348,11 @@ __host__ __device__ __forceinline__ int chunk_key(int r) {
   return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1);
 }
 
-// Row of the tile whose chunk this thread fetches in DMA instruction i, and
+// Tile row whose chunk this (producer) lane fetches in DMA instruction i, and
 // the element offset of that chunk inside the row: lane l writes slot l % 4
-// of row l / 4 of its 16-row group, so it fetches chunk (l % 4) ^ key.
-__device__ __forceinline__ int dma_row(int x_dma, int i) {
-  return 16 * ((int)(threadIdx.x >> 6) * x_dma + i) + ((threadIdx.x & 63) >> 2);
-}
+// of row l / 4 of the instruction's 16-row group, so it fetches chunk
+// (l % 4) ^ key.
+__device__ __forceinline__ int dma_row(int i) { return 16 * i + ((threadIdx.x & 63) >> 2); }
 __device__ __forceinline__ int dma_chunk_elem() {
   const int lane = threadIdx.x & 63;
   return ((lane & 3) ^ chunk_key(lane >> 2)) * 8;
@@ -338,22 +361,25 @@ __device__ __forceinline__ int dma_chunk_elem() {
 // One 16-byte-per-lane DMA: global -> LDS at lds + 16 * lane. Issued as
 // inline assembly so the compiler's wait-count pass does not treat it as an
 // LDS store: with many DMAs in flight it would otherwise make every LDS read
-// wait for all of them. Completion is tracked explicitly instead
-// (dma_wait_stage + barrier before a stage is read). M0 carries the LDS
-// base; nothing else in these kernels uses M0.
+// wait for all of them. Completion is tracked explicitly instead (the
+// producer's vmcnt wait + the barrier before a stage is read). M0 carries the
+// LDS base; nothing else in these kernels uses M0.
 __device__ __forceinline__ void dma16(const void* g, const bf16_t* lds) {
   const uint32_t a = (uint32_t)(uintptr_t)(lds_void_t*)lds;
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(a) : "memory");
 }
 
+// Producer `part`'s share of the DMA instructions of K step kt into stage
+// `stage`: A and B instructions i with i % kProducers == part.
 template <class Cfg>
-__device__ __forceinline__ void dma_issue(const DmaLoader<Cfg>& ld, int kt, bf16_t* As, bf16_t* Bs) {
-  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+__device__ __forceinline__ void dma_issue(const DmaLoader<Cfg>& ld, int kt, bf16_t* stage, int part) {
   const int64_t ka = (int64_t)kt * ld.a_kstep, kb = (int64_t)kt * ld.b_kstep;
 #pragma unroll
-  for (int i = 0; i < Cfg::A_DMA; ++i) dma16(ld.a[i] + ka, As + 16 * (wave * Cfg::A_DMA + i) * Cfg::BK);
+  for (int q = 0; q < Cfg::A_DMA / kProducers; ++q)
+    dma16(ld.a[q] + ka, stage + 16 * (q * kProducers + part) * Cfg::BK);
 #pragma unroll
-  for (int i = 0; i < Cfg::B_DMA; ++i) dma16(ld.b[i] + kb, Bs + 16 * (wave * Cfg::B_DMA + i) * Cfg::BK);
+  for (int q = 0; q < Cfg::B_DMA / kProducers; ++q)
+    dma16(ld.b[q] + kb, stage + Cfg::A_ELEMS + 16 * (q * kProducers + part) * Cfg::BK);
 }
 
 // Packed B operand: the weight tile of one (n block, K step) stored as the
@@ -362,101 +388,138 @@ __device__ __forceinline__ void dma_issue(const DmaLoader<Cfg>& ld, int kt, bf16
 // chunk of DMA instruction i, K step 0, given the tile's base.
 template <class Cfg>
 __device__ __forceinline__ const bf16_t* packed_b_ptr(const bf16_t* tile0, int i) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  return tile0 + (int64_t)(wave * Cfg::B_DMA + i) * 16 * Cfg::BK + lane * 8;
+  return tile0 + (int64_t)i * 16 * Cfg::BK + (threadIdx.x & 63) * 8;
 }
 constexpr int kPackTileElems = 128 * 32;  // one packed weight tile: 128 rows x 32 (8 KB)
 
-// One K step of 32 from a swizzled stage. The MFMA is fed (B, A) so that it
-// produces C^T fragments: lane l then holds output row (l % 16) and the four
-// consecutive output columns 4 * (l / 16) .. +3 of a 16 x 16 fragment, which
-// the epilogues write as one 8- or 16-byte store instead of four scattered
-// 2-byte ones (see dma_out_row / dma_out_col).
-template <class Cfg>
-__device__ __forceinline__ void dma_mfma(const bf16_t* As, const bf16_t* Bs, Acc<Cfg>& acc, int wm,
-                                         int wn, int lane) {
+// One K step of 32 from a swizzled stage (compute wave) over the wave's first
+// NF row fragments. Straight-line code: the fragment reads are issued up
+// front (B, then A by row fragment) and each MFMA group waits only for its
+// own operands, so LDS latency overlaps the matrix work. The MFMA is fed
+// (B, A) so that it produces C^T fragments: lane l then holds output row
+// (l % 16) and the four consecutive output columns 4 * (l / 16) .. +3 of a
+// 16 x 16 fragment, which the epilogues write as one 8- or 16-byte store
+// instead of four scattered 2-byte ones (see dma_out_row / dma_out_col).
+template <class Cfg, int NF>
+__device__ __forceinline__ void mma_step_n(const bf16_t* st, Acc<Cfg>& acc, int wm, int wn, int lane) {
+  const bf16_t* As = st;
+  const bf16_t* Bs = st + Cfg::A_ELEMS;
   const int r = lane & 15;
   const int slot = (lane >> 4) ^ chunk_key(r);
-  bf16x8 a[Cfg::FM], b[Cfg::FN];
-#pragma unroll
-  for (int i = 0; i < Cfg::FM; ++i)
-    a[i] = *reinterpret_cast<const bf16x8*>(&As[(wm * (Cfg::BM / 2) + i * 16 + r) * Cfg::BK + slot * 8]);
+  bf16x8 a[NF], b[Cfg::FN];
 #pragma unroll
   for (int j = 0; j < Cfg::FN; ++j)
-    b[j] = *reinterpret_cast<const bf16x8*>(&Bs[(wn * (Cfg::BN / 2) + j * 16 + r) * Cfg::BK + slot * 8]);
+    b[j] = *reinterpret_cast<const bf16x8*>(&Bs[(wn * (Cfg::BN / Cfg::WN) + j * 16 + r) * Cfg::BK + slot * 8]);
 #pragma unroll
-  for (int i = 0; i < Cfg::FM; ++i)
+  for (int i = 0; i < NF; ++i)
+    a[i] = *reinterpret_cast<const bf16x8*>(&As[(wm * (Cfg::BM / Cfg::WM) + i * 16 + r) * Cfg::BK + slot * 8]);
+#pragma unroll
+  for (int i = 0; i < NF; ++i)
 #pragma unroll
     for (int j = 0; j < Cfg::FN; ++j)
       acc.v[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[j], a[i], acc.v[i][j], 0, 0, 0);
+  // keep every LDS read ahead of the MFMAs (the scheduler would otherwise
+  // recycle operand registers in pairs and wait a full LDS round trip per pair)
+  __builtin_amdgcn_sched_group_barrier(0x100, NF + Cfg::FN, 0);  // DS reads
+  __builtin_amdgcn_sched_group_barrier(0x008, NF * Cfg::FN, 0);  // MFMAs
+}
+
+// The K loop of one item on the compute side, over the wave's first NF row
+// fragments: one barrier per K step (matching the producer's), then the
+// MFMAs of the stage in the ring slot `slot`.
+template <class Cfg, int NF>
+__device__ __forceinline__ void mma_item_n(int nk, const bf16_t* ring, int& slot, Acc<Cfg>& acc,
+                                           int wm, int wn, int lane) {
+  for (int kt = 0; kt < nk; ++kt) {
+    __builtin_amdgcn_s_barrier();
+    if constexpr (NF > 0) mma_step_n<Cfg, NF>(ring + slot * Cfg::STAGE_ELEMS, acc, wm, wn, lane);
+    slot = (slot + 1 == Cfg::STAGES) ? 0 : slot + 1;
+  }
+}
+
+// One item's K loop for a wave whose first nf row fragments hold valid rows.
+// The rest (padding of a partly filled row tile) is skipped in coarse steps -
+// the wave's whole tile, or its first 3/4, 1/2 or 1/4 - each its own loop,
+// so the choice is made once per item and every K step stays straight-line.
+template <class Cfg>
+__device__ __forceinline__ void mma_item(int nf, int nk, const bf16_t* ring, int& slot,
+                                         Acc<Cfg>& acc, int wm, int wn, int lane) {
+  constexpr int F = Cfg::FM;
+  if constexpr (F % 4 == 0) {
+    if (nf > 3 * F / 4)
+      mma_item_n<Cfg, F>(nk, ring, slot, acc, wm, wn, lane);
+    else if (nf > F / 2)
+      mma_item_n<Cfg, 3 * F / 4>(nk, ring, slot, acc, wm, wn, lane);
+    else if (nf > F / 4)
+      mma_item_n<Cfg, F / 2>(nk, ring, slot, acc, wm, wn, lane);
+    else if (nf > 0)
+      mma_item_n<Cfg, F / 4>(nk, ring, slot, acc, wm, wn, lane);
+    else
+      mma_item_n<Cfg, 0>(nk, ring, slot, acc, wm, wn, lane);
+  } else {
+    if (nf > 0)
+      mma_item_n<Cfg, F>(nk, ring, slot, acc, wm, wn, lane);
+    else
+      mma_item_n<Cfg, 0>(nk, ring, slot, acc, wm, wn, lane);
+  }
+}
+
+// Row fragments of wave row wm that hold some of the tile's first `valid` rows.
+template <class Cfg>
+__device__ __forceinline__ int dma_active_frags(int wm, int valid) {
+  const int rows = valid - wm * (Cfg::BM / Cfg::WM);
+  return rows <= 0 ? 0 : min(Cfg::FM, (rows + 15) >> 4);
 }
 
 // Output coordinates (within the tile) of acc.v[i][j][r] for the DMA driver:
-// row dma_out_row(i), column dma_out_col(j) + r, r = 0..3.
+// row dma_out_row(i), column dma_out_col(j) + r, r = 0..3. Compute wave w is
+// at (wm, wn) = (w / WN, w % WN) of the wave grid.
 template <class Cfg>
 __device__ __forceinline__ int dma_out_row(int wm, int i, int lane) {
-  return wm * (Cfg::BM / 2) + i * 16 + (lane & 15);
+  return wm * (Cfg::BM / Cfg::WM) + i * 16 + (lane & 15);
 }
 template <class Cfg>
 __device__ __forceinline__ int dma_out_col(int wn, int j, int lane) {
-  return wn * (Cfg::BN / 2) + j * 16 + (lane >> 4) * 4;
+  return wn * (Cfg::BN / Cfg::WN) + j * 16 + (lane >> 4) * 4;
 }
 
 // s_waitcnt with vmcnt = n (n < 64) and the other counters left alone: vmcnt
-// lives in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]. The count
-// must be an immediate, hence the table.
-#define MOE_VMCNT(n) \
-  case n: __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8)); break;
-#define MOE_VMCNT8(b) MOE_VMCNT(b) MOE_VMCNT(b + 1) MOE_VMCNT(b + 2) MOE_VMCNT(b + 3) \
-  MOE_VMCNT(b + 4) MOE_VMCNT(b + 5) MOE_VMCNT(b + 6) MOE_VMCNT(b + 7)
-__device__ __forceinline__ void wait_vmcnt(int n) {
-  switch (n) {
-    MOE_VMCNT8(0) MOE_VMCNT8(8) MOE_VMCNT8(16) MOE_VMCNT8(24)
-    MOE_VMCNT8(32) MOE_VMCNT8(40) MOE_VMCNT8(48) MOE_VMCNT8(56)
-    default: __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); break;  // vmcnt(0)
-  }
-}
-#undef MOE_VMCNT8
-#undef MOE_VMCNT
+// lives in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
 template <int N>
 __device__ __forceinline__ void wait_vmcnt_imm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
-
-// Before reading stage g: wait until this wave's DMAs of stage g have landed.
-// Vector-memory operations complete in order for the counter's purposes only
-// among loads; the operations issued after stage g's DMAs are the DMAs of the
-// younger stages in flight plus the epilogue stores of the last three steps
-// (stores share the counter on this GPU). Allowing exactly that many keeps the
-// stores from draining the pipeline; any count that is not exactly known
-// (younger_stores < 0) or does not fit the counter falls back to counting the
-// DMAs only, which waits longer and is always safe. Both arguments are
-// wave-uniform; the steady state (full ring, no recent stores) takes one
-// immediate wait, the rest a scalar branch table.
-template <class Cfg>
-__device__ __forceinline__ void dma_wait_stage(int younger_stages, int younger_stores) {
-  if (younger_stages == Cfg::STAGES - 2 && younger_stores == 0) {
-    wait_vmcnt_imm<(Cfg::STAGES - 2) * Cfg::DMA_PER_STAGE>();
-    return;
+// Producer wait before stage g is read, with `younger` stages (0 .. STAGES-2)
+// issued after it: at most younger * DMA_PER_PRODUCER DMAs may still be out.
+// The steady state (younger = STAGES - 2) is one immediate wait; the ring's
+// last steps select theirs from a short scalar chain.
+template <class Cfg, int Y = Cfg::STAGES - 2>
+__device__ __forceinline__ void dma_wait_stage(int younger) {
+  if constexpr (Y == 0) {
+    wait_vmcnt_imm<0>();
+  } else {
+    if (younger >= Y)
+      wait_vmcnt_imm<Y * Cfg::DMA_PER_PRODUCER>();
+    else
+      dma_wait_stage<Cfg, Y - 1>(younger);
   }
-  int n = younger_stages * Cfg::DMA_PER_STAGE;
-  if (younger_stores > 0 && n + younger_stores <= 63) n += younger_stores;
-  wait_vmcnt(n);
 }
 
-// Persistent driver on the DMA ring. Same contract as persistent_gemm, with
-// Prob::setup filling a DmaLoader and Prob::epilogue returning the number of
-// vector-memory store instructions the calling wave issued (-1 if not exactly
-// known, e.g. when the epilogue also loads). The ring has STAGES slots in one
-// LDS array; stage g lives in slot g % STAGES. Step g:
-//   wait for own DMAs of stage g, barrier (everyone's DMAs of g landed, and
-//   everyone finished reading slot (g-1) % STAGES), issue stage
-//   g + STAGES - 1 into that slot, MFMAs of stage g, epilogue if g closes an
-//   item.
-// The barrier is a bare s_barrier: the explicit vmcnt wait before it already
-// orders this wave's DMA writes, and a fenced barrier would wait for every
-// stage in flight.
+// Persistent warp-specialised driver on the DMA ring. Items are processed in
+// order; Prob::rows(item) gives an item's valid tile rows (row fragments past
+// them skip their MFMAs), Prob::setup(item, ld, part) fills producer part's
+// DmaLoader, Prob::epilogue(item, acc) writes an item's result (compute
+// waves). Step g (one K step of some item):
+//   producers: wait until their DMAs of stage g landed; barrier; issue stage
+//             g + STAGES - 1 into slot (g - 1) % STAGES.
+//   compute:  barrier; MFMAs of stage g; epilogue if g closes an item
+//             (the K loop of each item is specialised on how many of the
+//             wave's row fragments hold valid rows).
+// The barrier of step g publishes stage g to the compute waves and tells the
+// producer that slot (g - 1) % STAGES has been read. It is a bare s_barrier:
+// the producer's explicit vmcnt wait already orders its DMA writes, and a
+// fenced barrier would wait for every stage in flight.
 template <class Cfg, class Prob>
 __device__ __forceinline__ void persistent_gemm_dma(Prob& pb, int items, int nk) {
   constexpr int S = Cfg::STAGES;
@@ -465,56 +528,40 @@ __device__ __forceinline__ void persistent_gemm_dma(Prob& pb, int items, int nk)
   if (sp.first >= sp.end || nk <= 0) return;
   const int n_mine = (sp.end - sp.first + sp.stride - 1) / sp.stride;
   const int total = n_mine * nk;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  DmaLoader<Cfg> ld;
-  int l_ord = 0, l_kt = 0;  // load cursor
-  int l_slot = 0;           // ring slot of the next stage to load
-  pb.setup(sp.first, ld);
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 
-#define MOE_DMA_NEXT()                                                         \
-  {                                                                            \
-    bf16_t* st_ = ring + l_slot * Cfg::STAGE_ELEMS;                            \
-    dma_issue<Cfg>(ld, l_kt, st_, st_ + Cfg::A_ELEMS);                         \
-    l_slot = (l_slot + 1 == S) ? 0 : l_slot + 1;                               \
-    if (++l_kt == nk) {                                                        \
-      l_kt = 0;                                                                \
-      if (++l_ord < n_mine) pb.setup(sp.first + l_ord * sp.stride, ld);        \
-    }                                                                          \
-  }
-
-  // prologue: stages 0 .. S-2 in flight
-  for (int p = 0; p < S - 1 && p < total; ++p) MOE_DMA_NEXT();
-  Acc<Cfg> acc;
-  acc.zero();
-  int c_kt = 0, c_ord = 0, c_slot = 0;
-  // store instructions issued by the epilogues of the last S-1 steps (< 0:
-  // not exactly known); they were issued after the DMAs of the stage awaited
-  int st_hist[S - 1];
-#pragma unroll
-  for (int i = 0; i < S - 1; ++i) st_hist[i] = 0;
-  for (int g = 0; g < total; ++g) {
-    int ys = 0;
-#pragma unroll
-    for (int i = 0; i < S - 1; ++i) ys = (ys < 0 || st_hist[i] < 0) ? -1 : ys + st_hist[i];
-    dma_wait_stage<Cfg>(min(S - 2, total - 1 - g), ys);
-    __builtin_amdgcn_s_barrier();
-    if (g + S - 1 < total) MOE_DMA_NEXT();
-    const bf16_t* st = ring + c_slot * Cfg::STAGE_ELEMS;
-    dma_mfma<Cfg>(st, st + Cfg::A_ELEMS, acc, wm, wn, lane);
-    c_slot = (c_slot + 1 == S) ? 0 : c_slot + 1;
-#pragma unroll
-    for (int i = S - 2; i > 0; --i) st_hist[i] = st_hist[i - 1];
-    st_hist[0] = 0;
-    if (++c_kt == nk) {
-      // the count is wave-uniform; keep it (and the wait it selects) scalar
-      st_hist[0] = __builtin_amdgcn_readfirstlane(pb.epilogue(sp.first + c_ord * sp.stride, acc));
-      acc.zero();
-      c_kt = 0;
-      ++c_ord;
+  if (wave >= kComputeWaves) {
+    const int part = wave - kComputeWaves;
+    DmaLoader<Cfg> ld;
+    int l_ord = 0, l_kt = 0, l_slot = 0;  // load cursor
+    pb.setup(sp.first, ld, part);
+    auto issue_next = [&]() {
+      dma_issue<Cfg>(ld, l_kt, ring + l_slot * Cfg::STAGE_ELEMS, part);
+      l_slot = (l_slot + 1 == S) ? 0 : l_slot + 1;
+      if (++l_kt == nk) {
+        l_kt = 0;
+        if (++l_ord < n_mine) pb.setup(sp.first + l_ord * sp.stride, ld, part);
+      }
+    };
+    for (int p = 0; p < S - 1 && p < total; ++p) issue_next();
+    for (int g = 0; g < total; ++g) {
+      dma_wait_stage<Cfg>(total - 1 - g);
+      __builtin_amdgcn_s_barrier();
+      if (g + S - 1 < total) issue_next();
     }
+    return;
   }
-#undef MOE_DMA_NEXT
+
+  const int lane = threadIdx.x & 63;
+  const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
+  Acc<Cfg> acc;
+  int c_slot = 0;
+  for (int c_ord = 0; c_ord < n_mine; ++c_ord) {
+    const int item = sp.first + c_ord * sp.stride;
+    acc.zero();
+    mma_item<Cfg>(dma_active_frags<Cfg>(wm, pb.rows(item)), nk, ring, c_slot, acc, wm, wn, lane);
+    pb.epilogue(item, acc);
+  }
 }
 
 }  // namespace moe

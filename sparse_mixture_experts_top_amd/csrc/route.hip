@@ -23,22 +23,23 @@ struct RouterProb {
   float* logits;
   int T, d, E, nt;
 
-  __device__ __forceinline__ void setup(int item, DmaLoader<Cfg>& ld) const {
+  __device__ __forceinline__ int rows(int item) const { return min(Cfg::BM, T - (item / nt) * Cfg::BM); }
+
+  __device__ __forceinline__ void setup(int item, DmaLoader<Cfg>& ld, int part) const {
     const int m0 = (item / nt) * Cfg::BM, n0 = (item % nt) * Cfg::BN;
     const int ce = dma_chunk_elem();
 #pragma unroll
-    for (int i = 0; i < Cfg::A_DMA; ++i)
-      ld.a[i] = x + (int64_t)min(m0 + dma_row(Cfg::A_DMA, i), T - 1) * d + ce;
+    for (int q = 0; q < Cfg::A_DMA / kProducers; ++q)
+      ld.a[q] = x + (int64_t)min(m0 + dma_row(q * kProducers + part), T - 1) * d + ce;
 #pragma unroll
-    for (int i = 0; i < Cfg::B_DMA; ++i)
-      ld.b[i] = w + (int64_t)min(n0 + dma_row(Cfg::B_DMA, i), E - 1) * d + ce;
+    for (int q = 0; q < Cfg::B_DMA / kProducers; ++q)
+      ld.b[q] = w + (int64_t)min(n0 + dma_row(q * kProducers + part), E - 1) * d + ce;
   }
 
-  // Store count not tracked (-1): the router's tiles end rarely.
-  __device__ __forceinline__ int epilogue(int item, Acc<Cfg>& acc) const {
+  __device__ __forceinline__ void epilogue(int item, Acc<Cfg>& acc) const {
     const int m0 = (item / nt) * Cfg::BM, n0 = (item % nt) * Cfg::BN;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
 #pragma unroll
     for (int j = 0; j < Cfg::FN; ++j) {
       const int n = n0 + dma_out_col<Cfg>(wn, j, lane);
@@ -61,12 +62,11 @@ struct RouterProb {
         }
       }
     }
-    return -1;
   }
 };
 
 template <class Cfg>
-__global__ __launch_bounds__(256, 2) void router_gemm_bf16(RouterProb<Cfg> pb, int items) {
+__global__ __launch_bounds__(kDmaThreads, 2) void router_gemm_bf16(RouterProb<Cfg> pb, int items) {
   persistent_gemm_dma<Cfg>(pb, items, pb.d / Cfg::BK);
 }
 
@@ -94,7 +94,7 @@ static hipError_t launch_router_bf16(const Ctx& c, const moe_shape_t& s, const b
   const int grid = std::min(((items + 7) / 8) * 8, c.num_cus * 2);
   RouterProb<Cfg> pb{x, w, bias, logits, s.T, s.d, s.E, nt};
   TimedLaunch tl(MOE_K_ROUTER_GEMM, c.stream);
-  hipLaunchKernelGGL(router_gemm_bf16<Cfg>, dim3(grid), dim3(256), 0, c.stream, pb, items);
+  hipLaunchKernelGGL(router_gemm_bf16<Cfg>, dim3(grid), dim3(kDmaThreads), 0, c.stream, pb, items);
   return hipGetLastError();
 }
 
