@@ -32,10 +32,9 @@ namespace moe {
 #ifndef MOE_GEMM_STAGES
 #define MOE_GEMM_STAGES 4
 #endif
-// The 4 waves split the 128 columns (WM = 1): every wave holds all row
-// fragments, so the fragments of a partly filled row tile that are pure
-// padding are skipped by all four waves alike.
-using GemmCfg = DmaCfg<kGemmBM, 128, MOE_GEMM_STAGES, 1>;
+// 2 x 2 compute waves, each with 4 interleaved row fragments x 4 column
+// fragments (64 x 64 of the tile).
+using GemmCfg = DmaCfg<kGemmBM, 128, MOE_GEMM_STAGES, 2>;
 
 __global__ __launch_bounds__(1024) void build_row_tiles(const int32_t* __restrict__ offsets, int L,
                                                         int bm, int max_tiles,
@@ -172,7 +171,7 @@ struct GateUpProb {
     const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i) {
-      const int base = wm * (Cfg::BM / Cfg::WM) + i * 16;  // wave-uniform
+      const int base = frag_row0<Cfg>(wm, i);  // wave-uniform
       if (base >= t.valid) continue;
       const int rin = base + (lane & 15);
       const bool ok = rin < t.valid;
@@ -210,7 +209,7 @@ struct GateUpProb {
 };
 
 template <class Cfg>
-__global__ __launch_bounds__(kDmaThreads, 2) void gate_up_bf16(GateUpProb<Cfg> pb, int max_tiles) {
+__global__ __launch_bounds__(kDmaThreads, kDmaWavesPerSimd) void gate_up_bf16(GateUpProb<Cfg> pb, int max_tiles) {
   const int items = ld_uniform(pb.tiles, 2 * max_tiles) * pb.nt;
   persistent_gemm_dma<Cfg>(pb, items, pb.d / Cfg::BK);
 }
@@ -261,7 +260,7 @@ struct DownProb {
     const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i) {
-      const int base = wm * (Cfg::BM / Cfg::WM) + i * 16;  // wave-uniform
+      const int base = frag_row0<Cfg>(wm, i);  // wave-uniform
       if (base >= t.valid) continue;
       const int rin = base + (lane & 15);
       const bool ok = rin < t.valid;
@@ -290,7 +289,7 @@ struct DownProb {
 };
 
 template <class Cfg>
-__global__ __launch_bounds__(kDmaThreads, 2) void down_bf16(DownProb<Cfg> pb, int max_tiles) {
+__global__ __launch_bounds__(kDmaThreads, kDmaWavesPerSimd) void down_bf16(DownProb<Cfg> pb, int max_tiles) {
   const int items = ld_uniform(pb.tiles, 2 * max_tiles) * pb.nt;
   persistent_gemm_dma<Cfg>(pb, items, pb.f / Cfg::BK);
 }

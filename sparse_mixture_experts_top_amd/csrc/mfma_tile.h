@@ -302,6 +302,9 @@ typedef __attribute__((address_space(1))) void glb_void_t;
 constexpr int kComputeWaves = 4;  // waves 0..3
 constexpr int kProducers = 2;     // waves 4..5; producer p issues the DMAs i with i % kProducers == p
 constexpr int kDmaThreads = 64 * (kComputeWaves + kProducers);  // workgroup size of the DMA GEMMs
+// two workgroups per CU: 12 waves over 4 SIMDs (the launch-bounds occupancy
+// hint is in waves per SIMD, which caps each wave at 512 / 3 registers)
+constexpr int kDmaWavesPerSimd = (2 * (kComputeWaves + kProducers) + 3) / 4;
 
 template <int BM_, int BN_, int STAGES_ = 4, int WM_ = 2>
 struct DmaCfg {
@@ -392,83 +395,88 @@ __device__ __forceinline__ const bf16_t* packed_b_ptr(const bf16_t* tile0, int i
 }
 constexpr int kPackTileElems = 128 * 32;  // one packed weight tile: 128 rows x 32 (8 KB)
 
-// One K step of 32 from a swizzled stage (compute wave) over the wave's first
-// NF row fragments. Straight-line code: the fragment reads are issued up
-// front (B, then A by row fragment) and each MFMA group waits only for its
-// own operands, so LDS latency overlaps the matrix work. The MFMA is fed
-// (B, A) so that it produces C^T fragments: lane l then holds output row
-// (l % 16) and the four consecutive output columns 4 * (l / 16) .. +3 of a
-// 16 x 16 fragment, which the epilogues write as one 8- or 16-byte store
-// instead of four scattered 2-byte ones (see dma_out_row / dma_out_col).
-template <class Cfg, int NF>
-__device__ __forceinline__ void mma_step_n(const bf16_t* st, Acc<Cfg>& acc, int wm, int wn, int lane) {
+// First tile row of row fragment i of wave row wm. Row fragments are
+// interleaved over the wave rows (wave row wm holds fragments wm, wm + WM,
+// ...), so when a partly filled row tile skips its padding fragments, the
+// remaining work stays spread over all wave rows.
+template <class Cfg>
+__device__ __forceinline__ int frag_row0(int wm, int i) {
+  return 16 * (i * Cfg::WM + wm);
+}
+
+// Operand fragments of one K step for one compute wave: FN B fragments and
+// all FM A fragments (padding rows included; they are in bounds).
+template <class Cfg>
+struct Frags {
+  bf16x8 a[Cfg::FM], b[Cfg::FN];
+};
+
+// LDS reads of the wave's fragments of the stage at `st`.
+template <class Cfg>
+__device__ __forceinline__ void read_frags(Frags<Cfg>& fr, const bf16_t* st, int wm, int wn, int lane) {
   const bf16_t* As = st;
   const bf16_t* Bs = st + Cfg::A_ELEMS;
   const int r = lane & 15;
   const int slot = (lane >> 4) ^ chunk_key(r);
-  bf16x8 a[NF], b[Cfg::FN];
 #pragma unroll
   for (int j = 0; j < Cfg::FN; ++j)
-    b[j] = *reinterpret_cast<const bf16x8*>(&Bs[(wn * (Cfg::BN / Cfg::WN) + j * 16 + r) * Cfg::BK + slot * 8]);
+    fr.b[j] = *reinterpret_cast<const bf16x8*>(&Bs[(wn * (Cfg::BN / Cfg::WN) + j * 16 + r) * Cfg::BK + slot * 8]);
 #pragma unroll
-  for (int i = 0; i < NF; ++i)
-    a[i] = *reinterpret_cast<const bf16x8*>(&As[(wm * (Cfg::BM / Cfg::WM) + i * 16 + r) * Cfg::BK + slot * 8]);
-#pragma unroll
-  for (int i = 0; i < NF; ++i)
-#pragma unroll
-    for (int j = 0; j < Cfg::FN; ++j)
-      acc.v[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[j], a[i], acc.v[i][j], 0, 0, 0);
-  // keep every LDS read ahead of the MFMAs (the scheduler would otherwise
-  // recycle operand registers in pairs and wait a full LDS round trip per pair)
-  __builtin_amdgcn_sched_group_barrier(0x100, NF + Cfg::FN, 0);  // DS reads
-  __builtin_amdgcn_sched_group_barrier(0x008, NF * Cfg::FN, 0);  // MFMAs
+  for (int i = 0; i < Cfg::FM; ++i)
+    fr.a[i] = *reinterpret_cast<const bf16x8*>(&As[(frag_row0<Cfg>(wm, i) + r) * Cfg::BK + slot * 8]);
 }
 
-// The K loop of one item on the compute side, over the wave's first NF row
-// fragments: one barrier per K step (matching the producer's), then the
-// MFMAs of the stage in the ring slot `slot`.
-template <class Cfg, int NF>
-__device__ __forceinline__ void mma_item_n(int nk, const bf16_t* ring, int& slot, Acc<Cfg>& acc,
-                                           int wm, int wn, int lane) {
-  for (int kt = 0; kt < nk; ++kt) {
-    __builtin_amdgcn_s_barrier();
-    if constexpr (NF > 0) mma_step_n<Cfg, NF>(ring + slot * Cfg::STAGE_ELEMS, acc, wm, wn, lane);
-    slot = (slot + 1 == Cfg::STAGES) ? 0 : slot + 1;
-  }
+// Workgroup barrier without a memory fence (see persistent_gemm_dma), with
+// compiler-level memory clobbers on both sides: the s_barrier intrinsic is
+// not a memory operation to the optimiser, which could otherwise move LDS
+// reads across it.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
-// One item's K loop for a wave whose first nf row fragments hold valid rows.
-// The rest (padding of a partly filled row tile) is skipped in coarse steps -
-// the wave's whole tile, or its first 3/4, 1/2 or 1/4 - each its own loop,
-// so the choice is made once per item and every K step stays straight-line.
+// s_waitcnt lgkmcnt(0) with the other counters left alone.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14)); }
+
+// One compute step of the software pipeline: barrier g (stage g + 1 has
+// landed), LDS reads of stage g + 1 into `nxt` (unless g is the last step),
+// then the MFMAs of stage g from `cur` (read during the previous step) over
+// the wave's first nf row fragments - the rest, padding of a partly filled
+// row tile, is skipped behind wave-uniform branches with the accumulators
+// updated in place. The reads are issued ahead of the MFMAs so their latency
+// hides behind the matrix work; the caller completes them before the next
+// barrier, after which the producers may refill their slot. The MFMA is fed
+// (B, A) so that it produces C^T fragments: lane l then holds output row
+// (l % 16) and the four consecutive output columns 4 * (l / 16) .. +3 of a
+// 16 x 16 fragment, which the epilogues write as one 8- or 16-byte store
+// instead of four scattered 2-byte ones (see dma_out_row / dma_out_col).
 template <class Cfg>
-__device__ __forceinline__ void mma_item(int nf, int nk, const bf16_t* ring, int& slot,
-                                         Acc<Cfg>& acc, int wm, int wn, int lane) {
-  constexpr int F = Cfg::FM;
-  if constexpr (F % 4 == 0) {
-    if (nf > 3 * F / 4)
-      mma_item_n<Cfg, F>(nk, ring, slot, acc, wm, wn, lane);
-    else if (nf > F / 2)
-      mma_item_n<Cfg, 3 * F / 4>(nk, ring, slot, acc, wm, wn, lane);
-    else if (nf > F / 4)
-      mma_item_n<Cfg, F / 2>(nk, ring, slot, acc, wm, wn, lane);
-    else if (nf > 0)
-      mma_item_n<Cfg, F / 4>(nk, ring, slot, acc, wm, wn, lane);
-    else
-      mma_item_n<Cfg, 0>(nk, ring, slot, acc, wm, wn, lane);
-  } else {
-    if (nf > 0)
-      mma_item_n<Cfg, F>(nk, ring, slot, acc, wm, wn, lane);
-    else
-      mma_item_n<Cfg, 0>(nk, ring, slot, acc, wm, wn, lane);
+__device__ __forceinline__ void mma_pp_step(int g, int total, int nf, const bf16_t* ring, int& rslot,
+                                            const Frags<Cfg>& cur, Frags<Cfg>& nxt, Acc<Cfg>& acc,
+                                            int wm, int wn, int lane) {
+  ring_barrier();
+  if (g + 1 < total) {
+    read_frags<Cfg>(nxt, ring + rslot * Cfg::STAGE_ELEMS, wm, wn, lane);
+    rslot = (rslot + 1 == Cfg::STAGES) ? 0 : rslot + 1;
+  }
+#pragma unroll
+  for (int i = 0; i < Cfg::FM; ++i) {
+    if (i < nf) {
+#pragma unroll
+      for (int j = 0; j < Cfg::FN; ++j)
+        acc.v[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.b[j], cur.a[i], acc.v[i][j], 0, 0, 0);
+    }
   }
 }
 
-// Row fragments of wave row wm that hold some of the tile's first `valid` rows.
+// Row fragments of wave row wm that hold some of the tile's first `valid`
+// rows: fragments i with frag_row0(wm, i) < valid.
 template <class Cfg>
 __device__ __forceinline__ int dma_active_frags(int wm, int valid) {
-  const int rows = valid - wm * (Cfg::BM / Cfg::WM);
-  return rows <= 0 ? 0 : min(Cfg::FM, (rows + 15) >> 4);
+  const int used = (valid + 15) >> 4;  // 16-row blocks holding valid rows
+  const int n = (used - wm + Cfg::WM - 1) / Cfg::WM;
+  return n <= 0 ? 0 : min(Cfg::FM, n);
 }
 
 // Output coordinates (within the tile) of acc.v[i][j][r] for the DMA driver:
@@ -476,7 +484,7 @@ __device__ __forceinline__ int dma_active_frags(int wm, int valid) {
 // at (wm, wn) = (w / WN, w % WN) of the wave grid.
 template <class Cfg>
 __device__ __forceinline__ int dma_out_row(int wm, int i, int lane) {
-  return wm * (Cfg::BM / Cfg::WM) + i * 16 + (lane & 15);
+  return frag_row0<Cfg>(wm, i) + (lane & 15);
 }
 template <class Cfg>
 __device__ __forceinline__ int dma_out_col(int wn, int j, int lane) {
@@ -510,16 +518,20 @@ __device__ __forceinline__ void dma_wait_stage(int younger) {
 // order; Prob::rows(item) gives an item's valid tile rows (row fragments past
 // them skip their MFMAs), Prob::setup(item, ld, part) fills producer part's
 // DmaLoader, Prob::epilogue(item, acc) writes an item's result (compute
-// waves). Step g (one K step of some item):
-//   producers: wait until their DMAs of stage g landed; barrier; issue stage
-//             g + STAGES - 1 into slot (g - 1) % STAGES.
-//   compute:  barrier; MFMAs of stage g; epilogue if g closes an item
-//             (the K loop of each item is specialised on how many of the
-//             wave's row fragments hold valid rows).
-// The barrier of step g publishes stage g to the compute waves and tells the
-// producer that slot (g - 1) % STAGES has been read. It is a bare s_barrier:
-// the producer's explicit vmcnt wait already orders its DMA writes, and a
-// fenced barrier would wait for every stage in flight.
+// waves). K steps are numbered g = 0 .. total-1 over the workgroup's items
+// (nk per item, nk even). Barrier "-1" publishes stage 0; barrier g then
+// publishes stage g + 1 and tells the producers that slot g % STAGES (stage
+// g, read by the compute waves during step g - 1) is free:
+//   producers: wait until their DMAs of stage g + 1 landed; barrier g; issue
+//              stage g + STAGES into slot g % STAGES.
+//   compute:   barrier g; read stage g + 1 into one register set while the
+//              MFMAs of stage g run from the other; epilogue if g closes an
+//              item; finish the reads before the next barrier.
+// nk must be even (the register sets alternate per step); d and f are
+// multiples of 64 on this path, so it is.
+// Barriers are bare s_barrier: the producers' explicit vmcnt waits already
+// order their DMA writes, and a fenced barrier would wait for every stage in
+// flight.
 template <class Cfg, class Prob>
 __device__ __forceinline__ void persistent_gemm_dma(Prob& pb, int items, int nk) {
   constexpr int S = Cfg::STAGES;
@@ -544,10 +556,15 @@ __device__ __forceinline__ void persistent_gemm_dma(Prob& pb, int items, int nk)
       }
     };
     for (int p = 0; p < S - 1 && p < total; ++p) issue_next();
+    // barrier "-1": stage 0 landed
+    dma_wait_stage<Cfg>(total - 1);
+    ring_barrier();
+    if (S - 1 < total) issue_next();
     for (int g = 0; g < total; ++g) {
-      dma_wait_stage<Cfg>(total - 1 - g);
-      __builtin_amdgcn_s_barrier();
-      if (g + S - 1 < total) issue_next();
+      // barrier g: stage g + 1 landed (the compute waves read it during step g)
+      if (g + 1 < total) dma_wait_stage<Cfg>(total - 2 - g);
+      ring_barrier();
+      if (g + S < total) issue_next();
     }
     return;
   }
@@ -555,12 +572,26 @@ __device__ __forceinline__ void persistent_gemm_dma(Prob& pb, int items, int nk)
   const int lane = threadIdx.x & 63;
   const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
   Acc<Cfg> acc;
-  int c_slot = 0;
+  Frags<Cfg> f0, f1;
+  ring_barrier();  // barrier "-1"
+  read_frags<Cfg>(f0, ring, wm, wn, lane);
+  int rslot = 1 % S;  // ring slot of the next stage to read
+  wait_lgkm0();
+  // K steps ping-pong between the two register sets (nk is even, so every
+  // item starts with its first stage in f0)
   for (int c_ord = 0; c_ord < n_mine; ++c_ord) {
     const int item = sp.first + c_ord * sp.stride;
+    const int nf = dma_active_frags<Cfg>(wm, pb.rows(item));
+    const int g0 = c_ord * nk;
     acc.zero();
-    mma_item<Cfg>(dma_active_frags<Cfg>(wm, pb.rows(item)), nk, ring, c_slot, acc, wm, wn, lane);
+    for (int kt = 0; kt < nk; kt += 2) {
+      mma_pp_step<Cfg>(g0 + kt, total, nf, ring, rslot, f0, f1, acc, wm, wn, lane);
+      wait_lgkm0();
+      mma_pp_step<Cfg>(g0 + kt + 1, total, nf, ring, rslot, f1, f0, acc, wm, wn, lane);
+      if (kt + 2 < nk) wait_lgkm0();
+    }
     pb.epilogue(item, acc);
+    wait_lgkm0();
   }
 }
 

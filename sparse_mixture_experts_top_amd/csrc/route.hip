@@ -66,7 +66,7 @@ struct RouterProb {
 };
 
 template <class Cfg>
-__global__ __launch_bounds__(kDmaThreads, 2) void router_gemm_bf16(RouterProb<Cfg> pb, int items) {
+__global__ __launch_bounds__(kDmaThreads, kDmaWavesPerSimd) void router_gemm_bf16(RouterProb<Cfg> pb, int items) {
   persistent_gemm_dma<Cfg>(pb, items, pb.d / Cfg::BK);
 }
 
@@ -104,7 +104,7 @@ static hipError_t launch_router_bf16(const Ctx& c, const moe_shape_t& s, const b
 #define MOE_ROUTER_STAGES_128 4
 #endif
 #ifndef MOE_ROUTER_STAGES_64
-#define MOE_ROUTER_STAGES_64 6
+#define MOE_ROUTER_STAGES_64 4
 #endif
 
 hipError_t launch_router(const Ctx& c, const moe_shape_t& s, const void* x, const void* w,
