@@ -258,10 +258,12 @@ moe_status_t moe_lora_bwd(const moe_shape_t* shape, const moe_lora_t* lora, cons
                           float* db_down, void* ws, size_t ws_bytes, moe_stream_t stream);
 
 /* ---- kernel timing (profiling aid) -------------------------------------
- * When enabled, the library records a pair of HIP events on the launch
- * stream around every kernel it enqueues, per kernel kind. moe_timing_read
- * waits for the recorded events and returns the summed duration and the
- * launch count of one kind since the last reset. [host] */
+ * When enabled for a kernel kind, the library records a pair of HIP events
+ * on the launch stream around every kernel of that kind it enqueues.
+ * moe_timing_read waits for the recorded events and returns the summed
+ * duration and the launch count of one kind since the last reset. Each
+ * event pair adds a little time between launches, so a measurement of the
+ * whole step should enable only the kinds it needs. [host] */
 typedef enum {
   MOE_K_ROUTER_GEMM = 0,
   MOE_K_TOPK = 1,
@@ -282,7 +284,9 @@ typedef enum {
   MOE_K_COUNT = 16
 } moe_kernel_t;
 
-moe_status_t moe_timing_enable(int32_t on);  /* also resets the totals */
+/* mask: bit k (1 << moe_kernel_t) enables timing of kind k; 0 disables all,
+ * -1 enables all. Also resets the totals. */
+moe_status_t moe_timing_enable(int32_t mask);
 moe_status_t moe_timing_read(int32_t kernel, double* total_ms, int64_t* launches);
 
 #ifdef __cplusplus

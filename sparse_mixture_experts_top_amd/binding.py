@@ -195,8 +195,17 @@ def moe_lora_bwd(shape, lora, dy, offsets, row_src, row_gate, x, x_src, act_save
                               _dev(ws, torch.uint8), ws.numel(), _stream(stream)))
 
 
-def moe_timing_enable(on: bool) -> None:
-    _check(lib().moe_timing_enable(1 if on else 0))
+def moe_timing_enable(on=True) -> None:
+    """on: False (off), True (every kernel kind) or an iterable of kind names."""
+    if on is True:
+        mask = -1
+    elif not on:
+        mask = 0
+    else:
+        mask = 0
+        for name in on:
+            mask |= 1 << KERNELS.index(name)
+    _check(lib().moe_timing_enable(mask))
 
 
 def moe_timing_read(kernel: str):

@@ -141,6 +141,7 @@ namespace {
 struct Timing {
   std::mutex mu;
   bool on = false;
+  uint32_t mask = 0;  // bit k: kernel kind k is timed
   std::vector<hipEvent_t> pool;
   std::vector<std::pair<hipEvent_t, hipEvent_t>> pending[MOE_K_COUNT];
   double total_ms[MOE_K_COUNT] = {};
@@ -181,7 +182,7 @@ void drain(Timing& t, int kid) {
 void timing_begin(int kid, hipStream_t s) {
   Timing& t = timing();
   std::lock_guard<std::mutex> g(t.mu);
-  if (!t.on) return;
+  if (!t.on || !((t.mask >> kid) & 1u)) return;
   hipEvent_t e = take_event(t);
   if (e && hipEventRecord(e, s) == hipSuccess) t_open[kid] = e;
 }
@@ -416,7 +417,7 @@ moe_status_t moe_lora_bwd(const moe_shape_t* shape, const moe_lora_t* lora, cons
       "LoRA backward");
 }
 
-moe_status_t moe_timing_enable(int32_t on) {
+moe_status_t moe_timing_enable(int32_t mask) {
   Timing& t = timing();
   std::lock_guard<std::mutex> g(t.mu);
   for (int k = 0; k < MOE_K_COUNT; ++k) {
@@ -424,14 +425,15 @@ moe_status_t moe_timing_enable(int32_t on) {
     t.total_ms[k] = 0.0;
     t.launches[k] = 0;
   }
-  if (on && t.pool.size() < 512) {
+  if (mask && t.pool.size() < 512) {
     for (int i = 0; i < 512; ++i) {
       hipEvent_t e = nullptr;
       if (hipEventCreate(&e) != hipSuccess) return fail(MOE_ERR_HIP, "hipEventCreate failed");
       t.pool.push_back(e);
     }
   }
-  t.on = on != 0;
+  t.on = mask != 0;
+  t.mask = (uint32_t)mask;
   return MOE_OK;
 }
 

@@ -104,3 +104,19 @@ def forward(b: Buffers, x, w_router, bias, w_gate, w_up, w_down, lora=None, stre
         B.moe_expert_gemm(s, xr, src, b.offsets, w_gate, w_up, w_down, lora, b.act_save, b.y_perm,
                           b.ws, stream)
     B.moe_combine(s, b.y_perm, b.slot, b.topk_gate, b.y, stream)
+
+
+def capture(fn):
+    """Record the kernels fn() enqueues (through the C entry points, on
+    torch's current stream) into one HIP graph and return it; replay() then
+    re-runs exactly those launches with the same pointers and sizes. The
+    library enqueues no memset or allocation inside its entry points, so the
+    whole forward is capturable."""
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    return g

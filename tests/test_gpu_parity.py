@@ -267,3 +267,37 @@ def test_lora_forward_backward_and_aux(b_init, x_perm):
         assert (grads["da_up"] == 0).all() and (grads["da_down"] == 0).all()
         frozen = run_forward(w.replace(lora_r=0), dev, x_perm=x_perm)
         assert torch.equal(frozen.y, buf.y)
+
+
+@pytest.mark.parametrize("name", ["rows_bf16", "capacity_bf16"])
+def test_forward_graph_replays_match_eager(name):
+    """The whole forward captured into one HIP graph: every replay (with eager
+    work and synchronisations in between, outputs cleared before each one)
+    reproduces the eager forward bitwise."""
+    w = SMALL[name]
+    say(f"[case graph {name}]")
+    dev = upload(generate(w, seed=11))
+    shape = layer.shape_of(w)
+    buf = layer.alloc(shape, logits=True)
+    pk = layer.pack_weights(shape, dev["w_gate"], dev["w_up"], dev["w_down"])
+    fw = lambda: layer.forward(buf, dev["x"], dev["w_router"], dev.get("bias"), None, None, None,
+                               packed=pk)
+    fw()
+    torch.cuda.synchronize()
+    outs = ("topk_idx", "topk_gate", "logits", "counts", "offsets", "slot", "row_src", "row_gate",
+            "y_perm", "y")
+    R = int(buf.offsets[-1].item())
+    rowwise = ("row_src", "row_gate", "y_perm")  # only the R dispatched rows are written
+    view = lambda n: getattr(buf, n)[:R] if n in rowwise else getattr(buf, n)
+    ref = {n: view(n).clone() for n in outs}
+    g = layer.capture(fw)
+    for rep in range(3):
+        for n in outs:
+            getattr(buf, n).fill_(-1 if getattr(buf, n).dtype == torch.int32 else 7.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for n in outs:
+            assert torch.equal(view(n), ref[n]), (rep, n)
+        fw()  # eager work between replays
+        torch.cuda.synchronize()
