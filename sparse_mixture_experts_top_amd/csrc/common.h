@@ -118,7 +118,7 @@ struct Workspace {
   int64_t bytes;
 };
 
-constexpr int kTokTile = 256;      // tokens per dispatch tile
+constexpr int kTokTile = 32;       // tokens per dispatch tile (one 32-bit mask per expert)
 constexpr int kTopkTokPerWaveProb = 4;  // tokens per top-k wave when softmax sums are kept
 constexpr int kGemmBM = 128;       // grouped GEMM row tile
 

@@ -10,20 +10,29 @@
 // rank of a token inside its tile comes from a per-expert token bitmask and a
 // popcount, and the capacity threshold comes from an exact radix select.
 //
-//   K3 hist      per 256-token tile: LDS histogram over E -> tile_counts
-//   K4 scan      one block: per-expert running sum over tiles -> tile_base,
-//                counts; kept = min(count, C) -> offsets (exclusive scan)
-//   K6 scatter   per tile: position of (t, j) inside its expert =
-//                tile_base + number of earlier tokens of the tile with that
-//                expert; writes slot / row_src / row_gate, or, for an expert
-//                over capacity, a candidate (gate bits, assignment)
-//   K5 capacity  per over-capacity expert: C-th largest (gate, -token) key by
-//                radix select, then kept candidates in token order -> rows
-//   K7 gather    x_perm[p] = x[row_src[p]] with 16-byte loads and stores
-//                (optional: the grouped GEMM can read x through row_src)
+// Token tiles are 32 tokens wide, so a tile's tokens routed to one expert
+// form a single 32-bit mask; T = 4096 gives 128 tiles, enough workgroups to
+// spread over the GPU.
+//
+//   K3 hist       per tile: LDS histogram over E -> tile_counts
+//   K4 tile scan  per expert (16 per workgroup, 16 threads splitting the
+//                 tiles): running sum over tiles -> tile_base, counts
+//   K6 scatter    per tile: each workgroup first scans the per-expert kept
+//                 counts, kept = min(count, C), over the experts (workgroup
+//                 0 also writes offsets / dropped); then the position of
+//                 (t, j) inside its expert = tile_base + number of earlier
+//                 tokens of the tile with that expert; writes slot / row_src
+//                 / row_gate, or, for an expert over capacity, a candidate
+//                 (gate bits, assignment)
+//   K5 capacity   per over-capacity expert: C-th largest (gate, -token) key
+//                 by radix select, then kept candidates in token order -> rows
+//   K7 gather     x_perm[p] = x[row_src[p]] with 16-byte loads and stores
+//                 (optional: the grouped GEMM can read x through row_src)
 #include "common.h"
 
 namespace moe {
+
+static_assert(kTokTile == 32, "one 32-bit token mask per (tile, expert)");
 
 __global__ __launch_bounds__(256) void dispatch_hist(const int32_t* __restrict__ idx, int T, int k,
                                                      int E, int32_t* __restrict__ tile_counts) {
@@ -38,88 +47,139 @@ __global__ __launch_bounds__(256) void dispatch_hist(const int32_t* __restrict__
   for (int e = threadIdx.x; e < E; e += 256) tile_counts[(int64_t)blockIdx.x * E + e] = cnt[e];
 }
 
-// Exclusive scan of v over the block (blockDim.x == 1024); returns the
-// exclusive prefix for this thread and writes the total to *total.
-__device__ int block_exclusive_scan_1024(int v, int* total) {
-  __shared__ int wsum[16];
+// tile_base[tl, e] = sum of tile_counts[tl' < tl, e]; counts[e] = the total.
+// Workgroup b takes experts 16b .. 16b+15; thread (part, ex) sums one
+// sixteenth of the tiles, the parts are combined in LDS, then each thread
+// writes the running sums of its part.
+constexpr int kScanParts = 16;
+__global__ __launch_bounds__(256) void dispatch_tile_scan(const int32_t* __restrict__ tile_counts,
+                                                          int ntiles, int E,
+                                                          int32_t* __restrict__ tile_base,
+                                                          int32_t* __restrict__ counts) {
+  constexpr int EX = 256 / kScanParts;
+  __shared__ int psum[kScanParts][EX];
+  const int ex = threadIdx.x % EX, part = threadIdx.x / EX;
+  const int e = blockIdx.x * EX + ex;
+  const int per = (ntiles + kScanParts - 1) / kScanParts;
+  const int lo = min(part * per, ntiles), hi = min(lo + per, ntiles);
+  int sum = 0;
+  if (e < E) {
+#pragma unroll 8
+    for (int tl = lo; tl < hi; ++tl) sum += tile_counts[(int64_t)tl * E + e];
+  }
+  psum[part][ex] = sum;
+  __syncthreads();
+  int run = 0;
+  for (int p = 0; p < part; ++p) run += psum[p][ex];
+  if (e < E) {
+#pragma unroll 8
+    for (int tl = lo; tl < hi; ++tl) {
+      const int v = tile_counts[(int64_t)tl * E + e];
+      tile_base[(int64_t)tl * E + e] = run;
+      run += v;
+    }
+    if (part == kScanParts - 1) counts[e] = run;
+  }
+}
+
+// Exclusive scans over the experts (E <= 1024, 4 per thread of a 256-thread
+// workgroup) of kept = min(local count, C) and over = local count if above C
+// (else 0): s_off[e], s_cs[e] (non-local experts contribute 0, so the scans
+// over all experts equal the scans over local experts in order). Returns
+// (total kept, total over, total dropped) through the last three arguments.
+__device__ void expert_scans(const int32_t* __restrict__ counts, int E, int e_lo, int L,
+                             int capacity, int* s_off, int* s_cs, int* tot_kept, int* tot_over,
+                             int* tot_drop) {
+  __shared__ int wk[4], wo[4], wd[4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = v;
+  int kv[4], ov[4], ks = 0, os = 0, ds = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = 4 * threadIdx.x + q;
+    const int le = e - e_lo;
+    const int c = (e < E && le >= 0 && le < L) ? counts[e] : 0;
+    const bool over = capacity > 0 && c > capacity;
+    kv[q] = over ? capacity : c;
+    ov[q] = over ? c : 0;
+    ks += kv[q];
+    os += ov[q];
+    ds += c - kv[q];
+  }
+  int ki = ks, oi = os;
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) {
-    const int o = __shfl_up(incl, m, kWave);
-    if (lane >= m) incl += o;
-  }
-  if (lane == 63) wsum[wave] = incl;
-  __syncthreads();
-  int before = 0, all = 0;
-  for (int w = 0; w < 16; ++w) {
-    const int sw = wsum[w];
-    if (w < wave) before += sw;
-    all += sw;
-  }
-  __syncthreads();
-  *total = all;
-  return before + incl - v;
-}
-
-__global__ __launch_bounds__(1024) void dispatch_scan(const int32_t* __restrict__ tile_counts,
-                                                      int ntiles, int E, int e_lo, int L,
-                                                      int capacity,
-                                                      int32_t* __restrict__ tile_base,
-                                                      int32_t* __restrict__ counts,
-                                                      int32_t* __restrict__ offsets,
-                                                      int32_t* __restrict__ cseg,
-                                                      int32_t* __restrict__ dropped) {
-  const int e = threadIdx.x;
-  int run = 0;
-  if (e < E) {
-    for (int tl = 0; tl < ntiles; ++tl) {
-      tile_base[(int64_t)tl * E + e] = run;
-      run += tile_counts[(int64_t)tl * E + e];
+    const int a = __shfl_up(ki, m, kWave), b = __shfl_up(oi, m, kWave);
+    if (lane >= m) {
+      ki += a;
+      oi += b;
     }
-    counts[e] = run;
   }
-  const int le = e - e_lo;
-  const bool local = e < E && le >= 0 && le < L;
-  const int cnt = local ? run : 0;
-  const int kept = (capacity > 0 && cnt > capacity) ? capacity : cnt;
-  const int over = (capacity > 0 && cnt > capacity) ? cnt : 0;
-  int tot_kept, tot_over;
-  const int off = block_exclusive_scan_1024(kept, &tot_kept);
-  const int coff = block_exclusive_scan_1024(over, &tot_over);
-  if (local) {
-    offsets[le] = off;
-    cseg[le] = coff;
+  int dsum = ds;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) dsum += __shfl_xor(dsum, m, kWave);
+  if (lane == 63) {
+    wk[wave] = ki;
+    wo[wave] = oi;
   }
-  if (e == 0) {
-    offsets[L] = tot_kept;
-    cseg[L] = tot_over;
+  if (lane == 0) wd[wave] = dsum;
+  __syncthreads();
+  int kb = 0, ob = 0;
+  for (int w = 0; w < wave; ++w) {
+    kb += wk[w];
+    ob += wo[w];
   }
-  // dropped = sum over local experts of (cnt - kept)
-  int tot_drop;
-  block_exclusive_scan_1024(cnt - kept, &tot_drop);
-  if (e == 0 && dropped) *dropped = tot_drop;
+  kb += ki - ks;
+  ob += oi - os;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = 4 * threadIdx.x + q;
+    if (e < E) {
+      s_off[e] = kb;
+      s_cs[e] = ob;
+    }
+    kb += kv[q];
+    ob += ov[q];
+  }
+  *tot_kept = wk[0] + wk[1] + wk[2] + wk[3];
+  *tot_over = wo[0] + wo[1] + wo[2] + wo[3];
+  *tot_drop = wd[0] + wd[1] + wd[2] + wd[3];
+  __syncthreads();
 }
 
+// 256 threads: thread (token lt = tid / 8, jg = tid % 8) handles the
+// assignments j = jg, jg + 8, ... of token tile * 32 + lt.
 __global__ __launch_bounds__(256) void dispatch_scatter(
     const int32_t* __restrict__ idx, const float* __restrict__ gate, int T, int k, int E, int e_lo,
     int L, int capacity, const int32_t* __restrict__ tile_base, const int32_t* __restrict__ counts,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ cseg,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ cseg, int32_t* __restrict__ dropped,
     int32_t* __restrict__ slot, int32_t* __restrict__ row_src, float* __restrict__ row_gate,
     uint32_t* __restrict__ cand_key, int32_t* __restrict__ cand_idx) {
-  constexpr int W = kTokTile / 32;  // bitmask words per expert
-  __shared__ uint32_t mask[1024 * W];
-  for (int i = threadIdx.x; i < E * W; i += 256) mask[i] = 0u;
-  __syncthreads();
+  __shared__ uint32_t mask[1024];
+  __shared__ int s_off[1024], s_cs[1024];
+  for (int i = threadIdx.x; i < E; i += 256) mask[i] = 0u;
+  int tot_kept, tot_over, tot_drop;
+  expert_scans(counts, E, e_lo, L, capacity, s_off, s_cs, &tot_kept, &tot_over, &tot_drop);
+  if (blockIdx.x == 0) {
+    for (int le = threadIdx.x; le < L; le += 256) {
+      offsets[le] = s_off[e_lo + le];
+      cseg[le] = s_cs[e_lo + le];
+    }
+    if (threadIdx.x == 0) {
+      offsets[L] = tot_kept;
+      cseg[L] = tot_over;
+      if (dropped) *dropped = tot_drop;
+    }
+  }
   const int tl = blockIdx.x;
-  const int lt = threadIdx.x;  // token within the tile
+  const int lt = threadIdx.x >> 3, jg = threadIdx.x & 7;
   const int t = tl * kTokTile + lt;
   const bool valid = t < T;
   if (valid)
-    for (int j = 0; j < k; ++j) atomicOr(&mask[idx[(int64_t)t * k + j] * W + (lt >> 5)], 1u << (lt & 31));
+    for (int j = jg; j < k; j += 8) atomicOr(&mask[idx[(int64_t)t * k + j]], 1u << lt);
   __syncthreads();
   if (!valid) return;
-  for (int j = 0; j < k; ++j) {
+  const uint32_t below = (1u << lt) - 1u;
+  for (int j = jg; j < k; j += 8) {
     const int64_t a = (int64_t)t * k + j;
     const int e = idx[a];
     const int le = e - e_lo;
@@ -127,18 +187,14 @@ __global__ __launch_bounds__(256) void dispatch_scatter(
       slot[a] = -1;
       continue;
     }
-    int rank = 0;
-    const uint32_t* mw = &mask[e * W];
-    for (int w = 0; w < (lt >> 5); ++w) rank += __popc(mw[w]);
-    rank += __popc(mw[lt >> 5] & ((1u << (lt & 31)) - 1u));
-    const int pos = tile_base[(int64_t)tl * E + e] + rank;
+    const int pos = tile_base[(int64_t)tl * E + e] + __popc(mask[e] & below);
     const float g = gate[a];
     if (capacity > 0 && counts[e] > capacity) {
-      const int ci = cseg[le] + pos;
+      const int ci = s_cs[e] + pos;
       cand_key[ci] = __float_as_uint(g);
       cand_idx[ci] = (int32_t)a;
     } else {
-      const int row = offsets[le] + pos;
+      const int row = s_off[e] + pos;
       slot[a] = row;
       row_src[row] = t;
       row_gate[row] = g;
@@ -267,15 +323,17 @@ hipError_t launch_dispatch(const Ctx& c, const moe_shape_t& s, const Workspace& 
   if ((err = hipGetLastError()) != hipSuccess) return err;
   {
     TimedLaunch tl(MOE_K_SCAN, c.stream);
-    hipLaunchKernelGGL(dispatch_scan, dim3(1), dim3(1024), 0, c.stream, ws.tile_counts, ntiles,
-                       s.E, s.e_lo, L, s.capacity, ws.tile_base, counts, offsets, ws.cseg, dropped);
+    hipLaunchKernelGGL(dispatch_tile_scan, dim3((s.E + 256 / kScanParts - 1) / (256 / kScanParts)),
+                       dim3(256), 0, c.stream,
+                       ws.tile_counts, ntiles, s.E, ws.tile_base, counts);
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  if (ntiles > 0) {
+  {
+    // at least one workgroup: workgroup 0 writes offsets / dropped even for T = 0
     TimedLaunch tl(MOE_K_SCATTER, c.stream);
-    hipLaunchKernelGGL(dispatch_scatter, dim3(ntiles), dim3(kTokTile), 0, c.stream, idx, gate, s.T,
-                       s.k, s.E, s.e_lo, L, s.capacity, ws.tile_base, counts, offsets, ws.cseg,
-                       slot, row_src, row_gate, ws.cand_key, ws.cand_idx);
+    hipLaunchKernelGGL(dispatch_scatter, dim3(ntiles > 0 ? ntiles : 1), dim3(256), 0, c.stream, idx,
+                       gate, s.T, s.k, s.E, s.e_lo, L, s.capacity, ws.tile_base, counts, offsets,
+                       ws.cseg, dropped, slot, row_src, row_gate, ws.cand_key, ws.cand_idx);
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (s.capacity > 0) {

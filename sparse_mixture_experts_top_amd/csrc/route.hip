@@ -148,39 +148,20 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
-// Bitonic sort of one 64-bit key per lane across the wave, descending by
-// lane (lane 0 ends with the largest key).
-__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int size = 2; size <= 64; size <<= 1) {
-#pragma unroll
-    for (int j = size >> 1; j >= 1; j >>= 1) {
-      const uint32_t lo = __shfl_xor((uint32_t)v, j, kWave);
-      const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), j, kWave);
-      const uint64_t o = ((uint64_t)hi << 32) | lo;
-      // descending overall: blocks with (lane & size) == 0 sort descending
-      const bool desc = (lane & size) == 0;
-      const bool lower = (lane & j) == 0;
-      const bool take_max = (desc == lower);
-      const uint64_t mx = o > v ? o : v, mn = o > v ? v : o;
-      v = take_max ? mx : mn;
-    }
-  }
-  return v;
-}
-
 // One wave per token. Lane l holds the logits of experts l, l+64, ... as
 // 64-bit keys (ordered logit bits << 32 | ~expert): the largest key is the
 // largest logit and, among equal logits, the lowest expert id; keys are
 // unique. The k largest keys are found exactly in three steps:
-//   1. tau = k-th largest of the 64 lane maxima (bitwise search with ballot
-//      counts, no cross-lane shuffles). At least k keys (those maxima) are
-//      >= tau, so every one of the k largest keys is >= tau.
+//   1. tau = the high word of the k-th largest of the 64 lane maxima
+//      (bitwise search over the 32 logit bits with ballot counts, no
+//      cross-lane shuffles). At least k keys (those maxima) have a high word
+//      >= tau, so every one of the k largest keys does.
 //   2. keys >= tau are compacted through LDS (ballot + popcount positions).
-//   3. if at most 64 survive, one bitonic sort across the wave orders them
-//      and lanes 0..k-1 hold the answer; otherwise (many equal logits) k
-//      rounds of "wave maximum, remove it" over all keys.
+//   3. if at most 64 survive (typically k plus a few), each survivor counts
+//      the larger survivors (LDS broadcast reads) and the one of rank r < k
+//      lands in position r, so lanes 0..k-1 hold the answer in order;
+//      otherwise (many equal logits) k rounds of "wave maximum, remove it"
+//      over all keys.
 // Gates: exp(l_j - l_0) / sum over the picks. With prob_part, the wave also
 // sums the full softmax of its tokens per expert; the block's waves are added
 // in a fixed order into prob_part[block, E].
@@ -190,6 +171,7 @@ __global__ __launch_bounds__(256) void topk_softmax(const float* __restrict__ lo
                                                     float* __restrict__ gate_out,
                                                     float* __restrict__ prob_part) {
   __shared__ uint64_t cand[4][64];
+  __shared__ uint64_t sel[4][32];
   __shared__ float red[4][EPL * 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));  // lanes < this one
@@ -215,9 +197,13 @@ __global__ __launch_bounds__(256) void topk_softmax(const float* __restrict__ lo
       }
       lmax = key[i] > lmax ? key[i] : lmax;
     }
-    // 1. tau: largest value with at least k lane maxima >= it (a key value)
+    // 1. tau: the largest logit-bits value t (the key's high word) such that
+    //    at least k lane maxima have high word >= t; then at least k keys are
+    //    >= t << 32, so the k-th largest key is too, and every top-k key is a
+    //    candidate below. The low word (expert id) only orders ties, which
+    //    the sort of the candidates settles.
     uint64_t tau = 0;
-    for (int b = 63; b >= 0; --b) {
+    for (int b = 63; b >= 32; --b) {
       const uint64_t c = tau | (1ull << b);
       if (__popcll(__ballot(lmax >= c)) >= k) tau = c;
     }
@@ -237,9 +223,17 @@ __global__ __launch_bounds__(256) void topk_softmax(const float* __restrict__ lo
       }
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      // rank of each candidate = number of larger candidates (keys are
+      // unique); the candidate of rank r < k goes to position r
       const uint64_t v = lane < n ? cand[wave][lane] : 0ull;
+      int rank = 0;
+      for (int j = 0; j < n; ++j) rank += cand[wave][j] > v ? 1 : 0;
       __builtin_amdgcn_wave_barrier();
-      mine = wave_sort_desc(v);
+      if (lane < n && rank < k) sel[wave][rank] = v;
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      mine = lane < k ? sel[wave][lane] : 0ull;
+      __builtin_amdgcn_wave_barrier();
     } else {
       uint64_t kk[EPL];
 #pragma unroll
