@@ -12,29 +12,29 @@
 //   K-tiles   one block turns offsets into the list of (expert, first row)
 //             row tiles of 128 rows; the GEMMs walk that list on the device,
 //             so no row count ever travels to the host.
-//   K8 gate_up  per (row tile, 64 FFN columns), reading token rows through
+//   K8 gate_up  per (row tile, 128 FFN columns), reading token rows through
 //             row_src (the dispatch gather fused into the A loader, so the
 //             permuted copy of x never has to exist); the B tile interleaves 16 rows
 //             of W_g and the same 16 rows of W_u, so each lane ends up holding
 //             G and U of the same (row, column) and applies silu(G) * U in
 //             registers; H is rounded to bf16.
-//   K9 down   per (row tile, 128 output columns): O = H W_d^T (+ LoRA).
-// Both run on the persistent pipelined driver of mfma_tile.h: a grid of 2
-// workgroups per CU walks the items, each XCD taking a contiguous range so
-// row tiles that share A or B stay in one L2.
+//   K9 down   per (row tile, 256 output columns): O = H W_d^T (+ LoRA).
+// Both run on the persistent pipelined driver of mfma_tile.h: one workgroup
+// per CU walks the items, each XCD taking a contiguous range so row tiles
+// that share A or B stay in one L2.
 // fp32 path (small parity shapes): one thread per output element.
 #include "common.h"
 #include "mfma_tile.h"
 
 namespace moe {
 
-// Ring depth of the grouped GEMMs (4 slots of 16 KB: two workgroups per CU).
+// Ring depth of the grouped GEMMs (slots of 24 KB; one workgroup per CU).
 #ifndef MOE_GEMM_STAGES
-#define MOE_GEMM_STAGES 4
+#define MOE_GEMM_STAGES 6
 #endif
-// 2 x 2 compute waves, each with 4 interleaved row fragments x 4 column
-// fragments (64 x 64 of the tile).
-using GemmCfg = DmaCfg<kGemmBM, 128, MOE_GEMM_STAGES, 2>;
+// 128 x 256 tiles; 2 x 2 compute waves, each with 4 interleaved row
+// fragments x 8 column fragments (64 x 128 of the tile).
+using GemmCfg = DmaCfg<kGemmBM, 256, MOE_GEMM_STAGES, 2>;
 
 __global__ __launch_bounds__(1024) void build_row_tiles(const int32_t* __restrict__ offsets, int L,
                                                         int bm, int max_tiles,
@@ -111,7 +111,7 @@ __device__ __forceinline__ int64_t gathered_row(const int32_t* row_src, const Ro
   return (l3[1] & m3) | (l3[0] & ~m3);
 }
 
-// K8: H = silu(X W_g^T) * (X W_u^T [+ s Z_u B_u^T]) for one (row tile, 64
+// K8: H = silu(X W_g^T) * (X W_u^T [+ s Z_u B_u^T]) for one (row tile, 128
 // FFN columns) item. Rows of X are x[row_src[p]] (gather fused into the A
 // loader) or, with row_src == NULL, x[p] of an already gathered matrix.
 template <class Cfg>
@@ -130,7 +130,7 @@ struct GateUpProb {
   float scale;
   bf16_t* hbuf;
   bf16_t* act_save;
-  static constexpr int HALF = Cfg::BN / 2;  // FFN columns per item
+  static constexpr int HALF = Cfg::BN / 2;  // FFN columns per item (the last item may be partial)
 
   __device__ __forceinline__ int rows(int item) const {
     return row_tile<Cfg::BM>(tiles, offsets, item / nt).valid;
@@ -148,10 +148,17 @@ struct GateUpProb {
       ld.a[q] = x + src * d + ce;
     }
     if (w_packed) {
-      const bf16_t* tile0 = w_packed + ((int64_t)t.le * nt + ni) * (d / Cfg::BK) * kPackTileElems;
+      // packed tiles hold 64 FFN columns (128 interleaved rows) each; blocks
+      // past f (a partial last item) re-read the last block, never stored
+      const int nb = f / 64, nk = d / Cfg::BK;
+      const int64_t bstride = (int64_t)nk * kPackTileElems;
 #pragma unroll
-      for (int q = 0; q < Cfg::B_DMA / kProducers; ++q)
-        ld.b[q] = packed_b_ptr<Cfg>(tile0, q * kProducers + part);
+      for (int q = 0; q < Cfg::B_DMA / kProducers; ++q) {
+        const int i = q * kProducers + part;
+        const int b = min(ni * (HALF / 64) + i / (kPackTileRows / 16), nb - 1);
+        const bf16_t* tile0 = w_packed + ((int64_t)t.le * nb + b) * bstride;
+        ld.b[q] = packed_b_ptr(tile0, i % (kPackTileRows / 16), 0);
+      }
       ld.b_kstep = kPackTileElems;
       return;
     }
@@ -159,7 +166,7 @@ struct GateUpProb {
     for (int q = 0; q < Cfg::B_DMA / kProducers; ++q) {
       const int jb = dma_row(q * kProducers + part);
       const int frag = jb >> 4;
-      const int fcol = ni * HALF + (frag >> 1) * 16 + (jb & 15);
+      const int fcol = min(ni * HALF + (frag >> 1) * 16 + (jb & 15), f - 1);
       ld.b[q] = ((frag & 1) ? w_up : w_gate) + ((int64_t)t.le * f + fcol) * d + ce;
     }
   }
@@ -180,6 +187,8 @@ struct GateUpProb {
       for (int jj = 0; jj < Cfg::FN; jj += 2) {
         // fragment jg (even) holds G, jg + 1 holds U, for the same 16 FFN columns
         const int jg = wn * Cfg::FN + jj;
+        // f % 64 == 0: a 16-column fragment pair is all inside f or all past it
+        if (ni * HALF + (jg >> 1) * 16 >= f) continue;
         const int fcol = ni * HALF + (jg >> 1) * 16 + (lane >> 4) * 4;
         float h[4], g[4];
 #pragma unroll
@@ -214,7 +223,7 @@ __global__ __launch_bounds__(kDmaThreads, kDmaWavesPerSimd) void gate_up_bf16(Ga
   persistent_gemm_dma<Cfg>(pb, items, pb.d / Cfg::BK);
 }
 
-// K9: O = H W_d^T [+ s Z_d B_d^T] for one (row tile, 128 output columns) item.
+// K9: O = H W_d^T [+ s Z_d B_d^T] for one (row tile, 256 output columns) item.
 template <class Cfg>
 struct DownProb {
   const bf16_t* hbuf;
@@ -241,10 +250,17 @@ struct DownProb {
     for (int q = 0; q < Cfg::A_DMA / kProducers; ++q)
       ld.a[q] = hbuf + (t.row0 + min(dma_row(q * kProducers + part), t.valid - 1)) * f + ce;
     if (w_packed) {
-      const bf16_t* tile0 = w_packed + ((int64_t)t.le * nt + item % nt) * (f / Cfg::BK) * kPackTileElems;
+      // packed tiles hold 128 output columns each; blocks past d (a partial
+      // last item) re-read the last block, never stored
+      const int nb = d / kPackTileRows, nk = f / Cfg::BK;
+      const int64_t bstride = (int64_t)nk * kPackTileElems;
 #pragma unroll
-      for (int q = 0; q < Cfg::B_DMA / kProducers; ++q)
-        ld.b[q] = packed_b_ptr<Cfg>(tile0, q * kProducers + part);
+      for (int q = 0; q < Cfg::B_DMA / kProducers; ++q) {
+        const int i = q * kProducers + part;
+        const int b = min((item % nt) * (Cfg::BN / kPackTileRows) + i / (kPackTileRows / 16), nb - 1);
+        const bf16_t* tile0 = w_packed + ((int64_t)t.le * nb + b) * bstride;
+        ld.b[q] = packed_b_ptr(tile0, i % (kPackTileRows / 16), 0);
+      }
       ld.b_kstep = kPackTileElems;
       return;
     }
@@ -442,11 +458,12 @@ hipError_t launch_expert_gemm(const Ctx& c, const moe_shape_t& s, const Workspac
                                       lora->a_up, true, lora->r, ws.zu);
     if (err != hipSuccess) return err;
   }
-  const int grid = c.num_cus * 2;  // two 64 KB-LDS workgroups fit one CU
+  const int grid = c.num_cus;  // one workgroup per CU (see mfma_tile.h)
   {
     GateUpProb<GemmCfg> pb{xr, row_src, offsets, ws.gemm_tiles, (const bf16_t*)w_gate,
                            (const bf16_t*)w_up, (const bf16_t*)gu_packed, s.d, s.f,
-                           s.f / GateUpProb<GemmCfg>::HALF, s.e_hi - s.e_lo,
+                           (s.f + GateUpProb<GemmCfg>::HALF - 1) / GateUpProb<GemmCfg>::HALF,
+                           s.e_hi - s.e_lo,
                            lora ? ws.zu : nullptr, lora ? lora->b_up : nullptr, lora ? lora->r : 0,
                            lora ? lora->scale : 0.f, (bf16_t*)ws.hbuf, (bf16_t*)act_save};
     TimedLaunch tl(MOE_K_GATE_UP, c.stream);

@@ -273,7 +273,7 @@ __device__ __forceinline__ void persistent_gemm(Prob& pb, int items, int nk, bf1
 // bytes; the 64 lanes of one instruction fill 1 KB of LDS in lane order), so
 // no registers hold tiles in transit and several K steps can be in flight.
 //
-// Wave roles. A workgroup has 4 compute waves and 2 producer waves. The
+// Wave roles. A workgroup has 4 compute waves and 4 producer waves. The
 // producers issue every DMA of the ring and never store; the compute waves
 // read LDS, run the MFMAs and write the results. On this GPU stores share
 // the vector-memory counter with loads and the counter retires in issue
@@ -282,7 +282,7 @@ __device__ __forceinline__ void persistent_gemm(Prob& pb, int items, int nk, bf1
 // acknowledged - a bubble of a full write latency after every output tile.
 // With the roles split, a producer's waits count its own DMAs only (a
 // constant in the steady state) and the compute waves never wait on memory
-// counters. Two producers share each stage's DMAs: one wave alone issues
+// counters. Four producers share each stage's DMAs: one wave alone issues
 // them too slowly to keep the memory system busy.
 //
 // K step = 32. A stage holds A [BM][32] and B [BN][32] bf16 (64-byte rows,
@@ -299,12 +299,14 @@ __device__ __forceinline__ void persistent_gemm(Prob& pb, int items, int nk, bf1
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
+// One workgroup per CU: 4 compute waves (one per SIMD, each with a 64-row x
+// BN/2-column share of the tile) and 4 producer waves (one per SIMD). With
+// two waves per SIMD each wave may use 256 registers, which the compute
+// waves' accumulators and double-buffered operands need.
 constexpr int kComputeWaves = 4;  // waves 0..3
-constexpr int kProducers = 2;     // waves 4..5; producer p issues the DMAs i with i % kProducers == p
+constexpr int kProducers = 4;     // waves 4..7; producer p issues the DMAs i with i % kProducers == p
 constexpr int kDmaThreads = 64 * (kComputeWaves + kProducers);  // workgroup size of the DMA GEMMs
-// two workgroups per CU: 12 waves over 4 SIMDs (the launch-bounds occupancy
-// hint is in waves per SIMD, which caps each wave at 512 / 3 registers)
-constexpr int kDmaWavesPerSimd = (2 * (kComputeWaves + kProducers) + 3) / 4;
+constexpr int kDmaWavesPerSimd = (kComputeWaves + kProducers) / 4;  // launch-bounds occupancy hint
 
 template <int BM_, int BN_, int STAGES_ = 4, int WM_ = 2>
 struct DmaCfg {
@@ -385,15 +387,19 @@ __device__ __forceinline__ void dma_issue(const DmaLoader<Cfg>& ld, int kt, bf16
     dma16(ld.b[q] + kb, stage + Cfg::A_ELEMS + 16 * (q * kProducers + part) * Cfg::BK);
 }
 
-// Packed B operand: the weight tile of one (n block, K step) stored as the
-// exact image of its LDS stage (BN rows x 32, chunks swizzled as above), so
-// a DMA instruction copies 1 KB of contiguous memory. Pointer for this lane's
-// chunk of DMA instruction i, K step 0, given the tile's base.
-template <class Cfg>
-__device__ __forceinline__ const bf16_t* packed_b_ptr(const bf16_t* tile0, int i) {
-  return tile0 + (int64_t)i * 16 * Cfg::BK + (threadIdx.x & 63) * 8;
+// Packed B operand: a weight tile of 128 rows x one K step stored as the
+// exact image of its part of an LDS stage (chunks swizzled as above), so a
+// DMA instruction copies 1 KB of contiguous memory. A B stage of BN rows
+// spans BN / 128 such tiles. Pointer for this lane's chunk of DMA
+// instruction i (rows 16 i .. 16 i + 15 of the stage) at K step 0, given the
+// base of the stage's first tile and the element distance between the tiles
+// of consecutive 128-row blocks.
+constexpr int kPackTileRows = 128;
+constexpr int kPackTileElems = kPackTileRows * 32;  // one packed weight tile (8 KB)
+__device__ __forceinline__ const bf16_t* packed_b_ptr(const bf16_t* tile0, int i, int64_t block_stride) {
+  constexpr int per_tile = kPackTileRows / 16;  // DMA instructions per tile
+  return tile0 + (i / per_tile) * block_stride + (int64_t)(i % per_tile) * 16 * 32 + (threadIdx.x & 63) * 8;
 }
-constexpr int kPackTileElems = 128 * 32;  // one packed weight tile: 128 rows x 32 (8 KB)
 
 // First tile row of row fragment i of wave row wm. Row fragments are
 // interleaved over the wave rows (wave row wm holds fragments wm, wm + WM,
