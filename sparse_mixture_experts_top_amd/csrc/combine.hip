@@ -7,7 +7,9 @@
 // One workgroup per token (grid-stride over tokens). The token's slots and
 // gates are staged in LDS; each thread then owns 8 consecutive columns and
 // reads them from each selected row with one 16-byte load (bf16), so a row is
-// read by the workgroup as contiguous 4-8 KB.
+// read by the workgroup as contiguous 4-8 KB. The loads of 8 rows are issued
+// together and then accumulated in j order (the summation order is part of
+// the definition), so their latencies overlap.
 #include "common.h"
 
 namespace moe {
@@ -16,6 +18,7 @@ __global__ __launch_bounds__(256) void combine_bf16(const bf16_t* __restrict__ y
                                                     const int32_t* __restrict__ slot,
                                                     const float* __restrict__ gate, int T, int k,
                                                     int d, bf16_t* __restrict__ y) {
+  constexpr int B = 8;  // rows loaded per batch, before they are accumulated in order
   __shared__ int s_slot[32];
   __shared__ float s_gate[32];
   const int nvec = d / 8;
@@ -27,15 +30,25 @@ __global__ __launch_bounds__(256) void combine_bf16(const bf16_t* __restrict__ y
     __syncthreads();
     for (int v = threadIdx.x; v < nvec; v += blockDim.x) {
       float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      for (int j = 0; j < k; ++j) {
-        const int sl = s_slot[j];
-        if (sl < 0) continue;
-        const float g = s_gate[j];
-        const uint4 raw = *reinterpret_cast<const uint4*>(y_perm + (int64_t)sl * d + v * 8);
-        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+      for (int j0 = 0; j0 < k; j0 += B) {
+        uint4 raw[B];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-          acc[u] = fmaf(g, bf16_to_f32(static_cast<bf16_t>(w[u >> 1] >> ((u & 1) * 16))), acc[u]);
+        for (int b = 0; b < B; ++b) {
+          const int j = j0 + b;
+          const int sl = j < k ? s_slot[j] : -1;
+          raw[b] = sl >= 0 ? *reinterpret_cast<const uint4*>(y_perm + (int64_t)sl * d + v * 8)
+                           : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          const int j = j0 + b;
+          if (j >= k || s_slot[j] < 0) continue;
+          const float g = s_gate[j];
+          const uint32_t w[4] = {raw[b].x, raw[b].y, raw[b].z, raw[b].w};
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            acc[u] = fmaf(g, bf16_to_f32(static_cast<bf16_t>(w[u >> 1] >> ((u & 1) * 16))), acc[u]);
+        }
       }
       uint32_t o[4];
 #pragma unroll
