@@ -26,6 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/sec (route+dispatch+experts+combine); % bf16 MFMA/HBM peak"
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA, vendor figure
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
 PMC_FILE = os.path.join(ROOT, "profiles", "gate_up_full_router_pmc.txt")
@@ -227,6 +228,30 @@ def main() -> int:
             "avg_us": round(gu_us, 2)}
     # layer-level figures for context
     flops = 2 * w.T * w.d * w.E + 6 * R * w.d * w.f
+    # every stage against its own roofline, from the breakdown pass (durations
+    # there include the event pair around each launch)
+    stage_work = {
+        "router_gemm": ("mfma", 2.0 * w.T * w.d * w.E),
+        "topk": ("hbm", w.T * w.E * 4 + w.T * w.k * 8),
+        "dispatch": ("hbm", 3 * w.T * w.k * 4 + w.T * w.k * 4 + R * 8),
+        "gate_up": ("hbm", gu_bytes),
+        "down": ("hbm", active * w.d * w.f * 2 + R * w.f * 2 + R * w.d * 2),
+        "combine": ("hbm", R * w.d * 2 + w.T * w.k * 8 + w.T * w.d * 2),
+    }
+    stage_us = {k: v["avg_us"] for k, v in kernels.items()}
+    stage_us["dispatch"] = sum(stage_us.get(n, 0.0) for n in ("hist", "scan", "scatter", "capacity"))
+    stages = {}
+    for name, (bound, work) in stage_work.items():
+        us = stage_us.get(name)
+        if not us:
+            continue
+        rate = work / (us * 1e-6)
+        if bound == "mfma":
+            stages[name] = {"bound": "mfma", "us": round(us, 2), "tflops": round(rate / 1e12, 1),
+                            "frac": round(rate / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+        else:
+            stages[name] = {"bound": "hbm", "us": round(us, 2), "gbs": round(rate / 1e9, 1),
+                            "frac": round(rate / 1e9 / HBM_PEAK_GBS, 4)}
     out = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
@@ -239,6 +264,7 @@ def main() -> int:
         "roofline": roof,
         "layer_tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
         "kernels_us": {k: round(v["avg_us"], 2) for k, v in kernels.items()},
+        "stage_roofline": stages,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp)

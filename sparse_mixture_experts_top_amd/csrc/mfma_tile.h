@@ -273,8 +273,8 @@ __device__ __forceinline__ void persistent_gemm(Prob& pb, int items, int nk, bf1
 // bytes; the 64 lanes of one instruction fill 1 KB of LDS in lane order), so
 // no registers hold tiles in transit and several K steps can be in flight.
 //
-// Wave roles. A workgroup has 4 compute waves and 4 producer waves. The
-// producers issue every DMA of the ring and never store; the compute waves
+// Wave roles. A workgroup has compute waves and producer waves (counts in
+// DmaCfg). The producers issue every DMA of the ring and never store; the compute waves
 // read LDS, run the MFMAs and write the results. On this GPU stores share
 // the vector-memory counter with loads and the counter retires in issue
 // order, so in a wave that both loads and stores, every load issued after an
@@ -282,7 +282,7 @@ __device__ __forceinline__ void persistent_gemm(Prob& pb, int items, int nk, bf1
 // acknowledged - a bubble of a full write latency after every output tile.
 // With the roles split, a producer's waits count its own DMAs only (a
 // constant in the steady state) and the compute waves never wait on memory
-// counters. Four producers share each stage's DMAs: one wave alone issues
+// counters. Several producers share each stage's DMAs: one wave alone issues
 // them too slowly to keep the memory system busy.
 //
 // K step = 32. A stage holds A [BM][32] and B [BN][32] bf16 (64-byte rows,
@@ -299,23 +299,24 @@ __device__ __forceinline__ void persistent_gemm(Prob& pb, int items, int nk, bf1
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
-// One workgroup per CU: 4 compute waves (one per SIMD, each with a 64-row x
-// BN/2-column share of the tile) and 4 producer waves (one per SIMD). With
-// two waves per SIMD each wave may use 256 registers, which the compute
-// waves' accumulators and double-buffered operands need.
-constexpr int kComputeWaves = 4;  // waves 0..3
-constexpr int kProducers = 4;     // waves 4..7; producer p issues the DMAs i with i % kProducers == p
-constexpr int kDmaThreads = 64 * (kComputeWaves + kProducers);  // workgroup size of the DMA GEMMs
-constexpr int kDmaWavesPerSimd = (kComputeWaves + kProducers) / 4;  // launch-bounds occupancy hint
 
-template <int BM_, int BN_, int STAGES_ = 4, int WM_ = 2>
+// Tile BM x BN, STAGES ring slots, CW compute waves (waves 0 .. CW-1) in a
+// WM x (CW / WM) grid over the tile and PW producer waves (waves CW ..
+// CW+PW-1; producer p issues the DMAs i with i % PW == p). A workgroup runs
+// alone on its CU (THREADS = 64 (CW + PW)); the occupancy hint WAVES_PER_SIMD
+// caps the registers per wave at 512 / WAVES_PER_SIMD.
+template <int BM_, int BN_, int STAGES_ = 4, int WM_ = 2, int CW_ = 4, int PW_ = 4>
 struct DmaCfg {
   static constexpr int BM = BM_;
   static constexpr int BN = BN_;
   static constexpr int BK = 32;
   static constexpr int STAGES = STAGES_;  // ring slots; STAGES - 1 stages in flight
+  static constexpr int CW = CW_;
+  static constexpr int PW = PW_;
+  static constexpr int THREADS = 64 * (CW + PW);
+  static constexpr int WAVES_PER_SIMD = (CW + PW + 3) / 4;
   static constexpr int WM = WM_;          // the compute waves form a WM x WN grid over the tile
-  static constexpr int WN = kComputeWaves / WM_;
+  static constexpr int WN = CW_ / WM_;
   static constexpr int FM = BM / (16 * WM);  // 16 x 16 fragments per wave along M
   static constexpr int FN = BN / (16 * WN);
   static constexpr int A_DMA = BM / 16;  // producer DMA instructions per stage (16 rows each)
@@ -327,13 +328,14 @@ struct DmaCfg {
   static_assert(WM == 1 || WM == 2 || WM == 4, "wave grid");
   static_assert(FM >= 1 && FN >= 1 && FM * 16 * WM == BM && FN * 16 * WN == BN, "fragments");
   static_assert(BM % 16 == 0 && BN % 16 == 0, "DMA tiles are multiples of 16 rows");
-  static constexpr int DMA_PER_PRODUCER = DMA_PER_STAGE / kProducers;  // per stage
-  static_assert(A_DMA % kProducers == 0 && B_DMA % kProducers == 0, "DMA split");
+  static constexpr int DMA_PER_PRODUCER = DMA_PER_STAGE / PW;  // per stage
+  static_assert(A_DMA % PW == 0 && B_DMA % PW == 0, "DMA split");
+  static_assert(CW % WM == 0, "wave grid");
   static_assert(STAGES >= 3 && (STAGES - 2) * DMA_PER_PRODUCER <= 63, "ring depth vs vmcnt");
 };
 
 // Lane pointers of one producer for one item: a[q] / b[q] belong to the
-// producer's q-th DMA instruction of each operand, i = q * kProducers + part,
+// producer's q-th DMA instruction of each operand, i = q * PW + part,
 // and point at the logical chunk this lane fetches ((lane & 3) ^
 // chunk_key(lane / 4)) of tile row 16 i + lane / 4; set by
 // Prob::setup(item, ld, part).
@@ -341,8 +343,8 @@ struct DmaCfg {
 // (32 for a row-major operand; one whole packed tile for a packed one).
 template <class Cfg>
 struct DmaLoader {
-  const bf16_t* a[Cfg::A_DMA / kProducers];
-  const bf16_t* b[Cfg::B_DMA / kProducers];
+  const bf16_t* a[Cfg::A_DMA / Cfg::PW];
+  const bf16_t* b[Cfg::B_DMA / Cfg::PW];
   int a_kstep = Cfg::BK;
   int b_kstep = Cfg::BK;
 };
@@ -375,16 +377,16 @@ __device__ __forceinline__ void dma16(const void* g, const bf16_t* lds) {
 }
 
 // Producer `part`'s share of the DMA instructions of K step kt into stage
-// `stage`: A and B instructions i with i % kProducers == part.
+// `stage`: A and B instructions i with i % PW == part.
 template <class Cfg>
 __device__ __forceinline__ void dma_issue(const DmaLoader<Cfg>& ld, int kt, bf16_t* stage, int part) {
   const int64_t ka = (int64_t)kt * ld.a_kstep, kb = (int64_t)kt * ld.b_kstep;
 #pragma unroll
-  for (int q = 0; q < Cfg::A_DMA / kProducers; ++q)
-    dma16(ld.a[q] + ka, stage + 16 * (q * kProducers + part) * Cfg::BK);
+  for (int q = 0; q < Cfg::A_DMA / Cfg::PW; ++q)
+    dma16(ld.a[q] + ka, stage + 16 * (q * Cfg::PW + part) * Cfg::BK);
 #pragma unroll
-  for (int q = 0; q < Cfg::B_DMA / kProducers; ++q)
-    dma16(ld.b[q] + kb, stage + Cfg::A_ELEMS + 16 * (q * kProducers + part) * Cfg::BK);
+  for (int q = 0; q < Cfg::B_DMA / Cfg::PW; ++q)
+    dma16(ld.b[q] + kb, stage + Cfg::A_ELEMS + 16 * (q * Cfg::PW + part) * Cfg::BK);
 }
 
 // Packed B operand: a weight tile of 128 rows x one K step stored as the
@@ -548,8 +550,8 @@ __device__ __forceinline__ void persistent_gemm_dma(Prob& pb, int items, int nk)
   const int total = n_mine * nk;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 
-  if (wave >= kComputeWaves) {
-    const int part = wave - kComputeWaves;
+  if (wave >= Cfg::CW) {
+    const int part = wave - Cfg::CW;
     DmaLoader<Cfg> ld;
     int l_ord = 0, l_kt = 0, l_slot = 0;  // load cursor
     pb.setup(sp.first, ld, part);

@@ -29,11 +29,11 @@ struct RouterProb {
     const int m0 = (item / nt) * Cfg::BM, n0 = (item % nt) * Cfg::BN;
     const int ce = dma_chunk_elem();
 #pragma unroll
-    for (int q = 0; q < Cfg::A_DMA / kProducers; ++q)
-      ld.a[q] = x + (int64_t)min(m0 + dma_row(q * kProducers + part), T - 1) * d + ce;
+    for (int q = 0; q < Cfg::A_DMA / Cfg::PW; ++q)
+      ld.a[q] = x + (int64_t)min(m0 + dma_row(q * Cfg::PW + part), T - 1) * d + ce;
 #pragma unroll
-    for (int q = 0; q < Cfg::B_DMA / kProducers; ++q)
-      ld.b[q] = w + (int64_t)min(n0 + dma_row(q * kProducers + part), E - 1) * d + ce;
+    for (int q = 0; q < Cfg::B_DMA / Cfg::PW; ++q)
+      ld.b[q] = w + (int64_t)min(n0 + dma_row(q * Cfg::PW + part), E - 1) * d + ce;
   }
 
   __device__ __forceinline__ void epilogue(int item, Acc<Cfg>& acc) const {
@@ -66,7 +66,7 @@ struct RouterProb {
 };
 
 template <class Cfg>
-__global__ __launch_bounds__(kDmaThreads, kDmaWavesPerSimd) void router_gemm_bf16(RouterProb<Cfg> pb, int items) {
+__global__ __launch_bounds__(Cfg::THREADS, Cfg::WAVES_PER_SIMD) void router_gemm_bf16(RouterProb<Cfg> pb, int items) {
   persistent_gemm_dma<Cfg>(pb, items, pb.d / Cfg::BK);
 }
 
@@ -91,31 +91,40 @@ static hipError_t launch_router_bf16(const Ctx& c, const moe_shape_t& s, const b
                                      const bf16_t* w, const float* bias, float* logits) {
   const int mt = (s.T + Cfg::BM - 1) / Cfg::BM, nt = (s.E + Cfg::BN - 1) / Cfg::BN;
   const int items = mt * nt;
-  const int grid = std::min(((items + 7) / 8) * 8, c.num_cus * 2);
+  // one workgroup per CU (the workgroups are sized to fill one), a multiple of 8 (XCDs)
+  const int grid = std::min(((items + 7) / 8) * 8, c.num_cus);
   RouterProb<Cfg> pb{x, w, bias, logits, s.T, s.d, s.E, nt};
   TimedLaunch tl(MOE_K_ROUTER_GEMM, c.stream);
-  hipLaunchKernelGGL(router_gemm_bf16<Cfg>, dim3(grid), dim3(kDmaThreads), 0, c.stream, pb, items);
+  hipLaunchKernelGGL(router_gemm_bf16<Cfg>, dim3(grid), dim3(Cfg::THREADS), 0, c.stream, pb, items);
   return hipGetLastError();
 }
 
-// Ring depths: the router's operands come from L2 / MALL, so each K step is
-// short and the ring has to cover the cache latency.
-#ifndef MOE_ROUTER_STAGES_128
-#define MOE_ROUTER_STAGES_128 4
+// Router tile configurations (the router is a dense, compute-bound GEMM, so
+// the large ones run 8 compute waves - two per SIMD, which the MFMA issue
+// rate needs - next to 4 producers):
+//   large   128 x 256, 8 compute waves of 64 x 64, when there are at least
+//           as many such tiles as CUs (e.g. T = 16384, E = 896);
+//   medium  128 x 128, 8 compute waves of 64 x 32, when the 128 x 128 tiles
+//           cover at least half of the CUs (e.g. T = 4096, E = 896);
+//   small   64 x 128, 4 compute waves, otherwise.
+#ifndef MOE_ROUTER_STAGES
+#define MOE_ROUTER_STAGES 6
 #endif
-#ifndef MOE_ROUTER_STAGES_64
-#define MOE_ROUTER_STAGES_64 4
-#endif
+using RouterLarge = DmaCfg<128, 256, MOE_ROUTER_STAGES, 2, 8, 4>;
+using RouterMedium = DmaCfg<128, 128, MOE_ROUTER_STAGES, 2, 8, 4>;
+using RouterSmall = DmaCfg<64, 128, 4, 2, 4, 4>;
 
 hipError_t launch_router(const Ctx& c, const moe_shape_t& s, const void* x, const void* w,
                          const float* bias, float* logits) {
   if (s.dtype == MOE_BF16) {
-    const int tiles128 = ((s.T + 127) / 128) * ((s.E + 127) / 128);
-    if (tiles128 >= 2 * c.num_cus)
-      return launch_router_bf16<DmaCfg<128, 128, MOE_ROUTER_STAGES_128>>(c, s, (const bf16_t*)x,
-                                                                          (const bf16_t*)w, bias, logits);
-    return launch_router_bf16<DmaCfg<64, 128, MOE_ROUTER_STAGES_64>>(c, s, (const bf16_t*)x,
-                                                                      (const bf16_t*)w, bias, logits);
+    const bf16_t* xb = (const bf16_t*)x;
+    const bf16_t* wb = (const bf16_t*)w;
+    const int mt128 = (s.T + 127) / 128;
+    if (mt128 * ((s.E + 255) / 256) >= c.num_cus)
+      return launch_router_bf16<RouterLarge>(c, s, xb, wb, bias, logits);
+    if (2 * mt128 * ((s.E + 127) / 128) >= c.num_cus)
+      return launch_router_bf16<RouterMedium>(c, s, xb, wb, bias, logits);
+    return launch_router_bf16<RouterSmall>(c, s, xb, wb, bias, logits);
   }
   const int64_t n = (int64_t)s.T * s.E;
   TimedLaunch tl(MOE_K_ROUTER_GEMM, c.stream);
