@@ -24,8 +24,9 @@
 //                 tokens of the tile with that expert; writes slot / row_src
 //                 / row_gate, or, for an expert over capacity, a candidate
 //                 (gate bits, assignment)
-//   K5 capacity   per over-capacity expert: C-th largest (gate, -token) key
-//                 by radix select, then kept candidates in token order -> rows
+//   K5 capacity   per over-capacity expert: C-th largest gate by radix
+//                 select (keys staged in LDS), ties to the lower token, then
+//                 kept candidates in token order -> rows
 //   K7 gather     x_perm[p] = x[row_src[p]] with 16-byte loads and stores
 //                 (optional: the grouped GEMM can read x through row_src)
 #include "common.h"
@@ -202,82 +203,197 @@ __global__ __launch_bounds__(256) void dispatch_scatter(
   }
 }
 
-// One block per local expert; experts within capacity return at once.
-// Key of a candidate: gate bits (positive floats order like their bits) in
-// the high word, ~token in the low word, so the largest key is the largest
-// gate and, among equal gates, the lowest token. Keys are unique.
-__global__ __launch_bounds__(256) void dispatch_capacity(
+// Exclusive scan of v over a workgroup of NW waves; *total gets the sum.
+template <int NW>
+__device__ int block_exclusive_scan(int v, int* total) {
+  __shared__ int wsum[NW];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const int o = __shfl_up(incl, m, kWave);
+    if (lane >= m) incl += o;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    before += w < wave ? wsum[w] : 0;
+    all += wsum[w];
+  }
+  *total = all;
+  __syncthreads();
+  return before + incl - v;
+}
+
+// One workgroup per local expert; experts within capacity return at once.
+// The candidates of an over-capacity expert sit in token order (cseg[le]
+// onwards, written by the scatter). The kept set is the C assignments with
+// the largest gate, equal gates going to the lower token:
+//   1. g* = the C-th largest gate: radix select over the gate's 32 bits (gates
+//      are positive, so their bit patterns order like the values), four
+//      passes of 8 bits, each an LDS histogram and a suffix scan of its bins;
+//      `need` ends as the number of candidates equal to g* that are kept.
+//   2. keep = gate > g*, or gate == g* and fewer than `need` earlier
+//      candidates (lower tokens) equal g*.
+//   3. kept candidates get consecutive rows in token order: per (round of
+//      1024 consecutive candidates, wave) ballot counts of the equal and then
+//      of the kept candidates, each turned into candidate-order offsets by one
+//      workgroup scan, a chunk of kCapRounds rounds at a time.
+// The candidates (keys and assignment indices) are staged in LDS when they
+// fit (kCapLds); larger experts read them from global memory in every pass.
+constexpr int kCapThreads = 1024;
+constexpr int kCapWaves = kCapThreads / 64;
+constexpr int kCapLds = 8192;
+constexpr int kCapRounds = 16;  // rounds of 1024 per chunk, (round, wave) counts in LDS
+
+struct CapShared {
+  int hist[256];
+  int cnt[kCapWaves * kCapRounds], pre[kCapWaves * kCapRounds], kpre[kCapWaves * kCapRounds];
+  uint32_t prefix;
+  int need;
+  int eq_total, kept_total;  // running totals over the chunks done
+};
+
+// The selection and compaction for one expert; key_at(i) / idx_at(i) read
+// candidate i (from LDS or global memory: one instantiation each, so every
+// access has its own address space).
+template <class Key, class Idx>
+__device__ __forceinline__ void capacity_core(CapShared& sh, Key key_at, Idx idx_at, int n, int k,
+                                              int capacity, int base, int32_t* __restrict__ slot,
+                                              int32_t* __restrict__ row_src,
+                                              float* __restrict__ row_gate) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) {
+    sh.prefix = 0u;
+    sh.need = capacity;
+    sh.eq_total = 0;
+    sh.kept_total = 0;
+  }
+  uint32_t pmask = 0u;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    if (tid < 256) sh.hist[tid] = 0;
+    __syncthreads();
+    const uint32_t prefix = sh.prefix;
+    for (int i = tid; i < n; i += kCapThreads) {
+      const uint32_t key = key_at(i);
+      bool act = (key & pmask) == prefix;
+      const int bin = (int)((key >> shift) & 255u);
+      // gates crowd into few bins (the high bytes of values in (0, 1]): the
+      // lanes sharing the first active lane's bin add their count with one
+      // atomic, a few rounds, before the rest add one by one
+      for (int r = 0; r < 4; ++r) {
+        const uint64_t am = __ballot(act);
+        if (am == 0) break;
+        const int leader = __ffsll((long long)am) - 1;
+        const int lbin = __builtin_amdgcn_readlane(bin, leader);
+        const uint64_t same = __ballot(act && bin == lbin);
+        if (lane == leader) atomicAdd(&sh.hist[lbin], __popcll(same));
+        if (bin == lbin) act = false;
+      }
+      if (act) atomicAdd(&sh.hist[bin], 1);
+    }
+    __syncthreads();
+    // suffix sums: thread t holds bin 255 - t, so an exclusive scan over t
+    // gives the number of candidates in the bins above
+    const int need = sh.need;
+    const int bin = 255 - tid;
+    const int cnt = tid < 256 ? sh.hist[bin] : 0;
+    int tot;
+    const int above = block_exclusive_scan<kCapWaves>(cnt, &tot);
+    if (tid < 256 && above < need && above + cnt >= need) {  // exactly one bin
+      sh.prefix = prefix | ((uint32_t)bin << shift);
+      sh.need = need - above;
+    }
+    pmask |= 255u << shift;
+    __syncthreads();
+  }
+  const uint32_t gstar = sh.prefix;
+  const int need_eq = sh.need;  // candidates equal to g* that are kept (lowest tokens)
+  const uint64_t below = (1ull << lane) - 1ull;
+  const int rounds = (n + kCapThreads - 1) / kCapThreads;
+  for (int c0 = 0; c0 < rounds; c0 += kCapRounds) {
+    const int nr = min(kCapRounds, rounds - c0);
+    const int eq_carry = sh.eq_total, kept_carry = sh.kept_total;
+    for (int r = 0; r < nr; ++r) {
+      const int i = (c0 + r) * kCapThreads + tid;
+      const uint64_t bal = __ballot(i < n && key_at(i) == gstar);
+      if (lane == 0) sh.cnt[r * kCapWaves + wave] = __popcll(bal);
+    }
+    __syncthreads();
+    int etot;
+    int pre = block_exclusive_scan<kCapWaves>(tid < nr * kCapWaves ? sh.cnt[tid] : 0, &etot);
+    if (tid < nr * kCapWaves) sh.pre[tid] = eq_carry + pre;
+    __syncthreads();
+    for (int r = 0; r < nr; ++r) {
+      const int i = (c0 + r) * kCapThreads + tid;
+      const bool in = i < n;
+      const uint32_t key = in ? key_at(i) : 0u;
+      const bool eq = in && key == gstar;
+      const int eq_rank = sh.pre[r * kCapWaves + wave] + __popcll(__ballot(eq) & below);
+      const uint64_t kbal = __ballot(in && (key > gstar || (eq && eq_rank < need_eq)));
+      if (lane == 0) sh.cnt[r * kCapWaves + wave] = __popcll(kbal);
+    }
+    __syncthreads();
+    int ktot;
+    pre = block_exclusive_scan<kCapWaves>(tid < nr * kCapWaves ? sh.cnt[tid] : 0, &ktot);
+    if (tid < nr * kCapWaves) sh.kpre[tid] = kept_carry + pre;
+    __syncthreads();
+    for (int r = 0; r < nr; ++r) {
+      const int i = (c0 + r) * kCapThreads + tid;
+      const bool in = i < n;
+      const uint32_t key = in ? key_at(i) : 0u;
+      const bool eq = in && key == gstar;
+      const int eq_rank = sh.pre[r * kCapWaves + wave] + __popcll(__ballot(eq) & below);
+      const bool keep = in && (key > gstar || (eq && eq_rank < need_eq));
+      const uint64_t kbal = __ballot(keep);
+      if (in) {
+        const int a = idx_at(i);
+        if (keep) {
+          const int row = base + sh.kpre[r * kCapWaves + wave] + __popcll(kbal & below);
+          slot[a] = row;
+          row_src[row] = a / k;
+          row_gate[row] = __uint_as_float(key);
+        } else {
+          slot[a] = -1;
+        }
+      }
+    }
+    __syncthreads();
+    if (tid == 0) {
+      sh.eq_total = eq_carry + etot;
+      sh.kept_total = kept_carry + ktot;
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(kCapThreads) void dispatch_capacity(
     int k, int e_lo, int L, int capacity, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ cseg,
     const uint32_t* __restrict__ cand_key, const int32_t* __restrict__ cand_idx,
     int32_t* __restrict__ slot, int32_t* __restrict__ row_src, float* __restrict__ row_gate) {
-  __shared__ int hist[256];
-  __shared__ uint64_t s_prefix;
-  __shared__ int s_need;
-  __shared__ int wsum[4];
+  __shared__ uint32_t s_keys[kCapLds];
+  __shared__ int32_t s_idx[kCapLds];
+  __shared__ CapShared sh;
   const int le = blockIdx.x;
   const int n = counts[e_lo + le];
   if (n <= capacity) return;
   const uint32_t* ck = cand_key + cseg[le];
   const int32_t* ci = cand_idx + cseg[le];
-  auto key_of = [&](int i) -> uint64_t {
-    const uint32_t tok = (uint32_t)(ci[i] / k);
-    return ((uint64_t)ck[i] << 32) | (uint64_t)(0xffffffffu - tok);
-  };
-  if (threadIdx.x == 0) {
-    s_prefix = 0;
-    s_need = capacity;
-  }
-  uint64_t pmask = 0;
-  for (int shift = 56; shift >= 0; shift -= 8) {
-    hist[threadIdx.x] = 0;
-    __syncthreads();
-    const uint64_t prefix = s_prefix;
-    for (int i = threadIdx.x; i < n; i += 256) {
-      const uint64_t key = key_of(i);
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
+  const int base = offsets[le];
+  if (n <= kCapLds) {
+    for (int i = threadIdx.x; i < n; i += kCapThreads) {
+      s_keys[i] = ck[i];
+      s_idx[i] = ci[i];
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-      int need = s_need, above = 0, b = 255;
-      for (; b > 0; --b) {
-        if (above + hist[b] >= need) break;
-        above += hist[b];
-      }
-      s_prefix = prefix | ((uint64_t)b << shift);
-      s_need = need - above;
-    }
-    pmask |= (uint64_t)255 << shift;
-    __syncthreads();
-  }
-  const uint64_t thr = s_prefix;  // the capacity-th largest key
-  // Kept candidates in token order get consecutive rows.
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int carry = 0;
-  for (int base = 0; base < n; base += 256) {
-    const int i = base + threadIdx.x;
-    const bool in = i < n;
-    const bool keep = in && key_of(i) >= thr;
-    const unsigned long long bal = __ballot(keep);
-    const int before_in_wave = __popcll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) wsum[wave] = __popcll(bal);
-    __syncthreads();
-    int before = carry;
-    for (int w = 0; w < wave; ++w) before += wsum[w];
-    const int chunk_total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-    if (in) {
-      const int a = ci[i];
-      if (keep) {
-        const int row = offsets[le] + before + before_in_wave;
-        slot[a] = row;
-        row_src[row] = a / k;
-        row_gate[row] = __uint_as_float(ck[i]);
-      } else {
-        slot[a] = -1;
-      }
-    }
-    carry += chunk_total;
-    __syncthreads();
+    capacity_core(sh, [&](int i) { return s_keys[i]; }, [&](int i) { return s_idx[i]; }, n, k,
+                  capacity, base, slot, row_src, row_gate);
+  } else {
+    capacity_core(sh, [&](int i) { return ck[i]; }, [&](int i) { return ci[i]; }, n, k, capacity,
+                  base, slot, row_src, row_gate);
   }
 }
 
@@ -338,7 +454,7 @@ hipError_t launch_dispatch(const Ctx& c, const moe_shape_t& s, const Workspace& 
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (s.capacity > 0) {
     TimedLaunch tl(MOE_K_CAPACITY, c.stream);
-    hipLaunchKernelGGL(dispatch_capacity, dim3(L), dim3(256), 0, c.stream, s.k, s.e_lo, L,
+    hipLaunchKernelGGL(dispatch_capacity, dim3(L), dim3(kCapThreads), 0, c.stream, s.k, s.e_lo, L,
                        s.capacity, counts, offsets, ws.cseg, ws.cand_key, ws.cand_idx, slot,
                        row_src, row_gate);
     if ((err = hipGetLastError()) != hipSuccess) return err;
