@@ -197,8 +197,7 @@ moe_status_t moe_expert_gemm(const moe_shape_t* shape, const void* x, const int3
  *   down_packed [L, d, f]  elements: tile (le, b, kt) for b < d/128, kt < f/32
  *               holds rows 128b..128b+127 of w_down[le], K values 32kt..32kt+31
  * Within a tile, row r's 16-byte chunk c (K values 8c..8c+7) is stored at
- * chunk position c ^ key(r) of the row, key(r) = ((r >> 2) & 1) |
- * ((((r >> 1) ^ (r >> 3)) & 1) << 1).
+ * chunk position c ^ key(r) of the row, key(r) = (r >> 1) & 3.
  * bf16 only, d % 128 == 0. Either output may be NULL (that input is then
  * not read). */
 moe_status_t moe_pack_expert_weights(const moe_shape_t* shape, const void* w_gate, const void* w_up,

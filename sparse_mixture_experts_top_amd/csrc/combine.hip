@@ -85,7 +85,8 @@ __global__ __launch_bounds__(256) void combine_f32(const float* __restrict__ y_p
 
 hipError_t launch_combine(const Ctx& c, const moe_shape_t& s, const void* y_perm,
                           const int32_t* slot, const float* gate, void* y) {
-  const int grid = s.T < c.num_cus * 16 ? s.T : c.num_cus * 16;
+  // one token per workgroup up to 64 workgroups per CU, grid-stride beyond
+  const int grid = s.T < c.num_cus * 64 ? s.T : c.num_cus * 64;
   TimedLaunch tl(MOE_K_COMBINE, c.stream);
   if (s.dtype == MOE_BF16)
     hipLaunchKernelGGL(combine_bf16, dim3(grid), dim3(256), 0, c.stream, (const bf16_t*)y_perm, slot,

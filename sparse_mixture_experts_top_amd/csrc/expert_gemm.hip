@@ -141,8 +141,8 @@ struct GateUpProb {
     const int ni = item % nt;
     const int ce = dma_chunk_elem();
 #pragma unroll
-    for (int q = 0; q < Cfg::A_DMA / Cfg::PW; ++q) {
-      const int i = q * Cfg::PW + part;
+    for (int q = 0; q < Cfg::A_DMA / Cfg::DW; ++q) {
+      const int i = q * Cfg::DW + part;
       const int64_t src = row_src ? gathered_row<Cfg>(row_src, t, i, ld_uniform(offsets, L))
                                   : t.row0 + min(dma_row(i), t.valid - 1);
       ld.a[q] = x + src * d + ce;
@@ -153,8 +153,8 @@ struct GateUpProb {
       const int nb = f / 64, nk = d / Cfg::BK;
       const int64_t bstride = (int64_t)nk * kPackTileElems;
 #pragma unroll
-      for (int q = 0; q < Cfg::B_DMA / Cfg::PW; ++q) {
-        const int i = q * Cfg::PW + part;
+      for (int q = 0; q < Cfg::B_DMA / Cfg::DW; ++q) {
+        const int i = q * Cfg::DW + part;
         const int b = min(ni * (HALF / 64) + i / (kPackTileRows / 16), nb - 1);
         const bf16_t* tile0 = w_packed + ((int64_t)t.le * nb + b) * bstride;
         ld.b[q] = packed_b_ptr(tile0, i % (kPackTileRows / 16), 0);
@@ -163,8 +163,8 @@ struct GateUpProb {
       return;
     }
 #pragma unroll
-    for (int q = 0; q < Cfg::B_DMA / Cfg::PW; ++q) {
-      const int jb = dma_row(q * Cfg::PW + part);
+    for (int q = 0; q < Cfg::B_DMA / Cfg::DW; ++q) {
+      const int jb = dma_row(q * Cfg::DW + part);
       const int frag = jb >> 4;
       const int fcol = min(ni * HALF + (frag >> 1) * 16 + (jb & 15), f - 1);
       ld.b[q] = ((frag & 1) ? w_up : w_gate) + ((int64_t)t.le * f + fcol) * d + ce;
@@ -247,16 +247,16 @@ struct DownProb {
     const int n0 = (item % nt) * Cfg::BN;
     const int ce = dma_chunk_elem();
 #pragma unroll
-    for (int q = 0; q < Cfg::A_DMA / Cfg::PW; ++q)
-      ld.a[q] = hbuf + (t.row0 + min(dma_row(q * Cfg::PW + part), t.valid - 1)) * f + ce;
+    for (int q = 0; q < Cfg::A_DMA / Cfg::DW; ++q)
+      ld.a[q] = hbuf + (t.row0 + min(dma_row(q * Cfg::DW + part), t.valid - 1)) * f + ce;
     if (w_packed) {
       // packed tiles hold 128 output columns each; blocks past d (a partial
       // last item) re-read the last block, never stored
       const int nb = d / kPackTileRows, nk = f / Cfg::BK;
       const int64_t bstride = (int64_t)nk * kPackTileElems;
 #pragma unroll
-      for (int q = 0; q < Cfg::B_DMA / Cfg::PW; ++q) {
-        const int i = q * Cfg::PW + part;
+      for (int q = 0; q < Cfg::B_DMA / Cfg::DW; ++q) {
+        const int i = q * Cfg::DW + part;
         const int b = min((item % nt) * (Cfg::BN / kPackTileRows) + i / (kPackTileRows / 16), nb - 1);
         const bf16_t* tile0 = w_packed + ((int64_t)t.le * nb + b) * bstride;
         ld.b[q] = packed_b_ptr(tile0, i % (kPackTileRows / 16), 0);
@@ -265,8 +265,8 @@ struct DownProb {
       return;
     }
 #pragma unroll
-    for (int q = 0; q < Cfg::B_DMA / Cfg::PW; ++q)
-      ld.b[q] = w_down + ((int64_t)t.le * d + min(n0 + dma_row(q * Cfg::PW + part), d - 1)) * f + ce;
+    for (int q = 0; q < Cfg::B_DMA / Cfg::DW; ++q)
+      ld.b[q] = w_down + ((int64_t)t.le * d + min(n0 + dma_row(q * Cfg::DW + part), d - 1)) * f + ce;
   }
 
   __device__ __forceinline__ void epilogue(int item, Acc<Cfg>& acc) const {

@@ -286,13 +286,14 @@ __device__ __forceinline__ void persistent_gemm(Prob& pb, int items, int nk, bf1
 // them too slowly to keep the memory system busy.
 //
 // K step = 32. A stage holds A [BM][32] and B [BN][32] bf16 (64-byte rows,
-// 16 rows per DMA instruction). To keep the MFMA fragment reads (16 rows x one
-// 16-byte chunk per instruction) free of bank conflicts, the 16-byte chunk c
-// of row r is stored at slot c ^ chunk_key(r): among any 8 consecutive rows
-// (one 128-byte bank line holds two rows) the (row parity, slot) pairs are
-// all distinct, and among any 16 consecutive rows the (row mod 4, slot)
-// pairs are, so the read is conflict-free whether the LDS serves 8 or 16
-// lanes of a 16-byte read per cycle.
+// 16 rows per DMA instruction). To keep the MFMA fragment reads (lane l reads
+// 16-byte chunk l / 16 of row l % 16) free of bank conflicts, the chunk c of
+// row r is stored at slot c ^ chunk_key(r) with chunk_key(r) = bits 1..2 of
+// r. On gfx950 a ds_read_b128 of this pattern then runs at the LDS's full
+// rate, 4 cycles (256 bytes per cycle) with no bank-conflict cycles, as the
+// SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE counters show; unswizzled rows, or
+// keys that are a permutation within every 4 rows of equal r mod 4, take 8
+// cycles (2-way conflicts).
 // STAGES stages form a ring in one LDS array; stage g's slot is g % STAGES and
 // STAGES - 1 stages are in flight while one is consumed.
 
@@ -312,7 +313,8 @@ struct DmaCfg {
   static constexpr int BK = 32;
   static constexpr int STAGES = STAGES_;  // ring slots; STAGES - 1 stages in flight
   static constexpr int CW = CW_;
-  static constexpr int PW = PW_;
+  static constexpr int PW = PW_;  // 0: symmetric, every wave computes and issues DMAs
+  static constexpr int DW = PW_ > 0 ? PW_ : CW_;  // waves sharing the DMAs of a stage
   static constexpr int THREADS = 64 * (CW + PW);
   static constexpr int WAVES_PER_SIMD = (CW + PW + 3) / 4;
   static constexpr int WM = WM_;          // the compute waves form a WM x WN grid over the tile
@@ -328,14 +330,14 @@ struct DmaCfg {
   static_assert(WM == 1 || WM == 2 || WM == 4, "wave grid");
   static_assert(FM >= 1 && FN >= 1 && FM * 16 * WM == BM && FN * 16 * WN == BN, "fragments");
   static_assert(BM % 16 == 0 && BN % 16 == 0, "DMA tiles are multiples of 16 rows");
-  static constexpr int DMA_PER_PRODUCER = DMA_PER_STAGE / PW;  // per stage
-  static_assert(A_DMA % PW == 0 && B_DMA % PW == 0, "DMA split");
+  static constexpr int DMA_PER_PRODUCER = DMA_PER_STAGE / DW;  // per stage and DMA wave
+  static_assert(A_DMA % DW == 0 && B_DMA % DW == 0, "DMA split");
   static_assert(CW % WM == 0, "wave grid");
   static_assert(STAGES >= 3 && (STAGES - 2) * DMA_PER_PRODUCER <= 63, "ring depth vs vmcnt");
 };
 
 // Lane pointers of one producer for one item: a[q] / b[q] belong to the
-// producer's q-th DMA instruction of each operand, i = q * PW + part,
+// producer's q-th DMA instruction of each operand, i = q * DW + part,
 // and point at the logical chunk this lane fetches ((lane & 3) ^
 // chunk_key(lane / 4)) of tile row 16 i + lane / 4; set by
 // Prob::setup(item, ld, part).
@@ -343,17 +345,15 @@ struct DmaCfg {
 // (32 for a row-major operand; one whole packed tile for a packed one).
 template <class Cfg>
 struct DmaLoader {
-  const bf16_t* a[Cfg::A_DMA / Cfg::PW];
-  const bf16_t* b[Cfg::B_DMA / Cfg::PW];
+  const bf16_t* a[Cfg::A_DMA / Cfg::DW];
+  const bf16_t* b[Cfg::B_DMA / Cfg::DW];
   int a_kstep = Cfg::BK;
   int b_kstep = Cfg::BK;
 };
 
-// Swizzle key of tile row r (only r mod 16 matters): bit 0 = bit 2 of r,
-// bit 1 = bit 1 ^ bit 3 of r. XOR with it maps chunk -> slot and back.
-__host__ __device__ __forceinline__ int chunk_key(int r) {
-  return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1);
-}
+// Swizzle key of tile row r: bits 1..2 of r (only r mod 8 matters). XOR with
+// it maps chunk -> slot and back.
+__host__ __device__ __forceinline__ int chunk_key(int r) { return (r >> 1) & 3; }
 
 // Tile row whose chunk this (producer) lane fetches in DMA instruction i, and
 // the element offset of that chunk inside the row: lane l writes slot l % 4
@@ -377,16 +377,16 @@ __device__ __forceinline__ void dma16(const void* g, const bf16_t* lds) {
 }
 
 // Producer `part`'s share of the DMA instructions of K step kt into stage
-// `stage`: A and B instructions i with i % PW == part.
+// `stage`: A and B instructions i with i % DW == part.
 template <class Cfg>
 __device__ __forceinline__ void dma_issue(const DmaLoader<Cfg>& ld, int kt, bf16_t* stage, int part) {
   const int64_t ka = (int64_t)kt * ld.a_kstep, kb = (int64_t)kt * ld.b_kstep;
 #pragma unroll
-  for (int q = 0; q < Cfg::A_DMA / Cfg::PW; ++q)
-    dma16(ld.a[q] + ka, stage + 16 * (q * Cfg::PW + part) * Cfg::BK);
+  for (int q = 0; q < Cfg::A_DMA / Cfg::DW; ++q)
+    dma16(ld.a[q] + ka, stage + 16 * (q * Cfg::DW + part) * Cfg::BK);
 #pragma unroll
-  for (int q = 0; q < Cfg::B_DMA / Cfg::PW; ++q)
-    dma16(ld.b[q] + kb, stage + Cfg::A_ELEMS + 16 * (q * Cfg::PW + part) * Cfg::BK);
+  for (int q = 0; q < Cfg::B_DMA / Cfg::DW; ++q)
+    dma16(ld.b[q] + kb, stage + Cfg::A_ELEMS + 16 * (q * Cfg::DW + part) * Cfg::BK);
 }
 
 // Packed B operand: a weight tile of 128 rows x one K step stored as the
@@ -600,6 +600,72 @@ __device__ __forceinline__ void persistent_gemm_dma(Prob& pb, int items, int nk)
     }
     pb.epilogue(item, acc);
     wait_lgkm0();
+  }
+}
+
+// Persistent symmetric driver (DmaCfg with PW = 0): every wave issues its
+// share of each stage's DMAs and computes. Meant for a dense GEMM whose
+// workgroups process few items (the router), where the cost the wave roles
+// of persistent_gemm_dma avoid - a wave waiting for loads issued after its
+// own epilogue stores - occurs once per item: the first wait after an
+// epilogue drains the wave's counter. Step g: wait for the wave's own DMAs
+// of stage g; barrier (stage g landed everywhere, and every wave finished
+// reading slot (g - 1) % STAGES during step g - 1); issue stage
+// g + STAGES - 1 into that slot; LDS reads and MFMAs of stage g, which the
+// compiler interleaves; epilogue if g closes an item. Rows past the valid
+// ones are computed on clamped data and not stored. (Double-buffering the
+// fragments across steps, as persistent_gemm_dma does, measured slower here:
+// the 128 x 64 wave tile then needs 252 VGPRs.)
+template <class Cfg, class Prob>
+__device__ __forceinline__ void persistent_gemm_sym(Prob& pb, int items, int nk) {
+  static_assert(Cfg::PW == 0, "symmetric configuration");
+  constexpr int S = Cfg::STAGES;
+  __shared__ __align__(16) bf16_t ring[S * Cfg::STAGE_ELEMS];
+  const XcdSplit sp = xcd_split(items);
+  if (sp.first >= sp.end || nk <= 0) return;
+  const int n_mine = (sp.end - sp.first + sp.stride - 1) / sp.stride;
+  const int total = n_mine * nk;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
+  DmaLoader<Cfg> ld;
+  int l_ord = 0, l_kt = 0, l_slot = 0;  // load cursor
+  pb.setup(sp.first, ld, wave);
+  auto issue_next = [&]() {
+    dma_issue<Cfg>(ld, l_kt, ring + l_slot * Cfg::STAGE_ELEMS, wave);
+    l_slot = (l_slot + 1 == S) ? 0 : l_slot + 1;
+    if (++l_kt == nk) {
+      l_kt = 0;
+      if (++l_ord < n_mine) pb.setup(sp.first + l_ord * sp.stride, ld, wave);
+    }
+  };
+  for (int p = 0; p < S - 1 && p < total; ++p) issue_next();
+  Acc<Cfg> acc;
+  Frags<Cfg> fr;
+  int c_slot = 0;
+  bool drain = false;  // epilogue stores are still counted on vmcnt
+  for (int c_ord = 0; c_ord < n_mine; ++c_ord) {
+    acc.zero();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int g = c_ord * nk + kt;
+      if (drain) {
+        wait_vmcnt_imm<0>();
+        drain = false;
+      } else {
+        dma_wait_stage<Cfg>(total - 1 - g);
+      }
+      ring_barrier();
+      if (g + S - 1 < total) issue_next();
+      read_frags<Cfg>(fr, ring + c_slot * Cfg::STAGE_ELEMS, wm, wn, lane);
+#pragma unroll
+      for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < Cfg::FN; ++j)
+          acc.v[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr.b[j], fr.a[i], acc.v[i][j], 0, 0, 0);
+      c_slot = (c_slot + 1 == S) ? 0 : c_slot + 1;
+    }
+    pb.epilogue(sp.first + c_ord * sp.stride, acc);
+    drain = true;
   }
 }
 

@@ -29,11 +29,11 @@ struct RouterProb {
     const int m0 = (item / nt) * Cfg::BM, n0 = (item % nt) * Cfg::BN;
     const int ce = dma_chunk_elem();
 #pragma unroll
-    for (int q = 0; q < Cfg::A_DMA / Cfg::PW; ++q)
-      ld.a[q] = x + (int64_t)min(m0 + dma_row(q * Cfg::PW + part), T - 1) * d + ce;
+    for (int q = 0; q < Cfg::A_DMA / Cfg::DW; ++q)
+      ld.a[q] = x + (int64_t)min(m0 + dma_row(q * Cfg::DW + part), T - 1) * d + ce;
 #pragma unroll
-    for (int q = 0; q < Cfg::B_DMA / Cfg::PW; ++q)
-      ld.b[q] = w + (int64_t)min(n0 + dma_row(q * Cfg::PW + part), E - 1) * d + ce;
+    for (int q = 0; q < Cfg::B_DMA / Cfg::DW; ++q)
+      ld.b[q] = w + (int64_t)min(n0 + dma_row(q * Cfg::DW + part), E - 1) * d + ce;
   }
 
   __device__ __forceinline__ void epilogue(int item, Acc<Cfg>& acc) const {
@@ -67,7 +67,10 @@ struct RouterProb {
 
 template <class Cfg>
 __global__ __launch_bounds__(Cfg::THREADS, Cfg::WAVES_PER_SIMD) void router_gemm_bf16(RouterProb<Cfg> pb, int items) {
-  persistent_gemm_dma<Cfg>(pb, items, pb.d / Cfg::BK);
+  if constexpr (Cfg::PW == 0)
+    persistent_gemm_sym<Cfg>(pb, items, pb.d / Cfg::BK);
+  else
+    persistent_gemm_dma<Cfg>(pb, items, pb.d / Cfg::BK);
 }
 
 // fp32: one thread per logit, plain dot product (small parity workloads).
@@ -101,8 +104,11 @@ static hipError_t launch_router_bf16(const Ctx& c, const moe_shape_t& s, const b
 
 // Router tile configurations (the router is a dense, compute-bound GEMM, so
 // the large ones run 8 compute waves - two per SIMD, which the MFMA issue
-// rate needs - next to 4 producers):
-//   large   128 x 256, 8 compute waves of 64 x 64, when there are at least
+// rate needs):
+//   huge    256 x 256, 8 symmetric waves (each computes 128 x 64 and issues
+//           DMAs), when there are at least as many such tiles as CUs
+//           (e.g. T = 16384, E = 896);
+//   large   128 x 256, 8 compute waves of 64 x 64 + 4 producers, when there are at least
 //           as many such tiles as CUs (e.g. T = 16384, E = 896);
 //   medium  128 x 128, 8 compute waves of 64 x 32, when the 128 x 128 tiles
 //           cover at least half of the CUs (e.g. T = 4096, E = 896);
@@ -110,6 +116,7 @@ static hipError_t launch_router_bf16(const Ctx& c, const moe_shape_t& s, const b
 #ifndef MOE_ROUTER_STAGES
 #define MOE_ROUTER_STAGES 6
 #endif
+using RouterHuge = DmaCfg<256, 256, 4, 2, 8, 0>;
 using RouterLarge = DmaCfg<128, 256, MOE_ROUTER_STAGES, 2, 8, 4>;
 using RouterMedium = DmaCfg<128, 128, MOE_ROUTER_STAGES, 2, 8, 4>;
 using RouterSmall = DmaCfg<64, 128, 4, 2, 4, 4>;
@@ -120,6 +127,8 @@ hipError_t launch_router(const Ctx& c, const moe_shape_t& s, const void* x, cons
     const bf16_t* xb = (const bf16_t*)x;
     const bf16_t* wb = (const bf16_t*)w;
     const int mt128 = (s.T + 127) / 128;
+    if (((s.T + 255) / 256) * ((s.E + 255) / 256) >= c.num_cus)
+      return launch_router_bf16<RouterHuge>(c, s, xb, wb, bias, logits);
     if (mt128 * ((s.E + 255) / 256) >= c.num_cus)
       return launch_router_bf16<RouterLarge>(c, s, xb, wb, bias, logits);
     if (2 * mt128 * ((s.E + 127) / 128) >= c.num_cus)
@@ -194,16 +203,15 @@ __global__ __launch_bounds__(256) void topk_softmax(const float* __restrict__ lo
     uint64_t key[EPL];
     float val[EPL];
     uint64_t lmax = 0;
+    // all loads first (clamped, so unconditional): issued back to back, one wait
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) val[i] = row[min(lane + 64 * i, E - 1)];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       const int e = lane + 64 * i;
-      if (e < E) {
-        val[i] = row[e];
-        key[i] = ((uint64_t)ordered_bits(val[i]) << 32) | (uint32_t)(0xffffffffu - (uint32_t)e);
-      } else {
-        val[i] = 0.f;
-        key[i] = 0;
-      }
+      const bool ok = e < E;
+      val[i] = ok ? val[i] : 0.f;
+      key[i] = ok ? ((uint64_t)ordered_bits(val[i]) << 32) | (uint32_t)(0xffffffffu - (uint32_t)e) : 0ull;
       lmax = key[i] > lmax ? key[i] : lmax;
     }
     // 1. tau: the largest logit-bits value t (the key's high word) such that

@@ -175,7 +175,7 @@ def test_packed_weights_bitwise_equal_and_permutation():
 
 
 def _chunk_key(r):
-    return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1)
+    return (r >> 1) & 3
 
 
 def test_packed_weights_documented_layout():
