@@ -608,18 +608,66 @@ __device__ __forceinline__ void persistent_gemm_dma(Prob& pb, int items, int nk)
 // workgroups process few items (the router), where the cost the wave roles
 // of persistent_gemm_dma avoid - a wave waiting for loads issued after its
 // own epilogue stores - occurs once per item: the first wait after an
-// epilogue drains the wave's counter. Step g: wait for the wave's own DMAs
-// of stage g; barrier (stage g landed everywhere, and every wave finished
-// reading slot (g - 1) % STAGES during step g - 1); issue stage
-// g + STAGES - 1 into that slot; LDS reads and MFMAs of stage g, which the
-// compiler interleaves; epilogue if g closes an item. Rows past the valid
-// ones are computed on clamped data and not stored. (Double-buffering the
-// fragments across steps, as persistent_gemm_dma does, measured slower here:
-// the 128 x 64 wave tile then needs 252 VGPRs.)
+// epilogue drains the wave's counter.
+//
+// Half-step software pipeline: a wave's A fragments split into a low half
+// (rows i < FM/2) and a high half. Step g runs in two phases:
+//   1. LDS reads of stage g's high half; MFMAs of the low half (stage g's B
+//      and low A, read during phase 2 of step g - 1).
+//   2. wait for the wave's reads and for its own DMAs of stage g + 1;
+//      barrier (stage g + 1 landed everywhere; stage g fully read, so its
+//      slot g % STAGES is free); issue stage g + STAGES into that slot; LDS
+//      reads of stage g + 1's B and low half; MFMAs of the high half.
+// So every group of LDS reads is in flight behind FM/2 x FN MFMAs of the same
+// wave, and the two waves of a SIMD need not interleave to hide it. B and the
+// low half alternate between two register sets (two steps per loop turn, so
+// nk must be even); all rows are computed (rows past the valid ones on
+// clamped data) and the epilogue stores the valid ones.
+template <class Cfg>
+struct SymFrags {
+  bf16x8 b[Cfg::FN];
+  bf16x8 a[Cfg::FM / 2];
+};
+
+template <class Cfg>
+__device__ __forceinline__ void sym_read_lo(SymFrags<Cfg>& f, const bf16_t* st, int wm, int wn, int lane) {
+  const bf16_t* As = st;
+  const bf16_t* Bs = st + Cfg::A_ELEMS;
+  const int r = lane & 15;
+  const int slot = (lane >> 4) ^ chunk_key(r);
+#pragma unroll
+  for (int j = 0; j < Cfg::FN; ++j)
+    f.b[j] = *reinterpret_cast<const bf16x8*>(&Bs[(wn * (Cfg::BN / Cfg::WN) + j * 16 + r) * Cfg::BK + slot * 8]);
+#pragma unroll
+  for (int i = 0; i < Cfg::FM / 2; ++i)
+    f.a[i] = *reinterpret_cast<const bf16x8*>(&As[(frag_row0<Cfg>(wm, i) + r) * Cfg::BK + slot * 8]);
+}
+
+template <class Cfg>
+__device__ __forceinline__ void sym_read_hi(bf16x8 (&ahi)[Cfg::FM / 2], const bf16_t* st, int wm, int lane) {
+  const int r = lane & 15;
+  const int slot = (lane >> 4) ^ chunk_key(r);
+#pragma unroll
+  for (int i = 0; i < Cfg::FM / 2; ++i)
+    ahi[i] = *reinterpret_cast<const bf16x8*>(&st[(frag_row0<Cfg>(wm, i + Cfg::FM / 2) + r) * Cfg::BK + slot * 8]);
+}
+
+template <class Cfg>
+__device__ __forceinline__ void sym_mma(Acc<Cfg>& acc, const bf16x8 (&b)[Cfg::FN], const bf16x8 (&a)[Cfg::FM / 2],
+                                        int i0) {
+#pragma unroll
+  for (int i = 0; i < Cfg::FM / 2; ++i)
+#pragma unroll
+    for (int j = 0; j < Cfg::FN; ++j)
+      acc.v[i0 + i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[j], a[i], acc.v[i0 + i][j], 0, 0, 0);
+}
+
 template <class Cfg, class Prob>
 __device__ __forceinline__ void persistent_gemm_sym(Prob& pb, int items, int nk) {
   static_assert(Cfg::PW == 0, "symmetric configuration");
+  static_assert(Cfg::FM % 2 == 0, "two halves of A fragments");
   constexpr int S = Cfg::STAGES;
+  constexpr int H = Cfg::FM / 2;
   __shared__ __align__(16) bf16_t ring[S * Cfg::STAGE_ELEMS];
   const XcdSplit sp = xcd_split(items);
   if (sp.first >= sp.end || nk <= 0) return;
@@ -639,30 +687,54 @@ __device__ __forceinline__ void persistent_gemm_sym(Prob& pb, int items, int nk)
       if (++l_ord < n_mine) pb.setup(sp.first + l_ord * sp.stride, ld, wave);
     }
   };
+  // stages 0 .. S-1: S-1 before barrier "-1", stage S-1 into the never-used
+  // last slot right after it
   for (int p = 0; p < S - 1 && p < total; ++p) issue_next();
+  dma_wait_stage<Cfg>(total - 1);
+  ring_barrier();
+  if (S - 1 < total) issue_next();
   Acc<Cfg> acc;
-  Frags<Cfg> fr;
-  int c_slot = 0;
+  SymFrags<Cfg> f0, f1;
+  bf16x8 ahi[H];
+  sym_read_lo<Cfg>(f0, ring, wm, wn, lane);
+  int c_slot = 0;      // ring slot of stage g
   bool drain = false;  // epilogue stores are still counted on vmcnt
-  for (int c_ord = 0; c_ord < n_mine; ++c_ord) {
-    acc.zero();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int g = c_ord * nk + kt;
+  // phase 2 of step g: publish stage g + 1, refill slot g % S, read stage
+  // g + 1's low set into `nxt`, MFMAs of the high half from `cur`.b
+  auto phase2 = [&](int g, const SymFrags<Cfg>& cur, SymFrags<Cfg>& nxt) {
+    wait_lgkm0();
+    if (g + 1 < total) {
       if (drain) {
         wait_vmcnt_imm<0>();
         drain = false;
       } else {
-        dma_wait_stage<Cfg>(total - 1 - g);
+        dma_wait_stage<Cfg>(total - 2 - g);
       }
-      ring_barrier();
-      if (g + S - 1 < total) issue_next();
-      read_frags<Cfg>(fr, ring + c_slot * Cfg::STAGE_ELEMS, wm, wn, lane);
-#pragma unroll
-      for (int i = 0; i < Cfg::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < Cfg::FN; ++j)
-          acc.v[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr.b[j], fr.a[i], acc.v[i][j], 0, 0, 0);
-      c_slot = (c_slot + 1 == S) ? 0 : c_slot + 1;
+    }
+    ring_barrier();
+    if (g + S < total) issue_next();
+    const int n_slot = (c_slot + 1 == S) ? 0 : c_slot + 1;
+    if (g + 1 < total) sym_read_lo<Cfg>(nxt, ring + n_slot * Cfg::STAGE_ELEMS, wm, wn, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    sym_mma<Cfg>(acc, cur.b, ahi, H);
+    __builtin_amdgcn_sched_barrier(0);
+    c_slot = n_slot;
+  };
+  // phase 1 of step g: read stage g's high half, MFMAs of the low half
+  auto phase1 = [&](const SymFrags<Cfg>& cur) {
+    sym_read_hi<Cfg>(ahi, ring + c_slot * Cfg::STAGE_ELEMS, wm, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    sym_mma<Cfg>(acc, cur.b, cur.a, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  for (int c_ord = 0; c_ord < n_mine; ++c_ord) {
+    const int g0 = c_ord * nk;
+    acc.zero();
+    for (int kt = 0; kt < nk; kt += 2) {
+      phase1(f0);
+      phase2(g0 + kt, f0, f1);
+      phase1(f1);
+      phase2(g0 + kt + 1, f1, f0);
     }
     pb.epilogue(sp.first + c_ord * sp.stride, acc);
     drain = true;
