@@ -32,9 +32,21 @@ namespace moe {
 #ifndef MOE_GEMM_STAGES
 #define MOE_GEMM_STAGES 6
 #endif
-// 128 x 256 tiles; 2 x 2 compute waves, each with 4 interleaved row
-// fragments x 8 column fragments (64 x 128 of the tile).
+// 128 x 256 tiles. Two wave layouts:
+//   GemmCfg      2 x 2 compute waves (one per SIMD), each with 4 interleaved
+//                row fragments x 8 column fragments (64 x 128 of the tile),
+//                + 4 producers: for weight-streaming shapes (few rows per
+//                expert), where the MFMAs are far from the bound;
+//   GemmCfgWide  2 x 4 compute waves (two per SIMD: one wave alone issues
+//                MFMAs at about half the unit's rate), 64 x 64 each, + 4
+//                producers: for shapes with many rows per expert, where the
+//                MFMA issue rate decides.
 using GemmCfg = DmaCfg<kGemmBM, 256, MOE_GEMM_STAGES, 2>;
+using GemmCfgWide = DmaCfg<kGemmBM, 256, MOE_GEMM_STAGES, 2, 8, 4>;
+
+// Rows per local expert expected under uniform routing (capped by the
+// capacity) at which the wide layout is used.
+constexpr int kWideRowsPerExpert = 192;
 
 __global__ __launch_bounds__(1024) void build_row_tiles(const int32_t* __restrict__ offsets, int L,
                                                         int bm, int max_tiles,
@@ -139,12 +151,12 @@ struct GateUpProb {
   __device__ __forceinline__ void setup(int item, DmaLoader<Cfg>& ld, int part) const {
     const RowTile t = row_tile<Cfg::BM>(tiles, offsets, item / nt);
     const int ni = item % nt;
-    const int ce = dma_chunk_elem();
+    const int ce = dma_chunk_elem<Cfg>();
 #pragma unroll
     for (int q = 0; q < Cfg::A_DMA / Cfg::DW; ++q) {
       const int i = q * Cfg::DW + part;
       const int64_t src = row_src ? gathered_row<Cfg>(row_src, t, i, ld_uniform(offsets, L))
-                                  : t.row0 + min(dma_row(i), t.valid - 1);
+                                  : t.row0 + min(dma_row<Cfg>(i), t.valid - 1);
       ld.a[q] = x + src * d + ce;
     }
     if (w_packed) {
@@ -164,7 +176,7 @@ struct GateUpProb {
     }
 #pragma unroll
     for (int q = 0; q < Cfg::B_DMA / Cfg::DW; ++q) {
-      const int jb = dma_row(q * Cfg::DW + part);
+      const int jb = dma_row<Cfg>(q * Cfg::DW + part);
       const int frag = jb >> 4;
       const int fcol = min(ni * HALF + (frag >> 1) * 16 + (jb & 15), f - 1);
       ld.b[q] = ((frag & 1) ? w_up : w_gate) + ((int64_t)t.le * f + fcol) * d + ce;
@@ -245,10 +257,10 @@ struct DownProb {
   __device__ __forceinline__ void setup(int item, DmaLoader<Cfg>& ld, int part) const {
     const RowTile t = row_tile<Cfg::BM>(tiles, offsets, item / nt);
     const int n0 = (item % nt) * Cfg::BN;
-    const int ce = dma_chunk_elem();
+    const int ce = dma_chunk_elem<Cfg>();
 #pragma unroll
     for (int q = 0; q < Cfg::A_DMA / Cfg::DW; ++q)
-      ld.a[q] = hbuf + (t.row0 + min(dma_row(q * Cfg::DW + part), t.valid - 1)) * f + ce;
+      ld.a[q] = hbuf + (t.row0 + min(dma_row<Cfg>(q * Cfg::DW + part), t.valid - 1)) * f + ce;
     if (w_packed) {
       // packed tiles hold 128 output columns each; blocks past d (a partial
       // last item) re-read the last block, never stored
@@ -266,7 +278,7 @@ struct DownProb {
     }
 #pragma unroll
     for (int q = 0; q < Cfg::B_DMA / Cfg::DW; ++q)
-      ld.b[q] = w_down + ((int64_t)t.le * d + min(n0 + dma_row(q * Cfg::DW + part), d - 1)) * f + ce;
+      ld.b[q] = w_down + ((int64_t)t.le * d + min(n0 + dma_row<Cfg>(q * Cfg::DW + part), d - 1)) * f + ce;
   }
 
   __device__ __forceinline__ void epilogue(int item, Acc<Cfg>& acc) const {
@@ -428,6 +440,13 @@ hipError_t launch_row_tiles(const Ctx& c, const int32_t* offsets, int L, int max
   return hipGetLastError();
 }
 
+template <class Cfg>
+hipError_t launch_grouped_bf16(const Ctx& c, const moe_shape_t& s, const Workspace& ws, const bf16_t* xr,
+                               const int32_t* row_src, const int32_t* offsets, const void* gu_packed,
+                               const void* d_packed, const void* w_gate, const void* w_up,
+                               const void* w_down, const LoraArgs* lora, void* act_save, void* y_perm,
+                               int max_tiles);
+
 hipError_t launch_expert_gemm(const Ctx& c, const moe_shape_t& s, const Workspace& ws,
                               const void* x_rows, const int32_t* row_src, const int32_t* offsets,
                               const void* gu_packed, const void* d_packed, const void* w_gate,
@@ -458,16 +477,35 @@ hipError_t launch_expert_gemm(const Ctx& c, const moe_shape_t& s, const Workspac
                                       lora->a_up, true, lora->r, ws.zu);
     if (err != hipSuccess) return err;
   }
+  const int64_t tk = (int64_t)s.T * s.k;
+  int64_t per_expert = tk / s.E;
+  if (s.capacity > 0 && per_expert > s.capacity) per_expert = s.capacity;
+  if (per_expert >= kWideRowsPerExpert)
+    return launch_grouped_bf16<GemmCfgWide>(c, s, ws, xr, row_src, offsets, gu_packed, d_packed, w_gate,
+                                            w_up, w_down, lora, act_save, y_perm, max_tiles);
+  return launch_grouped_bf16<GemmCfg>(c, s, ws, xr, row_src, offsets, gu_packed, d_packed, w_gate, w_up,
+                                      w_down, lora, act_save, y_perm, max_tiles);
+}
+
+template <class Cfg>
+hipError_t launch_grouped_bf16(const Ctx& c, const moe_shape_t& s, const Workspace& ws, const bf16_t* xr,
+                               const int32_t* row_src, const int32_t* offsets, const void* gu_packed,
+                               const void* d_packed, const void* w_gate, const void* w_up,
+                               const void* w_down, const LoraArgs* lora, void* act_save, void* y_perm,
+                               int max_tiles) {
+  hipError_t err;
+  const int L = s.e_hi - s.e_lo;
+  const int64_t rmax = max_rows(s);
   const int grid = c.num_cus;  // one workgroup per CU (see mfma_tile.h)
   {
-    GateUpProb<GemmCfg> pb{xr, row_src, offsets, ws.gemm_tiles, (const bf16_t*)w_gate,
+    GateUpProb<Cfg> pb{xr, row_src, offsets, ws.gemm_tiles, (const bf16_t*)w_gate,
                            (const bf16_t*)w_up, (const bf16_t*)gu_packed, s.d, s.f,
-                           (s.f + GateUpProb<GemmCfg>::HALF - 1) / GateUpProb<GemmCfg>::HALF,
+                           (s.f + GateUpProb<Cfg>::HALF - 1) / GateUpProb<Cfg>::HALF,
                            s.e_hi - s.e_lo,
                            lora ? ws.zu : nullptr, lora ? lora->b_up : nullptr, lora ? lora->r : 0,
                            lora ? lora->scale : 0.f, (bf16_t*)ws.hbuf, (bf16_t*)act_save};
     TimedLaunch tl(MOE_K_GATE_UP, c.stream);
-    hipLaunchKernelGGL(gate_up_bf16<GemmCfg>, dim3(grid), dim3(GemmCfg::THREADS), 0, c.stream, pb, max_tiles);
+    hipLaunchKernelGGL(gate_up_bf16<Cfg>, dim3(grid), dim3(Cfg::THREADS), 0, c.stream, pb, max_tiles);
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (lora) {
@@ -475,13 +513,13 @@ hipError_t launch_expert_gemm(const Ctx& c, const moe_shape_t& s, const Workspac
                                       nullptr, s.f, lora->a_down, true, lora->r, ws.zd);
     if (err != hipSuccess) return err;
   }
-  DownProb<GemmCfg> pb{(const bf16_t*)ws.hbuf, offsets, ws.gemm_tiles, (const bf16_t*)w_down,
+  DownProb<Cfg> pb{(const bf16_t*)ws.hbuf, offsets, ws.gemm_tiles, (const bf16_t*)w_down,
                        (const bf16_t*)d_packed, s.d, s.f,
-                       (s.d + GemmCfg::BN - 1) / GemmCfg::BN, lora ? ws.zd : nullptr,
+                       (s.d + Cfg::BN - 1) / Cfg::BN, lora ? ws.zd : nullptr,
                        lora ? lora->b_down : nullptr, lora ? lora->r : 0, lora ? lora->scale : 0.f,
                        (bf16_t*)y_perm};
   TimedLaunch tl(MOE_K_DOWN, c.stream);
-  hipLaunchKernelGGL(down_bf16<GemmCfg>, dim3(grid), dim3(GemmCfg::THREADS), 0, c.stream, pb, max_tiles);
+  hipLaunchKernelGGL(down_bf16<Cfg>, dim3(grid), dim3(Cfg::THREADS), 0, c.stream, pb, max_tiles);
   return hipGetLastError();
 }
 

@@ -306,11 +306,14 @@ typedef __attribute__((address_space(1))) void glb_void_t;
 // CW+PW-1; producer p issues the DMAs i with i % PW == p). A workgroup runs
 // alone on its CU (THREADS = 64 (CW + PW)); the occupancy hint WAVES_PER_SIMD
 // caps the registers per wave at 512 / WAVES_PER_SIMD.
-template <int BM_, int BN_, int STAGES_ = 4, int WM_ = 2, int CW_ = 4, int PW_ = 4>
+template <int BM_, int BN_, int STAGES_ = 4, int WM_ = 2, int CW_ = 4, int PW_ = 4, int BK_ = 32>
 struct DmaCfg {
   static constexpr int BM = BM_;
   static constexpr int BN = BN_;
-  static constexpr int BK = 32;
+  static constexpr int BK = BK_;           // K values per stage: 32 or 64
+  static constexpr int CPR = BK / 8;       // 16-byte chunks per LDS row
+  static constexpr int RPD = 64 / CPR;     // rows per DMA instruction (1 KB)
+  static constexpr int KSUB = BK / 32;     // MFMA K steps per stage
   static constexpr int STAGES = STAGES_;  // ring slots; STAGES - 1 stages in flight
   static constexpr int CW = CW_;
   static constexpr int PW = PW_;  // 0: symmetric, every wave computes and issues DMAs
@@ -321,19 +324,20 @@ struct DmaCfg {
   static constexpr int WN = CW_ / WM_;
   static constexpr int FM = BM / (16 * WM);  // 16 x 16 fragments per wave along M
   static constexpr int FN = BN / (16 * WN);
-  static constexpr int A_DMA = BM / 16;  // producer DMA instructions per stage (16 rows each)
-  static constexpr int B_DMA = BN / 16;
+  static constexpr int A_DMA = BM / RPD;  // DMA instructions per stage (RPD rows each)
+  static constexpr int B_DMA = BN / RPD;
   static constexpr int DMA_PER_STAGE = A_DMA + B_DMA;
   static constexpr int A_ELEMS = BM * BK;
   static constexpr int B_ELEMS = BN * BK;
   static constexpr int STAGE_ELEMS = A_ELEMS + B_ELEMS;
   static_assert(WM == 1 || WM == 2 || WM == 4, "wave grid");
   static_assert(FM >= 1 && FN >= 1 && FM * 16 * WM == BM && FN * 16 * WN == BN, "fragments");
-  static_assert(BM % 16 == 0 && BN % 16 == 0, "DMA tiles are multiples of 16 rows");
+  static_assert(BK == 32 || BK == 64, "stage depth");
+  static_assert(BM % 16 == 0 && BN % 16 == 0, "fragments are 16 rows");
   static constexpr int DMA_PER_PRODUCER = DMA_PER_STAGE / DW;  // per stage and DMA wave
   static_assert(A_DMA % DW == 0 && B_DMA % DW == 0, "DMA split");
   static_assert(CW % WM == 0, "wave grid");
-  static_assert(STAGES >= 3 && (STAGES - 2) * DMA_PER_PRODUCER <= 63, "ring depth vs vmcnt");
+  static_assert(STAGES >= 2 && (STAGES - 2) * DMA_PER_PRODUCER <= 63, "ring depth vs vmcnt");
 };
 
 // Lane pointers of one producer for one item: a[q] / b[q] belong to the
@@ -351,18 +355,30 @@ struct DmaLoader {
   int b_kstep = Cfg::BK;
 };
 
-// Swizzle key of tile row r: bits 1..2 of r (only r mod 8 matters). XOR with
-// it maps chunk -> slot and back.
+// Swizzle key of tile row r for 64-byte rows (4 chunks; BK = 32, also the
+// packed weight layout): bits 1..2 of r. XOR with it maps chunk -> slot and
+// back.
 __host__ __device__ __forceinline__ int chunk_key(int r) { return (r >> 1) & 3; }
+// For 128-byte rows (8 chunks; BK = 64): bits 0..2 of r. The fragment read of
+// either K half (chunks 0..3 or 4..7 of rows r = lane % 16) is then
+// conflict-free on gfx950 as well (4 LDS cycles per ds_read_b128, measured).
+template <class Cfg>
+__device__ __forceinline__ int lds_key(int r) {
+  return Cfg::CPR == 4 ? chunk_key(r) : (r & 7);
+}
 
 // Tile row whose chunk this (producer) lane fetches in DMA instruction i, and
-// the element offset of that chunk inside the row: lane l writes slot l % 4
-// of row l / 4 of the instruction's 16-row group, so it fetches chunk
-// (l % 4) ^ key.
-__device__ __forceinline__ int dma_row(int i) { return 16 * i + ((threadIdx.x & 63) >> 2); }
+// the element offset of that chunk inside the row: lane l writes slot
+// l % CPR of row l / CPR of the instruction's RPD-row group, so it fetches
+// chunk (l % CPR) ^ key.
+template <class Cfg>
+__device__ __forceinline__ int dma_row(int i) {
+  return Cfg::RPD * i + (int)(threadIdx.x & 63) / Cfg::CPR;
+}
+template <class Cfg>
 __device__ __forceinline__ int dma_chunk_elem() {
   const int lane = threadIdx.x & 63;
-  return ((lane & 3) ^ chunk_key(lane >> 2)) * 8;
+  return ((lane % Cfg::CPR) ^ lds_key<Cfg>(lane / Cfg::CPR)) * 8;
 }
 
 // One 16-byte-per-lane DMA: global -> LDS at lds + 16 * lane. Issued as
@@ -383,10 +399,10 @@ __device__ __forceinline__ void dma_issue(const DmaLoader<Cfg>& ld, int kt, bf16
   const int64_t ka = (int64_t)kt * ld.a_kstep, kb = (int64_t)kt * ld.b_kstep;
 #pragma unroll
   for (int q = 0; q < Cfg::A_DMA / Cfg::DW; ++q)
-    dma16(ld.a[q] + ka, stage + 16 * (q * Cfg::DW + part) * Cfg::BK);
+    dma16(ld.a[q] + ka, stage + Cfg::RPD * (q * Cfg::DW + part) * Cfg::BK);
 #pragma unroll
   for (int q = 0; q < Cfg::B_DMA / Cfg::DW; ++q)
-    dma16(ld.b[q] + kb, stage + Cfg::A_ELEMS + 16 * (q * Cfg::DW + part) * Cfg::BK);
+    dma16(ld.b[q] + kb, stage + Cfg::A_ELEMS + Cfg::RPD * (q * Cfg::DW + part) * Cfg::BK);
 }
 
 // Packed B operand: a weight tile of 128 rows x one K step stored as the
@@ -421,11 +437,12 @@ struct Frags {
 
 // LDS reads of the wave's fragments of the stage at `st`.
 template <class Cfg>
-__device__ __forceinline__ void read_frags(Frags<Cfg>& fr, const bf16_t* st, int wm, int wn, int lane) {
+__device__ __forceinline__ void read_frags(Frags<Cfg>& fr, const bf16_t* st, int wm, int wn, int lane,
+                                           int sub = 0) {
   const bf16_t* As = st;
   const bf16_t* Bs = st + Cfg::A_ELEMS;
   const int r = lane & 15;
-  const int slot = (lane >> 4) ^ chunk_key(r);
+  const int slot = ((lane >> 4) + 4 * sub) ^ lds_key<Cfg>(r);
 #pragma unroll
   for (int j = 0; j < Cfg::FN; ++j)
     fr.b[j] = *reinterpret_cast<const bf16x8*>(&Bs[(wn * (Cfg::BN / Cfg::WN) + j * 16 + r) * Cfg::BK + slot * 8]);
@@ -542,6 +559,7 @@ __device__ __forceinline__ void dma_wait_stage(int younger) {
 // flight.
 template <class Cfg, class Prob>
 __device__ __forceinline__ void persistent_gemm_dma(Prob& pb, int items, int nk) {
+  static_assert(Cfg::KSUB == 1, "one MFMA K step per stage");
   constexpr int S = Cfg::STAGES;
   __shared__ __align__(16) bf16_t ring[S * Cfg::STAGE_ELEMS];
   const XcdSplit sp = xcd_split(items);
@@ -634,7 +652,7 @@ __device__ __forceinline__ void sym_read_lo(SymFrags<Cfg>& f, const bf16_t* st, 
   const bf16_t* As = st;
   const bf16_t* Bs = st + Cfg::A_ELEMS;
   const int r = lane & 15;
-  const int slot = (lane >> 4) ^ chunk_key(r);
+  const int slot = (lane >> 4) ^ lds_key<Cfg>(r);
 #pragma unroll
   for (int j = 0; j < Cfg::FN; ++j)
     f.b[j] = *reinterpret_cast<const bf16x8*>(&Bs[(wn * (Cfg::BN / Cfg::WN) + j * 16 + r) * Cfg::BK + slot * 8]);
@@ -646,7 +664,7 @@ __device__ __forceinline__ void sym_read_lo(SymFrags<Cfg>& f, const bf16_t* st, 
 template <class Cfg>
 __device__ __forceinline__ void sym_read_hi(bf16x8 (&ahi)[Cfg::FM / 2], const bf16_t* st, int wm, int lane) {
   const int r = lane & 15;
-  const int slot = (lane >> 4) ^ chunk_key(r);
+  const int slot = (lane >> 4) ^ lds_key<Cfg>(r);
 #pragma unroll
   for (int i = 0; i < Cfg::FM / 2; ++i)
     ahi[i] = *reinterpret_cast<const bf16x8*>(&st[(frag_row0<Cfg>(wm, i + Cfg::FM / 2) + r) * Cfg::BK + slot * 8]);
@@ -662,9 +680,91 @@ __device__ __forceinline__ void sym_mma(Acc<Cfg>& acc, const bf16x8 (&b)[Cfg::FN
       acc.v[i0 + i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[j], a[i], acc.v[i0 + i][j], 0, 0, 0);
 }
 
+// Symmetric driver for 64-K stages (KSUB = 2): the two phases of a step are
+// the stage's two MFMA K steps instead of two halves of the A fragments.
+//   1. LDS reads of stage g's second K half (all fragments) into one set;
+//      MFMAs of its first half from the other set (read in phase 2 of step
+//      g - 1).
+//   2. wait for the reads and the wave's own DMAs of stage g + 1; barrier;
+//      issue stage g + STAGES into slot g % STAGES; reads of stage g + 1's
+//      first half; MFMAs of stage g's second half.
+template <class Cfg, class Prob>
+__device__ __forceinline__ void persistent_gemm_sym_k64(Prob& pb, int items, int nk) {
+  static_assert(Cfg::PW == 0 && Cfg::KSUB == 2, "symmetric configuration, 64-K stages");
+  constexpr int S = Cfg::STAGES;
+  __shared__ __align__(16) bf16_t ring[S * Cfg::STAGE_ELEMS];
+  const XcdSplit sp = xcd_split(items);
+  if (sp.first >= sp.end || nk <= 0) return;
+  const int n_mine = (sp.end - sp.first + sp.stride - 1) / sp.stride;
+  const int total = n_mine * nk;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
+  DmaLoader<Cfg> ld;
+  int l_ord = 0, l_kt = 0, l_slot = 0;  // load cursor
+  pb.setup(sp.first, ld, wave);
+  auto issue_next = [&]() {
+    dma_issue<Cfg>(ld, l_kt, ring + l_slot * Cfg::STAGE_ELEMS, wave);
+    l_slot = (l_slot + 1 == S) ? 0 : l_slot + 1;
+    if (++l_kt == nk) {
+      l_kt = 0;
+      if (++l_ord < n_mine) pb.setup(sp.first + l_ord * sp.stride, ld, wave);
+    }
+  };
+  for (int p = 0; p < S - 1 && p < total; ++p) issue_next();
+  dma_wait_stage<Cfg>(total - 1);
+  ring_barrier();
+  if (S - 1 < total) issue_next();
+  Acc<Cfg> acc;
+  Frags<Cfg> f0, f1;  // first / second K half of a stage
+  read_frags<Cfg>(f0, ring, wm, wn, lane, 0);
+  int c_slot = 0;
+  bool drain = false;  // epilogue stores are still counted on vmcnt
+  auto mma = [&](const Frags<Cfg>& f) {
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < Cfg::FN; ++j)
+        acc.v[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.b[j], f.a[i], acc.v[i][j], 0, 0, 0);
+  };
+  for (int c_ord = 0; c_ord < n_mine; ++c_ord) {
+    const int g0 = c_ord * nk;
+    acc.zero();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int g = g0 + kt;
+      read_frags<Cfg>(f1, ring + c_slot * Cfg::STAGE_ELEMS, wm, wn, lane, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(f0);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_lgkm0();
+      if (g + 1 < total) {
+        if (drain) {
+          wait_vmcnt_imm<0>();
+          drain = false;
+        } else {
+          dma_wait_stage<Cfg>(total - 2 - g);
+        }
+      }
+      ring_barrier();
+      if (g + S < total) issue_next();
+      c_slot = (c_slot + 1 == S) ? 0 : c_slot + 1;
+      if (g + 1 < total) read_frags<Cfg>(f0, ring + c_slot * Cfg::STAGE_ELEMS, wm, wn, lane, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(f1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    pb.epilogue(sp.first + c_ord * sp.stride, acc);
+    drain = true;
+  }
+}
+
 template <class Cfg, class Prob>
 __device__ __forceinline__ void persistent_gemm_sym(Prob& pb, int items, int nk) {
   static_assert(Cfg::PW == 0, "symmetric configuration");
+  if constexpr (Cfg::KSUB == 2) {
+    persistent_gemm_sym_k64<Cfg>(pb, items, nk);
+    return;
+  } else {
   static_assert(Cfg::FM % 2 == 0, "two halves of A fragments");
   constexpr int S = Cfg::STAGES;
   constexpr int H = Cfg::FM / 2;
@@ -738,6 +838,7 @@ __device__ __forceinline__ void persistent_gemm_sym(Prob& pb, int items, int nk)
     }
     pb.epilogue(sp.first + c_ord * sp.stride, acc);
     drain = true;
+  }
   }
 }
 

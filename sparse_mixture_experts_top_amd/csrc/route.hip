@@ -27,13 +27,13 @@ struct RouterProb {
 
   __device__ __forceinline__ void setup(int item, DmaLoader<Cfg>& ld, int part) const {
     const int m0 = (item / nt) * Cfg::BM, n0 = (item % nt) * Cfg::BN;
-    const int ce = dma_chunk_elem();
+    const int ce = dma_chunk_elem<Cfg>();
 #pragma unroll
     for (int q = 0; q < Cfg::A_DMA / Cfg::DW; ++q)
-      ld.a[q] = x + (int64_t)min(m0 + dma_row(q * Cfg::DW + part), T - 1) * d + ce;
+      ld.a[q] = x + (int64_t)min(m0 + dma_row<Cfg>(q * Cfg::DW + part), T - 1) * d + ce;
 #pragma unroll
     for (int q = 0; q < Cfg::B_DMA / Cfg::DW; ++q)
-      ld.b[q] = w + (int64_t)min(n0 + dma_row(q * Cfg::DW + part), E - 1) * d + ce;
+      ld.b[q] = w + (int64_t)min(n0 + dma_row<Cfg>(q * Cfg::DW + part), E - 1) * d + ce;
   }
 
   __device__ __forceinline__ void epilogue(int item, Acc<Cfg>& acc) const {
@@ -116,7 +116,7 @@ static hipError_t launch_router_bf16(const Ctx& c, const moe_shape_t& s, const b
 #ifndef MOE_ROUTER_STAGES
 #define MOE_ROUTER_STAGES 6
 #endif
-using RouterHuge = DmaCfg<256, 256, 4, 2, 8, 0>;
+using RouterHuge = DmaCfg<256, 256, 2, 2, 8, 0, 64>;
 using RouterLarge = DmaCfg<128, 256, MOE_ROUTER_STAGES, 2, 8, 4>;
 using RouterMedium = DmaCfg<128, 128, MOE_ROUTER_STAGES, 2, 8, 4>;
 using RouterSmall = DmaCfg<64, 128, 4, 2, 4, 4>;
