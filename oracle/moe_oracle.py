@@ -45,6 +45,13 @@ reason in the design notes of the repository):
    base weights are frozen ([Guide §3]: do not tune the routing gates), so
    only the four adapter gradients are produced.
 
+8. The full backward of the layer (gradients of sum(y * dY) + L_aux with
+   respect to x and the router logits) treats the gates as functions of the
+   selected logits only (the selection itself is piecewise constant), the
+   load-balance fractions f_e as constants (counts are not differentiable),
+   assignments that were dropped or belong to other experts' ranks as
+   contributing nothing to y, and the expert and router weights as frozen.
+
 Parity pins: every function here is checked by tests against closed forms,
 invariants, brute force or finite differences (tests/test_oracle_*.py).
 """
@@ -323,3 +330,129 @@ def lora_backward(dy, x_perm, offsets, row_src, row_gate, G, H, w_down, lora):
         db_up[le] = s * dU.T @ Zu
         da_up[le] = s * (dU @ B_u[le]).T @ Xe
     return {"da_up": da_up, "db_up": db_up, "da_down": da_down, "db_down": db_down}
+
+
+# ---------------------------------------------------------- full backward --
+#
+# Gradients of the loss sum(y * dY) + L_aux, the full backward pass of the
+# layer ([Guide §3]: the adapters are trained through the frozen MoE layer,
+# so the upstream layers need dx; [FullOpt §3]: the backward runs the same
+# permute / grouped GEMM / unpermute stages in reverse).
+
+def silu_grad(a):
+    """d silu(a) / da = sigma(a) (1 + a (1 - sigma(a)))."""
+    a = _f64(a)
+    sg = 1.0 / (1.0 + np.exp(-a))
+    return sg * (1.0 + a * (1.0 - sg))
+
+
+def gate_backward(dy, o_rows, slot, gate, T: int):
+    """dg[t,j] = <dY_t, O[slot[t,j]]> for kept local slots, else 0: y is
+    linear in each gate with coefficient the expert's output row."""
+    dY, O = _f64(dy), _f64(o_rows)
+    slot = np.asarray(slot)
+    k = slot.shape[1]
+    dg = np.zeros((T, k), dtype=F64)
+    for t in range(T):
+        for j in range(k):
+            s = slot[t, j]
+            if s >= 0:
+                dg[t, j] = float(np.dot(dY[t], O[s]))
+    return dg
+
+
+def logits_backward(dgate, idx, gate, logits, counts=None, aux_coef: float = 0.0, k: Optional[int] = None):
+    """dL/dl for L = sum(y dY) + L_aux, given dg = dL/dg.
+
+    Gate path: g_j = exp(l_{idx_j}) / sum_i exp(l_{idx_i}) over the k
+    selected experts, so dl_{idx_j} = g_j (dg_j - sum_i g_i dg_i) and the
+    unselected logits get nothing from it.
+    Aux path (with counts): L_aux = coef E sum_e f_e P_e, f_e = counts_e /
+    (T k) held constant, P_e = (1/T) sum_t p_te with p_t = softmax(l_t) over
+    all E; dP_e/dl_tc = p_te (delta_ec - p_tc) / T, so
+    dL_aux/dl_tc = coef E / T * p_tc (f_c - sum_e f_e p_te)."""
+    dg, g = _f64(dgate), _f64(gate)
+    idx = np.asarray(idx)
+    l = _f64(logits)
+    T, E = l.shape
+    dl = np.zeros((T, E), dtype=F64)
+    inner = (g * dg).sum(axis=1, keepdims=True)
+    contrib = g * (dg - inner)
+    for t in range(T):
+        for j in range(idx.shape[1]):
+            dl[t, idx[t, j]] += contrib[t, j]
+    if counts is not None and aux_coef != 0.0:
+        kk = idx.shape[1] if k is None else k
+        fr = _f64(counts) / (T * kk)
+        p = softmax_full(l)
+        fp = (p * fr[None, :]).sum(axis=1, keepdims=True)
+        dl = dl + aux_coef * E / T * p * (fr[None, :] - fp)
+    return dl
+
+
+def experts_backward(dy, offsets, row_src, row_gate, slot, x_perm, w_gate, w_up, w_down, T: int,
+                     lora=None):
+    """dx through the frozen experts (gates held fixed). Per local expert,
+    with dO_p = g_p dY[src_p] and the forward's G, U recomputed from x_perm:
+      dH = dO W_d (+ s (dO B_d) A_d)
+      dG = dH * U * silu'(G),   dU = dH * silu(G)
+      dX = dG W_g + dU W_u (+ s (dU B_u) A_u)
+    and dx[t] = sum over the token's kept local slots j (in j order) of
+    dX[slot[t,j]] (the unpermute of the backward). Returns (dx [T,d],
+    dX rows [R,d], dict of G, U, dG, dU rows)."""
+    dY, X = _f64(dy), _f64(x_perm)
+    g = _f64(row_gate)
+    d = _f64(w_down).shape[1]
+    R = X.shape[0]
+    f = _f64(w_gate).shape[1]
+    dX = np.zeros((R, d), dtype=F64)
+    parts = {n: np.zeros((R, f), dtype=F64) for n in ("G", "U", "dG", "dU")}
+    for le in range(len(offsets) - 1):
+        a, b = int(offsets[le]), int(offsets[le + 1])
+        if a == b:
+            continue
+        lo = _lora_of(lora, le)
+        Xe = X[a:b]
+        Wg, Wu, Wd = _f64(w_gate[le]), _f64(w_up[le]), _f64(w_down[le])
+        G = Xe @ Wg.T
+        U = Xe @ Wu.T
+        if lo is not None:
+            U = U + lo["scale"] * (Xe @ _f64(lo["a_up"]).T) @ _f64(lo["b_up"]).T
+        dO = g[a:b, None] * dY[np.asarray(row_src[a:b])]
+        dH = dO @ Wd
+        if lo is not None:
+            dH = dH + lo["scale"] * (dO @ _f64(lo["b_down"])) @ _f64(lo["a_down"])
+        dG = dH * U * silu_grad(G)
+        dU = dH * silu(G)
+        dXe = dG @ Wg + dU @ Wu
+        if lo is not None:
+            dXe = dXe + lo["scale"] * (dU @ _f64(lo["b_up"])) @ _f64(lo["a_up"])
+        dX[a:b] = dXe
+        for n, v in (("G", G), ("U", U), ("dG", dG), ("dU", dU)):
+            parts[n][a:b] = v
+    dx = np.zeros((T, d), dtype=F64)
+    slot = np.asarray(slot)
+    for t in range(T):
+        for j in range(slot.shape[1]):
+            s = slot[t, j]
+            if s >= 0:
+                dx[t] += dX[s]
+    return dx, dX, parts
+
+
+def router_backward(dlogits, w_router):
+    """dx contribution of the router: logits = x W_r^T (+ b), so
+    dx[t] = sum_e dl[t,e] W_r[e]."""
+    return _f64(dlogits) @ _f64(w_router)
+
+
+def moe_layer_backward(fwd, dy, x, w_router, w_gate, w_up, w_down, k: int, T: int, lora=None,
+                       aux_coef: float = 0.0):
+    """The layer's full backward from an oracle forward ``fwd`` (moe_layer):
+    returns dgate, dlogits and dx = experts part + router part."""
+    dg = gate_backward(dy, fwd["o"], fwd["slot"], fwd["gate"], T)
+    dl = logits_backward(dg, fwd["idx"], fwd["gate"], fwd["logits"], fwd["counts"], aux_coef, k)
+    dx_e, _, _ = experts_backward(dy, fwd["offsets"], fwd["row_src"], fwd["row_gate"], fwd["slot"],
+                                  fwd["x_perm"], w_gate, w_up, w_down, T, lora)
+    return {"dgate": dg, "dlogits": dl, "dx_experts": dx_e,
+            "dx": dx_e + router_backward(dl, w_router)}

@@ -6,6 +6,7 @@ import pytest
 
 import oracle
 import oracle.moe_oracle as mo
+import test_oracle_backward as tbwd
 import test_oracle_dispatch as tdisp
 import test_oracle_experts as texp
 import test_oracle_routing as trout
@@ -61,8 +62,32 @@ def _aux_wrong_norm(counts, prob_sum, T, k, coef):
     return ORIG["aux_loss"](counts, prob_sum, T, 1, coef)
 
 
+def _silu_grad_is_silu(a):
+    return ORIG["silu"](a)
+
+
+def _dlogits_not_centred(dgate, idx, gate, logits, counts=None, aux_coef=0.0, k=None):
+    # drops the - sum_i g_i dg_i term of the softmax Jacobian
+    g, dg = np.asarray(gate, F64), np.asarray(dgate, F64)
+    out = ORIG["logits_backward"](dgate, idx, gate, logits, counts, aux_coef, k)
+    inner = (g * dg).sum(axis=1, keepdims=True)
+    np.add.at(out, (np.arange(out.shape[0])[:, None], np.asarray(idx)), g * inner)
+    return out
+
+
+def _dlogits_aux_sign(dgate, idx, gate, logits, counts=None, aux_coef=0.0, k=None):
+    return ORIG["logits_backward"](dgate, idx, gate, logits, counts, -aux_coef, k)
+
+
+def _experts_bwd_gate_up_swapped(dy, offsets, row_src, row_gate, slot, x_perm, w_gate, w_up, w_down, T,
+                                 lora=None):
+    return ORIG["experts_backward"](dy, offsets, row_src, row_gate, slot, x_perm, w_up, w_gate, w_down, T,
+                                    lora)
+
+
 ORIG = {n: getattr(mo, n) for n in ("topk_experts", "topk_gates", "silu", "expert_ffn",
-                                     "dispatch", "lora_backward", "aux_loss")}
+                                     "dispatch", "lora_backward", "aux_loss", "silu_grad",
+                                     "logits_backward", "experts_backward")}
 
 MUTANTS = {
     "ties_to_higher_id": ("topk_experts", _topk_ties_high),
@@ -74,7 +99,24 @@ MUTANTS = {
     "backward_ignores_gate": ("lora_backward", _bwd_no_gate),
     "backward_lora_dh_sign": ("lora_backward", _bwd_wrong_sign_lora_dh),
     "aux_loss_drops_k": ("aux_loss", _aux_wrong_norm),
+    "silu_grad_is_silu": ("silu_grad", _silu_grad_is_silu),
+    "dlogits_not_centred": ("logits_backward", _dlogits_not_centred),
+    "dlogits_aux_sign": ("logits_backward", _dlogits_aux_sign),
+    "experts_backward_gate_up_swapped": ("experts_backward", _experts_bwd_gate_up_swapped),
 }
+
+
+def _pin_dx_fd_plain():
+    tbwd.test_dx_matches_central_differences(tbwd.CASES[0], 0.3)
+
+
+def _pin_dx_fd_lora_capacity():
+    tbwd.test_dx_matches_central_differences(tbwd.CASES[3], 0.0)
+    tbwd.test_dx_matches_central_differences(tbwd.CASES[4], 0.0)
+
+
+def _pin_dlogits_fd():
+    tbwd.test_dlogits_matches_central_differences(tbwd.CASES[1])
 
 PINS = [
     trout.test_topk_matches_brute_force_with_ties, trout.test_topk_signed_zero_ties_to_lower_id,
@@ -87,6 +129,8 @@ PINS = [
     texp.test_layer_equals_per_token_sum_over_selected_experts,
     texp.test_aux_loss_uniform_and_hand_case, texp.test_lora_forward_equals_merged_weights,
     texp.test_lora_backward_matches_central_differences,
+    tbwd.test_silu_grad_closed_form_and_differences, _pin_dx_fd_plain, _pin_dx_fd_lora_capacity,
+    _pin_dlogits_fd, tbwd.test_dlogits_rows_sum_to_zero_and_k1_gate_path_vanishes,
 ]
 
 
