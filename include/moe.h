@@ -174,9 +174,10 @@ moe_status_t moe_dispatch(const moe_shape_t* shape, const int32_t* topk_idx,
  *   offsets  [L+1] int32           from moe_dispatch
  *   w_gate   [L, f, d]        w_up [L, f, d]        w_down [L, d, f]
  *   lora     [host] | NULL    adapters (bf16 only)
- *   act_save [Rmax, 2f]|NULL  OUT (optional): per row G (columns 0..f-1) and
- *                             the H fed to the down projection (f..2f-1);
- *                             moe_lora_bwd needs it
+ *   act_save [Rmax, 3f]|NULL  OUT (optional): per row G (columns 0..f-1),
+ *                             the H fed to the down projection (f..2f-1) and
+ *                             U (2f..3f-1, LoRA term included);
+ *                             moe_lora_bwd and moe_expert_bwd need it
  *   y_perm   [Rmax, d]        OUT: O per row (not gate-scaled)
  * Accumulation is fp32; in bf16 mode H is rounded to bf16 before the down
  * projection and O is stored as bf16. */
@@ -245,7 +246,7 @@ moe_status_t moe_aux_loss(const moe_shape_t* shape, const int32_t* counts,
  *   x, x_src                      input rows as for moe_expert_gemm: the
  *                                 tokens [T, d] with x_src = row_src, or
  *                                 x_perm [Rmax, d] with x_src = NULL
- *   act_save    [Rmax, 2f]        from moe_expert_gemm (G and H)
+ *   act_save    [Rmax, 3f]        from moe_expert_gemm (G, H, U)
  *   w_down      [L, d, f]
  *   da_up [L,r,d], db_up [L,f,r], da_down [L,r,f], db_down [L,d,r]   OUT, f32
  * bf16 only. Every gradient element is written (zero for experts with no
@@ -255,6 +256,66 @@ moe_status_t moe_lora_bwd(const moe_shape_t* shape, const moe_lora_t* lora, cons
                           const void* x, const int32_t* x_src, const void* act_save,
                           const void* w_down, float* da_up, float* db_up, float* da_down,
                           float* db_down, void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* ---- full backward --------------------------------------------------------
+ * Gradients of the loss sum(y * dy) + L_aux for training through the layer
+ * ("Full-Stack Engineering Guide", §3: adapters are trained through the
+ * frozen MoE layer, which therefore has to pass gradients down; "Full-Stack
+ * Optimization Practices", §3: the permute / grouped GEMM / unpermute stages
+ * run again in reverse). The router, the gates' selection and the expert
+ * weights are frozen; the selection is held (it is piecewise constant).
+ *
+ * moe_gate_bwd: gate and router-logit gradients.
+ *   dy        [T, d]      upstream gradient of y (the shape's dtype)
+ *   y_perm    [Rmax, d]   the forward's expert output rows (moe_expert_gemm)
+ *   slot      [T, k]      from moe_dispatch
+ *   topk_idx, topk_gate   [T, k] from moe_route
+ *   logits    [T, E] f32  from moe_route; read only with counts
+ *   counts    [E] | NULL  from moe_dispatch: adds the load-balance loss
+ *                         gradient (with aux_coef; NULL or coef 0: none)
+ *   dgate     [T, k] f32 | NULL  OUT: dg[t,j] = <dy[t], y_perm[slot[t,j]]>
+ *                         for kept local slots, else 0
+ *   dlogits   [T, E] f32  OUT: dl[t, idx_j] = g_j (dg_j - sum_i g_i dg_i)
+ *                         (the gates are the softmax over the selected
+ *                         logits), plus, with counts, coef E / T * p_te
+ *                         (f_e - sum_e' f_e' p_te'), p = softmax over all E,
+ *                         f = counts / (T k) held constant.
+ * Every element of dlogits is written. */
+moe_status_t moe_gate_bwd(const moe_shape_t* shape, const void* dy, const void* y_perm,
+                          const int32_t* slot, const int32_t* topk_idx, const float* topk_gate,
+                          const float* logits, const int32_t* counts, float aux_coef, float* dgate,
+                          float* dlogits, moe_stream_t stream);
+
+/* moe_expert_bwd: dx through the frozen experts (gates held). Per row p of
+ * local expert le, dO = g_p dy[row_src[p]]:
+ *   dH = dO w_down[le] (+ s (dO B_down) A_down),
+ *   dG = dH * U * silu'(G),  dU = dH * silu(G)   (G, U from act_save),
+ *   dX = dG w_gate[le] + dU w_up[le] (+ s (dU B_up) A_up),
+ * and dx[t] = sum over the token's kept local slots j, in j order, of dX.
+ *   lora      [host] | NULL  adapters of the forward (bf16 only)
+ *   dy        [T, d]         upstream gradient (the shape's dtype)
+ *   offsets, row_src, row_gate, slot   from moe_dispatch
+ *   act_save  [Rmax, 3f]     from moe_expert_gemm
+ *   w_gate, w_up [L, f, d], w_down [L, d, f]   row-major (not packed)
+ *   dgu       [Rmax, 2f]     scratch (the shape's dtype): dG | dU per row
+ *   dx_rows   [Rmax, d] f32  scratch: dX per row
+ *   dx        [T, d] f32     OUT (tokens with no kept local slot get 0)
+ * bf16 rounds dG and dU to bf16 before the dX product; accumulation is
+ * fp32 throughout. */
+moe_status_t moe_expert_bwd(const moe_shape_t* shape, const moe_lora_t* lora, const void* dy,
+                            const int32_t* offsets, const int32_t* row_src, const float* row_gate,
+                            const int32_t* slot, const void* act_save, const void* w_gate,
+                            const void* w_up, const void* w_down, void* dgu, float* dx_rows, float* dx,
+                            void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* moe_router_bwd: the router's part of dx, dx[t] += sum_e dlogits[t, e]
+ * w_router[e] (logits = x w_router^T + bias).
+ *   dlogits [T, E] f32 (moe_gate_bwd), w_router [E, d], dx [T, d] f32 IN/OUT.
+ * bf16 with E % 64 == 0 rounds dlogits to bf16 (in the workspace's logits
+ * area) and multiplies on the matrix cores with fp32 accumulation; other
+ * shapes use an fp32 loop. */
+moe_status_t moe_router_bwd(const moe_shape_t* shape, const float* dlogits, const void* w_router,
+                            float* dx, void* ws, size_t ws_bytes, moe_stream_t stream);
 
 /* ---- kernel timing (profiling aid) -------------------------------------
  * When enabled for a kernel kind, the library records a pair of HIP events
@@ -280,7 +341,12 @@ typedef enum {
   MOE_K_LORA_PROJ = 13,
   MOE_K_LORA_DH = 14,
   MOE_K_LORA_GRAD = 15,
-  MOE_K_COUNT = 16
+  MOE_K_GATE_BWD = 16,
+  MOE_K_EXPERT_DGU = 17,
+  MOE_K_EXPERT_DX = 18,
+  MOE_K_UNPERMUTE = 19,
+  MOE_K_ROUTER_BWD = 20,
+  MOE_K_COUNT = 21
 } moe_kernel_t;
 
 /* mask: bit k (1 << moe_kernel_t) enables timing of kind k; 0 disables all,

@@ -18,7 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_mi355x.so")
-SOURCES = ["api.hip", "route.hip", "dispatch.hip", "expert_gemm.hip", "combine.hip", "lora.hip"]
+SOURCES = ["api.hip", "route.hip", "dispatch.hip", "expert_gemm.hip", "combine.hip", "lora.hip",
+           "backward.hip"]
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
 

@@ -23,11 +23,12 @@ MOE_F32, MOE_BF16 = 0, 1
 
 KERNELS = ["router_gemm", "topk", "prob_reduce", "hist", "scan", "scatter", "capacity",
            "gather", "tiles", "gate_up", "down", "combine", "aux", "lora_proj", "lora_dh",
-           "lora_grad"]
+           "lora_grad", "gate_bwd", "expert_dgu", "expert_dx", "unpermute", "router_bwd"]
 
 EXPORTED = ["moe_workspace_bytes", "moe_max_rows", "moe_last_error", "moe_route",
             "moe_dispatch", "moe_expert_gemm", "moe_pack_expert_weights", "moe_expert_gemm_packed",
-            "moe_combine", "moe_aux_loss", "moe_lora_bwd", "moe_timing_enable", "moe_timing_read"]
+            "moe_combine", "moe_aux_loss", "moe_lora_bwd", "moe_gate_bwd", "moe_expert_bwd",
+            "moe_router_bwd", "moe_timing_enable", "moe_timing_read"]
 
 
 class MoeShape(ctypes.Structure):
@@ -71,10 +72,14 @@ def lib() -> ctypes.CDLL:
     L.moe_combine.argtypes = [shp, vp, vp, vp, vp, vp]
     L.moe_aux_loss.argtypes = [shp, vp, vp, f32, vp, vp]
     L.moe_lora_bwd.argtypes = [shp, lor, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_gate_bwd.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp]
+    L.moe_expert_bwd.argtypes = [shp, lor, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_router_bwd.argtypes = [shp, vp, vp, vp, vp, sz, vp]
     L.moe_timing_enable.argtypes = [i32]
     L.moe_timing_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     for fn in ("moe_route", "moe_dispatch", "moe_expert_gemm", "moe_pack_expert_weights",
                "moe_expert_gemm_packed", "moe_combine", "moe_aux_loss", "moe_lora_bwd",
+               "moe_gate_bwd", "moe_expert_bwd", "moe_router_bwd",
                "moe_timing_enable", "moe_timing_read"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
@@ -193,6 +198,32 @@ def moe_lora_bwd(shape, lora, dy, offsets, row_src, row_gate, x, x_src, act_save
                               _dev(act_save, bf), _dev(w_down, bf), _dev(da_up, f32),
                               _dev(db_up, f32), _dev(da_down, f32), _dev(db_down, f32),
                               _dev(ws, torch.uint8), ws.numel(), _stream(stream)))
+
+
+def moe_gate_bwd(shape, dy, y_perm, slot, topk_idx, topk_gate, logits, counts, aux_coef, dgate, dlogits,
+                 stream=None):
+    dt = _fdt(shape)
+    f32, i32 = torch.float32, torch.int32
+    _check(lib().moe_gate_bwd(ctypes.byref(shape), _dev(dy, dt), _dev(y_perm, dt), _dev(slot, i32),
+                              _dev(topk_idx, i32), _dev(topk_gate, f32), _dev(logits, f32), _dev(counts, i32),
+                              ctypes.c_float(aux_coef), _dev(dgate, f32), _dev(dlogits, f32), _stream(stream)))
+
+
+def moe_expert_bwd(shape, lora, dy, offsets, row_src, row_gate, slot, act_save, w_gate, w_up, w_down, dgu,
+                   dx_rows, dx, ws, stream=None):
+    dt = _fdt(shape)
+    f32, i32 = torch.float32, torch.int32
+    _check(lib().moe_expert_bwd(ctypes.byref(shape), ctypes.byref(lora) if lora is not None else None,
+                                _dev(dy, dt), _dev(offsets, i32), _dev(row_src, i32), _dev(row_gate, f32),
+                                _dev(slot, i32), _dev(act_save, dt), _dev(w_gate, dt), _dev(w_up, dt),
+                                _dev(w_down, dt), _dev(dgu, dt), _dev(dx_rows, f32), _dev(dx, f32),
+                                _dev(ws, torch.uint8), ws.numel(), _stream(stream)))
+
+
+def moe_router_bwd(shape, dlogits, w_router, dx, ws, stream=None):
+    dt = _fdt(shape)
+    _check(lib().moe_router_bwd(ctypes.byref(shape), _dev(dlogits, torch.float32), _dev(w_router, dt),
+                                _dev(dx, torch.float32), _dev(ws, torch.uint8), ws.numel(), _stream(stream)))
 
 
 def moe_timing_enable(on=True) -> None:

@@ -417,6 +417,83 @@ moe_status_t moe_lora_bwd(const moe_shape_t* shape, const moe_lora_t* lora, cons
       "LoRA backward");
 }
 
+moe_status_t moe_gate_bwd(const moe_shape_t* shape, const void* dy, const void* y_perm,
+                          const int32_t* slot, const int32_t* topk_idx, const float* topk_gate,
+                          const float* logits, const int32_t* counts, float aux_coef, float* dgate,
+                          float* dlogits, moe_stream_t stream) {
+  moe_status_t st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape_t& s = *shape;
+  const bool tok = s.T > 0;
+  MOE_REQUIRE_IF(tok, dy, "dy");
+  MOE_REQUIRE_IF(tok && max_rows(s) > 0, y_perm, "y_perm");
+  MOE_REQUIRE_IF(tok, slot, "slot");
+  MOE_REQUIRE_IF(tok, topk_idx, "topk_idx");
+  MOE_REQUIRE_IF(tok, topk_gate, "topk_gate");
+  MOE_REQUIRE_IF(tok && counts && aux_coef != 0.f, logits, "logits");
+  MOE_REQUIRE_IF(tok, dlogits, "dlogits");
+  Ctx c;
+  if ((st = make_ctx(stream, &c)) != MOE_OK) return st;
+  return hip_status(launch_gate_bwd(c, s, dy, y_perm, slot, topk_idx, topk_gate, logits, counts, aux_coef,
+                                    dgate, dlogits),
+                    "gate backward");
+}
+
+moe_status_t moe_expert_bwd(const moe_shape_t* shape, const moe_lora_t* lora, const void* dy,
+                            const int32_t* offsets, const int32_t* row_src, const float* row_gate,
+                            const int32_t* slot, const void* act_save, const void* w_gate,
+                            const void* w_up, const void* w_down, void* dgu, float* dx_rows, float* dx,
+                            void* ws, size_t ws_bytes, moe_stream_t stream) {
+  moe_status_t st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape_t& s = *shape;
+  if ((st = check_lora(s, lora)) != MOE_OK) return st;
+  const bool rows = max_rows(s) > 0;
+  MOE_REQUIRE_IF(s.T > 0, dy, "dy");
+  MOE_REQUIRE(offsets, "offsets");
+  MOE_REQUIRE_IF(rows, row_src, "row_src");
+  MOE_REQUIRE_IF(rows, row_gate, "row_gate");
+  MOE_REQUIRE_IF(s.T > 0, slot, "slot");
+  MOE_REQUIRE_IF(rows, act_save, "act_save");
+  MOE_REQUIRE(w_gate, "w_gate");
+  MOE_REQUIRE(w_up, "w_up");
+  MOE_REQUIRE(w_down, "w_down");
+  MOE_REQUIRE_IF(rows, dgu, "dgu");
+  MOE_REQUIRE_IF(rows, dx_rows, "dx_rows");
+  MOE_REQUIRE_IF(s.T > 0, dx, "dx");
+  if ((st = check_ws(s, lora ? lora->r : 0, ws, ws_bytes)) != MOE_OK) return st;
+  Ctx c;
+  if ((st = make_ctx(stream, &c)) != MOE_OK) return st;
+  const Workspace w = carve_workspace(s, lora ? lora->r : 0, ws);
+  LoraArgs la{};
+  if (lora) {
+    la.r = lora->r;
+    la.scale = lora->alpha / (float)lora->r;
+    la.a_up = static_cast<const bf16_t*>(lora->a_up);
+    la.b_up = static_cast<const bf16_t*>(lora->b_up);
+    la.a_down = static_cast<const bf16_t*>(lora->a_down);
+    la.b_down = static_cast<const bf16_t*>(lora->b_down);
+  }
+  return hip_status(launch_expert_bwd(c, s, w, lora ? &la : nullptr, dy, offsets, row_src, row_gate, slot,
+                                      act_save, w_gate, w_up, w_down, dgu, dx_rows, dx),
+                    "expert backward");
+}
+
+moe_status_t moe_router_bwd(const moe_shape_t* shape, const float* dlogits, const void* w_router,
+                            float* dx, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  moe_status_t st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape_t& s = *shape;
+  MOE_REQUIRE_IF(s.T > 0, dlogits, "dlogits");
+  MOE_REQUIRE(w_router, "w_router");
+  MOE_REQUIRE_IF(s.T > 0, dx, "dx");
+  if ((st = check_ws(s, 0, ws, ws_bytes)) != MOE_OK) return st;
+  Ctx c;
+  if ((st = make_ctx(stream, &c)) != MOE_OK) return st;
+  const Workspace w = carve_workspace(s, 0, ws);
+  return hip_status(launch_router_bwd(c, s, w, dlogits, w_router, dx), "router backward");
+}
+
 moe_status_t moe_timing_enable(int32_t mask) {
   Timing& t = timing();
   std::lock_guard<std::mutex> g(t.mu);

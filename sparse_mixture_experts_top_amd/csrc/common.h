@@ -172,6 +172,20 @@ hipError_t launch_lora_bwd(const Ctx& c, const moe_shape_t& s, const Workspace& 
                            const bf16_t* act_save, const bf16_t* w_down, float* da_up,
                            float* db_up, float* da_down, float* db_down);
 
+hipError_t launch_gate_bwd(const Ctx& c, const moe_shape_t& s, const void* dy, const void* y_perm,
+                           const int32_t* slot, const int32_t* idx, const float* gate,
+                           const float* logits, const int32_t* counts, float aux_coef, float* dgate,
+                           float* dlogits);
+
+hipError_t launch_expert_bwd(const Ctx& c, const moe_shape_t& s, const Workspace& ws, const LoraArgs* lo,
+                             const void* dy, const int32_t* offsets, const int32_t* row_src,
+                             const float* row_gate, const int32_t* slot, const void* act_save,
+                             const void* w_gate, const void* w_up, const void* w_down, void* dgu,
+                             float* dx_rows, float* dx);
+
+hipError_t launch_router_bwd(const Ctx& c, const moe_shape_t& s, const Workspace& ws, const float* dlogits,
+                             const void* w_router, float* dx);
+
 // LoRA building blocks shared by the forward (expert_gemm) and the backward.
 // out[p, q] = scale_p * sum_i in[src(p), i] * M(le(p), q, i) for rows p < R.
 //   m_qk: M stored [L, r, K] (true) or [L, K, r] (false)

@@ -202,7 +202,7 @@ struct GateUpProb {
         // f % 64 == 0: a 16-column fragment pair is all inside f or all past it
         if (ni * HALF + (jg >> 1) * 16 >= f) continue;
         const int fcol = ni * HALF + (jg >> 1) * 16 + (lane >> 4) * 4;
-        float h[4], g[4];
+        float h[4], g[4], uu[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           g[q] = acc.v[i][jj][q];
@@ -214,14 +214,17 @@ struct GateUpProb {
             for (int c = 0; c < r; ++c) s = fmaf(z[c], bf16_to_f32(bu[c]), s);
             u = fmaf(scale, s, u);
           }
+          uu[q] = u;
           h[q] = silu_f(g[q]) * u;
         }
         if (ok) {
           const uint2 hv = pack4_bf16(h[0], h[1], h[2], h[3]);
           *reinterpret_cast<uint2*>(hbuf + row * f + fcol) = hv;
           if (act_save) {
-            *reinterpret_cast<uint2*>(act_save + row * 2 * f + fcol) = pack4_bf16(g[0], g[1], g[2], g[3]);
-            *reinterpret_cast<uint2*>(act_save + row * 2 * f + f + fcol) = hv;
+            bf16_t* as = act_save + row * 3 * f + fcol;
+            *reinterpret_cast<uint2*>(as) = pack4_bf16(g[0], g[1], g[2], g[3]);
+            *reinterpret_cast<uint2*>(as + f) = hv;
+            *reinterpret_cast<uint2*>(as + 2 * f) = pack4_bf16(uu[0], uu[1], uu[2], uu[3]);
           }
         }
       }
@@ -407,8 +410,9 @@ __global__ __launch_bounds__(256) void gate_up_f32(const float* __restrict__ x_r
     const float h = silu_f(g) * u;
     hbuf[(int64_t)p * f + c] = h;
     if (act_save) {
-      act_save[(int64_t)p * 2 * f + c] = g;
-      act_save[(int64_t)p * 2 * f + f + c] = h;
+      act_save[(int64_t)p * 3 * f + c] = g;
+      act_save[(int64_t)p * 3 * f + f + c] = h;
+      act_save[(int64_t)p * 3 * f + 2 * f + c] = u;
     }
   }
 }

@@ -238,7 +238,7 @@ struct DhProb {
           const bf16_t* ad = a_down + (int64_t)le * r * f + n;
           for (int c = 0; c < r; ++c) t = fmaf(w[c], bf16_to_f32(ad[(int64_t)c * f]), t);
           const float dh = fmaf(row_gate[row], acc.v[i][j][q], s * t);
-          const float g = bf16_to_f32(act_save[row * 2 * f + n]);
+          const float g = bf16_to_f32(act_save[row * 3 * f + n]);
           du[row * f + n] = dh * silu_f(g);
         }
     }
@@ -262,13 +262,13 @@ hipError_t launch_lora_bwd(const Ctx& c, const moe_shape_t& sh, const Workspace&
   const int d = sh.d, f = sh.f, r = lo.r;
   const int64_t rmax = max_rows(sh);
   const int max_tiles = gemm_max_tiles(sh);
-  const bf16_t* H = act_save + f;  // rows of stride 2f
+  const bf16_t* H = act_save + f;  // rows of stride 3f (G | H | U)
   hipError_t err;
 #define MOE_TRY(x) \
   if ((err = (x)) != hipSuccess) return err
   MOE_TRY(launch_row_tiles(c, offsets, L, max_tiles, ws.gemm_tiles));
   MOE_TRY(launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, x_rows, d, x_src, nullptr, d, lo.a_up, true, r, ws.zu));
-  MOE_TRY(launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, H, 2 * f, nullptr, nullptr, f, lo.a_down, true, r, ws.zd));
+  MOE_TRY(launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, H, 3 * f, nullptr, nullptr, f, lo.a_down, true, r, ws.zd));
   MOE_TRY(launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, dy, d, row_src, row_gate, d, lo.b_down, false, r, ws.wproj));
   {
     TimedLaunch tl(MOE_K_LORA_DH, c.stream);
@@ -280,7 +280,7 @@ hipError_t launch_lora_bwd(const Ctx& c, const moe_shape_t& sh, const Workspace&
   }
   MOE_TRY(launch_lora_rowproj<float>(c, L, offsets, rmax, ws.du, f, nullptr, nullptr, f, lo.b_up, false, r, ws.vproj));
   MOE_TRY(launch_seg_outer<bf16_t>(c, L, offsets, ws.zd, r, dy, d, row_src, row_gate, d, lo.scale, false, db_down));
-  MOE_TRY(launch_seg_outer<bf16_t>(c, L, offsets, ws.wproj, r, H, 2 * f, nullptr, nullptr, f, lo.scale, true, da_down));
+  MOE_TRY(launch_seg_outer<bf16_t>(c, L, offsets, ws.wproj, r, H, 3 * f, nullptr, nullptr, f, lo.scale, true, da_down));
   MOE_TRY(launch_seg_outer<float>(c, L, offsets, ws.zu, r, ws.du, f, nullptr, nullptr, f, lo.scale, false, db_up));
   MOE_TRY(launch_seg_outer<bf16_t>(c, L, offsets, ws.vproj, r, x_rows, d, x_src, nullptr, d, lo.scale, true, da_up));
 #undef MOE_TRY

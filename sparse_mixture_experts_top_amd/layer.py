@@ -64,7 +64,7 @@ def alloc(shape: B.MoeShape, lora_r: int = 0, logits: bool = False, prob: bool =
         row_gate=torch.empty((max(rmax, 1),), dtype=torch.float32, **kw),
         x_perm=torch.empty((max(rmax, 1), d), dtype=dt, **kw) if x_perm else None,
         y_perm=torch.empty((max(rmax, 1), d), dtype=dt, **kw),
-        act_save=torch.empty((max(rmax, 1), 2 * f), dtype=dt, **kw) if act_save else None,
+        act_save=torch.empty((max(rmax, 1), 3 * f), dtype=dt, **kw) if act_save else None,
         y=torch.empty((T, d), dtype=dt, **kw),
         dropped=torch.zeros((1,), dtype=torch.int32, **kw),
         aux=torch.zeros((2,), dtype=torch.float32, **kw),

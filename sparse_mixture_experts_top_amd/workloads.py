@@ -128,8 +128,9 @@ def generate(w: Workload, seed: int = 0, threads: Optional[int] = None,
     """Draw every input of workload ``w`` as CPU tensors.
 
     Keys: x [T,d], w_router [E,d], bias [E] (fp32, only when zipf_s > 0),
-    w_gate [L,f,d], w_up [L,f,d], w_down [L,d,f], and for LoRA workloads
-    a_up [L,r,d], b_up [L,f,r], a_down [L,r,f], b_down [L,d,r], dy [T,d].
+    w_gate [L,f,d], w_up [L,f,d], w_down [L,d,f], for LoRA workloads
+    a_up [L,r,d], b_up [L,f,r], a_down [L,r,f], b_down [L,d,r], and with
+    with_dy the upstream gradient dy [T,d] of the backward.
     Expert tensors hold only the local experts e_lo..local_hi-1.
     """
     if threads is None:
@@ -163,7 +164,7 @@ def generate(w: Workload, seed: int = 0, threads: Optional[int] = None,
             else:
                 out["b_up"] = _to_tensor(_normal(ss["b_up"], (L, f, r), sb, 1, pool), w.dtype)
                 out["b_down"] = _to_tensor(_normal(ss["b_down"], (L, d, r), sb, 1, pool), w.dtype)
-        if w.lora_r > 0 and with_dy:
+        if with_dy:
             out["dy"] = _to_tensor(_normal(ss["dy"], (T, d), 1.0, _ROWS_PER_CHUNK, pool), w.dtype)
     return out
 

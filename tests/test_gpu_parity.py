@@ -260,7 +260,7 @@ def test_lora_forward_backward_and_aux(b_init, x_perm):
     lo = {"scale": w.lora_alpha / w.lora_r, **{n: to_f64(inp[n]) for n in ("a_up", "b_up", "a_down", "b_down")}}
     g_ref = oracle.lora_backward(to_f64(inp["dy"]), rows_x(w, inp, buf, np.arange(R)), host(buf.offsets),
                                  host(buf.row_src[:R]), buf.row_gate[:R].cpu().numpy(),
-                                 act[:, :w.f], act[:, w.f:], to_f64(inp["w_down"]), lo)
+                                 act[:, :w.f], act[:, w.f:2 * w.f], to_f64(inp["w_down"]), lo)
     for n in grads:
         assert_close(host(grads[n]), g_ref[n], "bf16", n)
     if b_init == "zero":

@@ -81,7 +81,7 @@ def test_lora_step_full():
               **{n: to_f64(inp[n][le:le + 1]) for n in ("a_up", "b_up", "a_down", "b_down")}}
         g_ref = oracle.lora_backward(dy64, rows_x(w, inp, buf, np.arange(a, b)), np.array([0, b - a]),
                                      host(buf.row_src[sl]), buf.row_gate[sl].cpu().numpy(),
-                                     act[:, :f], act[:, f:], to_f64(inp["w_down"][le:le + 1]), lo)
+                                     act[:, :f], act[:, f:2 * f], to_f64(inp["w_down"][le:le + 1]), lo)
         say(f"  expert {le}: {b - a} rows")
         for n in grads:
             assert_close(host(grads[n][le:le + 1]), g_ref[n], "bf16", f"{n}[{le}]")
