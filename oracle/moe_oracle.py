@@ -361,7 +361,8 @@ def gate_backward(dy, o_rows, slot, gate, T: int):
     return dg
 
 
-def logits_backward(dgate, idx, gate, logits, counts=None, aux_coef: float = 0.0, k: Optional[int] = None):
+def logits_backward(dgate, idx, gate, logits, counts=None, aux_coef: float = 0.0, k: Optional[int] = None,
+                    T_total: Optional[int] = None):
     """dL/dl for L = sum(y dY) + L_aux, given dg = dL/dg.
 
     Gate path: g_j = exp(l_{idx_j}) / sum_i exp(l_{idx_i}) over the k
@@ -370,15 +371,18 @@ def logits_backward(dgate, idx, gate, logits, counts=None, aux_coef: float = 0.0
     Aux path (with counts): L_aux = coef E sum_e f_e P_e, f_e = counts_e /
     (T k) held constant, P_e = (1/T) sum_t p_te with p_t = softmax(l_t) over
     all E; dP_e/dl_tc = p_te (delta_ec - p_tc) / T, so
-    dL_aux/dl_tc = coef E / T * p_tc (f_c - sum_e f_e p_te)."""
+    dL_aux/dl_tc = coef E / T * p_tc (f_c - sum_e f_e p_te).
+    T_total: the layer's token count when the rows given are a subset of the
+    tokens (every row is independent given the counts)."""
     dg, g = _f64(dgate), _f64(gate)
     idx = np.asarray(idx)
     l = _f64(logits)
     T, E = l.shape
-    dl = np.zeros((T, E), dtype=F64)
+    T = T if T_total is None else T_total
+    dl = np.zeros(l.shape, dtype=F64)
     inner = (g * dg).sum(axis=1, keepdims=True)
     contrib = g * (dg - inner)
-    for t in range(T):
+    for t in range(l.shape[0]):
         for j in range(idx.shape[1]):
             dl[t, idx[t, j]] += contrib[t, j]
     if counts is not None and aux_coef != 0.0:
