@@ -127,6 +127,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="full_router")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement pass")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--graph", dest="graph", action="store_true", default=False,
                     help="time one HIP-graph replay of the K steps (no per-kernel roofline: "
@@ -162,7 +163,6 @@ def main() -> int:
     buf = layer.alloc(shape)
     # the frozen expert weights live in their packed layout (one-time, outside the step)
     packed = layer.pack_weights(shape, dev["w_gate"], dev["w_up"], dev["w_down"])
-    del dev["w_gate"], dev["w_up"], dev["w_down"]
     torch.cuda.synchronize()
     args_fw = (dev["x"], dev["w_router"], dev.get("bias"), None, None, None)
 
@@ -266,10 +266,80 @@ def main() -> int:
         "kernels_us": {k: round(v["avg_us"], 2) for k, v in kernels.items()},
         "stage_roofline": stages,
     }
+    if not args.no_backward:
+        out["backward"] = backward_pass(w, dev, shape, packed, R, active)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp)
     print(json.dumps(out), flush=True)
     return 0
+
+
+def backward_pass(w, dev, shape, packed, R, active, reps=5):
+    """The full backward of the layer (gate / logit gradients with the
+    load-balance term, dx through the experts and the router) on the forward's
+    saved activations, outside the timed region: every kernel bracketed by
+    HIP events, averaged over ``reps`` passes, each against its roofline."""
+    import torch
+
+    from sparse_mixture_experts_top_amd import binding as B
+    from sparse_mixture_experts_top_amd import layer
+
+    T, d, E, k, f = w.T, w.d, w.E, w.k, w.f
+    buf = layer.alloc(shape, logits=True, prob=True, act_save=True)
+    layer.forward(buf, dev["x"], dev["w_router"], dev.get("bias"), None, None, None, packed=packed)
+    rmax = max(B.moe_max_rows(shape), 1)
+    dgate = torch.empty((T, k), device="cuda")
+    dlogits = torch.empty((T, E), device="cuda")
+    dgu = torch.empty((rmax, 2 * f), dtype=torch.bfloat16, device="cuda")
+    dx_rows = torch.empty((rmax, d), device="cuda")
+    dx = torch.empty((T, d), device="cuda")
+
+    def step():
+        B.moe_gate_bwd(shape, dev["dy"], buf.y_perm, buf.slot, buf.topk_idx, buf.topk_gate, buf.logits,
+                       buf.counts, 0.01, dgate, dlogits)
+        B.moe_expert_bwd(shape, None, dev["dy"], buf.offsets, buf.row_src, buf.row_gate, buf.slot,
+                         buf.act_save, dev["w_gate"], dev["w_up"], dev["w_down"], dgu, dx_rows, dx, buf.ws)
+        B.moe_router_bwd(shape, dlogits, dev["w_router"], dx, buf.ws)
+
+    step()
+    torch.cuda.synchronize()
+    names = ["gate_bwd", "tiles", "expert_dgu", "expert_dx", "unpermute", "router_bwd"]
+    B.moe_timing_enable(names)
+    for _ in range(reps):
+        step()
+    torch.cuda.synchronize()
+    us = {}
+    for n in names:
+        ms, cnt = B.moe_timing_read(n)
+        if cnt:
+            us[n] = 1000.0 * ms / cnt
+    B.moe_timing_enable(False)
+    work = {
+        "gate_bwd": ("hbm", R * d * 2 + T * d * 2 + 2 * T * E * 4 + T * k * 16),
+        "expert_dgu": ("hbm", active * d * f * 2 + R * d * 2 + 4 * R * f * 2),
+        "expert_dx": ("hbm", 2 * active * f * d * 2 + 2 * R * f * 2 + R * d * 4),
+        "unpermute": ("hbm", R * d * 4 + T * d * 4 + T * k * 4),
+        "router_bwd": ("mfma", 2.0 * T * E * d),
+    }
+    flops = {"expert_dgu": 2.0 * R * d * f, "expert_dx": 4.0 * R * f * d, "router_bwd": 2.0 * T * E * d}
+    stages = {}
+    for name, (bound, wk) in work.items():
+        if name not in us:
+            continue
+        rate = wk / (us[name] * 1e-6)
+        st = {"bound": bound, "us": round(us[name], 2)}
+        if bound == "mfma":
+            st.update(tflops=round(rate / 1e12, 1), frac=round(rate / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4))
+        else:
+            st.update(gbs=round(rate / 1e9, 1), frac=round(rate / 1e9 / HBM_PEAK_GBS, 4))
+            if name in flops:
+                st["tflops"] = round(flops[name] / (us[name] * 1e-6) / 1e12, 1)
+        stages[name] = st
+    total = sum(us.values())
+    return {"us_per_step": round(total, 2), "tokens_per_s": round(T / (total * 1e-6), 1),
+            "kernels_us": {n: round(v, 2) for n, v in us.items()}, "stage_roofline": stages,
+            "note": "gate + logit gradients (load-balance coef 0.01), dx through experts and router; "
+                    "sum of per-kernel event times, outside the timed region"}
 
 
 if __name__ == "__main__":

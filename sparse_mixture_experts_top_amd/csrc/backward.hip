@@ -417,20 +417,55 @@ __global__ __launch_bounds__(256) void expert_dx_f32(const float* __restrict__ d
 }
 
 // dx[t] = sum over the token's kept slots j, in j order, of dx_rows[slot].
+// Like the forward combine: TB tokens per workgroup, a wave per token
+// compacts its kept slots (ballot, j order) into LDS, then each thread owns
+// 4 consecutive columns and adds the rows in batches whose loads are all
+// issued before the first use (a short batch re-reads its last row and adds
+// it times 0 through selects).
+template <int NB>
+__device__ __forceinline__ void unpermute_batch(float4& acc, const float* __restrict__ rows, const int* s_slot,
+                                                int j0, int nb, int d, int v) {
+  float4 raw[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+    raw[b] = *reinterpret_cast<const float4*>(rows + (int64_t)s_slot[j0 + min(b, nb - 1)] * d + v * 4);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const float m = b < nb ? 1.f : 0.f;
+    acc.x = fmaf(m, raw[b].x, acc.x);
+    acc.y = fmaf(m, raw[b].y, acc.y);
+    acc.z = fmaf(m, raw[b].z, acc.z);
+    acc.w = fmaf(m, raw[b].w, acc.w);
+  }
+}
+
+template <int TB>
 __global__ __launch_bounds__(256) void unpermute_sum_f32(const float* __restrict__ dx_rows,
                                                          const int32_t* __restrict__ slot, int T, int k,
                                                          int d, float* __restrict__ dx) {
-  __shared__ int s_slot[32];
-  for (int t = blockIdx.x; t < T; t += gridDim.x) {
-    if (threadIdx.x < k) s_slot[threadIdx.x] = slot[(int64_t)t * k + threadIdx.x];
+  __shared__ int s_slot[TB][32];
+  __shared__ int s_n[TB];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nvec = d / 4;
+  for (int t0 = blockIdx.x * TB; t0 < T; t0 += gridDim.x * TB) {
+    const int nq = min(TB, T - t0);
+    for (int q = wave; q < nq; q += 4) {
+      const int sl = lane < k ? slot[(int64_t)(t0 + q) * k + lane] : -1;
+      const uint64_t kept = __ballot(sl >= 0);
+      const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+      if (sl >= 0) s_slot[q][__popcll(kept & below)] = sl;
+      if (lane == 0) s_n[q] = __popcll(kept);
+    }
     __syncthreads();
-    for (int c = threadIdx.x; c < d; c += blockDim.x) {
-      float acc = 0.f;
-      for (int j = 0; j < k; ++j) {
-        const int sl = s_slot[j];
-        if (sl >= 0) acc += dx_rows[(int64_t)sl * d + c];
+    for (int q = 0; q < nq; ++q) {
+      const int n = s_n[q];
+      for (int v = threadIdx.x; v < nvec; v += blockDim.x) {
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        int j0 = 0;
+        for (; j0 + 8 <= n; j0 += 8) unpermute_batch<8>(acc, dx_rows, s_slot[q], j0, 8, d, v);
+        for (; j0 < n; j0 += 2) unpermute_batch<2>(acc, dx_rows, s_slot[q], j0, n - j0, d, v);
+        *reinterpret_cast<float4*>(dx + (int64_t)(t0 + q) * d + v * 4) = acc;
       }
-      dx[(int64_t)t * d + c] = acc;
     }
     __syncthreads();
   }
@@ -496,8 +531,17 @@ hipError_t launch_expert_bwd(const Ctx& c, const moe_shape_t& s, const Workspace
   }
   if (s.T > 0) {
     TimedLaunch tl(MOE_K_UNPERMUTE, c.stream);
-    const int grid = s.T < c.num_cus * 16 ? s.T : c.num_cus * 16;
-    hipLaunchKernelGGL(unpermute_sum_f32, dim3(grid), dim3(256), 0, c.stream, dx_rows, slot, s.T, s.k, d, dx);
+    int tb = s.T / (c.num_cus * 8);
+    tb = tb >= 8 ? 8 : tb >= 4 ? 4 : tb >= 2 ? 2 : 1;
+    const int nblk = (s.T + tb - 1) / tb;
+    const int grid = nblk < c.num_cus * 64 ? nblk : c.num_cus * 64;
+#define MOE_UNP(N) \
+  hipLaunchKernelGGL(unpermute_sum_f32<N>, dim3(grid), dim3(256), 0, c.stream, dx_rows, slot, s.T, s.k, d, dx)
+    if (tb == 8) MOE_UNP(8);
+    else if (tb == 4) MOE_UNP(4);
+    else if (tb == 2) MOE_UNP(2);
+    else MOE_UNP(1);
+#undef MOE_UNP
     MOE_TRY(hipGetLastError());
   }
 #undef MOE_TRY
