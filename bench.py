@@ -293,12 +293,22 @@ def backward_pass(w, dev, shape, packed, R, active, reps=5):
     dgu = torch.empty((rmax, 2 * f), dtype=torch.bfloat16, device="cuda")
     dx_rows = torch.empty((rmax, d), device="cuda")
     dx = torch.empty((T, d), device="cuda")
+    # the frozen expert weights' transposes, packed once (outside the step)
+    bwd_packed = None
+    if f % 128 == 0 and d % 128 == 0:
+        bwd_packed = (torch.empty((w.L, f, d), dtype=torch.bfloat16, device="cuda"),
+                      torch.empty((w.L, d, 2 * f), dtype=torch.bfloat16, device="cuda"))
+        B.moe_pack_backward_weights(shape, dev["w_gate"], dev["w_up"], dev["w_down"], *bwd_packed)
 
     def step():
         B.moe_gate_bwd(shape, dev["dy"], buf.y_perm, buf.slot, buf.topk_idx, buf.topk_gate, buf.logits,
                        buf.counts, 0.01, dgate, dlogits)
-        B.moe_expert_bwd(shape, None, dev["dy"], buf.offsets, buf.row_src, buf.row_gate, buf.slot,
-                         buf.act_save, dev["w_gate"], dev["w_up"], dev["w_down"], dgu, dx_rows, dx, buf.ws)
+        if bwd_packed is not None:
+            B.moe_expert_bwd_packed(shape, None, dev["dy"], buf.offsets, buf.row_src, buf.row_gate, buf.slot,
+                                    buf.act_save, bwd_packed[0], bwd_packed[1], dgu, dx_rows, dx, buf.ws)
+        else:
+            B.moe_expert_bwd(shape, None, dev["dy"], buf.offsets, buf.row_src, buf.row_gate, buf.slot,
+                             buf.act_save, dev["w_gate"], dev["w_up"], dev["w_down"], dgu, dx_rows, dx, buf.ws)
         B.moe_router_bwd(shape, dlogits, dev["w_router"], dx, buf.ws)
 
     step()
@@ -338,6 +348,7 @@ def backward_pass(w, dev, shape, packed, R, active, reps=5):
     total = sum(us.values())
     return {"us_per_step": round(total, 2), "tokens_per_s": round(T / (total * 1e-6), 1),
             "kernels_us": {n: round(v, 2) for n, v in us.items()}, "stage_roofline": stages,
+            "packed_weights": bwd_packed is not None,
             "note": "gate + logit gradients (load-balance coef 0.01), dx through experts and router; "
                     "sum of per-kernel event times, outside the timed region"}
 

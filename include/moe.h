@@ -308,6 +308,32 @@ moe_status_t moe_expert_bwd(const moe_shape_t* shape, const moe_lora_t* lora, co
                             const void* w_up, const void* w_down, void* dgu, float* dx_rows, float* dx,
                             void* ws, size_t ws_bytes, moe_stream_t stream);
 
+/* Packed transposed weights for the backward's grouped GEMMs (frozen, so
+ * packed once): the two products contract over the other index of each
+ * weight than the forward does, so their streamed operands are the
+ * transposes, stored in the tile format of moe_pack_expert_weights' down
+ * tiles (128 rows x 32 K values, contiguous 8 KB, chunk c of row r at
+ * position c ^ key(r)):
+ *   dgu_packed [L, f, d] elements: tile (le, b, kt), b < f/128, kt < d/32:
+ *              rows n = 128b..128b+127, K values k = 32kt.., element
+ *              w_down[le][k][n]
+ *   dx_packed  [L, d, 2f] elements: tile (le, b, kt), b < d/128, kt < 2f/32:
+ *              rows n of d, K values k of 2f, element w_gate[le][k][n] for
+ *              k < f and w_up[le][k - f][n] otherwise
+ * bf16 only, d % 128 == 0 and f % 128 == 0. Either output may be NULL. */
+moe_status_t moe_pack_backward_weights(const moe_shape_t* shape, const void* w_gate, const void* w_up,
+                                       const void* w_down, void* dgu_packed, void* dx_packed,
+                                       moe_stream_t stream);
+
+/* moe_expert_bwd with the packed transposed weights: the two grouped GEMMs
+ * stream contiguous weight tiles on the DMA engine of the forward. Same
+ * arguments otherwise; same results up to the fp32 summation order. */
+moe_status_t moe_expert_bwd_packed(const moe_shape_t* shape, const moe_lora_t* lora, const void* dy,
+                                   const int32_t* offsets, const int32_t* row_src, const float* row_gate,
+                                   const int32_t* slot, const void* act_save, const void* dgu_packed,
+                                   const void* dx_packed, void* dgu, float* dx_rows, float* dx, void* ws,
+                                   size_t ws_bytes, moe_stream_t stream);
+
 /* moe_router_bwd: the router's part of dx, dx[t] += sum_e dlogits[t, e]
  * w_router[e] (logits = x w_router^T + bias).
  *   dlogits [T, E] f32 (moe_gate_bwd), w_router [E, d], dx [T, d] f32 IN/OUT.

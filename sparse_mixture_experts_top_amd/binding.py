@@ -28,7 +28,8 @@ KERNELS = ["router_gemm", "topk", "prob_reduce", "hist", "scan", "scatter", "cap
 EXPORTED = ["moe_workspace_bytes", "moe_max_rows", "moe_last_error", "moe_route",
             "moe_dispatch", "moe_expert_gemm", "moe_pack_expert_weights", "moe_expert_gemm_packed",
             "moe_combine", "moe_aux_loss", "moe_lora_bwd", "moe_gate_bwd", "moe_expert_bwd",
-            "moe_router_bwd", "moe_timing_enable", "moe_timing_read"]
+            "moe_router_bwd", "moe_pack_backward_weights", "moe_expert_bwd_packed", "moe_timing_enable",
+            "moe_timing_read"]
 
 
 class MoeShape(ctypes.Structure):
@@ -75,11 +76,14 @@ def lib() -> ctypes.CDLL:
     L.moe_gate_bwd.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp]
     L.moe_expert_bwd.argtypes = [shp, lor, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_router_bwd.argtypes = [shp, vp, vp, vp, vp, sz, vp]
+    L.moe_pack_backward_weights.argtypes = [shp, vp, vp, vp, vp, vp, vp]
+    L.moe_expert_bwd_packed.argtypes = [shp, lor, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_timing_enable.argtypes = [i32]
     L.moe_timing_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     for fn in ("moe_route", "moe_dispatch", "moe_expert_gemm", "moe_pack_expert_weights",
                "moe_expert_gemm_packed", "moe_combine", "moe_aux_loss", "moe_lora_bwd",
-               "moe_gate_bwd", "moe_expert_bwd", "moe_router_bwd",
+               "moe_gate_bwd", "moe_expert_bwd", "moe_router_bwd", "moe_pack_backward_weights",
+               "moe_expert_bwd_packed",
                "moe_timing_enable", "moe_timing_read"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
@@ -218,6 +222,22 @@ def moe_expert_bwd(shape, lora, dy, offsets, row_src, row_gate, slot, act_save, 
                                 _dev(slot, i32), _dev(act_save, dt), _dev(w_gate, dt), _dev(w_up, dt),
                                 _dev(w_down, dt), _dev(dgu, dt), _dev(dx_rows, f32), _dev(dx, f32),
                                 _dev(ws, torch.uint8), ws.numel(), _stream(stream)))
+
+
+def moe_pack_backward_weights(shape, w_gate, w_up, w_down, dgu_packed, dx_packed, stream=None):
+    bf = torch.bfloat16
+    _check(lib().moe_pack_backward_weights(ctypes.byref(shape), _dev(w_gate, bf), _dev(w_up, bf), _dev(w_down, bf),
+                                           _dev(dgu_packed, bf), _dev(dx_packed, bf), _stream(stream)))
+
+
+def moe_expert_bwd_packed(shape, lora, dy, offsets, row_src, row_gate, slot, act_save, dgu_packed, dx_packed,
+                          dgu, dx_rows, dx, ws, stream=None):
+    bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
+    _check(lib().moe_expert_bwd_packed(ctypes.byref(shape), ctypes.byref(lora) if lora is not None else None,
+                                       _dev(dy, bf), _dev(offsets, i32), _dev(row_src, i32), _dev(row_gate, f32),
+                                       _dev(slot, i32), _dev(act_save, bf), _dev(dgu_packed, bf),
+                                       _dev(dx_packed, bf), _dev(dgu, bf), _dev(dx_rows, f32), _dev(dx, f32),
+                                       _dev(ws, torch.uint8), ws.numel(), _stream(stream)))
 
 
 def moe_router_bwd(shape, dlogits, w_router, dx, ws, stream=None):

@@ -475,8 +475,67 @@ moe_status_t moe_expert_bwd(const moe_shape_t* shape, const moe_lora_t* lora, co
     la.b_down = static_cast<const bf16_t*>(lora->b_down);
   }
   return hip_status(launch_expert_bwd(c, s, w, lora ? &la : nullptr, dy, offsets, row_src, row_gate, slot,
-                                      act_save, w_gate, w_up, w_down, dgu, dx_rows, dx),
+                                      act_save, w_gate, w_up, w_down, nullptr, nullptr, dgu, dx_rows, dx),
                     "expert backward");
+}
+
+moe_status_t moe_pack_backward_weights(const moe_shape_t* shape, const void* w_gate, const void* w_up,
+                                       const void* w_down, void* dgu_packed, void* dx_packed,
+                                       moe_stream_t stream) {
+  moe_status_t st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape_t& s = *shape;
+  if ((st = check_packable(s)) != MOE_OK) return st;
+  if (s.f % 128 != 0) return fail(MOE_ERR_UNSUPPORTED, "packed backward weights need f % 128 == 0");
+  if (!dgu_packed && !dx_packed) return fail(MOE_ERR_INVALID_ARG, "no output requested");
+  MOE_REQUIRE_IF(dx_packed, w_gate, "w_gate");
+  MOE_REQUIRE_IF(dx_packed, w_up, "w_up");
+  MOE_REQUIRE_IF(dgu_packed, w_down, "w_down");
+  Ctx c;
+  if ((st = make_ctx(stream, &c)) != MOE_OK) return st;
+  return hip_status(launch_pack_bwd(c, s, w_gate, w_up, w_down, dgu_packed, dx_packed), "pack backward");
+}
+
+moe_status_t moe_expert_bwd_packed(const moe_shape_t* shape, const moe_lora_t* lora, const void* dy,
+                                   const int32_t* offsets, const int32_t* row_src, const float* row_gate,
+                                   const int32_t* slot, const void* act_save, const void* dgu_packed,
+                                   const void* dx_packed, void* dgu, float* dx_rows, float* dx, void* ws,
+                                   size_t ws_bytes, moe_stream_t stream) {
+  moe_status_t st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape_t& s = *shape;
+  if ((st = check_packable(s)) != MOE_OK) return st;
+  if (s.f % 128 != 0) return fail(MOE_ERR_UNSUPPORTED, "packed backward weights need f % 128 == 0");
+  if ((st = check_lora(s, lora)) != MOE_OK) return st;
+  const bool rows = max_rows(s) > 0;
+  MOE_REQUIRE_IF(s.T > 0, dy, "dy");
+  MOE_REQUIRE(offsets, "offsets");
+  MOE_REQUIRE_IF(rows, row_src, "row_src");
+  MOE_REQUIRE_IF(rows, row_gate, "row_gate");
+  MOE_REQUIRE_IF(s.T > 0, slot, "slot");
+  MOE_REQUIRE_IF(rows, act_save, "act_save");
+  MOE_REQUIRE(dgu_packed, "dgu_packed");
+  MOE_REQUIRE(dx_packed, "dx_packed");
+  MOE_REQUIRE_IF(rows, dgu, "dgu");
+  MOE_REQUIRE_IF(rows, dx_rows, "dx_rows");
+  MOE_REQUIRE_IF(s.T > 0, dx, "dx");
+  if ((st = check_ws(s, lora ? lora->r : 0, ws, ws_bytes)) != MOE_OK) return st;
+  Ctx c;
+  if ((st = make_ctx(stream, &c)) != MOE_OK) return st;
+  const Workspace w = carve_workspace(s, lora ? lora->r : 0, ws);
+  LoraArgs la{};
+  if (lora) {
+    la.r = lora->r;
+    la.scale = lora->alpha / (float)lora->r;
+    la.a_up = static_cast<const bf16_t*>(lora->a_up);
+    la.b_up = static_cast<const bf16_t*>(lora->b_up);
+    la.a_down = static_cast<const bf16_t*>(lora->a_down);
+    la.b_down = static_cast<const bf16_t*>(lora->b_down);
+  }
+  return hip_status(launch_expert_bwd(c, s, w, lora ? &la : nullptr, dy, offsets, row_src, row_gate, slot,
+                                      act_save, nullptr, nullptr, nullptr, dgu_packed, dx_packed, dgu, dx_rows,
+                                      dx),
+                    "expert backward (packed)");
 }
 
 moe_status_t moe_router_bwd(const moe_shape_t* shape, const float* dlogits, const void* w_router,

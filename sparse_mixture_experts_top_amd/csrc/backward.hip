@@ -474,8 +474,9 @@ __global__ __launch_bounds__(256) void unpermute_sum_f32(const float* __restrict
 hipError_t launch_expert_bwd(const Ctx& c, const moe_shape_t& s, const Workspace& ws, const LoraArgs* lo,
                              const void* dy, const int32_t* offsets, const int32_t* row_src,
                              const float* row_gate, const int32_t* slot, const void* act_save,
-                             const void* w_gate, const void* w_up, const void* w_down, void* dgu,
-                             float* dx_rows, float* dx) {
+                             const void* w_gate, const void* w_up, const void* w_down,
+                             const void* dgu_packed, const void* dx_packed, void* dgu, float* dx_rows,
+                             float* dx) {
   const int L = s.e_hi - s.e_lo;
   const int d = s.d, f = s.f;
   const int64_t rmax = max_rows(s);
@@ -496,6 +497,10 @@ hipError_t launch_expert_bwd(const Ctx& c, const moe_shape_t& s, const Workspace
                          (const float*)w_gate, (const float*)w_up, d, f, dx_rows);
       MOE_TRY(hipGetLastError());
     }
+  } else if (dgu_packed) {
+    MOE_TRY(launch_bwd_gemms_packed(c, s, ws, lo, (const bf16_t*)dy, row_src, row_gate, offsets,
+                                    (const bf16_t*)act_save, (const bf16_t*)dgu_packed,
+                                    (const bf16_t*)dx_packed, (bf16_t*)dgu, dx_rows));
   } else {
     using Cfg = TileCfg<kGemmBM, 128>;
     const int max_tiles = gemm_max_tiles(s);

@@ -180,8 +180,17 @@ hipError_t launch_gate_bwd(const Ctx& c, const moe_shape_t& s, const void* dy, c
 hipError_t launch_expert_bwd(const Ctx& c, const moe_shape_t& s, const Workspace& ws, const LoraArgs* lo,
                              const void* dy, const int32_t* offsets, const int32_t* row_src,
                              const float* row_gate, const int32_t* slot, const void* act_save,
-                             const void* w_gate, const void* w_up, const void* w_down, void* dgu,
-                             float* dx_rows, float* dx);
+                             const void* w_gate, const void* w_up, const void* w_down,
+                             const void* dgu_packed, const void* dx_packed, void* dgu, float* dx_rows,
+                             float* dx);
+
+hipError_t launch_bwd_gemms_packed(const Ctx& c, const moe_shape_t& s, const Workspace& ws, const LoraArgs* lo,
+                                   const bf16_t* dy, const int32_t* row_src, const float* row_gate,
+                                   const int32_t* offsets, const bf16_t* act_save, const bf16_t* dgu_packed,
+                                   const bf16_t* dx_packed, bf16_t* dgu, float* dx_rows);
+
+hipError_t launch_pack_bwd(const Ctx& c, const moe_shape_t& s, const void* w_gate, const void* w_up,
+                           const void* w_down, void* dgu_packed, void* dx_packed);
 
 hipError_t launch_router_bwd(const Ctx& c, const moe_shape_t& s, const Workspace& ws, const float* dlogits,
                              const void* w_router, float* dx);

@@ -325,6 +325,291 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::WAVES_PER_SIMD) void down_bf16(D
   persistent_gemm_dma<Cfg>(pb, items, pb.f / Cfg::BK);
 }
 
+// ------------------------------------------------- backward on the DMA engine
+// The full backward's two grouped GEMMs contract over the other index of the
+// frozen weights than the forward does (dH = dO W_d contracts over d, dX =
+// [dG dU] [W_g; W_u] over f), so their B operands are the transposed weights,
+// packed once (pack_trans below) into the same tile format as the forward's
+// down weights: W_d^T [L, f, d] for dH, [W_g; W_u]^T [L, d, 2f] for dX.
+
+// dH[row, n] = g_row dY[src_row] . W_d^T[n] (+ s wproj[row] . A_d[:, n]), then
+// dG = dH U silu'(G), dU = dH silu(G) (G, U from act_save) -> dgu bf16.
+template <class Cfg>
+struct DguPackedProb {
+  const bf16_t* dy;
+  const int32_t* row_src;
+  const float* row_gate;
+  const int32_t* offsets;
+  const int32_t* tiles;
+  const bf16_t* packed;  // W_d^T tiles
+  int d, f, nt, L;
+  const float* wproj;
+  const bf16_t* a_down;
+  int r;
+  float scale;
+  const bf16_t* act_save;
+  bf16_t* dgu;
+
+  __device__ __forceinline__ int rows(int item) const {
+    return row_tile<Cfg::BM>(tiles, offsets, item / nt).valid;
+  }
+
+  __device__ __forceinline__ void setup(int item, DmaLoader<Cfg>& ld, int part) const {
+    const RowTile t = row_tile<Cfg::BM>(tiles, offsets, item / nt);
+    const int ni = item % nt;
+    const int ce = dma_chunk_elem<Cfg>();
+#pragma unroll
+    for (int q = 0; q < Cfg::A_DMA / Cfg::DW; ++q) {
+      const int i = q * Cfg::DW + part;
+      ld.a[q] = dy + gathered_row<Cfg>(row_src, t, i, ld_uniform(offsets, L)) * d + ce;
+    }
+    const int nb = f / kPackTileRows, nk = d / Cfg::BK;
+    const int64_t bstride = (int64_t)nk * kPackTileElems;
+#pragma unroll
+    for (int q = 0; q < Cfg::B_DMA / Cfg::DW; ++q) {
+      const int i = q * Cfg::DW + part;
+      const int b = min(ni * (Cfg::BN / kPackTileRows) + i / (kPackTileRows / 16), nb - 1);
+      ld.b[q] = packed_b_ptr(packed + ((int64_t)t.le * nb + b) * bstride, i % (kPackTileRows / 16), 0);
+    }
+    ld.b_kstep = kPackTileElems;
+  }
+
+  __device__ __forceinline__ void epilogue(int item, Acc<Cfg>& acc) const {
+    const RowTile t = row_tile<Cfg::BM>(tiles, offsets, item / nt);
+    const int n0 = (item % nt) * Cfg::BN;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i) {
+      const int base = frag_row0<Cfg>(wm, i);
+      if (base >= t.valid) continue;
+      const int rin = base + (lane & 15);
+      const bool ok = rin < t.valid;
+      const int64_t row = t.row0 + rin;
+      const float g_row = ok ? row_gate[row] : 0.f;
+#pragma unroll
+      for (int j = 0; j < Cfg::FN; ++j) {
+        if (n0 + wn * (Cfg::BN / Cfg::WN) + j * 16 >= f) continue;
+        const int n = n0 + dma_out_col<Cfg>(wn, j, lane);
+        if (!ok) continue;
+        const bf16_t* as = act_save + row * 3 * f + n;
+        const uint2 gv = *reinterpret_cast<const uint2*>(as);
+        const uint2 uv = *reinterpret_cast<const uint2*>(as + 2 * f);
+        const uint32_t gw[2] = {gv.x, gv.y}, uw[2] = {uv.x, uv.y};
+        float dgv[4], duv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float lo = 0.f;
+          if (wproj) {
+            const float* w = wproj + row * r;
+            const bf16_t* ad = a_down + (int64_t)t.le * r * f + n + q;
+            for (int cc = 0; cc < r; ++cc) lo = fmaf(w[cc], bf16_to_f32(ad[(int64_t)cc * f]), lo);
+          }
+          const float dh = fmaf(g_row, acc.v[i][j][q], scale * lo);
+          const float g = bf16_to_f32(static_cast<bf16_t>(gw[q >> 1] >> ((q & 1) * 16)));
+          const float u = bf16_to_f32(static_cast<bf16_t>(uw[q >> 1] >> ((q & 1) * 16)));
+          const float sg = 1.0f / (1.0f + expf(-g));
+          dgv[q] = dh * u * (sg * (1.0f + g * (1.0f - sg)));
+          duv[q] = dh * g * sg;
+        }
+        *reinterpret_cast<uint2*>(dgu + row * 2 * f + n) = pack4_bf16(dgv[0], dgv[1], dgv[2], dgv[3]);
+        *reinterpret_cast<uint2*>(dgu + row * 2 * f + f + n) = pack4_bf16(duv[0], duv[1], duv[2], duv[3]);
+      }
+    }
+  }
+};
+
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::THREADS, Cfg::WAVES_PER_SIMD) void expert_dgu_dma(DguPackedProb<Cfg> pb,
+                                                                                   int max_tiles) {
+  const int items = ld_uniform(pb.tiles, 2 * max_tiles) * pb.nt;
+  persistent_gemm_dma<Cfg>(pb, items, pb.d / Cfg::BK);
+}
+
+// dX[row, n] = dgu[row] . [W_g; W_u]^T[n] (+ s vproj[row] . A_u[:, n]), fp32.
+template <class Cfg>
+struct DxPackedProb {
+  const bf16_t* dgu;
+  const int32_t* offsets;
+  const int32_t* tiles;
+  const bf16_t* packed;  // [W_g; W_u]^T tiles
+  int d, f, nt;
+  const float* vproj;
+  const bf16_t* a_up;
+  int r;
+  float scale;
+  float* dx_rows;
+
+  __device__ __forceinline__ int rows(int item) const {
+    return row_tile<Cfg::BM>(tiles, offsets, item / nt).valid;
+  }
+
+  __device__ __forceinline__ void setup(int item, DmaLoader<Cfg>& ld, int part) const {
+    const RowTile t = row_tile<Cfg::BM>(tiles, offsets, item / nt);
+    const int ni = item % nt;
+    const int ce = dma_chunk_elem<Cfg>();
+#pragma unroll
+    for (int q = 0; q < Cfg::A_DMA / Cfg::DW; ++q)
+      ld.a[q] = dgu + (t.row0 + min(dma_row<Cfg>(q * Cfg::DW + part), t.valid - 1)) * 2 * f + ce;
+    const int nb = d / kPackTileRows, nk = 2 * f / Cfg::BK;
+    const int64_t bstride = (int64_t)nk * kPackTileElems;
+#pragma unroll
+    for (int q = 0; q < Cfg::B_DMA / Cfg::DW; ++q) {
+      const int i = q * Cfg::DW + part;
+      const int b = min(ni * (Cfg::BN / kPackTileRows) + i / (kPackTileRows / 16), nb - 1);
+      ld.b[q] = packed_b_ptr(packed + ((int64_t)t.le * nb + b) * bstride, i % (kPackTileRows / 16), 0);
+    }
+    ld.b_kstep = kPackTileElems;
+  }
+
+  __device__ __forceinline__ void epilogue(int item, Acc<Cfg>& acc) const {
+    const RowTile t = row_tile<Cfg::BM>(tiles, offsets, item / nt);
+    const int n0 = (item % nt) * Cfg::BN;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i) {
+      const int base = frag_row0<Cfg>(wm, i);
+      if (base >= t.valid) continue;
+      const int rin = base + (lane & 15);
+      if (rin >= t.valid) continue;
+      const int64_t row = t.row0 + rin;
+#pragma unroll
+      for (int j = 0; j < Cfg::FN; ++j) {
+        if (n0 + wn * (Cfg::BN / Cfg::WN) + j * 16 >= d) continue;
+        const int n = n0 + dma_out_col<Cfg>(wn, j, lane);
+        float o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          o[q] = acc.v[i][j][q];
+          if (vproj) {
+            const float* w = vproj + row * r;
+            const bf16_t* au = a_up + (int64_t)t.le * r * d + n + q;
+            float lo = 0.f;
+            for (int cc = 0; cc < r; ++cc) lo = fmaf(w[cc], bf16_to_f32(au[(int64_t)cc * d]), lo);
+            o[q] = fmaf(scale, lo, o[q]);
+          }
+        }
+        *reinterpret_cast<float4*>(dx_rows + row * d + n) = make_float4(o[0], o[1], o[2], o[3]);
+      }
+    }
+  }
+};
+
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::THREADS, Cfg::WAVES_PER_SIMD) void expert_dx_dma(DxPackedProb<Cfg> pb,
+                                                                                  int max_tiles) {
+  const int items = ld_uniform(pb.tiles, 2 * max_tiles) * pb.nt;
+  persistent_gemm_dma<Cfg>(pb, items, 2 * pb.f / Cfg::BK);
+}
+
+template <class Cfg>
+static hipError_t launch_bwd_gemms_cfg(const Ctx& c, const moe_shape_t& s, const Workspace& ws,
+                                       const LoraArgs* lo, const bf16_t* dy, const int32_t* row_src,
+                                       const float* row_gate, const int32_t* offsets, const bf16_t* act_save,
+                                       const bf16_t* dgu_packed, const bf16_t* dx_packed, bf16_t* dgu,
+                                       float* dx_rows, int max_tiles) {
+  const int L = s.e_hi - s.e_lo;
+  const int64_t rmax = max_rows(s);
+  hipError_t err;
+  if (lo) {
+    err = launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, dy, s.d, row_src, row_gate, s.d, lo->b_down, false,
+                                      lo->r, ws.wproj);
+    if (err != hipSuccess) return err;
+  }
+  {
+    DguPackedProb<Cfg> pb{dy, row_src, row_gate, offsets, ws.gemm_tiles, dgu_packed, s.d, s.f,
+                          (s.f + Cfg::BN - 1) / Cfg::BN, L, lo ? ws.wproj : nullptr, lo ? lo->a_down : nullptr,
+                          lo ? lo->r : 0, lo ? lo->scale : 0.f, act_save, dgu};
+    TimedLaunch tl(MOE_K_EXPERT_DGU, c.stream);
+    hipLaunchKernelGGL(expert_dgu_dma<Cfg>, dim3(c.num_cus), dim3(Cfg::THREADS), 0, c.stream, pb, max_tiles);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  if (lo) {
+    err = launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, dgu + s.f, 2 * s.f, nullptr, nullptr, s.f, lo->b_up,
+                                      false, lo->r, ws.vproj);
+    if (err != hipSuccess) return err;
+  }
+  DxPackedProb<Cfg> pb{dgu, offsets, ws.gemm_tiles, dx_packed, s.d, s.f, (s.d + Cfg::BN - 1) / Cfg::BN,
+                       lo ? ws.vproj : nullptr, lo ? lo->a_up : nullptr, lo ? lo->r : 0, lo ? lo->scale : 0.f,
+                       dx_rows};
+  TimedLaunch tl(MOE_K_EXPERT_DX, c.stream);
+  hipLaunchKernelGGL(expert_dx_dma<Cfg>, dim3(c.num_cus), dim3(Cfg::THREADS), 0, c.stream, pb, max_tiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_gemms_packed(const Ctx& c, const moe_shape_t& s, const Workspace& ws, const LoraArgs* lo,
+                                   const bf16_t* dy, const int32_t* row_src, const float* row_gate,
+                                   const int32_t* offsets, const bf16_t* act_save, const bf16_t* dgu_packed,
+                                   const bf16_t* dx_packed, bf16_t* dgu, float* dx_rows) {
+  const int L = s.e_hi - s.e_lo;
+  const int max_tiles = gemm_max_tiles(s);
+  hipError_t err = launch_row_tiles(c, offsets, L, max_tiles, ws.gemm_tiles);
+  if (err != hipSuccess) return err;
+  int64_t per_expert = (int64_t)s.T * s.k / s.E;
+  if (s.capacity > 0 && per_expert > s.capacity) per_expert = s.capacity;
+  if (per_expert >= kWideRowsPerExpert)
+    return launch_bwd_gemms_cfg<GemmCfgWide>(c, s, ws, lo, dy, row_src, row_gate, offsets, act_save, dgu_packed,
+                                             dx_packed, dgu, dx_rows, max_tiles);
+  return launch_bwd_gemms_cfg<GemmCfg>(c, s, ws, lo, dy, row_src, row_gate, offsets, act_save, dgu_packed,
+                                       dx_packed, dgu, dx_rows, max_tiles);
+}
+
+// Transposing pack: tile (le, n block of 128 rows, K step) of the matrix
+// B[le][n][k] = (k < k_split ? src0 : src1)[le][k mod k_split][n] (row stride
+// ld_k between consecutive k), laid out like pack_down's tiles.
+__global__ __launch_bounds__(256) void pack_trans(const bf16_t* __restrict__ src0, const bf16_t* __restrict__ src1,
+                                                  int k_split, int L, int rows, int K, int64_t ld_k,
+                                                  int64_t le_stride, u32x4* __restrict__ out) {
+  const int nk = K / 32, nt = rows / 128;
+  const int64_t total = (int64_t)L * nt * nk * 512;
+  for (int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; id < total;
+       id += (int64_t)gridDim.x * blockDim.x) {
+    const int slot = (int)(id & 3), jb = (int)((id >> 2) & 127);
+    const int64_t tile = id >> 9;
+    const int kt = (int)(tile % nk);
+    const int64_t rest = tile / nk;
+    const int ni = (int)(rest % nt), le = (int)(rest / nt);
+    const int c = slot ^ chunk_key(jb);
+    const int n = ni * 128 + jb;
+    uint32_t w[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      uint32_t pair = 0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int k = kt * 32 + c * 8 + 2 * u + h;
+        const bf16_t* src = k < k_split ? src0 : src1;
+        const int kk = k < k_split ? k : k - k_split;
+        const uint32_t v = static_cast<uint32_t>(src[(int64_t)le * le_stride + (int64_t)kk * ld_k + n]);
+        pair |= v << (16 * h);
+      }
+      w[u] = pair;
+    }
+    out[id] = u32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+
+hipError_t launch_pack_bwd(const Ctx& c, const moe_shape_t& s, const void* w_gate, const void* w_up,
+                           const void* w_down, void* dgu_packed, void* dx_packed) {
+  const int L = s.e_hi - s.e_lo;
+  const int grid = c.num_cus * 8;
+  if (dgu_packed) {
+    // W_d^T: rows n < f, K = d, element (n, k) = w_down[le][k][n]
+    hipLaunchKernelGGL(pack_trans, dim3(grid), dim3(256), 0, c.stream, (const bf16_t*)w_down,
+                       (const bf16_t*)w_down, s.d, L, s.f, s.d, (int64_t)s.f, (int64_t)s.d * s.f,
+                       (u32x4*)dgu_packed);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (dx_packed)
+    // [W_g; W_u]^T: rows n < d, K = 2f, element (n, k) = w_gate / w_up[le][k][n]
+    hipLaunchKernelGGL(pack_trans, dim3(grid), dim3(256), 0, c.stream, (const bf16_t*)w_gate,
+                       (const bf16_t*)w_up, s.f, L, s.d, 2 * s.f, (int64_t)s.d, (int64_t)s.f * s.d,
+                       (u32x4*)dx_packed);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------ packing ---
 //
 // Frozen weights rearranged once so that every weight tile the grouped GEMMs

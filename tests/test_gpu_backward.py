@@ -45,7 +45,14 @@ def dot_bound(a, b):
     return g * np.sum(np.abs(a * b), axis=-1)
 
 
-def run_backward(w, dev, buf):
+def pack_backward(w, dev):
+    dgu_p = torch.empty((w.L, w.f, w.d), dtype=torch.bfloat16, device="cuda")
+    dx_p = torch.empty((w.L, w.d, 2 * w.f), dtype=torch.bfloat16, device="cuda")
+    B.moe_pack_backward_weights(layer.shape_of(w), dev["w_gate"], dev["w_up"], dev["w_down"], dgu_p, dx_p)
+    return dgu_p, dx_p
+
+
+def run_backward(w, dev, buf, packed=False):
     s = buf.shape
     T, d, E, k, f = w.T, w.d, w.E, w.k, w.f
     rmax = max(B.moe_max_rows(s), 1)
@@ -59,9 +66,14 @@ def run_backward(w, dev, buf):
     }
     B.moe_gate_bwd(s, dev["dy"], buf.y_perm, buf.slot, buf.topk_idx, buf.topk_gate, buf.logits, buf.counts,
                    AUX, out["dgate"], out["dlogits"])
-    B.moe_expert_bwd(s, lora_of(w, dev), dev["dy"], buf.offsets, buf.row_src, buf.row_gate, buf.slot,
-                     buf.act_save, dev["w_gate"], dev["w_up"], dev["w_down"], out["dgu"], out["dx_rows"],
-                     out["dx"], buf.ws)
+    if packed:
+        dgu_p, dx_p = pack_backward(w, dev)
+        B.moe_expert_bwd_packed(s, lora_of(w, dev), dev["dy"], buf.offsets, buf.row_src, buf.row_gate, buf.slot,
+                                buf.act_save, dgu_p, dx_p, out["dgu"], out["dx_rows"], out["dx"], buf.ws)
+    else:
+        B.moe_expert_bwd(s, lora_of(w, dev), dev["dy"], buf.offsets, buf.row_src, buf.row_gate, buf.slot,
+                         buf.act_save, dev["w_gate"], dev["w_up"], dev["w_down"], out["dgu"], out["dx_rows"],
+                         out["dx"], buf.ws)
     torch.cuda.synchronize()
     out["dx_experts"] = out["dx"].clone()
     out["dx_router"] = torch.zeros((T, d), device="cuda")
@@ -73,15 +85,18 @@ def run_backward(w, dev, buf):
     return out
 
 
-@pytest.mark.parametrize("name", sorted(CASES))
-def test_backward_stagewise(name):
+PACKABLE = [n for n, w in CASES.items() if w.dtype == "bf16" and w.d % 128 == 0 and w.f % 128 == 0]
+
+
+@pytest.mark.parametrize("name,packed", [(n, False) for n in sorted(CASES)] + [(n, True) for n in PACKABLE])
+def test_backward_stagewise(name, packed):
     w = CASES[name]
     say(f"[backward {name}] T={w.T} d={w.d} E={w.E} k={w.k} f={w.f} local=[{w.e_lo},{w.local_hi}) "
-        f"cap={w.capacity} lora={w.lora_r} dtype={w.dtype}")
+        f"cap={w.capacity} lora={w.lora_r} dtype={w.dtype} packed={packed}")
     inp = generate(w, seed=3)
     dev = upload(inp)
     buf = run_forward(w, dev, prob=True, act_save=True, x_perm=False)
-    g = run_backward(w, dev, buf)
+    g = run_backward(w, dev, buf, packed=packed)
     T = w.T
     R = int(host(buf.offsets)[-1])
     dy = to_f64(inp["dy"])
@@ -144,14 +159,14 @@ def test_backward_empty_and_no_local():
 @pytest.mark.parametrize("name", ["full_router", "ep64_rank"])
 def test_backward_full_size_sampled(name):
     """Full size, in the launch configuration of the benchmark's backward
-    pass; the oracle checks sampled tokens (their gate and logit gradients,
+    pass (packed transposed weights); the oracle checks sampled tokens (their gate and logit gradients,
     their dx summed from their rows, and the router part)."""
     w = WORKLOADS[name]
     say(f"[backward full {name}]")
     inp = generate(w, seed=0)
     dev = upload(inp)
     buf = run_forward(w, dev, prob=True, act_save=True, x_perm=False, packed=True)
-    g = run_backward(w, dev, buf)
+    g = run_backward(w, dev, buf, packed=True)
     rng = np.random.default_rng(5)
     slot_all = host(buf.slot).astype(np.int64)
     local = np.nonzero((slot_all >= 0).any(axis=1))[0]
