@@ -300,6 +300,11 @@ def backward_pass(w, dev, shape, packed, R, active, reps=5):
                       torch.empty((w.L, d, 2 * f), dtype=torch.bfloat16, device="cuda"))
         B.moe_pack_backward_weights(shape, dev["w_gate"], dev["w_up"], dev["w_down"], *bwd_packed)
 
+    wr_packed = None
+    if E % 64 == 0 and d % 128 == 0:
+        wr_packed = torch.empty((d, E), dtype=torch.bfloat16, device="cuda")
+        B.moe_pack_router_bwd(shape, dev["w_router"], wr_packed)
+
     def step():
         B.moe_gate_bwd(shape, dev["dy"], buf.y_perm, buf.slot, buf.topk_idx, buf.topk_gate, buf.logits,
                        buf.counts, 0.01, dgate, dlogits)
@@ -309,7 +314,10 @@ def backward_pass(w, dev, shape, packed, R, active, reps=5):
         else:
             B.moe_expert_bwd(shape, None, dev["dy"], buf.offsets, buf.row_src, buf.row_gate, buf.slot,
                              buf.act_save, dev["w_gate"], dev["w_up"], dev["w_down"], dgu, dx_rows, dx, buf.ws)
-        B.moe_router_bwd(shape, dlogits, dev["w_router"], dx, buf.ws)
+        if wr_packed is not None:
+            B.moe_router_bwd_packed(shape, dlogits, wr_packed, dx, buf.ws)
+        else:
+            B.moe_router_bwd(shape, dlogits, dev["w_router"], dx, buf.ws)
 
     step()
     torch.cuda.synchronize()

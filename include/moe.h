@@ -343,6 +343,19 @@ moe_status_t moe_expert_bwd_packed(const moe_shape_t* shape, const moe_lora_t* l
 moe_status_t moe_router_bwd(const moe_shape_t* shape, const float* dlogits, const void* w_router,
                             float* dx, void* ws, size_t ws_bytes, moe_stream_t stream);
 
+/* The router's transpose packed once for moe_router_bwd_packed (the router
+ * is frozen): wr_packed [d, E] elements in the tile format of the packed
+ * expert weights, rows n < d, K values e < E, element w_router[e][n].
+ * bf16 only, d % 128 == 0, E % 64 == 0. */
+moe_status_t moe_pack_router_bwd(const moe_shape_t* shape, const void* w_router, void* wr_packed,
+                                 moe_stream_t stream);
+
+/* moe_router_bwd with the packed transpose: dx[t] += sum_e dlogits[t, e]
+ * w_router[e] on the DMA engine (dlogits rounded to bf16 in the workspace,
+ * fp32 accumulation). */
+moe_status_t moe_router_bwd_packed(const moe_shape_t* shape, const float* dlogits, const void* wr_packed,
+                                   float* dx, void* ws, size_t ws_bytes, moe_stream_t stream);
+
 /* ---- kernel timing (profiling aid) -------------------------------------
  * When enabled for a kernel kind, the library records a pair of HIP events
  * on the launch stream around every kernel of that kind it enqueues.

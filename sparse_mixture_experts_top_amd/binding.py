@@ -28,8 +28,8 @@ KERNELS = ["router_gemm", "topk", "prob_reduce", "hist", "scan", "scatter", "cap
 EXPORTED = ["moe_workspace_bytes", "moe_max_rows", "moe_last_error", "moe_route",
             "moe_dispatch", "moe_expert_gemm", "moe_pack_expert_weights", "moe_expert_gemm_packed",
             "moe_combine", "moe_aux_loss", "moe_lora_bwd", "moe_gate_bwd", "moe_expert_bwd",
-            "moe_router_bwd", "moe_pack_backward_weights", "moe_expert_bwd_packed", "moe_timing_enable",
-            "moe_timing_read"]
+            "moe_router_bwd", "moe_pack_backward_weights", "moe_expert_bwd_packed", "moe_pack_router_bwd",
+            "moe_router_bwd_packed", "moe_timing_enable", "moe_timing_read"]
 
 
 class MoeShape(ctypes.Structure):
@@ -77,13 +77,15 @@ def lib() -> ctypes.CDLL:
     L.moe_expert_bwd.argtypes = [shp, lor, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_router_bwd.argtypes = [shp, vp, vp, vp, vp, sz, vp]
     L.moe_pack_backward_weights.argtypes = [shp, vp, vp, vp, vp, vp, vp]
+    L.moe_pack_router_bwd.argtypes = [shp, vp, vp, vp]
+    L.moe_router_bwd_packed.argtypes = [shp, vp, vp, vp, vp, sz, vp]
     L.moe_expert_bwd_packed.argtypes = [shp, lor, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_timing_enable.argtypes = [i32]
     L.moe_timing_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     for fn in ("moe_route", "moe_dispatch", "moe_expert_gemm", "moe_pack_expert_weights",
                "moe_expert_gemm_packed", "moe_combine", "moe_aux_loss", "moe_lora_bwd",
                "moe_gate_bwd", "moe_expert_bwd", "moe_router_bwd", "moe_pack_backward_weights",
-               "moe_expert_bwd_packed",
+               "moe_expert_bwd_packed", "moe_pack_router_bwd", "moe_router_bwd_packed",
                "moe_timing_enable", "moe_timing_read"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
@@ -237,6 +239,17 @@ def moe_expert_bwd_packed(shape, lora, dy, offsets, row_src, row_gate, slot, act
                                        _dev(dy, bf), _dev(offsets, i32), _dev(row_src, i32), _dev(row_gate, f32),
                                        _dev(slot, i32), _dev(act_save, bf), _dev(dgu_packed, bf),
                                        _dev(dx_packed, bf), _dev(dgu, bf), _dev(dx_rows, f32), _dev(dx, f32),
+                                       _dev(ws, torch.uint8), ws.numel(), _stream(stream)))
+
+
+def moe_pack_router_bwd(shape, w_router, wr_packed, stream=None):
+    bf = torch.bfloat16
+    _check(lib().moe_pack_router_bwd(ctypes.byref(shape), _dev(w_router, bf), _dev(wr_packed, bf), _stream(stream)))
+
+
+def moe_router_bwd_packed(shape, dlogits, wr_packed, dx, ws, stream=None):
+    _check(lib().moe_router_bwd_packed(ctypes.byref(shape), _dev(dlogits, torch.float32),
+                                       _dev(wr_packed, torch.bfloat16), _dev(dx, torch.float32),
                                        _dev(ws, torch.uint8), ws.numel(), _stream(stream)))
 
 

@@ -550,7 +550,38 @@ moe_status_t moe_router_bwd(const moe_shape_t* shape, const float* dlogits, cons
   Ctx c;
   if ((st = make_ctx(stream, &c)) != MOE_OK) return st;
   const Workspace w = carve_workspace(s, 0, ws);
-  return hip_status(launch_router_bwd(c, s, w, dlogits, w_router, dx), "router backward");
+  return hip_status(launch_router_bwd(c, s, w, dlogits, w_router, nullptr, dx), "router backward");
+}
+
+moe_status_t moe_pack_router_bwd(const moe_shape_t* shape, const void* w_router, void* wr_packed,
+                                 moe_stream_t stream) {
+  moe_status_t st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape_t& s = *shape;
+  if (s.dtype != MOE_BF16 || s.d % 128 != 0 || s.E % 64 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "packed router weights need bf16, d % 128 == 0 and E % 64 == 0");
+  MOE_REQUIRE(w_router, "w_router");
+  MOE_REQUIRE(wr_packed, "wr_packed");
+  Ctx c;
+  if ((st = make_ctx(stream, &c)) != MOE_OK) return st;
+  return hip_status(launch_pack_router_bwd(c, s, w_router, wr_packed), "pack router");
+}
+
+moe_status_t moe_router_bwd_packed(const moe_shape_t* shape, const float* dlogits, const void* wr_packed,
+                                   float* dx, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  moe_status_t st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape_t& s = *shape;
+  if (s.dtype != MOE_BF16 || s.d % 128 != 0 || s.E % 64 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "packed router weights need bf16, d % 128 == 0 and E % 64 == 0");
+  MOE_REQUIRE_IF(s.T > 0, dlogits, "dlogits");
+  MOE_REQUIRE(wr_packed, "wr_packed");
+  MOE_REQUIRE_IF(s.T > 0, dx, "dx");
+  if ((st = check_ws(s, 0, ws, ws_bytes)) != MOE_OK) return st;
+  Ctx c;
+  if ((st = make_ctx(stream, &c)) != MOE_OK) return st;
+  const Workspace w = carve_workspace(s, 0, ws);
+  return hip_status(launch_router_bwd(c, s, w, dlogits, nullptr, wr_packed, dx), "router backward (packed)");
 }
 
 moe_status_t moe_timing_enable(int32_t mask) {

@@ -626,7 +626,7 @@ __global__ __launch_bounds__(256) void router_bwd_simple(const float* __restrict
 }
 
 hipError_t launch_router_bwd(const Ctx& c, const moe_shape_t& s, const Workspace& ws, const float* dlogits,
-                             const void* w_router, float* dx) {
+                             const void* w_router, const void* wr_packed, float* dx) {
   if (s.T == 0) return hipSuccess;
   TimedLaunch tl(MOE_K_ROUTER_BWD, c.stream);
   if (s.dtype == MOE_BF16 && s.E % 64 == 0) {
@@ -637,6 +637,7 @@ hipError_t launch_router_bwd(const Ctx& c, const moe_shape_t& s, const Workspace
     hipLaunchKernelGGL(to_bf16_rows, dim3(cgrid), dim3(256), 0, c.stream, dlogits, n, dlb);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
+    if (wr_packed) return launch_router_bwd_packed(c, s, dlb, (const bf16_t*)wr_packed, dx);
     const int nt = (s.d + Cfg::BN - 1) / Cfg::BN;
     const int items = ((s.T + Cfg::BM - 1) / Cfg::BM) * nt;
     const int grid = std::min(((items + 7) / 8) * 8, c.num_cus * 2);

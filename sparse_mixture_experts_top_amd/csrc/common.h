@@ -192,8 +192,12 @@ hipError_t launch_bwd_gemms_packed(const Ctx& c, const moe_shape_t& s, const Wor
 hipError_t launch_pack_bwd(const Ctx& c, const moe_shape_t& s, const void* w_gate, const void* w_up,
                            const void* w_down, void* dgu_packed, void* dx_packed);
 
+hipError_t launch_pack_router_bwd(const Ctx& c, const moe_shape_t& s, const void* w_router, void* wr_packed);
+hipError_t launch_router_bwd_packed(const Ctx& c, const moe_shape_t& s, const bf16_t* dl, const bf16_t* wr_packed,
+                                    float* dx);
+
 hipError_t launch_router_bwd(const Ctx& c, const moe_shape_t& s, const Workspace& ws, const float* dlogits,
-                             const void* w_router, float* dx);
+                             const void* w_router, const void* wr_packed, float* dx);
 
 // LoRA building blocks shared by the forward (expert_gemm) and the backward.
 // out[p, q] = scale_p * sum_i in[src(p), i] * M(le(p), q, i) for rows p < R.

@@ -590,6 +590,83 @@ __global__ __launch_bounds__(256) void pack_trans(const bf16_t* __restrict__ src
   }
 }
 
+// Router part of dx on the DMA engine: dx[t, n] += dl_bf16[t] . W_r^T[n]
+// (W_r^T packed like the expert tiles, rows n < d, K = E), dense items of
+// 128 tokens x BN columns; the epilogue adds into the fp32 dx.
+template <class Cfg>
+struct RouterBwdPackedProb {
+  const bf16_t* dl;      // [T, E] bf16
+  const bf16_t* packed;  // W_r^T tiles
+  int T, E, d, nt;
+  float* dx;
+
+  __device__ __forceinline__ int rows(int item) const { return min(Cfg::BM, T - (item / nt) * Cfg::BM); }
+
+  __device__ __forceinline__ void setup(int item, DmaLoader<Cfg>& ld, int part) const {
+    const int m0 = (item / nt) * Cfg::BM, ni = item % nt;
+    const int ce = dma_chunk_elem<Cfg>();
+#pragma unroll
+    for (int q = 0; q < Cfg::A_DMA / Cfg::DW; ++q)
+      ld.a[q] = dl + (int64_t)min(m0 + dma_row<Cfg>(q * Cfg::DW + part), T - 1) * E + ce;
+    const int nb = d / kPackTileRows, nk = E / Cfg::BK;
+    const int64_t bstride = (int64_t)nk * kPackTileElems;
+#pragma unroll
+    for (int q = 0; q < Cfg::B_DMA / Cfg::DW; ++q) {
+      const int i = q * Cfg::DW + part;
+      const int b = min(ni * (Cfg::BN / kPackTileRows) + i / (kPackTileRows / 16), nb - 1);
+      ld.b[q] = packed_b_ptr(packed + (int64_t)b * bstride, i % (kPackTileRows / 16), 0);
+    }
+    ld.b_kstep = kPackTileElems;
+  }
+
+  __device__ __forceinline__ void epilogue(int item, Acc<Cfg>& acc) const {
+    const int m0 = (item / nt) * Cfg::BM, n0 = (item % nt) * Cfg::BN;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i) {
+      const int m = m0 + dma_out_row<Cfg>(wm, i, lane);
+      if (m0 + frag_row0<Cfg>(wm, i) >= T || m >= T) continue;
+#pragma unroll
+      for (int j = 0; j < Cfg::FN; ++j) {
+        if (n0 + wn * (Cfg::BN / Cfg::WN) + j * 16 >= d) continue;
+        const int n = n0 + dma_out_col<Cfg>(wn, j, lane);
+        float4* p = reinterpret_cast<float4*>(dx + (int64_t)m * d + n);
+        float4 v = *p;
+        v.x += acc.v[i][j][0];
+        v.y += acc.v[i][j][1];
+        v.z += acc.v[i][j][2];
+        v.w += acc.v[i][j][3];
+        *p = v;
+      }
+    }
+  }
+};
+
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::THREADS, Cfg::WAVES_PER_SIMD) void router_bwd_dma(RouterBwdPackedProb<Cfg> pb,
+                                                                                   int items) {
+  persistent_gemm_dma<Cfg>(pb, items, pb.E / Cfg::BK);
+}
+
+hipError_t launch_router_bwd_packed(const Ctx& c, const moe_shape_t& s, const bf16_t* dl, const bf16_t* wr_packed,
+                                    float* dx) {
+  using Cfg = GemmCfgWide;
+  const int nt = (s.d + Cfg::BN - 1) / Cfg::BN;
+  const int items = ((s.T + Cfg::BM - 1) / Cfg::BM) * nt;
+  const int grid = std::min(((items + 7) / 8) * 8, c.num_cus);
+  RouterBwdPackedProb<Cfg> pb{dl, wr_packed, s.T, s.E, s.d, nt, dx};
+  hipLaunchKernelGGL(router_bwd_dma<Cfg>, dim3(grid), dim3(Cfg::THREADS), 0, c.stream, pb, items);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_router_bwd(const Ctx& c, const moe_shape_t& s, const void* w_router, void* wr_packed) {
+  // W_r^T: rows n < d, K = E, element (n, e) = w_router[e][n]
+  hipLaunchKernelGGL(pack_trans, dim3(c.num_cus * 8), dim3(256), 0, c.stream, (const bf16_t*)w_router,
+                     (const bf16_t*)w_router, s.E, 1, s.d, s.E, (int64_t)s.d, (int64_t)0, (u32x4*)wr_packed);
+  return hipGetLastError();
+}
+
 hipError_t launch_pack_bwd(const Ctx& c, const moe_shape_t& s, const void* w_gate, const void* w_up,
                            const void* w_down, void* dgu_packed, void* dx_packed) {
   const int L = s.e_hi - s.e_lo;

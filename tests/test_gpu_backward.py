@@ -26,6 +26,8 @@ CASES = {
     "k1_bf16": W("k1_bf16", T=257, d=128, E=16, k=1, f=128),
     # E % 64 == 0: the router part runs on the matrix cores; two K steps of 64
     "router128_bf16": W("router128_bf16", T=333, d=320, E=128, k=4, f=64),
+    # packable for every backward product (d, f % 128 == 0, E % 64 == 0)
+    "router128p_bf16": W("router128p_bf16", T=333, d=256, E=128, k=4, f=128),
     "lora_bf16": W("lora_bf16", T=256, d=128, E=12, k=4, f=128, e_lo=2, e_hi=9, lora_r=16,
                    lora_alpha=32.0, lora_b="normal"),
 }
@@ -77,8 +79,14 @@ def run_backward(w, dev, buf, packed=False):
     torch.cuda.synchronize()
     out["dx_experts"] = out["dx"].clone()
     out["dx_router"] = torch.zeros((T, d), device="cuda")
-    B.moe_router_bwd(s, out["dlogits"], dev["w_router"], out["dx_router"], buf.ws)
-    B.moe_router_bwd(s, out["dlogits"], dev["w_router"], out["dx"], buf.ws)  # accumulates
+    if packed and E % 64 == 0 and d % 128 == 0:
+        wr_p = torch.empty((d, E), dtype=torch.bfloat16, device="cuda")
+        B.moe_pack_router_bwd(s, dev["w_router"], wr_p)
+        B.moe_router_bwd_packed(s, out["dlogits"], wr_p, out["dx_router"], buf.ws)
+        B.moe_router_bwd_packed(s, out["dlogits"], wr_p, out["dx"], buf.ws)  # accumulates
+    else:
+        B.moe_router_bwd(s, out["dlogits"], dev["w_router"], out["dx_router"], buf.ws)
+        B.moe_router_bwd(s, out["dlogits"], dev["w_router"], out["dx"], buf.ws)  # accumulates
     torch.cuda.synchronize()
     # same products, so the accumulated result is exactly one fp32 addition
     assert torch.equal(out["dx"], out["dx_experts"] + out["dx_router"])
