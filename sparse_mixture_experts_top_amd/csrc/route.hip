@@ -296,14 +296,28 @@ __global__ __launch_bounds__(256) void topk_softmax(const float* __restrict__ lo
     prob_part[(int64_t)blockIdx.x * E + e] = ((red[0][e] + red[1][e]) + red[2][e]) + red[3][e];
 }
 
-// prob_sum[e] = sum over blocks of prob_part[b, e], blocks in order.
-__global__ __launch_bounds__(256) void prob_reduce(const float* __restrict__ part, int nblk, int E,
-                                                   float* __restrict__ out) {
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= E) return;
+// prob_sum[e] = sum over blocks of prob_part[b, e]. Workgroup (e-group of
+// 64 experts, 16 waves): lane l of wave w sums blocks w, w + 16, ... of
+// expert 64 g + l in order, then the waves' partials are added in wave order
+// - a fixed order, so the result does not depend on scheduling.
+__global__ __launch_bounds__(1024) void prob_reduce(const float* __restrict__ part, int nblk, int E,
+                                                    float* __restrict__ out) {
+  __shared__ float red[16][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int e = blockIdx.x * 64 + lane;
   float acc = 0.f;
-  for (int b = 0; b < nblk; ++b) acc += part[(int64_t)b * E + e];
-  out[e] = acc;
+  if (e < E) {
+#pragma unroll 8
+    for (int b = wave; b < nblk; b += 16) acc += part[(int64_t)b * E + e];
+  }
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0 && e < E) {
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) sum += red[w][lane];
+    out[e] = sum;
+  }
 }
 
 hipError_t launch_topk(const Ctx& c, const moe_shape_t& s, const float* logits, int32_t* idx,
@@ -334,8 +348,7 @@ hipError_t launch_topk(const Ctx& c, const moe_shape_t& s, const float* logits, 
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || !prob_sum) return err;
   TimedLaunch tl(MOE_K_PROB_REDUCE, c.stream);
-  hipLaunchKernelGGL(prob_reduce, dim3((s.E + 255) / 256), dim3(256), 0, c.stream, part, nblk, s.E,
-                     prob_sum);
+  hipLaunchKernelGGL(prob_reduce, dim3((s.E + 63) / 64), dim3(1024), 0, c.stream, part, nblk, s.E, prob_sum);
   return hipGetLastError();
 }
 
