@@ -10,8 +10,9 @@
 // guide: y = sum_i g_i E_i(x) with the auxiliary load-balance loss.
 //
 //   gate_bwd   one wave per token: dg_j = <dY_t, O[slot_tj]> for kept local
-//              slots; the softmax-over-the-selection Jacobian
-//              dl_{idx_j} = g_j (dg_j - sum_i g_i dg_i); with counts, the
+//              slots (8 rows' loads in flight per chunk); the softmax-over-
+//              the-selection Jacobian dl_{idx_j} = g_j (dg_j - sum_i g_i dg_i);
+//              with counts, the
 //              load-balance term coef E / T * p_te (f_e - sum_e' f_e' p_te')
 //              (p = softmax over all E, f = counts / (T k), held constant)
 //   dgu        grouped GEMM, per (row tile, 128 FFN columns): dH = g_p dY[src_p]
@@ -53,9 +54,12 @@ __device__ __forceinline__ void load8f<float>(const float* p, float (&v)[8]) {
 
 // ------------------------------------------------------------ gate bwd ---
 // One wave per token (4 per workgroup). Lane j < k holds slot, gate and
-// selected expert of assignment j; the dot products run 4 assignments at a
+// selected expert of assignment j; the dot products run 8 assignments at a
 // time over 8-element chunks of the row (d % 8 == 0), lanes striding the
-// chunks; lane l holds logits l, l + 64, ... (EPL of them).
+// chunks, and a group whose slots are all empty (dropped or not local) is
+// skipped; lane l holds logits l, l + 64, ... (EPL of them). The
+// load-balance fractions counts[e] / (T k) are staged once per workgroup in
+// LDS.
 template <class T, int EPL>
 __global__ __launch_bounds__(256) void gate_bwd(const T* __restrict__ dy, const T* __restrict__ y_perm,
                                                 const int32_t* __restrict__ slot,
@@ -65,7 +69,13 @@ __global__ __launch_bounds__(256) void gate_bwd(const T* __restrict__ dy, const 
                                                 const int32_t* __restrict__ counts, float aux_scale,
                                                 float inv_tk, int Tn, int d, int E, int k,
                                                 float* __restrict__ dgate, float* __restrict__ dlogits) {
+  constexpr int G = 8;  // assignments per group of row loads
+  __shared__ float s_fr[EPL * 64];
   const int lane = threadIdx.x & 63;
+  if (counts) {
+    for (int e = threadIdx.x; e < EPL * 64; e += 256) s_fr[e] = e < E ? (float)counts[e] * inv_tk : 0.f;
+    __syncthreads();
+  }
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= Tn) return;
   const int my_slot = lane < k ? slot[(int64_t)t * k + lane] : -1;
@@ -73,18 +83,24 @@ __global__ __launch_bounds__(256) void gate_bwd(const T* __restrict__ dy, const 
   const int my_e = lane < k ? idx[(int64_t)t * k + lane] : 0;
   const T* dyr = dy + (int64_t)t * d;
   float my_dg = 0.f;
-  for (int j0 = 0; j0 < k; j0 += 4) {
-    int s[4];
+  for (int j0 = 0; j0 < k; j0 += G) {
+    int s[G];
+    bool any = false;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) s[q] = __shfl(j0 + q < k ? my_slot : -1, j0 + q < k ? j0 + q : 0, kWave);
+    for (int q = 0; q < G; ++q) {
+      s[q] = __shfl(my_slot, j0 + q < k ? j0 + q : 0, kWave);
+      s[q] = j0 + q < k ? s[q] : -1;
+      any = any || s[q] >= 0;
+    }
+    if (!any) continue;  // wave-uniform
+    float acc[G];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) s[q] = j0 + q < k ? s[q] : -1;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < G; ++q) acc[q] = 0.f;
     for (int i0 = lane * 8; i0 < d; i0 += 64 * 8) {
       float a[8];
       load8f<T>(dyr + i0, a);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < G; ++q) {
         if (s[q] < 0) continue;
         float o[8];
         load8f<T>(y_perm + (int64_t)s[q] * d + i0, o);
@@ -93,7 +109,8 @@ __global__ __launch_bounds__(256) void gate_bwd(const T* __restrict__ dy, const 
       }
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < G; ++q) {
+      if (s[q] < 0) continue;  // wave-uniform; its dg stays 0
       const float v = wave_sum(acc[q]);
       if (lane == j0 + q) my_dg = v;
     }
@@ -123,9 +140,8 @@ __global__ __launch_bounds__(256) void gate_bwd(const T* __restrict__ dy, const 
     float fp = 0.f, fr[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
-      const int e = lane + 64 * i;
       l[i] *= inv_z;  // p
-      fr[i] = e < E ? (float)counts[e] * inv_tk : 0.f;
+      fr[i] = s_fr[lane + 64 * i];
       fp = fmaf(l[i], fr[i], fp);
     }
     fp = wave_sum(fp);
