@@ -84,3 +84,33 @@ def test_max_rows_and_workspace_sizes():
         assert ws0 % 256 == 0
     # the logits scratch alone is T*E fp32
     assert B.moe_workspace_bytes(full, 0) > 4096 * 896 * 4
+
+
+def test_backward_entry_points_validate_on_the_host():
+    lib = B.lib()
+    s = shape()
+    fake = ctypes.c_void_p(0x100000)      # never dereferenced: validation fails first
+    # gate backward: dlogits is required; logits only with counts and a coefficient
+    assert lib.moe_gate_bwd(ctypes.byref(s), fake, fake, fake, fake, fake, None, None, ctypes.c_float(0.0),
+                            None, None, None) == B.MOE_ERR_INVALID_ARG
+    assert b"dlogits is NULL" in lib.moe_last_error()
+    assert lib.moe_gate_bwd(ctypes.byref(s), fake, fake, fake, fake, fake, None, fake, ctypes.c_float(0.01),
+                            None, fake, None) == B.MOE_ERR_INVALID_ARG
+    assert b"logits is NULL" in lib.moe_last_error()
+    # expert backward: scratch and output buffers, then the workspace size
+    args = [fake] * 13
+    args[9] = None  # dgu
+    assert lib.moe_expert_bwd(ctypes.byref(s), None, *args, 1 << 30, None) == B.MOE_ERR_INVALID_ARG
+    assert b"dgu is NULL" in lib.moe_last_error()
+    args = [fake] * 13
+    assert lib.moe_expert_bwd(ctypes.byref(s), None, *args, 16, None) == B.MOE_ERR_WORKSPACE
+    # packed paths: bf16 with d, f % 128 == 0 (and E % 64 == 0 for the router)
+    bf = shape(dtype=B.MOE_BF16, d=128, f=64)
+    assert lib.moe_pack_backward_weights(ctypes.byref(bf), fake, fake, fake, fake, fake,
+                                         None) == B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_pack_router_bwd(ctypes.byref(bf), fake, fake, None) == B.MOE_ERR_UNSUPPORTED  # E = 16
+    bf2 = shape(dtype=B.MOE_BF16, d=128, f=128)
+    assert lib.moe_pack_backward_weights(ctypes.byref(bf2), fake, fake, fake, None, None,
+                                         None) == B.MOE_ERR_INVALID_ARG                      # no output
+    assert lib.moe_router_bwd(ctypes.byref(s), None, fake, fake, fake, 1 << 30,
+                              None) == B.MOE_ERR_INVALID_ARG
