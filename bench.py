@@ -91,14 +91,23 @@ def cpu_baseline(w, inp):
     bias = inp["bias"].numpy() if "bias" in inp else None
     S = min(64, w.T)          # about 15-20 s of float64 NumPy on 8-16 cores
     x = inp["x"][:S].to(torch.float64).numpy()
+    lora = None
+    if w.lora_r:
+        lora = {"scale": w.lora_alpha / w.lora_r,
+                **{n: inp[n].to(torch.float64).numpy() for n in ("a_up", "b_up", "a_down", "b_down")}}
     t0 = time.perf_counter()
-    oracle.moe_layer(x, wr, wg, wu, wd, w.k, bias=bias, e_lo=w.e_lo, e_hi=w.local_hi,
-                     capacity=0)
+    fwd = oracle.moe_layer(x, wr, wg, wu, wd, w.k, bias=bias, e_lo=w.e_lo, e_hi=w.local_hi,
+                           capacity=0, lora=lora, aux_coef=w.aux_coef)
+    what = "route over all {E} experts, dispatch, SwiGLU experts, combine".format(E=w.E)
+    if lora is not None:
+        dy = inp["dy"][:S].to(torch.float64).numpy()
+        oracle.lora_backward(dy, fwd["x_perm"], fwd["offsets"], fwd["row_src"], fwd["row_gate"], fwd["G"],
+                             fwd["H"], wd, lora)
+        what += " with LoRA, load-balance loss, LoRA adapter gradients"
     spent, total_tok = time.perf_counter() - t0, S
     log(f"[cpu_baseline] oracle on {S} tokens: {spent:.2f} s")
     return {"value": total_tok / spent, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {total_tok} of {w.T} tokens of {w.name} (route over all {w.E} experts, "
-                      f"dispatch, SwiGLU experts, combine; float64 NumPy), {spent:.1f} s"}
+            "sample": f"first {total_tok} of {w.T} tokens of {w.name} ({what}; float64 NumPy), {spent:.1f} s"}
 
 
 def calibrate_copy(nbytes: int = 1 << 30, reps: int = 5) -> None:
@@ -151,8 +160,6 @@ def main() -> int:
         return 0
 
     w = WORKLOADS[args.workload]
-    if w.lora_r:
-        raise SystemExit("bench.py times the forward layer; pick a workload without LoRA")
     log(f"[bench] generating {w.name}: T={w.T} d={w.d} E={w.E} k={w.k} f={w.f} L={w.L}")
     t0 = time.time()
     inp = generate(w, seed=0)
@@ -160,6 +167,10 @@ def main() -> int:
     torch.cuda.synchronize()
     log(f"[bench] inputs ready in {time.time() - t0:.1f} s")
     shape = layer.shape_of(w)
+    if w.lora_r:
+        out = lora_step_bench(args, w, inp, dev, shape)
+        print(json.dumps(out), flush=True)
+        return 0
     buf = layer.alloc(shape)
     # the frozen expert weights live in their packed layout (one-time, outside the step)
     packed = layer.pack_weights(shape, dev["w_gate"], dev["w_up"], dev["w_down"])
@@ -272,6 +283,86 @@ def main() -> int:
         out["cpu_baseline"] = cpu_baseline(w, inp)
     print(json.dumps(out), flush=True)
     return 0
+
+
+def lora_step_bench(args, w, inp, dev, shape):
+    """One LoRA fine-tuning step of the layer: the forward with the rank-r
+    adapters on the up and down projections (route with the softmax sums,
+    dispatch, expert GEMMs saving G/H/U, combine), the load-balance loss, and
+    the four adapter gradients for an upstream gradient dY. The frozen expert
+    weights are packed once before timing; router and base weights get no
+    gradient. tokens/s counts the layer's T tokens per step."""
+    import torch
+
+    from sparse_mixture_experts_top_amd import binding as B
+    from sparse_mixture_experts_top_amd import layer
+
+    L, r, d, f = w.L, w.lora_r, w.d, w.f
+    buf = layer.alloc(shape, lora_r=r, prob=True, act_save=True)
+    packed = layer.pack_weights(shape, dev["w_gate"], dev["w_up"], dev["w_down"])
+    lora = B.make_lora(r, w.lora_alpha, dev["a_up"], dev["b_up"], dev["a_down"], dev["b_down"])
+    grads = [torch.empty(sz, dtype=torch.float32, device="cuda")
+             for sz in ((L, r, d), (L, f, r), (L, r, f), (L, d, r))]
+    torch.cuda.synchronize()
+
+    def step():
+        layer.forward(buf, dev["x"], dev["w_router"], dev.get("bias"), None, None, None, lora, packed=packed)
+        B.moe_aux_loss(shape, buf.counts, buf.prob_sum, w.aux_coef, buf.aux)
+        xr, xs = layer.x_rows(buf, dev["x"])
+        B.moe_lora_bwd(shape, lora, dev["dy"], buf.offsets, buf.row_src, buf.row_gate, xr, xs, buf.act_save,
+                       dev["w_down"], *grads, buf.ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    B.moe_timing_enable(["gate_up"])
+    stream = torch.cuda.current_stream()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    elapsed_ms = start.elapsed_time(stop)
+    gu_ms, gu_n = B.moe_timing_read("gate_up")
+    B.moe_timing_enable(True)
+    for _ in range(max(1, min(args.steps, 10))):
+        step()
+    torch.cuda.synchronize()
+    kernels = {}  # microseconds per step, summed over a kind's launches in the step
+    for name in B.KERNELS:
+        ms, n = B.moe_timing_read(name)
+        if n:
+            kernels[name] = round(1000.0 * ms / max(1, min(args.steps, 10)), 2)
+    B.moe_timing_enable(False)
+    ms_step = elapsed_ms / args.steps
+    counts = buf.offsets.diff().cpu().numpy()
+    R = int(buf.offsets[-1].item())
+    active = int((counts > 0).sum())
+    gu_bytes = 2 * active * f * d * 2 + R * d * 2 + R * f * 2
+    gu_us = 1000.0 * gu_ms / gu_n
+    achieved = gu_bytes / (gu_us * 1e-6) / 1e9
+    gu_flops = 4.0 * R * d * f
+    out = {
+        "metric": METRIC, "value": round(w.T / (ms_step / 1000.0), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) tokens and dY, N(0,1/fan_in) weights, LoRA A ~ N(0,1/d), "
+                "B ~ N(0,1e-3))",
+        "config": {"workload": w.name, "launch": "eager", "T": w.T, "d": d, "E": w.E, "k": w.k, "f": f,
+                   "local_experts": L, "lora_rank": r, "lora_alpha": w.lora_alpha, "aux_coef": w.aux_coef,
+                   "rows": R, "active_experts": active,
+                   "step": "forward with LoRA + load-balance loss + LoRA adapter gradients"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(w.name),
+                     "kernel": "gate_up_bf16", "algorithmic_bytes": gu_bytes, "avg_us": round(gu_us, 2),
+                     "mfma_tflops": round(gu_flops / (gu_us * 1e-6) / 1e12, 1),
+                     "mfma_frac": round(gu_flops / (gu_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "kernels_us_per_step": kernels,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inp)
+    return out
 
 
 def backward_pass(w, dev, shape, packed, R, active, reps=5):

@@ -525,7 +525,7 @@ hipError_t launch_expert_bwd(const Ctx& c, const moe_shape_t& s, const Workspace
     bf16_t* dgub = (bf16_t*)dgu;
     if (lo) {
       MOE_TRY(launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, dyb, d, row_src, row_gate, d, lo->b_down, false,
-                                          lo->r, ws.wproj));
+                                          lo->r, ws.wproj, ws.lora_mt));
     }
     {
       TimedLaunch tl(MOE_K_EXPERT_DGU, c.stream);
@@ -538,7 +538,7 @@ hipError_t launch_expert_bwd(const Ctx& c, const moe_shape_t& s, const Workspace
     }
     if (lo) {
       MOE_TRY(launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, dgub + f, 2 * f, nullptr, nullptr, f, lo->b_up,
-                                          false, lo->r, ws.vproj));
+                                          false, lo->r, ws.vproj, ws.lora_mt));
     }
     {
       TimedLaunch tl(MOE_K_EXPERT_DX, c.stream);

@@ -113,6 +113,7 @@ struct Workspace {
   float* wproj;          // [Rmax, rmax] LoRA dO B_down
   float* vproj;          // [Rmax, rmax] LoRA dU B_up
   float* du;             // [Rmax, f]   LoRA backward dU (f32)
+  bf16_t* lora_mt;       // [L, r, max(d, f)] a [K, r] adapter transposed for the rank-r projections
   float* logits;         // [T, E]
   float* prob_part;      // [prob_blocks, E]
   int64_t bytes;
@@ -202,10 +203,13 @@ hipError_t launch_router_bwd(const Ctx& c, const moe_shape_t& s, const Workspace
 // LoRA building blocks shared by the forward (expert_gemm) and the backward.
 // out[p, q] = scale_p * sum_i in[src(p), i] * M(le(p), q, i) for rows p < R.
 //   m_qk: M stored [L, r, K] (true) or [L, K, r] (false)
+//   mt:   scratch of L * r * K bf16 for M transposed to [L, r, K] when it is
+//         stored [L, K, r] (the matrix-core path reads K-contiguous rows), or
+//         NULL (then such an M takes the plain per-row path)
 template <class TIn>
 hipError_t launch_lora_rowproj(const Ctx& c, int L, const int32_t* offsets, int64_t rmax_rows,
                                const TIn* in, int64_t in_stride, const int32_t* src,
                                const float* row_scale, int K, const bf16_t* M, bool m_qk, int r,
-                               float* out);
+                               float* out, bf16_t* mt = nullptr);
 
 }  // namespace moe

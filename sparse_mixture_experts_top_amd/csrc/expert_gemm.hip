@@ -514,7 +514,7 @@ static hipError_t launch_bwd_gemms_cfg(const Ctx& c, const moe_shape_t& s, const
   hipError_t err;
   if (lo) {
     err = launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, dy, s.d, row_src, row_gate, s.d, lo->b_down, false,
-                                      lo->r, ws.wproj);
+                                      lo->r, ws.wproj, ws.lora_mt);
     if (err != hipSuccess) return err;
   }
   {
@@ -527,7 +527,7 @@ static hipError_t launch_bwd_gemms_cfg(const Ctx& c, const moe_shape_t& s, const
   }
   if (lo) {
     err = launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, dgu + s.f, 2 * s.f, nullptr, nullptr, s.f, lo->b_up,
-                                      false, lo->r, ws.vproj);
+                                      false, lo->r, ws.vproj, ws.lora_mt);
     if (err != hipSuccess) return err;
   }
   DxPackedProb<Cfg> pb{dgu, offsets, ws.gemm_tiles, dx_packed, s.d, s.f, (s.d + Cfg::BN - 1) / Cfg::BN,

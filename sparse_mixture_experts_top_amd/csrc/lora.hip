@@ -92,11 +92,133 @@ __global__ __launch_bounds__(256) void lora_rowproj(int L, const int32_t* __rest
   }
 }
 
+// Largest le with off[le] <= p (off[0] <= p < off[L]), wave-uniform: a
+// binary search on scalar loads.
+__device__ __forceinline__ int segment_of_uniform(const int32_t* off, int L, int p) {
+  int lo = 0, hi = L;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (ld_uniform(off, mid) <= p) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// Eight consecutive K values of one row as an MFMA operand: bf16 as is; fp32
+// split into a bf16 high part and the bf16 rounding of the remainder (their
+// sum carries about 16 significant bits).
+__device__ __forceinline__ void frag_load(const bf16_t* p, bf16x8& hi, bf16x8& lo, bool) {
+  hi = *reinterpret_cast<const bf16x8*>(p);
+  (void)lo;
+}
+__device__ __forceinline__ void frag_load(const float* p, bf16x8& hi, bf16x8& lo, bool) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    h[u] = f32x2_to_bf16x2(v[2 * u], v[2 * u + 1]);
+    const float r0 = v[2 * u] - bf16_to_f32(static_cast<bf16_t>(h[u]));
+    const float r1 = v[2 * u + 1] - bf16_to_f32(static_cast<bf16_t>(h[u] >> 16));
+    l[u] = f32x2_to_bf16x2(r0, r1);
+  }
+  hi = __builtin_bit_cast(bf16x8, u32x4{h[0], h[1], h[2], h[3]});
+  lo = __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]});
+}
+
+// out[p, q] = scale_p * in[src_p] . Mt[le][q] for q < r <= 16 on the matrix
+// cores. One workgroup per 16 consecutive dispatched rows; its 4 waves take
+// the K steps of 32 in turn (wave w: steps w, w + 4, ...) and their 16 x 16
+// partial sums are added in wave order through LDS. A group that spans an
+// expert boundary is computed once per expert it touches, each pass storing
+// that expert's rows. Lane l supplies row l % 16 of the in-rows and of Mt
+// (ranks) at K offset 8 (l / 16) and receives rows 4 (l / 16) + i, rank l % 16.
+template <class TIn>
+__global__ __launch_bounds__(256) void lora_proj_mfma(int L, const int32_t* __restrict__ offsets,
+                                                      const TIn* __restrict__ in, int64_t in_stride,
+                                                      const int32_t* __restrict__ src,
+                                                      const float* __restrict__ row_scale, int K,
+                                                      const bf16_t* __restrict__ Mt, int r,
+                                                      float* __restrict__ out) {
+  constexpr bool kSplit = sizeof(TIn) == 4;
+  constexpr int U = 4;  // K steps per load batch
+  __shared__ f32x4 part[4][64];
+  const int R = ld_uniform(offsets, L);
+  const int p0 = blockIdx.x * 16;
+  if (p0 >= R) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int row = lane & 15, kc = lane >> 4;
+  const int le_first = segment_of_uniform(offsets, L, p0);
+  const int le_last = segment_of_uniform(offsets, L, min(p0 + 15, R - 1));
+  const int prow = min(p0 + row, R - 1);
+  const int64_t srow = src ? (int64_t)src[prow] : (int64_t)prow;
+  const TIn* a_ptr = in + srow * in_stride + kc * 8;
+  const int nsteps = K / 32;
+  for (int le = le_first; le <= le_last; ++le) {
+    const int seg0 = ld_uniform(offsets, le), seg1 = ld_uniform(offsets, le + 1);
+    if (seg0 == seg1) continue;  // wave-uniform
+    const bf16_t* b_ptr = Mt + ((int64_t)le * r + min(row, r - 1)) * K + kc * 8;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = wave; s0 < nsteps; s0 += 4 * U) {
+      bf16x8 ah[U], al[U], b[U];
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        const int st = s0 + 4 * j;
+        if (st < nsteps) {
+          frag_load(a_ptr + (int64_t)st * 32, ah[j], al[j], kSplit);
+          b[j] = *reinterpret_cast<const bf16x8*>(b_ptr + (int64_t)st * 32);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        if (s0 + 4 * j < nsteps) {
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[j], b[j], acc, 0, 0, 0);
+          if constexpr (kSplit) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[j], b[j], acc, 0, 0, 0);
+        }
+      }
+    }
+    part[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+      const f32x4 t = part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane];
+      const int q = lane & 15;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int p = p0 + 4 * kc + i;
+        if (q < r && p >= seg0 && p < seg1) out[(int64_t)p * r + q] = (row_scale ? row_scale[p] : 1.f) * t[i];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Mt[le][q][k] = M[le][k][q]: a [L, K, r] adapter made K-contiguous.
+__global__ __launch_bounds__(256) void lora_transpose_kr(const bf16_t* __restrict__ M, int L, int K, int r,
+                                                         bf16_t* __restrict__ Mt) {
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= (int64_t)L * K) return;
+  const int64_t le = id / K, k = id % K;
+  for (int q = 0; q < r; ++q) Mt[(le * r + q) * K + k] = M[id * r + q];
+}
+
 template <class TIn>
 hipError_t launch_lora_rowproj(const Ctx& c, int L, const int32_t* offsets, int64_t rmax_rows,
                                const TIn* in, int64_t in_stride, const int32_t* src,
                                const float* row_scale, int K, const bf16_t* M, bool m_qk, int r,
-                               float* out) {
+                               float* out, bf16_t* mt) {
+  if (r <= 16 && K % 32 == 0 && in_stride % 8 == 0 && (m_qk || mt) && rmax_rows > 0) {
+    TimedLaunch tl(MOE_K_LORA_PROJ, c.stream);
+    if (!m_qk) {
+      const int64_t n = (int64_t)L * K;
+      hipLaunchKernelGGL(lora_transpose_kr, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, c.stream, M, L, K, r,
+                         mt);
+      M = mt;
+    }
+    hipLaunchKernelGGL(lora_proj_mfma<TIn>, dim3((unsigned)((rmax_rows + 15) / 16)), dim3(256), 0, c.stream, L,
+                       offsets, in, in_stride, src, row_scale, K, M, r, out);
+    return hipGetLastError();
+  }
   const int64_t want = (rmax_rows + 3) / 4;
   const int grid = (int)(want < (int64_t)c.num_cus * 8 ? (want > 0 ? want : 1) : (int64_t)c.num_cus * 8);
   TimedLaunch tl(MOE_K_LORA_PROJ, c.stream);
@@ -112,10 +234,11 @@ hipError_t launch_lora_rowproj(const Ctx& c, int L, const int32_t* offsets, int6
 
 template hipError_t launch_lora_rowproj<bf16_t>(const Ctx&, int, const int32_t*, int64_t,
                                                 const bf16_t*, int64_t, const int32_t*,
-                                                const float*, int, const bf16_t*, bool, int, float*);
+                                                const float*, int, const bf16_t*, bool, int, float*,
+                                                bf16_t*);
 template hipError_t launch_lora_rowproj<float>(const Ctx&, int, const int32_t*, int64_t,
                                                const float*, int64_t, const int32_t*, const float*,
-                                               int, const bf16_t*, bool, int, float*);
+                                               int, const bf16_t*, bool, int, float*, bf16_t*);
 
 // out[le] = s * sum_{p in rows of le} P[p, q] * qscale_p * in[qsrc_p, c], for
 // q < r, c < C; stored [L, r, C] (out_qc) or [L, C, r].
@@ -164,10 +287,121 @@ __global__ __launch_bounds__(256) void lora_seg_outer(const int32_t* __restrict_
   }
 }
 
+// Same sums for r <= 16 and C % 4 == 0, with the rows spread over the
+// workgroup: one workgroup per (256 columns, expert), 8 waves, wave w taking
+// the expert's rows w, w + 8, ... in order, each lane 4 consecutive columns
+// x 16 ranks in registers. A row's P values are wave-uniform (one scalar
+// load of 16 floats); four rows' loads are issued before their FMAs. The
+// 8 waves' partial sums are then added in wave order through LDS, so the
+// result does not depend on timing.
+typedef float f32x16_t __attribute__((ext_vector_type(16), aligned(4)));
+typedef const __attribute__((address_space(4))) f32x16_t* const_f32x16_ptr_t;
+typedef const __attribute__((address_space(4))) float* const_f32_ptr_t;
+
+template <class TIn> struct Vec4;
+template <> struct Vec4<bf16_t> {
+  static __device__ __forceinline__ void load(const bf16_t* p, float (&v)[4]) {
+    const uint2 raw = *reinterpret_cast<const uint2*>(p);
+    v[0] = bf16_to_f32(static_cast<bf16_t>(raw.x));
+    v[1] = bf16_to_f32(static_cast<bf16_t>(raw.x >> 16));
+    v[2] = bf16_to_f32(static_cast<bf16_t>(raw.y));
+    v[3] = bf16_to_f32(static_cast<bf16_t>(raw.y >> 16));
+  }
+};
+template <> struct Vec4<float> {
+  static __device__ __forceinline__ void load(const float* p, float (&v)[4]) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  }
+};
+
+constexpr int kSegWaves = 8;   // waves per workgroup
+constexpr int kSegCols = 256;  // columns per workgroup (4 per lane)
+constexpr int kSegRq = 16;     // ranks held per lane
+
+template <class TIn>
+__global__ __launch_bounds__(64 * kSegWaves) void lora_seg_outer16(
+    const int32_t* __restrict__ offsets, const float* __restrict__ P, int r, const TIn* __restrict__ in,
+    int64_t in_stride, const int32_t* __restrict__ qsrc, const float* __restrict__ qscale, int C, float s,
+    int out_qc, float* __restrict__ out) {
+  constexpr int B = 4;  // rows per load batch
+  __shared__ float red[kSegWaves][kSegRq][kSegCols];
+  const int le = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int cb = blockIdx.x * kSegCols;
+  const int c0 = cb + lane * 4;
+  const bool cok = c0 < C;
+  const int a = ld_uniform(offsets, le), b = ld_uniform(offsets, le + 1);
+  float acc[kSegRq][4];
+#pragma unroll
+  for (int q = 0; q < kSegRq; ++q)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[q][u] = 0.f;
+  for (int p0 = a + wave; p0 < b; p0 += kSegWaves * B) {
+    float v[B][4];
+    f32x16_t pr[B];
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const int p = p0 + j * kSegWaves;  // wave-uniform
+      if (p < b) {
+        const int64_t src = qsrc ? (int64_t)ld_uniform(qsrc, p) : (int64_t)p;
+        const float sc = qscale ? ((const_f32_ptr_t)qscale)[p] : 1.f;
+        if (cok) {
+          Vec4<TIn>::load(in + src * in_stride + c0, v[j]);
+        } else {
+          v[j][0] = v[j][1] = v[j][2] = v[j][3] = 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[j][u] *= sc;
+        if (r == kSegRq) {
+          pr[j] = *(const_f32x16_ptr_t)(P + (int64_t)p * r);
+        } else {
+#pragma unroll
+          for (int q = 0; q < kSegRq; ++q) pr[j][q] = q < r ? ((const_f32_ptr_t)P)[(int64_t)p * r + q] : 0.f;
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[j][u] = 0.f;
+#pragma unroll
+        for (int q = 0; q < kSegRq; ++q) pr[j][q] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < B; ++j)
+#pragma unroll
+      for (int q = 0; q < kSegRq; ++q)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[q][u] = fmaf(pr[j][q], v[j][u], acc[q][u]);
+  }
+#pragma unroll
+  for (int q = 0; q < kSegRq; ++q)
+    *reinterpret_cast<float4*>(&red[wave][q][lane * 4]) = make_float4(acc[q][0], acc[q][1], acc[q][2], acc[q][3]);
+  __syncthreads();
+  // outputs of this workgroup: kSegRq x kSegCols, each the sum over the waves in order
+  for (int o = threadIdx.x; o < kSegRq * kSegCols; o += 64 * kSegWaves) {
+    // [L, r, C]: column fastest; [L, C, r]: rank fastest (coalesced stores either way)
+    const int q = out_qc ? o / kSegCols : o % kSegRq;
+    const int cc = out_qc ? o % kSegCols : o / kSegRq;
+    if (q >= r || cb + cc >= C) continue;
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < kSegWaves; ++w) t += red[w][q][cc];
+    if (out_qc) out[((int64_t)le * r + q) * C + cb + cc] = s * t;
+    else out[((int64_t)le * C + cb + cc) * r + q] = s * t;
+  }
+}
+
 template <class TIn>
 static hipError_t launch_seg_outer(const Ctx& c, int L, const int32_t* offsets, const float* P,
                                    int r, const TIn* in, int64_t in_stride, const int32_t* qsrc,
                                    const float* qscale, int C, float s, bool out_qc, float* out) {
+  if (r <= kSegRq && C % 4 == 0 && in_stride % 4 == 0) {
+    TimedLaunch tl(MOE_K_LORA_GRAD, c.stream);
+    hipLaunchKernelGGL(lora_seg_outer16<TIn>, dim3((C + kSegCols - 1) / kSegCols, L), dim3(64 * kSegWaves), 0,
+                       c.stream, offsets, P, r, in, in_stride, qsrc, qscale, C, s, (int)out_qc, out);
+    return hipGetLastError();
+  }
   dim3 grid((C + 255) / 256, L);
   TimedLaunch tl(MOE_K_LORA_GRAD, c.stream);
 #define MOE_SO(N)                                                                             \
@@ -269,7 +503,7 @@ hipError_t launch_lora_bwd(const Ctx& c, const moe_shape_t& sh, const Workspace&
   MOE_TRY(launch_row_tiles(c, offsets, L, max_tiles, ws.gemm_tiles));
   MOE_TRY(launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, x_rows, d, x_src, nullptr, d, lo.a_up, true, r, ws.zu));
   MOE_TRY(launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, H, 3 * f, nullptr, nullptr, f, lo.a_down, true, r, ws.zd));
-  MOE_TRY(launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, dy, d, row_src, row_gate, d, lo.b_down, false, r, ws.wproj));
+  MOE_TRY(launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, dy, d, row_src, row_gate, d, lo.b_down, false, r, ws.wproj, ws.lora_mt));
   {
     TimedLaunch tl(MOE_K_LORA_DH, c.stream);
     DhProb<Cfg> pb{dy, row_src, row_gate, offsets, ws.gemm_tiles, w_down, d, f, (f + Cfg::BN - 1) / Cfg::BN,
@@ -278,7 +512,7 @@ hipError_t launch_lora_bwd(const Ctx& c, const moe_shape_t& sh, const Workspace&
                        max_tiles);
     MOE_TRY(hipGetLastError());
   }
-  MOE_TRY(launch_lora_rowproj<float>(c, L, offsets, rmax, ws.du, f, nullptr, nullptr, f, lo.b_up, false, r, ws.vproj));
+  MOE_TRY(launch_lora_rowproj<float>(c, L, offsets, rmax, ws.du, f, nullptr, nullptr, f, lo.b_up, false, r, ws.vproj, ws.lora_mt));
   MOE_TRY(launch_seg_outer<bf16_t>(c, L, offsets, ws.zd, r, dy, d, row_src, row_gate, d, lo.scale, false, db_down));
   MOE_TRY(launch_seg_outer<bf16_t>(c, L, offsets, ws.wproj, r, H, 3 * f, nullptr, nullptr, f, lo.scale, true, da_down));
   MOE_TRY(launch_seg_outer<float>(c, L, offsets, ws.zu, r, ws.du, f, nullptr, nullptr, f, lo.scale, false, db_up));

@@ -30,6 +30,10 @@ CASES = {
     "router128p_bf16": W("router128p_bf16", T=333, d=256, E=128, k=4, f=128),
     "lora_bf16": W("lora_bf16", T=256, d=128, E=12, k=4, f=128, e_lo=2, e_hi=9, lora_r=16,
                    lora_alpha=32.0, lora_b="normal"),
+    # ~300 rows per expert: the layout with two compute waves per SIMD (three
+    # row tiles per expert, the last one ragged), a local range and LoRA
+    "wide_bf16": W("wide_bf16", T=1200, d=256, E=16, k=4, f=128, e_lo=2, e_hi=13, lora_r=16,
+                   lora_alpha=32.0, lora_b="normal"),
 }
 
 

@@ -29,6 +29,9 @@ SMALL = {
                       capacity=25, zipf_s=1.0, dtype="f32"),
     "k_equals_E_bf16": W("k_equals_E_bf16", T=130, d=64, E=8, k=8, f=64),
     "k1_bf16": W("k1_bf16", T=257, d=128, E=16, k=1, f=128),
+    # ~300 rows per expert: the layout with two compute waves per SIMD (three
+    # row tiles per expert, the last one ragged), local range
+    "wide_bf16": W("wide_bf16", T=1200, d=256, E=16, k=4, f=128, e_lo=2, e_hi=13),
 }
 
 
@@ -55,7 +58,8 @@ def test_stagewise_parity(name):
     run_and_check(SMALL[name])
 
 
-@pytest.mark.parametrize("name", ["tiny_f32", "ragged_bf16", "local_bf16", "rows_bf16", "capacity_bf16"])
+@pytest.mark.parametrize("name", ["tiny_f32", "ragged_bf16", "local_bf16", "rows_bf16", "capacity_bf16",
+                                  "wide_bf16"])
 def test_stagewise_parity_fused_gather(name):
     """The expert GEMM reading x through row_src (no x_perm copy)."""
     run_and_check(SMALL[name], seed=7, x_perm=False)
@@ -151,7 +155,7 @@ def test_capacity_one_everywhere():
     assert R == int((ref["counts"] > 0).sum())
 
 
-@pytest.mark.parametrize("name", ["ragged_bf16", "rows_bf16", "capacity_bf16", "k1_bf16"])
+@pytest.mark.parametrize("name", ["ragged_bf16", "rows_bf16", "capacity_bf16", "k1_bf16", "wide_bf16"])
 def test_stagewise_parity_packed_weights(name):
     """Expert weights streamed from their packed copies (fused gather too)."""
     run_and_check(SMALL[name], seed=8, x_perm=False, packed=True)
