@@ -54,6 +54,65 @@ __device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) 
   return make_uint2(f32x2_to_bf16x2(a, b), f32x2_to_bf16x2(c, d));
 }
 
+// LoRA terms of one lane's four consecutive output columns n .. n+3 for one
+// row with rank-r projection z (fp32, r values): t[q] = sum_c z[c] W[n+q][c]
+// for an adapter W stored [N, r] (w_n = W + n r), or t[q] = sum_c z[c]
+// A[c][n+q] for one stored [r, N] with row stride lda (a_n = A + n). At r = 16
+// the operands arrive in 16-byte (z, W) or 8-byte (A) loads.
+__device__ __forceinline__ float bf16_lane(uint32_t w, int hi) {
+  return bf16_to_f32(static_cast<bf16_t>(hi ? (w >> 16) : w));
+}
+__device__ __forceinline__ void lora_term_rows(const float* z, const bf16_t* w_n, int r, float (&t)[4]) {
+  t[0] = t[1] = t[2] = t[3] = 0.f;
+  if (r == 16) {
+    // four ranks at a time: one 16-byte load of z, one 8-byte load per column
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float4 zz = reinterpret_cast<const float4*>(z)[u];
+      uint2 wv[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) wv[q] = *reinterpret_cast<const uint2*>(w_n + q * 16 + 4 * u);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        t[q] = fmaf(zz.x, bf16_lane(wv[q].x, 0), t[q]);
+        t[q] = fmaf(zz.y, bf16_lane(wv[q].x, 1), t[q]);
+        t[q] = fmaf(zz.z, bf16_lane(wv[q].y, 0), t[q]);
+        t[q] = fmaf(zz.w, bf16_lane(wv[q].y, 1), t[q]);
+      }
+    }
+    return;
+  }
+  for (int c = 0; c < r; ++c)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) t[q] = fmaf(z[c], bf16_to_f32(w_n[q * r + c]), t[q]);
+}
+__device__ __forceinline__ void lora_term_cols(const float* z, const bf16_t* a_n, int64_t lda, int r,
+                                               float (&t)[4]) {
+  t[0] = t[1] = t[2] = t[3] = 0.f;
+  if (r == 16) {
+    // four ranks at a time: one 16-byte load of z, one 8-byte load per rank
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float4 zz = reinterpret_cast<const float4*>(z)[u];
+      const float zc[4] = {zz.x, zz.y, zz.z, zz.w};
+      uint2 av[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) av[c] = *reinterpret_cast<const uint2*>(a_n + (4 * u + c) * lda);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        t[0] = fmaf(zc[c], bf16_lane(av[c].x, 0), t[0]);
+        t[1] = fmaf(zc[c], bf16_lane(av[c].x, 1), t[1]);
+        t[2] = fmaf(zc[c], bf16_lane(av[c].y, 0), t[2]);
+        t[3] = fmaf(zc[c], bf16_lane(av[c].y, 1), t[3]);
+      }
+    }
+    return;
+  }
+  for (int c = 0; c < r; ++c)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) t[q] = fmaf(z[c], bf16_to_f32(a_n[c * lda + q]), t[q]);
+}
+
 // Index of the row block containing row p: largest le with off[le] <= p
 // (off has L+1 non-decreasing entries, off[0] = 0, p < off[L]).
 __device__ __forceinline__ int segment_of(const int32_t* off, int L, int p) {

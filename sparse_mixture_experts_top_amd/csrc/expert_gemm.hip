@@ -23,6 +23,8 @@
 // per CU walks the items, each XCD taking a contiguous range so row tiles
 // that share A or B stay in one L2.
 // fp32 path (small parity shapes): one thread per output element.
+#include <type_traits>
+
 #include "common.h"
 #include "mfma_tile.h"
 
@@ -126,7 +128,9 @@ __device__ __forceinline__ int64_t gathered_row(const int32_t* row_src, const Ro
 // K8: H = silu(X W_g^T) * (X W_u^T [+ s Z_u B_u^T]) for one (row tile, 128
 // FFN columns) item. Rows of X are x[row_src[p]] (gather fused into the A
 // loader) or, with row_src == NULL, x[p] of an already gathered matrix.
-template <class Cfg>
+// LORA: the epilogue adds the rank-r adapter term (a separate instantiation,
+// so the plain kernels carry no adapter code).
+template <class Cfg, bool LORA = false>
 struct GateUpProb {
   const bf16_t* x;
   const int32_t* row_src;
@@ -202,18 +206,15 @@ struct GateUpProb {
         // f % 64 == 0: a 16-column fragment pair is all inside f or all past it
         if (ni * HALF + (jg >> 1) * 16 >= f) continue;
         const int fcol = ni * HALF + (jg >> 1) * 16 + (lane >> 4) * 4;
-        float h[4], g[4], uu[4];
+        float h[4], g[4], uu[4], lt[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (LORA) {
+          if (ok) lora_term_rows(zu + row * r, b_up + ((int64_t)t.le * f + fcol) * r, r, lt);
+        }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           g[q] = acc.v[i][jj][q];
           float u = acc.v[i][jj + 1][q];
-          if (zu && ok) {
-            const float* z = zu + row * r;
-            const bf16_t* bu = b_up + ((int64_t)t.le * f + fcol + q) * r;
-            float s = 0.f;
-            for (int c = 0; c < r; ++c) s = fmaf(z[c], bf16_to_f32(bu[c]), s);
-            u = fmaf(scale, s, u);
-          }
+          if constexpr (LORA) u = fmaf(scale, lt[q], u);
           uu[q] = u;
           h[q] = silu_f(g[q]) * u;
         }
@@ -232,14 +233,16 @@ struct GateUpProb {
   }
 };
 
-template <class Cfg>
-__global__ __launch_bounds__(Cfg::THREADS, Cfg::WAVES_PER_SIMD) void gate_up_bf16(GateUpProb<Cfg> pb, int max_tiles) {
+template <class Cfg, bool LORA>
+__global__ __launch_bounds__(Cfg::THREADS, Cfg::WAVES_PER_SIMD) void gate_up_bf16(GateUpProb<Cfg, LORA> pb, int max_tiles) {
   const int items = ld_uniform(pb.tiles, 2 * max_tiles) * pb.nt;
   persistent_gemm_dma<Cfg>(pb, items, pb.d / Cfg::BK);
 }
 
 // K9: O = H W_d^T [+ s Z_d B_d^T] for one (row tile, 256 output columns) item.
-template <class Cfg>
+// LORA: the epilogue adds the rank-r adapter term (a separate instantiation,
+// so the plain kernels carry no adapter code).
+template <class Cfg, bool LORA = false>
 struct DownProb {
   const bf16_t* hbuf;
   const int32_t* offsets;
@@ -301,17 +304,14 @@ struct DownProb {
         // d % 64 == 0: a wave's 16-column fragment is all valid or all not
         if (n0 + wn * (Cfg::BN / Cfg::WN) + j * 16 >= d) continue;
         const int n = n0 + dma_out_col<Cfg>(wn, j, lane);
-        float o[4];
+        float o[4], lt[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (LORA) {
+          if (ok) lora_term_rows(zd + row * r, b_down + ((int64_t)t.le * d + n) * r, r, lt);
+        }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           o[q] = acc.v[i][j][q];
-          if (zd && ok) {
-            const float* z = zd + row * r;
-            const bf16_t* bd = b_down + ((int64_t)t.le * d + n + q) * r;
-            float s = 0.f;
-            for (int c = 0; c < r; ++c) s = fmaf(z[c], bf16_to_f32(bd[c]), s);
-            o[q] = fmaf(scale, s, o[q]);
-          }
+          if constexpr (LORA) o[q] = fmaf(scale, lt[q], o[q]);
         }
         if (ok) *reinterpret_cast<uint2*>(y_perm + row * d + n) = pack4_bf16(o[0], o[1], o[2], o[3]);
       }
@@ -319,8 +319,8 @@ struct DownProb {
   }
 };
 
-template <class Cfg>
-__global__ __launch_bounds__(Cfg::THREADS, Cfg::WAVES_PER_SIMD) void down_bf16(DownProb<Cfg> pb, int max_tiles) {
+template <class Cfg, bool LORA>
+__global__ __launch_bounds__(Cfg::THREADS, Cfg::WAVES_PER_SIMD) void down_bf16(DownProb<Cfg, LORA> pb, int max_tiles) {
   const int items = ld_uniform(pb.tiles, 2 * max_tiles) * pb.nt;
   persistent_gemm_dma<Cfg>(pb, items, pb.f / Cfg::BK);
 }
@@ -334,7 +334,9 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::WAVES_PER_SIMD) void down_bf16(D
 
 // dH[row, n] = g_row dY[src_row] . W_d^T[n] (+ s wproj[row] . A_d[:, n]), then
 // dG = dH U silu'(G), dU = dH silu(G) (G, U from act_save) -> dgu bf16.
-template <class Cfg>
+// LORA: the epilogue adds the rank-r adapter term (a separate instantiation,
+// so the plain kernels carry no adapter code).
+template <class Cfg, bool LORA = false>
 struct DguPackedProb {
   const bf16_t* dy;
   const int32_t* row_src;
@@ -396,16 +398,11 @@ struct DguPackedProb {
         const uint2 gv = *reinterpret_cast<const uint2*>(as);
         const uint2 uv = *reinterpret_cast<const uint2*>(as + 2 * f);
         const uint32_t gw[2] = {gv.x, gv.y}, uw[2] = {uv.x, uv.y};
-        float dgv[4], duv[4];
+        float dgv[4], duv[4], lt[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (LORA) lora_term_cols(wproj + row * r, a_down + (int64_t)t.le * r * f + n, f, r, lt);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          float lo = 0.f;
-          if (wproj) {
-            const float* w = wproj + row * r;
-            const bf16_t* ad = a_down + (int64_t)t.le * r * f + n + q;
-            for (int cc = 0; cc < r; ++cc) lo = fmaf(w[cc], bf16_to_f32(ad[(int64_t)cc * f]), lo);
-          }
-          const float dh = fmaf(g_row, acc.v[i][j][q], scale * lo);
+          const float dh = fmaf(g_row, acc.v[i][j][q], scale * lt[q]);
           const float g = bf16_to_f32(static_cast<bf16_t>(gw[q >> 1] >> ((q & 1) * 16)));
           const float u = bf16_to_f32(static_cast<bf16_t>(uw[q >> 1] >> ((q & 1) * 16)));
           const float sg = 1.0f / (1.0f + expf(-g));
@@ -419,15 +416,17 @@ struct DguPackedProb {
   }
 };
 
-template <class Cfg>
-__global__ __launch_bounds__(Cfg::THREADS, Cfg::WAVES_PER_SIMD) void expert_dgu_dma(DguPackedProb<Cfg> pb,
+template <class Cfg, bool LORA>
+__global__ __launch_bounds__(Cfg::THREADS, Cfg::WAVES_PER_SIMD) void expert_dgu_dma(DguPackedProb<Cfg, LORA> pb,
                                                                                    int max_tiles) {
   const int items = ld_uniform(pb.tiles, 2 * max_tiles) * pb.nt;
   persistent_gemm_dma<Cfg>(pb, items, pb.d / Cfg::BK);
 }
 
 // dX[row, n] = dgu[row] . [W_g; W_u]^T[n] (+ s vproj[row] . A_u[:, n]), fp32.
-template <class Cfg>
+// LORA: the epilogue adds the rank-r adapter term (a separate instantiation,
+// so the plain kernels carry no adapter code).
+template <class Cfg, bool LORA = false>
 struct DxPackedProb {
   const bf16_t* dgu;
   const int32_t* offsets;
@@ -478,17 +477,12 @@ struct DxPackedProb {
       for (int j = 0; j < Cfg::FN; ++j) {
         if (n0 + wn * (Cfg::BN / Cfg::WN) + j * 16 >= d) continue;
         const int n = n0 + dma_out_col<Cfg>(wn, j, lane);
-        float o[4];
+        float o[4], lt[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (LORA) lora_term_cols(vproj + row * r, a_up + (int64_t)t.le * r * d + n, d, r, lt);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           o[q] = acc.v[i][j][q];
-          if (vproj) {
-            const float* w = vproj + row * r;
-            const bf16_t* au = a_up + (int64_t)t.le * r * d + n + q;
-            float lo = 0.f;
-            for (int cc = 0; cc < r; ++cc) lo = fmaf(w[cc], bf16_to_f32(au[(int64_t)cc * d]), lo);
-            o[q] = fmaf(scale, lo, o[q]);
-          }
+          if constexpr (LORA) o[q] = fmaf(scale, lt[q], o[q]);
         }
         *reinterpret_cast<float4*>(dx_rows + row * d + n) = make_float4(o[0], o[1], o[2], o[3]);
       }
@@ -496,8 +490,8 @@ struct DxPackedProb {
   }
 };
 
-template <class Cfg>
-__global__ __launch_bounds__(Cfg::THREADS, Cfg::WAVES_PER_SIMD) void expert_dx_dma(DxPackedProb<Cfg> pb,
+template <class Cfg, bool LORA>
+__global__ __launch_bounds__(Cfg::THREADS, Cfg::WAVES_PER_SIMD) void expert_dx_dma(DxPackedProb<Cfg, LORA> pb,
                                                                                   int max_tiles) {
   const int items = ld_uniform(pb.tiles, 2 * max_tiles) * pb.nt;
   persistent_gemm_dma<Cfg>(pb, items, 2 * pb.f / Cfg::BK);
@@ -517,25 +511,31 @@ static hipError_t launch_bwd_gemms_cfg(const Ctx& c, const moe_shape_t& s, const
                                       lo->r, ws.wproj, ws.lora_mt);
     if (err != hipSuccess) return err;
   }
-  {
-    DguPackedProb<Cfg> pb{dy, row_src, row_gate, offsets, ws.gemm_tiles, dgu_packed, s.d, s.f,
-                          (s.f + Cfg::BN - 1) / Cfg::BN, L, lo ? ws.wproj : nullptr, lo ? lo->a_down : nullptr,
-                          lo ? lo->r : 0, lo ? lo->scale : 0.f, act_save, dgu};
+  auto dgu_launch = [&](auto with_lora) {
+    constexpr bool LO = decltype(with_lora)::value;
+    DguPackedProb<Cfg, LO> pb{dy, row_src, row_gate, offsets, ws.gemm_tiles, dgu_packed, s.d, s.f,
+                              (s.f + Cfg::BN - 1) / Cfg::BN, L, lo ? ws.wproj : nullptr, lo ? lo->a_down : nullptr,
+                              lo ? lo->r : 0, lo ? lo->scale : 0.f, act_save, dgu};
     TimedLaunch tl(MOE_K_EXPERT_DGU, c.stream);
-    hipLaunchKernelGGL(expert_dgu_dma<Cfg>, dim3(c.num_cus), dim3(Cfg::THREADS), 0, c.stream, pb, max_tiles);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-  }
+    hipLaunchKernelGGL((expert_dgu_dma<Cfg, LO>), dim3(c.num_cus), dim3(Cfg::THREADS), 0, c.stream, pb, max_tiles);
+    return hipGetLastError();
+  };
+  if ((err = lo ? dgu_launch(std::true_type{}) : dgu_launch(std::false_type{})) != hipSuccess) return err;
   if (lo) {
     err = launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, dgu + s.f, 2 * s.f, nullptr, nullptr, s.f, lo->b_up,
                                       false, lo->r, ws.vproj, ws.lora_mt);
     if (err != hipSuccess) return err;
   }
-  DxPackedProb<Cfg> pb{dgu, offsets, ws.gemm_tiles, dx_packed, s.d, s.f, (s.d + Cfg::BN - 1) / Cfg::BN,
-                       lo ? ws.vproj : nullptr, lo ? lo->a_up : nullptr, lo ? lo->r : 0, lo ? lo->scale : 0.f,
-                       dx_rows};
-  TimedLaunch tl(MOE_K_EXPERT_DX, c.stream);
-  hipLaunchKernelGGL(expert_dx_dma<Cfg>, dim3(c.num_cus), dim3(Cfg::THREADS), 0, c.stream, pb, max_tiles);
-  return hipGetLastError();
+  auto dx_launch = [&](auto with_lora) {
+    constexpr bool LO = decltype(with_lora)::value;
+    DxPackedProb<Cfg, LO> pb{dgu, offsets, ws.gemm_tiles, dx_packed, s.d, s.f, (s.d + Cfg::BN - 1) / Cfg::BN,
+                             lo ? ws.vproj : nullptr, lo ? lo->a_up : nullptr, lo ? lo->r : 0,
+                             lo ? lo->scale : 0.f, dx_rows};
+    TimedLaunch tl(MOE_K_EXPERT_DX, c.stream);
+    hipLaunchKernelGGL((expert_dx_dma<Cfg, LO>), dim3(c.num_cus), dim3(Cfg::THREADS), 0, c.stream, pb, max_tiles);
+    return hipGetLastError();
+  };
+  return lo ? dx_launch(std::true_type{}) : dx_launch(std::false_type{});
 }
 
 hipError_t launch_bwd_gemms_packed(const Ctx& c, const moe_shape_t& s, const Workspace& ws, const LoraArgs* lo,
@@ -863,30 +863,36 @@ hipError_t launch_grouped_bf16(const Ctx& c, const moe_shape_t& s, const Workspa
   const int L = s.e_hi - s.e_lo;
   const int64_t rmax = max_rows(s);
   const int grid = c.num_cus;  // one workgroup per CU (see mfma_tile.h)
-  {
-    GateUpProb<Cfg> pb{xr, row_src, offsets, ws.gemm_tiles, (const bf16_t*)w_gate,
-                           (const bf16_t*)w_up, (const bf16_t*)gu_packed, s.d, s.f,
-                           (s.f + GateUpProb<Cfg>::HALF - 1) / GateUpProb<Cfg>::HALF,
-                           s.e_hi - s.e_lo,
-                           lora ? ws.zu : nullptr, lora ? lora->b_up : nullptr, lora ? lora->r : 0,
-                           lora ? lora->scale : 0.f, (bf16_t*)ws.hbuf, (bf16_t*)act_save};
+  auto gu_launch = [&](auto with_lora) {
+    constexpr bool LO = decltype(with_lora)::value;
+    using P = GateUpProb<Cfg, LO>;
+    P pb{xr, row_src, offsets, ws.gemm_tiles, (const bf16_t*)w_gate,
+         (const bf16_t*)w_up, (const bf16_t*)gu_packed, s.d, s.f,
+         (s.f + P::HALF - 1) / P::HALF, s.e_hi - s.e_lo,
+         lora ? ws.zu : nullptr, lora ? lora->b_up : nullptr, lora ? lora->r : 0,
+         lora ? lora->scale : 0.f, (bf16_t*)ws.hbuf, (bf16_t*)act_save};
     TimedLaunch tl(MOE_K_GATE_UP, c.stream);
-    hipLaunchKernelGGL(gate_up_bf16<Cfg>, dim3(grid), dim3(Cfg::THREADS), 0, c.stream, pb, max_tiles);
-  }
-  if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL((gate_up_bf16<Cfg, LO>), dim3(grid), dim3(Cfg::THREADS), 0, c.stream, pb, max_tiles);
+    return hipGetLastError();
+  };
+  if ((err = lora ? gu_launch(std::true_type{}) : gu_launch(std::false_type{})) != hipSuccess) return err;
   if (lora) {
     err = launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, (const bf16_t*)ws.hbuf, s.f, nullptr,
                                       nullptr, s.f, lora->a_down, true, lora->r, ws.zd);
     if (err != hipSuccess) return err;
   }
-  DownProb<Cfg> pb{(const bf16_t*)ws.hbuf, offsets, ws.gemm_tiles, (const bf16_t*)w_down,
-                       (const bf16_t*)d_packed, s.d, s.f,
-                       (s.d + Cfg::BN - 1) / Cfg::BN, lora ? ws.zd : nullptr,
-                       lora ? lora->b_down : nullptr, lora ? lora->r : 0, lora ? lora->scale : 0.f,
-                       (bf16_t*)y_perm};
-  TimedLaunch tl(MOE_K_DOWN, c.stream);
-  hipLaunchKernelGGL(down_bf16<Cfg>, dim3(grid), dim3(Cfg::THREADS), 0, c.stream, pb, max_tiles);
-  return hipGetLastError();
+  auto dn_launch = [&](auto with_lora) {
+    constexpr bool LO = decltype(with_lora)::value;
+    DownProb<Cfg, LO> pb{(const bf16_t*)ws.hbuf, offsets, ws.gemm_tiles, (const bf16_t*)w_down,
+                         (const bf16_t*)d_packed, s.d, s.f,
+                         (s.d + Cfg::BN - 1) / Cfg::BN, lora ? ws.zd : nullptr,
+                         lora ? lora->b_down : nullptr, lora ? lora->r : 0, lora ? lora->scale : 0.f,
+                         (bf16_t*)y_perm};
+    TimedLaunch tl(MOE_K_DOWN, c.stream);
+    hipLaunchKernelGGL((down_bf16<Cfg, LO>), dim3(grid), dim3(Cfg::THREADS), 0, c.stream, pb, max_tiles);
+    return hipGetLastError();
+  };
+  return lora ? dn_launch(std::true_type{}) : dn_launch(std::false_type{});
 }
 
 }  // namespace moe
