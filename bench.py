@@ -303,14 +303,23 @@ def lora_step_bench(args, w, inp, dev, shape):
     lora = B.make_lora(r, w.lora_alpha, dev["a_up"], dev["b_up"], dev["a_down"], dev["b_down"])
     grads = [torch.empty(sz, dtype=torch.float32, device="cuda")
              for sz in ((L, r, d), (L, f, r), (L, r, f), (L, d, r))]
+    # W_d^T packed once for the adapter backward's dH product (W_d is frozen)
+    dgu_packed = None
+    if d % 128 == 0 and f % 128 == 0:
+        dgu_packed = torch.empty((L, f, d), dtype=torch.bfloat16, device="cuda")
+        B.moe_pack_backward_weights(shape, dev["w_gate"], dev["w_up"], dev["w_down"], dgu_packed, None)
     torch.cuda.synchronize()
 
     def step():
         layer.forward(buf, dev["x"], dev["w_router"], dev.get("bias"), None, None, None, lora, packed=packed)
         B.moe_aux_loss(shape, buf.counts, buf.prob_sum, w.aux_coef, buf.aux)
         xr, xs = layer.x_rows(buf, dev["x"])
-        B.moe_lora_bwd(shape, lora, dev["dy"], buf.offsets, buf.row_src, buf.row_gate, xr, xs, buf.act_save,
-                       dev["w_down"], *grads, buf.ws)
+        if dgu_packed is not None:
+            B.moe_lora_bwd_packed(shape, lora, dev["dy"], buf.offsets, buf.row_src, buf.row_gate, xr, xs,
+                                  buf.act_save, dgu_packed, *grads, buf.ws)
+        else:
+            B.moe_lora_bwd(shape, lora, dev["dy"], buf.offsets, buf.row_src, buf.row_gate, xr, xs, buf.act_save,
+                           dev["w_down"], *grads, buf.ws)
 
     for _ in range(args.warmup):
         step()

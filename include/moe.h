@@ -257,6 +257,18 @@ moe_status_t moe_lora_bwd(const moe_shape_t* shape, const moe_lora_t* lora, cons
                           const void* w_down, float* da_up, float* db_up, float* da_down,
                           float* db_down, void* ws, size_t ws_bytes, moe_stream_t stream);
 
+/* moe_lora_bwd with the frozen w_down's transpose packed once: dgu_packed
+ * [L, f, d] elements as written by moe_pack_backward_weights (its dx_packed
+ * may be NULL). The dH product then streams contiguous weight tiles on the
+ * DMA engine of the forward. Same arguments otherwise (w_down replaced);
+ * same results up to the fp32 summation order. bf16 only, d % 128 == 0 and
+ * f % 128 == 0 (MOE_ERR_UNSUPPORTED otherwise). */
+moe_status_t moe_lora_bwd_packed(const moe_shape_t* shape, const moe_lora_t* lora, const void* dy,
+                                 const int32_t* offsets, const int32_t* row_src, const float* row_gate,
+                                 const void* x, const int32_t* x_src, const void* act_save,
+                                 const void* dgu_packed, float* da_up, float* db_up, float* da_down,
+                                 float* db_down, void* ws, size_t ws_bytes, moe_stream_t stream);
+
 /* ---- full backward --------------------------------------------------------
  * Gradients of the loss sum(y * dy) + L_aux for training through the layer
  * ("Full-Stack Engineering Guide", §3: adapters are trained through the

@@ -27,7 +27,7 @@ KERNELS = ["router_gemm", "topk", "prob_reduce", "hist", "scan", "scatter", "cap
 
 EXPORTED = ["moe_workspace_bytes", "moe_max_rows", "moe_last_error", "moe_route",
             "moe_dispatch", "moe_expert_gemm", "moe_pack_expert_weights", "moe_expert_gemm_packed",
-            "moe_combine", "moe_aux_loss", "moe_lora_bwd", "moe_gate_bwd", "moe_expert_bwd",
+            "moe_combine", "moe_aux_loss", "moe_lora_bwd", "moe_lora_bwd_packed", "moe_gate_bwd", "moe_expert_bwd",
             "moe_router_bwd", "moe_pack_backward_weights", "moe_expert_bwd_packed", "moe_pack_router_bwd",
             "moe_router_bwd_packed", "moe_timing_enable", "moe_timing_read"]
 
@@ -73,6 +73,7 @@ def lib() -> ctypes.CDLL:
     L.moe_combine.argtypes = [shp, vp, vp, vp, vp, vp]
     L.moe_aux_loss.argtypes = [shp, vp, vp, f32, vp, vp]
     L.moe_lora_bwd.argtypes = [shp, lor, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_lora_bwd_packed.argtypes = [shp, lor, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_gate_bwd.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp]
     L.moe_expert_bwd.argtypes = [shp, lor, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_router_bwd.argtypes = [shp, vp, vp, vp, vp, sz, vp]
@@ -83,7 +84,7 @@ def lib() -> ctypes.CDLL:
     L.moe_timing_enable.argtypes = [i32]
     L.moe_timing_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     for fn in ("moe_route", "moe_dispatch", "moe_expert_gemm", "moe_pack_expert_weights",
-               "moe_expert_gemm_packed", "moe_combine", "moe_aux_loss", "moe_lora_bwd",
+               "moe_expert_gemm_packed", "moe_combine", "moe_aux_loss", "moe_lora_bwd", "moe_lora_bwd_packed",
                "moe_gate_bwd", "moe_expert_bwd", "moe_router_bwd", "moe_pack_backward_weights",
                "moe_expert_bwd_packed", "moe_pack_router_bwd", "moe_router_bwd_packed",
                "moe_timing_enable", "moe_timing_read"):
@@ -193,6 +194,17 @@ def moe_aux_loss(shape, counts, prob_sum, coef, out, stream=None):
     _check(lib().moe_aux_loss(ctypes.byref(shape), _dev(counts, torch.int32),
                               _dev(prob_sum, torch.float32), float(coef), _dev(out, torch.float32),
                               _stream(stream)))
+
+
+def moe_lora_bwd_packed(shape, lora, dy, offsets, row_src, row_gate, x, x_src, act_save, dgu_packed, da_up,
+                        db_up, da_down, db_down, ws, stream=None):
+    """moe_lora_bwd with W_d^T packed by moe_pack_backward_weights (dgu_packed)."""
+    bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
+    _check(lib().moe_lora_bwd_packed(ctypes.byref(shape), ctypes.byref(lora), _dev(dy, bf), _dev(offsets, i32),
+                                     _dev(row_src, i32), _dev(row_gate, f32), _dev(x, bf), _dev(x_src, i32),
+                                     _dev(act_save, bf), _dev(dgu_packed, bf), _dev(da_up, f32),
+                                     _dev(db_up, f32), _dev(da_down, f32), _dev(db_down, f32),
+                                     _dev(ws, torch.uint8), ws.numel(), _stream(stream)))
 
 
 def moe_lora_bwd(shape, lora, dy, offsets, row_src, row_gate, x, x_src, act_save, w_down, da_up,

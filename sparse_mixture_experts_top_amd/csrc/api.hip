@@ -418,6 +418,44 @@ moe_status_t moe_lora_bwd(const moe_shape_t* shape, const moe_lora_t* lora, cons
       "LoRA backward");
 }
 
+moe_status_t moe_lora_bwd_packed(const moe_shape_t* shape, const moe_lora_t* lora, const void* dy,
+                          const int32_t* offsets, const int32_t* row_src, const float* row_gate,
+                          const void* x, const int32_t* x_src, const void* act_save,
+                          const void* dgu_packed, float* da_up, float* db_up, float* da_down, float* db_down, void* ws,
+                          size_t ws_bytes, moe_stream_t stream) {
+  moe_status_t st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape_t& s = *shape;
+  if ((st = check_packable(s)) != MOE_OK) return st;
+  if (s.f % 128 != 0) return fail(MOE_ERR_UNSUPPORTED, "packed backward weights need f % 128 == 0");
+  MOE_REQUIRE(lora, "lora");
+  if ((st = check_lora(s, lora)) != MOE_OK) return st;
+  const bool rows = max_rows(s) > 0;
+  MOE_REQUIRE_IF(s.T > 0, dy, "dy");
+  MOE_REQUIRE(offsets, "offsets");
+  MOE_REQUIRE_IF(rows, row_src, "row_src");
+  MOE_REQUIRE_IF(rows, row_gate, "row_gate");
+  MOE_REQUIRE_IF(rows, x, "x");
+  MOE_REQUIRE_IF(rows, act_save, "act_save");
+  MOE_REQUIRE(dgu_packed, "dgu_packed");
+  MOE_REQUIRE(da_up, "da_up");
+  MOE_REQUIRE(db_up, "db_up");
+  MOE_REQUIRE(da_down, "da_down");
+  MOE_REQUIRE(db_down, "db_down");
+  if ((st = check_ws(s, lora->r, ws, ws_bytes)) != MOE_OK) return st;
+  Ctx c;
+  if ((st = make_ctx(stream, &c)) != MOE_OK) return st;
+  const Workspace w = carve_workspace(s, lora->r, ws);
+  LoraArgs la{lora->r, lora->alpha / (float)lora->r, static_cast<const bf16_t*>(lora->a_up),
+              static_cast<const bf16_t*>(lora->b_up), static_cast<const bf16_t*>(lora->a_down),
+              static_cast<const bf16_t*>(lora->b_down)};
+  return hip_status(
+      launch_lora_bwd(c, s, w, la, static_cast<const bf16_t*>(dy), offsets, row_src, row_gate,
+                      static_cast<const bf16_t*>(x), x_src, static_cast<const bf16_t*>(act_save),
+                      nullptr, da_up, db_up, da_down, db_down, static_cast<const bf16_t*>(dgu_packed)),
+      "LoRA backward (packed)");
+}
+
 moe_status_t moe_gate_bwd(const moe_shape_t* shape, const void* dy, const void* y_perm,
                           const int32_t* slot, const int32_t* topk_idx, const float* topk_gate,
                           const float* logits, const int32_t* counts, float aux_coef, float* dgate,

@@ -230,7 +230,12 @@ hipError_t launch_lora_bwd(const Ctx& c, const moe_shape_t& s, const Workspace& 
                            const int32_t* row_src, const float* row_gate, const bf16_t* x_rows,
                            const int32_t* x_src,
                            const bf16_t* act_save, const bf16_t* w_down, float* da_up,
-                           float* db_up, float* da_down, float* db_down);
+                           float* db_up, float* da_down, float* db_down,
+                           const bf16_t* dgu_packed = nullptr);
+// dU of the LoRA backward on the packed W_d^T (expert_gemm.hip)
+hipError_t launch_lora_dh_packed(const Ctx& c, const moe_shape_t& s, const Workspace& ws, const LoraArgs& lo,
+                                 const bf16_t* dy, const int32_t* row_src, const float* row_gate,
+                                 const int32_t* offsets, const bf16_t* act_save, const bf16_t* dgu_packed);
 
 hipError_t launch_gate_bwd(const Ctx& c, const moe_shape_t& s, const void* dy, const void* y_perm,
                            const int32_t* slot, const int32_t* idx, const float* gate,

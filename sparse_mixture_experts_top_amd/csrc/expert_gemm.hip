@@ -336,7 +336,9 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::WAVES_PER_SIMD) void down_bf16(D
 // dG = dH U silu'(G), dU = dH silu(G) (G, U from act_save) -> dgu bf16.
 // LORA: the epilogue adds the rank-r adapter term (a separate instantiation,
 // so the plain kernels carry no adapter code).
-template <class Cfg, bool LORA = false>
+// DU32: only dU = dH silu(G), in fp32, to du32 [Rmax, f] (the LoRA adapter
+// gradients need no dG).
+template <class Cfg, bool LORA = false, bool DU32 = false>
 struct DguPackedProb {
   const bf16_t* dy;
   const int32_t* row_src;
@@ -351,6 +353,7 @@ struct DguPackedProb {
   float scale;
   const bf16_t* act_save;
   bf16_t* dgu;
+  float* du32 = nullptr;
 
   __device__ __forceinline__ int rows(int item) const {
     return row_tile<Cfg::BM>(tiles, offsets, item / nt).valid;
@@ -396,10 +399,21 @@ struct DguPackedProb {
         if (!ok) continue;
         const bf16_t* as = act_save + row * 3 * f + n;
         const uint2 gv = *reinterpret_cast<const uint2*>(as);
-        const uint2 uv = *reinterpret_cast<const uint2*>(as + 2 * f);
-        const uint32_t gw[2] = {gv.x, gv.y}, uw[2] = {uv.x, uv.y};
         float dgv[4], duv[4], lt[4] = {0.f, 0.f, 0.f, 0.f};
         if constexpr (LORA) lora_term_cols(wproj + row * r, a_down + (int64_t)t.le * r * f + n, f, r, lt);
+        if constexpr (DU32) {
+          const uint32_t gw[2] = {gv.x, gv.y};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float dh = fmaf(g_row, acc.v[i][j][q], scale * lt[q]);
+            const float g = bf16_to_f32(static_cast<bf16_t>(gw[q >> 1] >> ((q & 1) * 16)));
+            duv[q] = dh * (g / (1.0f + expf(-g)));
+          }
+          *reinterpret_cast<float4*>(du32 + row * f + n) = make_float4(duv[0], duv[1], duv[2], duv[3]);
+          continue;
+        }
+        const uint2 uv = *reinterpret_cast<const uint2*>(as + 2 * f);
+        const uint32_t gw[2] = {gv.x, gv.y}, uw[2] = {uv.x, uv.y};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float dh = fmaf(g_row, acc.v[i][j][q], scale * lt[q]);
@@ -416,8 +430,8 @@ struct DguPackedProb {
   }
 };
 
-template <class Cfg, bool LORA>
-__global__ __launch_bounds__(Cfg::THREADS, Cfg::WAVES_PER_SIMD) void expert_dgu_dma(DguPackedProb<Cfg, LORA> pb,
+template <class Cfg, bool LORA, bool DU32 = false>
+__global__ __launch_bounds__(Cfg::THREADS, Cfg::WAVES_PER_SIMD) void expert_dgu_dma(DguPackedProb<Cfg, LORA, DU32> pb,
                                                                                    int max_tiles) {
   const int items = ld_uniform(pb.tiles, 2 * max_tiles) * pb.nt;
   persistent_gemm_dma<Cfg>(pb, items, pb.d / Cfg::BK);
@@ -536,6 +550,36 @@ static hipError_t launch_bwd_gemms_cfg(const Ctx& c, const moe_shape_t& s, const
     return hipGetLastError();
   };
   return lo ? dx_launch(std::true_type{}) : dx_launch(std::false_type{});
+}
+
+// The LoRA backward's dU = (g dY W_d + s (dO B_d) A_d) silu(G), fp32 into
+// ws.du, on the packed W_d^T (moe_pack_backward_weights); ws.wproj holds
+// dO B_d and ws.gemm_tiles the row tiles.
+template <class Cfg>
+static hipError_t launch_lora_dh_cfg(const Ctx& c, const moe_shape_t& s, const Workspace& ws, const LoraArgs& lo,
+                                     const bf16_t* dy, const int32_t* row_src, const float* row_gate,
+                                     const int32_t* offsets, const bf16_t* act_save, const bf16_t* dgu_packed,
+                                     int max_tiles) {
+  DguPackedProb<Cfg, true, true> pb{dy, row_src, row_gate, offsets, ws.gemm_tiles, dgu_packed, s.d, s.f,
+                                    (s.f + Cfg::BN - 1) / Cfg::BN, s.e_hi - s.e_lo, ws.wproj, lo.a_down, lo.r,
+                                    lo.scale, act_save, nullptr, ws.du};
+  TimedLaunch tl(MOE_K_LORA_DH, c.stream);
+  hipLaunchKernelGGL((expert_dgu_dma<Cfg, true, true>), dim3(c.num_cus), dim3(Cfg::THREADS), 0, c.stream, pb,
+                     max_tiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_lora_dh_packed(const Ctx& c, const moe_shape_t& s, const Workspace& ws, const LoraArgs& lo,
+                                 const bf16_t* dy, const int32_t* row_src, const float* row_gate,
+                                 const int32_t* offsets, const bf16_t* act_save, const bf16_t* dgu_packed) {
+  const int max_tiles = gemm_max_tiles(s);
+  int64_t per_expert = (int64_t)s.T * s.k / s.E;
+  if (s.capacity > 0 && per_expert > s.capacity) per_expert = s.capacity;
+  if (per_expert >= kWideRowsPerExpert)
+    return launch_lora_dh_cfg<GemmCfgWide>(c, s, ws, lo, dy, row_src, row_gate, offsets, act_save, dgu_packed,
+                                           max_tiles);
+  return launch_lora_dh_cfg<GemmCfg>(c, s, ws, lo, dy, row_src, row_gate, offsets, act_save, dgu_packed,
+                                     max_tiles);
 }
 
 hipError_t launch_bwd_gemms_packed(const Ctx& c, const moe_shape_t& s, const Workspace& ws, const LoraArgs* lo,

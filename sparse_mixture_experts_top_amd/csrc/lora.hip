@@ -490,7 +490,7 @@ hipError_t launch_lora_bwd(const Ctx& c, const moe_shape_t& sh, const Workspace&
                            const LoraArgs& lo, const bf16_t* dy, const int32_t* offsets,
                            const int32_t* row_src, const float* row_gate, const bf16_t* x_rows,
                            const int32_t* x_src, const bf16_t* act_save, const bf16_t* w_down, float* da_up,
-                           float* db_up, float* da_down, float* db_down) {
+                           float* db_up, float* da_down, float* db_down, const bf16_t* dgu_packed) {
   using Cfg = TileCfg<kGemmBM, 128>;
   const int L = sh.e_hi - sh.e_lo;
   const int d = sh.d, f = sh.f, r = lo.r;
@@ -504,7 +504,9 @@ hipError_t launch_lora_bwd(const Ctx& c, const moe_shape_t& sh, const Workspace&
   MOE_TRY(launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, x_rows, d, x_src, nullptr, d, lo.a_up, true, r, ws.zu));
   MOE_TRY(launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, H, 3 * f, nullptr, nullptr, f, lo.a_down, true, r, ws.zd));
   MOE_TRY(launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, dy, d, row_src, row_gate, d, lo.b_down, false, r, ws.wproj, ws.lora_mt));
-  {
+  if (dgu_packed) {
+    MOE_TRY(launch_lora_dh_packed(c, sh, ws, lo, dy, row_src, row_gate, offsets, act_save, dgu_packed));
+  } else {
     TimedLaunch tl(MOE_K_LORA_DH, c.stream);
     DhProb<Cfg> pb{dy, row_src, row_gate, offsets, ws.gemm_tiles, w_down, d, f, (f + Cfg::BN - 1) / Cfg::BN,
                    ws.wproj, lo.a_down, r, lo.scale, act_save, ws.du};

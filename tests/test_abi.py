@@ -114,3 +114,21 @@ def test_backward_entry_points_validate_on_the_host():
                                          None) == B.MOE_ERR_INVALID_ARG                      # no output
     assert lib.moe_router_bwd(ctypes.byref(s), None, fake, fake, fake, 1 << 30,
                               None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_lora_backward_packed_validates_on_the_host():
+    lib = B.lib()
+    fake = ctypes.c_void_p(0x100000)      # never dereferenced: validation fails first
+    lora = B.MoeLora(16, 32.0, 0x100000, 0x100000, 0x100000, 0x100000)
+    bf = shape(dtype=B.MOE_BF16, d=128, f=128)
+    args = [fake] * 13
+    args[7] = None  # dgu_packed
+    assert lib.moe_lora_bwd_packed(ctypes.byref(bf), ctypes.byref(lora), *args, 1 << 30,
+                                   None) == B.MOE_ERR_INVALID_ARG
+    assert b"dgu_packed is NULL" in lib.moe_last_error()
+    # the packed transposes need d, f % 128 == 0 and bf16
+    for bad in (shape(dtype=B.MOE_BF16, d=128, f=64), shape(dtype=B.MOE_F32, d=128, f=128)):
+        assert lib.moe_lora_bwd_packed(ctypes.byref(bad), ctypes.byref(lora), *([fake] * 13), 1 << 30,
+                                       None) == B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_lora_bwd_packed(ctypes.byref(bf), ctypes.byref(lora), *([fake] * 13), 16,
+                                   None) == B.MOE_ERR_WORKSPACE

@@ -267,8 +267,18 @@ def test_lora_forward_backward_and_aux(b_init, x_perm):
                                  act[:, :w.f], act[:, w.f:2 * w.f], to_f64(inp["w_down"]), lo)
     for n in grads:
         assert_close(host(grads[n]), g_ref[n], "bf16", n)
+    # the same gradients with W_d^T packed once (the dH product on the DMA engine)
+    dgu_p = torch.empty((L, w.f, w.d), dtype=torch.bfloat16, device="cuda")
+    B.moe_pack_backward_weights(buf.shape, dev["w_gate"], dev["w_up"], dev["w_down"], dgu_p, None)
+    gp = {n: torch.full_like(g, float("nan")) for n, g in grads.items()}
+    B.moe_lora_bwd_packed(buf.shape, lora, dev["dy"], buf.offsets, buf.row_src, buf.row_gate, xr, xs,
+                          buf.act_save, dgu_p, gp["da_up"], gp["db_up"], gp["da_down"], gp["db_down"], buf.ws)
+    torch.cuda.synchronize()
+    for n in grads:
+        assert_close(host(gp[n]), g_ref[n], "bf16", n + " (packed)")
     if b_init == "zero":
         assert (grads["da_up"] == 0).all() and (grads["da_down"] == 0).all()
+        assert (gp["da_up"] == 0).all() and (gp["da_down"] == 0).all()
         frozen = run_forward(w.replace(lora_r=0), dev, x_perm=x_perm)
         assert torch.equal(frozen.y, buf.y)
 

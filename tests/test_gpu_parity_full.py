@@ -70,6 +70,12 @@ def test_lora_step_full():
     B.moe_lora_bwd(buf.shape, lora, dev["dy"], buf.offsets, buf.row_src, buf.row_gate, xr, xs,
                    buf.act_save, dev["w_down"], grads["da_up"], grads["db_up"], grads["da_down"],
                    grads["db_down"], buf.ws)
+    # the packed variant the benchmark times (W_d^T packed once)
+    dgu_p = torch.empty((L, f, d), dtype=torch.bfloat16, device="cuda")
+    B.moe_pack_backward_weights(buf.shape, dev["w_gate"], dev["w_up"], dev["w_down"], dgu_p, None)
+    gp = {n: torch.full_like(g, float("nan")) for n, g in grads.items()}
+    B.moe_lora_bwd_packed(buf.shape, lora, dev["dy"], buf.offsets, buf.row_src, buf.row_gate, xr, xs,
+                          buf.act_save, dgu_p, gp["da_up"], gp["db_up"], gp["da_down"], gp["db_down"], buf.ws)
     torch.cuda.synchronize()
     offsets = host(buf.offsets)
     dy64 = to_f64(inp["dy"])
@@ -85,3 +91,4 @@ def test_lora_step_full():
         say(f"  expert {le}: {b - a} rows")
         for n in grads:
             assert_close(host(grads[n][le:le + 1]), g_ref[n], "bf16", f"{n}[{le}]")
+            assert_close(host(gp[n][le:le + 1]), g_ref[n], "bf16", f"{n}[{le}] (packed)")
