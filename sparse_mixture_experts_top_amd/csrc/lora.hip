@@ -127,14 +127,16 @@ __device__ __forceinline__ void frag_load(const float* p, bf16x8& hi, bf16x8& lo
 }
 
 // out[p, q] = scale_p * in[src_p] . Mt[le][q] for q < r <= 16 on the matrix
-// cores. One workgroup per 16 consecutive dispatched rows; its 4 waves take
-// the K steps of 32 in turn (wave w: steps w, w + 4, ...) and their 16 x 16
+// cores. One workgroup per 16 consecutive dispatched rows; its 8 waves take
+// the K steps of 32 in turn (wave w: steps w, w + 8, ...) and their 16 x 16
 // partial sums are added in wave order through LDS. A group that spans an
 // expert boundary is computed once per expert it touches, each pass storing
 // that expert's rows. Lane l supplies row l % 16 of the in-rows and of Mt
 // (ranks) at K offset 8 (l / 16) and receives rows 4 (l / 16) + i, rank l % 16.
+constexpr int kProjWaves = 8;
+
 template <class TIn>
-__global__ __launch_bounds__(256) void lora_proj_mfma(int L, const int32_t* __restrict__ offsets,
+__global__ __launch_bounds__(64 * kProjWaves) void lora_proj_mfma(int L, const int32_t* __restrict__ offsets,
                                                       const TIn* __restrict__ in, int64_t in_stride,
                                                       const int32_t* __restrict__ src,
                                                       const float* __restrict__ row_scale, int K,
@@ -142,7 +144,7 @@ __global__ __launch_bounds__(256) void lora_proj_mfma(int L, const int32_t* __re
                                                       float* __restrict__ out) {
   constexpr bool kSplit = sizeof(TIn) == 4;
   constexpr int U = 4;  // K steps per load batch
-  __shared__ f32x4 part[4][64];
+  __shared__ f32x4 part[kProjWaves][64];
   const int R = ld_uniform(offsets, L);
   const int p0 = blockIdx.x * 16;
   if (p0 >= R) return;
@@ -160,11 +162,11 @@ __global__ __launch_bounds__(256) void lora_proj_mfma(int L, const int32_t* __re
     if (seg0 == seg1) continue;  // wave-uniform
     const bf16_t* b_ptr = Mt + ((int64_t)le * r + min(row, r - 1)) * K + kc * 8;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = wave; s0 < nsteps; s0 += 4 * U) {
+    for (int s0 = wave; s0 < nsteps; s0 += kProjWaves * U) {
       bf16x8 ah[U], al[U], b[U];
 #pragma unroll
       for (int j = 0; j < U; ++j) {
-        const int st = s0 + 4 * j;
+        const int st = s0 + kProjWaves * j;
         if (st < nsteps) {
           frag_load(a_ptr + (int64_t)st * 32, ah[j], al[j], kSplit);
           b[j] = *reinterpret_cast<const bf16x8*>(b_ptr + (int64_t)st * 32);
@@ -172,7 +174,7 @@ __global__ __launch_bounds__(256) void lora_proj_mfma(int L, const int32_t* __re
       }
 #pragma unroll
       for (int j = 0; j < U; ++j) {
-        if (s0 + 4 * j < nsteps) {
+        if (s0 + kProjWaves * j < nsteps) {
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[j], b[j], acc, 0, 0, 0);
           if constexpr (kSplit) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[j], b[j], acc, 0, 0, 0);
         }
@@ -181,7 +183,9 @@ __global__ __launch_bounds__(256) void lora_proj_mfma(int L, const int32_t* __re
     part[wave][lane] = acc;
     __syncthreads();
     if (wave == 0) {
-      const f32x4 t = part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane];
+      f32x4 t = part[0][lane];
+#pragma unroll
+      for (int w = 1; w < kProjWaves; ++w) t += part[w][lane];
       const int q = lane & 15;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -215,7 +219,8 @@ hipError_t launch_lora_rowproj(const Ctx& c, int L, const int32_t* offsets, int6
                          mt);
       M = mt;
     }
-    hipLaunchKernelGGL(lora_proj_mfma<TIn>, dim3((unsigned)((rmax_rows + 15) / 16)), dim3(256), 0, c.stream, L,
+    hipLaunchKernelGGL(lora_proj_mfma<TIn>, dim3((unsigned)((rmax_rows + 15) / 16)), dim3(64 * kProjWaves), 0,
+                       c.stream, L,
                        offsets, in, in_stride, src, row_scale, K, M, r, out);
     return hipGetLastError();
   }
@@ -288,14 +293,14 @@ __global__ __launch_bounds__(256) void lora_seg_outer(const int32_t* __restrict_
 }
 
 // Same sums for r <= 16 and C % 4 == 0, with the rows spread over the
-// workgroup: one workgroup per (256 columns, expert), 8 waves, wave w taking
-// the expert's rows w, w + 8, ... in order, each lane 4 consecutive columns
-// x 16 ranks in registers. A row's P values are wave-uniform (one scalar
-// load of 16 floats); four rows' loads are issued before their FMAs. The
-// 8 waves' partial sums are then added in wave order through LDS, so the
+// workgroup: one workgroup per (256 columns, expert), 16 waves, wave w taking
+// the expert's rows w, w + 16, ... in order, each lane 4 consecutive columns
+// x 16 ranks in registers. Rows go in batches of 4: a batch's loads (its
+// rows of `in` and its 4 x 16 P values, one per lane) are issued before the
+// previous batch's FMAs; the source rows and row scales come 64 rows at a
+// time in one vector load and are read per row with readlane. The 16 waves'
+// partial sums are then added in a fixed tree order through LDS, so the
 // result does not depend on timing.
-typedef float f32x16_t __attribute__((ext_vector_type(16), aligned(4)));
-typedef const __attribute__((address_space(4))) f32x16_t* const_f32x16_ptr_t;
 typedef const __attribute__((address_space(4))) float* const_f32_ptr_t;
 
 template <class TIn> struct Vec4;
@@ -315,17 +320,18 @@ template <> struct Vec4<float> {
   }
 };
 
-constexpr int kSegWaves = 8;   // waves per workgroup
+constexpr int kSegWaves = 16;  // waves per workgroup
 constexpr int kSegCols = 256;  // columns per workgroup (4 per lane)
 constexpr int kSegRq = 16;     // ranks held per lane
+constexpr int kSegSlots = 8;   // LDS partial-sum slots of the reduction tree
 
 template <class TIn>
 __global__ __launch_bounds__(64 * kSegWaves) void lora_seg_outer16(
     const int32_t* __restrict__ offsets, const float* __restrict__ P, int r, const TIn* __restrict__ in,
     int64_t in_stride, const int32_t* __restrict__ qsrc, const float* __restrict__ qscale, int C, float s,
     int out_qc, float* __restrict__ out) {
-  constexpr int B = 4;  // rows per load batch
-  __shared__ float red[kSegWaves][kSegRq][kSegCols];
+  constexpr int B = 4;  // rows per batch
+  __shared__ float red[kSegSlots][kSegRq][kSegCols];
   const int le = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -333,62 +339,90 @@ __global__ __launch_bounds__(64 * kSegWaves) void lora_seg_outer16(
   const int c0 = cb + lane * 4;
   const bool cok = c0 < C;
   const int a = ld_uniform(offsets, le), b = ld_uniform(offsets, le + 1);
+  // this wave's rows: a + wave + kSegWaves m, m < M
+  const int M = b - a > wave ? (b - a - wave + kSegWaves - 1) / kSegWaves : 0;
   float acc[kSegRq][4];
 #pragma unroll
   for (int q = 0; q < kSegRq; ++q)
 #pragma unroll
     for (int u = 0; u < 4; ++u) acc[q][u] = 0.f;
-  for (int p0 = a + wave; p0 < b; p0 += kSegWaves * B) {
-    float v[B][4];
-    f32x16_t pr[B];
-#pragma unroll
-    for (int j = 0; j < B; ++j) {
-      const int p = p0 + j * kSegWaves;  // wave-uniform
-      if (p < b) {
-        const int64_t src = qsrc ? (int64_t)ld_uniform(qsrc, p) : (int64_t)p;
-        const float sc = qscale ? ((const_f32_ptr_t)qscale)[p] : 1.f;
-        if (cok) {
-          Vec4<TIn>::load(in + src * in_stride + c0, v[j]);
-        } else {
-          v[j][0] = v[j][1] = v[j][2] = v[j][3] = 0.f;
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) v[j][u] *= sc;
-        if (r == kSegRq) {
-          pr[j] = *(const_f32x16_ptr_t)(P + (int64_t)p * r);
-        } else {
-#pragma unroll
-          for (int q = 0; q < kSegRq; ++q) pr[j][q] = q < r ? ((const_f32_ptr_t)P)[(int64_t)p * r + q] : 0.f;
-        }
-      } else {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) v[j][u] = 0.f;
-#pragma unroll
-        for (int q = 0; q < kSegRq; ++q) pr[j][q] = 0.f;
+  const int jp = lane >> 4, qp = lane & 15;  // P value this lane fetches: row jp of a batch, rank qp
+  int srcv = 0;      // lane l: source row of window row l (64 rows per window)
+  float sclv = 1.f;  // lane l: its scale
+  float vc[B][4], vn[B][4], pc = 0.f, pn = 0.f;
+  for (int m0 = 0; m0 < M + B; m0 += B) {
+    // fetch batch m0 (if any) into (vn, pn) while batch m0 - B, in (vc, pc), is consumed
+    if (m0 < M) {
+      if ((m0 & 63) == 0) {
+        const int m = m0 + lane;
+        const int p = a + wave + kSegWaves * m;
+        srcv = m < M ? (qsrc ? qsrc[p] : p) : 0;
+        sclv = (m < M && qscale) ? qscale[p] : 1.f;
       }
+      const int mp = m0 + jp;
+      pn = (mp < M && qp < r) ? P[(int64_t)(a + wave + kSegWaves * mp) * r + qp] : 0.f;
+#pragma unroll
+      for (int j = 0; j < B; ++j) {
+        const int src = __builtin_amdgcn_readlane(srcv, (m0 + j) & 63);
+        if (m0 + j < M && cok) {
+          Vec4<TIn>::load(in + (int64_t)src * in_stride + c0, vn[j]);
+        } else {
+          vn[j][0] = vn[j][1] = vn[j][2] = vn[j][3] = 0.f;
+        }
+        // fold the row scale in right away (rows past M have scale 1 and zeros)
+        const float sc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sclv),
+                                                                             (m0 + j) & 63));
+#pragma unroll
+        for (int u = 0; u < 4; ++u) vn[j][u] *= sc;
+      }
+    }
+    if (m0 > 0) {
+#pragma unroll
+      for (int j = 0; j < B; ++j)
+#pragma unroll
+        for (int q = 0; q < kSegRq; ++q) {
+          const float pq = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pc), 16 * j + q));
+#pragma unroll
+          for (int u = 0; u < 4; ++u) acc[q][u] = fmaf(pq, vc[j][u], acc[q][u]);
+        }
     }
 #pragma unroll
     for (int j = 0; j < B; ++j)
 #pragma unroll
-      for (int q = 0; q < kSegRq; ++q)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) acc[q][u] = fmaf(pr[j][q], v[j][u], acc[q][u]);
+      for (int u = 0; u < 4; ++u) vc[j][u] = vn[j][u];
+    pc = pn;
   }
+  // fixed-order tree over the waves: 16 -> 8 -> 4 -> 2 -> 1
+  for (int half = kSegWaves / 2; half >= 1; half >>= 1) {
+    if (wave >= half && wave < 2 * half) {
 #pragma unroll
-  for (int q = 0; q < kSegRq; ++q)
-    *reinterpret_cast<float4*>(&red[wave][q][lane * 4]) = make_float4(acc[q][0], acc[q][1], acc[q][2], acc[q][3]);
-  __syncthreads();
-  // outputs of this workgroup: kSegRq x kSegCols, each the sum over the waves in order
-  for (int o = threadIdx.x; o < kSegRq * kSegCols; o += 64 * kSegWaves) {
-    // [L, r, C]: column fastest; [L, C, r]: rank fastest (coalesced stores either way)
-    const int q = out_qc ? o / kSegCols : o % kSegRq;
-    const int cc = out_qc ? o % kSegCols : o / kSegRq;
-    if (q >= r || cb + cc >= C) continue;
-    float t = 0.f;
+      for (int q = 0; q < kSegRq; ++q)
+        *reinterpret_cast<float4*>(&red[wave - half][q][lane * 4]) =
+            make_float4(acc[q][0], acc[q][1], acc[q][2], acc[q][3]);
+    }
+    __syncthreads();
+    if (wave < half) {
 #pragma unroll
-    for (int w = 0; w < kSegWaves; ++w) t += red[w][q][cc];
-    if (out_qc) out[((int64_t)le * r + q) * C + cb + cc] = s * t;
-    else out[((int64_t)le * C + cb + cc) * r + q] = s * t;
+      for (int q = 0; q < kSegRq; ++q) {
+        const float4 o = *reinterpret_cast<const float4*>(&red[wave][q][lane * 4]);
+        acc[q][0] += o.x; acc[q][1] += o.y; acc[q][2] += o.z; acc[q][3] += o.w;
+      }
+    }
+    __syncthreads();
+  }
+  if (wave != 0 || !cok) return;
+  if (out_qc) {
+#pragma unroll
+    for (int q = 0; q < kSegRq; ++q)
+      if (q < r)
+        *reinterpret_cast<float4*>(out + ((int64_t)le * r + q) * C + c0) =
+            make_float4(s * acc[q][0], s * acc[q][1], s * acc[q][2], s * acc[q][3]);
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int q = 0; q < kSegRq; ++q)
+        if (q < r) out[((int64_t)le * C + c0 + u) * r + q] = s * acc[q][u];
   }
 }
 
