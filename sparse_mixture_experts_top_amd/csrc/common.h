@@ -173,6 +173,7 @@ struct Workspace {
   float* vproj;          // [Rmax, rmax] LoRA dU B_up
   float* du;             // [Rmax, f]   LoRA backward dU (f32)
   bf16_t* lora_mt;       // [L, r, max(d, f)] a [K, r] adapter transposed for the rank-r projections
+  bf16_t* zx;            // [Rmax, 2r] s Z as bf16 high | low parts (the extra adapter K step)
   float* logits;         // [T, E]
   float* prob_part;      // [prob_blocks, E]
   int64_t bytes;
@@ -270,10 +271,15 @@ hipError_t launch_router_bwd(const Ctx& c, const moe_shape_t& s, const Workspace
 //   mt:   scratch of L * r * K bf16 for M transposed to [L, r, K] when it is
 //         stored [L, K, r] (the matrix-core path reads K-contiguous rows), or
 //         NULL (then such an M takes the plain per-row path)
+//   out_hl: if not NULL, hl_scale * out is written there instead of out, as
+//         [rows, 2r] bf16: the bf16 rounding in columns [0, r) and the bf16
+//         rounding of the remainder in [r, 2r) (matrix-core path only;
+//         hipErrorInvalidValue otherwise)
 template <class TIn>
 hipError_t launch_lora_rowproj(const Ctx& c, int L, const int32_t* offsets, int64_t rmax_rows,
                                const TIn* in, int64_t in_stride, const int32_t* src,
                                const float* row_scale, int K, const bf16_t* M, bool m_qk, int r,
-                               float* out, bf16_t* mt = nullptr);
+                               float* out, bf16_t* mt = nullptr, bf16_t* out_hl = nullptr,
+                               float hl_scale = 1.f);
 
 }  // namespace moe

@@ -80,6 +80,9 @@ __global__ __launch_bounds__(1024) void build_row_tiles(const int32_t* __restric
   if (le == 0) tiles[2 * max_tiles] = total;
 }
 
+// 64 bytes of zeros: the B rows of gate columns in the extra adapter K step.
+__device__ __align__(64) bf16_t kLoraZeroRow[32] = {};
+
 // Row-tile item of a grouped GEMM: expert, first row of the tile, rows valid.
 struct RowTile {
   int le, r0, valid;
@@ -128,10 +131,14 @@ __device__ __forceinline__ int64_t gathered_row(const int32_t* row_src, const Ro
 // K8: H = silu(X W_g^T) * (X W_u^T [+ s Z_u B_u^T]) for one (row tile, 128
 // FFN columns) item. Rows of X are x[row_src[p]] (gather fused into the A
 // loader) or, with row_src == NULL, x[p] of an already gathered matrix.
-// LORA: the epilogue adds the rank-r adapter term (a separate instantiation,
-// so the plain kernels carry no adapter code).
-template <class Cfg, bool LORA = false>
+// LORA (a separate instantiation each, so the plain kernels carry no adapter
+// code): 0 none; 1 the epilogue adds the rank-r adapter term in fp32;
+// 2 (r = 16) one extra K step carries it through the matrix cores: A = the
+// row's s Z as bf16 high and low parts (zx, 32 per row), B = the adapter row
+// twice (high and low parts meet the same values), zeros for gate columns.
+template <class Cfg, int LORA = 0>
 struct GateUpProb {
+  static constexpr int kExtra = LORA == 2 ? 1 : 0;
   const bf16_t* x;
   const int32_t* row_src;
   const int32_t* offsets;
@@ -146,6 +153,7 @@ struct GateUpProb {
   float scale;
   bf16_t* hbuf;
   bf16_t* act_save;
+  const bf16_t* zx = nullptr;  // LORA == 2: [Rmax, 32] s Z_u high | low
   static constexpr int HALF = Cfg::BN / 2;  // FFN columns per item (the last item may be partial)
 
   __device__ __forceinline__ int rows(int item) const {
@@ -187,6 +195,23 @@ struct GateUpProb {
     }
   }
 
+  // LORA == 2: pointers of the extra K step (see above)
+  __device__ __forceinline__ void setup_extra(int item, DmaLoader<Cfg>& ld, int part) const {
+    const RowTile t = row_tile<Cfg::BM>(tiles, offsets, item / nt);
+    const int ni = item % nt;
+    const int ce = dma_chunk_elem<Cfg>();
+#pragma unroll
+    for (int q = 0; q < Cfg::A_DMA / Cfg::DW; ++q)
+      ld.a[q] = zx + (t.row0 + min(dma_row<Cfg>(q * Cfg::DW + part), t.valid - 1)) * 32 + ce;
+#pragma unroll
+    for (int q = 0; q < Cfg::B_DMA / Cfg::DW; ++q) {
+      const int jb = dma_row<Cfg>(q * Cfg::DW + part);
+      const int frag = jb >> 4;
+      const int fcol = min(ni * HALF + (frag >> 1) * 16 + (jb & 15), f - 1);
+      ld.b[q] = (frag & 1) ? b_up + ((int64_t)t.le * f + fcol) * 16 + (ce & 8) : kLoraZeroRow;
+    }
+  }
+
   __device__ __forceinline__ void epilogue(int item, Acc<Cfg>& acc) const {
     const RowTile t = row_tile<Cfg::BM>(tiles, offsets, item / nt);
     const int ni = item % nt;
@@ -207,14 +232,14 @@ struct GateUpProb {
         if (ni * HALF + (jg >> 1) * 16 >= f) continue;
         const int fcol = ni * HALF + (jg >> 1) * 16 + (lane >> 4) * 4;
         float h[4], g[4], uu[4], lt[4] = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (LORA) {
+        if constexpr (LORA == 1) {
           if (ok) lora_term_rows(zu + row * r, b_up + ((int64_t)t.le * f + fcol) * r, r, lt);
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           g[q] = acc.v[i][jj][q];
           float u = acc.v[i][jj + 1][q];
-          if constexpr (LORA) u = fmaf(scale, lt[q], u);
+          if constexpr (LORA == 1) u = fmaf(scale, lt[q], u);
           uu[q] = u;
           h[q] = silu_f(g[q]) * u;
         }
@@ -233,17 +258,21 @@ struct GateUpProb {
   }
 };
 
-template <class Cfg, bool LORA>
+template <class Cfg, int LORA>
 __global__ __launch_bounds__(Cfg::THREADS, Cfg::WAVES_PER_SIMD) void gate_up_bf16(GateUpProb<Cfg, LORA> pb, int max_tiles) {
   const int items = ld_uniform(pb.tiles, 2 * max_tiles) * pb.nt;
   persistent_gemm_dma<Cfg>(pb, items, pb.d / Cfg::BK);
 }
 
 // K9: O = H W_d^T [+ s Z_d B_d^T] for one (row tile, 256 output columns) item.
-// LORA: the epilogue adds the rank-r adapter term (a separate instantiation,
-// so the plain kernels carry no adapter code).
-template <class Cfg, bool LORA = false>
+// LORA (a separate instantiation each, so the plain kernels carry no adapter
+// code): 0 none; 1 the epilogue adds the rank-r adapter term in fp32;
+// 2 (r = 16) one extra K step carries it through the matrix cores: A = the
+// row's s Z as bf16 high and low parts (zx, 32 per row), B = the adapter row
+// twice (high and low parts meet the same values), zeros for gate columns.
+template <class Cfg, int LORA = 0>
 struct DownProb {
+  static constexpr int kExtra = LORA == 2 ? 1 : 0;
   const bf16_t* hbuf;
   const int32_t* offsets;
   const int32_t* tiles;
@@ -255,6 +284,7 @@ struct DownProb {
   int r;
   float scale;
   bf16_t* y_perm;
+  const bf16_t* zx = nullptr;  // LORA == 2: [Rmax, 32] s Z_d high | low
 
   __device__ __forceinline__ int rows(int item) const {
     return row_tile<Cfg::BM>(tiles, offsets, item / nt).valid;
@@ -287,6 +317,21 @@ struct DownProb {
       ld.b[q] = w_down + ((int64_t)t.le * d + min(n0 + dma_row<Cfg>(q * Cfg::DW + part), d - 1)) * f + ce;
   }
 
+  // LORA == 2: pointers of the extra K step (see GateUpProb)
+  __device__ __forceinline__ void setup_extra(int item, DmaLoader<Cfg>& ld, int part) const {
+    const RowTile t = row_tile<Cfg::BM>(tiles, offsets, item / nt);
+    const int n0 = (item % nt) * Cfg::BN;
+    const int ce = dma_chunk_elem<Cfg>();
+#pragma unroll
+    for (int q = 0; q < Cfg::A_DMA / Cfg::DW; ++q)
+      ld.a[q] = zx + (t.row0 + min(dma_row<Cfg>(q * Cfg::DW + part), t.valid - 1)) * 32 + ce;
+#pragma unroll
+    for (int q = 0; q < Cfg::B_DMA / Cfg::DW; ++q) {
+      const int n = min(n0 + dma_row<Cfg>(q * Cfg::DW + part), d - 1);
+      ld.b[q] = b_down + ((int64_t)t.le * d + n) * 16 + (ce & 8);
+    }
+  }
+
   __device__ __forceinline__ void epilogue(int item, Acc<Cfg>& acc) const {
     const RowTile t = row_tile<Cfg::BM>(tiles, offsets, item / nt);
     const int n0 = (item % nt) * Cfg::BN;
@@ -305,13 +350,13 @@ struct DownProb {
         if (n0 + wn * (Cfg::BN / Cfg::WN) + j * 16 >= d) continue;
         const int n = n0 + dma_out_col<Cfg>(wn, j, lane);
         float o[4], lt[4] = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (LORA) {
+        if constexpr (LORA == 1) {
           if (ok) lora_term_rows(zd + row * r, b_down + ((int64_t)t.le * d + n) * r, r, lt);
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           o[q] = acc.v[i][j][q];
-          if constexpr (LORA) o[q] = fmaf(scale, lt[q], o[q]);
+          if constexpr (LORA == 1) o[q] = fmaf(scale, lt[q], o[q]);
         }
         if (ok) *reinterpret_cast<uint2*>(y_perm + row * d + n) = pack4_bf16(o[0], o[1], o[2], o[3]);
       }
@@ -319,7 +364,7 @@ struct DownProb {
   }
 };
 
-template <class Cfg, bool LORA>
+template <class Cfg, int LORA>
 __global__ __launch_bounds__(Cfg::THREADS, Cfg::WAVES_PER_SIMD) void down_bf16(DownProb<Cfg, LORA> pb, int max_tiles) {
   const int items = ld_uniform(pb.tiles, 2 * max_tiles) * pb.nt;
   persistent_gemm_dma<Cfg>(pb, items, pb.f / Cfg::BK);
@@ -855,7 +900,7 @@ hipError_t launch_grouped_bf16(const Ctx& c, const moe_shape_t& s, const Workspa
                                const int32_t* row_src, const int32_t* offsets, const void* gu_packed,
                                const void* d_packed, const void* w_gate, const void* w_up,
                                const void* w_down, const LoraArgs* lora, void* act_save, void* y_perm,
-                               int max_tiles);
+                               int max_tiles, int lora_mode);
 
 hipError_t launch_expert_gemm(const Ctx& c, const moe_shape_t& s, const Workspace& ws,
                               const void* x_rows, const int32_t* row_src, const int32_t* offsets,
@@ -882,9 +927,16 @@ hipError_t launch_expert_gemm(const Ctx& c, const moe_shape_t& s, const Workspac
   const int max_tiles = gemm_max_tiles(s);
   if ((err = launch_row_tiles(c, offsets, L, max_tiles, ws.gemm_tiles)) != hipSuccess) return err;
   const bf16_t* xr = (const bf16_t*)x_rows;
+  // adapter terms: through the matrix cores as one extra K step at r = 16
+  // (the projection's matrix-core path applies: d, f % 32 == 0), else in
+  // the epilogues
+  const int lora_mode = !lora ? 0 : (lora->r == 16 && s.d % 32 == 0 && s.f % 32 == 0 && ws.zx) ? 2 : 1;
   if (lora) {
-    err = launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, xr, s.d, row_src, nullptr, s.d,
-                                      lora->a_up, true, lora->r, ws.zu);
+    err = lora_mode == 2
+              ? launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, xr, s.d, row_src, nullptr, s.d, lora->a_up, true,
+                                            lora->r, nullptr, nullptr, ws.zx, lora->scale)
+              : launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, xr, s.d, row_src, nullptr, s.d, lora->a_up, true,
+                                            lora->r, ws.zu);
     if (err != hipSuccess) return err;
   }
   const int64_t tk = (int64_t)s.T * s.k;
@@ -892,9 +944,9 @@ hipError_t launch_expert_gemm(const Ctx& c, const moe_shape_t& s, const Workspac
   if (s.capacity > 0 && per_expert > s.capacity) per_expert = s.capacity;
   if (per_expert >= kWideRowsPerExpert)
     return launch_grouped_bf16<GemmCfgWide>(c, s, ws, xr, row_src, offsets, gu_packed, d_packed, w_gate,
-                                            w_up, w_down, lora, act_save, y_perm, max_tiles);
+                                            w_up, w_down, lora, act_save, y_perm, max_tiles, lora_mode);
   return launch_grouped_bf16<GemmCfg>(c, s, ws, xr, row_src, offsets, gu_packed, d_packed, w_gate, w_up,
-                                      w_down, lora, act_save, y_perm, max_tiles);
+                                      w_down, lora, act_save, y_perm, max_tiles, lora_mode);
 }
 
 template <class Cfg>
@@ -902,41 +954,51 @@ hipError_t launch_grouped_bf16(const Ctx& c, const moe_shape_t& s, const Workspa
                                const int32_t* row_src, const int32_t* offsets, const void* gu_packed,
                                const void* d_packed, const void* w_gate, const void* w_up,
                                const void* w_down, const LoraArgs* lora, void* act_save, void* y_perm,
-                               int max_tiles) {
+                               int max_tiles, int lora_mode) {
   hipError_t err;
   const int L = s.e_hi - s.e_lo;
   const int64_t rmax = max_rows(s);
   const int grid = c.num_cus;  // one workgroup per CU (see mfma_tile.h)
-  auto gu_launch = [&](auto with_lora) {
-    constexpr bool LO = decltype(with_lora)::value;
+  auto gu_launch = [&](auto mode) {
+    constexpr int LO = decltype(mode)::value;
     using P = GateUpProb<Cfg, LO>;
     P pb{xr, row_src, offsets, ws.gemm_tiles, (const bf16_t*)w_gate,
          (const bf16_t*)w_up, (const bf16_t*)gu_packed, s.d, s.f,
          (s.f + P::HALF - 1) / P::HALF, s.e_hi - s.e_lo,
          lora ? ws.zu : nullptr, lora ? lora->b_up : nullptr, lora ? lora->r : 0,
          lora ? lora->scale : 0.f, (bf16_t*)ws.hbuf, (bf16_t*)act_save};
+    pb.zx = ws.zx;
     TimedLaunch tl(MOE_K_GATE_UP, c.stream);
     hipLaunchKernelGGL((gate_up_bf16<Cfg, LO>), dim3(grid), dim3(Cfg::THREADS), 0, c.stream, pb, max_tiles);
     return hipGetLastError();
   };
-  if ((err = lora ? gu_launch(std::true_type{}) : gu_launch(std::false_type{})) != hipSuccess) return err;
+  err = lora_mode == 2   ? gu_launch(std::integral_constant<int, 2>{})
+        : lora_mode == 1 ? gu_launch(std::integral_constant<int, 1>{})
+                         : gu_launch(std::integral_constant<int, 0>{});
+  if (err != hipSuccess) return err;
   if (lora) {
-    err = launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, (const bf16_t*)ws.hbuf, s.f, nullptr,
-                                      nullptr, s.f, lora->a_down, true, lora->r, ws.zd);
+    err = lora_mode == 2 ? launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, (const bf16_t*)ws.hbuf, s.f, nullptr,
+                                                       nullptr, s.f, lora->a_down, true, lora->r, nullptr,
+                                                       nullptr, ws.zx, lora->scale)
+                         : launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, (const bf16_t*)ws.hbuf, s.f, nullptr,
+                                                       nullptr, s.f, lora->a_down, true, lora->r, ws.zd);
     if (err != hipSuccess) return err;
   }
-  auto dn_launch = [&](auto with_lora) {
-    constexpr bool LO = decltype(with_lora)::value;
+  auto dn_launch = [&](auto mode) {
+    constexpr int LO = decltype(mode)::value;
     DownProb<Cfg, LO> pb{(const bf16_t*)ws.hbuf, offsets, ws.gemm_tiles, (const bf16_t*)w_down,
                          (const bf16_t*)d_packed, s.d, s.f,
                          (s.d + Cfg::BN - 1) / Cfg::BN, lora ? ws.zd : nullptr,
                          lora ? lora->b_down : nullptr, lora ? lora->r : 0, lora ? lora->scale : 0.f,
                          (bf16_t*)y_perm};
+    pb.zx = ws.zx;
     TimedLaunch tl(MOE_K_DOWN, c.stream);
     hipLaunchKernelGGL((down_bf16<Cfg, LO>), dim3(grid), dim3(Cfg::THREADS), 0, c.stream, pb, max_tiles);
     return hipGetLastError();
   };
-  return lora ? dn_launch(std::true_type{}) : dn_launch(std::false_type{});
+  return lora_mode == 2   ? dn_launch(std::integral_constant<int, 2>{})
+         : lora_mode == 1 ? dn_launch(std::integral_constant<int, 1>{})
+                          : dn_launch(std::integral_constant<int, 0>{});
 }
 
 }  // namespace moe

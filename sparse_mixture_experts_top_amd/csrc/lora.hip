@@ -141,7 +141,8 @@ __global__ __launch_bounds__(64 * kProjWaves) void lora_proj_mfma(int L, const i
                                                       const int32_t* __restrict__ src,
                                                       const float* __restrict__ row_scale, int K,
                                                       const bf16_t* __restrict__ Mt, int r,
-                                                      float* __restrict__ out) {
+                                                      float* __restrict__ out, bf16_t* __restrict__ out_hl,
+                                                      float hl_scale) {
   constexpr bool kSplit = sizeof(TIn) == 4;
   constexpr int U = 4;  // K steps per load batch
   __shared__ f32x4 part[kProjWaves][64];
@@ -190,7 +191,18 @@ __global__ __launch_bounds__(64 * kProjWaves) void lora_proj_mfma(int L, const i
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int p = p0 + 4 * kc + i;
-        if (q < r && p >= seg0 && p < seg1) out[(int64_t)p * r + q] = (row_scale ? row_scale[p] : 1.f) * t[i];
+        if (q < r && p >= seg0 && p < seg1) {
+          const float v = (row_scale ? row_scale[p] : 1.f) * t[i];
+          if (out_hl) {
+            // hl_scale v as a bf16 high part and the bf16 rounding of the rest
+            const float sv = hl_scale * v;
+            const bf16_t hi = f32_to_bf16(sv);
+            out_hl[(int64_t)p * 2 * r + q] = hi;
+            out_hl[(int64_t)p * 2 * r + r + q] = f32_to_bf16(sv - bf16_to_f32(hi));
+          } else {
+            out[(int64_t)p * r + q] = v;
+          }
+        }
       }
     }
     __syncthreads();
@@ -210,8 +222,9 @@ template <class TIn>
 hipError_t launch_lora_rowproj(const Ctx& c, int L, const int32_t* offsets, int64_t rmax_rows,
                                const TIn* in, int64_t in_stride, const int32_t* src,
                                const float* row_scale, int K, const bf16_t* M, bool m_qk, int r,
-                               float* out, bf16_t* mt) {
-  if (r <= 16 && K % 32 == 0 && in_stride % 8 == 0 && (m_qk || mt) && rmax_rows > 0) {
+                               float* out, bf16_t* mt, bf16_t* out_hl, float hl_scale) {
+  if (rmax_rows <= 0) return hipSuccess;
+  if (r <= 16 && K % 32 == 0 && in_stride % 8 == 0 && (m_qk || mt)) {
     TimedLaunch tl(MOE_K_LORA_PROJ, c.stream);
     if (!m_qk) {
       const int64_t n = (int64_t)L * K;
@@ -221,9 +234,10 @@ hipError_t launch_lora_rowproj(const Ctx& c, int L, const int32_t* offsets, int6
     }
     hipLaunchKernelGGL(lora_proj_mfma<TIn>, dim3((unsigned)((rmax_rows + 15) / 16)), dim3(64 * kProjWaves), 0,
                        c.stream, L,
-                       offsets, in, in_stride, src, row_scale, K, M, r, out);
+                       offsets, in, in_stride, src, row_scale, K, M, r, out, out_hl, hl_scale);
     return hipGetLastError();
   }
+  if (out_hl) return hipErrorInvalidValue;  // the high/low output exists on the matrix-core path only
   const int64_t want = (rmax_rows + 3) / 4;
   const int grid = (int)(want < (int64_t)c.num_cus * 8 ? (want > 0 ? want : 1) : (int64_t)c.num_cus * 8);
   TimedLaunch tl(MOE_K_LORA_PROJ, c.stream);
@@ -240,10 +254,11 @@ hipError_t launch_lora_rowproj(const Ctx& c, int L, const int32_t* offsets, int6
 template hipError_t launch_lora_rowproj<bf16_t>(const Ctx&, int, const int32_t*, int64_t,
                                                 const bf16_t*, int64_t, const int32_t*,
                                                 const float*, int, const bf16_t*, bool, int, float*,
-                                                bf16_t*);
+                                                bf16_t*, bf16_t*, float);
 template hipError_t launch_lora_rowproj<float>(const Ctx&, int, const int32_t*, int64_t,
                                                const float*, int64_t, const int32_t*, const float*,
-                                               int, const bf16_t*, bool, int, float*, bf16_t*);
+                                               int, const bf16_t*, bool, int, float*, bf16_t*, bf16_t*,
+                                               float);
 
 // out[le] = s * sum_{p in rows of le} P[p, q] * qscale_p * in[qsrc_p, c], for
 // q < r, c < C; stored [L, r, C] (out_qc) or [L, C, r].

@@ -12,6 +12,8 @@
 // results C[4 * (l / 16) + i][l % 16], i = 0..3.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
@@ -539,12 +541,25 @@ __device__ __forceinline__ void dma_wait_stage(int younger) {
   }
 }
 
+// Extra K steps a problem appends to each item (Prob::kExtra, default 0):
+// stages whose operands come from a second loader filled by
+// Prob::setup_extra(item, ld, part), e.g. a rank-r adapter term carried
+// through the matrix cores after the item's nk main steps.
+template <class P, class = void>
+struct ExtraSteps {
+  static constexpr int value = 0;
+};
+template <class P>
+struct ExtraSteps<P, std::void_t<decltype(P::kExtra)>> {
+  static constexpr int value = P::kExtra;
+};
+
 // Persistent warp-specialised driver on the DMA ring. Items are processed in
 // order; Prob::rows(item) gives an item's valid tile rows (row fragments past
 // them skip their MFMAs), Prob::setup(item, ld, part) fills producer part's
 // DmaLoader, Prob::epilogue(item, acc) writes an item's result (compute
 // waves). K steps are numbered g = 0 .. total-1 over the workgroup's items
-// (nk per item, nk even). Barrier "-1" publishes stage 0; barrier g then
+// (nk = nk_main + extra steps per item). Barrier "-1" publishes stage 0; barrier g then
 // publishes stage g + 1 and tells the producers that slot g % STAGES (stage
 // g, read by the compute waves during step g - 1) is free:
 //   producers: wait until their DMAs of stage g + 1 landed; barrier g; issue
@@ -552,33 +567,42 @@ __device__ __forceinline__ void dma_wait_stage(int younger) {
 //   compute:   barrier g; read stage g + 1 into one register set while the
 //              MFMAs of stage g run from the other; epilogue if g closes an
 //              item; finish the reads before the next barrier.
-// nk must be even (the register sets alternate per step); d and f are
-// multiples of 64 on this path, so it is.
+// The register sets alternate per step; an item with an odd step count
+// hands the next item's first stage over from the second set to the first.
 // Barriers are bare s_barrier: the producers' explicit vmcnt waits already
 // order their DMA writes, and a fenced barrier would wait for every stage in
 // flight.
 template <class Cfg, class Prob>
-__device__ __forceinline__ void persistent_gemm_dma(Prob& pb, int items, int nk) {
+__device__ __forceinline__ void persistent_gemm_dma(Prob& pb, int items, int nk_main) {
   static_assert(Cfg::KSUB == 1, "one MFMA K step per stage");
   constexpr int S = Cfg::STAGES;
+  constexpr int NX = ExtraSteps<Prob>::value;
   __shared__ __align__(16) bf16_t ring[S * Cfg::STAGE_ELEMS];
   const XcdSplit sp = xcd_split(items);
-  if (sp.first >= sp.end || nk <= 0) return;
+  if (sp.first >= sp.end || nk_main <= 0) return;
+  const int nk = nk_main + NX;  // K steps per item
   const int n_mine = (sp.end - sp.first + sp.stride - 1) / sp.stride;
   const int total = n_mine * nk;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 
   if (wave >= Cfg::CW) {
     const int part = wave - Cfg::CW;
-    DmaLoader<Cfg> ld;
+    DmaLoader<Cfg> ld, ldx;
     int l_ord = 0, l_kt = 0, l_slot = 0;  // load cursor
     pb.setup(sp.first, ld, part);
+    if constexpr (NX > 0) pb.setup_extra(sp.first, ldx, part);
     auto issue_next = [&]() {
-      dma_issue<Cfg>(ld, l_kt, ring + l_slot * Cfg::STAGE_ELEMS, part);
+      if (NX > 0 && l_kt >= nk_main)
+        dma_issue<Cfg>(ldx, l_kt - nk_main, ring + l_slot * Cfg::STAGE_ELEMS, part);
+      else
+        dma_issue<Cfg>(ld, l_kt, ring + l_slot * Cfg::STAGE_ELEMS, part);
       l_slot = (l_slot + 1 == S) ? 0 : l_slot + 1;
       if (++l_kt == nk) {
         l_kt = 0;
-        if (++l_ord < n_mine) pb.setup(sp.first + l_ord * sp.stride, ld, part);
+        if (++l_ord < n_mine) {
+          pb.setup(sp.first + l_ord * sp.stride, ld, part);
+          if constexpr (NX > 0) pb.setup_extra(sp.first + l_ord * sp.stride, ldx, part);
+        }
       }
     };
     for (int p = 0; p < S - 1 && p < total; ++p) issue_next();
@@ -603,21 +627,26 @@ __device__ __forceinline__ void persistent_gemm_dma(Prob& pb, int items, int nk)
   read_frags<Cfg>(f0, ring, wm, wn, lane);
   int rslot = 1 % S;  // ring slot of the next stage to read
   wait_lgkm0();
-  // K steps ping-pong between the two register sets (nk is even, so every
-  // item starts with its first stage in f0)
+  // K steps ping-pong between the two register sets; every item starts with
+  // its first stage in f0 (with an odd step count the last step reads the
+  // next item's first stage into f1, which is moved to f0 after the epilogue)
   for (int c_ord = 0; c_ord < n_mine; ++c_ord) {
     const int item = sp.first + c_ord * sp.stride;
     const int nf = dma_active_frags<Cfg>(wm, pb.rows(item));
     const int g0 = c_ord * nk;
     acc.zero();
-    for (int kt = 0; kt < nk; kt += 2) {
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
       mma_pp_step<Cfg>(g0 + kt, total, nf, ring, rslot, f0, f1, acc, wm, wn, lane);
       wait_lgkm0();
       mma_pp_step<Cfg>(g0 + kt + 1, total, nf, ring, rslot, f1, f0, acc, wm, wn, lane);
       if (kt + 2 < nk) wait_lgkm0();
     }
+    const bool odd = kt < nk;  // wave-uniform
+    if (odd) mma_pp_step<Cfg>(g0 + kt, total, nf, ring, rslot, f0, f1, acc, wm, wn, lane);
     pb.epilogue(item, acc);
     wait_lgkm0();
+    if (odd) f0 = f1;
   }
 }
 

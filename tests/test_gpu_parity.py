@@ -229,11 +229,14 @@ def test_packed_weights_need_d_multiple_of_128():
     assert e.value.status == B.MOE_ERR_UNSUPPORTED
 
 
-@pytest.mark.parametrize("b_init,x_perm", [("normal", True), ("normal", False), ("zero", False)])
-def test_lora_forward_backward_and_aux(b_init, x_perm):
-    w = W("lora_small", T=256, d=128, E=12, k=4, f=128, e_lo=2, e_hi=9, lora_r=16,
+# r = 16 carries the adapter terms through the matrix cores (one extra K
+# step); other ranks take the fp32 epilogue path
+@pytest.mark.parametrize("b_init,x_perm,r", [("normal", True, 16), ("normal", False, 16), ("zero", False, 16),
+                                             ("normal", False, 8)])
+def test_lora_forward_backward_and_aux(b_init, x_perm, r):
+    w = W("lora_small", T=256, d=128, E=12, k=4, f=128, e_lo=2, e_hi=9, lora_r=r,
           lora_alpha=32.0, lora_b=b_init, aux_coef=0.01)
-    say(f"[case lora_small b={b_init} x_perm={x_perm}]")
+    say(f"[case lora_small b={b_init} x_perm={x_perm} r={r}]")
     inp = generate(w, seed=6)
     dev = upload(inp)
     buf = run_forward(w, dev, prob=True, act_save=True, x_perm=x_perm)
