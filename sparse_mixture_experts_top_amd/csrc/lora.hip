@@ -318,53 +318,68 @@ __global__ __launch_bounds__(256) void lora_seg_outer(const int32_t* __restrict_
 // result does not depend on timing.
 typedef const __attribute__((address_space(4))) float* const_f32_ptr_t;
 
-template <class TIn> struct Vec4;
-template <> struct Vec4<bf16_t> {
-  static __device__ __forceinline__ void load(const bf16_t* p, float (&v)[4]) {
+// N consecutive values (N = 1, 2 or 4) in one load, as floats.
+template <int N>
+__device__ __forceinline__ void load_vec(const bf16_t* p, float (&v)[N]) {
+  if constexpr (N == 4) {
     const uint2 raw = *reinterpret_cast<const uint2*>(p);
     v[0] = bf16_to_f32(static_cast<bf16_t>(raw.x));
     v[1] = bf16_to_f32(static_cast<bf16_t>(raw.x >> 16));
     v[2] = bf16_to_f32(static_cast<bf16_t>(raw.y));
     v[3] = bf16_to_f32(static_cast<bf16_t>(raw.y >> 16));
+  } else if constexpr (N == 2) {
+    const uint32_t raw = *reinterpret_cast<const uint32_t*>(p);
+    v[0] = bf16_to_f32(static_cast<bf16_t>(raw));
+    v[1] = bf16_to_f32(static_cast<bf16_t>(raw >> 16));
+  } else {
+    v[0] = bf16_to_f32(*p);
   }
-};
-template <> struct Vec4<float> {
-  static __device__ __forceinline__ void load(const float* p, float (&v)[4]) {
+}
+template <int N>
+__device__ __forceinline__ void load_vec(const float* p, float (&v)[N]) {
+  if constexpr (N == 4) {
     const float4 a = *reinterpret_cast<const float4*>(p);
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  } else if constexpr (N == 2) {
+    const float2 a = *reinterpret_cast<const float2*>(p);
+    v[0] = a.x; v[1] = a.y;
+  } else {
+    v[0] = *p;
   }
-};
+}
 
 constexpr int kSegWaves = 16;  // waves per workgroup
-constexpr int kSegCols = 256;  // columns per workgroup (4 per lane)
 constexpr int kSegRq = 16;     // ranks held per lane
 constexpr int kSegSlots = 8;   // LDS partial-sum slots of the reduction tree
 
-template <class TIn>
+// CPL columns per lane (1, 2 or 4), 64 CPL per workgroup: fewer columns per
+// lane for narrow C, so that enough workgroups share the work.
+template <class TIn, int CPL>
 __global__ __launch_bounds__(64 * kSegWaves) void lora_seg_outer16(
     const int32_t* __restrict__ offsets, const float* __restrict__ P, int r, const TIn* __restrict__ in,
     int64_t in_stride, const int32_t* __restrict__ qsrc, const float* __restrict__ qscale, int C, float s,
     int out_qc, float* __restrict__ out) {
   constexpr int B = 4;  // rows per batch
+  constexpr int kSegCols = 64 * CPL;
   __shared__ float red[kSegSlots][kSegRq][kSegCols];
   const int le = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int cb = blockIdx.x * kSegCols;
-  const int c0 = cb + lane * 4;
+  const int c0 = cb + lane * CPL;
   const bool cok = c0 < C;
   const int a = ld_uniform(offsets, le), b = ld_uniform(offsets, le + 1);
   // this wave's rows: a + wave + kSegWaves m, m < M
   const int M = b - a > wave ? (b - a - wave + kSegWaves - 1) / kSegWaves : 0;
-  float acc[kSegRq][4];
+  float acc[kSegRq][CPL];
 #pragma unroll
   for (int q = 0; q < kSegRq; ++q)
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc[q][u] = 0.f;
+    for (int u = 0; u < CPL; ++u) acc[q][u] = 0.f;
   const int jp = lane >> 4, qp = lane & 15;  // P value this lane fetches: row jp of a batch, rank qp
   int srcv = 0;      // lane l: source row of window row l (64 rows per window)
   float sclv = 1.f;  // lane l: its scale
-  float vc[B][4], vn[B][4], pc = 0.f, pn = 0.f;
+  float vc[B][CPL], vn[B][CPL], pc = 0.f, pn = 0.f;
   for (int m0 = 0; m0 < M + B; m0 += B) {
     // fetch batch m0 (if any) into (vn, pn) while batch m0 - B, in (vc, pc), is consumed
     if (m0 < M) {
@@ -380,15 +395,16 @@ __global__ __launch_bounds__(64 * kSegWaves) void lora_seg_outer16(
       for (int j = 0; j < B; ++j) {
         const int src = __builtin_amdgcn_readlane(srcv, (m0 + j) & 63);
         if (m0 + j < M && cok) {
-          Vec4<TIn>::load(in + (int64_t)src * in_stride + c0, vn[j]);
+          load_vec<CPL>(in + (int64_t)src * in_stride + c0, vn[j]);
         } else {
-          vn[j][0] = vn[j][1] = vn[j][2] = vn[j][3] = 0.f;
+#pragma unroll
+          for (int u = 0; u < CPL; ++u) vn[j][u] = 0.f;
         }
         // fold the row scale in right away (rows past M have scale 1 and zeros)
         const float sc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sclv),
                                                                              (m0 + j) & 63));
 #pragma unroll
-        for (int u = 0; u < 4; ++u) vn[j][u] *= sc;
+        for (int u = 0; u < CPL; ++u) vn[j][u] *= sc;
       }
     }
     if (m0 > 0) {
@@ -398,13 +414,13 @@ __global__ __launch_bounds__(64 * kSegWaves) void lora_seg_outer16(
         for (int q = 0; q < kSegRq; ++q) {
           const float pq = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pc), 16 * j + q));
 #pragma unroll
-          for (int u = 0; u < 4; ++u) acc[q][u] = fmaf(pq, vc[j][u], acc[q][u]);
+          for (int u = 0; u < CPL; ++u) acc[q][u] = fmaf(pq, vc[j][u], acc[q][u]);
         }
     }
 #pragma unroll
     for (int j = 0; j < B; ++j)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) vc[j][u] = vn[j][u];
+      for (int u = 0; u < CPL; ++u) vc[j][u] = vn[j][u];
     pc = pn;
   }
   // fixed-order tree over the waves: 16 -> 8 -> 4 -> 2 -> 1
@@ -412,16 +428,15 @@ __global__ __launch_bounds__(64 * kSegWaves) void lora_seg_outer16(
     if (wave >= half && wave < 2 * half) {
 #pragma unroll
       for (int q = 0; q < kSegRq; ++q)
-        *reinterpret_cast<float4*>(&red[wave - half][q][lane * 4]) =
-            make_float4(acc[q][0], acc[q][1], acc[q][2], acc[q][3]);
+#pragma unroll
+        for (int u = 0; u < CPL; ++u) red[wave - half][q][lane * CPL + u] = acc[q][u];
     }
     __syncthreads();
     if (wave < half) {
 #pragma unroll
-      for (int q = 0; q < kSegRq; ++q) {
-        const float4 o = *reinterpret_cast<const float4*>(&red[wave][q][lane * 4]);
-        acc[q][0] += o.x; acc[q][1] += o.y; acc[q][2] += o.z; acc[q][3] += o.w;
-      }
+      for (int q = 0; q < kSegRq; ++q)
+#pragma unroll
+        for (int u = 0; u < CPL; ++u) acc[q][u] += red[wave][q][lane * CPL + u];
     }
     __syncthreads();
   }
@@ -430,11 +445,11 @@ __global__ __launch_bounds__(64 * kSegWaves) void lora_seg_outer16(
 #pragma unroll
     for (int q = 0; q < kSegRq; ++q)
       if (q < r)
-        *reinterpret_cast<float4*>(out + ((int64_t)le * r + q) * C + c0) =
-            make_float4(s * acc[q][0], s * acc[q][1], s * acc[q][2], s * acc[q][3]);
+#pragma unroll
+        for (int u = 0; u < CPL; ++u) out[((int64_t)le * r + q) * C + c0 + u] = s * acc[q][u];
   } else {
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < CPL; ++u)
 #pragma unroll
       for (int q = 0; q < kSegRq; ++q)
         if (q < r) out[((int64_t)le * C + c0 + u) * r + q] = s * acc[q][u];
@@ -447,8 +462,16 @@ static hipError_t launch_seg_outer(const Ctx& c, int L, const int32_t* offsets, 
                                    const float* qscale, int C, float s, bool out_qc, float* out) {
   if (r <= kSegRq && C % 4 == 0 && in_stride % 4 == 0) {
     TimedLaunch tl(MOE_K_LORA_GRAD, c.stream);
-    hipLaunchKernelGGL(lora_seg_outer16<TIn>, dim3((C + kSegCols - 1) / kSegCols, L), dim3(64 * kSegWaves), 0,
-                       c.stream, offsets, P, r, in, in_stride, qsrc, qscale, C, s, (int)out_qc, out);
+    // columns per lane: the widest that still gives about 200 workgroups
+    const int64_t want = 200;
+    const int cpl = (int64_t)((C + 255) / 256) * L >= want ? 4 : (int64_t)((C + 127) / 128) * L >= want ? 2 : 1;
+#define MOE_SEG(N)                                                                                        \
+  hipLaunchKernelGGL((lora_seg_outer16<TIn, N>), dim3((C + 64 * N - 1) / (64 * N), L), dim3(64 * kSegWaves), 0, \
+                     c.stream, offsets, P, r, in, in_stride, qsrc, qscale, C, s, (int)out_qc, out)
+    if (cpl == 4) MOE_SEG(4);
+    else if (cpl == 2) MOE_SEG(2);
+    else MOE_SEG(1);
+#undef MOE_SEG
     return hipGetLastError();
   }
   dim3 grid((C + 255) / 256, L);
