@@ -83,36 +83,43 @@ __global__ __launch_bounds__(256) void gate_bwd(const T* __restrict__ dy, const 
   const int my_e = lane < k ? idx[(int64_t)t * k + lane] : 0;
   const T* dyr = dy + (int64_t)t * d;
   float my_dg = 0.f;
-  for (int j0 = 0; j0 < k; j0 += G) {
-    int s[G];
-    bool any = false;
+  // the token's kept local slots, compacted in j order (slot and j per entry)
+  __shared__ int s_cs[4][64], s_cj[4][64];
+  const int wv = threadIdx.x >> 6;
+  const uint64_t kept = __ballot(my_slot >= 0);
+  const int n = __popcll(kept);
+  if (my_slot >= 0) {
+    const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    const int pos = __popcll(kept & below);
+    s_cs[wv][pos] = my_slot;
+    s_cj[wv][pos] = lane;
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  for (int j0 = 0; j0 < n; j0 += G) {
+    // G entries (past n: the last kept row again, its sum discarded), the
+    // G + 1 loads of a row chunk in flight before its FMAs
+    int64_t rb[G];
 #pragma unroll
-    for (int q = 0; q < G; ++q) {
-      s[q] = __shfl(my_slot, j0 + q < k ? j0 + q : 0, kWave);
-      s[q] = j0 + q < k ? s[q] : -1;
-      any = any || s[q] >= 0;
-    }
-    if (!any) continue;  // wave-uniform
+    for (int q = 0; q < G; ++q) rb[q] = (int64_t)s_cs[wv][min(j0 + q, n - 1)] * d;
     float acc[G];
 #pragma unroll
     for (int q = 0; q < G; ++q) acc[q] = 0.f;
     for (int i0 = lane * 8; i0 < d; i0 += 64 * 8) {
-      float a[8];
-      load8f<T>(dyr + i0, a);
+      float a0[8], o0[G][8];
+      load8f<T>(dyr + i0, a0);
 #pragma unroll
-      for (int q = 0; q < G; ++q) {
-        if (s[q] < 0) continue;
-        float o[8];
-        load8f<T>(y_perm + (int64_t)s[q] * d + i0, o);
+      for (int q = 0; q < G; ++q) load8f<T>(y_perm + rb[q] + i0, o0[q]);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) acc[q] = fmaf(a[u], o[u], acc[q]);
-      }
+      for (int q = 0; q < G; ++q)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc[q] = fmaf(a0[u], o0[q][u], acc[q]);
     }
 #pragma unroll
     for (int q = 0; q < G; ++q) {
-      if (s[q] < 0) continue;  // wave-uniform; its dg stays 0
+      if (j0 + q >= n) break;  // wave-uniform
       const float v = wave_sum(acc[q]);
-      if (lane == j0 + q) my_dg = v;
+      if (lane == s_cj[wv][j0 + q]) my_dg = v;
     }
   }
   if (dgate && lane < k) dgate[(int64_t)t * k + lane] = my_dg;
