@@ -231,15 +231,16 @@ def test_packed_weights_need_d_multiple_of_128():
 
 # r = 16 carries the adapter terms through the matrix cores (one extra K
 # step); other ranks take the fp32 epilogue path
-@pytest.mark.parametrize("b_init,x_perm,r", [("normal", True, 16), ("normal", False, 16), ("zero", False, 16),
-                                             ("normal", False, 8)])
-def test_lora_forward_backward_and_aux(b_init, x_perm, r):
+@pytest.mark.parametrize("b_init,x_perm,r,packed", [("normal", True, 16, False), ("normal", False, 16, False),
+                                                    ("zero", False, 16, False), ("normal", False, 8, False),
+                                                    ("normal", False, 16, True)])
+def test_lora_forward_backward_and_aux(b_init, x_perm, r, packed):
     w = W("lora_small", T=256, d=128, E=12, k=4, f=128, e_lo=2, e_hi=9, lora_r=r,
           lora_alpha=32.0, lora_b=b_init, aux_coef=0.01)
-    say(f"[case lora_small b={b_init} x_perm={x_perm} r={r}]")
+    say(f"[case lora_small b={b_init} x_perm={x_perm} r={r} packed={packed}]")
     inp = generate(w, seed=6)
     dev = upload(inp)
-    buf = run_forward(w, dev, prob=True, act_save=True, x_perm=x_perm)
+    buf = run_forward(w, dev, prob=True, act_save=True, x_perm=x_perm, packed=packed)
     lg, idx, gate = check_route(w, inp, buf)
     ref, R = check_dispatch(w, dev, buf, idx, gate)
     lo64 = {"scale": w.lora_alpha / w.lora_r}
