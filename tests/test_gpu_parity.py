@@ -145,6 +145,34 @@ def test_no_local_assignment():
     assert (buf.slot == -1).all() and (host(buf.y) == 0).all()
 
 
+def test_lora_no_local_rows_gives_zero_gradients():
+    """No token picks a local expert (large bias on experts 0..3, local range
+    12..15): the forward has no rows and every adapter gradient element is
+    written as exactly 0, through both the plain and the packed backward."""
+    w = W("lora_nolocal", T=90, d=128, E=16, k=4, f=128, e_lo=12, e_hi=16, lora_r=16, lora_alpha=32.0,
+          lora_b="normal", aux_coef=0.01)
+    inp = generate(w, seed=4)
+    inp["bias"] = torch.tensor([50.0] * 4 + [0.0] * 12)
+    dev = upload(inp)
+    buf = run_forward(w, dev, act_save=True, x_perm=False, packed=True)
+    assert int(buf.offsets[-1].item()) == 0 and (host(buf.y) == 0).all()
+    L, r = w.L, w.lora_r
+    lora = B.make_lora(r, w.lora_alpha, dev["a_up"], dev["b_up"], dev["a_down"], dev["b_down"])
+    dgu_p = torch.empty((L, w.f, w.d), dtype=torch.bfloat16, device="cuda")
+    B.moe_pack_backward_weights(buf.shape, dev["w_gate"], dev["w_up"], dev["w_down"], dgu_p, None)
+    xr, xs = layer.x_rows(buf, dev["x"])
+    for packed in (False, True):
+        g = [torch.full(sz, float("nan"), device="cuda") for sz in ((L, r, w.d), (L, w.f, r), (L, r, w.f), (L, w.d, r))]
+        if packed:
+            B.moe_lora_bwd_packed(buf.shape, lora, dev["dy"], buf.offsets, buf.row_src, buf.row_gate, xr, xs,
+                                  buf.act_save, dgu_p, *g, buf.ws)
+        else:
+            B.moe_lora_bwd(buf.shape, lora, dev["dy"], buf.offsets, buf.row_src, buf.row_gate, xr, xs,
+                           buf.act_save, dev["w_down"], *g, buf.ws)
+        torch.cuda.synchronize()
+        assert all((t == 0).all() for t in g), f"packed={packed}"
+
+
 def test_capacity_one_everywhere():
     w = W("cap1", T=64, d=64, E=8, k=2, f=64, capacity=1)
     inp = generate(w, seed=5)
