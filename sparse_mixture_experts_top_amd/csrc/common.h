@@ -180,7 +180,7 @@ struct Workspace {
 };
 
 constexpr int kTokTile = 32;       // tokens per dispatch tile (one 32-bit mask per expert)
-constexpr int kTopkTokPerWaveProb = 4;  // tokens per top-k wave when softmax sums are kept
+constexpr int kTopkTokPerWaveProb = 2;  // tokens per top-k wave when softmax sums are kept
 constexpr int kGemmBM = 128;       // grouped GEMM row tile
 
 Workspace carve_workspace(const moe_shape_t& s, int lora_r, void* base);

@@ -298,17 +298,27 @@ __global__ __launch_bounds__(256) void topk_softmax(const float* __restrict__ lo
 
 // prob_sum[e] = sum over blocks of prob_part[b, e]. Workgroup (e-group of
 // 64 experts, 16 waves): lane l of wave w sums blocks w, w + 16, ... of
-// expert 64 g + l in order, then the waves' partials are added in wave order
-// - a fixed order, so the result does not depend on scheduling.
+// expert 64 g + l in order (32 loads in flight per batch), then the waves'
+// partials are added in wave order - a fixed order, so the result does not
+// depend on scheduling.
 __global__ __launch_bounds__(1024) void prob_reduce(const float* __restrict__ part, int nblk, int E,
                                                     float* __restrict__ out) {
+  constexpr int NB = 32;
   __shared__ float red[16][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int e = blockIdx.x * 64 + lane;
   float acc = 0.f;
   if (e < E) {
-#pragma unroll 8
-    for (int b = wave; b < nblk; b += 16) acc += part[(int64_t)b * E + e];
+    for (int b0 = wave; b0 < nblk; b0 += 16 * NB) {
+      float v[NB];
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int b = b0 + 16 * u;
+        v[u] = b < nblk ? part[(int64_t)b * E + e] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < NB; ++u) acc += v[u];
+    }
   }
   red[wave][lane] = acc;
   __syncthreads();
