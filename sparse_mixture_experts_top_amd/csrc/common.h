@@ -234,9 +234,14 @@ hipError_t launch_lora_bwd(const Ctx& c, const moe_shape_t& s, const Workspace& 
                            float* db_up, float* da_down, float* db_down,
                            const bf16_t* dgu_packed = nullptr);
 // dU of the LoRA backward on the packed W_d^T (expert_gemm.hip)
+// adt: A_d^T [L, f, 16] (lora_transpose_rn) to carry the adapter term as an
+// extra K step whose A operand is ws.zx (s dY B_d, high/low), or NULL for the
+// fp32 epilogue term from ws.wproj
 hipError_t launch_lora_dh_packed(const Ctx& c, const moe_shape_t& s, const Workspace& ws, const LoraArgs& lo,
                                  const bf16_t* dy, const int32_t* row_src, const float* row_gate,
-                                 const int32_t* offsets, const bf16_t* act_save, const bf16_t* dgu_packed);
+                                 const int32_t* offsets, const bf16_t* act_save, const bf16_t* dgu_packed,
+                                 const bf16_t* adt);
+hipError_t launch_lora_transpose_rn(const Ctx& c, const bf16_t* A, int L, int r, int N, bf16_t* At);
 
 hipError_t launch_gate_bwd(const Ctx& c, const moe_shape_t& s, const void* dy, const void* y_perm,
                            const int32_t* slot, const int32_t* idx, const float* gate,
@@ -271,10 +276,11 @@ hipError_t launch_router_bwd(const Ctx& c, const moe_shape_t& s, const Workspace
 //   mt:   scratch of L * r * K bf16 for M transposed to [L, r, K] when it is
 //         stored [L, K, r] (the matrix-core path reads K-contiguous rows), or
 //         NULL (then such an M takes the plain per-row path)
-//   out_hl: if not NULL, hl_scale * out is written there instead of out, as
-//         [rows, 2r] bf16: the bf16 rounding in columns [0, r) and the bf16
-//         rounding of the remainder in [r, 2r) (matrix-core path only;
-//         hipErrorInvalidValue otherwise)
+//   out_hl: if not NULL, hl_scale * in[src_p] . M (without the row scale)
+//         is also written there as [rows, 2r] bf16: the bf16 rounding in
+//         columns [0, r) and the bf16 rounding of the remainder in [r, 2r)
+//         (matrix-core path only; hipErrorInvalidValue otherwise); out may
+//         then be NULL
 template <class TIn>
 hipError_t launch_lora_rowproj(const Ctx& c, int L, const int32_t* offsets, int64_t rmax_rows,
                                const TIn* in, int64_t in_stride, const int32_t* src,

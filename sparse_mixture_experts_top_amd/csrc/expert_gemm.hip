@@ -383,8 +383,13 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::WAVES_PER_SIMD) void down_bf16(D
 // so the plain kernels carry no adapter code).
 // DU32: only dU = dH silu(G), in fp32, to du32 [Rmax, f] (the LoRA adapter
 // gradients need no dG).
-template <class Cfg, bool LORA = false, bool DU32 = false>
+// KX (with LORA): the adapter term rides as one extra K step instead: A =
+// zx (s dY B_d as bf16 high | low, 32 per row), B = adt rows (A_d^T, the
+// 16 adapter values of each output column, read twice); the row gate then
+// scales the whole sum.
+template <class Cfg, bool LORA = false, bool DU32 = false, bool KX = false>
 struct DguPackedProb {
+  static constexpr int kExtra = KX ? 1 : 0;
   const bf16_t* dy;
   const int32_t* row_src;
   const float* row_gate;
@@ -399,6 +404,22 @@ struct DguPackedProb {
   const bf16_t* act_save;
   bf16_t* dgu;
   float* du32 = nullptr;
+  const bf16_t* zx = nullptr;   // KX: [Rmax, 32]
+  const bf16_t* adt = nullptr;  // KX: [L, f, 16]
+
+  __device__ __forceinline__ void setup_extra(int item, DmaLoader<Cfg>& ld, int part) const {
+    const RowTile t = row_tile<Cfg::BM>(tiles, offsets, item / nt);
+    const int n0 = (item % nt) * Cfg::BN;
+    const int ce = dma_chunk_elem<Cfg>();
+#pragma unroll
+    for (int q = 0; q < Cfg::A_DMA / Cfg::DW; ++q)
+      ld.a[q] = zx + (t.row0 + min(dma_row<Cfg>(q * Cfg::DW + part), t.valid - 1)) * 32 + ce;
+#pragma unroll
+    for (int q = 0; q < Cfg::B_DMA / Cfg::DW; ++q) {
+      const int n = min(n0 + dma_row<Cfg>(q * Cfg::DW + part), f - 1);
+      ld.b[q] = adt + ((int64_t)t.le * f + n) * 16 + (ce & 8);
+    }
+  }
 
   __device__ __forceinline__ int rows(int item) const {
     return row_tile<Cfg::BM>(tiles, offsets, item / nt).valid;
@@ -445,7 +466,7 @@ struct DguPackedProb {
         const bf16_t* as = act_save + row * 3 * f + n;
         const uint2 gv = *reinterpret_cast<const uint2*>(as);
         float dgv[4], duv[4], lt[4] = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (LORA) lora_term_cols(wproj + row * r, a_down + (int64_t)t.le * r * f + n, f, r, lt);
+        if constexpr (LORA && !KX) lora_term_cols(wproj + row * r, a_down + (int64_t)t.le * r * f + n, f, r, lt);
         if constexpr (DU32) {
           const uint32_t gw[2] = {gv.x, gv.y};
 #pragma unroll
@@ -475,8 +496,8 @@ struct DguPackedProb {
   }
 };
 
-template <class Cfg, bool LORA, bool DU32 = false>
-__global__ __launch_bounds__(Cfg::THREADS, Cfg::WAVES_PER_SIMD) void expert_dgu_dma(DguPackedProb<Cfg, LORA, DU32> pb,
+template <class Cfg, bool LORA, bool DU32 = false, bool KX = false>
+__global__ __launch_bounds__(Cfg::THREADS, Cfg::WAVES_PER_SIMD) void expert_dgu_dma(DguPackedProb<Cfg, LORA, DU32, KX> pb,
                                                                                    int max_tiles) {
   const int items = ld_uniform(pb.tiles, 2 * max_tiles) * pb.nt;
   persistent_gemm_dma<Cfg>(pb, items, pb.d / Cfg::BK);
@@ -600,31 +621,35 @@ static hipError_t launch_bwd_gemms_cfg(const Ctx& c, const moe_shape_t& s, const
 // The LoRA backward's dU = (g dY W_d + s (dO B_d) A_d) silu(G), fp32 into
 // ws.du, on the packed W_d^T (moe_pack_backward_weights); ws.wproj holds
 // dO B_d and ws.gemm_tiles the row tiles.
-template <class Cfg>
+template <class Cfg, bool KX>
 static hipError_t launch_lora_dh_cfg(const Ctx& c, const moe_shape_t& s, const Workspace& ws, const LoraArgs& lo,
                                      const bf16_t* dy, const int32_t* row_src, const float* row_gate,
                                      const int32_t* offsets, const bf16_t* act_save, const bf16_t* dgu_packed,
-                                     int max_tiles) {
-  DguPackedProb<Cfg, true, true> pb{dy, row_src, row_gate, offsets, ws.gemm_tiles, dgu_packed, s.d, s.f,
-                                    (s.f + Cfg::BN - 1) / Cfg::BN, s.e_hi - s.e_lo, ws.wproj, lo.a_down, lo.r,
-                                    lo.scale, act_save, nullptr, ws.du};
+                                     const bf16_t* adt, int max_tiles) {
+  DguPackedProb<Cfg, true, true, KX> pb{dy, row_src, row_gate, offsets, ws.gemm_tiles, dgu_packed, s.d, s.f,
+                                        (s.f + Cfg::BN - 1) / Cfg::BN, s.e_hi - s.e_lo, ws.wproj, lo.a_down, lo.r,
+                                        lo.scale, act_save, nullptr, ws.du};
+  pb.zx = ws.zx;
+  pb.adt = adt;
   TimedLaunch tl(MOE_K_LORA_DH, c.stream);
-  hipLaunchKernelGGL((expert_dgu_dma<Cfg, true, true>), dim3(c.num_cus), dim3(Cfg::THREADS), 0, c.stream, pb,
+  hipLaunchKernelGGL((expert_dgu_dma<Cfg, true, true, KX>), dim3(c.num_cus), dim3(Cfg::THREADS), 0, c.stream, pb,
                      max_tiles);
   return hipGetLastError();
 }
 
 hipError_t launch_lora_dh_packed(const Ctx& c, const moe_shape_t& s, const Workspace& ws, const LoraArgs& lo,
                                  const bf16_t* dy, const int32_t* row_src, const float* row_gate,
-                                 const int32_t* offsets, const bf16_t* act_save, const bf16_t* dgu_packed) {
+                                 const int32_t* offsets, const bf16_t* act_save, const bf16_t* dgu_packed,
+                                 const bf16_t* adt) {
   const int max_tiles = gemm_max_tiles(s);
   int64_t per_expert = (int64_t)s.T * s.k / s.E;
   if (s.capacity > 0 && per_expert > s.capacity) per_expert = s.capacity;
-  if (per_expert >= kWideRowsPerExpert)
-    return launch_lora_dh_cfg<GemmCfgWide>(c, s, ws, lo, dy, row_src, row_gate, offsets, act_save, dgu_packed,
-                                           max_tiles);
-  return launch_lora_dh_cfg<GemmCfg>(c, s, ws, lo, dy, row_src, row_gate, offsets, act_save, dgu_packed,
-                                     max_tiles);
+  const bool wide = per_expert >= kWideRowsPerExpert;
+#define MOE_DH(C, K) \
+  launch_lora_dh_cfg<C, K>(c, s, ws, lo, dy, row_src, row_gate, offsets, act_save, dgu_packed, adt, max_tiles)
+  if (adt) return wide ? MOE_DH(GemmCfgWide, true) : MOE_DH(GemmCfg, true);
+  return wide ? MOE_DH(GemmCfgWide, false) : MOE_DH(GemmCfg, false);
+#undef MOE_DH
 }
 
 hipError_t launch_bwd_gemms_packed(const Ctx& c, const moe_shape_t& s, const Workspace& ws, const LoraArgs* lo,

@@ -192,21 +192,38 @@ __global__ __launch_bounds__(64 * kProjWaves) void lora_proj_mfma(int L, const i
       for (int i = 0; i < 4; ++i) {
         const int p = p0 + 4 * kc + i;
         if (q < r && p >= seg0 && p < seg1) {
-          const float v = (row_scale ? row_scale[p] : 1.f) * t[i];
           if (out_hl) {
-            // hl_scale v as a bf16 high part and the bf16 rounding of the rest
-            const float sv = hl_scale * v;
+            // hl_scale t (before the row scale) as a bf16 high part and the
+            // bf16 rounding of the rest
+            const float sv = hl_scale * t[i];
             const bf16_t hi = f32_to_bf16(sv);
             out_hl[(int64_t)p * 2 * r + q] = hi;
             out_hl[(int64_t)p * 2 * r + r + q] = f32_to_bf16(sv - bf16_to_f32(hi));
-          } else {
-            out[(int64_t)p * r + q] = v;
           }
+          if (out) out[(int64_t)p * r + q] = (row_scale ? row_scale[p] : 1.f) * t[i];
         }
       }
     }
     __syncthreads();
   }
+}
+
+// At[le][n][q] = A[le][q][n]: an [L, r, N] adapter as [L, N, r] rows (the
+// B operand of an extra adapter K step).
+__global__ __launch_bounds__(256) void lora_transpose_rn(const bf16_t* __restrict__ A, int L, int r, int N,
+                                                         bf16_t* __restrict__ At) {
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over L * r * N, N fastest
+  if (id >= (int64_t)L * r * N) return;
+  const int64_t n = id % N, q = (id / N) % r, le = id / ((int64_t)N * r);
+  At[(le * N + n) * r + q] = A[id];
+}
+
+hipError_t launch_lora_transpose_rn(const Ctx& c, const bf16_t* A, int L, int r, int N, bf16_t* At) {
+  const int64_t n = (int64_t)L * r * N;
+  if (n == 0) return hipSuccess;
+  TimedLaunch tl(MOE_K_LORA_PROJ, c.stream);
+  hipLaunchKernelGGL(lora_transpose_rn, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, c.stream, A, L, r, N, At);
+  return hipGetLastError();
 }
 
 // Mt[le][q][k] = M[le][k][q]: a [L, K, r] adapter made K-contiguous.
@@ -575,9 +592,15 @@ hipError_t launch_lora_bwd(const Ctx& c, const moe_shape_t& sh, const Workspace&
   MOE_TRY(launch_row_tiles(c, offsets, L, max_tiles, ws.gemm_tiles));
   MOE_TRY(launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, x_rows, d, x_src, nullptr, d, lo.a_up, true, r, ws.zu));
   MOE_TRY(launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, H, 3 * f, nullptr, nullptr, f, lo.a_down, true, r, ws.zd));
-  MOE_TRY(launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, dy, d, row_src, row_gate, d, lo.b_down, false, r, ws.wproj, ws.lora_mt));
+  // dO B_d (row-scaled, fp32) and, for the packed dH product's extra K step,
+  // s dY B_d as bf16 high/low parts (the row gate scales the whole dH there)
+  const bool kx = dgu_packed && lo.r == 16 && ws.zx;
+  MOE_TRY(launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, dy, d, row_src, row_gate, d, lo.b_down, false, r, ws.wproj,
+                                      ws.lora_mt, kx ? ws.zx : nullptr, lo.scale));
   if (dgu_packed) {
-    MOE_TRY(launch_lora_dh_packed(c, sh, ws, lo, dy, row_src, row_gate, offsets, act_save, dgu_packed));
+    if (kx) MOE_TRY(launch_lora_transpose_rn(c, lo.a_down, L, r, f, ws.lora_mt));
+    MOE_TRY(launch_lora_dh_packed(c, sh, ws, lo, dy, row_src, row_gate, offsets, act_save, dgu_packed,
+                                  kx ? ws.lora_mt : nullptr));
   } else {
     TimedLaunch tl(MOE_K_LORA_DH, c.stream);
     DhProb<Cfg> pb{dy, row_src, row_gate, offsets, ws.gemm_tiles, w_down, d, f, (f + Cfg::BN - 1) / Cfg::BN,
