@@ -127,70 +127,115 @@ __device__ __forceinline__ void frag_load(const float* p, bf16x8& hi, bf16x8& lo
 }
 
 // out[p, q] = scale_p * in[src_p] . Mt[le][q] for q < r <= 16 on the matrix
-// cores. One workgroup per 16 consecutive dispatched rows; its 8 waves take
+// cores. One workgroup per kProjRowGroups x 16 consecutive dispatched rows
+// (the row fragments share each B fragment); its 8 waves take
 // the K steps of 32 in turn (wave w: steps w, w + 8, ...) and their 16 x 16
 // partial sums are added in wave order through LDS. A group that spans an
 // expert boundary is computed once per expert it touches, each pass storing
 // that expert's rows. Lane l supplies row l % 16 of the in-rows and of Mt
 // (ranks) at K offset 8 (l / 16) and receives rows 4 (l / 16) + i, rank l % 16.
 constexpr int kProjWaves = 8;
+// 16-row groups per workgroup (sharing each B fragment load); two measured
+// slower on the 14-expert LoRA step (fewer workgroups outweigh the halved
+// adapter re-reads from L2)
+constexpr int kProjRowGroups = 1;
 
+// One projection: out[p, q] = row_scale_p * in[src_p] . Mt[le(p)][q] (and
+// out_hl, see launch_lora_rowproj).
 template <class TIn>
-__global__ __launch_bounds__(64 * kProjWaves) void lora_proj_mfma(int L, const int32_t* __restrict__ offsets,
-                                                      const TIn* __restrict__ in, int64_t in_stride,
-                                                      const int32_t* __restrict__ src,
-                                                      const float* __restrict__ row_scale, int K,
-                                                      const bf16_t* __restrict__ Mt, int r,
-                                                      float* __restrict__ out, bf16_t* __restrict__ out_hl,
-                                                      float hl_scale) {
+struct ProjJob {
+  const TIn* in;
+  int64_t in_stride;
+  const int32_t* src;
+  const float* row_scale;
+  int K;
+  const bf16_t* Mt;
+  float* out;
+  bf16_t* out_hl;
+  float hl_scale;
+};
+// NJ independent projections over the same dispatched rows in one launch
+// (blockIdx.y selects the job), so they share the GPU instead of each
+// leaving it partly idle.
+template <class TIn, int NJ>
+struct ProjJobs {
+  ProjJob<TIn> j[NJ];
+};
+
+template <class TIn, int NJ>
+__global__ __launch_bounds__(64 * kProjWaves) void lora_proj_mfma(int L, const int32_t* __restrict__ offsets, int r,
+                                                                  ProjJobs<TIn, NJ> jobs) {
   constexpr bool kSplit = sizeof(TIn) == 4;
   constexpr int U = 4;  // K steps per load batch
-  __shared__ f32x4 part[kProjWaves][64];
+  constexpr int RG = kProjRowGroups;
+  __shared__ f32x4 part[kProjWaves][RG][64];
+  const ProjJob<TIn>& jb = jobs.j[NJ == 1 ? 0 : blockIdx.y];
+  const TIn* __restrict__ in = jb.in;
+  const int64_t in_stride = jb.in_stride;
+  const int32_t* __restrict__ src = jb.src;
+  const float* __restrict__ row_scale = jb.row_scale;
+  const int K = jb.K;
+  const bf16_t* __restrict__ Mt = jb.Mt;
+  float* __restrict__ out = jb.out;
+  bf16_t* __restrict__ out_hl = jb.out_hl;
+  const float hl_scale = jb.hl_scale;
   const int R = ld_uniform(offsets, L);
-  const int p0 = blockIdx.x * 16;
+  const int p0 = blockIdx.x * 16 * RG;
   if (p0 >= R) return;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int row = lane & 15, kc = lane >> 4;
   const int le_first = segment_of_uniform(offsets, L, p0);
-  const int le_last = segment_of_uniform(offsets, L, min(p0 + 15, R - 1));
-  const int prow = min(p0 + row, R - 1);
-  const int64_t srow = src ? (int64_t)src[prow] : (int64_t)prow;
-  const TIn* a_ptr = in + srow * in_stride + kc * 8;
+  const int le_last = segment_of_uniform(offsets, L, min(p0 + 16 * RG - 1, R - 1));
+  const TIn* a_ptr[RG];
+#pragma unroll
+  for (int g = 0; g < RG; ++g) {
+    const int prow = min(p0 + 16 * g + row, R - 1);
+    const int64_t srow = src ? (int64_t)src[prow] : (int64_t)prow;
+    a_ptr[g] = in + srow * in_stride + kc * 8;
+  }
   const int nsteps = K / 32;
   for (int le = le_first; le <= le_last; ++le) {
     const int seg0 = ld_uniform(offsets, le), seg1 = ld_uniform(offsets, le + 1);
     if (seg0 == seg1) continue;  // wave-uniform
     const bf16_t* b_ptr = Mt + ((int64_t)le * r + min(row, r - 1)) * K + kc * 8;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[RG];
+#pragma unroll
+    for (int g = 0; g < RG; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int s0 = wave; s0 < nsteps; s0 += kProjWaves * U) {
-      bf16x8 ah[U], al[U], b[U];
+      bf16x8 ah[U][RG], al[U][RG], b[U];
 #pragma unroll
       for (int j = 0; j < U; ++j) {
         const int st = s0 + kProjWaves * j;
         if (st < nsteps) {
-          frag_load(a_ptr + (int64_t)st * 32, ah[j], al[j], kSplit);
           b[j] = *reinterpret_cast<const bf16x8*>(b_ptr + (int64_t)st * 32);
+#pragma unroll
+          for (int g = 0; g < RG; ++g) frag_load(a_ptr[g] + (int64_t)st * 32, ah[j][g], al[j][g], kSplit);
         }
       }
 #pragma unroll
       for (int j = 0; j < U; ++j) {
         if (s0 + kProjWaves * j < nsteps) {
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[j], b[j], acc, 0, 0, 0);
-          if constexpr (kSplit) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[j], b[j], acc, 0, 0, 0);
+#pragma unroll
+          for (int g = 0; g < RG; ++g) {
+            acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[j][g], b[j], acc[g], 0, 0, 0);
+            if constexpr (kSplit) acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[j][g], b[j], acc[g], 0, 0, 0);
+          }
         }
       }
     }
-    part[wave][lane] = acc;
-    __syncthreads();
-    if (wave == 0) {
-      f32x4 t = part[0][lane];
 #pragma unroll
-      for (int w = 1; w < kProjWaves; ++w) t += part[w][lane];
+    for (int g = 0; g < RG; ++g) part[wave][g][lane] = acc[g];
+    __syncthreads();
+    if (wave < RG) {  // wave g finishes row group g
+      const int g = wave;
+      f32x4 t = part[0][g][lane];
+#pragma unroll
+      for (int w = 1; w < kProjWaves; ++w) t += part[w][g][lane];
       const int q = lane & 15;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int p = p0 + 4 * kc + i;
+        const int p = p0 + 16 * g + 4 * kc + i;
         if (q < r && p >= seg0 && p < seg1) {
           if (out_hl) {
             // hl_scale t (before the row scale) as a bf16 high part and the
@@ -249,9 +294,11 @@ hipError_t launch_lora_rowproj(const Ctx& c, int L, const int32_t* offsets, int6
                          mt);
       M = mt;
     }
-    hipLaunchKernelGGL(lora_proj_mfma<TIn>, dim3((unsigned)((rmax_rows + 15) / 16)), dim3(64 * kProjWaves), 0,
-                       c.stream, L,
-                       offsets, in, in_stride, src, row_scale, K, M, r, out, out_hl, hl_scale);
+    ProjJobs<TIn, 1> jobs{{{in, in_stride, src, row_scale, K, M, out, out_hl, hl_scale}}};
+    hipLaunchKernelGGL((lora_proj_mfma<TIn, 1>), dim3((unsigned)((rmax_rows + 16 * kProjRowGroups - 1) /
+                                                                  (16 * kProjRowGroups))),
+                       dim3(64 * kProjWaves), 0,
+                       c.stream, L, offsets, r, jobs);
     return hipGetLastError();
   }
   if (out_hl) return hipErrorInvalidValue;  // the high/low output exists on the matrix-core path only
@@ -590,13 +637,34 @@ hipError_t launch_lora_bwd(const Ctx& c, const moe_shape_t& sh, const Workspace&
 #define MOE_TRY(x) \
   if ((err = (x)) != hipSuccess) return err
   MOE_TRY(launch_row_tiles(c, offsets, L, max_tiles, ws.gemm_tiles));
-  MOE_TRY(launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, x_rows, d, x_src, nullptr, d, lo.a_up, true, r, ws.zu));
-  MOE_TRY(launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, H, 3 * f, nullptr, nullptr, f, lo.a_down, true, r, ws.zd));
-  // dO B_d (row-scaled, fp32) and, for the packed dH product's extra K step,
-  // s dY B_d as bf16 high/low parts (the row gate scales the whole dH there)
+  // Z_u = X A_u^T, Z_d = H A_d^T, and dO B_d (row-scaled, fp32) plus, for the
+  // packed dH product's extra K step, s dY B_d as bf16 high/low parts (the
+  // row gate scales the whole dH there)
   const bool kx = dgu_packed && lo.r == 16 && ws.zx;
-  MOE_TRY(launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, dy, d, row_src, row_gate, d, lo.b_down, false, r, ws.wproj,
-                                      ws.lora_mt, kx ? ws.zx : nullptr, lo.scale));
+  if (rmax > 0 && r <= 16 && d % 32 == 0 && f % 32 == 0 && ws.lora_mt) {
+    // the three projections are independent: one launch, B_d made K-contiguous first
+    {
+      TimedLaunch tl(MOE_K_LORA_PROJ, c.stream);
+      const int64_t n = (int64_t)L * d;
+      hipLaunchKernelGGL(lora_transpose_kr, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, c.stream, lo.b_down, L,
+                         d, r, ws.lora_mt);
+      MOE_TRY(hipGetLastError());
+    }
+    ProjJobs<bf16_t, 3> jobs{{{x_rows, d, x_src, nullptr, d, lo.a_up, ws.zu, nullptr, 1.f},
+                              {H, 3 * f, nullptr, nullptr, f, lo.a_down, ws.zd, nullptr, 1.f},
+                              {dy, d, row_src, row_gate, d, ws.lora_mt, ws.wproj, kx ? ws.zx : nullptr, lo.scale}}};
+    TimedLaunch tl(MOE_K_LORA_PROJ, c.stream);
+    hipLaunchKernelGGL((lora_proj_mfma<bf16_t, 3>),
+                       dim3((unsigned)((rmax + 16 * kProjRowGroups - 1) / (16 * kProjRowGroups)), 3),
+                       dim3(64 * kProjWaves), 0,
+                       c.stream, L, offsets, r, jobs);
+    MOE_TRY(hipGetLastError());
+  } else {
+    MOE_TRY(launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, x_rows, d, x_src, nullptr, d, lo.a_up, true, r, ws.zu));
+    MOE_TRY(launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, H, 3 * f, nullptr, nullptr, f, lo.a_down, true, r, ws.zd));
+    MOE_TRY(launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, dy, d, row_src, row_gate, d, lo.b_down, false, r,
+                                        ws.wproj, ws.lora_mt, kx ? ws.zx : nullptr, lo.scale));
+  }
   if (dgu_packed) {
     if (kx) MOE_TRY(launch_lora_transpose_rn(c, lo.a_down, L, r, f, ws.lora_mt));
     MOE_TRY(launch_lora_dh_packed(c, sh, ws, lo, dy, row_src, row_gate, offsets, act_save, dgu_packed,
