@@ -349,6 +349,53 @@ def test_forward_graph_replays_match_eager(name):
         torch.cuda.synchronize()
 
 
+def test_lora_step_deterministic_and_graph_replays_match_eager():
+    """The whole LoRA step (forward with adapters and softmax sums, load-balance
+    loss, packed adapter backward) gives bitwise equal results on two eager
+    runs, and captured as one HIP graph every replay (outputs cleared before
+    each, eager work in between) reproduces the eager results bitwise."""
+    w = W("lora_graph", T=300, d=256, E=16, k=4, f=128, e_lo=2, e_hi=13, lora_r=16, lora_alpha=32.0,
+          lora_b="normal", aux_coef=0.01)
+    say("[case lora step graph]")
+    inp = generate(w, seed=12)
+    dev = upload(inp)
+    shape = layer.shape_of(w)
+    L, r = w.L, w.lora_r
+    buf = layer.alloc(shape, lora_r=r, prob=True, act_save=True)
+    pk = layer.pack_weights(shape, dev["w_gate"], dev["w_up"], dev["w_down"])
+    dgu_p = torch.empty((L, w.f, w.d), dtype=torch.bfloat16, device="cuda")
+    B.moe_pack_backward_weights(shape, dev["w_gate"], dev["w_up"], dev["w_down"], dgu_p, None)
+    lora = B.make_lora(r, w.lora_alpha, dev["a_up"], dev["b_up"], dev["a_down"], dev["b_down"])
+    grads = [torch.empty(sz, device="cuda") for sz in ((L, r, w.d), (L, w.f, r), (L, r, w.f), (L, w.d, r))]
+
+    def step():
+        layer.forward(buf, dev["x"], dev["w_router"], None, None, None, None, lora, packed=pk)
+        B.moe_aux_loss(shape, buf.counts, buf.prob_sum, w.aux_coef, buf.aux)
+        xr, xs = layer.x_rows(buf, dev["x"])
+        B.moe_lora_bwd_packed(shape, lora, dev["dy"], buf.offsets, buf.row_src, buf.row_gate, xr, xs,
+                              buf.act_save, dgu_p, *grads, buf.ws)
+
+    outs = lambda: [buf.topk_idx, buf.topk_gate, buf.prob_sum, buf.y, buf.aux, *grads]
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs()]
+    step()
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(zip(ref, outs())):
+        assert torch.equal(a, b), f"eager rerun differs in output {i}"
+    g = layer.capture(step)
+    for rep in range(3):
+        for t in outs():
+            t.fill_(-1 if t.dtype == torch.int32 else 7.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(ref, outs())):
+            assert torch.equal(a, b), (rep, i)
+        step()  # eager work between replays
+        torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("T,need", [(12000, 8192), (20000, 16384)])
 def test_capacity_large_expert(T, need):
     """One expert receives nearly every token: more candidates than the
