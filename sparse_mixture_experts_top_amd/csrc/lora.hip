@@ -10,13 +10,23 @@
 //   db_up   = s dU^T Z_u               da_up   = s (dU B_u)^T X
 //
 // Kernels:
-//   rowproj    one wave per row: out[p, 0..r) = scale_p * in[src_p] . M rows
-//              (the rank-r projections Z_u, Z_d, dO B_d, dU B_u), fp32
-//   dh         MFMA GEMM of the gathered dY rows against W_d (stored [d, f],
-//              so B is transposed while staged into LDS), scaled by the row
-//              gate, plus the rank-r term, times silu(G) -> dU (fp32)
-//   seg_outer  per expert and column block: sum over the expert's rows of
-//              P[p, q] * Q[p, c] -> the gradients, fp32, rows in order
+//   proj_mfma  the rank-r projections (Z_u, Z_d, dO B_d, dU B_u) on the matrix
+//              cores, 16 dispatched rows per workgroup, K split over its
+//              waves; fp32 out and/or s * (.) as bf16 high/low parts (the A
+//              operand of the grouped GEMMs' extra adapter K step); several
+//              independent projections in one launch
+//   rowproj    the plain fallback (r > 16 or unaligned shapes): one wave per
+//              row, fp32
+//   transpose  [L, K, r] -> [L, r, K] (K-contiguous adapter rows for the
+//              projections) and [L, r, N] -> [L, N, r] (the adapter rows of an
+//              extra K step)
+//   dh         the register-staged dH GEMM for unpacked W_d (the packed path
+//              runs on the DMA engine in expert_gemm.hip): g dY W_d plus the
+//              rank-r term, times silu(G) -> dU (fp32)
+//   seg_outer16  per expert and column block: sum over the expert's rows of
+//              P[p, q] * V[p, c] -> the gradients, fp32, 16 waves over the
+//              rows and a fixed-order reduction (seg_outer: the plain
+//              fallback for r > 16)
 #include "common.h"
 #include "mfma_tile.h"
 
@@ -106,11 +116,11 @@ __device__ __forceinline__ int segment_of_uniform(const int32_t* off, int L, int
 // Eight consecutive K values of one row as an MFMA operand: bf16 as is; fp32
 // split into a bf16 high part and the bf16 rounding of the remainder (their
 // sum carries about 16 significant bits).
-__device__ __forceinline__ void frag_load(const bf16_t* p, bf16x8& hi, bf16x8& lo, bool) {
+__device__ __forceinline__ void frag_load(const bf16_t* p, bf16x8& hi, bf16x8& lo) {
   hi = *reinterpret_cast<const bf16x8*>(p);
   (void)lo;
 }
-__device__ __forceinline__ void frag_load(const float* p, bf16x8& hi, bf16x8& lo, bool) {
+__device__ __forceinline__ void frag_load(const float* p, bf16x8& hi, bf16x8& lo) {
   const float4 a = *reinterpret_cast<const float4*>(p);
   const float4 b = *reinterpret_cast<const float4*>(p + 4);
   const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
@@ -210,7 +220,7 @@ __global__ __launch_bounds__(64 * kProjWaves) void lora_proj_mfma(int L, const i
         if (st < nsteps) {
           b[j] = *reinterpret_cast<const bf16x8*>(b_ptr + (int64_t)st * 32);
 #pragma unroll
-          for (int g = 0; g < RG; ++g) frag_load(a_ptr[g] + (int64_t)st * 32, ah[j][g], al[j][g], kSplit);
+          for (int g = 0; g < RG; ++g) frag_load(a_ptr[g] + (int64_t)st * 32, ah[j][g], al[j][g]);
         }
       }
 #pragma unroll
