@@ -405,38 +405,54 @@ def backward_pass(w, dev, shape, packed, R, active, reps=5):
         wr_packed = torch.empty((d, E), dtype=torch.bfloat16, device="cuda")
         B.moe_pack_router_bwd(shape, dev["w_router"], wr_packed)
 
-    def step():
+    # both packed: the router product is stored into dx and the expert rows
+    # are added only for tokens with a kept local slot
+    fused = bwd_packed is not None and wr_packed is not None
+    t_kept = int((buf.slot >= 0).any(dim=1).sum().item())
+
+    def step(fuse):
         B.moe_gate_bwd(shape, dev["dy"], buf.y_perm, buf.slot, buf.topk_idx, buf.topk_gate, buf.logits,
                        buf.counts, 0.01, dgate, dlogits)
         if bwd_packed is not None:
             B.moe_expert_bwd_packed(shape, None, dev["dy"], buf.offsets, buf.row_src, buf.row_gate, buf.slot,
-                                    buf.act_save, bwd_packed[0], bwd_packed[1], dgu, dx_rows, dx, buf.ws)
+                                    buf.act_save, bwd_packed[0], bwd_packed[1], dgu, dx_rows,
+                                    None if fuse else dx, buf.ws)
         else:
             B.moe_expert_bwd(shape, None, dev["dy"], buf.offsets, buf.row_src, buf.row_gate, buf.slot,
                              buf.act_save, dev["w_gate"], dev["w_up"], dev["w_down"], dgu, dx_rows, dx, buf.ws)
-        if wr_packed is not None:
+        if fuse:
+            B.moe_router_bwd_unpermute_packed(shape, dlogits, wr_packed, dx_rows, buf.slot, dx, buf.ws)
+        elif wr_packed is not None:
             B.moe_router_bwd_packed(shape, dlogits, wr_packed, dx, buf.ws)
         else:
             B.moe_router_bwd(shape, dlogits, dev["w_router"], dx, buf.ws)
 
-    step()
-    torch.cuda.synchronize()
     names = ["gate_bwd", "tiles", "expert_dgu", "expert_dx", "unpermute", "router_bwd"]
-    B.moe_timing_enable(names)
-    for _ in range(reps):
-        step()
-    torch.cuda.synchronize()
-    us = {}
-    for n in names:
-        ms, cnt = B.moe_timing_read(n)
-        if cnt:
-            us[n] = 1000.0 * ms / cnt
-    B.moe_timing_enable(False)
+
+    def timed(fuse):
+        step(fuse)
+        torch.cuda.synchronize()
+        B.moe_timing_enable(names)
+        for _ in range(reps):
+            step(fuse)
+        torch.cuda.synchronize()
+        us = {}
+        for n in names:
+            ms, cnt = B.moe_timing_read(n)
+            if cnt:
+                us[n] = 1000.0 * ms / cnt
+        B.moe_timing_enable(False)
+        return us
+
+    two_pass = timed(False) if fused else None
+    us = timed(fused)
     work = {
         "gate_bwd": ("hbm", R * d * 2 + T * d * 2 + 2 * T * E * 4 + T * k * 16),
         "expert_dgu": ("hbm", active * d * f * 2 + R * d * 2 + 4 * R * f * 2),
         "expert_dx": ("hbm", 2 * active * f * d * 2 + 2 * R * f * 2 + R * d * 4),
-        "unpermute": ("hbm", R * d * 4 + T * d * 4 + T * k * 4),
+        # two-pass: every token's dx written; combined: dx read and written
+        # for the tokens with a kept slot only
+        "unpermute": ("hbm", R * d * 4 + T * k * 4 + (2 * t_kept * d * 4 if fused else T * d * 4)),
         "router_bwd": ("mfma", 2.0 * T * E * d),
     }
     flops = {"expert_dgu": 2.0 * R * d * f, "expert_dx": 4.0 * R * f * d, "router_bwd": 2.0 * T * E * d}
@@ -454,11 +470,16 @@ def backward_pass(w, dev, shape, packed, R, active, reps=5):
                 st["tflops"] = round(flops[name] / (us[name] * 1e-6) / 1e12, 1)
         stages[name] = st
     total = sum(us.values())
-    return {"us_per_step": round(total, 2), "tokens_per_s": round(T / (total * 1e-6), 1),
-            "kernels_us": {n: round(v, 2) for n, v in us.items()}, "stage_roofline": stages,
-            "packed_weights": bwd_packed is not None,
-            "note": "gate + logit gradients (load-balance coef 0.01), dx through experts and router; "
-                    "sum of per-kernel event times, outside the timed region"}
+    res = {"us_per_step": round(total, 2), "tokens_per_s": round(T / (total * 1e-6), 1),
+           "kernels_us": {n: round(v, 2) for n, v in us.items()}, "stage_roofline": stages,
+           "packed_weights": bwd_packed is not None, "router_then_row_sums": fused,
+           "tokens_with_local_rows": t_kept,
+           "note": "gate + logit gradients (load-balance coef 0.01), dx through experts and router; "
+                   "sum of per-kernel event times, outside the timed region"}
+    if two_pass is not None:
+        res["two_pass"] = {"us_per_step": round(sum(two_pass.values()), 2),
+                           "kernels_us": {n: round(v, 2) for n, v in two_pass.items()}}
+    return res
 
 
 if __name__ == "__main__":

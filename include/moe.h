@@ -339,7 +339,9 @@ moe_status_t moe_pack_backward_weights(const moe_shape_t* shape, const void* w_g
 
 /* moe_expert_bwd with the packed transposed weights: the two grouped GEMMs
  * stream contiguous weight tiles on the DMA engine of the forward. Same
- * arguments otherwise; same results up to the fp32 summation order. */
+ * arguments otherwise; same results up to the fp32 summation order. dx may
+ * be NULL here (and slot with it): the per-token sum of dx_rows is then
+ * skipped, for moe_router_bwd_unpermute_packed to form it. */
 moe_status_t moe_expert_bwd_packed(const moe_shape_t* shape, const moe_lora_t* lora, const void* dy,
                                    const int32_t* offsets, const int32_t* row_src, const float* row_gate,
                                    const int32_t* slot, const void* act_save, const void* dgu_packed,
@@ -367,6 +369,26 @@ moe_status_t moe_pack_router_bwd(const moe_shape_t* shape, const void* w_router,
  * fp32 accumulation). */
 moe_status_t moe_router_bwd_packed(const moe_shape_t* shape, const float* dlogits, const void* wr_packed,
                                    float* dx, void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* The two parts of dx in one call (backward of "Switch Transformers:
+ * Scaling to Trillion Parameter Models with Simple and Efficient Sparsity",
+ * §2.1, through the gate and through the experts):
+ *   dx[t] = sum over the token's slots j with slot[t, j] >= 0, in j order,
+ *           of dx_rows[slot[t, j]]  +  sum_e dlogits[t, e] w_router[e]
+ * bitwise equal to moe_expert_bwd_packed's unpermute followed by
+ * moe_router_bwd_packed. The product is stored (dx is not read for it),
+ * then the rows are added for the tokens that have a kept slot only: where
+ * most slots are remote (a local expert range) most of dx is written once
+ * and never read. Three kernels on the stream, in order: dlogits to bf16
+ * (in the workspace), the product, the row sums.
+ *   dlogits [T, E] f32, wr_packed as for moe_router_bwd_packed,
+ *   dx_rows [Rmax, d] f32 (moe_expert_bwd_packed with dx NULL; read only
+ *   through kept slots, so NULL is accepted when no rows are local),
+ *   slot [T, k] int32 (moe_dispatch), dx [T, d] f32 OUT.
+ * bf16 only, d % 128 == 0, E % 64 == 0, else MOE_ERR_UNSUPPORTED. */
+moe_status_t moe_router_bwd_unpermute_packed(const moe_shape_t* shape, const float* dlogits,
+                                             const void* wr_packed, const float* dx_rows, const int32_t* slot,
+                                             float* dx, void* ws, size_t ws_bytes, moe_stream_t stream);
 
 /* ---- kernel timing (profiling aid) -------------------------------------
  * When enabled for a kernel kind, the library records a pair of HIP events

@@ -29,7 +29,8 @@ EXPORTED = ["moe_workspace_bytes", "moe_max_rows", "moe_last_error", "moe_route"
             "moe_dispatch", "moe_expert_gemm", "moe_pack_expert_weights", "moe_expert_gemm_packed",
             "moe_combine", "moe_aux_loss", "moe_lora_bwd", "moe_lora_bwd_packed", "moe_gate_bwd", "moe_expert_bwd",
             "moe_router_bwd", "moe_pack_backward_weights", "moe_expert_bwd_packed", "moe_pack_router_bwd",
-            "moe_router_bwd_packed", "moe_timing_enable", "moe_timing_read"]
+            "moe_router_bwd_packed", "moe_router_bwd_unpermute_packed", "moe_timing_enable",
+            "moe_timing_read"]
 
 
 class MoeShape(ctypes.Structure):
@@ -80,6 +81,7 @@ def lib() -> ctypes.CDLL:
     L.moe_pack_backward_weights.argtypes = [shp, vp, vp, vp, vp, vp, vp]
     L.moe_pack_router_bwd.argtypes = [shp, vp, vp, vp]
     L.moe_router_bwd_packed.argtypes = [shp, vp, vp, vp, vp, sz, vp]
+    L.moe_router_bwd_unpermute_packed.argtypes = [shp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_expert_bwd_packed.argtypes = [shp, lor, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_timing_enable.argtypes = [i32]
     L.moe_timing_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
@@ -87,7 +89,7 @@ def lib() -> ctypes.CDLL:
                "moe_expert_gemm_packed", "moe_combine", "moe_aux_loss", "moe_lora_bwd", "moe_lora_bwd_packed",
                "moe_gate_bwd", "moe_expert_bwd", "moe_router_bwd", "moe_pack_backward_weights",
                "moe_expert_bwd_packed", "moe_pack_router_bwd", "moe_router_bwd_packed",
-               "moe_timing_enable", "moe_timing_read"):
+               "moe_router_bwd_unpermute_packed", "moe_timing_enable", "moe_timing_read"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
     return L
@@ -263,6 +265,13 @@ def moe_router_bwd_packed(shape, dlogits, wr_packed, dx, ws, stream=None):
     _check(lib().moe_router_bwd_packed(ctypes.byref(shape), _dev(dlogits, torch.float32),
                                        _dev(wr_packed, torch.bfloat16), _dev(dx, torch.float32),
                                        _dev(ws, torch.uint8), ws.numel(), _stream(stream)))
+
+
+def moe_router_bwd_unpermute_packed(shape, dlogits, wr_packed, dx_rows, slot, dx, ws, stream=None):
+    _check(lib().moe_router_bwd_unpermute_packed(ctypes.byref(shape), _dev(dlogits, torch.float32),
+                                                 _dev(wr_packed, torch.bfloat16), _dev(dx_rows, torch.float32),
+                                                 _dev(slot, torch.int32), _dev(dx, torch.float32),
+                                                 _dev(ws, torch.uint8), ws.numel(), _stream(stream)))
 
 
 def moe_router_bwd(shape, dlogits, w_router, dx, ws, stream=None):

@@ -552,13 +552,12 @@ moe_status_t moe_expert_bwd_packed(const moe_shape_t* shape, const moe_lora_t* l
   MOE_REQUIRE(offsets, "offsets");
   MOE_REQUIRE_IF(rows, row_src, "row_src");
   MOE_REQUIRE_IF(rows, row_gate, "row_gate");
-  MOE_REQUIRE_IF(s.T > 0, slot, "slot");
+  MOE_REQUIRE_IF(s.T > 0 && dx, slot, "slot");
   MOE_REQUIRE_IF(rows, act_save, "act_save");
   MOE_REQUIRE(dgu_packed, "dgu_packed");
   MOE_REQUIRE(dx_packed, "dx_packed");
   MOE_REQUIRE_IF(rows, dgu, "dgu");
   MOE_REQUIRE_IF(rows, dx_rows, "dx_rows");
-  MOE_REQUIRE_IF(s.T > 0, dx, "dx");
   if ((st = check_ws(s, lora ? lora->r : 0, ws, ws_bytes)) != MOE_OK) return st;
   Ctx c;
   if ((st = make_ctx(stream, &c)) != MOE_OK) return st;
@@ -572,6 +571,7 @@ moe_status_t moe_expert_bwd_packed(const moe_shape_t* shape, const moe_lora_t* l
     la.a_down = static_cast<const bf16_t*>(lora->a_down);
     la.b_down = static_cast<const bf16_t*>(lora->b_down);
   }
+  // dx null: the per-token sum is left to moe_router_bwd_unpermute_packed
   return hip_status(launch_expert_bwd(c, s, w, lora ? &la : nullptr, dy, offsets, row_src, row_gate, slot,
                                       act_save, nullptr, nullptr, nullptr, dgu_packed, dx_packed, dgu, dx_rows,
                                       dx),
@@ -622,6 +622,27 @@ moe_status_t moe_router_bwd_packed(const moe_shape_t* shape, const float* dlogit
   if ((st = make_ctx(stream, &c)) != MOE_OK) return st;
   const Workspace w = carve_workspace(s, 0, ws);
   return hip_status(launch_router_bwd(c, s, w, dlogits, nullptr, wr_packed, dx), "router backward (packed)");
+}
+
+moe_status_t moe_router_bwd_unpermute_packed(const moe_shape_t* shape, const float* dlogits,
+                                             const void* wr_packed, const float* dx_rows, const int32_t* slot,
+                                             float* dx, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  moe_status_t st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape_t& s = *shape;
+  if (s.dtype != MOE_BF16 || s.d % 128 != 0 || s.E % 64 != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "packed router weights need bf16, d % 128 == 0 and E % 64 == 0");
+  MOE_REQUIRE_IF(s.T > 0, dlogits, "dlogits");
+  MOE_REQUIRE(wr_packed, "wr_packed");
+  MOE_REQUIRE_IF(max_rows(s) > 0, dx_rows, "dx_rows");
+  MOE_REQUIRE_IF(s.T > 0, slot, "slot");
+  MOE_REQUIRE_IF(s.T > 0, dx, "dx");
+  if ((st = check_ws(s, 0, ws, ws_bytes)) != MOE_OK) return st;
+  Ctx c;
+  if ((st = make_ctx(stream, &c)) != MOE_OK) return st;
+  const Workspace w = carve_workspace(s, 0, ws);
+  return hip_status(launch_router_bwd(c, s, w, dlogits, nullptr, wr_packed, dx, dx_rows, slot),
+                    "router backward + unpermute (packed)");
 }
 
 moe_status_t moe_timing_enable(int32_t mask) {

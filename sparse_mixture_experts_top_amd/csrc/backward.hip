@@ -462,7 +462,9 @@ __device__ __forceinline__ void unpermute_batch(float4& acc, const float* __rest
   }
 }
 
-template <int TB>
+// ADD: dx[t] += the sum, only for tokens with a kept slot (the rest of dx
+// is neither read nor written).
+template <int TB, bool ADD>
 __global__ __launch_bounds__(256) void unpermute_sum_f32(const float* __restrict__ dx_rows,
                                                          const int32_t* __restrict__ slot, int T, int k,
                                                          int d, float* __restrict__ dx) {
@@ -482,16 +484,48 @@ __global__ __launch_bounds__(256) void unpermute_sum_f32(const float* __restrict
     __syncthreads();
     for (int q = 0; q < nq; ++q) {
       const int n = s_n[q];
+      if (ADD && n == 0) continue;   // uniform: s_n is shared
       for (int v = threadIdx.x; v < nvec; v += blockDim.x) {
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
         int j0 = 0;
         for (; j0 + 8 <= n; j0 += 8) unpermute_batch<8>(acc, dx_rows, s_slot[q], j0, 8, d, v);
         for (; j0 < n; j0 += 2) unpermute_batch<2>(acc, dx_rows, s_slot[q], j0, n - j0, d, v);
-        *reinterpret_cast<float4*>(dx + (int64_t)(t0 + q) * d + v * 4) = acc;
+        float4* p = reinterpret_cast<float4*>(dx + (int64_t)(t0 + q) * d + v * 4);
+        if (ADD) {
+          const float4 o = *p;
+          acc.x = o.x + acc.x;
+          acc.y = o.y + acc.y;
+          acc.z = o.z + acc.z;
+          acc.w = o.w + acc.w;
+        }
+        *p = acc;
       }
     }
     __syncthreads();
   }
+}
+
+hipError_t launch_unpermute(const Ctx& c, const moe_shape_t& s, const float* dx_rows, const int32_t* slot,
+                            float* dx, bool add) {
+  if (s.T == 0) return hipSuccess;
+  TimedLaunch tl(MOE_K_UNPERMUTE, c.stream);
+  int tb = s.T / (c.num_cus * 8);
+  tb = tb >= 8 ? 8 : tb >= 4 ? 4 : tb >= 2 ? 2 : 1;
+  const int nblk = (s.T + tb - 1) / tb;
+  const int grid = nblk < c.num_cus * 64 ? nblk : c.num_cus * 64;
+#define MOE_UNP(N)                                                                                       \
+  if (add)                                                                                               \
+    hipLaunchKernelGGL((unpermute_sum_f32<N, true>), dim3(grid), dim3(256), 0, c.stream, dx_rows, slot, \
+                       s.T, s.k, s.d, dx);                                                               \
+  else                                                                                                   \
+    hipLaunchKernelGGL((unpermute_sum_f32<N, false>), dim3(grid), dim3(256), 0, c.stream, dx_rows, slot, \
+                       s.T, s.k, s.d, dx)
+  if (tb == 8) MOE_UNP(8);
+  else if (tb == 4) MOE_UNP(4);
+  else if (tb == 2) MOE_UNP(2);
+  else MOE_UNP(1);
+#undef MOE_UNP
+  return hipGetLastError();
 }
 
 hipError_t launch_expert_bwd(const Ctx& c, const moe_shape_t& s, const Workspace& ws, const LoraArgs* lo,
@@ -557,21 +591,7 @@ hipError_t launch_expert_bwd(const Ctx& c, const moe_shape_t& s, const Workspace
       MOE_TRY(hipGetLastError());
     }
   }
-  if (s.T > 0) {
-    TimedLaunch tl(MOE_K_UNPERMUTE, c.stream);
-    int tb = s.T / (c.num_cus * 8);
-    tb = tb >= 8 ? 8 : tb >= 4 ? 4 : tb >= 2 ? 2 : 1;
-    const int nblk = (s.T + tb - 1) / tb;
-    const int grid = nblk < c.num_cus * 64 ? nblk : c.num_cus * 64;
-#define MOE_UNP(N) \
-  hipLaunchKernelGGL(unpermute_sum_f32<N>, dim3(grid), dim3(256), 0, c.stream, dx_rows, slot, s.T, s.k, d, dx)
-    if (tb == 8) MOE_UNP(8);
-    else if (tb == 4) MOE_UNP(4);
-    else if (tb == 2) MOE_UNP(2);
-    else MOE_UNP(1);
-#undef MOE_UNP
-    MOE_TRY(hipGetLastError());
-  }
+  if (s.T > 0 && dx) MOE_TRY(launch_unpermute(c, s, dx_rows, slot, dx, false));
 #undef MOE_TRY
   return hipSuccess;
 }
@@ -649,8 +669,26 @@ __global__ __launch_bounds__(256) void router_bwd_simple(const float* __restrict
 }
 
 hipError_t launch_router_bwd(const Ctx& c, const moe_shape_t& s, const Workspace& ws, const float* dlogits,
-                             const void* w_router, const void* wr_packed, float* dx) {
+                             const void* w_router, const void* wr_packed, float* dx, const float* dx_rows,
+                             const int32_t* slot) {
   if (s.T == 0) return hipSuccess;
+  if (slot) {
+    // dx = the product (stored, not added), then the expert rows added where
+    // a token has any: dx is read only for those tokens
+    if (s.dtype != MOE_BF16 || s.E % 64 != 0 || !wr_packed) return hipErrorInvalidValue;
+    {
+      TimedLaunch tl(MOE_K_ROUTER_BWD, c.stream);
+      bf16_t* dlb = reinterpret_cast<bf16_t*>(ws.logits);
+      const int64_t n = (int64_t)s.T * s.E;
+      const int cgrid = (int)std::min<int64_t>((n / 8 + 255) / 256, (int64_t)c.num_cus * 16);
+      hipLaunchKernelGGL(to_bf16_rows, dim3(cgrid), dim3(256), 0, c.stream, dlogits, n, dlb);
+      hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return err;
+      err = launch_router_bwd_packed(c, s, dlb, (const bf16_t*)wr_packed, dx, true);
+      if (err != hipSuccess) return err;
+    }
+    return launch_unpermute(c, s, dx_rows, slot, dx, true);
+  }
   TimedLaunch tl(MOE_K_ROUTER_BWD, c.stream);
   if (s.dtype == MOE_BF16 && s.E % 64 == 0) {
     using Cfg = TileCfg<128, 128>;

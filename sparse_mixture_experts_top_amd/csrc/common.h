@@ -264,11 +264,18 @@ hipError_t launch_pack_bwd(const Ctx& c, const moe_shape_t& s, const void* w_gat
                            const void* w_down, void* dgu_packed, void* dx_packed);
 
 hipError_t launch_pack_router_bwd(const Ctx& c, const moe_shape_t& s, const void* w_router, void* wr_packed);
+// dx += dl . W_r, or with store set dx = dl . W_r (dx not read)
 hipError_t launch_router_bwd_packed(const Ctx& c, const moe_shape_t& s, const bf16_t* dl, const bf16_t* wr_packed,
-                                    float* dx);
+                                    float* dx, bool store = false);
+
+// dx[t] = sum over the token's kept slots j, in j order, of dx_rows[slot];
+// with add, dx[t] += that sum for tokens with a kept slot, others untouched
+hipError_t launch_unpermute(const Ctx& c, const moe_shape_t& s, const float* dx_rows, const int32_t* slot,
+                            float* dx, bool add);
 
 hipError_t launch_router_bwd(const Ctx& c, const moe_shape_t& s, const Workspace& ws, const float* dlogits,
-                             const void* w_router, const void* wr_packed, float* dx);
+                             const void* w_router, const void* wr_packed, float* dx,
+                             const float* dx_rows = nullptr, const int32_t* slot = nullptr);
 
 // LoRA building blocks shared by the forward (expert_gemm) and the backward.
 // out[p, q] = scale_p * sum_i in[src(p), i] * M(le(p), q, i) for rows p < R.

@@ -712,7 +712,9 @@ __global__ __launch_bounds__(256) void pack_trans(const bf16_t* __restrict__ src
 // Router part of dx on the DMA engine: dx[t, n] += dl_bf16[t] . W_r^T[n]
 // (W_r^T packed like the expert tiles, rows n < d, K = E), dense items of
 // 128 tokens x BN columns; the epilogue adds into the fp32 dx.
-template <class Cfg>
+// STORE: dx = the product, written without reading dx (the expert part is
+// added afterwards, only where a token has local rows).
+template <class Cfg, bool STORE = false>
 struct RouterBwdPackedProb {
   const bf16_t* dl;      // [T, E] bf16
   const bf16_t* packed;  // W_r^T tiles
@@ -751,7 +753,8 @@ struct RouterBwdPackedProb {
         if (n0 + wn * (Cfg::BN / Cfg::WN) + j * 16 >= d) continue;
         const int n = n0 + dma_out_col<Cfg>(wn, j, lane);
         float4* p = reinterpret_cast<float4*>(dx + (int64_t)m * d + n);
-        float4 v = *p;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if constexpr (!STORE) v = *p;
         v.x += acc.v[i][j][0];
         v.y += acc.v[i][j][1];
         v.z += acc.v[i][j][2];
@@ -761,21 +764,25 @@ struct RouterBwdPackedProb {
     }
   }
 };
-
-template <class Cfg>
-__global__ __launch_bounds__(Cfg::THREADS, Cfg::WAVES_PER_SIMD) void router_bwd_dma(RouterBwdPackedProb<Cfg> pb,
+template <class Cfg, bool STORE>
+__global__ __launch_bounds__(Cfg::THREADS, Cfg::WAVES_PER_SIMD) void router_bwd_dma(RouterBwdPackedProb<Cfg, STORE> pb,
                                                                                    int items) {
   persistent_gemm_dma<Cfg>(pb, items, pb.E / Cfg::BK);
 }
 
 hipError_t launch_router_bwd_packed(const Ctx& c, const moe_shape_t& s, const bf16_t* dl, const bf16_t* wr_packed,
-                                    float* dx) {
+                                    float* dx, bool store) {
   using Cfg = GemmCfgWide;
   const int nt = (s.d + Cfg::BN - 1) / Cfg::BN;
   const int items = ((s.T + Cfg::BM - 1) / Cfg::BM) * nt;
   const int grid = std::min(((items + 7) / 8) * 8, c.num_cus);
-  RouterBwdPackedProb<Cfg> pb{dl, wr_packed, s.T, s.E, s.d, nt, dx};
-  hipLaunchKernelGGL(router_bwd_dma<Cfg>, dim3(grid), dim3(Cfg::THREADS), 0, c.stream, pb, items);
+  if (store) {
+    RouterBwdPackedProb<Cfg, true> pb{dl, wr_packed, s.T, s.E, s.d, nt, dx};
+    hipLaunchKernelGGL((router_bwd_dma<Cfg, true>), dim3(grid), dim3(Cfg::THREADS), 0, c.stream, pb, items);
+  } else {
+    RouterBwdPackedProb<Cfg, false> pb{dl, wr_packed, s.T, s.E, s.d, nt, dx};
+    hipLaunchKernelGGL((router_bwd_dma<Cfg, false>), dim3(grid), dim3(Cfg::THREADS), 0, c.stream, pb, items);
+  }
   return hipGetLastError();
 }
 

@@ -132,3 +132,23 @@ def test_lora_backward_packed_validates_on_the_host():
                                        None) == B.MOE_ERR_UNSUPPORTED
     assert lib.moe_lora_bwd_packed(ctypes.byref(bf), ctypes.byref(lora), *([fake] * 13), 16,
                                    None) == B.MOE_ERR_WORKSPACE
+
+
+def test_router_backward_with_unpermute_validates_on_the_host():
+    lib = B.lib()
+    fake = ctypes.c_void_p(0x100000)      # never dereferenced: validation fails first
+    ok = shape(dtype=B.MOE_BF16, d=128, f=128, E=64, e_hi=64)
+    # the product runs on the packed transpose: bf16, d % 128 == 0, E % 64 == 0
+    for bad in (shape(dtype=B.MOE_BF16, d=128, f=128),                      # E = 16
+                shape(dtype=B.MOE_F32, d=128, f=128, E=64, e_hi=64),
+                shape(dtype=B.MOE_BF16, d=192, f=128, E=64, e_hi=64)):
+        assert lib.moe_router_bwd_unpermute_packed(ctypes.byref(bad), *([fake] * 5), fake, 1 << 30,
+                                                   None) == B.MOE_ERR_UNSUPPORTED
+    for i, name in enumerate(["dlogits", "wr_packed", "dx_rows", "slot", "dx"]):
+        args = [fake] * 5
+        args[i] = None
+        assert lib.moe_router_bwd_unpermute_packed(ctypes.byref(ok), *args, fake, 1 << 30,
+                                                   None) == B.MOE_ERR_INVALID_ARG, name
+        assert f"{name} is NULL".encode() in lib.moe_last_error()
+    assert lib.moe_router_bwd_unpermute_packed(ctypes.byref(ok), *([fake] * 5), fake, 16,
+                                               None) == B.MOE_ERR_WORKSPACE

@@ -28,6 +28,8 @@ CASES = {
     "router128_bf16": W("router128_bf16", T=333, d=320, E=128, k=4, f=64),
     # packable for every backward product (d, f % 128 == 0, E % 64 == 0)
     "router128p_bf16": W("router128p_bf16", T=333, d=256, E=128, k=4, f=128),
+    # the same with a local expert range: most slots are remote (-1)
+    "router128p_local_bf16": W("router128p_local_bf16", T=333, d=256, E=128, k=4, f=128, e_lo=40, e_hi=52),
     "lora_bf16": W("lora_bf16", T=256, d=128, E=12, k=4, f=128, e_lo=2, e_hi=9, lora_r=16,
                    lora_alpha=32.0, lora_b="normal"),
     # ~300 rows per expert: the layout with two compute waves per SIMD (three
@@ -88,12 +90,21 @@ def run_backward(w, dev, buf, packed=False):
         B.moe_pack_router_bwd(s, dev["w_router"], wr_p)
         B.moe_router_bwd_packed(s, out["dlogits"], wr_p, out["dx_router"], buf.ws)
         B.moe_router_bwd_packed(s, out["dlogits"], wr_p, out["dx"], buf.ws)  # accumulates
+        # the fused pass: expert rows without their unpermute, then one pass
+        # that sums them per token and adds the router product
+        dgu2, rows2 = torch.empty_like(out["dgu"]), torch.full_like(out["dx_rows"], float("nan"))
+        B.moe_expert_bwd_packed(s, lora_of(w, dev), dev["dy"], buf.offsets, buf.row_src, buf.row_gate, None,
+                                buf.act_save, dgu_p, dx_p, dgu2, rows2, None, buf.ws)
+        out["dx_fused"] = torch.full((T, d), float("nan"), device="cuda")
+        B.moe_router_bwd_unpermute_packed(s, out["dlogits"], wr_p, rows2, buf.slot, out["dx_fused"], buf.ws)
     else:
         B.moe_router_bwd(s, out["dlogits"], dev["w_router"], out["dx_router"], buf.ws)
         B.moe_router_bwd(s, out["dlogits"], dev["w_router"], out["dx"], buf.ws)  # accumulates
     torch.cuda.synchronize()
     # same products, so the accumulated result is exactly one fp32 addition
     assert torch.equal(out["dx"], out["dx_experts"] + out["dx_router"])
+    if "dx_fused" in out:   # same sums in the same order: bitwise equal
+        assert torch.equal(out["dx_fused"], out["dx"])
     return out
 
 
