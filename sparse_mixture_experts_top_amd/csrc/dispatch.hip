@@ -24,8 +24,9 @@
 //                 tokens of the tile with that expert; writes slot / row_src
 //                 / row_gate, or, for an expert over capacity, a candidate
 //                 (gate bits, assignment)
-//   K5 capacity   per over-capacity expert: C-th largest gate by radix
-//                 select (keys staged in LDS), ties to the lower token, then
+//   K5 capacity   per over-capacity expert: C-th largest gate (bitwise
+//                 search over keys held in registers, or radix select for
+//                 more than 8192 candidates), ties to the lower token, then
 //                 kept candidates in token order -> rows
 //   K7 gather     x_perm[p] = x[row_src[p]] with 16-byte loads and stores
 //                 (optional: the grouped GEMM can read x through row_src)
@@ -241,12 +242,14 @@ __device__ int block_exclusive_scan(int v, int* total) {
 //      1024 consecutive candidates, wave) ballot counts of the equal and then
 //      of the kept candidates, each turned into candidate-order offsets by one
 //      workgroup scan, a chunk of kCapRounds rounds at a time.
-// The candidates (keys and assignment indices) are staged in LDS when they
-// fit (kCapLds); larger experts read them from global memory in every pass.
+// Up to kCapLds candidates are held in registers (capacity_core_regs, which
+// finds g* by a bitwise search instead of the histograms); larger experts
+// read them from global memory in every pass.
 constexpr int kCapThreads = 1024;
 constexpr int kCapWaves = kCapThreads / 64;
 constexpr int kCapLds = 8192;
 constexpr int kCapRounds = 16;  // rounds of 1024 per chunk, (round, wave) counts in LDS
+static_assert(kCapLds % kCapThreads == 0, "LDS staging in whole rounds");
 
 struct CapShared {
   int hist[256];
@@ -369,28 +372,114 @@ __device__ __forceinline__ void capacity_core(CapShared& sh, Key key_at, Idx idx
   }
 }
 
+// The same selection for n <= kCapLds with the candidates in registers:
+// candidate i = u * kCapThreads + tid is kv[u] / iv[u] (round u of the
+// compaction). g* is found bit by bit, from the top: v | 2^b is kept as the
+// prefix when at least C candidates are >= it, one workgroup count per bit
+// (32 counts; each reads only registers, the per-wave counts alternate
+// between two LDS rows so one barrier per bit suffices). The counts are
+// exact, so g* and `need` equal the radix select's.
+template <int U>
+__device__ __forceinline__ void capacity_core_regs(CapShared& sh, const uint32_t (&kv)[U],
+                                                   const int32_t (&iv)[U], int n, int k, int capacity,
+                                                   int base, int32_t* __restrict__ slot,
+                                                   int32_t* __restrict__ row_src,
+                                                   float* __restrict__ row_gate) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  auto count_ge = [&](uint32_t t, int buf) {
+    int c = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) c += __popcll(__ballot(u * kCapThreads + tid < n && kv[u] >= t));
+    if (lane == 0) sh.cnt[buf * kCapWaves + wave] = c;
+    __syncthreads();
+    int tot = 0;
+#pragma unroll
+    for (int w = 0; w < kCapWaves; ++w) tot += sh.cnt[buf * kCapWaves + w];
+    return tot;
+  };
+  uint32_t v = 0u;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t t = v | (1u << b);
+    if (count_ge(t, b & 1) >= capacity) v = t;
+  }
+  // keys > g* are those >= g* + 1; row 1 of the counts was last read before
+  // the barrier of bit 0, and the barrier after this count ends its reads
+  // before the sweeps below reuse the rows
+  const uint32_t gstar = v;
+  const int above = gstar == 0xffffffffu ? 0 : count_ge(gstar + 1u, 1);
+  const int need_eq = capacity - above;
+  __syncthreads();
+  const uint64_t below = (1ull << lane) - 1ull;
+  // equal-gate ranks, then kept ranks, in candidate order
+  bool eqs[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    eqs[u] = u * kCapThreads + tid < n && kv[u] == gstar;
+    const uint64_t bal = __ballot(eqs[u]);
+    if (lane == 0) sh.cnt[u * kCapWaves + wave] = __popcll(bal);
+  }
+  __syncthreads();
+  int etot;
+  int pre = block_exclusive_scan<kCapWaves>(tid < U * kCapWaves ? sh.cnt[tid] : 0, &etot);
+  if (tid < U * kCapWaves) sh.pre[tid] = pre;
+  __syncthreads();
+  bool keep[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const bool in = u * kCapThreads + tid < n;
+    const int eq_rank = sh.pre[u * kCapWaves + wave] + __popcll(__ballot(eqs[u]) & below);
+    keep[u] = in && (kv[u] > gstar || (eqs[u] && eq_rank < need_eq));
+    const uint64_t kbal = __ballot(keep[u]);
+    if (lane == 0) sh.cnt[u * kCapWaves + wave] = __popcll(kbal);
+  }
+  __syncthreads();
+  int ktot;
+  pre = block_exclusive_scan<kCapWaves>(tid < U * kCapWaves ? sh.cnt[tid] : 0, &ktot);
+  if (tid < U * kCapWaves) sh.kpre[tid] = pre;
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint64_t kbal = __ballot(keep[u]);
+    if (u * kCapThreads + tid >= n) continue;
+    const int a = iv[u];
+    if (keep[u]) {
+      const int row = base + sh.kpre[u * kCapWaves + wave] + __popcll(kbal & below);
+      slot[a] = row;
+      row_src[row] = a / k;
+      row_gate[row] = __uint_as_float(kv[u]);
+    } else {
+      slot[a] = -1;
+    }
+  }
+}
+
 __global__ __launch_bounds__(kCapThreads) void dispatch_capacity(
     int k, int e_lo, int L, int capacity, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ cseg,
     const uint32_t* __restrict__ cand_key, const int32_t* __restrict__ cand_idx,
     int32_t* __restrict__ slot, int32_t* __restrict__ row_src, float* __restrict__ row_gate) {
-  __shared__ uint32_t s_keys[kCapLds];
-  __shared__ int32_t s_idx[kCapLds];
   __shared__ CapShared sh;
   const int le = blockIdx.x;
+  // the three loads issued together (le < L: all in bounds)
   const int n = counts[e_lo + le];
-  if (n <= capacity) return;
-  const uint32_t* ck = cand_key + cseg[le];
-  const int32_t* ci = cand_idx + cseg[le];
+  const int cs = cseg[le];
   const int base = offsets[le];
+  if (n <= capacity) return;
+  const uint32_t* ck = cand_key + cs;
+  const int32_t* ci = cand_idx + cs;
   if (n <= kCapLds) {
-    for (int i = threadIdx.x; i < n; i += kCapThreads) {
-      s_keys[i] = ck[i];
-      s_idx[i] = ci[i];
+    // all of a thread's loads in flight at once; the candidates stay in
+    // registers
+    constexpr int U = kCapLds / kCapThreads;
+    uint32_t kv[U];
+    int32_t iv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = u * kCapThreads + (int)threadIdx.x;
+      kv[u] = i < n ? ck[i] : 0u;
+      iv[u] = i < n ? ci[i] : 0;
     }
-    __syncthreads();
-    capacity_core(sh, [&](int i) { return s_keys[i]; }, [&](int i) { return s_idx[i]; }, n, k,
-                  capacity, base, slot, row_src, row_gate);
+    capacity_core_regs<U>(sh, kv, iv, n, k, capacity, base, slot, row_src, row_gate);
   } else {
     capacity_core(sh, [&](int i) { return ck[i]; }, [&](int i) { return ci[i]; }, n, k, capacity,
                   base, slot, row_src, row_gate);
