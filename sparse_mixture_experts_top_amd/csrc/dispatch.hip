@@ -376,9 +376,10 @@ __device__ __forceinline__ void capacity_core(CapShared& sh, Key key_at, Idx idx
 // candidate i = u * kCapThreads + tid is kv[u] / iv[u] (round u of the
 // compaction). g* is found bit by bit, from the top: v | 2^b is kept as the
 // prefix when at least C candidates are >= it, one workgroup count per bit
-// (32 counts; each reads only registers, the per-wave counts alternate
-// between two LDS rows so one barrier per bit suffices). The counts are
-// exact, so g* and `need` equal the radix select's.
+// (each reads only registers; the per-wave counts alternate between two LDS
+// rows so one barrier per bit suffices), stopping early once exactly C
+// candidates are >= the prefix. The counts are exact, so g* and `need`
+// equal the radix select's.
 template <int U>
 __device__ __forceinline__ void capacity_core_regs(CapShared& sh, const uint32_t (&kv)[U],
                                                    const int32_t (&iv)[U], int n, int k, int capacity,
@@ -386,10 +387,12 @@ __device__ __forceinline__ void capacity_core_regs(CapShared& sh, const uint32_t
                                                    int32_t* __restrict__ row_src,
                                                    float* __restrict__ row_gate) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // padding keys (i >= n) are 0 and every threshold tried is >= 1, so the
+  // compare alone decides
   auto count_ge = [&](uint32_t t, int buf) {
     int c = 0;
 #pragma unroll
-    for (int u = 0; u < U; ++u) c += __popcll(__ballot(u * kCapThreads + tid < n && kv[u] >= t));
+    for (int u = 0; u < U; ++u) c += __popcll(__ballot(kv[u] >= t));
     if (lane == 0) sh.cnt[buf * kCapWaves + wave] = c;
     __syncthreads();
     int tot = 0;
@@ -397,16 +400,36 @@ __device__ __forceinline__ void capacity_core_regs(CapShared& sh, const uint32_t
     for (int w = 0; w < kCapWaves; ++w) tot += sh.cnt[buf * kCapWaves + w];
     return tot;
   };
+  // v: the bits of g* fixed so far, cv = #keys >= v (>= C). Once cv == C the
+  // keys >= v are exactly the C largest and g* is the smallest of them.
   uint32_t v = 0u;
-  for (int b = 31; b >= 0; --b) {
+  int cv = n, buf = 0;
+  for (int b = 31; b >= 0 && cv != capacity; --b) {
     const uint32_t t = v | (1u << b);
-    if (count_ge(t, b & 1) >= capacity) v = t;
+    const int c = count_ge(t, buf);
+    buf ^= 1;
+    if (c >= capacity) {
+      v = t;
+      cv = c;
+    }
   }
-  // keys > g* are those >= g* + 1; row 1 of the counts was last read before
-  // the barrier of bit 0, and the barrier after this count ends its reads
-  // before the sweeps below reuse the rows
-  const uint32_t gstar = v;
-  const int above = gstar == 0xffffffffu ? 0 : count_ge(gstar + 1u, 1);
+  __syncthreads();  // the last count's reads end before its rows are reused
+  uint32_t gstar = v;
+  if (cv == capacity) {
+    uint32_t m = 0xffffffffu;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (u * kCapThreads + tid < n && kv[u] >= v) m = min(m, kv[u]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = min(m, (uint32_t)__shfl_xor((int)m, o, kWave));
+    if (lane == 0) sh.hist[wave] = (int)m;
+    __syncthreads();
+    uint32_t mm = 0xffffffffu;
+    for (int w = 0; w < kCapWaves; ++w) mm = min(mm, (uint32_t)sh.hist[w]);
+    gstar = mm;
+  }
+  // keys > g* are those >= g* + 1 (g* + 1 >= 1, so padding stays out)
+  const int above = gstar == 0xffffffffu ? 0 : count_ge(gstar + 1u, 0);
   const int need_eq = capacity - above;
   __syncthreads();
   const uint64_t below = (1ull << lane) - 1ull;
