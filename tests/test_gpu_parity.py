@@ -120,6 +120,28 @@ def test_zero_input_ties_and_uniform_gates():
     assert (host(buf.y) == 0).all()
 
 
+def test_capacity_with_every_gate_tied():
+    """Zero input: every token picks experts 0..4 with gate 1/5, so each of
+    them has T candidates for C places, all tied at g*. The tie rule keeps
+    the C lowest tokens, in token order: slot[t, j] = j C + t for t < C,
+    else -1 (the capacity search runs all 32 bits here: no prefix ever has
+    exactly C candidates at or above it)."""
+    C = 20
+    w = W("zeros_cap_bf16", T=70, d=128, E=24, k=5, f=64, capacity=C)
+    inp = generate(w, seed=3)
+    inp["x"] = torch.zeros_like(inp["x"])
+    dev = upload(inp)
+    buf = run_forward(w, dev)
+    slot = host(buf.slot)
+    t = np.arange(w.T)[:, None]
+    want = np.where(t < C, np.arange(w.k)[None, :] * C + t, -1)
+    assert (slot == want).all()
+    R = int(host(buf.offsets)[-1])
+    assert R == w.k * C
+    assert (host(buf.row_src[:R]) == np.tile(np.arange(C), w.k)).all()
+    assert (buf.row_gate[:R] == 0.2).all()
+
+
 def test_empty_batch():
     w = W("empty", T=0, d=128, E=16, k=4, f=64)
     shape = layer.shape_of(w)
