@@ -382,14 +382,15 @@ __global__ __launch_bounds__(256) void lora_seg_outer(const int32_t* __restrict_
 }
 
 // Same sums for r <= 16 and C % 4 == 0, with the rows spread over the
-// workgroup: one workgroup per (256 columns, expert), 16 waves, wave w taking
-// the expert's rows w, w + 16, ... in order, each lane 4 consecutive columns
-// x 16 ranks in registers. Rows go in batches of 4: a batch's loads (its
-// rows of `in` and its 4 x 16 P values, one per lane) are issued before the
-// previous batch's FMAs; the source rows and row scales come 64 rows at a
-// time in one vector load and are read per row with readlane. The 16 waves'
-// partial sums are then added in a fixed tree order through LDS, so the
-// result does not depend on timing.
+// workgroup: one workgroup per (64 CPL columns, expert), 16 waves, wave w
+// taking the expert's rows w, w + 16, ... in order, each lane CPL
+// consecutive columns x 16 ranks in registers. Rows go in batches of 8 (4
+// for fp32 rows of 4 columns): a batch's loads (its rows of `in`, kept as
+// loaded until their FMAs, and its P values, one per lane per 4 rows) are
+// issued before the previous batch's FMAs; the source rows and row scales
+// come 64 rows at a time in one vector load and are read per row with
+// readlane. The 16 waves' partial sums are then added in a fixed tree order
+// through LDS, so the result does not depend on timing.
 typedef const __attribute__((address_space(4))) float* const_f32_ptr_t;
 
 // N consecutive values (N = 1, 2 or 4) in one load, as floats.
@@ -422,6 +423,44 @@ __device__ __forceinline__ void load_vec(const float* p, float (&v)[N]) {
   }
 }
 
+// CPL consecutive row values as loaded (bf16 words, or fp32), widened one
+// at a time where they are used.
+template <class TIn, int N>
+struct RawVec;
+template <int N>
+struct RawVec<bf16_t, N> {
+  uint32_t w[(N + 1) / 2];
+  __device__ __forceinline__ void load(const bf16_t* p) {
+    if constexpr (N == 4) {
+      const uint2 raw = *reinterpret_cast<const uint2*>(p);
+      w[0] = raw.x;
+      w[1] = raw.y;
+    } else if constexpr (N == 2) {
+      w[0] = *reinterpret_cast<const uint32_t*>(p);
+    } else {
+      w[0] = static_cast<uint32_t>(*p);
+    }
+  }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < (N + 1) / 2; ++i) w[i] = 0u;
+  }
+  __device__ __forceinline__ float at(int u) const {
+    const uint32_t x = w[u >> 1];
+    return __uint_as_float((u & 1) ? (x & 0xffff0000u) : (x << 16));
+  }
+};
+template <int N>
+struct RawVec<float, N> {
+  float v[N];
+  __device__ __forceinline__ void load(const float* p) { load_vec<N>(p, v); }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = 0.f;
+  }
+  __device__ __forceinline__ float at(int u) const { return v[u]; }
+};
+
 constexpr int kSegWaves = 16;  // waves per workgroup
 constexpr int kSegRq = 16;     // ranks held per lane
 constexpr int kSegSlots = 8;   // LDS partial-sum slots of the reduction tree
@@ -433,7 +472,10 @@ __global__ __launch_bounds__(64 * kSegWaves) void lora_seg_outer16(
     const int32_t* __restrict__ offsets, const float* __restrict__ P, int r, const TIn* __restrict__ in,
     int64_t in_stride, const int32_t* __restrict__ qsrc, const float* __restrict__ qscale, int C, float s,
     int out_qc, float* __restrict__ out) {
-  constexpr int B = 4;  // rows per batch
+  // rows per batch: 8, or 4 where 8 fp32 rows of 4 columns would not fit in
+  // registers; NH groups of 4 rows x 16 ranks of P per batch
+  constexpr int B = (sizeof(TIn) == 4 && CPL == 4) ? 4 : 8;
+  constexpr int NH = B / 4;
   constexpr int kSegCols = 64 * CPL;
   __shared__ float red[kSegSlots][kSegRq][kSegCols];
   const int le = blockIdx.y;
@@ -450,10 +492,15 @@ __global__ __launch_bounds__(64 * kSegWaves) void lora_seg_outer16(
   for (int q = 0; q < kSegRq; ++q)
 #pragma unroll
     for (int u = 0; u < CPL; ++u) acc[q][u] = 0.f;
-  const int jp = lane >> 4, qp = lane & 15;  // P value this lane fetches: row jp of a batch, rank qp
+  // P values this lane fetches: rows jp + 4 h of a batch, rank qp
+  const int jp = lane >> 4, qp = lane & 15;
   int srcv = 0;      // lane l: source row of window row l (64 rows per window)
   float sclv = 1.f;  // lane l: its scale
-  float vc[B][CPL], vn[B][CPL], pc = 0.f, pn = 0.f;
+  RawVec<TIn, CPL> vc[B], vn[B];
+  float sc_c[B], sc_n[B];  // row scales of the two batches (1 past M)
+  float pc[NH], pn[NH];
+#pragma unroll
+  for (int h = 0; h < NH; ++h) pc[h] = pn[h] = 0.f;
   for (int m0 = 0; m0 < M + B; m0 += B) {
     // fetch batch m0 (if any) into (vn, pn) while batch m0 - B, in (vc, pc), is consumed
     if (m0 < M) {
@@ -463,39 +510,43 @@ __global__ __launch_bounds__(64 * kSegWaves) void lora_seg_outer16(
         srcv = m < M ? (qsrc ? qsrc[p] : p) : 0;
         sclv = (m < M && qscale) ? qscale[p] : 1.f;
       }
-      const int mp = m0 + jp;
-      pn = (mp < M && qp < r) ? P[(int64_t)(a + wave + kSegWaves * mp) * r + qp] : 0.f;
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        const int mp = m0 + jp + 4 * h;
+        pn[h] = (mp < M && qp < r) ? P[(int64_t)(a + wave + kSegWaves * mp) * r + qp] : 0.f;
+      }
 #pragma unroll
       for (int j = 0; j < B; ++j) {
         const int src = __builtin_amdgcn_readlane(srcv, (m0 + j) & 63);
-        if (m0 + j < M && cok) {
-          load_vec<CPL>(in + (int64_t)src * in_stride + c0, vn[j]);
-        } else {
-#pragma unroll
-          for (int u = 0; u < CPL; ++u) vn[j][u] = 0.f;
-        }
-        // fold the row scale in right away (rows past M have scale 1 and zeros)
-        const float sc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sclv),
-                                                                             (m0 + j) & 63));
-#pragma unroll
-        for (int u = 0; u < CPL; ++u) vn[j][u] *= sc;
+        if (m0 + j < M && cok) vn[j].load(in + (int64_t)src * in_stride + c0);
+        else vn[j].zero();
+        // rows past M have scale 1 and zeros
+        sc_n[j] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sclv),
+                                                                      (m0 + j) & 63));
       }
     }
     if (m0 > 0) {
 #pragma unroll
-      for (int j = 0; j < B; ++j)
+      for (int j = 0; j < B; ++j) {
+        float v[CPL];
+#pragma unroll
+        for (int u = 0; u < CPL; ++u) v[u] = vc[j].at(u) * sc_c[j];
 #pragma unroll
         for (int q = 0; q < kSegRq; ++q) {
-          const float pq = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pc), 16 * j + q));
+          const float pq = __builtin_bit_cast(
+              float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pc[j >> 2]), 16 * (j & 3) + q));
 #pragma unroll
-          for (int u = 0; u < CPL; ++u) acc[q][u] = fmaf(pq, vc[j][u], acc[q][u]);
+          for (int u = 0; u < CPL; ++u) acc[q][u] = fmaf(pq, v[u], acc[q][u]);
         }
+      }
     }
 #pragma unroll
-    for (int j = 0; j < B; ++j)
+    for (int j = 0; j < B; ++j) {
+      vc[j] = vn[j];
+      sc_c[j] = sc_n[j];
+    }
 #pragma unroll
-      for (int u = 0; u < CPL; ++u) vc[j][u] = vn[j][u];
-    pc = pn;
+    for (int h = 0; h < NH; ++h) pc[h] = pn[h];
   }
   // fixed-order tree over the waves: 16 -> 8 -> 4 -> 2 -> 1
   for (int half = kSegWaves / 2; half >= 1; half >>= 1) {
