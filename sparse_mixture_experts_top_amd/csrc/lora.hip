@@ -23,10 +23,15 @@
 //   dh         the register-staged dH GEMM for unpacked W_d (the packed path
 //              runs on the DMA engine in expert_gemm.hip): g dY W_d plus the
 //              rank-r term, times silu(G) -> dU (fp32)
-//   seg_outer16  per expert and column block: sum over the expert's rows of
-//              P[p, q] * V[p, c] -> the gradients, fp32, 16 waves over the
-//              rows and a fixed-order reduction (seg_outer: the plain
-//              fallback for r > 16)
+//   seg_mfma   per expert and 128 columns: sum over the expert's rows of
+//              P[p, q] * V[p, c] -> the gradients, on the MFMAs for bf16 V
+//              (rows staged per wave in LDS and read down the columns, P as
+//              bf16 high + low parts), fixed-order reduction over the waves
+//   seg_outer16  the same sums on the VALU for fp32 V (and shapes the MFMA
+//              form does not take), 16 waves over the rows (seg_outer: the
+//              plain fallback for r > 16)
+#include <type_traits>
+
 #include "common.h"
 #include "mfma_tile.h"
 
@@ -581,10 +586,146 @@ __global__ __launch_bounds__(64 * kSegWaves) void lora_seg_outer16(
   }
 }
 
+// The same sums on the matrix cores for bf16 rows, r <= 16 and C % 128 == 0:
+// out[le] = s * sum over the expert's rows p of (scale_p P[p])^T in[src_p],
+// as [r x 32] . [32 x kSmCols] MFMA products per step of 32 rows. One
+// workgroup per (kSmCols columns, expert), kSmWaves waves, wave w taking the
+// steps w, w + kSmWaves, ... A step's rows are staged in the wave's own LDS
+// tile (32 x kSmCols bf16, each 16-byte chunk c of row j at chunk
+// c ^ 2 (j / 8 % 4), so the column reads below hit 32 different banks); the
+// B operand is read from it down the columns (8 rows of one column per
+// lane), the A operand is the scaled P values split into bf16 high and low
+// parts (two MFMAs, about 16 bits of P). The waves' 16 x kSmCols partial
+// sums are then added in a fixed tree order through LDS, so the result does
+// not depend on timing.
+// 8 waves x 128 columns (two workgroups per CU) measured fastest on the
+// 14-expert LoRA step; 8 x 256, 16 x 128, 8 x 64 and 4 x 128 were slower.
+constexpr int kSmWaves = 8;
+constexpr int kSmCols = 128;
+constexpr int kSmFrags = kSmCols / 16;  // 16-column MFMA fragments
+constexpr int kSmChunks = kSmCols / 8;  // 16-byte chunks per tile row
+
+static_assert(kSmWaves * 32 * kSmCols * 2 <= 160 * 1024, "LDS tiles");
+static_assert(kSmChunks <= 64 && kSmCols % 64 == 0, "tile rows");
+
+__global__ __launch_bounds__(64 * kSmWaves) void lora_seg_mfma(
+    const int32_t* __restrict__ offsets, const float* __restrict__ P, int r, const bf16_t* __restrict__ in,
+    int64_t in_stride, const int32_t* __restrict__ qsrc, const float* __restrict__ qscale, int C, float s,
+    int out_qc, float* __restrict__ out) {
+  __shared__ __align__(16) bf16_t tile[kSmWaves * 32 * kSmCols];
+  const int le = blockIdx.y;
+  const int cb = blockIdx.x * kSmCols;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int a = ld_uniform(offsets, le), b = ld_uniform(offsets, le + 1);
+  const int nsteps = (b - a + 31) / 32;
+  const int q = lane & 15, kg = lane >> 4;  // MFMA lane roles: row / column q, K group kg
+  f32x4 acc[kSmFrags];
+#pragma unroll
+  for (int n = 0; n < kSmFrags; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bf16_t* my = tile + wave * 32 * kSmCols;
+  for (int st = wave; st < nsteps; st += kSmWaves) {
+    const int p0 = a + st * 32;
+    // lane l holds the source row of step row l % 32 (rows past the expert:
+    // its last row, whose P values below are 0)
+    const int pl = min(p0 + (lane & 31), b - 1);
+    const int srcl = qsrc ? qsrc[pl] : pl;
+    // this lane's chunks: rows (64 / kSmChunks) t + lane / kSmChunks, 8
+    // columns at chunk lane % kSmChunks
+    constexpr int RPT = 64 / kSmChunks, NT = 32 / RPT;
+    uint4 v[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int srow = __shfl(srcl, RPT * t + lane / kSmChunks, kWave);
+      v[t] = *reinterpret_cast<const uint4*>(in + (int64_t)srow * in_stride + cb + (lane % kSmChunks) * 8);
+    }
+    // A: rank q of rows p0 + 8 kg + i, times the row scale, as bf16 hi + lo
+    float pv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int p = p0 + 8 * kg + i;
+      pv[i] = (p < b && q < r) ? P[(int64_t)p * r + q] * (qscale ? qscale[p] : 1.f) : 0.f;
+    }
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      h[u] = f32x2_to_bf16x2(pv[2 * u], pv[2 * u + 1]);
+      l[u] = f32x2_to_bf16x2(pv[2 * u] - bf16_to_f32(static_cast<bf16_t>(h[u])),
+                             pv[2 * u + 1] - bf16_to_f32(static_cast<bf16_t>(h[u] >> 16)));
+    }
+    const bf16x8 ah = __builtin_bit_cast(bf16x8, u32x4{h[0], h[1], h[2], h[3]});
+    const bf16x8 al = __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]});
+    // (the previous step's reads of the tile precede these writes: one
+    // wave's LDS accesses complete in order)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int row = RPT * t + lane / kSmChunks, cc = lane % kSmChunks;
+      *reinterpret_cast<uint4*>(my + row * kSmCols + ((cc ^ (2 * ((row >> 3) & 3))) * 8)) = v[t];
+    }
+#pragma unroll
+    for (int n = 0; n < kSmFrags; ++n) {
+      // column 16 n + q, rows 8 kg .. 8 kg + 7 (their chunk key is kg)
+      const int col = ((((2 * n + (q >> 3)) ^ (2 * kg))) * 8) + (q & 7);
+      uint32_t w[4];
+#pragma unroll
+      for (int i2 = 0; i2 < 4; ++i2) {
+        const uint32_t lo = my[(8 * kg + 2 * i2) * kSmCols + col];
+        const uint32_t hi = my[(8 * kg + 2 * i2 + 1) * kSmCols + col];
+        w[i2] = lo | (hi << 16);
+      }
+      const bf16x8 bv = __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+      acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bv, acc[n], 0, 0, 0);
+      acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bv, acc[n], 0, 0, 0);
+    }
+  }
+  // fixed-order tree over the waves, halving (the tiles reused: half the
+  // waves x 64 kSmFrags floats per lane)
+  constexpr int kRed = kSmFrags * 4 * 64;
+  static_assert((kSmWaves / 2) * kRed * 4 <= kSmWaves * 32 * kSmCols * 2, "reduction fits the tiles");
+  float* red = reinterpret_cast<float*>(tile);
+  __syncthreads();
+  for (int half = kSmWaves / 2; half >= 1; half >>= 1) {
+    if (wave >= half && wave < 2 * half) {
+#pragma unroll
+      for (int n = 0; n < kSmFrags; ++n)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) red[(wave - half) * kRed + (n * 4 + j) * 64 + lane] = acc[n][j];
+    }
+    __syncthreads();
+    if (wave < half) {
+#pragma unroll
+      for (int n = 0; n < kSmFrags; ++n)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[n][j] += red[wave * kRed + (n * 4 + j) * 64 + lane];
+    }
+    __syncthreads();
+  }
+  if (wave != 0) return;
+  // lane: column cb + 16 n + q, ranks 4 kg + j
+#pragma unroll
+  for (int n = 0; n < kSmFrags; ++n)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int qo = 4 * kg + j, c = cb + 16 * n + q;
+      if (qo < r) {
+        if (out_qc) out[((int64_t)le * r + qo) * C + c] = s * acc[n][j];
+        else out[((int64_t)le * C + c) * r + qo] = s * acc[n][j];
+      }
+    }
+}
+
 template <class TIn>
 static hipError_t launch_seg_outer(const Ctx& c, int L, const int32_t* offsets, const float* P,
                                    int r, const TIn* in, int64_t in_stride, const int32_t* qsrc,
                                    const float* qscale, int C, float s, bool out_qc, float* out) {
+  if constexpr (std::is_same<TIn, bf16_t>::value) {
+    if (r <= 16 && C % kSmCols == 0 && in_stride % 8 == 0 && (reinterpret_cast<uintptr_t>(in) & 15) == 0) {
+      TimedLaunch tl(MOE_K_LORA_GRAD, c.stream);
+      hipLaunchKernelGGL(lora_seg_mfma, dim3(C / kSmCols, L), dim3(64 * kSmWaves), 0, c.stream, offsets, P, r,
+                         in, in_stride, qsrc, qscale, C, s, (int)out_qc, out);
+      return hipGetLastError();
+    }
+  }
   if (r <= kSegRq && C % 4 == 0 && in_stride % 4 == 0) {
     TimedLaunch tl(MOE_K_LORA_GRAD, c.stream);
     // columns per lane: the widest that still gives about 200 workgroups
