@@ -383,7 +383,7 @@ moe_status_t moe_router_bwd_packed(const moe_shape_t* shape, const float* dlogit
  * (in the workspace), the product, the row sums.
  *   dlogits [T, E] f32, wr_packed as for moe_router_bwd_packed,
  *   dx_rows [Rmax, d] f32 (moe_expert_bwd_packed with dx NULL; read only
- *   through kept slots, so NULL is accepted when no rows are local),
+ *   through kept slots; NULL only when Rmax = 0),
  *   slot [T, k] int32 (moe_dispatch), dx [T, d] f32 OUT.
  * bf16 only, d % 128 == 0, E % 64 == 0, else MOE_ERR_UNSUPPORTED. */
 moe_status_t moe_router_bwd_unpermute_packed(const moe_shape_t* shape, const float* dlogits,

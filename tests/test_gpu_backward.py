@@ -179,6 +179,32 @@ def test_backward_empty_and_no_local():
         assert np.isfinite(host(g["dlogits"])).all() and np.isfinite(host(g["dx"])).all()
 
 
+def test_router_backward_with_row_sums_and_no_local_rows():
+    """No token picks a local expert (large bias on experts 0..3, local range
+    40..48): the combined call must store exactly the router product, never
+    reading the expert rows (filled with NaN here); T = 0 is a no-op."""
+    for w in (W("nolocal_rb", T=90, d=128, E=64, k=4, f=128, e_lo=40, e_hi=48),
+              W("empty_rb", T=0, d=128, E=64, k=4, f=128)):
+        say(f"[router backward + row sums {w.name}]")
+        inp = generate(w, seed=2)
+        inp["bias"] = torch.tensor([50.0] * 4 + [0.0] * 60)
+        dev = upload(inp)
+        buf = run_forward(w, dev, prob=True, act_save=True, x_perm=False)
+        s = buf.shape
+        assert int(buf.offsets[-1].item()) == 0
+        g = torch.Generator().manual_seed(7)
+        dlogits = torch.randn((w.T, w.E), generator=g).to("cuda")
+        wr_p = torch.empty((w.d, w.E), dtype=torch.bfloat16, device="cuda")
+        B.moe_pack_router_bwd(s, dev["w_router"], wr_p)
+        ref = torch.zeros((w.T, w.d), device="cuda")
+        B.moe_router_bwd_packed(s, dlogits, wr_p, ref, buf.ws)
+        rows = torch.full((max(B.moe_max_rows(s), 1), w.d), float("nan"), device="cuda")
+        dx = torch.full((w.T, w.d), float("nan"), device="cuda")
+        B.moe_router_bwd_unpermute_packed(s, dlogits, wr_p, rows, buf.slot, dx, buf.ws)
+        torch.cuda.synchronize()
+        assert torch.equal(dx, ref)
+
+
 @pytest.mark.parametrize("name", ["full_router", "ep64_rank"])
 def test_backward_full_size_sampled(name):
     """Full size, in the launch configuration of the benchmark's backward
