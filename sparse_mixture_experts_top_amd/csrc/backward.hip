@@ -21,7 +21,9 @@
 //   dx rows    grouped GEMM over K = 2f: dX = [dG dU] [W_g; W_u] (+ s (dU B_u)
 //              A_u), fp32 rows
 //   unpermute  dx[t] = sum over the token's kept slots, in j order (the
-//              combine kernel with unit gates)
+//              combine kernel with unit gates); the adding form after the
+//              router's stored product (one wave per token) touches only
+//              tokens with a kept slot
 //   router     dx[t] += sum_e dl[t, e] W_r[e]: a dense GEMM with K = E on
 //              bf16-rounded logit gradients (fp32 fallback kernels for the
 //              small fp32 shapes or E % 64 != 0)
@@ -462,9 +464,7 @@ __device__ __forceinline__ void unpermute_batch(float4& acc, const float* __rest
   }
 }
 
-// ADD: dx[t] += the sum, only for tokens with a kept slot (the rest of dx
-// is neither read nor written).
-template <int TB, bool ADD>
+template <int TB>
 __global__ __launch_bounds__(256) void unpermute_sum_f32(const float* __restrict__ dx_rows,
                                                          const int32_t* __restrict__ slot, int T, int k,
                                                          int d, float* __restrict__ dx) {
@@ -484,24 +484,70 @@ __global__ __launch_bounds__(256) void unpermute_sum_f32(const float* __restrict
     __syncthreads();
     for (int q = 0; q < nq; ++q) {
       const int n = s_n[q];
-      if (ADD && n == 0) continue;   // uniform: s_n is shared
       for (int v = threadIdx.x; v < nvec; v += blockDim.x) {
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
         int j0 = 0;
         for (; j0 + 8 <= n; j0 += 8) unpermute_batch<8>(acc, dx_rows, s_slot[q], j0, 8, d, v);
         for (; j0 < n; j0 += 2) unpermute_batch<2>(acc, dx_rows, s_slot[q], j0, n - j0, d, v);
-        float4* p = reinterpret_cast<float4*>(dx + (int64_t)(t0 + q) * d + v * 4);
-        if (ADD) {
-          const float4 o = *p;
-          acc.x = o.x + acc.x;
-          acc.y = o.y + acc.y;
-          acc.z = o.z + acc.z;
-          acc.w = o.w + acc.w;
-        }
-        *p = acc;
+        *reinterpret_cast<float4*>(dx + (int64_t)(t0 + q) * d + v * 4) = acc;
       }
     }
     __syncthreads();
+  }
+}
+
+// dx[t] += sum over the token's kept slots (j order) of dx_rows[slot], one
+// wave per token; U column chunks of 4 per lane, all loads of a slot pair in
+// flight before the adds (a lone last slot re-reads its row, added times 0).
+template <int U>
+__global__ __launch_bounds__(256) void unpermute_add_wave(const float* __restrict__ rows,
+                                                          const int32_t* __restrict__ slot, int T, int k, int d,
+                                                          float* __restrict__ dx) {
+  const int lane = threadIdx.x & 63;
+  const int nw = gridDim.x * 4;
+  for (int t = blockIdx.x * 4 + (int)(threadIdx.x >> 6); t < T; t += nw) {
+    const int sl = lane < k ? slot[(int64_t)t * k + lane] : -1;
+    const uint64_t kept = __ballot(sl >= 0);
+    if (kept == 0) continue;
+    for (int c0 = lane * 4; c0 < d; c0 += 64 * 4 * U) {
+      float4 acc[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      uint64_t m = kept;
+      while (m) {
+        const int b0 = __ffsll((long long)m) - 1;
+        m &= m - 1;
+        const bool two = m != 0;
+        const int b1 = two ? __ffsll((long long)m) - 1 : b0;
+        if (two) m &= m - 1;
+        const int64_t r0 = (int64_t)__builtin_amdgcn_readlane(sl, b0) * d;
+        const int64_t r1 = (int64_t)__builtin_amdgcn_readlane(sl, b1) * d;
+        float4 x0[U], x1[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int c = min(c0 + 256 * u, d - 4);
+          x0[u] = *reinterpret_cast<const float4*>(rows + r0 + c);
+          x1[u] = *reinterpret_cast<const float4*>(rows + r1 + c);
+        }
+        const float w1 = two ? 1.f : 0.f;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          acc[u].x = fmaf(w1, x1[u].x, acc[u].x + x0[u].x);
+          acc[u].y = fmaf(w1, x1[u].y, acc[u].y + x0[u].y);
+          acc[u].z = fmaf(w1, x1[u].z, acc[u].z + x0[u].z);
+          acc[u].w = fmaf(w1, x1[u].w, acc[u].w + x0[u].w);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + 256 * u;
+        if (c < d) {
+          float4* p = reinterpret_cast<float4*>(dx + (int64_t)t * d + c);
+          const float4 o = *p;
+          *p = make_float4(o.x + acc[u].x, o.y + acc[u].y, o.z + acc[u].z, o.w + acc[u].w);
+        }
+      }
+    }
   }
 }
 
@@ -509,17 +555,22 @@ hipError_t launch_unpermute(const Ctx& c, const moe_shape_t& s, const float* dx_
                             float* dx, bool add) {
   if (s.T == 0) return hipSuccess;
   TimedLaunch tl(MOE_K_UNPERMUTE, c.stream);
+  if (add) {
+    if (s.d % 4 != 0) return hipErrorInvalidValue;
+    // one wave per token: tokens without a kept slot cost one ballot
+    const int nblk = (s.T + 3) / 4;
+    const int grid = nblk < c.num_cus * 16 ? nblk : c.num_cus * 16;
+    hipLaunchKernelGGL(unpermute_add_wave<4>, dim3(grid), dim3(256), 0, c.stream, dx_rows, slot, s.T, s.k, s.d,
+                       dx);
+    return hipGetLastError();
+  }
   int tb = s.T / (c.num_cus * 8);
   tb = tb >= 8 ? 8 : tb >= 4 ? 4 : tb >= 2 ? 2 : 1;
   const int nblk = (s.T + tb - 1) / tb;
   const int grid = nblk < c.num_cus * 64 ? nblk : c.num_cus * 64;
-#define MOE_UNP(N)                                                                                       \
-  if (add)                                                                                               \
-    hipLaunchKernelGGL((unpermute_sum_f32<N, true>), dim3(grid), dim3(256), 0, c.stream, dx_rows, slot, \
-                       s.T, s.k, s.d, dx);                                                               \
-  else                                                                                                   \
-    hipLaunchKernelGGL((unpermute_sum_f32<N, false>), dim3(grid), dim3(256), 0, c.stream, dx_rows, slot, \
-                       s.T, s.k, s.d, dx)
+#define MOE_UNP(N)                                                                                  \
+  hipLaunchKernelGGL((unpermute_sum_f32<N>), dim3(grid), dim3(256), 0, c.stream, dx_rows, slot, s.T, s.k, \
+                     s.d, dx)
   if (tb == 8) MOE_UNP(8);
   else if (tb == 4) MOE_UNP(4);
   else if (tb == 2) MOE_UNP(2);
