@@ -152,3 +152,20 @@ def test_router_backward_with_unpermute_validates_on_the_host():
         assert f"{name} is NULL".encode() in lib.moe_last_error()
     assert lib.moe_router_bwd_unpermute_packed(ctypes.byref(ok), *([fake] * 5), fake, 16,
                                                None) == B.MOE_ERR_WORKSPACE
+
+
+def test_expert_backward_packed_accepts_null_dx_and_slot():
+    """dx NULL skips the per-token sum (done by the combined router call), so
+    slot may be NULL with it: validation passes the pointer checks and stops
+    at the too-small workspace; slot NULL with dx set is still an error."""
+    lib = B.lib()
+    fake = ctypes.c_void_p(0x100000)      # never dereferenced: validation fails first
+    bf = shape(dtype=B.MOE_BF16, d=128, f=128)
+    # dy, offsets, row_src, row_gate, slot, act_save, dgu_packed, dx_packed, dgu, dx_rows, dx, ws
+    args = [fake] * 12
+    args[4] = None   # slot
+    args[10] = None  # dx
+    assert lib.moe_expert_bwd_packed(ctypes.byref(bf), None, *args, 16, None) == B.MOE_ERR_WORKSPACE
+    args[10] = fake
+    assert lib.moe_expert_bwd_packed(ctypes.byref(bf), None, *args, 1 << 30, None) == B.MOE_ERR_INVALID_ARG
+    assert b"slot is NULL" in lib.moe_last_error()
