@@ -143,7 +143,7 @@ def main() -> int:
                          "HIP cannot time events recorded inside a graph)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(the expert-parallel all-to-all is design only). Run with --gpus 1.",
               file=sys.stderr)
         return 2
