@@ -280,14 +280,19 @@ def test_packed_weights_need_d_multiple_of_128():
 
 
 # r = 16 carries the adapter terms through the matrix cores (one extra K
-# step); other ranks take the fp32 epilogue path
-@pytest.mark.parametrize("b_init,x_perm,r,packed", [("normal", True, 16, False), ("normal", False, 16, False),
-                                                    ("zero", False, 16, False), ("normal", False, 8, False),
-                                                    ("normal", False, 16, True)])
-def test_lora_forward_backward_and_aux(b_init, x_perm, r, packed):
-    w = W("lora_small", T=256, d=128, E=12, k=4, f=128, e_lo=2, e_hi=9, lora_r=r,
+# step); other ranks take the fp32 epilogue path. d = f = 192 (not a multiple
+# of 128) sends the gradient sums with bf16 rows to the VALU form instead of
+# the matrix-core one.
+@pytest.mark.parametrize("b_init,x_perm,r,packed,dims", [("normal", True, 16, False, 128),
+                                                         ("normal", False, 16, False, 128),
+                                                         ("zero", False, 16, False, 128),
+                                                         ("normal", False, 8, False, 128),
+                                                         ("normal", False, 16, True, 128),
+                                                         ("normal", False, 16, False, 192)])
+def test_lora_forward_backward_and_aux(b_init, x_perm, r, packed, dims):
+    w = W("lora_small", T=256, d=dims, E=12, k=4, f=dims, e_lo=2, e_hi=9, lora_r=r,
           lora_alpha=32.0, lora_b=b_init, aux_coef=0.01)
-    say(f"[case lora_small b={b_init} x_perm={x_perm} r={r} packed={packed}]")
+    say(f"[case lora_small b={b_init} x_perm={x_perm} r={r} packed={packed} d=f={dims}]")
     inp = generate(w, seed=6)
     dev = upload(inp)
     buf = run_forward(w, dev, prob=True, act_save=True, x_perm=x_perm, packed=packed)
@@ -321,18 +326,22 @@ def test_lora_forward_backward_and_aux(b_init, x_perm, r, packed):
                                  act[:, :w.f], act[:, w.f:2 * w.f], to_f64(inp["w_down"]), lo)
     for n in grads:
         assert_close(host(grads[n]), g_ref[n], "bf16", n)
-    # the same gradients with W_d^T packed once (the dH product on the DMA engine)
-    dgu_p = torch.empty((L, w.f, w.d), dtype=torch.bfloat16, device="cuda")
-    B.moe_pack_backward_weights(buf.shape, dev["w_gate"], dev["w_up"], dev["w_down"], dgu_p, None)
-    gp = {n: torch.full_like(g, float("nan")) for n, g in grads.items()}
-    B.moe_lora_bwd_packed(buf.shape, lora, dev["dy"], buf.offsets, buf.row_src, buf.row_gate, xr, xs,
-                          buf.act_save, dgu_p, gp["da_up"], gp["db_up"], gp["da_down"], gp["db_down"], buf.ws)
-    torch.cuda.synchronize()
-    for n in grads:
-        assert_close(host(gp[n]), g_ref[n], "bf16", n + " (packed)")
+    # the same gradients with W_d^T packed once (the dH product on the DMA
+    # engine; the packed transposes need d, f % 128 == 0)
+    gp = None
+    if w.d % 128 == 0 and w.f % 128 == 0:
+        dgu_p = torch.empty((L, w.f, w.d), dtype=torch.bfloat16, device="cuda")
+        B.moe_pack_backward_weights(buf.shape, dev["w_gate"], dev["w_up"], dev["w_down"], dgu_p, None)
+        gp = {n: torch.full_like(g, float("nan")) for n, g in grads.items()}
+        B.moe_lora_bwd_packed(buf.shape, lora, dev["dy"], buf.offsets, buf.row_src, buf.row_gate, xr, xs,
+                              buf.act_save, dgu_p, gp["da_up"], gp["db_up"], gp["da_down"], gp["db_down"], buf.ws)
+        torch.cuda.synchronize()
+        for n in grads:
+            assert_close(host(gp[n]), g_ref[n], "bf16", n + " (packed)")
     if b_init == "zero":
         assert (grads["da_up"] == 0).all() and (grads["da_down"] == 0).all()
-        assert (gp["da_up"] == 0).all() and (gp["da_down"] == 0).all()
+        if gp is not None:
+            assert (gp["da_up"] == 0).all() and (gp["da_down"] == 0).all()
         frozen = run_forward(w.replace(lora_r=0), dev, x_perm=x_perm)
         assert torch.equal(frozen.y, buf.y)
 
