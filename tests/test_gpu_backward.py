@@ -205,7 +205,7 @@ def test_router_backward_with_row_sums_and_no_local_rows():
         assert torch.equal(dx, ref)
 
 
-@pytest.mark.parametrize("name", ["full_router", "ep64_rank"])
+@pytest.mark.parametrize("name", ["full_router", "ep64_rank", "skewed_capacity"])
 def test_backward_full_size_sampled(name):
     """Full size, in the launch configuration of the benchmark's backward
     pass (packed transposed weights); the oracle checks sampled tokens (their gate and logit gradients,
