@@ -370,9 +370,12 @@ moe_status_t moe_pack_router_bwd(const moe_shape_t* shape, const void* w_router,
 moe_status_t moe_router_bwd_packed(const moe_shape_t* shape, const float* dlogits, const void* wr_packed,
                                    float* dx, void* ws, size_t ws_bytes, moe_stream_t stream);
 
-/* The two parts of dx in one call (backward of "Switch Transformers:
- * Scaling to Trillion Parameter Models with Simple and Efficient Sparsity",
- * §2.1, through the gate and through the experts):
+/* The two parts of dx in one call: the frozen layer passes gradients down
+ * through the experts and through the router ("Adapting Trillion-Parameter
+ * MoE Models for LoRA Fine-Tuning: A Full-Stack Engineering Guide", §2.1 and
+ * §3), the unpermute and the router product of the reversed pipeline of
+ * "Trillion-Parameter MoE Model Training Adaptation: Full-Stack Optimization
+ * Practices", §3:
  *   dx[t] = sum over the token's slots j with slot[t, j] >= 0, in j order,
  *           of dx_rows[slot[t, j]]  +  sum_e dlogits[t, e] w_router[e]
  * bitwise equal to moe_expert_bwd_packed's unpermute followed by
@@ -423,7 +426,11 @@ typedef enum {
 } moe_kernel_t;
 
 /* mask: bit k (1 << moe_kernel_t) enables timing of kind k; 0 disables all,
- * -1 enables all. Also resets the totals. */
+ * -1 enables all. Also resets the totals. The events are created here (512
+ * of them); the entry points only record pooled events, so they still
+ * allocate nothing. A launch whose events find the pool empty (all pending,
+ * i.e. more than 256 timed launches since the last moe_timing_read) is not
+ * timed and not counted. */
 moe_status_t moe_timing_enable(int32_t mask);
 moe_status_t moe_timing_read(int32_t kernel, double* total_ms, int64_t* launches);
 

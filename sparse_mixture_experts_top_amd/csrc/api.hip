@@ -155,12 +155,10 @@ Timing& timing() {
 }
 thread_local hipEvent_t t_open[MOE_K_COUNT] = {};
 
+// Events come only from the pool moe_timing_enable fills, so an entry point
+// never creates one; with every pooled event pending, the sample is skipped.
 hipEvent_t take_event(Timing& t) {
-  if (t.pool.empty()) {
-    hipEvent_t e = nullptr;
-    if (hipEventCreate(&e) != hipSuccess) return nullptr;
-    return e;
-  }
+  if (t.pool.empty()) return nullptr;
   hipEvent_t e = t.pool.back();
   t.pool.pop_back();
   return e;
@@ -186,7 +184,9 @@ void timing_begin(int kid, hipStream_t s) {
   std::lock_guard<std::mutex> g(t.mu);
   if (!t.on || !((t.mask >> kid) & 1u)) return;
   hipEvent_t e = take_event(t);
-  if (e && hipEventRecord(e, s) == hipSuccess) t_open[kid] = e;
+  if (!e) return;
+  if (hipEventRecord(e, s) == hipSuccess) t_open[kid] = e;
+  else t.pool.push_back(e);
 }
 
 void timing_end(int kid, hipStream_t s) {
@@ -196,7 +196,13 @@ void timing_end(int kid, hipStream_t s) {
   t_open[kid] = nullptr;
   if (!t.on || !start) return;
   hipEvent_t e = take_event(t);
-  if (e && hipEventRecord(e, s) == hipSuccess) t.pending[kid].push_back({start, e});
+  if (e && hipEventRecord(e, s) == hipSuccess) {
+    t.pending[kid].push_back({start, e});
+    return;
+  }
+  // no end event: the sample is dropped and its events go back to the pool
+  t.pool.push_back(start);
+  if (e) t.pool.push_back(e);
 }
 
 }  // namespace moe

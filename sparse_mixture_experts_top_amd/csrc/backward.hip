@@ -53,16 +53,18 @@ __device__ __forceinline__ void load8f<float>(const float* p, float (&v)[8]) {
   v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
+__device__ __forceinline__ float load1f(const float* p) { return *p; }
+__device__ __forceinline__ float load1f(const bf16_t* p) { return bf16_to_f32(*p); }
 
 // ------------------------------------------------------------ gate bwd ---
 // One wave per token (4 per workgroup). Lane j < k holds slot, gate and
 // selected expert of assignment j; the dot products run 8 assignments at a
-// time over 8-element chunks of the row (d % 8 == 0), lanes striding the
-// chunks, and a group whose slots are all empty (dropped or not local) is
-// skipped; lane l holds logits l, l + 64, ... (EPL of them). The
-// load-balance fractions counts[e] / (T k) are staged once per workgroup in
-// LDS.
-template <class T, int EPL>
+// time over 8-element chunks of the row (VEC, d % 8 == 0; otherwise single
+// elements), lanes striding the chunks, and a group whose slots are all
+// empty (dropped or not local) is skipped; lane l holds logits l, l + 64,
+// ... (EPL of them). The load-balance fractions counts[e] / (T k) are staged
+// once per workgroup in LDS.
+template <class T, int EPL, bool VEC>
 __global__ __launch_bounds__(256) void gate_bwd(const T* __restrict__ dy, const T* __restrict__ y_perm,
                                                 const int32_t* __restrict__ slot,
                                                 const int32_t* __restrict__ idx,
@@ -107,15 +109,23 @@ __global__ __launch_bounds__(256) void gate_bwd(const T* __restrict__ dy, const 
     float acc[G];
 #pragma unroll
     for (int q = 0; q < G; ++q) acc[q] = 0.f;
-    for (int i0 = lane * 8; i0 < d; i0 += 64 * 8) {
-      float a0[8], o0[G][8];
-      load8f<T>(dyr + i0, a0);
+    if (VEC) {
+      for (int i0 = lane * 8; i0 < d; i0 += 64 * 8) {
+        float a0[8], o0[G][8];
+        load8f<T>(dyr + i0, a0);
 #pragma unroll
-      for (int q = 0; q < G; ++q) load8f<T>(y_perm + rb[q] + i0, o0[q]);
+        for (int q = 0; q < G; ++q) load8f<T>(y_perm + rb[q] + i0, o0[q]);
 #pragma unroll
-      for (int q = 0; q < G; ++q)
+        for (int q = 0; q < G; ++q)
 #pragma unroll
-        for (int u = 0; u < 8; ++u) acc[q] = fmaf(a0[u], o0[q][u], acc[q]);
+          for (int u = 0; u < 8; ++u) acc[q] = fmaf(a0[u], o0[q][u], acc[q]);
+      }
+    } else {
+      for (int i = lane; i < d; i += 64) {
+        const float a0 = load1f(dyr + i);
+#pragma unroll
+        for (int q = 0; q < G; ++q) acc[q] = fmaf(a0, load1f(y_perm + rb[q] + i), acc[q]);
+      }
     }
 #pragma unroll
     for (int q = 0; q < G; ++q) {
@@ -185,10 +195,16 @@ hipError_t launch_gate_bwd(const Ctx& c, const moe_shape_t& s, const void* dy, c
   const float inv_tk = 1.0f / ((float)s.T * (float)s.k);
   const int grid = (s.T + 3) / 4;
   TimedLaunch tl(MOE_K_GATE_BWD, c.stream);
+  const bool vec = s.d % 8 == 0;
 #define MOE_GB(TT, N)                                                                                   \
-  hipLaunchKernelGGL((gate_bwd<TT, N>), dim3(grid), dim3(256), 0, c.stream, (const TT*)dy,              \
+  do {                                                                                                  \
+    if (vec) MOE_GB2(TT, N, true)                                                                       \
+    else MOE_GB2(TT, N, false)                                                                          \
+  } while (0)
+#define MOE_GB2(TT, N, V)                                                                               \
+  hipLaunchKernelGGL((gate_bwd<TT, N, V>), dim3(grid), dim3(256), 0, c.stream, (const TT*)dy,           \
                      (const TT*)y_perm, slot, idx, gate, logits, aux ? counts : nullptr, aux_scale,    \
-                     inv_tk, s.T, s.d, s.E, s.k, dgate, dlogits)
+                     inv_tk, s.T, s.d, s.E, s.k, dgate, dlogits);
 #define MOE_GB_E(TT)                      \
   if (epl <= 1) MOE_GB(TT, 1);            \
   else if (epl <= 2) MOE_GB(TT, 2);       \
@@ -203,6 +219,7 @@ hipError_t launch_gate_bwd(const Ctx& c, const moe_shape_t& s, const void* dy, c
   }
 #undef MOE_GB_E
 #undef MOE_GB
+#undef MOE_GB2
   return hipGetLastError();
 }
 
@@ -484,12 +501,21 @@ __global__ __launch_bounds__(256) void unpermute_sum_f32(const float* __restrict
     __syncthreads();
     for (int q = 0; q < nq; ++q) {
       const int n = s_n[q];
-      for (int v = threadIdx.x; v < nvec; v += blockDim.x) {
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        int j0 = 0;
-        for (; j0 + 8 <= n; j0 += 8) unpermute_batch<8>(acc, dx_rows, s_slot[q], j0, 8, d, v);
-        for (; j0 < n; j0 += 2) unpermute_batch<2>(acc, dx_rows, s_slot[q], j0, n - j0, d, v);
-        *reinterpret_cast<float4*>(dx + (int64_t)(t0 + q) * d + v * 4) = acc;
+      if (d % 4 == 0) {
+        for (int v = threadIdx.x; v < nvec; v += blockDim.x) {
+          float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+          int j0 = 0;
+          for (; j0 + 8 <= n; j0 += 8) unpermute_batch<8>(acc, dx_rows, s_slot[q], j0, 8, d, v);
+          for (; j0 < n; j0 += 2) unpermute_batch<2>(acc, dx_rows, s_slot[q], j0, n - j0, d, v);
+          *reinterpret_cast<float4*>(dx + (int64_t)(t0 + q) * d + v * 4) = acc;
+        }
+      } else {
+        // rows not 16-byte aligned: one column per thread, same j order
+        for (int c = threadIdx.x; c < d; c += blockDim.x) {
+          float acc = 0.f;
+          for (int j = 0; j < n; ++j) acc += dx_rows[(int64_t)s_slot[q][j] * d + c];
+          dx[(int64_t)(t0 + q) * d + c] = acc;
+        }
       }
     }
     __syncthreads();

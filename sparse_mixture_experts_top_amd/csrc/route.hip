@@ -332,7 +332,7 @@ __global__ __launch_bounds__(1024) void prob_reduce(const float* __restrict__ pa
 
 hipError_t launch_topk(const Ctx& c, const moe_shape_t& s, const float* logits, int32_t* idx,
                        float* gate, float* prob_part, float* prob_sum) {
-  // one token per wave; with the softmax sums requested, four tokens per wave
+  // one token per wave; with the softmax sums requested, kTopkTokPerWaveProb tokens per wave
   // so the per-block partial sums stay small
   const int tpw = prob_sum ? kTopkTokPerWaveProb : 1;
   const int nblk = (s.T + 4 * tpw - 1) / (4 * tpw);

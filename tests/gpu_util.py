@@ -57,8 +57,20 @@ def host(t: Optional[torch.Tensor]) -> Optional[np.ndarray]:
     return t.numpy()
 
 
-def assert_close(got, ref, dtype: str, what: str, stored_bf16: bool = False) -> dict:
+def bf16_round(a: np.ndarray) -> np.ndarray:
+    """float64 values rounded to bf16 (through fp32, round to nearest even),
+    returned as float64: the rounding a bf16 store applies."""
+    return torch.from_numpy(np.asarray(a, np.float64)).to(torch.float32).to(torch.bfloat16).to(
+        torch.float64).numpy()
+
+
+def assert_close(got, ref, dtype: str, what: str, stored_bf16: bool = False,
+                 scale_atol: bool = False) -> dict:
     """max-abs <= atol and relative Frobenius <= rtol (TOL[dtype]).
+
+    scale_atol: the max-abs bound is atol * max(1, |ref|inf), for sums whose
+    inputs carry a relative rounding (bf16 storage) that no accumulation
+    order removes.
 
     stored_bf16: ``got`` is an intermediate kept in bf16 storage (the expert
     rows y_perm). Its representation alone is off by up to half a bf16 ulp,
@@ -72,6 +84,8 @@ def assert_close(got, ref, dtype: str, what: str, stored_bf16: bool = False) -> 
     if stored_bf16 and dtype == "bf16":
         err = np.maximum(err - 2.0 ** -8 * np.abs(ref), 0.0)
     max_abs = float(err.max()) if err.size else 0.0
+    if scale_atol and ref.size:
+        atol = atol * max(1.0, float(np.abs(ref).max()))
     denom = float(np.linalg.norm(ref))
     rel = float(np.linalg.norm(got - ref) / denom) if denom > 0 else float(np.linalg.norm(got - ref))
     info = {"what": what, "max_abs": max_abs, "rel_frob": rel,
@@ -148,17 +162,41 @@ def rows_x(w: Workload, inp, buf: layer.Buffers, rows: np.ndarray) -> np.ndarray
     return to_f64(inp["x"])[host(buf.row_src[idx])]
 
 
-def expert_ref_rows(w: Workload, inp, buf: layer.Buffers, rows: np.ndarray, lora=None):
-    """Oracle expert output for the given dispatched rows."""
+def expert_ref_rows(w: Workload, inp, buf: layer.Buffers, rows: np.ndarray, lora=None,
+                    return_parts: bool = False):
+    """Oracle expert output for the given dispatched rows (and, with
+    return_parts, the oracle's own G, U and H of those rows)."""
     offsets = host(buf.offsets)
     xp = rows_x(w, inp, buf, rows)
     out = np.zeros((len(rows), w.d))
+    parts = {n: np.zeros((len(rows), w.f)) for n in ("G", "U", "H")}
     les = np.searchsorted(offsets, rows, side="right") - 1
     for le in np.unique(les):
         m = les == le
         lo = None
         if lora is not None:
             lo = {"scale": lora["scale"], **{n: to_f64(inp[n][le]) for n in ("a_up", "b_up", "a_down", "b_down")}}
-        out[m] = oracle.expert_ffn(xp[m], to_f64(inp["w_gate"][le]), to_f64(inp["w_up"][le]),
-                                   to_f64(inp["w_down"][le]), lo)
-    return out
+        o, p = oracle.expert_ffn(xp[m], to_f64(inp["w_gate"][le]), to_f64(inp["w_up"][le]),
+                                 to_f64(inp["w_down"][le]), lo, return_parts=True)
+        out[m] = o
+        for n in parts:
+            parts[n][m] = p[n]
+    return (out, parts) if return_parts else out
+
+
+def check_act_save(w: Workload, inp, buf: layer.Buffers, rows: np.ndarray, lora=None,
+                   what: str = "act_save"):
+    """The saved activations of the given rows -- G in columns [0, f), the H
+    fed to the down projection in [f, 2f), U (adapter term included) in
+    [2f, 3f) -- against the oracle's G, H and U of the same input rows.
+    They are stored in the layer's dtype, so in bf16 each element carries up
+    to half a bf16 ulp of storage rounding on top of the tolerance.
+    Returns the oracle parts."""
+    _, parts = expert_ref_rows(w, inp, buf, rows, lora=lora, return_parts=True)
+    if len(rows) == 0:
+        return parts
+    act = host(buf.act_save[torch.as_tensor(rows, device="cuda").long()])
+    f = w.f
+    for c, n in enumerate(("G", "H", "U")):
+        assert_close(act[:, c * f:(c + 1) * f], parts[n], w.dtype, f"{what} {n}", stored_bf16=True)
+    return parts

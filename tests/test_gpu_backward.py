@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import assert_close, host, lora_of, run_forward, say, upload
+from gpu_util import assert_close, check_act_save, host, lora_of, run_forward, say, upload
 from sparse_mixture_experts_top_amd import binding as B
 from sparse_mixture_experts_top_amd import layer
 from sparse_mixture_experts_top_amd.workloads import WORKLOADS, Workload, generate, to_f64
@@ -24,6 +24,10 @@ CASES = {
     "capacity_f32": W("capacity_f32", T=200, d=48, E=12, k=3, f=20, e_lo=2, e_hi=10,
                       capacity=25, zipf_s=1.0, dtype="f32"),
     "k1_bf16": W("k1_bf16", T=257, d=128, E=16, k=1, f=128),
+    # fp32 rows that are not a multiple of 8 (d = 44) or of 4 elements (d = 45):
+    # the element-wise paths of the gate gradient and of the row sums
+    "d44_f32": W("d44_f32", T=150, d=44, E=10, k=3, f=24, e_lo=1, e_hi=9, dtype="f32"),
+    "d45_f32": W("d45_f32", T=131, d=45, E=9, k=2, f=19, capacity=40, zipf_s=1.0, dtype="f32"),
     # E % 64 == 0: the router part runs on the matrix cores; two K steps of 64
     "router128_bf16": W("router128_bf16", T=333, d=320, E=128, k=4, f=64),
     # packable for every backward product (d, f % 128 == 0, E % 64 == 0)
@@ -122,6 +126,9 @@ def test_backward_stagewise(name, packed):
     g = run_backward(w, dev, buf, packed=packed)
     T = w.T
     R = int(host(buf.offsets)[-1])
+    # the saved G | H | U rows the backward reads
+    lo = _lora64(w, inp)
+    check_act_save(w, inp, buf, np.arange(R), lora=None if lo is None else {"scale": lo["scale"]})
     dy = to_f64(inp["dy"])
     slot = host(buf.slot).astype(np.int64)
     gate = buf.topk_gate.cpu().numpy().astype(np.float64)

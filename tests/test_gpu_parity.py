@@ -6,8 +6,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import (assert_close, check_dispatch, check_route, expert_ref_rows, host, rows_x,
-                      run_forward, say, upload)
+from gpu_util import (assert_close, bf16_round, check_act_save, check_dispatch, check_route, expert_ref_rows,
+                      host, rows_x, run_forward, say, upload)
 from sparse_mixture_experts_top_amd import binding as B
 from sparse_mixture_experts_top_amd import layer
 from sparse_mixture_experts_top_amd.workloads import WORKLOADS, Workload, generate, to_f64
@@ -301,6 +301,8 @@ def test_lora_forward_backward_and_aux(b_init, x_perm, r, packed, dims):
     lo64 = {"scale": w.lora_alpha / w.lora_r}
     o_ref = expert_ref_rows(w, inp, buf, np.arange(R), lora=lo64)
     assert_close(host(buf.y_perm[:R]), o_ref, "bf16", "expert rows (LoRA)", stored_bf16=True)
+    # the saved G | H | U rows the backward reads, against the oracle's own
+    parts = check_act_save(w, inp, buf, np.arange(R), lora=lo64)
     # aux loss from the GPU counts and probabilities
     B.moe_aux_loss(buf.shape, buf.counts, buf.prob_sum, w.aux_coef, buf.aux)
     p_ref = oracle.softmax_full(lg).sum(0)
@@ -326,6 +328,18 @@ def test_lora_forward_backward_and_aux(b_init, x_perm, r, packed, dims):
                                  act[:, :w.f], act[:, w.f:2 * w.f], to_f64(inp["w_down"]), lo)
     for n in grads:
         assert_close(host(grads[n]), g_ref[n], "bf16", n)
+    # the same gradients from the oracle's own G and H (nothing the GPU
+    # saved): rounded to bf16 where act_save stores them, at the plain
+    # tolerance; unrounded, the gradient sums keep the stored rows' relative
+    # rounding (random-sign sums), so max-abs scales with |ref|inf
+    args = (to_f64(inp["dy"]), rows_x(w, inp, buf, np.arange(R)), host(buf.offsets),
+            host(buf.row_src[:R]), buf.row_gate[:R].cpu().numpy())
+    g_own = oracle.lora_backward(*args, bf16_round(parts["G"]), bf16_round(parts["H"]),
+                                 to_f64(inp["w_down"]), lo)
+    g_own64 = oracle.lora_backward(*args, parts["G"], parts["H"], to_f64(inp["w_down"]), lo)
+    for n in grads:
+        assert_close(host(grads[n]), g_own[n], "bf16", n + " (oracle G, H at bf16)")
+        assert_close(host(grads[n]), g_own64[n], "bf16", n + " (oracle G, H unrounded)", scale_atol=True)
     # the same gradients with W_d^T packed once (the dH product on the DMA
     # engine; the packed transposes need d, f % 128 == 0)
     gp = None

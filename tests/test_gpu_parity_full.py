@@ -7,8 +7,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import (assert_close, check_dispatch, check_route, expert_ref_rows, host, rows_x,
-                      run_forward, say, upload)
+from gpu_util import (assert_close, bf16_round, check_act_save, check_dispatch, check_route, expert_ref_rows,
+                      host, rows_x, run_forward, say, upload)
 from sparse_mixture_experts_top_amd import layer
 from sparse_mixture_experts_top_amd import binding as B
 from sparse_mixture_experts_top_amd.workloads import WORKLOADS, generate, to_f64
@@ -79,16 +79,28 @@ def test_lora_step_full():
     torch.cuda.synchronize()
     offsets = host(buf.offsets)
     dy64 = to_f64(inp["dy"])
-    for le in (0, 6, 13):
+    for le in range(L):        # every local expert
         a, b = int(offsets[le]), int(offsets[le + 1])
         sl = torch.arange(a, b, device="cuda")
+        say(f"  expert {le}: {b - a} rows")
+        # the saved G | H | U rows against the oracle's own
+        parts = check_act_save(w, inp, buf, np.arange(a, b), lora={"scale": w.lora_alpha / r},
+                               what=f"act_save[{le}]")
         act = host(buf.act_save[sl])
         lo = {"scale": w.lora_alpha / r,
               **{n: to_f64(inp[n][le:le + 1]) for n in ("a_up", "b_up", "a_down", "b_down")}}
-        g_ref = oracle.lora_backward(dy64, rows_x(w, inp, buf, np.arange(a, b)), np.array([0, b - a]),
-                                     host(buf.row_src[sl]), buf.row_gate[sl].cpu().numpy(),
-                                     act[:, :f], act[:, f:2 * f], to_f64(inp["w_down"][le:le + 1]), lo)
-        say(f"  expert {le}: {b - a} rows")
+        xe = rows_x(w, inp, buf, np.arange(a, b))
+        args = (dy64, xe, np.array([0, b - a]), host(buf.row_src[sl]), buf.row_gate[sl].cpu().numpy())
+        # fed the GPU's saved G and H, then the oracle's own: rounded to bf16
+        # where act_save stores them (plain tolerance) and unrounded (max-abs
+        # scaled by |ref|inf: the stored rows' relative rounding stays)
+        wd = to_f64(inp["w_down"][le:le + 1])
+        g_ref = oracle.lora_backward(*args, act[:, :f], act[:, f:2 * f], wd, lo)
+        g_own = oracle.lora_backward(*args, bf16_round(parts["G"]), bf16_round(parts["H"]), wd, lo)
+        g_own64 = oracle.lora_backward(*args, parts["G"], parts["H"], wd, lo)
         for n in grads:
             assert_close(host(grads[n][le:le + 1]), g_ref[n], "bf16", f"{n}[{le}]")
             assert_close(host(gp[n][le:le + 1]), g_ref[n], "bf16", f"{n}[{le}] (packed)")
+            assert_close(host(gp[n][le:le + 1]), g_own[n], "bf16", f"{n}[{le}] (packed, oracle G, H at bf16)")
+            assert_close(host(gp[n][le:le + 1]), g_own64[n], "bf16", f"{n}[{le}] (packed, oracle G, H unrounded)",
+                         scale_atol=True)
