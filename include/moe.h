@@ -162,6 +162,27 @@ moe_status_t moe_dispatch(const moe_shape_t* shape, const int32_t* topk_idx,
                           void* x_perm, int32_t* dropped, void* ws, size_t ws_bytes,
                           moe_stream_t stream);
 
+/* moe_dispatch without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. Same arguments (minus ws, ws_bytes) and
+ * bitwise the same outputs as moe_dispatch. It allocates and frees nothing,
+ * not even on its first call: its scratch (per-tile expert histograms and
+ * their scan; with a capacity, the candidate gate keys) is a device array of
+ * MOE_DISPATCH_NOALLOC_SCRATCH_BYTES bytes that the library owns, one copy on
+ * each device it runs on, held until the process ends. A shape needs
+ *   2 * a(ceil(T / 32) * E * 4) + a((L + 1) * 4)
+ *     + (capacity > 0 ? 2 * a(T * k * 4) : 0)   bytes, a(n) = n rounded up
+ * to a multiple of 256; more returns MOE_ERR_WORKSPACE (T = 16384, E = 896:
+ * about 3.7 MB). Every word of the scratch is written before it is read, so
+ * its contents on entry do not matter; calls on one device share the one
+ * array, so calls that overlap on one device (two streams, two threads)
+ * race and must be serialised by the caller. */
+#define MOE_DISPATCH_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+moe_status_t moe_dispatch_noalloc(const moe_shape_t* shape, const int32_t* topk_idx,
+                                  const float* topk_gate, const void* x, int32_t* counts,
+                                  int32_t* offsets, int32_t* slot, int32_t* row_src, float* row_gate,
+                                  void* x_perm, int32_t* dropped, moe_stream_t stream);
+
 /* Grouped expert FFN ("Trillion-Parameter ... Full-Stack Optimization
  * Practices", §3: experts compute in grouped matrix multiplications; SwiGLU
  * expert network). For the rows of local expert le:

@@ -26,7 +26,7 @@ KERNELS = ["router_gemm", "topk", "prob_reduce", "hist", "scan", "scatter", "cap
            "lora_grad", "gate_bwd", "expert_dgu", "expert_dx", "unpermute", "router_bwd"]
 
 EXPORTED = ["moe_workspace_bytes", "moe_max_rows", "moe_last_error", "moe_route",
-            "moe_dispatch", "moe_expert_gemm", "moe_pack_expert_weights", "moe_expert_gemm_packed",
+            "moe_dispatch", "moe_dispatch_noalloc", "moe_expert_gemm", "moe_pack_expert_weights", "moe_expert_gemm_packed",
             "moe_combine", "moe_aux_loss", "moe_lora_bwd", "moe_lora_bwd_packed", "moe_gate_bwd", "moe_expert_bwd",
             "moe_router_bwd", "moe_pack_backward_weights", "moe_expert_bwd_packed", "moe_pack_router_bwd",
             "moe_router_bwd_packed", "moe_router_bwd_unpermute_packed", "moe_timing_enable",
@@ -68,6 +68,7 @@ def lib() -> ctypes.CDLL:
     L.moe_last_error.argtypes, L.moe_last_error.restype = [], ctypes.c_char_p
     L.moe_route.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_dispatch.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_dispatch_noalloc.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.moe_expert_gemm.argtypes = [shp, vp, vp, vp, vp, vp, vp, lor, vp, vp, vp, sz, vp]
     L.moe_pack_expert_weights.argtypes = [shp, vp, vp, vp, vp, vp, vp]
     L.moe_expert_gemm_packed.argtypes = [shp, vp, vp, vp, vp, vp, lor, vp, vp, vp, sz, vp]
@@ -155,6 +156,16 @@ def moe_dispatch(shape, topk_idx, topk_gate, x, counts, offsets, slot, row_src, 
                               _dev(x, dt), _dev(counts, i32), _dev(offsets, i32), _dev(slot, i32),
                               _dev(row_src, i32), _dev(row_gate, torch.float32), _dev(x_perm, dt),
                               _dev(dropped, i32), _dev(ws, torch.uint8), ws.numel(), _stream(stream)))
+
+
+def moe_dispatch_noalloc(shape, topk_idx, topk_gate, x, counts, offsets, slot, row_src, row_gate, x_perm,
+                         dropped, stream=None):
+    """moe_dispatch on the library's own scratch (no workspace argument)."""
+    dt, i32 = _fdt(shape), torch.int32
+    _check(lib().moe_dispatch_noalloc(ctypes.byref(shape), _dev(topk_idx, i32), _dev(topk_gate, torch.float32),
+                                      _dev(x, dt), _dev(counts, i32), _dev(offsets, i32), _dev(slot, i32),
+                                      _dev(row_src, i32), _dev(row_gate, torch.float32), _dev(x_perm, dt),
+                                      _dev(dropped, i32), _stream(stream)))
 
 
 def moe_expert_gemm(shape, x, row_src, offsets, w_gate, w_up, w_down, lora, act_save, y_perm, ws,

@@ -29,7 +29,7 @@ int gemm_max_tiles(const moe_shape_t& s) {
   return (int)((max_rows(s) + kGemmBM - 1) / kGemmBM + (s.e_hi - s.e_lo));
 }
 
-Workspace carve_workspace(const moe_shape_t& s, int lora_r, void* base) {
+Workspace carve_workspace(const moe_shape_t& s, int lora_r, void* base, bool dispatch_only) {
   Workspace w{};
   char* p = static_cast<char*>(base);
   int64_t off = 0;
@@ -49,6 +49,9 @@ Workspace carve_workspace(const moe_shape_t& s, int lora_r, void* base) {
     w.cand_key = static_cast<uint32_t*>(take((int64_t)s.T * s.k * 4));
     w.cand_idx = static_cast<int32_t*>(take((int64_t)s.T * s.k * 4));
   }
+  // everything dispatch uses lies before this point
+  w.dispatch_bytes = off;
+  if (dispatch_only) return w;
   w.gemm_tiles = static_cast<int32_t*>(take((2 * (int64_t)gemm_max_tiles(s) + 1) * 4));
   w.hbuf = take(rmax * s.f * elt);
   if (lora_r > 0) {
@@ -205,6 +208,34 @@ void timing_end(int kid, hipStream_t s) {
   if (e) t.pool.push_back(e);
 }
 
+// ------------------------------------------- library-owned dispatch scratch ---
+// moe_dispatch_noalloc's scratch: the leading dispatch part of the workspace
+// layout (per-tile expert histograms, their scan, with a capacity the
+// candidate keys), in a device array the library owns. Each device holds its
+// own copy from the first use until the process ends. In host code the name
+// `scratch` is only a host-side stand-in for the symbol: its device address
+// comes from hipGetSymbolAddress, once per device, and only that address is
+// handed to kernels.
+static __device__ __align__(256) unsigned char scratch[MOE_DISPATCH_NOALLOC_SCRATCH_BYTES];
+
+static moe_status_t scratch_on_current_device(void** out) {
+  static std::mutex mu;
+  static void* ptr[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+    return fail(MOE_ERR_HIP, "hipGetDevice failed (no HIP device?)");
+  std::lock_guard<std::mutex> g(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MOE_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    ptr[dev] = p;
+  }
+  *out = ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -270,6 +301,38 @@ moe_status_t moe_dispatch(const moe_shape_t* shape, const int32_t* topk_idx,
   return hip_status(launch_dispatch(c, s, w, topk_idx, topk_gate, x, counts, offsets, slot, row_src,
                                     row_gate, x_perm, dropped),
                     "dispatch");
+}
+
+moe_status_t moe_dispatch_noalloc(const moe_shape_t* shape, const int32_t* topk_idx,
+                                  const float* topk_gate, const void* x, int32_t* counts,
+                                  int32_t* offsets, int32_t* slot, int32_t* row_src, float* row_gate,
+                                  void* x_perm, int32_t* dropped, moe_stream_t stream) {
+  moe_status_t st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape_t& s = *shape;
+  const bool rows = max_rows(s) > 0;
+  MOE_REQUIRE_IF(s.T > 0, topk_idx, "topk_idx");
+  MOE_REQUIRE_IF(s.T > 0, topk_gate, "topk_gate");
+  MOE_REQUIRE_IF(s.T > 0 && x_perm, x, "x");
+  MOE_REQUIRE(counts, "counts");
+  MOE_REQUIRE(offsets, "offsets");
+  MOE_REQUIRE_IF(s.T > 0, slot, "slot");
+  MOE_REQUIRE_IF(rows, row_src, "row_src");
+  MOE_REQUIRE_IF(rows, row_gate, "row_gate");
+  const int64_t need = carve_workspace(s, 0, nullptr, true).dispatch_bytes;
+  if (need > (int64_t)MOE_DISPATCH_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ERR_WORKSPACE, "moe_dispatch_noalloc: this shape needs " + std::to_string(need) +
+                                       " bytes of scratch, more than the library's " +
+                                       std::to_string((int64_t)MOE_DISPATCH_NOALLOC_SCRATCH_BYTES) +
+                                       "; use moe_dispatch with a workspace");
+  Ctx c;
+  if ((st = make_ctx(stream, &c)) != MOE_OK) return st;
+  void* base = nullptr;
+  if ((st = scratch_on_current_device(&base)) != MOE_OK) return st;
+  const Workspace w = carve_workspace(s, 0, base, true);
+  return hip_status(launch_dispatch(c, s, w, topk_idx, topk_gate, x, counts, offsets, slot, row_src,
+                                    row_gate, x_perm, dropped),
+                    "dispatch (no allocation)");
 }
 
 moe_status_t moe_expert_gemm(const moe_shape_t* shape, const void* x, const int32_t* row_src,

@@ -176,14 +176,17 @@ struct Workspace {
   bf16_t* zx;            // [Rmax, 2r] s Z as bf16 high | low parts (the extra adapter K step)
   float* logits;         // [T, E]
   float* prob_part;      // [prob_blocks, E]
-  int64_t bytes;
+  int64_t dispatch_bytes;  // the leading part dispatch uses (tile_counts .. cand_idx)
+  int64_t bytes;           // all of it (0 when carved with dispatch_only)
 };
 
 constexpr int kTokTile = 32;       // tokens per dispatch tile (one 32-bit mask per expert)
 constexpr int kTopkTokPerWaveProb = 2;  // tokens per top-k wave when softmax sums are kept
 constexpr int kGemmBM = 128;       // grouped GEMM row tile
 
-Workspace carve_workspace(const moe_shape_t& s, int lora_r, void* base);
+// dispatch_only: lay out the leading dispatch part only (no pointer past it
+// is formed), for a scratch area that holds just that part.
+Workspace carve_workspace(const moe_shape_t& s, int lora_r, void* base, bool dispatch_only = false);
 int64_t max_rows(const moe_shape_t& s);
 int gemm_max_tiles(const moe_shape_t& s);
 

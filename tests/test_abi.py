@@ -169,3 +169,18 @@ def test_expert_backward_packed_accepts_null_dx_and_slot():
     args[10] = fake
     assert lib.moe_expert_bwd_packed(ctypes.byref(bf), None, *args, 1 << 30, None) == B.MOE_ERR_INVALID_ARG
     assert b"slot is NULL" in lib.moe_last_error()
+
+
+def test_dispatch_noalloc_rejects_shapes_beyond_its_scratch():
+    """The no-allocation dispatch checks the scratch a shape needs against the
+    library's fixed array on the host, before any device call."""
+    lib = B.lib()
+    fake = ctypes.c_void_p(0x100000)      # never dereferenced: validation fails first
+    # 2^20 tokens over 1024 experts: 2 * 32768 * 1024 * 4 B = 256 MiB of tile histograms
+    s = shape(T=1 << 20, E=1024, e_hi=1024, k=2, dtype=B.MOE_BF16, d=128, f=64)
+    st = lib.moe_dispatch_noalloc(ctypes.byref(s), fake, fake, None, fake, fake, fake, fake, fake, None,
+                                  None, None)
+    assert st == B.MOE_ERR_WORKSPACE
+    assert b"scratch" in lib.moe_last_error()
+    assert lib.moe_dispatch_noalloc(ctypes.byref(shape()), None, fake, None, fake, fake, fake, fake, fake,
+                                    None, None, None) == B.MOE_ERR_INVALID_ARG
