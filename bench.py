@@ -8,10 +8,15 @@ f=256, bf16, all experts on this GPU), inputs resident in HBM before timing.
 Prints ONE JSON line: tokens/s, ms per step, the roofline of the dominant
 kernel (the gate/up grouped GEMM, which streams 1.9 GB of expert weights per
 step) from HIP events recorded around it on its launch stream, and the CPU
-oracle timed on a bounded token sample of the same workload.
+oracle timed on a bounded token sample of the same workload. With the
+default workload the line also carries "workloads": the one-rank share at
+EP = 64 (16384 tokens, 14 local experts, f = 1024), the skewed routing with
+capacity and the LoRA fine-tuning step, each with ms per step, tokens/s and
+every stage against its roofline (fewer steps, no CPU baseline).
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                  [--no-cpu-baseline] [--calibrate-copy]
+                  [--no-cpu-baseline] [--no-backward] [--no-extra-workloads]
+                  [--graph] [--calibrate-copy]
 """
 from __future__ import annotations
 
@@ -137,6 +142,8 @@ def main() -> int:
     ap.add_argument("--workload", default="full_router")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement pass")
+    ap.add_argument("--no-extra-workloads", action="store_true",
+                    help="with the default workload, skip the ep64_rank / skewed_capacity / lora_step lines")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--graph", dest="graph", action="store_true", default=False,
                     help="time one HIP-graph replay of the K steps (no per-kernel roofline: "
@@ -148,18 +155,65 @@ def main() -> int:
               file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
 
-    from sparse_mixture_experts_top_amd import binding as B
-    from sparse_mixture_experts_top_amd import layer
-    from sparse_mixture_experts_top_amd.workloads import WORKLOADS, generate
+    from sparse_mixture_experts_top_amd.workloads import WORKLOADS
 
     if args.calibrate_copy:
         calibrate_copy()
         return 0
 
     w = WORKLOADS[args.workload]
+    out = run_workload(args, w, args.steps, args.warmup, backward=not args.no_backward,
+                       cpu=not args.no_cpu_baseline, graph=args.graph)
+    if args.workload == "full_router" and not args.no_extra_workloads:
+        # the other single-GPU workloads, fewer steps, each with its dominant
+        # kernel against its roofline (no backward pass, no CPU baseline)
+        out["workloads"] = {}
+        for name in ("ep64_rank", "skewed_capacity", "lora_step"):
+            torch.cuda.empty_cache()
+            res = run_workload(args, WORKLOADS[name], min(args.steps, 10), min(args.warmup, 3),
+                               backward=False, cpu=False, graph=False)
+            out["workloads"][name] = summarise(res)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def summarise(res):
+    """The figures of one extra workload that the bench line carries."""
+    keep = ("ms_per_step", "value", "steps", "warmup")
+    s = {k: res[k] for k in keep}
+    s["tokens_per_s"] = s.pop("value")
+    s["config"] = res["config"]
+    s["dominant_kernel"] = res["dominant_kernel"]
+    s["roofline"] = res["roofline"]
+    s["stage_roofline"] = res.get("stage_roofline")
+    s["kernels_us"] = res.get("kernels_us", res.get("kernels_us_per_step"))
+    return s
+
+
+def gemm_roofline(name, flops, nbytes, us):
+    """A grouped GEMM against both of its roofs: the bound is whichever of
+    flops / MFMA peak and bytes / HBM peak takes longer."""
+    tf = flops / (us * 1e-6) / 1e12
+    gbs = nbytes / (us * 1e-6) / 1e9
+    t_mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    return {"bound": "mfma" if t_mfma > t_hbm else "hbm", "us": round(us, 2), "tflops": round(tf, 1),
+            "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "gbs": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "frac": round(max(t_mfma, t_hbm) / (us * 1e-6), 4)}
+
+
+def run_workload(args, w, steps, warmup, backward, cpu, graph):
+    """Time ``steps`` forward steps of workload ``w`` (the LoRA step for a
+    LoRA workload) and return its bench record."""
+    import torch
+
+    from sparse_mixture_experts_top_amd import binding as B
+    from sparse_mixture_experts_top_amd import layer
+    from sparse_mixture_experts_top_amd.workloads import generate
+
     log(f"[bench] generating {w.name}: T={w.T} d={w.d} E={w.E} k={w.k} f={w.f} L={w.L}")
     t0 = time.time()
     inp = generate(w, seed=0)
@@ -168,16 +222,14 @@ def main() -> int:
     log(f"[bench] inputs ready in {time.time() - t0:.1f} s")
     shape = layer.shape_of(w)
     if w.lora_r:
-        out = lora_step_bench(args, w, inp, dev, shape)
-        print(json.dumps(out), flush=True)
-        return 0
+        return lora_step_bench(args, w, inp, dev, shape, steps, warmup, cpu)
     buf = layer.alloc(shape)
     # the frozen expert weights live in their packed layout (one-time, outside the step)
     packed = layer.pack_weights(shape, dev["w_gate"], dev["w_up"], dev["w_down"])
     torch.cuda.synchronize()
     args_fw = (dev["x"], dev["w_router"], dev.get("bias"), None, None, None)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         layer.forward(buf, *args_fw, packed=packed)
     torch.cuda.synchronize()
 
@@ -186,11 +238,10 @@ def main() -> int:
     # --graph the K steps are captured once into one HIP graph and the timed
     # region is one replay of it (the roofline kernel is then timed in the
     # breakdown pass below instead).
-    graph = None
-    if args.graph:
-        graph = layer.capture(lambda: [layer.forward(buf, *args_fw, packed=packed)
-                                       for _ in range(args.steps)])
-        graph.replay()
+    g = None
+    if graph:
+        g = layer.capture(lambda: [layer.forward(buf, *args_fw, packed=packed) for _ in range(steps)])
+        g.replay()
         torch.cuda.synchronize()
     else:
         B.moe_timing_enable(["gate_up"])
@@ -198,20 +249,20 @@ def main() -> int:
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
-    if graph is not None:
-        graph.replay()
+    if g is not None:
+        g.replay()
     else:
-        for _ in range(args.steps):
+        for _ in range(steps):
             layer.forward(buf, *args_fw, packed=packed)
     stop.record(stream)
     torch.cuda.synchronize()
     elapsed_ms = start.elapsed_time(stop)
-    gu_ms, gu_n = (0.0, 0) if graph else B.moe_timing_read("gate_up")
-    log(f"[bench] {args.steps} steps in {elapsed_ms:.3f} ms ({'one graph replay' if graph else 'eager launches'})")
+    gu_ms, gu_n = (0.0, 0) if g else B.moe_timing_read("gate_up")
+    log(f"[bench] {w.name}: {steps} steps in {elapsed_ms:.3f} ms ({'one graph replay' if g else 'eager launches'})")
     # per-kernel breakdown from extra steps outside the timed region (every
     # kernel bracketed by events)
     B.moe_timing_enable(True)
-    for _ in range(max(1, min(args.steps, 10))):
+    for _ in range(max(1, min(steps, 10))):
         layer.forward(buf, *args_fw, packed=packed)
     torch.cuda.synchronize()
     kernels = {}
@@ -221,7 +272,7 @@ def main() -> int:
             kernels[name] = {"avg_us": 1000.0 * ms / n, "launches": n}
     B.moe_timing_enable(False)
 
-    ms_step = elapsed_ms / args.steps
+    ms_step = elapsed_ms / steps
     tok_s = w.T / (ms_step / 1000.0)
 
     # algorithmic bytes of one gate/up launch: the gate and up weights of every
@@ -233,10 +284,13 @@ def main() -> int:
     gu_us = 1000.0 * gu_ms / gu_n if gu_n else kernels["gate_up"]["avg_us"]
     achieved = gu_bytes / (gu_us * 1e-6) / 1e9
     traffic = recorded_traffic(w.name)
+    gu_flops = 4.0 * R * w.d * w.f
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic, "kernel": "gate_up_bf16", "algorithmic_bytes": gu_bytes,
-            "avg_us": round(gu_us, 2)}
+            "avg_us": round(gu_us, 2),
+            "mfma_tflops": round(gu_flops / (gu_us * 1e-6) / 1e12, 1),
+            "mfma_frac": round(gu_flops / (gu_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
     # layer-level figures for context
     flops = 2 * w.T * w.d * w.E + 6 * R * w.d * w.f
     # every stage against its own roofline, from the breakdown pass (durations
@@ -245,9 +299,11 @@ def main() -> int:
         "router_gemm": ("mfma", 2.0 * w.T * w.d * w.E),
         "topk": ("hbm", w.T * w.E * 4 + w.T * w.k * 8),
         "dispatch": ("hbm", 3 * w.T * w.k * 4 + w.T * w.k * 4 + R * 8),
-        "gate_up": ("hbm", gu_bytes),
-        "down": ("hbm", active * w.d * w.f * 2 + R * w.f * 2 + R * w.d * 2),
         "combine": ("hbm", R * w.d * 2 + w.T * w.k * 8 + w.T * w.d * 2),
+    }
+    gemm_work = {
+        "gate_up": (gu_flops, gu_bytes),
+        "down": (2.0 * R * w.d * w.f, active * w.d * w.f * 2 + R * w.f * 2 + R * w.d * 2),
     }
     stage_us = {k: v["avg_us"] for k, v in kernels.items()}
     stage_us["dispatch"] = sum(stage_us.get(n, 0.0) for n in ("hist", "scan", "scatter", "capacity"))
@@ -263,29 +319,33 @@ def main() -> int:
         else:
             stages[name] = {"bound": "hbm", "us": round(us, 2), "gbs": round(rate / 1e9, 1),
                             "frac": round(rate / 1e9 / HBM_PEAK_GBS, 4)}
+    for name, (fl, nb) in gemm_work.items():
+        if stage_us.get(name):
+            stages[name] = gemm_roofline(name, fl, nb, stage_us[name])
+    dominant = max(stages, key=lambda n: stages[n]["us"]) if stages else None
     out = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "steps": steps, "warmup": warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) tokens, N(0,1/fan_in) weights)",
-        "config": {"workload": w.name, "launch": "hip_graph" if graph else "eager",
+        "config": {"workload": w.name, "launch": "hip_graph" if g else "eager",
                    "T": w.T, "d": w.d, "E": w.E, "k": w.k, "f": w.f,
                    "local_experts": w.L, "capacity": w.capacity, "rows": R,
                    "active_experts": active},
         "roofline": roof,
+        "dominant_kernel": {"name": dominant, **stages[dominant]} if dominant else None,
         "layer_tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
         "kernels_us": {k: round(v["avg_us"], 2) for k, v in kernels.items()},
         "stage_roofline": stages,
     }
-    if not args.no_backward:
+    if backward:
         out["backward"] = backward_pass(w, dev, shape, packed, R, active)
-    if not args.no_cpu_baseline:
+    if cpu:
         out["cpu_baseline"] = cpu_baseline(w, inp)
-    print(json.dumps(out), flush=True)
-    return 0
+    return out
 
 
-def lora_step_bench(args, w, inp, dev, shape):
+def lora_step_bench(args, w, inp, dev, shape, steps, warmup, cpu):
     """One LoRA fine-tuning step of the layer: the forward with the rank-r
     adapters on the up and down projections (route with the softmax sums,
     dispatch, expert GEMMs saving G/H/U, combine), the load-balance loss, and
@@ -321,30 +381,33 @@ def lora_step_bench(args, w, inp, dev, shape):
             B.moe_lora_bwd(shape, lora, dev["dy"], buf.offsets, buf.row_src, buf.row_gate, xr, xs, buf.act_save,
                            dev["w_down"], *grads, buf.ws)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     B.moe_timing_enable(["gate_up"])
     stream = torch.cuda.current_stream()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     stop.record(stream)
     torch.cuda.synchronize()
     elapsed_ms = start.elapsed_time(stop)
     gu_ms, gu_n = B.moe_timing_read("gate_up")
     B.moe_timing_enable(True)
-    for _ in range(max(1, min(args.steps, 10))):
+    nb = max(1, min(steps, 10))
+    for _ in range(nb):
         step()
     torch.cuda.synchronize()
     kernels = {}  # microseconds per step, summed over a kind's launches in the step
+    launches = {}
     for name in B.KERNELS:
         ms, n = B.moe_timing_read(name)
         if n:
-            kernels[name] = round(1000.0 * ms / max(1, min(args.steps, 10)), 2)
+            kernels[name] = round(1000.0 * ms / nb, 2)
+            launches[name] = n
     B.moe_timing_enable(False)
-    ms_step = elapsed_ms / args.steps
+    ms_step = elapsed_ms / steps
     counts = buf.offsets.diff().cpu().numpy()
     R = int(buf.offsets[-1].item())
     active = int((counts > 0).sum())
@@ -354,7 +417,7 @@ def lora_step_bench(args, w, inp, dev, shape):
     gu_flops = 4.0 * R * d * f
     out = {
         "metric": METRIC, "value": round(w.T / (ms_step / 1000.0), 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "steps": steps, "warmup": warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) tokens and dY, N(0,1/fan_in) weights, LoRA A ~ N(0,1/d), "
                 "B ~ N(0,1e-3))",
@@ -369,7 +432,23 @@ def lora_step_bench(args, w, inp, dev, shape):
                      "mfma_frac": round(gu_flops / (gu_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
         "kernels_us_per_step": kernels,
     }
-    if not args.no_cpu_baseline:
+    # the step's grouped GEMMs and router against their roofs (per launch)
+    per_launch = {n: kernels[n] * nb / launches[n] for n in kernels}
+    stages = {}
+    if "router_gemm" in per_launch:
+        rt = 2.0 * w.T * d * w.E / (per_launch["router_gemm"] * 1e-6) / 1e12
+        stages["router_gemm"] = {"bound": "mfma", "us": round(per_launch["router_gemm"], 2),
+                                 "tflops": round(rt, 1), "frac": round(rt / MFMA_BF16_PEAK_TFLOPS, 4)}
+    if "gate_up" in per_launch:
+        stages["gate_up"] = gemm_roofline("gate_up", gu_flops, gu_bytes, per_launch["gate_up"])
+    if "down" in per_launch:
+        stages["down"] = gemm_roofline("down", 2.0 * R * d * f, active * d * f * 2 + R * f * 2 + R * d * 2,
+                                       per_launch["down"])
+    out["stage_roofline"] = stages
+    dominant = max(kernels, key=lambda n: kernels[n])
+    out["dominant_kernel"] = {"name": dominant, "us_per_step": kernels[dominant],
+                              **({k: v for k, v in stages[dominant].items()} if dominant in stages else {})}
+    if cpu:
         out["cpu_baseline"] = cpu_baseline(w, inp)
     return out
 

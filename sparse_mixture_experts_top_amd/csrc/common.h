@@ -223,8 +223,10 @@ hipError_t launch_expert_gemm(const Ctx& c, const moe_shape_t& s, const Workspac
 hipError_t launch_pack(const Ctx& c, const moe_shape_t& s, const void* w_gate, const void* w_up,
                        const void* w_down, void* gu_packed, void* d_packed);
 
+// Row tiles of bm rows (kGemmBM unless the GEMM that reads the list uses
+// another tile height; max_tiles from gemm_max_tiles bounds any bm >= kGemmBM).
 hipError_t launch_row_tiles(const Ctx& c, const int32_t* offsets, int L, int max_tiles,
-                            int32_t* tiles);
+                            int32_t* tiles, int bm = kGemmBM);
 
 hipError_t launch_combine(const Ctx& c, const moe_shape_t& s, const void* y_perm,
                           const int32_t* slot, const float* gate, void* y);

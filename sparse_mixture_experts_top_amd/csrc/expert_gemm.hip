@@ -45,9 +45,19 @@ namespace moe {
 //                MFMA issue rate decides.
 using GemmCfg = DmaCfg<kGemmBM, 256, MOE_GEMM_STAGES, 2>;
 using GemmCfgWide = DmaCfg<kGemmBM, 256, MOE_GEMM_STAGES, 2, 8, 4>;
+// 320 x 128 tiles for experts with a few hundred rows: an item takes up to
+// 320 rows, i.e. all rows of an expert with at most 320, so each weight tile
+// is streamed once per expert instead of once per 128-row tile, and the
+// items (experts x column blocks) fit the CUs in one round. 4 x 2 compute
+// waves (two per SIMD), each 5 interleaved row fragments x 4 column
+// fragments (80 x 64), + 4 producers; 5 ring slots of 28 KB.
+#ifndef MOE_GEMM_TALL_STAGES
+#define MOE_GEMM_TALL_STAGES 5
+#endif
+using GemmCfgTall = DmaCfg<320, 128, MOE_GEMM_TALL_STAGES, 4, 8, 4>;
 
 // Rows per local expert expected under uniform routing (capped by the
-// capacity) at which the wide layout is used.
+// capacity) at which the tall layout is used.
 constexpr int kWideRowsPerExpert = 192;
 
 __global__ __launch_bounds__(1024) void build_row_tiles(const int32_t* __restrict__ offsets, int L,
@@ -154,6 +164,9 @@ struct GateUpProb {
   bf16_t* hbuf;
   bf16_t* act_save;
   const bf16_t* zx = nullptr;  // LORA == 2: [Rmax, 32] s Z_u high | low
+  // the weight tiles are expected to be read by one row tile each (an
+  // expert's rows fit one tile): fetch them with the streaming hint
+  bool stream_b = false;
   static constexpr int HALF = Cfg::BN / 2;  // FFN columns per item (the last item may be partial)
 
   __device__ __forceinline__ int rows(int item) const {
@@ -164,6 +177,7 @@ struct GateUpProb {
     const RowTile t = row_tile<Cfg::BM>(tiles, offsets, item / nt);
     const int ni = item % nt;
     const int ce = dma_chunk_elem<Cfg>();
+    ld.b_stream = stream_b;
 #pragma unroll
     for (int q = 0; q < Cfg::A_DMA / Cfg::DW; ++q) {
       const int i = q * Cfg::DW + part;
@@ -285,6 +299,7 @@ struct DownProb {
   float scale;
   bf16_t* y_perm;
   const bf16_t* zx = nullptr;  // LORA == 2: [Rmax, 32] s Z_d high | low
+  bool stream_b = false;        // as GateUpProb
 
   __device__ __forceinline__ int rows(int item) const {
     return row_tile<Cfg::BM>(tiles, offsets, item / nt).valid;
@@ -294,6 +309,7 @@ struct DownProb {
     const RowTile t = row_tile<Cfg::BM>(tiles, offsets, item / nt);
     const int n0 = (item % nt) * Cfg::BN;
     const int ce = dma_chunk_elem<Cfg>();
+    ld.b_stream = stream_b;
 #pragma unroll
     for (int q = 0; q < Cfg::A_DMA / Cfg::DW; ++q)
       ld.a[q] = hbuf + (t.row0 + min(dma_row<Cfg>(q * Cfg::DW + part), t.valid - 1)) * f + ce;
@@ -925,9 +941,9 @@ __global__ __launch_bounds__(256) void down_f32(const float* __restrict__ hbuf,
 // ------------------------------------------------------------- launchers ---
 
 hipError_t launch_row_tiles(const Ctx& c, const int32_t* offsets, int L, int max_tiles,
-                            int32_t* tiles) {
+                            int32_t* tiles, int bm) {
   TimedLaunch tl(MOE_K_TILES, c.stream);
-  hipLaunchKernelGGL(build_row_tiles, dim3(1), dim3(1024), 0, c.stream, offsets, L, kGemmBM,
+  hipLaunchKernelGGL(build_row_tiles, dim3(1), dim3(1024), 0, c.stream, offsets, L, bm,
                      max_tiles, tiles);
   return hipGetLastError();
 }
@@ -962,7 +978,6 @@ hipError_t launch_expert_gemm(const Ctx& c, const moe_shape_t& s, const Workspac
     return hipGetLastError();
   }
   const int max_tiles = gemm_max_tiles(s);
-  if ((err = launch_row_tiles(c, offsets, L, max_tiles, ws.gemm_tiles)) != hipSuccess) return err;
   const bf16_t* xr = (const bf16_t*)x_rows;
   // adapter terms: through the matrix cores as one extra K step at r = 16
   // (the projection's matrix-core path applies: d, f % 32 == 0), else in
@@ -980,7 +995,7 @@ hipError_t launch_expert_gemm(const Ctx& c, const moe_shape_t& s, const Workspac
   int64_t per_expert = tk / s.E;
   if (s.capacity > 0 && per_expert > s.capacity) per_expert = s.capacity;
   if (per_expert >= kWideRowsPerExpert)
-    return launch_grouped_bf16<GemmCfgWide>(c, s, ws, xr, row_src, offsets, gu_packed, d_packed, w_gate,
+    return launch_grouped_bf16<GemmCfgTall>(c, s, ws, xr, row_src, offsets, gu_packed, d_packed, w_gate,
                                             w_up, w_down, lora, act_save, y_perm, max_tiles, lora_mode);
   return launch_grouped_bf16<GemmCfg>(c, s, ws, xr, row_src, offsets, gu_packed, d_packed, w_gate, w_up,
                                       w_down, lora, act_save, y_perm, max_tiles, lora_mode);
@@ -996,6 +1011,13 @@ hipError_t launch_grouped_bf16(const Ctx& c, const moe_shape_t& s, const Workspa
   const int L = s.e_hi - s.e_lo;
   const int64_t rmax = max_rows(s);
   const int grid = c.num_cus;  // one workgroup per CU (see mfma_tile.h)
+  if ((err = launch_row_tiles(c, offsets, L, max_tiles, ws.gemm_tiles, Cfg::BM)) != hipSuccess) return err;
+  // Weight tiles are fetched with the streaming hint when an expert's rows are
+  // expected to fit one row tile (the capacity, or the even share T k / E
+  // with 5% to spare); where experts span several row tiles that share each
+  // weight tile, the hint measured slower (capacity 183 on 128-row tiles).
+  const int64_t even = (int64_t)s.T * s.k / s.E;
+  const bool stream_b = s.capacity > 0 ? s.capacity <= Cfg::BM : even * 20 <= (int64_t)Cfg::BM * 19;
   auto gu_launch = [&](auto mode) {
     constexpr int LO = decltype(mode)::value;
     using P = GateUpProb<Cfg, LO>;
@@ -1005,6 +1027,7 @@ hipError_t launch_grouped_bf16(const Ctx& c, const moe_shape_t& s, const Workspa
          lora ? ws.zu : nullptr, lora ? lora->b_up : nullptr, lora ? lora->r : 0,
          lora ? lora->scale : 0.f, (bf16_t*)ws.hbuf, (bf16_t*)act_save};
     pb.zx = ws.zx;
+    pb.stream_b = stream_b;
     TimedLaunch tl(MOE_K_GATE_UP, c.stream);
     hipLaunchKernelGGL((gate_up_bf16<Cfg, LO>), dim3(grid), dim3(Cfg::THREADS), 0, c.stream, pb, max_tiles);
     return hipGetLastError();
@@ -1029,6 +1052,7 @@ hipError_t launch_grouped_bf16(const Ctx& c, const moe_shape_t& s, const Workspa
                          lora ? lora->b_down : nullptr, lora ? lora->r : 0, lora ? lora->scale : 0.f,
                          (bf16_t*)y_perm};
     pb.zx = ws.zx;
+    pb.stream_b = stream_b;
     TimedLaunch tl(MOE_K_DOWN, c.stream);
     hipLaunchKernelGGL((down_bf16<Cfg, LO>), dim3(grid), dim3(Cfg::THREADS), 0, c.stream, pb, max_tiles);
     return hipGetLastError();

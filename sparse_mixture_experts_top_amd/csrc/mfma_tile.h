@@ -349,12 +349,15 @@ struct DmaCfg {
 // Prob::setup(item, ld, part).
 // a_kstep / b_kstep: elements between consecutive K steps of one operand
 // (32 for a row-major operand; one whole packed tile for a packed one).
+// b_stream: every B line is read by this item only (streamed weight tiles),
+// so B is fetched with the non-temporal hint (see dma16_nt).
 template <class Cfg>
 struct DmaLoader {
   const bf16_t* a[Cfg::A_DMA / Cfg::DW];
   const bf16_t* b[Cfg::B_DMA / Cfg::DW];
   int a_kstep = Cfg::BK;
   int b_kstep = Cfg::BK;
+  bool b_stream = false;
 };
 
 // Swizzle key of tile row r for 64-byte rows (4 chunks; BK = 32, also the
@@ -394,6 +397,16 @@ __device__ __forceinline__ void dma16(const void* g, const bf16_t* lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(a) : "memory");
 }
 
+// The same with the non-temporal hint, for an operand every line of which is
+// read by one workgroup only (streamed weight tiles): the L2 then evicts those
+// lines first and keeps the operand tiles that neighbouring CUs share (a
+// 320-row expert tile's token rows, read by all its column blocks), which
+// the streamed weights otherwise push out (ep64 gate/up 119 -> 110 us).
+__device__ __forceinline__ void dma16_nt(const void* g, const bf16_t* lds) {
+  const uint32_t a = (uint32_t)(uintptr_t)(lds_void_t*)lds;
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(g), "s"(a) : "memory");
+}
+
 // Producer `part`'s share of the DMA instructions of K step kt into stage
 // `stage`: A and B instructions i with i % DW == part.
 template <class Cfg>
@@ -402,9 +415,15 @@ __device__ __forceinline__ void dma_issue(const DmaLoader<Cfg>& ld, int kt, bf16
 #pragma unroll
   for (int q = 0; q < Cfg::A_DMA / Cfg::DW; ++q)
     dma16(ld.a[q] + ka, stage + Cfg::RPD * (q * Cfg::DW + part) * Cfg::BK);
+  if (ld.b_stream) {  // wave-uniform
 #pragma unroll
-  for (int q = 0; q < Cfg::B_DMA / Cfg::DW; ++q)
-    dma16(ld.b[q] + kb, stage + Cfg::A_ELEMS + Cfg::RPD * (q * Cfg::DW + part) * Cfg::BK);
+    for (int q = 0; q < Cfg::B_DMA / Cfg::DW; ++q)
+      dma16_nt(ld.b[q] + kb, stage + Cfg::A_ELEMS + Cfg::RPD * (q * Cfg::DW + part) * Cfg::BK);
+  } else {
+#pragma unroll
+    for (int q = 0; q < Cfg::B_DMA / Cfg::DW; ++q)
+      dma16(ld.b[q] + kb, stage + Cfg::A_ELEMS + Cfg::RPD * (q * Cfg::DW + part) * Cfg::BK);
+  }
 }
 
 // Packed B operand: a weight tile of 128 rows x one K step stored as the
@@ -554,6 +573,7 @@ struct ExtraSteps<P, std::void_t<decltype(P::kExtra)>> {
   static constexpr int value = P::kExtra;
 };
 
+
 // Persistent warp-specialised driver on the DMA ring. Items are processed in
 // order; Prob::rows(item) gives an item's valid tile rows (row fragments past
 // them skip their MFMAs), Prob::setup(item, ld, part) fills producer part's
@@ -600,8 +620,9 @@ __device__ __forceinline__ void persistent_gemm_dma(Prob& pb, int items, int nk_
       if (++l_kt == nk) {
         l_kt = 0;
         if (++l_ord < n_mine) {
-          pb.setup(sp.first + l_ord * sp.stride, ld, part);
-          if constexpr (NX > 0) pb.setup_extra(sp.first + l_ord * sp.stride, ldx, part);
+          const int item = sp.first + l_ord * sp.stride;
+          pb.setup(item, ld, part);
+          if constexpr (NX > 0) pb.setup_extra(item, ldx, part);
         }
       }
     };
@@ -640,7 +661,7 @@ __device__ __forceinline__ void persistent_gemm_dma(Prob& pb, int items, int nk_
       mma_pp_step<Cfg>(g0 + kt, total, nf, ring, rslot, f0, f1, acc, wm, wn, lane);
       wait_lgkm0();
       mma_pp_step<Cfg>(g0 + kt + 1, total, nf, ring, rslot, f1, f0, acc, wm, wn, lane);
-      if (kt + 2 < nk) wait_lgkm0();
+      wait_lgkm0();
     }
     const bool odd = kt < nk;  // wave-uniform
     if (odd) mma_pp_step<Cfg>(g0 + kt, total, nf, ring, rslot, f0, f1, acc, wm, wn, lane);
