@@ -184,6 +184,102 @@ def dispatch(idx, gate, E: int, e_lo: int = 0, e_hi: Optional[int] = None,
     }
 
 
+def dispatch_remap(idx, alt, gate, E: int, e_lo: int = 0, e_hi: Optional[int] = None,
+                   capacity: int = 0) -> Dict[str, np.ndarray]:
+    """Dispatch with token remapping instead of dropping ([Paths §3.3]:
+    tokens above an expert's capacity are remapped or dropped).
+
+    Reading (the pages give no rule):
+      1. The capacity rule of ``dispatch`` runs over all E experts: expert e
+         keeps its C assignments with the largest gate (ties to the lower
+         token); the others overflow.
+      2. Each token sends its overflowing assignments, in slot order j, to
+         its next-ranked experts outside its selection: the m-th overflowing
+         assignment of token t proposes to alt[t, m], where alt[t] lists the
+         experts ranked k, k+1, ... by logit (the same order as the
+         selection). A token therefore never proposes twice to one expert,
+         nor to an expert it already selected.
+      3. Expert e accepts proposals into the room its kept assignments left,
+         C - kept_e, preferring the larger gate, then the lower token; the
+         other proposals are dropped. An accepted assignment keeps its gate
+         g[t, j]: the token's combine weights do not change, only the expert
+         that serves the slot.
+    Rows are grouped by local expert ascending and by token ascending inside
+    an expert, as in ``dispatch``.
+
+    Returns the keys of ``dispatch`` (counts = assignments per expert before
+    capacity, over the original selection) plus
+      expert   [T,k]  the expert serving each assignment (primary or alt),
+                      -1 when dropped
+      moved    int    accepted proposals on local experts
+      dropped  int    rejected proposals to local experts
+    """
+    idx = np.asarray(idx)
+    alt = np.asarray(alt)
+    g = np.asarray(gate)
+    T, k = idx.shape
+    if e_hi is None:
+        e_hi = E
+    L = e_hi - e_lo
+    counts = np.zeros(E, dtype=np.int64)
+    for e in idx.ravel():
+        counts[e] += 1
+    # 1. the capacity rule over every expert (which assignments overflow)
+    primary = dispatch(idx, gate, E, 0, E, capacity)
+    kept1 = primary["slot"] >= 0
+    kept_per_expert = np.zeros(E, dtype=np.int64)
+    for t in range(T):
+        for j in range(k):
+            if kept1[t, j]:
+                kept_per_expert[idx[t, j]] += 1
+    # 2. proposals: the m-th overflowing slot of token t goes to alt[t, m]
+    target = idx.copy()
+    proposal = np.zeros((T, k), dtype=bool)
+    for t in range(T):
+        m = 0
+        for j in range(k):
+            if not kept1[t, j]:
+                target[t, j] = alt[t, m]
+                proposal[t, j] = True
+                m += 1
+    # 3. each expert fills its room with the best proposals
+    accepted = np.zeros((T, k), dtype=bool)
+    for e in range(E):
+        ts, js = np.nonzero(proposal & (target == e))
+        room = max(capacity - int(kept_per_expert[e]), 0) if capacity > 0 else len(ts)
+        order = np.lexsort((ts, -g[ts, js].astype(F64)))   # larger gate, then lower token
+        for q in order[:room]:
+            accepted[ts[q], js[q]] = True
+    served = kept1 | accepted
+    expert = np.where(served, target, -1)
+    # rows: local experts ascending, tokens ascending inside an expert
+    slot = np.full((T, k), -1, dtype=np.int64)
+    rows_src, rows_gate = [], []
+    offsets = np.zeros(L + 1, dtype=np.int64)
+    moved = dropped = 0
+    for le in range(L):
+        e = e_lo + le
+        offsets[le] = len(rows_src)
+        ts, js = np.nonzero(expert == e)        # row-major: token ascending
+        for t, j in zip(ts, js):
+            slot[t, j] = len(rows_src)
+            rows_src.append(t)
+            rows_gate.append(g[t, j])
+        moved += int((accepted & (target == e)).sum())
+        dropped += int((proposal & ~accepted & (target == e)).sum())
+    offsets[L] = len(rows_src)
+    return {
+        "counts": counts,
+        "offsets": offsets,
+        "slot": slot,
+        "row_src": np.asarray(rows_src, dtype=np.int64),
+        "row_gate": np.asarray(rows_gate, dtype=F64),
+        "expert": expert,
+        "moved": moved,
+        "dropped": dropped,
+    }
+
+
 # ----------------------------------------------------------------- experts --
 
 def silu(a):

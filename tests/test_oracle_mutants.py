@@ -9,6 +9,7 @@ import oracle.moe_oracle as mo
 import test_oracle_backward as tbwd
 import test_oracle_dispatch as tdisp
 import test_oracle_experts as texp
+import test_oracle_remap as tremap
 import test_oracle_routing as trout
 
 F64 = np.float64
@@ -85,9 +86,53 @@ def _experts_bwd_gate_up_swapped(dy, offsets, row_src, row_gate, slot, x_perm, w
                                     lora)
 
 
+def _remap_variant(first_alt_only=False, lower_gate_first=False, gate_one=False, room_ignores_kept=False):
+    """dispatch_remap with one planted mistake (the rule restated with a flag)."""
+    def fn(idx, alt, gate, E, e_lo=0, e_hi=None, capacity=0):
+        idx, alt, g = np.asarray(idx), np.asarray(alt), np.asarray(gate, F64)
+        T, k = idx.shape
+        e_hi = E if e_hi is None else e_hi
+        kept1 = ORIG["dispatch"](idx, gate, E, 0, E, capacity)["slot"] >= 0
+        kept_e = np.bincount(idx[kept1], minlength=E)
+        target, prop = idx.copy(), np.zeros((T, k), bool)
+        for t in range(T):
+            m = 0
+            for j in range(k):
+                if not kept1[t, j]:
+                    target[t, j] = alt[t, 0 if first_alt_only else m]
+                    prop[t, j] = True
+                    m += 1
+        acc = np.zeros((T, k), bool)
+        for e in range(E):
+            ts, js = np.nonzero(prop & (target == e))
+            room = capacity if room_ignores_kept else max(capacity - int(kept_e[e]), 0)
+            order = np.lexsort((ts, g[ts, js] if lower_gate_first else -g[ts, js]))
+            for q in order[:room]:
+                acc[ts[q], js[q]] = True
+        expert = np.where(kept1 | acc, target, -1)
+        L = e_hi - e_lo
+        slot = np.full((T, k), -1, np.int64)
+        src, rg, off = [], [], np.zeros(L + 1, np.int64)
+        moved = dropped = 0
+        for le in range(L):
+            e = e_lo + le
+            off[le] = len(src)
+            for t, j in zip(*np.nonzero(expert == e)):
+                slot[t, j] = len(src)
+                src.append(t)
+                rg.append(1.0 if (gate_one and acc[t, j]) else g[t, j])
+            moved += int((acc & (target == e)).sum())
+            dropped += int((prop & ~acc & (target == e)).sum())
+        off[L] = len(src)
+        return {"counts": np.bincount(idx.ravel(), minlength=E), "offsets": off, "slot": slot,
+                "row_src": np.asarray(src, np.int64), "row_gate": np.asarray(rg, F64), "expert": expert,
+                "moved": moved, "dropped": dropped}
+    return fn
+
+
 ORIG = {n: getattr(mo, n) for n in ("topk_experts", "topk_gates", "silu", "expert_ffn",
                                      "dispatch", "lora_backward", "aux_loss", "silu_grad",
-                                     "logits_backward", "experts_backward")}
+                                     "logits_backward", "experts_backward", "dispatch_remap")}
 
 MUTANTS = {
     "ties_to_higher_id": ("topk_experts", _topk_ties_high),
@@ -103,7 +148,16 @@ MUTANTS = {
     "dlogits_not_centred": ("logits_backward", _dlogits_not_centred),
     "dlogits_aux_sign": ("logits_backward", _dlogits_aux_sign),
     "experts_backward_gate_up_swapped": ("experts_backward", _experts_bwd_gate_up_swapped),
+    "remap_every_overflow_to_first_alternate": ("dispatch_remap", _remap_variant(first_alt_only=True)),
+    "remap_prefers_lower_gates": ("dispatch_remap", _remap_variant(lower_gate_first=True)),
+    "remap_drops_the_gate": ("dispatch_remap", _remap_variant(gate_one=True)),
+    "remap_room_ignores_kept_rows": ("dispatch_remap", _remap_variant(room_ignores_kept=True)),
 }
+
+
+def _pin_remap_invariants():
+    for case in [(60, 12, 3, 14, 0), (200, 24, 4, 30, 1), (40, 16, 8, 18, 3)]:
+        tremap.test_remap_invariants_on_skewed_routing(*case)
 
 
 def _pin_dx_fd_plain():
@@ -131,6 +185,8 @@ PINS = [
     texp.test_lora_backward_matches_central_differences,
     tbwd.test_silu_grad_closed_form_and_differences, _pin_dx_fd_plain, _pin_dx_fd_lora_capacity,
     _pin_dlogits_fd, tbwd.test_dlogits_rows_sum_to_zero_and_k1_gate_path_vanishes,
+    tremap.test_hand_case_single_slot, tremap.test_hand_case_two_overflowing_slots_of_one_token,
+    _pin_remap_invariants, tremap.test_remap_with_tied_gates, tremap.test_no_overflow_equals_plain_dispatch,
 ]
 
 
