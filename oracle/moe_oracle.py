@@ -81,6 +81,16 @@ def router_logits(x, w_router, bias=None) -> np.ndarray:
     return l
 
 
+def latent_router_logits(x, w_latent, w_router, bias=None):
+    """Routing from a low-dimensional projection of the tokens ([DayLvl §2.1]:
+    tokens are first mapped to a more stable low-dimensional representation,
+    then routed). Reading: a linear map z = x W_c^T to d_c dimensions (no
+    bias, no normalisation), then l = z W_r^T (+ b) with W_r [E, d_c].
+    Returns (l, z)."""
+    z = _f64(x) @ _f64(w_latent).T
+    return router_logits(z, w_router, bias), z
+
+
 def topk_experts(logits, k: int) -> np.ndarray:
     """Indices of the k largest logits per row, descending, ties to the lower
     expert id ([DayLvl §2.1]: each token activates 16 of 896 experts).

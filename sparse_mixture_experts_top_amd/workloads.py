@@ -27,8 +27,13 @@ Distributions: x ~ N(0,1); router, gate and up weights ~ N(0, 1/d); down weights
 bf16 workloads are drawn in float32 and rounded to bfloat16 (round to nearest
 even); the tiny workload stays float32.
 
-Seeding: ``SeedSequence(seed).spawn(11)`` gives one child per tensor in the fixed
-order [x, w_router, w_gate, w_up, w_down, bias_perm, a_up, b_up, a_down, b_down, dy].
+Latent-space router variant (``latent_dc`` > 0): tokens are projected to d_c
+dimensions before routing; w_latent [d_c, d] ~ N(0, 1/d) and the router
+weight becomes [E, d_c] ~ N(0, 1/d_c).
+
+Seeding: ``SeedSequence(seed).spawn(12)`` gives one child per tensor in the fixed
+order [x, w_router, w_gate, w_up, w_down, bias_perm, a_up, b_up, a_down, b_down, dy,
+w_latent] (the first eleven are the children ``spawn(11)`` gives).
 Each child is split further into independent per-chunk streams (one per expert for
 expert tensors, one per 1024 rows for token tensors), so the result does not depend
 on how many threads draw it.
@@ -46,7 +51,7 @@ import numpy as np
 import torch
 
 _TENSOR_ORDER = ("x", "w_router", "w_gate", "w_up", "w_down", "bias_perm",
-                 "a_up", "b_up", "a_down", "b_down", "dy")
+                 "a_up", "b_up", "a_down", "b_down", "dy", "w_latent")
 _ROWS_PER_CHUNK = 1024
 
 
@@ -67,6 +72,7 @@ class Workload:
     lora_alpha: float = 0.0
     lora_b: str = "normal"  # "zero" or "normal"
     aux_coef: float = 0.0  # load-balance loss coefficient (0 = not requested)
+    latent_dc: int = 0     # latent routing width, 0 = the router reads x directly
 
     @property
     def local_hi(self) -> int:
@@ -91,6 +97,12 @@ WORKLOADS: Dict[str, Workload] = {
     "lora_step": Workload("lora_step", T=16384, d=4096, E=896, k=16, f=1024,
                           e_lo=0, e_hi=14, lora_r=16, lora_alpha=32.0,
                           lora_b="normal", aux_coef=0.01),
+    # the skewed workload with overflow remapped instead of dropped
+    "skewed_remap": Workload("skewed_remap", T=8192, d=2048, E=896, k=16, f=256,
+                             capacity=183, zipf_s=1.2),
+    # the full-router workload routed from a d/8-dimensional projection
+    "latent_router": Workload("latent_router", T=4096, d=2048, E=896, k=16, f=256,
+                              latent_dc=256),
 }
 
 
@@ -127,7 +139,8 @@ def generate(w: Workload, seed: int = 0, threads: Optional[int] = None,
              with_lora: bool = True, with_dy: bool = True) -> Dict[str, torch.Tensor]:
     """Draw every input of workload ``w`` as CPU tensors.
 
-    Keys: x [T,d], w_router [E,d], bias [E] (fp32, only when zipf_s > 0),
+    Keys: x [T,d], w_router [E,d] ([E,d_c] with latent routing, plus
+    w_latent [d_c,d]), bias [E] (fp32, only when zipf_s > 0),
     w_gate [L,f,d], w_up [L,f,d], w_down [L,d,f], for LoRA workloads
     a_up [L,r,d], b_up [L,f,r], a_down [L,r,f], b_down [L,d,r], and with
     with_dy the upstream gradient dy [T,d] of the backward.
@@ -140,8 +153,12 @@ def generate(w: Workload, seed: int = 0, threads: Optional[int] = None,
     out: Dict[str, torch.Tensor] = {}
     with ThreadPoolExecutor(max_workers=threads) as pool:
         out["x"] = _to_tensor(_normal(ss["x"], (T, d), 1.0, _ROWS_PER_CHUNK, pool), w.dtype)
+        dr = w.latent_dc if w.latent_dc > 0 else d  # the router's input width
         out["w_router"] = _to_tensor(
-            _normal(ss["w_router"], (E, d), 1.0 / math.sqrt(d), _ROWS_PER_CHUNK, pool), w.dtype)
+            _normal(ss["w_router"], (E, dr), 1.0 / math.sqrt(dr), _ROWS_PER_CHUNK, pool), w.dtype)
+        if w.latent_dc > 0:
+            out["w_latent"] = _to_tensor(
+                _normal(ss["w_latent"], (w.latent_dc, d), 1.0 / math.sqrt(d), _ROWS_PER_CHUNK, pool), w.dtype)
         out["w_gate"] = _to_tensor(_normal(ss["w_gate"], (L, f, d), 1.0 / math.sqrt(d), 1, pool), w.dtype)
         out["w_up"] = _to_tensor(_normal(ss["w_up"], (L, f, d), 1.0 / math.sqrt(d), 1, pool), w.dtype)
         out["w_down"] = _to_tensor(_normal(ss["w_down"], (L, d, f), 1.0 / math.sqrt(f), 1, pool), w.dtype)

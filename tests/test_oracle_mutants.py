@@ -130,9 +130,18 @@ def _remap_variant(first_alt_only=False, lower_gate_first=False, gate_one=False,
     return fn
 
 
+def _latent_projection_negated(x, w_latent, w_router, bias=None):
+    return ORIG["latent_router_logits"](-np.asarray(x, F64), w_latent, w_router, bias)
+
+
+def _latent_bias_dropped(x, w_latent, w_router, bias=None):
+    return ORIG["latent_router_logits"](x, w_latent, w_router, None)
+
+
 ORIG = {n: getattr(mo, n) for n in ("topk_experts", "topk_gates", "silu", "expert_ffn",
                                      "dispatch", "lora_backward", "aux_loss", "silu_grad",
-                                     "logits_backward", "experts_backward", "dispatch_remap")}
+                                     "logits_backward", "experts_backward", "dispatch_remap",
+                                     "latent_router_logits")}
 
 MUTANTS = {
     "ties_to_higher_id": ("topk_experts", _topk_ties_high),
@@ -152,6 +161,8 @@ MUTANTS = {
     "remap_prefers_lower_gates": ("dispatch_remap", _remap_variant(lower_gate_first=True)),
     "remap_drops_the_gate": ("dispatch_remap", _remap_variant(gate_one=True)),
     "remap_room_ignores_kept_rows": ("dispatch_remap", _remap_variant(room_ignores_kept=True)),
+    "latent_projection_negated": ("latent_router_logits", _latent_projection_negated),
+    "latent_bias_dropped": ("latent_router_logits", _latent_bias_dropped),
 }
 
 
@@ -187,6 +198,8 @@ PINS = [
     _pin_dlogits_fd, tbwd.test_dlogits_rows_sum_to_zero_and_k1_gate_path_vanishes,
     tremap.test_hand_case_single_slot, tremap.test_hand_case_two_overflowing_slots_of_one_token,
     _pin_remap_invariants, tremap.test_remap_with_tied_gates, tremap.test_no_overflow_equals_plain_dispatch,
+    trout.test_latent_router_hand_case, trout.test_latent_router_identity_projection_is_the_plain_router,
+    trout.test_latent_router_equals_merged_weight_and_python_loop,
 ]
 
 

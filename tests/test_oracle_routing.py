@@ -139,3 +139,36 @@ def test_capacity_rounding():
     # exact multiples are not rounded up further
     assert oracle.expert_capacity(1.0, 896, 16, 896) == 16
     assert oracle.expert_capacity(1.25, 64, 4, 16) == 20
+
+
+# ------------------------------------------------------ latent-space router --
+
+def test_latent_router_hand_case():
+    # x = [1, 2], W_c = [[1, -1]] -> z = [-1]; W_r = [[2], [-3]], b = [0.5, 0]
+    l, z = oracle.latent_router_logits(np.array([[1.0, 2.0]]), np.array([[1.0, -1.0]]),
+                                       np.array([[2.0], [-3.0]]), np.array([0.5, 0.0]))
+    assert z.tolist() == [[-1.0]]
+    assert l.tolist() == [[-1.5, 3.0]]
+
+
+def test_latent_router_identity_projection_is_the_plain_router():
+    rng = np.random.default_rng(11)
+    x, wr, b = rng.standard_normal((9, 12)), rng.standard_normal((7, 12)), rng.standard_normal(7)
+    l, z = oracle.latent_router_logits(x, np.eye(12), wr, b)
+    assert np.array_equal(z, x)
+    assert np.allclose(l, oracle.router_logits(x, wr, b), rtol=0, atol=1e-13)
+
+
+def test_latent_router_equals_merged_weight_and_python_loop():
+    # non-square shapes (T=5, d=6, d_c=3, E=4) so a transposed operand fails
+    rng = np.random.default_rng(12)
+    x, wc, wr = rng.standard_normal((5, 6)), rng.standard_normal((3, 6)), rng.standard_normal((4, 3))
+    l, z = oracle.latent_router_logits(x, wc, wr)
+    assert np.allclose(l, x @ (wr @ wc).T, rtol=0, atol=1e-12)
+    for t in range(5):
+        for e in range(4):
+            ref = 0.0
+            for c in range(3):
+                zc = sum(x[t, i] * wc[c, i] for i in range(6))
+                ref += zc * wr[e, c]
+            assert abs(l[t, e] - ref) <= 1e-12
