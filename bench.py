@@ -11,8 +11,9 @@ step) from HIP events recorded around it on its launch stream, and the CPU
 oracle timed on a bounded token sample of the same workload. With the
 default workload the line also carries "workloads": the one-rank share at
 EP = 64 (16384 tokens, 14 local experts, f = 1024), the skewed routing with
-capacity and the LoRA fine-tuning step, each with ms per step, tokens/s and
-every stage against its roofline (fewer steps, no CPU baseline).
+capacity (overflow dropped, and remapped to the next-ranked experts), the
+LoRA fine-tuning step and the latent-space router, each with ms per step,
+tokens/s and every stage against its roofline (fewer steps, no CPU baseline).
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                   [--no-cpu-baseline] [--no-backward] [--no-extra-workloads]
@@ -170,7 +171,7 @@ def main() -> int:
         # the other single-GPU workloads, fewer steps, each with its dominant
         # kernel against its roofline (no backward pass, no CPU baseline)
         out["workloads"] = {}
-        for name in ("ep64_rank", "skewed_capacity", "lora_step"):
+        for name in ("ep64_rank", "skewed_capacity", "lora_step", "skewed_remap", "latent_router"):
             torch.cuda.empty_cache()
             res = run_workload(args, WORKLOADS[name], min(args.steps, 10), min(args.warmup, 3),
                                backward=False, cpu=False, graph=False)
@@ -226,11 +227,12 @@ def run_workload(args, w, steps, warmup, backward, cpu, graph):
     buf = layer.alloc(shape)
     # the frozen expert weights live in their packed layout (one-time, outside the step)
     packed = layer.pack_weights(shape, dev["w_gate"], dev["w_up"], dev["w_down"])
+    variant = layer.variant_buffers(w, dev)
     torch.cuda.synchronize()
     args_fw = (dev["x"], dev["w_router"], dev.get("bias"), None, None, None)
 
     for _ in range(warmup):
-        layer.forward(buf, *args_fw, packed=packed)
+        layer.forward(buf, *args_fw, packed=packed, variant=variant)
     torch.cuda.synchronize()
 
     # timed region: K steps. The library brackets only the gate/up kernel with
@@ -240,7 +242,8 @@ def run_workload(args, w, steps, warmup, backward, cpu, graph):
     # breakdown pass below instead).
     g = None
     if graph:
-        g = layer.capture(lambda: [layer.forward(buf, *args_fw, packed=packed) for _ in range(steps)])
+        g = layer.capture(lambda: [layer.forward(buf, *args_fw, packed=packed, variant=variant)
+                                   for _ in range(steps)])
         g.replay()
         torch.cuda.synchronize()
     else:
@@ -253,7 +256,7 @@ def run_workload(args, w, steps, warmup, backward, cpu, graph):
         g.replay()
     else:
         for _ in range(steps):
-            layer.forward(buf, *args_fw, packed=packed)
+            layer.forward(buf, *args_fw, packed=packed, variant=variant)
     stop.record(stream)
     torch.cuda.synchronize()
     elapsed_ms = start.elapsed_time(stop)
@@ -262,14 +265,17 @@ def run_workload(args, w, steps, warmup, backward, cpu, graph):
     # per-kernel breakdown from extra steps outside the timed region (every
     # kernel bracketed by events)
     B.moe_timing_enable(True)
-    for _ in range(max(1, min(steps, 10))):
-        layer.forward(buf, *args_fw, packed=packed)
+    nb = max(1, min(steps, 10))
+    for _ in range(nb):
+        layer.forward(buf, *args_fw, packed=packed, variant=variant)
     torch.cuda.synchronize()
     kernels = {}
     for name in B.KERNELS:
         ms, n = B.moe_timing_read(name)
         if n:
-            kernels[name] = {"avg_us": 1000.0 * ms / n, "launches": n}
+            # per launch, and per step (a kind can run more than once a step:
+            # the two dispatch passes of remapping, the latent router's GEMMs)
+            kernels[name] = {"avg_us": 1000.0 * ms / n, "launches": n, "step_us": 1000.0 * ms / nb}
     B.moe_timing_enable(False)
 
     ms_step = elapsed_ms / steps
@@ -292,11 +298,12 @@ def run_workload(args, w, steps, warmup, backward, cpu, graph):
             "mfma_tflops": round(gu_flops / (gu_us * 1e-6) / 1e12, 1),
             "mfma_frac": round(gu_flops / (gu_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
     # layer-level figures for context
-    flops = 2 * w.T * w.d * w.E + 6 * R * w.d * w.f
+    router_flops = (2.0 * w.T * w.latent_dc * (w.d + w.E)) if w.latent_dc else 2.0 * w.T * w.d * w.E
+    flops = router_flops + 6 * R * w.d * w.f
     # every stage against its own roofline, from the breakdown pass (durations
-    # there include the event pair around each launch)
+    # there include the event pair around each launch), per step
     stage_work = {
-        "router_gemm": ("mfma", 2.0 * w.T * w.d * w.E),
+        "router_gemm": ("mfma", router_flops),
         "topk": ("hbm", w.T * w.E * 4 + w.T * w.k * 8),
         "dispatch": ("hbm", 3 * w.T * w.k * 4 + w.T * w.k * 4 + R * 8),
         "combine": ("hbm", R * w.d * 2 + w.T * w.k * 8 + w.T * w.d * 2),
@@ -305,7 +312,7 @@ def run_workload(args, w, steps, warmup, backward, cpu, graph):
         "gate_up": (gu_flops, gu_bytes),
         "down": (2.0 * R * w.d * w.f, active * w.d * w.f * 2 + R * w.f * 2 + R * w.d * 2),
     }
-    stage_us = {k: v["avg_us"] for k, v in kernels.items()}
+    stage_us = {k: v["step_us"] for k, v in kernels.items()}
     stage_us["dispatch"] = sum(stage_us.get(n, 0.0) for n in ("hist", "scan", "scatter", "capacity"))
     stages = {}
     for name, (bound, work) in stage_work.items():
@@ -335,9 +342,14 @@ def run_workload(args, w, steps, warmup, backward, cpu, graph):
         "roofline": roof,
         "dominant_kernel": {"name": dominant, **stages[dominant]} if dominant else None,
         "layer_tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
-        "kernels_us": {k: round(v["avg_us"], 2) for k, v in kernels.items()},
+        "kernels_us": {k: round(v["step_us"], 2) for k, v in kernels.items()},
         "stage_roofline": stages,
     }
+    if w.remap:
+        out["config"]["moved"] = int(variant.moved.item())
+        out["config"]["dropped"] = int(buf.dropped.item())
+    if w.latent_dc:
+        out["config"]["latent_dc"] = w.latent_dc
     if backward:
         out["backward"] = backward_pass(w, dev, shape, packed, R, active)
     if cpu:

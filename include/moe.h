@@ -137,6 +137,34 @@ moe_status_t moe_route(const moe_shape_t* shape, const void* x, const void* w_ro
                        float* logits, float* prob_sum, void* ws, size_t ws_bytes,
                        moe_stream_t stream);
 
+/* moe_route plus the experts ranked next: alt_idx [T, k] int32 OUT holds,
+ * for each token, the experts of rank k .. 2k-1 by logit (the same order and
+ * tie rule as topk_idx), the candidates moe_dispatch_remap moves
+ * overflowing assignments to. topk_idx, topk_gate, logits and prob_sum are
+ * those of moe_route. Needs 2k <= E and 2k <= 32 (MOE_ERR_UNSUPPORTED).
+ * ("Adapting Ultra-Large MoE Models: Engineering Practices and Optimization
+ * Pathways", §3.3: excess tokens are remapped or dropped.) */
+moe_status_t moe_route_alt(const moe_shape_t* shape, const void* x, const void* w_router,
+                           const float* bias, int32_t* topk_idx, float* topk_gate, int32_t* alt_idx,
+                           float* logits, float* prob_sum, void* ws, size_t ws_bytes,
+                           moe_stream_t stream);
+
+/* Routing from a low-dimensional projection of the tokens ("Day-Level
+ * Adaptation and LoRA Fine-Tuning of Ultra-Large-Scale Sparse MoE Models",
+ * §2.1: tokens are first mapped to a more stable low-dimensional
+ * representation, then routed):
+ *   z = x w_latent^T            z [T, d_c] bf16 OUT (fp32 accumulation,
+ *                               rounded to bf16: it feeds the next product)
+ *   logits = z w_router^T + bias, then top-k and gates as moe_route.
+ *   d_c         latent width, a positive multiple of 64
+ *   w_latent    [d_c, d]        w_router [E, d_c]
+ * bf16 only (MOE_ERR_UNSUPPORTED otherwise). The other arguments are those
+ * of moe_route. */
+moe_status_t moe_route_latent(const moe_shape_t* shape, int32_t d_c, const void* x, const void* w_latent,
+                              const void* w_router, const float* bias, void* z, int32_t* topk_idx,
+                              float* topk_gate, float* logits, float* prob_sum, void* ws, size_t ws_bytes,
+                              moe_stream_t stream);
+
 /* Dispatch ("Trillion-Parameter ... Full-Stack Optimization Practices", §3
  * and §4.3: permute tokens by routing result).
  *   topk_idx, topk_gate       from moe_route
@@ -162,6 +190,34 @@ moe_status_t moe_dispatch(const moe_shape_t* shape, const int32_t* topk_idx,
                           void* x_perm, int32_t* dropped, void* ws, size_t ws_bytes,
                           moe_stream_t stream);
 
+/* Dispatch with token remapping instead of dropping ("Adapting Ultra-Large
+ * MoE Models: Engineering Practices and Optimization Pathways", §3.3: excess
+ * tokens are remapped or dropped). With C = capacity (> 0, else
+ * MOE_ERR_INVALID_ARG):
+ *   1. every expert (all E, not only the local ones) keeps its C assignments
+ *      with the largest gate, equal gates going to the lower token, as in
+ *      moe_dispatch; the others overflow;
+ *   2. the m-th overflowing assignment of a token (in j order) is proposed to
+ *      alt_idx[t, m] (moe_route_alt), the expert ranked k + m;
+ *   3. an expert accepts proposals into the room its kept assignments left,
+ *      C - kept, preferring the larger gate, then the lower token; the other
+ *      proposals are dropped.
+ * An accepted assignment keeps its gate: slot[t, j] then names a row of the
+ * alternate expert, and moe_combine / moe_expert_gemm work unchanged. Rows
+ * are grouped by local expert and token as in moe_dispatch; a token has at
+ * most one row per expert.
+ *   counts   [E]        OUT: assignments per expert before capacity (the
+ *                       original selection), as in moe_dispatch
+ *   moved    [1] | NULL OUT: proposals accepted by local experts
+ *   dropped  [1] | NULL OUT: proposals to local experts that were rejected
+ * The other arguments are those of moe_dispatch; the workspace of
+ * moe_workspace_bytes for a shape with capacity > 0 includes the scratch of
+ * the all-expert pass. Needs 2k <= E. */
+moe_status_t moe_dispatch_remap(const moe_shape_t* shape, const int32_t* topk_idx, const float* topk_gate,
+                                const int32_t* alt_idx, const void* x, int32_t* counts, int32_t* offsets,
+                                int32_t* slot, int32_t* row_src, float* row_gate, void* x_perm, int32_t* moved,
+                                int32_t* dropped, void* ws, size_t ws_bytes, moe_stream_t stream);
+
 /* moe_dispatch without a workspace argument, for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc. Same arguments (minus ws, ws_bytes) and
@@ -170,7 +226,7 @@ moe_status_t moe_dispatch(const moe_shape_t* shape, const int32_t* topk_idx,
  * their scan; with a capacity, the candidate gate keys) is a device array of
  * MOE_DISPATCH_NOALLOC_SCRATCH_BYTES bytes that the library owns, one copy on
  * each device it runs on, held until the process ends. A shape needs
- *   2 * a(ceil(T / 32) * E * 4) + a((L + 1) * 4)
+ *   2 * a(ceil(T / 32) * E * 4) + a((E + 1) * 4)
  *     + (capacity > 0 ? 2 * a(T * k * 4) : 0)   bytes, a(n) = n rounded up
  * to a multiple of 256; more returns MOE_ERR_WORKSPACE (T = 16384, E = 896:
  * about 3.7 MB). Every word of the scratch is written before it is read, so

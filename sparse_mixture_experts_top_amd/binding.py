@@ -25,7 +25,8 @@ KERNELS = ["router_gemm", "topk", "prob_reduce", "hist", "scan", "scatter", "cap
            "gather", "tiles", "gate_up", "down", "combine", "aux", "lora_proj", "lora_dh",
            "lora_grad", "gate_bwd", "expert_dgu", "expert_dx", "unpermute", "router_bwd"]
 
-EXPORTED = ["moe_workspace_bytes", "moe_max_rows", "moe_last_error", "moe_route",
+EXPORTED = ["moe_workspace_bytes", "moe_max_rows", "moe_last_error", "moe_route", "moe_route_alt",
+            "moe_route_latent", "moe_dispatch_remap",
             "moe_dispatch", "moe_dispatch_noalloc", "moe_expert_gemm", "moe_pack_expert_weights", "moe_expert_gemm_packed",
             "moe_combine", "moe_aux_loss", "moe_lora_bwd", "moe_lora_bwd_packed", "moe_gate_bwd", "moe_expert_bwd",
             "moe_router_bwd", "moe_pack_backward_weights", "moe_expert_bwd_packed", "moe_pack_router_bwd",
@@ -69,6 +70,9 @@ def lib() -> ctypes.CDLL:
     L.moe_route.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_dispatch.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_dispatch_noalloc.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.moe_route_alt.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_route_latent.argtypes = [shp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.moe_dispatch_remap.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_expert_gemm.argtypes = [shp, vp, vp, vp, vp, vp, vp, lor, vp, vp, vp, sz, vp]
     L.moe_pack_expert_weights.argtypes = [shp, vp, vp, vp, vp, vp, vp]
     L.moe_expert_gemm_packed.argtypes = [shp, vp, vp, vp, vp, vp, lor, vp, vp, vp, sz, vp]
@@ -156,6 +160,37 @@ def moe_dispatch(shape, topk_idx, topk_gate, x, counts, offsets, slot, row_src, 
                               _dev(x, dt), _dev(counts, i32), _dev(offsets, i32), _dev(slot, i32),
                               _dev(row_src, i32), _dev(row_gate, torch.float32), _dev(x_perm, dt),
                               _dev(dropped, i32), _dev(ws, torch.uint8), ws.numel(), _stream(stream)))
+
+
+def moe_route_alt(shape, x, w_router, bias, topk_idx, topk_gate, alt_idx, logits, prob_sum, ws, stream=None):
+    """moe_route plus alt_idx [T, k]: the experts ranked k .. 2k-1."""
+    dt = _fdt(shape)
+    _check(lib().moe_route_alt(ctypes.byref(shape), _dev(x, dt), _dev(w_router, dt), _dev(bias, torch.float32),
+                               _dev(topk_idx, torch.int32), _dev(topk_gate, torch.float32),
+                               _dev(alt_idx, torch.int32), _dev(logits, torch.float32),
+                               _dev(prob_sum, torch.float32), _dev(ws, torch.uint8), ws.numel(), _stream(stream)))
+
+
+def moe_route_latent(shape, d_c, x, w_latent, w_router, bias, z, topk_idx, topk_gate, logits, prob_sum, ws,
+                     stream=None):
+    """Routing from z = x w_latent^T ([T, d_c], written to z)."""
+    dt = _fdt(shape)
+    _check(lib().moe_route_latent(ctypes.byref(shape), int(d_c), _dev(x, dt), _dev(w_latent, dt),
+                                  _dev(w_router, dt), _dev(bias, torch.float32), _dev(z, dt),
+                                  _dev(topk_idx, torch.int32), _dev(topk_gate, torch.float32),
+                                  _dev(logits, torch.float32), _dev(prob_sum, torch.float32),
+                                  _dev(ws, torch.uint8), ws.numel(), _stream(stream)))
+
+
+def moe_dispatch_remap(shape, topk_idx, topk_gate, alt_idx, x, counts, offsets, slot, row_src, row_gate,
+                       x_perm, moved, dropped, ws, stream=None):
+    """Dispatch with overflowing assignments moved to the alternates."""
+    dt, i32 = _fdt(shape), torch.int32
+    _check(lib().moe_dispatch_remap(ctypes.byref(shape), _dev(topk_idx, i32), _dev(topk_gate, torch.float32),
+                                    _dev(alt_idx, i32), _dev(x, dt), _dev(counts, i32), _dev(offsets, i32),
+                                    _dev(slot, i32), _dev(row_src, i32), _dev(row_gate, torch.float32),
+                                    _dev(x_perm, dt), _dev(moved, i32), _dev(dropped, i32),
+                                    _dev(ws, torch.uint8), ws.numel(), _stream(stream)))
 
 
 def moe_dispatch_noalloc(shape, topk_idx, topk_gate, x, counts, offsets, slot, row_src, row_gate, x_perm,

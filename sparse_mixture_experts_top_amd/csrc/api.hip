@@ -44,7 +44,8 @@ Workspace carve_workspace(const moe_shape_t& s, int lora_r, void* base, bool dis
   const int64_t elt = s.dtype == MOE_BF16 ? 2 : 4;
   w.tile_counts = static_cast<int32_t*>(take(ntok_tiles * s.E * 4));
   w.tile_base = static_cast<int32_t*>(take(ntok_tiles * s.E * 4));
-  w.cseg = static_cast<int32_t*>(take((L + 1) * 4));
+  // E + 1 (not L + 1): the all-expert pass of token remapping uses it too
+  w.cseg = static_cast<int32_t*>(take(((int64_t)s.E + 1) * 4));
   if (s.capacity > 0) {
     w.cand_key = static_cast<uint32_t*>(take((int64_t)s.T * s.k * 4));
     w.cand_idx = static_cast<int32_t*>(take((int64_t)s.T * s.k * 4));
@@ -52,6 +53,17 @@ Workspace carve_workspace(const moe_shape_t& s, int lora_r, void* base, bool dis
   // everything dispatch uses lies before this point
   w.dispatch_bytes = off;
   if (dispatch_only) return w;
+  if (s.capacity > 0) {
+    const int64_t tk = (int64_t)s.T * s.k;
+    const int64_t r1 = std::min<int64_t>(tk, (int64_t)s.E * s.capacity);
+    w.rm_offsets1 = static_cast<int32_t*>(take(((int64_t)s.E + 1) * 4));
+    w.rm_slot1 = static_cast<int32_t*>(take(tk * 4));
+    w.rm_src1 = static_cast<int32_t*>(take(r1 * 4));
+    w.rm_gate1 = static_cast<float*>(take(r1 * 4));
+    w.rm_idx2 = static_cast<int32_t*>(take(tk * 4));
+    w.rm_key2 = static_cast<float*>(take(tk * 4));
+    w.rm_counts2 = static_cast<int32_t*>(take((int64_t)s.E * 4));
+  }
   w.gemm_tiles = static_cast<int32_t*>(take((2 * (int64_t)gemm_max_tiles(s) + 1) * 4));
   w.hbuf = take(rmax * s.f * elt);
   if (lora_r > 0) {
@@ -275,6 +287,91 @@ moe_status_t moe_route(const moe_shape_t* shape, const void* x, const void* w_ro
     if ((st = hip_status(launch_router(c, s, x, w_router, bias, lg), "router GEMM")) != MOE_OK) return st;
   }
   return hip_status(launch_topk(c, s, lg, topk_idx, topk_gate, w.prob_part, prob_sum), "top-k");
+}
+
+moe_status_t moe_route_alt(const moe_shape_t* shape, const void* x, const void* w_router, const float* bias,
+                           int32_t* topk_idx, float* topk_gate, int32_t* alt_idx, float* logits, float* prob_sum,
+                           void* ws, size_t ws_bytes, moe_stream_t stream) {
+  moe_status_t st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape_t& s = *shape;
+  if (2 * s.k > s.E || 2 * s.k > 32)
+    return fail(MOE_ERR_UNSUPPORTED, "alternates need 2k <= E and 2k <= 32");
+  MOE_REQUIRE_IF(s.T > 0, x, "x");
+  MOE_REQUIRE(w_router, "w_router");
+  MOE_REQUIRE_IF(s.T > 0, topk_idx, "topk_idx");
+  MOE_REQUIRE_IF(s.T > 0, topk_gate, "topk_gate");
+  MOE_REQUIRE_IF(s.T > 0, alt_idx, "alt_idx");
+  if ((st = check_ws(s, 0, ws, ws_bytes)) != MOE_OK) return st;
+  Ctx c;
+  if ((st = make_ctx(stream, &c)) != MOE_OK) return st;
+  const Workspace w = carve_workspace(s, 0, ws);
+  float* lg = logits ? logits : w.logits;
+  if (s.T > 0) {
+    if ((st = hip_status(launch_router(c, s, x, w_router, bias, lg), "router GEMM")) != MOE_OK) return st;
+  }
+  return hip_status(launch_topk(c, s, lg, topk_idx, topk_gate, w.prob_part, prob_sum, alt_idx), "top-k");
+}
+
+moe_status_t moe_route_latent(const moe_shape_t* shape, int32_t d_c, const void* x, const void* w_latent,
+                              const void* w_router, const float* bias, void* z, int32_t* topk_idx,
+                              float* topk_gate, float* logits, float* prob_sum, void* ws, size_t ws_bytes,
+                              moe_stream_t stream) {
+  moe_status_t st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape_t& s = *shape;
+  if (s.dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the latent router needs dtype MOE_BF16");
+  if (d_c < 64 || d_c % 64 != 0) return fail(MOE_ERR_UNSUPPORTED, "the latent width d_c must be a positive multiple of 64");
+  MOE_REQUIRE_IF(s.T > 0, x, "x");
+  MOE_REQUIRE(w_latent, "w_latent");
+  MOE_REQUIRE(w_router, "w_router");
+  MOE_REQUIRE_IF(s.T > 0, z, "z");
+  MOE_REQUIRE_IF(s.T > 0, topk_idx, "topk_idx");
+  MOE_REQUIRE_IF(s.T > 0, topk_gate, "topk_gate");
+  if ((st = check_ws(s, 0, ws, ws_bytes)) != MOE_OK) return st;
+  Ctx c;
+  if ((st = make_ctx(stream, &c)) != MOE_OK) return st;
+  const Workspace w = carve_workspace(s, 0, ws);
+  float* lg = logits ? logits : w.logits;
+  if (s.T > 0) {
+    bf16_t* zb = static_cast<bf16_t*>(z);
+    if ((st = hip_status(launch_router_mnk(c, s.T, d_c, s.d, (const bf16_t*)x, (const bf16_t*)w_latent, nullptr,
+                                           nullptr, zb),
+                         "latent projection")) != MOE_OK)
+      return st;
+    if ((st = hip_status(launch_router_mnk(c, s.T, s.E, d_c, zb, (const bf16_t*)w_router, bias, lg, nullptr),
+                         "router GEMM")) != MOE_OK)
+      return st;
+  }
+  return hip_status(launch_topk(c, s, lg, topk_idx, topk_gate, w.prob_part, prob_sum), "top-k");
+}
+
+moe_status_t moe_dispatch_remap(const moe_shape_t* shape, const int32_t* topk_idx, const float* topk_gate,
+                                const int32_t* alt_idx, const void* x, int32_t* counts, int32_t* offsets,
+                                int32_t* slot, int32_t* row_src, float* row_gate, void* x_perm, int32_t* moved,
+                                int32_t* dropped, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  moe_status_t st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape_t& s = *shape;
+  if (s.capacity <= 0) return fail(MOE_ERR_INVALID_ARG, "token remapping needs a capacity > 0");
+  if (2 * s.k > s.E) return fail(MOE_ERR_UNSUPPORTED, "alternates need 2k <= E");
+  const bool rows = max_rows(s) > 0;
+  MOE_REQUIRE_IF(s.T > 0, topk_idx, "topk_idx");
+  MOE_REQUIRE_IF(s.T > 0, topk_gate, "topk_gate");
+  MOE_REQUIRE_IF(s.T > 0, alt_idx, "alt_idx");
+  MOE_REQUIRE_IF(s.T > 0 && x_perm, x, "x");
+  MOE_REQUIRE(counts, "counts");
+  MOE_REQUIRE(offsets, "offsets");
+  MOE_REQUIRE_IF(s.T > 0, slot, "slot");
+  MOE_REQUIRE_IF(rows, row_src, "row_src");
+  MOE_REQUIRE_IF(rows, row_gate, "row_gate");
+  if ((st = check_ws(s, 0, ws, ws_bytes)) != MOE_OK) return st;
+  Ctx c;
+  if ((st = make_ctx(stream, &c)) != MOE_OK) return st;
+  const Workspace w = carve_workspace(s, 0, ws);
+  return hip_status(launch_dispatch_remap(c, s, w, topk_idx, topk_gate, alt_idx, x, counts, offsets, slot, row_src,
+                                          row_gate, x_perm, moved, dropped),
+                    "dispatch with remapping");
 }
 
 moe_status_t moe_dispatch(const moe_shape_t* shape, const int32_t* topk_idx,

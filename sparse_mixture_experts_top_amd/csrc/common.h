@@ -176,6 +176,14 @@ struct Workspace {
   bf16_t* zx;            // [Rmax, 2r] s Z as bf16 high | low parts (the extra adapter K step)
   float* logits;         // [T, E]
   float* prob_part;      // [prob_blocks, E]
+  // token remapping (capacity > 0): the all-expert pass and the proposals
+  int32_t* rm_offsets1;  // [E+1]
+  int32_t* rm_slot1;     // [T*k]
+  int32_t* rm_src1;      // [min(T*k, E*C)]
+  float* rm_gate1;       // [min(T*k, E*C)]
+  int32_t* rm_idx2;      // [T*k]
+  float* rm_key2;        // [T*k]
+  int32_t* rm_counts2;   // [E]
   int64_t dispatch_bytes;  // the leading part dispatch uses (tile_counts .. cand_idx)
   int64_t bytes;           // all of it (0 when carved with dispatch_only)
 };
@@ -195,11 +203,17 @@ int gemm_max_tiles(const moe_shape_t& s);
 
 hipError_t launch_router(const Ctx& c, const moe_shape_t& s, const void* x, const void* w,
                          const float* bias, float* logits);
+hipError_t launch_router_mnk(const Ctx& c, int M, int N, int K, const bf16_t* x, const bf16_t* w,
+                             const float* bias, float* logits, bf16_t* out_b);
 hipError_t launch_topk(const Ctx& c, const moe_shape_t& s, const float* logits, int32_t* idx,
-                       float* gate, float* prob_part, float* prob_sum);
+                       float* gate, float* prob_part, float* prob_sum, int32_t* alt = nullptr);
 hipError_t launch_aux(const Ctx& c, const moe_shape_t& s, const int32_t* counts,
                       const float* prob_sum, float coef, float* out);
 
+hipError_t launch_dispatch_remap(const Ctx& c, const moe_shape_t& s, const Workspace& ws, const int32_t* idx,
+                                 const float* gate, const int32_t* alt, const void* x, int32_t* counts,
+                                 int32_t* offsets, int32_t* slot, int32_t* row_src, float* row_gate, void* x_perm,
+                                 int32_t* moved, int32_t* dropped);
 hipError_t launch_dispatch(const Ctx& c, const moe_shape_t& s, const Workspace& ws,
                            const int32_t* idx, const float* gate, const void* x, int32_t* counts,
                            int32_t* offsets, int32_t* slot, int32_t* row_src, float* row_gate,

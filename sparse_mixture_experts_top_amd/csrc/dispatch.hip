@@ -509,6 +509,67 @@ __global__ __launch_bounds__(kCapThreads) void dispatch_capacity(
   }
 }
 
+// ------------------------------------------------------ token remapping ---
+// Overflowing assignments go to the token's next-ranked experts instead of
+// being dropped ("Adapting Ultra-Large MoE Models: Engineering Practices and
+// Optimization Pathways", §3.3: excess tokens are remapped or dropped). Four
+// steps on the stream:
+//   1. the capacity dispatch over all E experts (which slots overflow);
+//   2. remap_prep: per token, the m-th overflowing slot (j order) proposes to
+//      alt[t, m], the expert ranked k + m, keyed by its gate; a kept slot
+//      stays with its expert and a key above every gate (+inf);
+//   3. the capacity dispatch of those (expert, key) pairs over the local
+//      experts: an expert keeps all its kept slots (at most C, all +inf) and
+//      fills the room left with the best proposals (key desc, token asc),
+//      rows in token order;
+//   4. remap_fixup: the rows' gates (step 3 stored the keys) and the number
+//      of accepted proposals.
+// A token's served experts stay distinct: alternates lie outside its
+// selection and are distinct among themselves.
+
+// One wave per token (4 per workgroup), lanes j < k. Workgroup 0 also zeroes
+// `moved`, which remap_fixup counts into afterwards on the same stream.
+__global__ __launch_bounds__(256) void remap_prep(const int32_t* __restrict__ idx,
+                                                  const int32_t* __restrict__ alt,
+                                                  const float* __restrict__ gate,
+                                                  const int32_t* __restrict__ slot1, int T, int k,
+                                                  int32_t* __restrict__ idx2, float* __restrict__ key2,
+                                                  int32_t* __restrict__ moved) {
+  if (blockIdx.x == 0 && threadIdx.x == 0 && moved) *moved = 0;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  if (t >= T) return;
+  const bool in = lane < k;
+  const int64_t a = (int64_t)t * k + lane;
+  const bool kept = in && slot1[a] >= 0;
+  const uint64_t over = __ballot(in && !kept);
+  const int m = __popcll(over & ((1ull << lane) - 1ull));  // earlier overflowing slots
+  if (in) {
+    idx2[a] = kept ? idx[a] : alt[(int64_t)t * k + m];
+    key2[a] = kept ? __uint_as_float(0x7f800000u) : gate[a];
+  }
+}
+
+// row_gate[slot[a]] = gate[a] for every served assignment; *moved += the
+// served assignments that were proposals (key below +inf). Integer adds, so
+// the count does not depend on the order.
+__global__ __launch_bounds__(256) void remap_fixup(const float* __restrict__ gate,
+                                                   const float* __restrict__ key2,
+                                                   const int32_t* __restrict__ slot, int64_t n,
+                                                   float* __restrict__ row_gate, int32_t* __restrict__ moved) {
+  int cnt = 0;
+  for (int64_t a = (int64_t)blockIdx.x * 256 + threadIdx.x; a < n; a += (int64_t)gridDim.x * 256) {
+    const int r = slot[a];
+    if (r >= 0) {
+      row_gate[r] = gate[a];
+      cnt += __float_as_uint(key2[a]) != 0x7f800000u ? 1 : 0;
+    }
+  }
+  if (!moved) return;
+  for (int o = 32; o >= 1; o >>= 1) cnt += __shfl_xor(cnt, o, kWave);
+  if ((threadIdx.x & 63) == 0 && cnt) atomicAdd(moved, cnt);
+}
+
 // x_perm[p, :] = x[row_src[p], :] for p < R = offsets[L]; one row per
 // block iteration, 16-byte vectors.
 __global__ __launch_bounds__(256) void dispatch_gather(const uint4* __restrict__ x,
@@ -583,6 +644,35 @@ hipError_t launch_dispatch(const Ctx& c, const moe_shape_t& s, const Workspace& 
     hipLaunchKernelGGL(dispatch_gather_f32, dim3(grid), dim3(256), 0, c.stream, (const float*)x,
                        row_src, offsets, L, s.d, (float*)x_perm);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch_remap(const Ctx& c, const moe_shape_t& s, const Workspace& ws, const int32_t* idx,
+                                 const float* gate, const int32_t* alt, const void* x, int32_t* counts,
+                                 int32_t* offsets, int32_t* slot, int32_t* row_src, float* row_gate, void* x_perm,
+                                 int32_t* moved, int32_t* dropped) {
+  hipError_t err;
+  // 1. which slots overflow: the capacity rule over every expert
+  moe_shape_t all = s;
+  all.e_lo = 0;
+  all.e_hi = s.E;
+  if ((err = launch_dispatch(c, all, ws, idx, gate, nullptr, counts, ws.rm_offsets1, ws.rm_slot1, ws.rm_src1,
+                             ws.rm_gate1, nullptr, nullptr)) != hipSuccess)
+    return err;
+  // 2. proposals
+  const int blocks = s.T > 0 ? (s.T + 3) / 4 : 1;
+  hipLaunchKernelGGL(remap_prep, dim3(blocks), dim3(256), 0, c.stream, idx, alt, gate, ws.rm_slot1, s.T, s.k,
+                     ws.rm_idx2, ws.rm_key2, moved);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  // 3. kept slots plus the best proposals, on the local experts
+  if ((err = launch_dispatch(c, s, ws, ws.rm_idx2, ws.rm_key2, x, ws.rm_counts2, offsets, slot, row_src, row_gate,
+                             x_perm, dropped)) != hipSuccess)
+    return err;
+  // 4. gates of the rows, accepted proposals
+  const int64_t n = (int64_t)s.T * s.k;
+  if (n == 0) return hipSuccess;
+  const int grid = (int)std::min<int64_t>((n + 255) / 256, (int64_t)c.num_cus * 8);
+  hipLaunchKernelGGL(remap_fixup, dim3(grid), dim3(256), 0, c.stream, gate, ws.rm_key2, slot, n, row_gate, moved);
   return hipGetLastError();
 }
 

@@ -15,6 +15,9 @@ namespace moe {
 
 // bf16: logits[T, E] (f32) = x[T, d] * w[E, d]^T + bias, one 128 x 128 (or
 // 64 x 128) tile per item on the persistent pipelined driver.
+// The same engine computes the latent router's projection z = x W_c^T
+// (T, d, E read as rows, K, output columns): out_b set stores the product
+// rounded to bf16, without a bias.
 template <class Cfg>
 struct RouterProb {
   const bf16_t* x;
@@ -22,6 +25,7 @@ struct RouterProb {
   const float* bias;
   float* logits;
   int T, d, E, nt;
+  bf16_t* out_b = nullptr;
 
   __device__ __forceinline__ int rows(int item) const { return min(Cfg::BM, T - (item / nt) * Cfg::BM); }
 
@@ -40,6 +44,21 @@ struct RouterProb {
     const int m0 = (item / nt) * Cfg::BM, n0 = (item % nt) * Cfg::BN;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
+    if (out_b) {  // E % 4 == 0 here: a lane's four columns are all valid or all not
+#pragma unroll
+      for (int j = 0; j < Cfg::FN; ++j) {
+        const int n = n0 + dma_out_col<Cfg>(wn, j, lane);
+        if (n >= E) continue;
+#pragma unroll
+        for (int i = 0; i < Cfg::FM; ++i) {
+          const int m = m0 + dma_out_row<Cfg>(wm, i, lane);
+          if (m < T)
+            *reinterpret_cast<uint2*>(out_b + (int64_t)m * E + n) =
+                pack4_bf16(acc.v[i][j][0], acc.v[i][j][1], acc.v[i][j][2], acc.v[i][j][3]);
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < Cfg::FN; ++j) {
       const int n = n0 + dma_out_col<Cfg>(wn, j, lane);
@@ -90,13 +109,14 @@ __global__ __launch_bounds__(256) void router_gemm_f32(const float* __restrict__
 }
 
 template <class Cfg>
-static hipError_t launch_router_bf16(const Ctx& c, const moe_shape_t& s, const bf16_t* x,
-                                     const bf16_t* w, const float* bias, float* logits) {
-  const int mt = (s.T + Cfg::BM - 1) / Cfg::BM, nt = (s.E + Cfg::BN - 1) / Cfg::BN;
+static hipError_t launch_router_bf16(const Ctx& c, int M, int N, int K, const bf16_t* x, const bf16_t* w,
+                                     const float* bias, float* logits, bf16_t* out_b) {
+  const int mt = (M + Cfg::BM - 1) / Cfg::BM, nt = (N + Cfg::BN - 1) / Cfg::BN;
   const int items = mt * nt;
   // one workgroup per CU (the workgroups are sized to fill one), a multiple of 8 (XCDs)
   const int grid = std::min(((items + 7) / 8) * 8, c.num_cus);
-  RouterProb<Cfg> pb{x, w, bias, logits, s.T, s.d, s.E, nt};
+  RouterProb<Cfg> pb{x, w, bias, logits, M, K, N, nt};
+  pb.out_b = out_b;
   TimedLaunch tl(MOE_K_ROUTER_GEMM, c.stream);
   hipLaunchKernelGGL(router_gemm_bf16<Cfg>, dim3(grid), dim3(Cfg::THREADS), 0, c.stream, pb, items);
   return hipGetLastError();
@@ -121,20 +141,24 @@ using RouterLarge = DmaCfg<128, 256, MOE_ROUTER_STAGES, 2, 8, 4>;
 using RouterMedium = DmaCfg<128, 128, MOE_ROUTER_STAGES, 2, 8, 4>;
 using RouterSmall = DmaCfg<64, 128, 4, 2, 4, 4>;
 
+// bf16 [M, K] x [N, K]^T on the router engine: fp32 out (+ bias) or, with
+// out_b, bf16 out. K % 64 == 0.
+hipError_t launch_router_mnk(const Ctx& c, int M, int N, int K, const bf16_t* xb, const bf16_t* wb,
+                             const float* bias, float* logits, bf16_t* out_b) {
+  const int mt128 = (M + 127) / 128;
+  if (((M + 255) / 256) * ((N + 255) / 256) >= c.num_cus)
+    return launch_router_bf16<RouterHuge>(c, M, N, K, xb, wb, bias, logits, out_b);
+  if (mt128 * ((N + 255) / 256) >= c.num_cus)
+    return launch_router_bf16<RouterLarge>(c, M, N, K, xb, wb, bias, logits, out_b);
+  if (2 * mt128 * ((N + 127) / 128) >= c.num_cus)
+    return launch_router_bf16<RouterMedium>(c, M, N, K, xb, wb, bias, logits, out_b);
+  return launch_router_bf16<RouterSmall>(c, M, N, K, xb, wb, bias, logits, out_b);
+}
+
 hipError_t launch_router(const Ctx& c, const moe_shape_t& s, const void* x, const void* w,
                          const float* bias, float* logits) {
-  if (s.dtype == MOE_BF16) {
-    const bf16_t* xb = (const bf16_t*)x;
-    const bf16_t* wb = (const bf16_t*)w;
-    const int mt128 = (s.T + 127) / 128;
-    if (((s.T + 255) / 256) * ((s.E + 255) / 256) >= c.num_cus)
-      return launch_router_bf16<RouterHuge>(c, s, xb, wb, bias, logits);
-    if (mt128 * ((s.E + 255) / 256) >= c.num_cus)
-      return launch_router_bf16<RouterLarge>(c, s, xb, wb, bias, logits);
-    if (2 * mt128 * ((s.E + 127) / 128) >= c.num_cus)
-      return launch_router_bf16<RouterMedium>(c, s, xb, wb, bias, logits);
-    return launch_router_bf16<RouterSmall>(c, s, xb, wb, bias, logits);
-  }
+  if (s.dtype == MOE_BF16)
+    return launch_router_mnk(c, s.T, s.E, s.d, (const bf16_t*)x, (const bf16_t*)w, bias, logits, nullptr);
   const int64_t n = (int64_t)s.T * s.E;
   TimedLaunch tl(MOE_K_ROUTER_GEMM, c.stream);
   hipLaunchKernelGGL(router_gemm_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, c.stream,
@@ -180,13 +204,16 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 //      lands in position r, so lanes 0..k-1 hold the answer in order;
 //      otherwise (many equal logits) k rounds of "wave maximum, remove it"
 //      over all keys.
-// Gates: exp(l_j - l_0) / sum over the picks. With prob_part, the wave also
-// sums the full softmax of its tokens per expert; the block's waves are added
-// in a fixed order into prob_part[block, E].
+// Gates: exp(l_j - l_0) / sum over the first kg picks. With alt_out, k = kg +
+// the number of alternates: picks kg .. k-1 (the experts ranked next) go to
+// alt_out [T, k - kg] and take no gate. With prob_part, the wave also sums the
+// full softmax of its tokens per expert; the block's waves are added in a
+// fixed order into prob_part[block, E].
 template <int EPL, int TPW>
 __global__ __launch_bounds__(256) void topk_softmax(const float* __restrict__ logits, int T, int E,
-                                                    int k, int32_t* __restrict__ idx_out,
+                                                    int k, int kg, int32_t* __restrict__ idx_out,
                                                     float* __restrict__ gate_out,
+                                                    int32_t* __restrict__ alt_out,
                                                     float* __restrict__ prob_part) {
   __shared__ uint64_t cand[4][64];
   __shared__ uint64_t sel[4][32];
@@ -269,11 +296,13 @@ __global__ __launch_bounds__(256) void topk_softmax(const float* __restrict__ lo
     const float top = from_ordered((uint32_t)(__shfl(mine, 0, kWave) >> 32));
     const float my_logit = from_ordered((uint32_t)(mine >> 32));
     const int my_idx = (int)(0xffffffffu - (uint32_t)mine);
-    const float ex = lane < k ? expf(my_logit - top) : 0.f;
+    const float ex = lane < kg ? expf(my_logit - top) : 0.f;
     const float den = wave_sum(ex);
-    if (lane < k) {
-      idx_out[(int64_t)t * k + lane] = my_idx;
-      gate_out[(int64_t)t * k + lane] = ex / den;
+    if (lane < kg) {
+      idx_out[(int64_t)t * kg + lane] = my_idx;
+      gate_out[(int64_t)t * kg + lane] = ex / den;
+    } else if (lane < k) {
+      alt_out[(int64_t)t * (k - kg) + (lane - kg)] = my_idx;
     }
     if (prob_part) {
       float z[EPL], zs = 0.f;
@@ -331,7 +360,9 @@ __global__ __launch_bounds__(1024) void prob_reduce(const float* __restrict__ pa
 }
 
 hipError_t launch_topk(const Ctx& c, const moe_shape_t& s, const float* logits, int32_t* idx,
-                       float* gate, float* prob_part, float* prob_sum) {
+                       float* gate, float* prob_part, float* prob_sum, int32_t* alt) {
+  // with alt: k alternates after the k selected experts (2k picks in all)
+  const int ksel = alt ? 2 * s.k : s.k;
   // one token per wave; with the softmax sums requested, kTopkTokPerWaveProb tokens per wave
   // so the per-block partial sums stay small
   const int tpw = prob_sum ? kTopkTokPerWaveProb : 1;
@@ -343,10 +374,10 @@ hipError_t launch_topk(const Ctx& c, const moe_shape_t& s, const float* logits, 
 #define MOE_TOPK(N)                                                                                  \
   if (prob_sum)                                                                                      \
     hipLaunchKernelGGL((topk_softmax<N, kTopkTokPerWaveProb>), dim3(nblk), dim3(256), 0, c.stream,    \
-                       logits, s.T, s.E, s.k, idx, gate, part);                                      \
+                       logits, s.T, s.E, ksel, s.k, idx, gate, alt, part);                           \
   else                                                                                               \
     hipLaunchKernelGGL((topk_softmax<N, 1>), dim3(nblk), dim3(256), 0, c.stream, logits, s.T, s.E,    \
-                       s.k, idx, gate, part)
+                       ksel, s.k, idx, gate, alt, part)
     if (epl <= 1) MOE_TOPK(1);
     else if (epl <= 2) MOE_TOPK(2);
     else if (epl <= 4) MOE_TOPK(4);

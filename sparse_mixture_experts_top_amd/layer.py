@@ -87,15 +87,48 @@ def pack_weights(shape: B.MoeShape, w_gate, w_up, w_down, stream=None):
     return gu, dn
 
 
+@dataclass
+class Variant:
+    """Routing variants of the forward: remapping (alt [T,k] int32 and
+    moved [1] int32 buffers) or a latent router (w_latent [d_c,d] and the
+    z [T,d_c] buffer)."""
+    alt: Optional[torch.Tensor] = None
+    moved: Optional[torch.Tensor] = None
+    w_latent: Optional[torch.Tensor] = None
+    z: Optional[torch.Tensor] = None
+
+
+def variant_buffers(w: Workload, dev, device: str = "cuda") -> Optional[Variant]:
+    if w.remap:
+        return Variant(alt=torch.empty((w.T, w.k), dtype=torch.int32, device=device),
+                       moved=torch.zeros((1,), dtype=torch.int32, device=device))
+    if w.latent_dc > 0:
+        return Variant(w_latent=dev["w_latent"],
+                       z=torch.empty((w.T, w.latent_dc), dtype=dev["x"].dtype, device=device))
+    return None
+
+
 def forward(b: Buffers, x, w_router, bias, w_gate, w_up, w_down, lora=None, stream=None,
-            packed=None) -> None:
+            packed=None, variant: Optional[Variant] = None) -> None:
     """route -> dispatch -> expert GEMM -> combine; results stay in ``b``.
     packed: (gu_packed, down_packed) from pack_weights, used instead of the
-    row-major expert weights."""
+    row-major expert weights. variant: remapped dispatch or latent routing."""
     s = b.shape
-    B.moe_route(s, x, w_router, bias, b.topk_idx, b.topk_gate, b.logits, b.prob_sum, b.ws, stream)
-    B.moe_dispatch(s, b.topk_idx, b.topk_gate, x, b.counts, b.offsets, b.slot, b.row_src,
-                   b.row_gate, b.x_perm, b.dropped, b.ws, stream)
+    v = variant or Variant()
+    if v.w_latent is not None:
+        B.moe_route_latent(s, v.z.shape[1], x, v.w_latent, w_router, bias, v.z, b.topk_idx, b.topk_gate,
+                           b.logits, b.prob_sum, b.ws, stream)
+    elif v.alt is not None:
+        B.moe_route_alt(s, x, w_router, bias, b.topk_idx, b.topk_gate, v.alt, b.logits, b.prob_sum, b.ws,
+                        stream)
+    else:
+        B.moe_route(s, x, w_router, bias, b.topk_idx, b.topk_gate, b.logits, b.prob_sum, b.ws, stream)
+    if v.alt is not None:
+        B.moe_dispatch_remap(s, b.topk_idx, b.topk_gate, v.alt, x, b.counts, b.offsets, b.slot, b.row_src,
+                             b.row_gate, b.x_perm, v.moved, b.dropped, b.ws, stream)
+    else:
+        B.moe_dispatch(s, b.topk_idx, b.topk_gate, x, b.counts, b.offsets, b.slot, b.row_src,
+                       b.row_gate, b.x_perm, b.dropped, b.ws, stream)
     xr, src = x_rows(b, x)
     if packed is not None:
         B.moe_expert_gemm_packed(s, xr, src, b.offsets, packed[0], packed[1], lora, b.act_save,

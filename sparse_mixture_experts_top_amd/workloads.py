@@ -73,6 +73,7 @@ class Workload:
     lora_b: str = "normal"  # "zero" or "normal"
     aux_coef: float = 0.0  # load-balance loss coefficient (0 = not requested)
     latent_dc: int = 0     # latent routing width, 0 = the router reads x directly
+    remap: bool = False    # overflowing assignments remapped to the next-ranked experts
 
     @property
     def local_hi(self) -> int:
@@ -99,7 +100,7 @@ WORKLOADS: Dict[str, Workload] = {
                           lora_b="normal", aux_coef=0.01),
     # the skewed workload with overflow remapped instead of dropped
     "skewed_remap": Workload("skewed_remap", T=8192, d=2048, E=896, k=16, f=256,
-                             capacity=183, zipf_s=1.2),
+                             capacity=183, zipf_s=1.2, remap=True),
     # the full-router workload routed from a d/8-dimensional projection
     "latent_router": Workload("latent_router", T=4096, d=2048, E=896, k=16, f=256,
                               latent_dc=256),

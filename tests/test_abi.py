@@ -184,3 +184,28 @@ def test_dispatch_noalloc_rejects_shapes_beyond_its_scratch():
     assert b"scratch" in lib.moe_last_error()
     assert lib.moe_dispatch_noalloc(ctypes.byref(shape()), None, fake, None, fake, fake, fake, fake, fake,
                                     None, None, None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_remap_and_latent_routing_argument_checks():
+    """Host-side validation of the remapping and latent-routing entry points."""
+    lib = B.lib()
+    fake = ctypes.c_void_p(0x100000)      # never dereferenced: validation fails first
+    s = shape(dtype=B.MOE_BF16, d=128, f=64, capacity=0)
+    assert lib.moe_dispatch_remap(ctypes.byref(s), fake, fake, fake, None, fake, fake, fake, fake, fake, None,
+                                  None, None, fake, 1 << 30, None) == B.MOE_ERR_INVALID_ARG   # no capacity
+    assert b"capacity" in lib.moe_last_error()
+    s = shape(dtype=B.MOE_BF16, d=128, f=64, capacity=20, E=16, e_hi=16, k=9)            # 2k > E
+    assert lib.moe_dispatch_remap(ctypes.byref(s), fake, fake, fake, None, fake, fake, fake, fake, fake, None,
+                                  None, None, fake, 1 << 30, None) == B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_route_alt(ctypes.byref(s), fake, fake, None, fake, fake, fake, None, None, fake, 1 << 30,
+                             None) == B.MOE_ERR_UNSUPPORTED
+    s = shape(dtype=B.MOE_BF16, d=128, f=64)
+    assert lib.moe_route_alt(ctypes.byref(s), fake, fake, None, fake, fake, None, None, None, fake, 1 << 30,
+                             None) == B.MOE_ERR_INVALID_ARG                                  # alt_idx NULL
+    assert lib.moe_route_latent(ctypes.byref(s), 96, fake, fake, fake, None, fake, fake, fake, None, None, fake,
+                                1 << 30, None) == B.MOE_ERR_UNSUPPORTED                      # d_c % 64
+    s32 = shape()
+    assert lib.moe_route_latent(ctypes.byref(s32), 64, fake, fake, fake, None, fake, fake, fake, None, None, fake,
+                                1 << 30, None) == B.MOE_ERR_UNSUPPORTED                      # fp32
+    assert lib.moe_route_latent(ctypes.byref(s), 64, fake, None, fake, None, fake, fake, fake, None, None, fake,
+                                1 << 30, None) == B.MOE_ERR_INVALID_ARG                      # w_latent NULL

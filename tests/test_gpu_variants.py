@@ -1,0 +1,231 @@
+"""GPU parity of the routing variants, through the C ABI:
+
+* token remapping (moe_route_alt + moe_dispatch_remap): alternates, counts,
+  offsets, slots and rows bit-exact against the oracle fed the GPU's ids,
+  alternates and fp32 gates; then the expert rows and the combine;
+* the latent-space router (moe_route_latent): z within the fp32 bound plus
+  its bf16 rounding, logits within the fp32 bound around the oracle applied
+  to the GPU's own z, ids bit-exact, gates within 1e-5.
+Small shapes over several tiles with ragged tails, the edge cases, and the
+full workloads."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import assert_close, expert_ref_rows, host, logit_bound, say, upload
+from sparse_mixture_experts_top_amd import binding as B
+from sparse_mixture_experts_top_amd import layer
+from sparse_mixture_experts_top_amd.workloads import WORKLOADS, Workload, generate, to_f64
+
+pytestmark = pytest.mark.gpu
+
+W = Workload
+
+
+# --------------------------------------------------------- token remapping --
+
+def remap_forward(w, dev, x_perm=True, packed=False):
+    """route with alternates -> dispatch with remapping -> experts -> combine."""
+    s = layer.shape_of(w)
+    buf = layer.alloc(s, logits=True, x_perm=x_perm)
+    alt = torch.full((w.T, w.k), -7, dtype=torch.int32, device="cuda")
+    moved = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    B.moe_route_alt(s, dev["x"], dev["w_router"], dev.get("bias"), buf.topk_idx, buf.topk_gate, alt, buf.logits,
+                    None, buf.ws)
+    B.moe_dispatch_remap(s, buf.topk_idx, buf.topk_gate, alt, dev["x"], buf.counts, buf.offsets, buf.slot,
+                         buf.row_src, buf.row_gate, buf.x_perm, moved, buf.dropped, buf.ws)
+    xr, src = layer.x_rows(buf, dev["x"])
+    if packed:
+        gu, dn = layer.pack_weights(s, dev["w_gate"], dev["w_up"], dev["w_down"])
+        B.moe_expert_gemm_packed(s, xr, src, buf.offsets, gu, dn, None, None, buf.y_perm, buf.ws)
+    else:
+        B.moe_expert_gemm(s, xr, src, buf.offsets, dev["w_gate"], dev["w_up"], dev["w_down"], None, None,
+                          buf.y_perm, buf.ws)
+    B.moe_combine(s, buf.y_perm, buf.slot, buf.topk_gate, buf.y)
+    torch.cuda.synchronize()
+    return buf, alt, moved
+
+
+def check_remap(w, inp, dev, buf, alt, moved, sample_rows=None):
+    lg = host(buf.logits)
+    ranked = oracle.topk_experts(lg, 2 * w.k)
+    idx = host(buf.topk_idx)
+    assert (idx == ranked[:, :w.k]).all(), "top-k ids differ"
+    assert (host(alt) == ranked[:, w.k:]).all(), "alternates differ"
+    gate = host(buf.topk_gate)
+    assert np.abs(gate - oracle.topk_gates(lg, idx)).max() <= 1e-5
+    ref = oracle.dispatch_remap(idx, host(alt), gate.astype(np.float32), w.E, w.e_lo, w.local_hi, w.capacity)
+    for n in ("counts", "offsets", "slot"):
+        assert (host(getattr(buf, n)) == ref[n]).all(), f"{n} differs"
+    R = int(ref["offsets"][-1])
+    assert (host(buf.row_src)[:R] == ref["row_src"]).all(), "row_src differs"
+    assert (buf.row_gate[:R].cpu().numpy() == ref["row_gate"].astype(np.float32)).all(), "row_gate differs"
+    assert int(moved.item()) == ref["moved"] and int(buf.dropped.item()) == ref["dropped"]
+    if buf.x_perm is not None:
+        assert torch.equal(buf.x_perm[:R], dev["x"][buf.row_src[:R].long()])
+    say(f"  remap: R={R} moved={ref['moved']} dropped={ref['dropped']} bit-exact")
+    rows = np.arange(R) if sample_rows is None else np.sort(
+        np.random.default_rng(9).choice(R, min(R, sample_rows), replace=False))
+    o_ref = expert_ref_rows(w, inp, buf, rows)
+    assert_close(host(buf.y_perm[torch.as_tensor(rows, device="cuda").long()]), o_ref, w.dtype,
+                 "expert rows (remapped dispatch)", stored_bf16=True)
+    return ref, R
+
+
+REMAP = {
+    "remap_bf16": W("remap_bf16", T=700, d=128, E=32, k=4, f=64, capacity=30, zipf_s=1.2),
+    "remap_local_bf16": W("remap_local_bf16", T=520, d=192, E=24, k=5, f=192, e_lo=3, e_hi=17, capacity=40,
+                          zipf_s=1.0),
+    "remap_f32": W("remap_f32", T=200, d=48, E=12, k=3, f=20, e_lo=2, e_hi=10, capacity=25, zipf_s=1.0,
+                   dtype="f32"),
+    "remap_k1_bf16": W("remap_k1_bf16", T=300, d=128, E=16, k=1, f=128, capacity=12, zipf_s=1.5),
+    "remap_cap1_bf16": W("remap_cap1_bf16", T=90, d=64, E=40, k=2, f=64, capacity=1, zipf_s=0.5),
+}
+
+
+@pytest.mark.parametrize("name", sorted(REMAP))
+def test_remap_stagewise(name):
+    w = REMAP[name]
+    say(f"[remap {name}] T={w.T} d={w.d} E={w.E} k={w.k} cap={w.capacity} local=[{w.e_lo},{w.local_hi})")
+    inp = generate(w, seed=4)
+    dev = upload(inp)
+    buf, alt, moved = remap_forward(w, dev)
+    ref, R = check_remap(w, inp, dev, buf, alt, moved)
+    assert ref["moved"] > 0
+    # combine over the remapped slots, fed the GPU's rows
+    y_ref = oracle.combine(host(buf.y_perm[:R]) if R else np.zeros((0, w.d)), host(buf.slot), host(buf.topk_gate),
+                           w.T)
+    assert_close(host(buf.y), y_ref, w.dtype, "combine (remapped)")
+
+
+def test_remap_conservation_over_all_experts_and_fused_gather():
+    w = REMAP["remap_bf16"]
+    inp = generate(w, seed=5)
+    dev = upload(inp)
+    buf, alt, moved = remap_forward(w, dev, x_perm=False, packed=True)
+    ref, R = check_remap(w, inp, dev, buf, alt, moved)
+    kept1 = int(np.minimum(host(buf.counts), w.capacity).sum())
+    assert kept1 + int(moved.item()) + int(buf.dropped.item()) == w.T * w.k
+    assert (np.diff(host(buf.offsets)) <= w.capacity).all()
+
+
+def test_remap_empty_batch():
+    w = W("remap_empty", T=0, d=128, E=16, k=4, f=64, capacity=10)
+    s = layer.shape_of(w)
+    buf = layer.alloc(s, x_perm=False)
+    moved = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    buf.dropped.fill_(-7)
+    B.moe_dispatch_remap(s, None, None, None, None, buf.counts, buf.offsets, None, None, None, None, moved,
+                         buf.dropped, buf.ws)
+    torch.cuda.synchronize()
+    assert (buf.counts == 0).all() and (buf.offsets == 0).all()
+    assert int(moved.item()) == 0 and int(buf.dropped.item()) == 0
+
+
+def test_remap_full_size():
+    w = WORKLOADS["skewed_remap"]
+    say(f"[remap full {w.name}] T={w.T} E={w.E} k={w.k} cap={w.capacity}")
+    inp = generate(w, seed=0)
+    dev = upload(inp)
+    buf, alt, moved = remap_forward(w, dev, x_perm=False, packed=True)
+    ref, R = check_remap(w, inp, dev, buf, alt, moved, sample_rows=384)
+    rng = np.random.default_rng(10)
+    tt = np.sort(rng.choice(w.T, 128, replace=False))
+    slot = host(buf.slot)[tt]
+    rows = np.unique(slot[slot >= 0])
+    o = host(buf.y_perm[torch.as_tensor(rows, device="cuda").long()])
+    remap_rows = -np.ones(R, dtype=np.int64)
+    remap_rows[rows] = np.arange(len(rows))
+    cs = np.where(slot >= 0, remap_rows[np.maximum(slot, 0)], -1)
+    y_ref = oracle.combine(o, cs, host(buf.topk_gate)[tt], len(tt))
+    assert_close(host(buf.y[torch.as_tensor(tt, device="cuda").long()]), y_ref, "bf16", "combine (sampled tokens)")
+    say(f"  kept {int(np.minimum(host(buf.counts), w.capacity).sum())} moved {ref['moved']} dropped {ref['dropped']}")
+
+
+# ------------------------------------------------------ latent-space router --
+
+def latent_route(w, dev):
+    s = layer.shape_of(w)
+    buf = layer.alloc(s, logits=True, x_perm=False)
+    z = torch.full((w.T, w.latent_dc), float("nan"), dtype=torch.bfloat16, device="cuda")
+    B.moe_route_latent(s, w.latent_dc, dev["x"], dev["w_latent"], dev["w_router"], dev.get("bias"), z,
+                       buf.topk_idx, buf.topk_gate, buf.logits, None, buf.ws)
+    torch.cuda.synchronize()
+    return buf, z
+
+
+def check_latent(w, inp, buf, z, tokens=None):
+    ts = np.arange(w.T) if tokens is None else tokens
+    x64, wc64, wr64 = to_f64(inp["x"])[ts], to_f64(inp["w_latent"]), to_f64(inp["w_router"])
+    bias = to_f64(inp.get("bias"))
+    # z: fp32 accumulation, then rounded to bf16
+    _, z_ref = oracle.latent_router_logits(x64, wc64, wr64, bias)
+    zg = host(z)[ts]
+    bound = logit_bound(x64, wc64) + 2.0 ** -8 * np.abs(z_ref)
+    dz = np.abs(zg - z_ref)
+    say(f"  z: max |d|={dz.max():.3e} max(|d|/bound)={(dz / bound).max():.3f}")
+    assert (dz <= bound).all(), "z outside its bound"
+    # logits from the GPU's own z
+    lg = host(buf.logits)
+    l_ref = oracle.router_logits(zg, wr64, bias)
+    lb = logit_bound(zg, wr64, bias)
+    dl = np.abs(lg[ts] - l_ref)
+    say(f"  logits: max |d|={dl.max():.3e} max(|d|/bound)={(dl / lb).max():.3f}")
+    assert (dl <= lb).all(), "logit outside the fp32 bound"
+    idx = host(buf.topk_idx)
+    assert (idx == oracle.topk_experts(lg, w.k)).all(), "top-k ids differ"
+    assert np.abs(host(buf.topk_gate) - oracle.topk_gates(lg, idx)).max() <= 1e-5
+    return lg
+
+
+LATENT = {
+    "latent_bf16": W("latent_bf16", T=300, d=256, E=40, k=6, f=128, latent_dc=64),
+    "latent_bias_bf16": W("latent_bias_bf16", T=520, d=192, E=24, k=5, f=192, e_lo=3, e_hi=17, latent_dc=128,
+                          zipf_s=1.0),
+    "latent_wide_bf16": W("latent_wide_bf16", T=1100, d=512, E=128, k=8, f=64, latent_dc=192),
+}
+
+
+@pytest.mark.parametrize("name", sorted(LATENT))
+def test_latent_router_stagewise(name):
+    w = LATENT[name]
+    say(f"[latent {name}] T={w.T} d={w.d} d_c={w.latent_dc} E={w.E} k={w.k}")
+    inp = generate(w, seed=6)
+    dev = upload(inp)
+    buf, z = latent_route(w, dev)
+    check_latent(w, inp, buf, z)
+    # the rest of the layer on the latent routing: dispatch, experts, combine
+    s = buf.shape
+    B.moe_dispatch(s, buf.topk_idx, buf.topk_gate, None, buf.counts, buf.offsets, buf.slot, buf.row_src,
+                   buf.row_gate, None, buf.dropped, buf.ws)
+    B.moe_expert_gemm(s, dev["x"], buf.row_src, buf.offsets, dev["w_gate"], dev["w_up"], dev["w_down"], None, None,
+                      buf.y_perm, buf.ws)
+    B.moe_combine(s, buf.y_perm, buf.slot, buf.topk_gate, buf.y)
+    torch.cuda.synchronize()
+    d = oracle.dispatch(host(buf.topk_idx), host(buf.topk_gate).astype(np.float32), w.E, w.e_lo, w.local_hi)
+    assert (host(buf.slot) == d["slot"]).all()
+    R = int(d["offsets"][-1])
+    o_ref = expert_ref_rows(w, inp, buf, np.arange(R))
+    y_ref = oracle.combine(o_ref, d["slot"], host(buf.topk_gate), w.T)
+    assert_close(host(buf.y), y_ref, "bf16", "y (latent routing)")
+
+
+def test_latent_router_zero_tokens_tie_to_lower_ids():
+    w = LATENT["latent_bf16"]
+    inp = generate(w, seed=7)
+    inp["x"] = torch.zeros_like(inp["x"])
+    dev = upload(inp)
+    buf, z = latent_route(w, dev)
+    assert (z == 0).all()
+    assert (host(buf.topk_idx) == np.arange(w.k)[None, :]).all()
+
+
+def test_latent_router_full_size():
+    w = WORKLOADS["latent_router"]
+    say(f"[latent full] T={w.T} d={w.d} d_c={w.latent_dc} E={w.E}")
+    inp = generate(w, seed=0)
+    dev = upload(inp)
+    buf, z = latent_route(w, dev)
+    ts = np.sort(np.random.default_rng(3).choice(w.T, 64, replace=False))
+    check_latent(w, inp, buf, z, tokens=ts)
