@@ -50,11 +50,18 @@ using GemmCfgWide = DmaCfg<kGemmBM, 256, MOE_GEMM_STAGES, 2, 8, 4>;
 // is streamed once per expert instead of once per 128-row tile, and the
 // items (experts x column blocks) fit the CUs in one round. 4 x 2 compute
 // waves (two per SIMD), each 5 interleaved row fragments x 4 column
-// fragments (80 x 64), + 4 producers; 5 ring slots of 28 KB.
+// fragments (80 x 64), + 4 producers. Split ring: the token rows (20 KB a
+// stage, shared through the L2 by the expert's column blocks) in
+// MOE_GEMM_TALL_STAGES slots, the streamed weight tiles (8 KB a stage, from
+// HBM) in MOE_GEMM_TALL_BSTAGES slots, so more of the weight stream is in
+// flight.
 #ifndef MOE_GEMM_TALL_STAGES
-#define MOE_GEMM_TALL_STAGES 5
+#define MOE_GEMM_TALL_STAGES 3
 #endif
-using GemmCfgTall = DmaCfg<320, 128, MOE_GEMM_TALL_STAGES, 4, 8, 4>;
+#ifndef MOE_GEMM_TALL_BSTAGES
+#define MOE_GEMM_TALL_BSTAGES 12
+#endif
+using GemmCfgTall = DmaCfg<320, 128, MOE_GEMM_TALL_STAGES, 4, 8, 4, 32, MOE_GEMM_TALL_BSTAGES>;
 
 // Rows per local expert expected under uniform routing (capped by the
 // capacity) at which the tall layout is used.

@@ -297,7 +297,9 @@ __device__ __forceinline__ void persistent_gemm(Prob& pb, int items, int nk, bf1
 // keys that are a permutation within every 4 rows of equal r mod 4, take 8
 // cycles (2-way conflicts).
 // STAGES stages form a ring in one LDS array; stage g's slot is g % STAGES and
-// STAGES - 1 stages are in flight while one is consumed.
+// STAGES - 1 stages are in flight while one is consumed. With SB > 0 the two
+// operands have rings of their own: A keeps STAGES slots, B gets SB slots and
+// is fetched SB - STAGES stages further ahead (see persistent_gemm_dma).
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
@@ -307,8 +309,9 @@ typedef __attribute__((address_space(1))) void glb_void_t;
 // WM x (CW / WM) grid over the tile and PW producer waves (waves CW ..
 // CW+PW-1; producer p issues the DMAs i with i % PW == p). A workgroup runs
 // alone on its CU (THREADS = 64 (CW + PW)); the occupancy hint WAVES_PER_SIMD
-// caps the registers per wave at 512 / WAVES_PER_SIMD.
-template <int BM_, int BN_, int STAGES_ = 4, int WM_ = 2, int CW_ = 4, int PW_ = 4, int BK_ = 32>
+// caps the registers per wave at 512 / WAVES_PER_SIMD. SB_ > 0 splits the
+// ring: A in STAGES slots, B in SB_ slots.
+template <int BM_, int BN_, int STAGES_ = 4, int WM_ = 2, int CW_ = 4, int PW_ = 4, int BK_ = 32, int SB_ = 0>
 struct DmaCfg {
   static constexpr int BM = BM_;
   static constexpr int BN = BN_;
@@ -340,6 +343,14 @@ struct DmaCfg {
   static_assert(A_DMA % DW == 0 && B_DMA % DW == 0, "DMA split");
   static_assert(CW % WM == 0, "wave grid");
   static_assert(STAGES >= 2 && (STAGES - 2) * DMA_PER_PRODUCER <= 63, "ring depth vs vmcnt");
+  // split ring: B slots, the lead of B over A in stages, LDS elements
+  static constexpr int SB = SB_;
+  static constexpr bool SPLIT = SB_ > 0;
+  static constexpr int B_LEAD = SPLIT ? SB_ - STAGES_ : 0;
+  static constexpr int A_PER = A_DMA / DW, B_PER = B_DMA / DW;  // per stage and producer
+  static constexpr int RING_ELEMS = SPLIT ? STAGES * A_ELEMS + SB * B_ELEMS : STAGES * STAGE_ELEMS;
+  static_assert(!SPLIT || (SB_ > STAGES_ && PW_ > 0 && STAGES_ >= 2), "split ring: producers, B ring deeper");
+  static_assert(!SPLIT || (STAGES_ - 1) * A_PER + (SB_ - 1) * B_PER <= 63, "split ring vs vmcnt");
 };
 
 // Lane pointers of one producer for one item: a[q] / b[q] belong to the
@@ -407,23 +418,33 @@ __device__ __forceinline__ void dma16_nt(const void* g, const bf16_t* lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(g), "s"(a) : "memory");
 }
 
-// Producer `part`'s share of the DMA instructions of K step kt into stage
-// `stage`: A and B instructions i with i % DW == part.
+// Producer `part`'s share of the DMA instructions of K step kt: A
+// instructions i with i % DW == part into the A part of a stage at a_dst, B
+// ones into the B part at b_dst; dma_issue does both, A first.
 template <class Cfg>
-__device__ __forceinline__ void dma_issue(const DmaLoader<Cfg>& ld, int kt, bf16_t* stage, int part) {
-  const int64_t ka = (int64_t)kt * ld.a_kstep, kb = (int64_t)kt * ld.b_kstep;
+__device__ __forceinline__ void dma_issue_a(const DmaLoader<Cfg>& ld, int kt, bf16_t* a_dst, int part) {
+  const int64_t ka = (int64_t)kt * ld.a_kstep;
 #pragma unroll
   for (int q = 0; q < Cfg::A_DMA / Cfg::DW; ++q)
-    dma16(ld.a[q] + ka, stage + Cfg::RPD * (q * Cfg::DW + part) * Cfg::BK);
+    dma16(ld.a[q] + ka, a_dst + Cfg::RPD * (q * Cfg::DW + part) * Cfg::BK);
+}
+template <class Cfg>
+__device__ __forceinline__ void dma_issue_b(const DmaLoader<Cfg>& ld, int kt, bf16_t* b_dst, int part) {
+  const int64_t kb = (int64_t)kt * ld.b_kstep;
   if (ld.b_stream) {  // wave-uniform
 #pragma unroll
     for (int q = 0; q < Cfg::B_DMA / Cfg::DW; ++q)
-      dma16_nt(ld.b[q] + kb, stage + Cfg::A_ELEMS + Cfg::RPD * (q * Cfg::DW + part) * Cfg::BK);
+      dma16_nt(ld.b[q] + kb, b_dst + Cfg::RPD * (q * Cfg::DW + part) * Cfg::BK);
   } else {
 #pragma unroll
     for (int q = 0; q < Cfg::B_DMA / Cfg::DW; ++q)
-      dma16(ld.b[q] + kb, stage + Cfg::A_ELEMS + Cfg::RPD * (q * Cfg::DW + part) * Cfg::BK);
+      dma16(ld.b[q] + kb, b_dst + Cfg::RPD * (q * Cfg::DW + part) * Cfg::BK);
   }
+}
+template <class Cfg>
+__device__ __forceinline__ void dma_issue(const DmaLoader<Cfg>& ld, int kt, bf16_t* stage, int part) {
+  dma_issue_a<Cfg>(ld, kt, stage, part);
+  dma_issue_b<Cfg>(ld, kt, stage + Cfg::A_ELEMS, part);
 }
 
 // Packed B operand: a weight tile of 128 rows x one K step stored as the
@@ -456,12 +477,11 @@ struct Frags {
   bf16x8 a[Cfg::FM], b[Cfg::FN];
 };
 
-// LDS reads of the wave's fragments of the stage at `st`.
+// LDS reads of the wave's fragments of a stage whose A and B parts are at
+// As and Bs (read_frags: one slot of the joint ring at `st`).
 template <class Cfg>
-__device__ __forceinline__ void read_frags(Frags<Cfg>& fr, const bf16_t* st, int wm, int wn, int lane,
-                                           int sub = 0) {
-  const bf16_t* As = st;
-  const bf16_t* Bs = st + Cfg::A_ELEMS;
+__device__ __forceinline__ void read_frags_ab(Frags<Cfg>& fr, const bf16_t* As, const bf16_t* Bs, int wm, int wn,
+                                              int lane, int sub = 0) {
   const int r = lane & 15;
   const int slot = ((lane >> 4) + 4 * sub) ^ lds_key<Cfg>(r);
 #pragma unroll
@@ -471,6 +491,29 @@ __device__ __forceinline__ void read_frags(Frags<Cfg>& fr, const bf16_t* st, int
   for (int i = 0; i < Cfg::FM; ++i)
     fr.a[i] = *reinterpret_cast<const bf16x8*>(&As[(frag_row0<Cfg>(wm, i) + r) * Cfg::BK + slot * 8]);
 }
+template <class Cfg>
+__device__ __forceinline__ void read_frags(Frags<Cfg>& fr, const bf16_t* st, int wm, int wn, int lane,
+                                           int sub = 0) {
+  read_frags_ab<Cfg>(fr, st, st + Cfg::A_ELEMS, wm, wn, lane, sub);
+}
+
+// Read cursor of the compute waves over the ring: the A and B parts of the
+// next stage to read, advanced one stage at a time.
+template <class Cfg>
+struct RingCursor {
+  const bf16_t* ring;
+  int sa = 1 % Cfg::STAGES, sb = 1 % (Cfg::SPLIT ? Cfg::SB : 1);
+  __device__ __forceinline__ const bf16_t* a() const {
+    return Cfg::SPLIT ? ring + sa * Cfg::A_ELEMS : ring + sa * Cfg::STAGE_ELEMS;
+  }
+  __device__ __forceinline__ const bf16_t* b() const {
+    return Cfg::SPLIT ? ring + Cfg::STAGES * Cfg::A_ELEMS + sb * Cfg::B_ELEMS : a() + Cfg::A_ELEMS;
+  }
+  __device__ __forceinline__ void advance() {
+    sa = (sa + 1 == Cfg::STAGES) ? 0 : sa + 1;
+    if (Cfg::SPLIT) sb = (sb + 1 == Cfg::SB) ? 0 : sb + 1;
+  }
+};
 
 // Workgroup barrier without a memory fence (see persistent_gemm_dma), with
 // compiler-level memory clobbers on both sides: the s_barrier intrinsic is
@@ -498,13 +541,13 @@ __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt((15) |
 // 16 x 16 fragment, which the epilogues write as one 8- or 16-byte store
 // instead of four scattered 2-byte ones (see dma_out_row / dma_out_col).
 template <class Cfg>
-__device__ __forceinline__ void mma_pp_step(int g, int total, int nf, const bf16_t* ring, int& rslot,
+__device__ __forceinline__ void mma_pp_step(int g, int total, int nf, RingCursor<Cfg>& rc,
                                             const Frags<Cfg>& cur, Frags<Cfg>& nxt, Acc<Cfg>& acc,
                                             int wm, int wn, int lane) {
   ring_barrier();
   if (g + 1 < total) {
-    read_frags<Cfg>(nxt, ring + rslot * Cfg::STAGE_ELEMS, wm, wn, lane);
-    rslot = (rslot + 1 == Cfg::STAGES) ? 0 : rslot + 1;
+    read_frags_ab<Cfg>(nxt, rc.a(), rc.b(), wm, wn, lane);
+    rc.advance();
   }
 #pragma unroll
   for (int i = 0; i < Cfg::FM; ++i) {
@@ -560,6 +603,42 @@ __device__ __forceinline__ void dma_wait_stage(int younger) {
   }
 }
 
+// Producer wait with a run-time count: vmcnt <= the largest immediate <= n.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_le(int n) {
+  if constexpr (N == 0) {
+    wait_vmcnt_imm<0>();
+  } else {
+    if (n >= N)
+      wait_vmcnt_imm<N>();
+    else
+      wait_vmcnt_le<N - 1>(n);
+  }
+}
+
+// Split ring (Cfg::SPLIT): a producer issues its DMAs in steps, step j being
+// A of stage j then B of stage j + B_LEAD (steps past the last stage issue
+// nothing for that operand), after B_LEAD B-only steps at the start. When it
+// waits for stage j, steps up to j + STAGES - 2 have been issued, and since
+// loads complete in issue order, stage j (both parts) has landed once at most
+// these are still out: B of step j and both parts of steps j + 1 ..
+// j + STAGES - 2, as far as they exist (rem = stages left from j on).
+template <class Cfg>
+__device__ __forceinline__ int split_younger(int rem) {
+  int c = Cfg::B_LEAD < rem ? Cfg::B_PER : 0;
+#pragma unroll
+  for (int m = 1; m <= Cfg::STAGES - 2; ++m) c += (m < rem ? Cfg::A_PER : 0) + (m + Cfg::B_LEAD < rem ? Cfg::B_PER : 0);
+  return c;
+}
+template <class Cfg>
+__device__ __forceinline__ void split_wait_stage(int rem) {
+  constexpr int steady = Cfg::B_PER + (Cfg::STAGES - 2) * (Cfg::A_PER + Cfg::B_PER);
+  if (rem > Cfg::STAGES - 2 + Cfg::B_LEAD)
+    wait_vmcnt_imm<steady>();
+  else
+    wait_vmcnt_le<steady>(split_younger<Cfg>(rem));
+}
+
 // Extra K steps a problem appends to each item (Prob::kExtra, default 0):
 // stages whose operands come from a second loader filled by
 // Prob::setup_extra(item, ld, part), e.g. a rank-r adapter term carried
@@ -592,12 +671,18 @@ struct ExtraSteps<P, std::void_t<decltype(P::kExtra)>> {
 // Barriers are bare s_barrier: the producers' explicit vmcnt waits already
 // order their DMA writes, and a fenced barrier would wait for every stage in
 // flight.
+// Split ring (Cfg::SB > 0): A stays in STAGES slots, B gets SB slots of its
+// own, so barrier g frees A slot g % STAGES and B slot g % SB, and the
+// producers refill them with A of stage g + STAGES and B of stage g + SB.
+// B then has SB - 1 stages in flight where A has STAGES - 1: for streamed
+// weights, whose lines come from HBM once, against token rows that the
+// column blocks of an expert share through the L2.
 template <class Cfg, class Prob>
 __device__ __forceinline__ void persistent_gemm_dma(Prob& pb, int items, int nk_main) {
   static_assert(Cfg::KSUB == 1, "one MFMA K step per stage");
   constexpr int S = Cfg::STAGES;
   constexpr int NX = ExtraSteps<Prob>::value;
-  __shared__ __align__(16) bf16_t ring[S * Cfg::STAGE_ELEMS];
+  __shared__ __align__(16) bf16_t ring[Cfg::RING_ELEMS];
   const XcdSplit sp = xcd_split(items);
   if (sp.first >= sp.end || nk_main <= 0) return;
   const int nk = nk_main + NX;  // K steps per item
@@ -605,7 +690,70 @@ __device__ __forceinline__ void persistent_gemm_dma(Prob& pb, int items, int nk_
   const int total = n_mine * nk;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 
-  if (wave >= Cfg::CW) {
+  if constexpr (Cfg::SPLIT) {
+    if (wave >= Cfg::CW) {
+      const int part = wave - Cfg::CW;
+      // separate cursors (item, K step, slot) for the A and the B stream
+      struct Cursor {
+        int ord = 0, kt = 0, slot = 0, n = 0;  // n: stages issued
+        DmaLoader<Cfg> ld, ldx;
+      };
+      Cursor ca, cb;
+      pb.setup(sp.first, ca.ld, part);
+      pb.setup(sp.first, cb.ld, part);
+      if constexpr (NX > 0) {
+        pb.setup_extra(sp.first, ca.ldx, part);
+        pb.setup_extra(sp.first, cb.ldx, part);
+      }
+      auto advance = [&](Cursor& c, int slots) {
+        c.slot = (c.slot + 1 == slots) ? 0 : c.slot + 1;
+        ++c.n;
+        if (++c.kt == nk) {
+          c.kt = 0;
+          if (++c.ord < n_mine) {
+            const int item = sp.first + c.ord * sp.stride;
+            pb.setup(item, c.ld, part);
+            if constexpr (NX > 0) pb.setup_extra(item, c.ldx, part);
+          }
+        }
+      };
+      auto issue_a = [&]() {
+        if (ca.n >= total) return;
+        bf16_t* dst = ring + ca.slot * Cfg::A_ELEMS;
+        if (NX > 0 && ca.kt >= nk_main)
+          dma_issue_a<Cfg>(ca.ldx, ca.kt - nk_main, dst, part);
+        else
+          dma_issue_a<Cfg>(ca.ld, ca.kt, dst, part);
+        advance(ca, S);
+      };
+      auto issue_b = [&]() {
+        if (cb.n >= total) return;
+        bf16_t* dst = ring + S * Cfg::A_ELEMS + cb.slot * Cfg::B_ELEMS;
+        if (NX > 0 && cb.kt >= nk_main)
+          dma_issue_b<Cfg>(cb.ldx, cb.kt - nk_main, dst, part);
+        else
+          dma_issue_b<Cfg>(cb.ld, cb.kt, dst, part);
+        advance(cb, Cfg::SB);
+      };
+      for (int p = 0; p < Cfg::B_LEAD; ++p) issue_b();
+      for (int p = 0; p < S - 1; ++p) {
+        issue_a();
+        issue_b();
+      }
+      // barrier "-1": stage 0 landed
+      split_wait_stage<Cfg>(total);
+      ring_barrier();
+      issue_a();
+      issue_b();
+      for (int g = 0; g < total; ++g) {
+        if (g + 1 < total) split_wait_stage<Cfg>(total - 1 - g);
+        ring_barrier();
+        issue_a();  // stage g + S into A slot g % S
+        issue_b();  // stage g + SB into B slot g % SB
+      }
+      return;
+    }
+  } else if (wave >= Cfg::CW) {
     const int part = wave - Cfg::CW;
     DmaLoader<Cfg> ld, ldx;
     int l_ord = 0, l_kt = 0, l_slot = 0;  // load cursor
@@ -645,8 +793,8 @@ __device__ __forceinline__ void persistent_gemm_dma(Prob& pb, int items, int nk_
   Acc<Cfg> acc;
   Frags<Cfg> f0, f1;
   ring_barrier();  // barrier "-1"
-  read_frags<Cfg>(f0, ring, wm, wn, lane);
-  int rslot = 1 % S;  // ring slot of the next stage to read
+  RingCursor<Cfg> rc{ring};  // next stage to read: 1
+  read_frags_ab<Cfg>(f0, ring, ring + (Cfg::SPLIT ? S * Cfg::A_ELEMS : Cfg::A_ELEMS), wm, wn, lane);
   wait_lgkm0();
   // K steps ping-pong between the two register sets; every item starts with
   // its first stage in f0 (with an odd step count the last step reads the
@@ -658,13 +806,13 @@ __device__ __forceinline__ void persistent_gemm_dma(Prob& pb, int items, int nk_
     acc.zero();
     int kt = 0;
     for (; kt + 1 < nk; kt += 2) {
-      mma_pp_step<Cfg>(g0 + kt, total, nf, ring, rslot, f0, f1, acc, wm, wn, lane);
+      mma_pp_step<Cfg>(g0 + kt, total, nf, rc, f0, f1, acc, wm, wn, lane);
       wait_lgkm0();
-      mma_pp_step<Cfg>(g0 + kt + 1, total, nf, ring, rslot, f1, f0, acc, wm, wn, lane);
+      mma_pp_step<Cfg>(g0 + kt + 1, total, nf, rc, f1, f0, acc, wm, wn, lane);
       wait_lgkm0();
     }
     const bool odd = kt < nk;  // wave-uniform
-    if (odd) mma_pp_step<Cfg>(g0 + kt, total, nf, ring, rslot, f0, f1, acc, wm, wn, lane);
+    if (odd) mma_pp_step<Cfg>(g0 + kt, total, nf, rc, f0, f1, acc, wm, wn, lane);
     pb.epilogue(item, acc);
     wait_lgkm0();
     if (odd) f0 = f1;
@@ -742,6 +890,7 @@ template <class Cfg, class Prob>
 __device__ __forceinline__ void persistent_gemm_sym_k64(Prob& pb, int items, int nk) {
   static_assert(Cfg::PW == 0 && Cfg::KSUB == 2, "symmetric configuration, 64-K stages");
   constexpr int S = Cfg::STAGES;
+  static_assert(!Cfg::SPLIT, "joint ring");
   __shared__ __align__(16) bf16_t ring[S * Cfg::STAGE_ELEMS];
   const XcdSplit sp = xcd_split(items);
   if (sp.first >= sp.end || nk <= 0) return;
@@ -818,6 +967,7 @@ __device__ __forceinline__ void persistent_gemm_sym(Prob& pb, int items, int nk)
   static_assert(Cfg::FM % 2 == 0, "two halves of A fragments");
   constexpr int S = Cfg::STAGES;
   constexpr int H = Cfg::FM / 2;
+  static_assert(!Cfg::SPLIT, "joint ring");
   __shared__ __align__(16) bf16_t ring[S * Cfg::STAGE_ELEMS];
   const XcdSplit sp = xcd_split(items);
   if (sp.first >= sp.end || nk <= 0) return;

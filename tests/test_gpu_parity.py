@@ -29,9 +29,14 @@ SMALL = {
                       capacity=25, zipf_s=1.0, dtype="f32"),
     "k_equals_E_bf16": W("k_equals_E_bf16", T=130, d=64, E=8, k=8, f=64),
     "k1_bf16": W("k1_bf16", T=257, d=128, E=16, k=1, f=128),
-    # ~300 rows per expert: the layout with two compute waves per SIMD (three
-    # row tiles per expert, the last one ragged), local range
+    # ~300 rows per expert: the 320-row tiles (one row tile per expert, some
+    # experts with a second, ragged one), local range
     "wide_bf16": W("wide_bf16", T=1200, d=256, E=16, k=4, f=128, e_lo=2, e_hi=13),
+    # 320-row tiles with two K steps (d = 64) and two or more items per
+    # workgroup: the weight ring's lead exceeds a workgroup's whole sequence
+    "tall_shortk_bf16": W("tall_shortk_bf16", T=8192, d=64, E=64, k=2, f=512),
+    # the same with four K steps (packed weights need d % 128 == 0)
+    "tall_k128_bf16": W("tall_k128_bf16", T=8192, d=128, E=64, k=2, f=512),
 }
 
 
@@ -205,7 +210,8 @@ def test_capacity_one_everywhere():
     assert R == int((ref["counts"] > 0).sum())
 
 
-@pytest.mark.parametrize("name", ["ragged_bf16", "rows_bf16", "capacity_bf16", "k1_bf16", "wide_bf16"])
+@pytest.mark.parametrize("name", ["ragged_bf16", "rows_bf16", "capacity_bf16", "k1_bf16", "wide_bf16",
+                                  "tall_k128_bf16"])
 def test_stagewise_parity_packed_weights(name):
     """Expert weights streamed from their packed copies (fused gather too)."""
     run_and_check(SMALL[name], seed=8, x_perm=False, packed=True)
