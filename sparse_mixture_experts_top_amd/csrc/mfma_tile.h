@@ -339,15 +339,19 @@ struct DmaCfg {
   static_assert(FM >= 1 && FN >= 1 && FM * 16 * WM == BM && FN * 16 * WN == BN, "fragments");
   static_assert(BK == 32 || BK == 64, "stage depth");
   static_assert(BM % 16 == 0 && BN % 16 == 0, "fragments are 16 rows");
-  static constexpr int DMA_PER_PRODUCER = DMA_PER_STAGE / DW;  // per stage and DMA wave
-  static_assert(A_DMA % DW == 0 && B_DMA % DW == 0, "DMA split");
+  // B instructions per DMA wave and stage: with B_DMA % DW != 0 (symmetric
+  // drivers only) the last round's missing instructions repeat instruction
+  // B_DMA - 1 (the same rows into the same LDS rows; see b_inst)
+  static constexpr int B_Q = (B_DMA + DW - 1) / DW;
+  static constexpr int DMA_PER_PRODUCER = A_DMA / DW + B_Q;  // per stage and DMA wave
+  static_assert(A_DMA % DW == 0 && (B_DMA % DW == 0 || PW_ == 0), "DMA split");
   static_assert(CW % WM == 0, "wave grid");
   static_assert(STAGES >= 2 && (STAGES - 2) * DMA_PER_PRODUCER <= 63, "ring depth vs vmcnt");
   // split ring: B slots, the lead of B over A in stages, LDS elements
   static constexpr int SB = SB_;
   static constexpr bool SPLIT = SB_ > 0;
   static constexpr int B_LEAD = SPLIT ? SB_ - STAGES_ : 0;
-  static constexpr int A_PER = A_DMA / DW, B_PER = B_DMA / DW;  // per stage and producer
+  static constexpr int A_PER = A_DMA / DW, B_PER = B_Q;  // per stage and producer
   static constexpr int RING_ELEMS = SPLIT ? STAGES * A_ELEMS + SB * B_ELEMS : STAGES * STAGE_ELEMS;
   static_assert(!SPLIT || (SB_ > STAGES_ && PW_ > 0 && STAGES_ >= 2), "split ring: producers, B ring deeper");
   static_assert(!SPLIT || (STAGES_ - 1) * A_PER + (SB_ - 1) * B_PER <= 63, "split ring vs vmcnt");
@@ -365,7 +369,7 @@ struct DmaCfg {
 template <class Cfg>
 struct DmaLoader {
   const bf16_t* a[Cfg::A_DMA / Cfg::DW];
-  const bf16_t* b[Cfg::B_DMA / Cfg::DW];
+  const bf16_t* b[Cfg::B_Q];
   int a_kstep = Cfg::BK;
   int b_kstep = Cfg::BK;
   bool b_stream = false;
@@ -428,17 +432,23 @@ __device__ __forceinline__ void dma_issue_a(const DmaLoader<Cfg>& ld, int kt, bf
   for (int q = 0; q < Cfg::A_DMA / Cfg::DW; ++q)
     dma16(ld.a[q] + ka, a_dst + Cfg::RPD * (q * Cfg::DW + part) * Cfg::BK);
 }
+// B instruction of round q for DMA wave `part` (repeats the last one when
+// the waves do not split B evenly).
+template <class Cfg>
+__device__ __forceinline__ int b_inst(int q, int part) {
+  return Cfg::B_DMA % Cfg::DW == 0 ? q * Cfg::DW + part : min(q * Cfg::DW + part, Cfg::B_DMA - 1);
+}
 template <class Cfg>
 __device__ __forceinline__ void dma_issue_b(const DmaLoader<Cfg>& ld, int kt, bf16_t* b_dst, int part) {
   const int64_t kb = (int64_t)kt * ld.b_kstep;
   if (ld.b_stream) {  // wave-uniform
 #pragma unroll
-    for (int q = 0; q < Cfg::B_DMA / Cfg::DW; ++q)
-      dma16_nt(ld.b[q] + kb, b_dst + Cfg::RPD * (q * Cfg::DW + part) * Cfg::BK);
+    for (int q = 0; q < Cfg::B_Q; ++q)
+      dma16_nt(ld.b[q] + kb, b_dst + Cfg::RPD * b_inst<Cfg>(q, part) * Cfg::BK);
   } else {
 #pragma unroll
-    for (int q = 0; q < Cfg::B_DMA / Cfg::DW; ++q)
-      dma16(ld.b[q] + kb, b_dst + Cfg::RPD * (q * Cfg::DW + part) * Cfg::BK);
+    for (int q = 0; q < Cfg::B_Q; ++q)
+      dma16(ld.b[q] + kb, b_dst + Cfg::RPD * b_inst<Cfg>(q, part) * Cfg::BK);
   }
 }
 template <class Cfg>

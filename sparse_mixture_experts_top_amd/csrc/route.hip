@@ -36,8 +36,8 @@ struct RouterProb {
     for (int q = 0; q < Cfg::A_DMA / Cfg::DW; ++q)
       ld.a[q] = x + (int64_t)min(m0 + dma_row<Cfg>(q * Cfg::DW + part), T - 1) * d + ce;
 #pragma unroll
-    for (int q = 0; q < Cfg::B_DMA / Cfg::DW; ++q)
-      ld.b[q] = w + (int64_t)min(n0 + dma_row<Cfg>(q * Cfg::DW + part), E - 1) * d + ce;
+    for (int q = 0; q < Cfg::B_Q; ++q)
+      ld.b[q] = w + (int64_t)min(n0 + dma_row<Cfg>(b_inst<Cfg>(q, part)), E - 1) * d + ce;
   }
 
   __device__ __forceinline__ void epilogue(int item, Acc<Cfg>& acc) const {
@@ -125,9 +125,13 @@ static hipError_t launch_router_bf16(const Ctx& c, int M, int N, int K, const bf
 // Router tile configurations (the router is a dense, compute-bound GEMM, so
 // the large ones run 8 compute waves - two per SIMD, which the MFMA issue
 // rate needs):
+//   wide    256 x 224, 8 symmetric waves (each computes 64 x 112 and issues
+//           DMAs), when there are at least as many such tiles as CUs and
+//           224-wide column tiles waste fewer columns than 256-wide ones
+//           (e.g. T = 16384, E = 896: 4 x 224 columns exactly, where 256-wide
+//           tiles would compute 1024);
 //   huge    256 x 256, 8 symmetric waves (each computes 128 x 64 and issues
-//           DMAs), when there are at least as many such tiles as CUs
-//           (e.g. T = 16384, E = 896);
+//           DMAs), when there are at least as many such tiles as CUs;
 //   large   128 x 256, 8 compute waves of 64 x 64 + 4 producers, when there are at least
 //           as many such tiles as CUs (e.g. T = 16384, E = 896);
 //   medium  128 x 128, 8 compute waves of 64 x 32, when the 128 x 128 tiles
@@ -136,6 +140,7 @@ static hipError_t launch_router_bf16(const Ctx& c, int M, int N, int K, const bf
 #ifndef MOE_ROUTER_STAGES
 #define MOE_ROUTER_STAGES 6
 #endif
+using RouterWide = DmaCfg<256, 224, 2, 4, 8, 0, 64>;
 using RouterHuge = DmaCfg<256, 256, 2, 2, 8, 0, 64>;
 using RouterLarge = DmaCfg<128, 256, MOE_ROUTER_STAGES, 2, 8, 4>;
 using RouterMedium = DmaCfg<128, 128, MOE_ROUTER_STAGES, 2, 8, 4>;
@@ -146,7 +151,10 @@ using RouterSmall = DmaCfg<64, 128, 4, 2, 4, 4>;
 hipError_t launch_router_mnk(const Ctx& c, int M, int N, int K, const bf16_t* xb, const bf16_t* wb,
                              const float* bias, float* logits, bf16_t* out_b) {
   const int mt128 = (M + 127) / 128;
-  if (((M + 255) / 256) * ((N + 255) / 256) >= c.num_cus)
+  const int nt224 = (N + 223) / 224, nt256 = (N + 255) / 256;
+  if (((M + 255) / 256) * nt224 >= c.num_cus && nt224 * 224 < nt256 * 256)
+    return launch_router_bf16<RouterWide>(c, M, N, K, xb, wb, bias, logits, out_b);
+  if (((M + 255) / 256) * nt256 >= c.num_cus)
     return launch_router_bf16<RouterHuge>(c, M, N, K, xb, wb, bias, logits, out_b);
   if (mt128 * ((N + 255) / 256) >= c.num_cus)
     return launch_router_bf16<RouterLarge>(c, M, N, K, xb, wb, bias, logits, out_b);

@@ -37,6 +37,9 @@ SMALL = {
     "tall_shortk_bf16": W("tall_shortk_bf16", T=8192, d=64, E=64, k=2, f=512),
     # the same with four K steps (packed weights need d % 128 == 0)
     "tall_k128_bf16": W("tall_k128_bf16", T=8192, d=128, E=64, k=2, f=512),
+    # router on 256 x 224 tiles (64 x 4 = 256 of them) with a partial last
+    # column tile (880 = 3 x 224 + 208)
+    "router_wide_bf16": W("router_wide_bf16", T=16384, d=128, E=880, k=4, f=64),
 }
 
 
