@@ -190,6 +190,21 @@ moe_status_t moe_dispatch(const moe_shape_t* shape, const int32_t* topk_idx,
                           void* x_perm, int32_t* dropped, void* ws, size_t ws_bytes,
                           moe_stream_t stream);
 
+/* Routing and dispatch as one call ("Day-Level Adaptation and LoRA
+ * Fine-Tuning of Ultra-Large-Scale Sparse MoE Models", §3.3: routing score,
+ * Top-k selection and expert dispatch merged into a few large kernels). The
+ * results equal those of moe_route followed by moe_dispatch with the same
+ * arguments, bit for bit; fewer kernels run: the router GEMM also clears the
+ * per-tile expert histogram in ws, the top-k kernel adds its selections into
+ * it, and the dispatch starts from it (no histogram pass of its own).
+ * Arguments: those of moe_route (x .. prob_sum), then those of moe_dispatch
+ * (counts .. dropped), then the workspace and stream. */
+moe_status_t moe_route_dispatch(const moe_shape_t* shape, const void* x, const void* w_router,
+                                const float* bias, int32_t* topk_idx, float* topk_gate, float* logits,
+                                float* prob_sum, int32_t* counts, int32_t* offsets, int32_t* slot,
+                                int32_t* row_src, float* row_gate, void* x_perm, int32_t* dropped,
+                                void* ws, size_t ws_bytes, moe_stream_t stream);
+
 /* Dispatch with token remapping instead of dropping ("Adapting Ultra-Large
  * MoE Models: Engineering Practices and Optimization Pathways", §3.3: excess
  * tokens are remapped or dropped). With C = capacity (> 0, else

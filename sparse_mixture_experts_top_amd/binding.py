@@ -26,7 +26,7 @@ KERNELS = ["router_gemm", "topk", "prob_reduce", "hist", "scan", "scatter", "cap
            "lora_grad", "gate_bwd", "expert_dgu", "expert_dx", "unpermute", "router_bwd"]
 
 EXPORTED = ["moe_workspace_bytes", "moe_max_rows", "moe_last_error", "moe_route", "moe_route_alt",
-            "moe_route_latent", "moe_dispatch_remap",
+            "moe_route_latent", "moe_dispatch_remap", "moe_route_dispatch",
             "moe_dispatch", "moe_dispatch_noalloc", "moe_expert_gemm", "moe_pack_expert_weights", "moe_expert_gemm_packed",
             "moe_combine", "moe_aux_loss", "moe_lora_bwd", "moe_lora_bwd_packed", "moe_gate_bwd", "moe_expert_bwd",
             "moe_router_bwd", "moe_pack_backward_weights", "moe_expert_bwd_packed", "moe_pack_router_bwd",
@@ -70,6 +70,7 @@ def lib() -> ctypes.CDLL:
     L.moe_route.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_dispatch.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_dispatch_noalloc.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.moe_route_dispatch.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_route_alt.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_route_latent.argtypes = [shp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_dispatch_remap.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -160,6 +161,17 @@ def moe_dispatch(shape, topk_idx, topk_gate, x, counts, offsets, slot, row_src, 
                               _dev(x, dt), _dev(counts, i32), _dev(offsets, i32), _dev(slot, i32),
                               _dev(row_src, i32), _dev(row_gate, torch.float32), _dev(x_perm, dt),
                               _dev(dropped, i32), _dev(ws, torch.uint8), ws.numel(), _stream(stream)))
+
+
+def moe_route_dispatch(shape, x, w_router, bias, topk_idx, topk_gate, logits, prob_sum, counts, offsets, slot,
+                       row_src, row_gate, x_perm, dropped, ws, stream=None):
+    """moe_route then moe_dispatch in one call (fewer kernels, same results)."""
+    dt, i32, f32 = _fdt(shape), torch.int32, torch.float32
+    _check(lib().moe_route_dispatch(ctypes.byref(shape), _dev(x, dt), _dev(w_router, dt), _dev(bias, f32),
+                                    _dev(topk_idx, i32), _dev(topk_gate, f32), _dev(logits, f32),
+                                    _dev(prob_sum, f32), _dev(counts, i32), _dev(offsets, i32), _dev(slot, i32),
+                                    _dev(row_src, i32), _dev(row_gate, f32), _dev(x_perm, dt), _dev(dropped, i32),
+                                    _dev(ws, torch.uint8), ws.numel(), _stream(stream)))
 
 
 def moe_route_alt(shape, x, w_router, bias, topk_idx, topk_gate, alt_idx, logits, prob_sum, ws, stream=None):

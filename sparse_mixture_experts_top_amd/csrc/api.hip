@@ -400,6 +400,43 @@ moe_status_t moe_dispatch(const moe_shape_t* shape, const int32_t* topk_idx,
                     "dispatch");
 }
 
+moe_status_t moe_route_dispatch(const moe_shape_t* shape, const void* x, const void* w_router,
+                                const float* bias, int32_t* topk_idx, float* topk_gate, float* logits,
+                                float* prob_sum, int32_t* counts, int32_t* offsets, int32_t* slot,
+                                int32_t* row_src, float* row_gate, void* x_perm, int32_t* dropped,
+                                void* ws, size_t ws_bytes, moe_stream_t stream) {
+  moe_status_t st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  const moe_shape_t& s = *shape;
+  const bool rows = max_rows(s) > 0;
+  MOE_REQUIRE_IF(s.T > 0, x, "x");
+  MOE_REQUIRE(w_router, "w_router");
+  MOE_REQUIRE_IF(s.T > 0, topk_idx, "topk_idx");
+  MOE_REQUIRE_IF(s.T > 0, topk_gate, "topk_gate");
+  MOE_REQUIRE(counts, "counts");
+  MOE_REQUIRE(offsets, "offsets");
+  MOE_REQUIRE_IF(s.T > 0, slot, "slot");
+  MOE_REQUIRE_IF(rows, row_src, "row_src");
+  MOE_REQUIRE_IF(rows, row_gate, "row_gate");
+  if ((st = check_ws(s, 0, ws, ws_bytes)) != MOE_OK) return st;
+  Ctx c;
+  if ((st = make_ctx(stream, &c)) != MOE_OK) return st;
+  const Workspace w = carve_workspace(s, 0, ws);
+  float* lg = logits ? logits : w.logits;
+  const int64_t hist_n = (int64_t)((s.T + kTokTile - 1) / kTokTile) * s.E;
+  if (s.T > 0) {
+    if ((st = hip_status(launch_router(c, s, x, w_router, bias, lg, w.tile_counts, hist_n), "router GEMM")) !=
+        MOE_OK)
+      return st;
+  }
+  if ((st = hip_status(launch_topk(c, s, lg, topk_idx, topk_gate, w.prob_part, prob_sum, nullptr, w.tile_counts),
+                       "top-k")) != MOE_OK)
+    return st;
+  return hip_status(launch_dispatch(c, s, w, topk_idx, topk_gate, x, counts, offsets, slot, row_src, row_gate,
+                                    x_perm, dropped, true),
+                    "dispatch");
+}
+
 moe_status_t moe_dispatch_noalloc(const moe_shape_t* shape, const int32_t* topk_idx,
                                   const float* topk_gate, const void* x, int32_t* counts,
                                   int32_t* offsets, int32_t* slot, int32_t* row_src, float* row_gate,

@@ -201,12 +201,18 @@ int gemm_max_tiles(const moe_shape_t& s);
 // ------------------------------------------------------ kernel launchers ---
 // Each returns hipSuccess or the launch error.
 
+// zero / zero_n: an int32 buffer the router kernel clears on the side (the
+// per-tile expert histogram that the top-k kernel then fills).
 hipError_t launch_router(const Ctx& c, const moe_shape_t& s, const void* x, const void* w,
-                         const float* bias, float* logits);
+                         const float* bias, float* logits, int32_t* zero = nullptr, int64_t zero_n = 0);
 hipError_t launch_router_mnk(const Ctx& c, int M, int N, int K, const bf16_t* x, const bf16_t* w,
-                             const float* bias, float* logits, bf16_t* out_b);
+                             const float* bias, float* logits, bf16_t* out_b, int32_t* zero = nullptr,
+                             int64_t zero_n = 0);
+// hist: per 32-token tile expert counts [ceil(T/32), E], cleared beforehand,
+// to which each token adds its k selections.
 hipError_t launch_topk(const Ctx& c, const moe_shape_t& s, const float* logits, int32_t* idx,
-                       float* gate, float* prob_part, float* prob_sum, int32_t* alt = nullptr);
+                       float* gate, float* prob_part, float* prob_sum, int32_t* alt = nullptr,
+                       int32_t* hist = nullptr);
 hipError_t launch_aux(const Ctx& c, const moe_shape_t& s, const int32_t* counts,
                       const float* prob_sum, float coef, float* out);
 
@@ -217,7 +223,7 @@ hipError_t launch_dispatch_remap(const Ctx& c, const moe_shape_t& s, const Works
 hipError_t launch_dispatch(const Ctx& c, const moe_shape_t& s, const Workspace& ws,
                            const int32_t* idx, const float* gate, const void* x, int32_t* counts,
                            int32_t* offsets, int32_t* slot, int32_t* row_src, float* row_gate,
-                           void* x_perm, int32_t* dropped);
+                           void* x_perm, int32_t* dropped, bool hist_done = false);
 
 struct LoraArgs {
   int r;

@@ -14,7 +14,9 @@
 // form a single 32-bit mask; T = 4096 gives 128 tiles, enough workgroups to
 // spread over the GPU.
 //
-//   K3 hist       per tile: LDS histogram over E -> tile_counts
+//   K3 hist       per tile: LDS histogram over E -> tile_counts (or the
+//                 top-k kernel adds its selections into them, when routing
+//                 and dispatch run as one call)
 //   K4 tile scan  per expert (16 per workgroup, 16 threads splitting the
 //                 tiles): running sum over tiles -> tile_base, counts
 //   K6 scatter    per tile: each workgroup first scans the per-expert kept
@@ -600,11 +602,11 @@ __global__ __launch_bounds__(256) void dispatch_gather_f32(const float* __restri
 hipError_t launch_dispatch(const Ctx& c, const moe_shape_t& s, const Workspace& ws,
                            const int32_t* idx, const float* gate, const void* x, int32_t* counts,
                            int32_t* offsets, int32_t* slot, int32_t* row_src, float* row_gate,
-                           void* x_perm, int32_t* dropped) {
+                           void* x_perm, int32_t* dropped, bool hist_done) {
   const int ntiles = (s.T + kTokTile - 1) / kTokTile;
   const int L = s.e_hi - s.e_lo;
   hipError_t err;
-  if (ntiles > 0) {
+  if (ntiles > 0 && !hist_done) {  // else the top-k kernel filled tile_counts
     TimedLaunch tl(MOE_K_HIST, c.stream);
     hipLaunchKernelGGL(dispatch_hist, dim3(ntiles), dim3(256), 0, c.stream, idx, s.T, s.k, s.E,
                        ws.tile_counts);

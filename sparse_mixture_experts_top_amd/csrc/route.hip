@@ -26,6 +26,8 @@ struct RouterProb {
   float* logits;
   int T, d, E, nt;
   bf16_t* out_b = nullptr;
+  int32_t* zero = nullptr;  // cleared by the kernel on the side (zero_n entries)
+  int64_t zero_n = 0;
 
   __device__ __forceinline__ int rows(int item) const { return min(Cfg::BM, T - (item / nt) * Cfg::BM); }
 
@@ -84,12 +86,21 @@ struct RouterProb {
   }
 };
 
+// Grid-stride clear of n int32 (16-byte stores; the buffer is 16-byte aligned).
+__device__ __forceinline__ void clear_i32(int32_t* p, int64_t n) {
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t nthr = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = tid; i < n / 4; i += nthr) reinterpret_cast<int4*>(p)[i] = make_int4(0, 0, 0, 0);
+  for (int64_t i = (n / 4) * 4 + tid; i < n; i += nthr) p[i] = 0;
+}
+
 template <class Cfg>
 __global__ __launch_bounds__(Cfg::THREADS, Cfg::WAVES_PER_SIMD) void router_gemm_bf16(RouterProb<Cfg> pb, int items) {
   if constexpr (Cfg::PW == 0)
     persistent_gemm_sym<Cfg>(pb, items, pb.d / Cfg::BK);
   else
     persistent_gemm_dma<Cfg>(pb, items, pb.d / Cfg::BK);
+  if (pb.zero) clear_i32(pb.zero, pb.zero_n);
 }
 
 // fp32: one thread per logit, plain dot product (small parity workloads).
@@ -97,8 +108,9 @@ __global__ __launch_bounds__(256) void router_gemm_f32(const float* __restrict__
                                                        const float* __restrict__ w,
                                                        const float* __restrict__ bias,
                                                        float* __restrict__ logits, int T, int d,
-                                                       int E) {
+                                                       int E, int32_t* __restrict__ zero, int64_t zero_n) {
   const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (id < zero_n) zero[id] = 0;  // zero_n <= T * E
   if (id >= (int64_t)T * E) return;
   const int t = (int)(id / E), e = (int)(id % E);
   const float* xr = x + (int64_t)t * d;
@@ -110,13 +122,16 @@ __global__ __launch_bounds__(256) void router_gemm_f32(const float* __restrict__
 
 template <class Cfg>
 static hipError_t launch_router_bf16(const Ctx& c, int M, int N, int K, const bf16_t* x, const bf16_t* w,
-                                     const float* bias, float* logits, bf16_t* out_b) {
+                                     const float* bias, float* logits, bf16_t* out_b, int32_t* zero,
+                                     int64_t zero_n) {
   const int mt = (M + Cfg::BM - 1) / Cfg::BM, nt = (N + Cfg::BN - 1) / Cfg::BN;
   const int items = mt * nt;
   // one workgroup per CU (the workgroups are sized to fill one), a multiple of 8 (XCDs)
   const int grid = std::min(((items + 7) / 8) * 8, c.num_cus);
   RouterProb<Cfg> pb{x, w, bias, logits, M, K, N, nt};
   pb.out_b = out_b;
+  pb.zero = zero;
+  pb.zero_n = zero_n;
   TimedLaunch tl(MOE_K_ROUTER_GEMM, c.stream);
   hipLaunchKernelGGL(router_gemm_bf16<Cfg>, dim3(grid), dim3(Cfg::THREADS), 0, c.stream, pb, items);
   return hipGetLastError();
@@ -149,28 +164,29 @@ using RouterSmall = DmaCfg<64, 128, 4, 2, 4, 4>;
 // bf16 [M, K] x [N, K]^T on the router engine: fp32 out (+ bias) or, with
 // out_b, bf16 out. K % 64 == 0.
 hipError_t launch_router_mnk(const Ctx& c, int M, int N, int K, const bf16_t* xb, const bf16_t* wb,
-                             const float* bias, float* logits, bf16_t* out_b) {
+                             const float* bias, float* logits, bf16_t* out_b, int32_t* zero, int64_t zero_n) {
   const int mt128 = (M + 127) / 128;
   const int nt224 = (N + 223) / 224, nt256 = (N + 255) / 256;
   if (((M + 255) / 256) * nt224 >= c.num_cus && nt224 * 224 < nt256 * 256)
-    return launch_router_bf16<RouterWide>(c, M, N, K, xb, wb, bias, logits, out_b);
+    return launch_router_bf16<RouterWide>(c, M, N, K, xb, wb, bias, logits, out_b, zero, zero_n);
   if (((M + 255) / 256) * nt256 >= c.num_cus)
-    return launch_router_bf16<RouterHuge>(c, M, N, K, xb, wb, bias, logits, out_b);
+    return launch_router_bf16<RouterHuge>(c, M, N, K, xb, wb, bias, logits, out_b, zero, zero_n);
   if (mt128 * ((N + 255) / 256) >= c.num_cus)
-    return launch_router_bf16<RouterLarge>(c, M, N, K, xb, wb, bias, logits, out_b);
+    return launch_router_bf16<RouterLarge>(c, M, N, K, xb, wb, bias, logits, out_b, zero, zero_n);
   if (2 * mt128 * ((N + 127) / 128) >= c.num_cus)
-    return launch_router_bf16<RouterMedium>(c, M, N, K, xb, wb, bias, logits, out_b);
-  return launch_router_bf16<RouterSmall>(c, M, N, K, xb, wb, bias, logits, out_b);
+    return launch_router_bf16<RouterMedium>(c, M, N, K, xb, wb, bias, logits, out_b, zero, zero_n);
+  return launch_router_bf16<RouterSmall>(c, M, N, K, xb, wb, bias, logits, out_b, zero, zero_n);
 }
 
 hipError_t launch_router(const Ctx& c, const moe_shape_t& s, const void* x, const void* w,
-                         const float* bias, float* logits) {
+                         const float* bias, float* logits, int32_t* zero, int64_t zero_n) {
   if (s.dtype == MOE_BF16)
-    return launch_router_mnk(c, s.T, s.E, s.d, (const bf16_t*)x, (const bf16_t*)w, bias, logits, nullptr);
+    return launch_router_mnk(c, s.T, s.E, s.d, (const bf16_t*)x, (const bf16_t*)w, bias, logits, nullptr, zero,
+                             zero_n);
   const int64_t n = (int64_t)s.T * s.E;
   TimedLaunch tl(MOE_K_ROUTER_GEMM, c.stream);
   hipLaunchKernelGGL(router_gemm_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, c.stream,
-                     (const float*)x, (const float*)w, bias, logits, s.T, s.d, s.E);
+                     (const float*)x, (const float*)w, bias, logits, s.T, s.d, s.E, zero, zero_n);
   return hipGetLastError();
 }
 
@@ -216,13 +232,17 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 // the number of alternates: picks kg .. k-1 (the experts ranked next) go to
 // alt_out [T, k - kg] and take no gate. With prob_part, the wave also sums the
 // full softmax of its tokens per expert; the block's waves are added in a
-// fixed order into prob_part[block, E].
+// fixed order into prob_part[block, E]. With hist, each of the first kg
+// picks adds one to hist[t / 32, expert] (integer atomics: the counts do not
+// depend on the order the waves run in), the per-tile expert histogram the
+// dispatch's tile scan starts from.
 template <int EPL, int TPW>
 __global__ __launch_bounds__(256) void topk_softmax(const float* __restrict__ logits, int T, int E,
                                                     int k, int kg, int32_t* __restrict__ idx_out,
                                                     float* __restrict__ gate_out,
                                                     int32_t* __restrict__ alt_out,
-                                                    float* __restrict__ prob_part) {
+                                                    float* __restrict__ prob_part,
+                                                    int32_t* __restrict__ hist) {
   __shared__ uint64_t cand[4][64];
   __shared__ uint64_t sel[4][32];
   __shared__ float red[4][EPL * 64];
@@ -309,6 +329,7 @@ __global__ __launch_bounds__(256) void topk_softmax(const float* __restrict__ lo
     if (lane < kg) {
       idx_out[(int64_t)t * kg + lane] = my_idx;
       gate_out[(int64_t)t * kg + lane] = ex / den;
+      if (hist) atomicAdd(hist + (int64_t)(t / kTokTile) * E + my_idx, 1);
     } else if (lane < k) {
       alt_out[(int64_t)t * (k - kg) + (lane - kg)] = my_idx;
     }
@@ -368,7 +389,7 @@ __global__ __launch_bounds__(1024) void prob_reduce(const float* __restrict__ pa
 }
 
 hipError_t launch_topk(const Ctx& c, const moe_shape_t& s, const float* logits, int32_t* idx,
-                       float* gate, float* prob_part, float* prob_sum, int32_t* alt) {
+                       float* gate, float* prob_part, float* prob_sum, int32_t* alt, int32_t* hist) {
   // with alt: k alternates after the k selected experts (2k picks in all)
   const int ksel = alt ? 2 * s.k : s.k;
   // one token per wave; with the softmax sums requested, kTopkTokPerWaveProb tokens per wave
@@ -382,10 +403,10 @@ hipError_t launch_topk(const Ctx& c, const moe_shape_t& s, const float* logits, 
 #define MOE_TOPK(N)                                                                                  \
   if (prob_sum)                                                                                      \
     hipLaunchKernelGGL((topk_softmax<N, kTopkTokPerWaveProb>), dim3(nblk), dim3(256), 0, c.stream,    \
-                       logits, s.T, s.E, ksel, s.k, idx, gate, alt, part);                           \
+                       logits, s.T, s.E, ksel, s.k, idx, gate, alt, part, hist);                     \
   else                                                                                               \
     hipLaunchKernelGGL((topk_softmax<N, 1>), dim3(nblk), dim3(256), 0, c.stream, logits, s.T, s.E,    \
-                       ksel, s.k, idx, gate, alt, part)
+                       ksel, s.k, idx, gate, alt, part, hist)
     if (epl <= 1) MOE_TOPK(1);
     else if (epl <= 2) MOE_TOPK(2);
     else if (epl <= 4) MOE_TOPK(4);

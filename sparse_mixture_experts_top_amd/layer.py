@@ -109,26 +109,32 @@ def variant_buffers(w: Workload, dev, device: str = "cuda") -> Optional[Variant]
 
 
 def forward(b: Buffers, x, w_router, bias, w_gate, w_up, w_down, lora=None, stream=None,
-            packed=None, variant: Optional[Variant] = None) -> None:
+            packed=None, variant: Optional[Variant] = None, fused_route: bool = True) -> None:
     """route -> dispatch -> expert GEMM -> combine; results stay in ``b``.
     packed: (gu_packed, down_packed) from pack_weights, used instead of the
-    row-major expert weights. variant: remapped dispatch or latent routing."""
+    row-major expert weights. variant: remapped dispatch or latent routing.
+    fused_route: the plain routing and dispatch as one call
+    (moe_route_dispatch) instead of moe_route + moe_dispatch."""
     s = b.shape
     v = variant or Variant()
-    if v.w_latent is not None:
-        B.moe_route_latent(s, v.z.shape[1], x, v.w_latent, w_router, bias, v.z, b.topk_idx, b.topk_gate,
-                           b.logits, b.prob_sum, b.ws, stream)
-    elif v.alt is not None:
-        B.moe_route_alt(s, x, w_router, bias, b.topk_idx, b.topk_gate, v.alt, b.logits, b.prob_sum, b.ws,
-                        stream)
+    if fused_route and v.w_latent is None and v.alt is None:
+        B.moe_route_dispatch(s, x, w_router, bias, b.topk_idx, b.topk_gate, b.logits, b.prob_sum, b.counts,
+                             b.offsets, b.slot, b.row_src, b.row_gate, b.x_perm, b.dropped, b.ws, stream)
     else:
-        B.moe_route(s, x, w_router, bias, b.topk_idx, b.topk_gate, b.logits, b.prob_sum, b.ws, stream)
-    if v.alt is not None:
-        B.moe_dispatch_remap(s, b.topk_idx, b.topk_gate, v.alt, x, b.counts, b.offsets, b.slot, b.row_src,
-                             b.row_gate, b.x_perm, v.moved, b.dropped, b.ws, stream)
-    else:
-        B.moe_dispatch(s, b.topk_idx, b.topk_gate, x, b.counts, b.offsets, b.slot, b.row_src,
-                       b.row_gate, b.x_perm, b.dropped, b.ws, stream)
+        if v.w_latent is not None:
+            B.moe_route_latent(s, v.z.shape[1], x, v.w_latent, w_router, bias, v.z, b.topk_idx, b.topk_gate,
+                               b.logits, b.prob_sum, b.ws, stream)
+        elif v.alt is not None:
+            B.moe_route_alt(s, x, w_router, bias, b.topk_idx, b.topk_gate, v.alt, b.logits, b.prob_sum, b.ws,
+                            stream)
+        else:
+            B.moe_route(s, x, w_router, bias, b.topk_idx, b.topk_gate, b.logits, b.prob_sum, b.ws, stream)
+        if v.alt is not None:
+            B.moe_dispatch_remap(s, b.topk_idx, b.topk_gate, v.alt, x, b.counts, b.offsets, b.slot, b.row_src,
+                                 b.row_gate, b.x_perm, v.moved, b.dropped, b.ws, stream)
+        else:
+            B.moe_dispatch(s, b.topk_idx, b.topk_gate, x, b.counts, b.offsets, b.slot, b.row_src,
+                           b.row_gate, b.x_perm, b.dropped, b.ws, stream)
     xr, src = x_rows(b, x)
     if packed is not None:
         B.moe_expert_gemm_packed(s, xr, src, b.offsets, packed[0], packed[1], lora, b.act_save,

@@ -163,6 +163,43 @@ def test_empty_batch():
     assert (buf.counts == 0).all() and (buf.offsets == 0).all() and (buf.prob_sum == 0).all()
 
 
+def _bits(t):
+    return host(t.view(torch.int32) if t.dtype == torch.float32 else t.view(torch.int16))
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "ragged_bf16", "local_bf16", "capacity_bf16", "capacity_f32",
+                                  "k1_bf16", "router_wide_bf16"])
+def test_route_dispatch_fused_equals_separate(name):
+    """moe_route_dispatch (histogram folded into the top-k kernel) against
+    moe_route + moe_dispatch: every output bitwise equal, on two calls in a
+    row on the same workspace (the histogram is cleared by each call)."""
+    w = SMALL[name]
+    say(f"[case {name}] fused route+dispatch vs separate")
+    inp = generate(w, seed=3)
+    dev = upload(inp)
+    s = layer.shape_of(w)
+    sep = layer.alloc(s, logits=True, prob=True, x_perm=True)
+    fus = layer.alloc(s, logits=True, prob=True, x_perm=True)
+    args = (dev["x"], dev["w_router"], dev.get("bias"))
+    B.moe_route(s, *args, sep.topk_idx, sep.topk_gate, sep.logits, sep.prob_sum, sep.ws)
+    B.moe_dispatch(s, sep.topk_idx, sep.topk_gate, dev["x"], sep.counts, sep.offsets, sep.slot, sep.row_src,
+                   sep.row_gate, sep.x_perm, sep.dropped, sep.ws)
+    for rep in range(2):
+        fus.ws.fill_(0x5A if rep else 0)
+        B.moe_route_dispatch(s, *args, fus.topk_idx, fus.topk_gate, fus.logits, fus.prob_sum, fus.counts,
+                             fus.offsets, fus.slot, fus.row_src, fus.row_gate, fus.x_perm, fus.dropped, fus.ws)
+        torch.cuda.synchronize()
+        R = int(host(sep.offsets)[-1])
+        assert int(host(fus.offsets)[-1]) == R
+        for n in ("topk_idx", "counts", "offsets", "slot", "dropped"):
+            assert (host(getattr(fus, n)) == host(getattr(sep, n))).all(), n
+        for n in ("topk_gate", "logits", "prob_sum"):
+            assert (_bits(getattr(fus, n)) == _bits(getattr(sep, n))).all(), n
+        assert (host(fus.row_src[:R]) == host(sep.row_src[:R])).all()
+        assert (_bits(fus.row_gate[:R]) == _bits(sep.row_gate[:R])).all()
+        assert (_bits(fus.x_perm[:R]) == _bits(sep.x_perm[:R])).all()
+
+
 def test_no_local_assignment():
     """Every token prefers experts 0..3 (large bias) while the local range is
     12..15: no rows, y is all zero, slots all -1."""
