@@ -372,7 +372,9 @@ def lora_step_bench(args, w, inp, dev, shape, steps, warmup, cpu):
     L, r, d, f = w.L, w.lora_r, w.d, w.f
     buf = layer.alloc(shape, lora_r=r, prob=True, act_save=True)
     packed = layer.pack_weights(shape, dev["w_gate"], dev["w_up"], dev["w_down"])
-    lora = B.make_lora(r, w.lora_alpha, dev["a_up"], dev["b_up"], dev["a_down"], dev["b_down"])
+    # the forward keeps the rows' rank-r projections for the backward
+    z_save = torch.empty((2, max(B.moe_max_rows(shape), 1), r), dtype=torch.float32, device="cuda")
+    lora = B.make_lora(r, w.lora_alpha, dev["a_up"], dev["b_up"], dev["a_down"], dev["b_down"], z_save)
     grads = [torch.empty(sz, dtype=torch.float32, device="cuda")
              for sz in ((L, r, d), (L, f, r), (L, r, f), (L, d, r))]
     # W_d^T packed once for the adapter backward's dH product (W_d is frozen)

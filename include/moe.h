@@ -95,7 +95,14 @@ typedef struct {
  * Fine-Tuning: A Full-Stack Engineering Guide", §3). bf16 only, 1 <= r <= 64.
  *   a_up   [L, r, d]   b_up   [L, f, r]     (U  += s (X A_up^T) B_up^T)
  *   a_down [L, r, f]   b_down [L, d, r]     (O  += s (H A_down^T) B_down^T)
- * with s = alpha / r. */
+ * with s = alpha / r.
+ *   z_save [2, Rmax, r] f32 | NULL  (Rmax = moe_max_rows): the rank-r
+ *          projections of the rows, Z_u = X A_up^T in z_save[0] and
+ *          Z_d = H A_down^T in z_save[1]. moe_expert_gemm(_packed) writes
+ *          them; moe_lora_bwd(_packed) then reads them instead of projecting
+ *          X and H again (the caller keeps the buffer, the rows and the
+ *          adapters unchanged between the two calls). NULL: the backward
+ *          recomputes them. */
 typedef struct {
   int32_t r;
   float alpha;
@@ -103,6 +110,7 @@ typedef struct {
   const void* b_up;
   const void* a_down;
   const void* b_down;
+  float* z_save;
 } moe_lora_t;
 
 /* [host] Scratch bytes every entry point below needs for this shape

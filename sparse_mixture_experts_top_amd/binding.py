@@ -41,7 +41,8 @@ class MoeShape(ctypes.Structure):
 
 class MoeLora(ctypes.Structure):
     _fields_ = [("r", ctypes.c_int32), ("alpha", ctypes.c_float), ("a_up", ctypes.c_void_p),
-                ("b_up", ctypes.c_void_p), ("a_down", ctypes.c_void_p), ("b_down", ctypes.c_void_p)]
+                ("b_up", ctypes.c_void_p), ("a_down", ctypes.c_void_p), ("b_down", ctypes.c_void_p),
+                ("z_save", ctypes.c_void_p)]
 
 
 class MoeError(RuntimeError):
@@ -110,10 +111,13 @@ def make_shape(T, d, E, k, f, e_lo=0, e_hi=None, capacity=0, dtype=MOE_BF16) -> 
     return MoeShape(T, d, E, k, f, e_lo, E if e_hi is None else e_hi, capacity, dtype)
 
 
-def make_lora(r: int, alpha: float, a_up, b_up, a_down, b_down) -> MoeLora:
+def make_lora(r: int, alpha: float, a_up, b_up, a_down, b_down, z_save=None) -> MoeLora:
+    """z_save: optional [2, Rmax, r] float32 buffer for the row projections kept
+    from the forward to the backward."""
     for t in (a_up, b_up, a_down, b_down):
         _dev(t, torch.bfloat16)
-    return MoeLora(r, alpha, a_up.data_ptr(), b_up.data_ptr(), a_down.data_ptr(), b_down.data_ptr())
+    return MoeLora(r, alpha, a_up.data_ptr(), b_up.data_ptr(), a_down.data_ptr(), b_down.data_ptr(),
+                   _dev(z_save, torch.float32))
 
 
 def _dev(t: Optional[torch.Tensor], dtype=None):

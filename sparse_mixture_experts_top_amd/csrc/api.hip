@@ -100,6 +100,19 @@ static moe_status_t check_shape(const moe_shape_t* s) {
   return MOE_OK;
 }
 
+static LoraArgs lora_args(const moe_lora_t* lo) {
+  LoraArgs la{};
+  if (!lo) return la;
+  la.r = lo->r;
+  la.scale = lo->alpha / (float)lo->r;
+  la.a_up = static_cast<const bf16_t*>(lo->a_up);
+  la.b_up = static_cast<const bf16_t*>(lo->b_up);
+  la.a_down = static_cast<const bf16_t*>(lo->a_down);
+  la.b_down = static_cast<const bf16_t*>(lo->b_down);
+  la.z_save = lo->z_save;
+  return la;
+}
+
 static moe_status_t check_lora(const moe_shape_t& s, const moe_lora_t* lo) {
   if (!lo) return MOE_OK;
   if (lo->r < 1) return fail(MOE_ERR_INVALID_ARG, "LoRA rank must be >= 1");
@@ -489,15 +502,7 @@ moe_status_t moe_expert_gemm(const moe_shape_t* shape, const void* x, const int3
   Ctx c;
   if ((st = make_ctx(stream, &c)) != MOE_OK) return st;
   const Workspace w = carve_workspace(s, r, ws);
-  LoraArgs la{};
-  if (lora) {
-    la.r = lora->r;
-    la.scale = lora->alpha / (float)lora->r;
-    la.a_up = static_cast<const bf16_t*>(lora->a_up);
-    la.b_up = static_cast<const bf16_t*>(lora->b_up);
-    la.a_down = static_cast<const bf16_t*>(lora->a_down);
-    la.b_down = static_cast<const bf16_t*>(lora->b_down);
-  }
+  const LoraArgs la = lora_args(lora);
   return hip_status(launch_expert_gemm(c, s, w, x, row_src, offsets, nullptr, nullptr, w_gate, w_up, w_down,
                                        lora ? &la : nullptr, act_save, y_perm),
                     "expert GEMM");
@@ -545,15 +550,7 @@ moe_status_t moe_expert_gemm_packed(const moe_shape_t* shape, const void* x, con
   Ctx c;
   if ((st = make_ctx(stream, &c)) != MOE_OK) return st;
   const Workspace w = carve_workspace(s, r, ws);
-  LoraArgs la{};
-  if (lora) {
-    la.r = lora->r;
-    la.scale = lora->alpha / (float)lora->r;
-    la.a_up = static_cast<const bf16_t*>(lora->a_up);
-    la.b_up = static_cast<const bf16_t*>(lora->b_up);
-    la.a_down = static_cast<const bf16_t*>(lora->a_down);
-    la.b_down = static_cast<const bf16_t*>(lora->b_down);
-  }
+  const LoraArgs la = lora_args(lora);
   return hip_status(launch_expert_gemm(c, s, w, x, row_src, offsets, gu_packed, down_packed, nullptr,
                                        nullptr, nullptr, lora ? &la : nullptr, act_save, y_perm),
                     "expert GEMM (packed)");
@@ -612,9 +609,7 @@ moe_status_t moe_lora_bwd(const moe_shape_t* shape, const moe_lora_t* lora, cons
   Ctx c;
   if ((st = make_ctx(stream, &c)) != MOE_OK) return st;
   const Workspace w = carve_workspace(s, lora->r, ws);
-  LoraArgs la{lora->r, lora->alpha / (float)lora->r, static_cast<const bf16_t*>(lora->a_up),
-              static_cast<const bf16_t*>(lora->b_up), static_cast<const bf16_t*>(lora->a_down),
-              static_cast<const bf16_t*>(lora->b_down)};
+  const LoraArgs la = lora_args(lora);
   return hip_status(
       launch_lora_bwd(c, s, w, la, static_cast<const bf16_t*>(dy), offsets, row_src, row_gate,
                       static_cast<const bf16_t*>(x), x_src, static_cast<const bf16_t*>(act_save),
@@ -650,9 +645,7 @@ moe_status_t moe_lora_bwd_packed(const moe_shape_t* shape, const moe_lora_t* lor
   Ctx c;
   if ((st = make_ctx(stream, &c)) != MOE_OK) return st;
   const Workspace w = carve_workspace(s, lora->r, ws);
-  LoraArgs la{lora->r, lora->alpha / (float)lora->r, static_cast<const bf16_t*>(lora->a_up),
-              static_cast<const bf16_t*>(lora->b_up), static_cast<const bf16_t*>(lora->a_down),
-              static_cast<const bf16_t*>(lora->b_down)};
+  const LoraArgs la = lora_args(lora);
   return hip_status(
       launch_lora_bwd(c, s, w, la, static_cast<const bf16_t*>(dy), offsets, row_src, row_gate,
                       static_cast<const bf16_t*>(x), x_src, static_cast<const bf16_t*>(act_save),
@@ -708,15 +701,7 @@ moe_status_t moe_expert_bwd(const moe_shape_t* shape, const moe_lora_t* lora, co
   Ctx c;
   if ((st = make_ctx(stream, &c)) != MOE_OK) return st;
   const Workspace w = carve_workspace(s, lora ? lora->r : 0, ws);
-  LoraArgs la{};
-  if (lora) {
-    la.r = lora->r;
-    la.scale = lora->alpha / (float)lora->r;
-    la.a_up = static_cast<const bf16_t*>(lora->a_up);
-    la.b_up = static_cast<const bf16_t*>(lora->b_up);
-    la.a_down = static_cast<const bf16_t*>(lora->a_down);
-    la.b_down = static_cast<const bf16_t*>(lora->b_down);
-  }
+  const LoraArgs la = lora_args(lora);
   return hip_status(launch_expert_bwd(c, s, w, lora ? &la : nullptr, dy, offsets, row_src, row_gate, slot,
                                       act_save, w_gate, w_up, w_down, nullptr, nullptr, dgu, dx_rows, dx),
                     "expert backward");
@@ -765,15 +750,7 @@ moe_status_t moe_expert_bwd_packed(const moe_shape_t* shape, const moe_lora_t* l
   Ctx c;
   if ((st = make_ctx(stream, &c)) != MOE_OK) return st;
   const Workspace w = carve_workspace(s, lora ? lora->r : 0, ws);
-  LoraArgs la{};
-  if (lora) {
-    la.r = lora->r;
-    la.scale = lora->alpha / (float)lora->r;
-    la.a_up = static_cast<const bf16_t*>(lora->a_up);
-    la.b_up = static_cast<const bf16_t*>(lora->b_up);
-    la.a_down = static_cast<const bf16_t*>(lora->a_down);
-    la.b_down = static_cast<const bf16_t*>(lora->b_down);
-  }
+  const LoraArgs la = lora_args(lora);
   // dx null: the per-token sum is left to moe_router_bwd_unpermute_packed
   return hip_status(launch_expert_bwd(c, s, w, lora ? &la : nullptr, dy, offsets, row_src, row_gate, slot,
                                       act_save, nullptr, nullptr, nullptr, dgu_packed, dx_packed, dgu, dx_rows,

@@ -232,6 +232,7 @@ struct LoraArgs {
   const bf16_t* b_up;
   const bf16_t* a_down;
   const bf16_t* b_down;
+  float* z_save;  // [2, Rmax, r] f32 | NULL: Z_u then Z_d, kept from forward to backward
 };
 
 hipError_t launch_expert_gemm(const Ctx& c, const moe_shape_t& s, const Workspace& ws,

@@ -990,12 +990,15 @@ hipError_t launch_expert_gemm(const Ctx& c, const moe_shape_t& s, const Workspac
   // (the projection's matrix-core path applies: d, f % 32 == 0), else in
   // the epilogues
   const int lora_mode = !lora ? 0 : (lora->r == 16 && s.d % 32 == 0 && s.f % 32 == 0 && ws.zx) ? 2 : 1;
+  // fp32 Z_u: kept for the backward in the caller's z_save, else in ws
+  // (needed there only by the epilogue form)
+  float* zu = lora && lora->z_save ? lora->z_save : ws.zu;
   if (lora) {
     err = lora_mode == 2
               ? launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, xr, s.d, row_src, nullptr, s.d, lora->a_up, true,
-                                            lora->r, nullptr, nullptr, ws.zx, lora->scale)
+                                            lora->r, lora->z_save ? zu : nullptr, nullptr, ws.zx, lora->scale)
               : launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, xr, s.d, row_src, nullptr, s.d, lora->a_up, true,
-                                            lora->r, ws.zu);
+                                            lora->r, zu);
     if (err != hipSuccess) return err;
   }
   const int64_t tk = (int64_t)s.T * s.k;
@@ -1018,6 +1021,8 @@ hipError_t launch_grouped_bf16(const Ctx& c, const moe_shape_t& s, const Workspa
   const int L = s.e_hi - s.e_lo;
   const int64_t rmax = max_rows(s);
   const int grid = c.num_cus;  // one workgroup per CU (see mfma_tile.h)
+  float* zu = lora && lora->z_save ? lora->z_save : ws.zu;
+  float* zd = lora && lora->z_save ? lora->z_save + rmax * lora->r : ws.zd;
   if ((err = launch_row_tiles(c, offsets, L, max_tiles, ws.gemm_tiles, Cfg::BM)) != hipSuccess) return err;
   // Weight tiles are fetched with the streaming hint when an expert's rows are
   // expected to fit one row tile (the capacity, or the even share T k / E
@@ -1031,7 +1036,7 @@ hipError_t launch_grouped_bf16(const Ctx& c, const moe_shape_t& s, const Workspa
     P pb{xr, row_src, offsets, ws.gemm_tiles, (const bf16_t*)w_gate,
          (const bf16_t*)w_up, (const bf16_t*)gu_packed, s.d, s.f,
          (s.f + P::HALF - 1) / P::HALF, s.e_hi - s.e_lo,
-         lora ? ws.zu : nullptr, lora ? lora->b_up : nullptr, lora ? lora->r : 0,
+         lora ? zu : nullptr, lora ? lora->b_up : nullptr, lora ? lora->r : 0,
          lora ? lora->scale : 0.f, (bf16_t*)ws.hbuf, (bf16_t*)act_save};
     pb.zx = ws.zx;
     pb.stream_b = stream_b;
@@ -1045,17 +1050,17 @@ hipError_t launch_grouped_bf16(const Ctx& c, const moe_shape_t& s, const Workspa
   if (err != hipSuccess) return err;
   if (lora) {
     err = lora_mode == 2 ? launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, (const bf16_t*)ws.hbuf, s.f, nullptr,
-                                                       nullptr, s.f, lora->a_down, true, lora->r, nullptr,
-                                                       nullptr, ws.zx, lora->scale)
+                                                       nullptr, s.f, lora->a_down, true, lora->r,
+                                                       lora->z_save ? zd : nullptr, nullptr, ws.zx, lora->scale)
                          : launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, (const bf16_t*)ws.hbuf, s.f, nullptr,
-                                                       nullptr, s.f, lora->a_down, true, lora->r, ws.zd);
+                                                       nullptr, s.f, lora->a_down, true, lora->r, zd);
     if (err != hipSuccess) return err;
   }
   auto dn_launch = [&](auto mode) {
     constexpr int LO = decltype(mode)::value;
     DownProb<Cfg, LO> pb{(const bf16_t*)ws.hbuf, offsets, ws.gemm_tiles, (const bf16_t*)w_down,
                          (const bf16_t*)d_packed, s.d, s.f,
-                         (s.d + Cfg::BN - 1) / Cfg::BN, lora ? ws.zd : nullptr,
+                         (s.d + Cfg::BN - 1) / Cfg::BN, lora ? zd : nullptr,
                          lora ? lora->b_down : nullptr, lora ? lora->r : 0, lora ? lora->scale : 0.f,
                          (bf16_t*)y_perm};
     pb.zx = ws.zx;

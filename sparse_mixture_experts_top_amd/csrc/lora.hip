@@ -154,6 +154,9 @@ constexpr int kProjWaves = 8;
 // slower on the 14-expert LoRA step (fewer workgroups outweigh the halved
 // adapter re-reads from L2)
 constexpr int kProjRowGroups = 1;
+#ifndef MOE_PROJ_U
+#define MOE_PROJ_U 4
+#endif
 
 // One projection: out[p, q] = row_scale_p * in[src_p] . Mt[le(p)][q] (and
 // out_hl, see launch_lora_rowproj).
@@ -181,7 +184,7 @@ template <class TIn, int NJ>
 __global__ __launch_bounds__(64 * kProjWaves) void lora_proj_mfma(int L, const int32_t* __restrict__ offsets, int r,
                                                                   ProjJobs<TIn, NJ> jobs) {
   constexpr bool kSplit = sizeof(TIn) == 4;
-  constexpr int U = 4;  // K steps per load batch
+  constexpr int U = MOE_PROJ_U;  // K steps per load batch
   constexpr int RG = kProjRowGroups;
   __shared__ f32x4 part[kProjWaves][RG][64];
   const ProjJob<TIn>& jb = jobs.j[NJ == 1 ? 0 : blockIdx.y];
@@ -835,6 +838,10 @@ hipError_t launch_lora_bwd(const Ctx& c, const moe_shape_t& sh, const Workspace&
   const int64_t rmax = max_rows(sh);
   const int max_tiles = gemm_max_tiles(sh);
   const bf16_t* H = act_save + f;  // rows of stride 3f (G | H | U)
+  // Z_u, Z_d: kept by the forward in z_save, else projected here
+  const bool have_z = lo.z_save != nullptr;
+  float* zu = have_z ? lo.z_save : ws.zu;
+  float* zd = have_z ? lo.z_save + rmax * r : ws.zd;
   hipError_t err;
 #define MOE_TRY(x) \
   if ((err = (x)) != hipSuccess) return err
@@ -852,18 +859,26 @@ hipError_t launch_lora_bwd(const Ctx& c, const moe_shape_t& sh, const Workspace&
                          d, r, ws.lora_mt);
       MOE_TRY(hipGetLastError());
     }
-    ProjJobs<bf16_t, 3> jobs{{{x_rows, d, x_src, nullptr, d, lo.a_up, ws.zu, nullptr, 1.f},
-                              {H, 3 * f, nullptr, nullptr, f, lo.a_down, ws.zd, nullptr, 1.f},
-                              {dy, d, row_src, row_gate, d, ws.lora_mt, ws.wproj, kx ? ws.zx : nullptr, lo.scale}}};
+    const ProjJob<bf16_t> j_dob{dy, d, row_src, row_gate, d, ws.lora_mt, ws.wproj, kx ? ws.zx : nullptr, lo.scale};
+    const unsigned gx = (unsigned)((rmax + 16 * kProjRowGroups - 1) / (16 * kProjRowGroups));
     TimedLaunch tl(MOE_K_LORA_PROJ, c.stream);
-    hipLaunchKernelGGL((lora_proj_mfma<bf16_t, 3>),
-                       dim3((unsigned)((rmax + 16 * kProjRowGroups - 1) / (16 * kProjRowGroups)), 3),
-                       dim3(64 * kProjWaves), 0,
-                       c.stream, L, offsets, r, jobs);
+    if (have_z) {
+      ProjJobs<bf16_t, 1> jobs{{j_dob}};
+      hipLaunchKernelGGL((lora_proj_mfma<bf16_t, 1>), dim3(gx), dim3(64 * kProjWaves), 0, c.stream, L, offsets, r,
+                         jobs);
+    } else {
+      ProjJobs<bf16_t, 3> jobs{{{x_rows, d, x_src, nullptr, d, lo.a_up, zu, nullptr, 1.f},
+                                {H, 3 * f, nullptr, nullptr, f, lo.a_down, zd, nullptr, 1.f},
+                                j_dob}};
+      hipLaunchKernelGGL((lora_proj_mfma<bf16_t, 3>), dim3(gx, 3), dim3(64 * kProjWaves), 0, c.stream, L, offsets,
+                         r, jobs);
+    }
     MOE_TRY(hipGetLastError());
   } else {
-    MOE_TRY(launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, x_rows, d, x_src, nullptr, d, lo.a_up, true, r, ws.zu));
-    MOE_TRY(launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, H, 3 * f, nullptr, nullptr, f, lo.a_down, true, r, ws.zd));
+    if (!have_z) {
+      MOE_TRY(launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, x_rows, d, x_src, nullptr, d, lo.a_up, true, r, zu));
+      MOE_TRY(launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, H, 3 * f, nullptr, nullptr, f, lo.a_down, true, r, zd));
+    }
     MOE_TRY(launch_lora_rowproj<bf16_t>(c, L, offsets, rmax, dy, d, row_src, row_gate, d, lo.b_down, false, r,
                                         ws.wproj, ws.lora_mt, kx ? ws.zx : nullptr, lo.scale));
   }
@@ -880,9 +895,9 @@ hipError_t launch_lora_bwd(const Ctx& c, const moe_shape_t& sh, const Workspace&
     MOE_TRY(hipGetLastError());
   }
   MOE_TRY(launch_lora_rowproj<float>(c, L, offsets, rmax, ws.du, f, nullptr, nullptr, f, lo.b_up, false, r, ws.vproj, ws.lora_mt));
-  MOE_TRY(launch_seg_outer<bf16_t>(c, L, offsets, ws.zd, r, dy, d, row_src, row_gate, d, lo.scale, false, db_down));
+  MOE_TRY(launch_seg_outer<bf16_t>(c, L, offsets, zd, r, dy, d, row_src, row_gate, d, lo.scale, false, db_down));
   MOE_TRY(launch_seg_outer<bf16_t>(c, L, offsets, ws.wproj, r, H, 3 * f, nullptr, nullptr, f, lo.scale, true, da_down));
-  MOE_TRY(launch_seg_outer<float>(c, L, offsets, ws.zu, r, ws.du, f, nullptr, nullptr, f, lo.scale, false, db_up));
+  MOE_TRY(launch_seg_outer<float>(c, L, offsets, zu, r, ws.du, f, nullptr, nullptr, f, lo.scale, false, db_up));
   MOE_TRY(launch_seg_outer<bf16_t>(c, L, offsets, ws.vproj, r, x_rows, d, x_src, nullptr, d, lo.scale, true, da_up));
 #undef MOE_TRY
   return hipSuccess;

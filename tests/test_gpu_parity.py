@@ -7,7 +7,7 @@ import torch
 
 import oracle
 from gpu_util import (assert_close, bf16_round, check_act_save, check_dispatch, check_route, expert_ref_rows,
-                      host, rows_x, run_forward, say, upload)
+                      host, lora_of, rows_x, run_forward, say, upload)
 from sparse_mixture_experts_top_amd import binding as B
 from sparse_mixture_experts_top_amd import layer
 from sparse_mixture_experts_top_amd.workloads import WORKLOADS, Workload, generate, to_f64
@@ -404,6 +404,66 @@ def test_lora_forward_backward_and_aux(b_init, x_perm, r, packed, dims):
             assert (gp["da_up"] == 0).all() and (gp["da_down"] == 0).all()
         frozen = run_forward(w.replace(lora_r=0), dev, x_perm=x_perm)
         assert torch.equal(frozen.y, buf.y)
+
+
+@pytest.mark.parametrize("r,packed,dims", [(16, True, 128), (16, False, 128), (8, False, 128), (16, False, 192)])
+def test_lora_saved_projections(r, packed, dims):
+    """z_save: the forward keeps Z_u = X A_up^T and Z_d = H A_down^T (checked
+    against float64 products of the rows the GPU used, within the fp32
+    accumulation bound), its own outputs unchanged, and the backward reading
+    them gives the gradients of the backward that projects again, bitwise."""
+    w = W("lora_zsave", T=256, d=dims, E=12, k=4, f=dims, e_lo=2, e_hi=9, lora_r=r,
+          lora_alpha=32.0, lora_b="normal", aux_coef=0.01)
+    say(f"[case lora z_save r={r} packed={packed} d=f={dims}]")
+    inp = generate(w, seed=13)
+    dev = upload(inp)
+    shape = layer.shape_of(w)
+    L, rmax = w.L, B.moe_max_rows(shape)
+    pk = layer.pack_weights(shape, dev["w_gate"], dev["w_up"], dev["w_down"]) if packed else None
+    fwd = lambda b, lo: layer.forward(b, dev["x"], dev["w_router"], dev.get("bias"), dev["w_gate"], dev["w_up"],
+                                      dev["w_down"], lo, packed=pk)
+    plain = layer.alloc(shape, lora_r=r, act_save=True)
+    fwd(plain, lora_of(w, dev))
+    z_save = torch.full((2, rmax, r), float("nan"), dtype=torch.float32, device="cuda")
+    lo_z = B.make_lora(r, w.lora_alpha, dev["a_up"], dev["b_up"], dev["a_down"], dev["b_down"], z_save)
+    buf = layer.alloc(shape, lora_r=r, act_save=True)
+    fwd(buf, lo_z)
+    torch.cuda.synchronize()
+    R = int(host(buf.offsets)[-1])
+    assert R > 0 and torch.equal(buf.y_perm[:R], plain.y_perm[:R]) and torch.equal(buf.act_save[:R], plain.act_save[:R])
+    # the kept projections against float64 products of the same rows
+    off = host(buf.offsets)
+    le_of = np.searchsorted(off, np.arange(R), side="right") - 1
+    X = rows_x(w, inp, buf, np.arange(R))
+    H = host(buf.act_save[:R])[:, w.f:2 * w.f]
+    for part, (rows, A) in enumerate(((X, to_f64(inp["a_up"])), (H, to_f64(inp["a_down"])))):
+        ref = np.einsum("pk,pqk->pq", rows, A[le_of])
+        # fp32 accumulation over K products (exact in fp32): |err| <= K u sum |x a|
+        K = rows.shape[1]
+        bound = (K + 8) * 2.0 ** -24 * np.einsum("pk,pqk->pq", np.abs(rows), np.abs(A[le_of])) + 1e-30
+        got = host(z_save[part, :R])
+        assert np.all(np.abs(got - ref) <= bound), f"z_save[{part}]"
+    # gradients: kept projections vs projected again, bitwise
+    xr, xs = layer.x_rows(buf, dev["x"])
+    shapes = ((L, r, w.d), (L, w.f, r), (L, r, w.f), (L, w.d, r))
+    dgu_p = None
+    if dims % 128 == 0:
+        dgu_p = torch.empty((L, w.f, w.d), dtype=torch.bfloat16, device="cuda")
+        B.moe_pack_backward_weights(shape, dev["w_gate"], dev["w_up"], dev["w_down"], dgu_p, None)
+    for bwd_packed in ((False, True) if dgu_p is not None else (False,)):
+        out = []
+        for lo in (lora_of(w, dev), lo_z):
+            g = [torch.full(sz, float("nan"), device="cuda") for sz in shapes]
+            if bwd_packed:
+                B.moe_lora_bwd_packed(shape, lo, dev["dy"], buf.offsets, buf.row_src, buf.row_gate, xr, xs,
+                                      buf.act_save, dgu_p, *g, buf.ws)
+            else:
+                B.moe_lora_bwd(shape, lo, dev["dy"], buf.offsets, buf.row_src, buf.row_gate, xr, xs, buf.act_save,
+                               dev["w_down"], *g, buf.ws)
+            out.append(g)
+        torch.cuda.synchronize()
+        for a, b in zip(*out):
+            assert torch.equal(a, b), f"bwd_packed={bwd_packed}"
 
 
 @pytest.mark.parametrize("name", ["rows_bf16", "capacity_bf16"])
