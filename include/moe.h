@@ -325,7 +325,7 @@ moe_status_t moe_combine(const moe_shape_t* shape, const void* y_perm, const int
 
 /* Load-balance loss ("Full-Stack Engineering Guide", §2.1 and "Engineering
  * Practices and Optimization Pathways", §3.3: auxiliary loss that encourages
- * uniform routing), in the Switch form:
+ * uniform routing), as load times probability:
  *   out[1] = E * sum_e (counts[e] / (T k)) * (prob_sum[e] / T),
  *   out[0] = coef * out[1].
  *   counts [E] int32 (moe_dispatch), prob_sum [E] f32 (moe_route), out [2] f32. */

@@ -36,8 +36,8 @@ reason in the design notes of the repository):
 5. Only experts in [e_lo, e_hi) are computed (one expert-parallel rank's
    share, [FullOpt §4.1]); the other assignments are not drops, they belong to
    other ranks, and tokens with no local expert get y = 0.
-6. The load-balance loss ([Guide §2.1], [Paths §3.3]) is the Switch form
-   coef * E * sum_e f_e P_e, with f_e the fraction of the T*k assignments
+6. The load-balance loss ([Guide §2.1], [Paths §3.3]) is the product of
+   load and probability, coef * E * sum_e f_e P_e, with f_e the fraction of the T*k assignments
    routed to e (before capacity) and P_e the mean full-softmax probability.
 7. LoRA ([Guide §3] eq. W' = W0 + (alpha/r) B A) sits on the up and down
    projections of every local expert; dropout is 0. The backward takes an
@@ -363,7 +363,7 @@ def combine(o_rows, slot, gate, T: int) -> np.ndarray:
 
 
 def aux_loss(counts, prob_sum, T: int, k: int, coef: float):
-    """Switch-style load balance: f_e = counts_e / (T k), P_e = prob_sum_e / T,
+    """Load balance as load times probability: f_e = counts_e / (T k), P_e = prob_sum_e / T,
     returns (coef * E * sum f P, E * sum f P)."""
     c = _f64(counts)
     P = _f64(prob_sum) / T
