@@ -611,13 +611,40 @@ constexpr int kSmChunks = kSmCols / 8;  // 16-byte chunks per tile row
 static_assert(kSmWaves * 32 * kSmCols * 2 <= 160 * 1024, "LDS tiles");
 static_assert(kSmChunks <= 64 && kSmCols % 64 == 0, "tile rows");
 
-__global__ __launch_bounds__(64 * kSmWaves) void lora_seg_mfma(
-    const int32_t* __restrict__ offsets, const float* __restrict__ P, int r, const bf16_t* __restrict__ in,
-    int64_t in_stride, const int32_t* __restrict__ qsrc, const float* __restrict__ qscale, int C, float s,
-    int out_qc, float* __restrict__ out) {
+// One gradient sum: out = s * sum over rows p (qscale_p P[p])^T in[qsrc_p]
+// per expert, [L, r, C] (out_qc) or [L, C, r].
+struct SegJob {
+  const float* P;
+  const bf16_t* in;
+  int64_t in_stride;
+  const int32_t* qsrc;
+  const float* qscale;
+  int C, out_qc;
+  float* out;
+};
+// NJ independent sums over the same experts in one launch (blockIdx.z picks
+// the job; workgroups past a job's columns return), so their latencies
+// overlap instead of adding up.
+template <int NJ>
+struct SegJobs {
+  SegJob j[NJ];
+};
+
+template <int NJ>
+__global__ __launch_bounds__(64 * kSmWaves) void lora_seg_mfma(const int32_t* __restrict__ offsets, int r, float s,
+                                                               SegJobs<NJ> jobs) {
   __shared__ __align__(16) bf16_t tile[kSmWaves * 32 * kSmCols];
+  const SegJob& jb = jobs.j[NJ == 1 ? 0 : blockIdx.z];
+  const float* __restrict__ P = jb.P;
+  const bf16_t* __restrict__ in = jb.in;
+  const int64_t in_stride = jb.in_stride;
+  const int32_t* __restrict__ qsrc = jb.qsrc;
+  const float* __restrict__ qscale = jb.qscale;
+  const int C = jb.C, out_qc = jb.out_qc;
+  float* __restrict__ out = jb.out;
   const int le = blockIdx.y;
   const int cb = blockIdx.x * kSmCols;
+  if (cb >= C) return;  // workgroup-uniform, before any barrier
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int a = ld_uniform(offsets, le), b = ld_uniform(offsets, le + 1);
@@ -717,15 +744,22 @@ __global__ __launch_bounds__(64 * kSmWaves) void lora_seg_mfma(
     }
 }
 
+// The MFMA form takes bf16 rows, r <= 16, whole 128-column blocks and
+// 16-byte aligned rows.
+static bool seg_mfma_ok(int r, const bf16_t* in, int64_t in_stride, int C) {
+  return r <= 16 && C % kSmCols == 0 && in_stride % 8 == 0 && (reinterpret_cast<uintptr_t>(in) & 15) == 0;
+}
+
 template <class TIn>
 static hipError_t launch_seg_outer(const Ctx& c, int L, const int32_t* offsets, const float* P,
                                    int r, const TIn* in, int64_t in_stride, const int32_t* qsrc,
                                    const float* qscale, int C, float s, bool out_qc, float* out) {
   if constexpr (std::is_same<TIn, bf16_t>::value) {
-    if (r <= 16 && C % kSmCols == 0 && in_stride % 8 == 0 && (reinterpret_cast<uintptr_t>(in) & 15) == 0) {
+    if (seg_mfma_ok(r, in, in_stride, C)) {
       TimedLaunch tl(MOE_K_LORA_GRAD, c.stream);
-      hipLaunchKernelGGL(lora_seg_mfma, dim3(C / kSmCols, L), dim3(64 * kSmWaves), 0, c.stream, offsets, P, r,
-                         in, in_stride, qsrc, qscale, C, s, (int)out_qc, out);
+      SegJobs<1> jobs{{{P, in, in_stride, qsrc, qscale, C, (int)out_qc, out}}};
+      hipLaunchKernelGGL((lora_seg_mfma<1>), dim3(C / kSmCols, L), dim3(64 * kSmWaves), 0, c.stream, offsets, r, s,
+                         jobs);
       return hipGetLastError();
     }
   }
@@ -895,8 +929,18 @@ hipError_t launch_lora_bwd(const Ctx& c, const moe_shape_t& sh, const Workspace&
     MOE_TRY(hipGetLastError());
   }
   MOE_TRY(launch_lora_rowproj<float>(c, L, offsets, rmax, ws.du, f, nullptr, nullptr, f, lo.b_up, false, r, ws.vproj, ws.lora_mt));
-  MOE_TRY(launch_seg_outer<bf16_t>(c, L, offsets, zd, r, dy, d, row_src, row_gate, d, lo.scale, false, db_down));
-  MOE_TRY(launch_seg_outer<bf16_t>(c, L, offsets, ws.wproj, r, H, 3 * f, nullptr, nullptr, f, lo.scale, true, da_down));
+  if (seg_mfma_ok(r, dy, d, d) && seg_mfma_ok(r, H, 3 * f, f)) {
+    // db_down and da_down together (both bf16 rows)
+    TimedLaunch tl(MOE_K_LORA_GRAD, c.stream);
+    SegJobs<2> jobs{{{zd, dy, d, row_src, row_gate, d, 0, db_down}, {ws.wproj, H, 3 * f, nullptr, nullptr, f, 1, da_down}}};
+    hipLaunchKernelGGL((lora_seg_mfma<2>), dim3(std::max(d, f) / kSmCols, L, 2), dim3(64 * kSmWaves), 0, c.stream,
+                       offsets, r, lo.scale, jobs);
+    MOE_TRY(hipGetLastError());
+  } else {
+    MOE_TRY(launch_seg_outer<bf16_t>(c, L, offsets, zd, r, dy, d, row_src, row_gate, d, lo.scale, false, db_down));
+    MOE_TRY(launch_seg_outer<bf16_t>(c, L, offsets, ws.wproj, r, H, 3 * f, nullptr, nullptr, f, lo.scale, true,
+                                     da_down));
+  }
   MOE_TRY(launch_seg_outer<float>(c, L, offsets, zu, r, ws.du, f, nullptr, nullptr, f, lo.scale, false, db_up));
   MOE_TRY(launch_seg_outer<bf16_t>(c, L, offsets, ws.vproj, r, x_rows, d, x_src, nullptr, d, lo.scale, true, da_up));
 #undef MOE_TRY
