@@ -117,10 +117,15 @@ PACKABLE = [n for n, w in CASES.items() if w.dtype == "bf16" and w.d % 128 == 0 
 
 @pytest.mark.parametrize("name,packed", [(n, False) for n in sorted(CASES)] + [(n, True) for n in PACKABLE])
 def test_backward_stagewise(name, packed):
-    w = CASES[name]
-    say(f"[backward {name}] T={w.T} d={w.d} E={w.E} k={w.k} f={w.f} local=[{w.e_lo},{w.local_hi}) "
+    check_backward(CASES[name], packed)
+
+
+def check_backward(w, packed, seed=3):
+    """The forward, then every backward stage against the oracle fed the GPU's
+    own upstream results."""
+    say(f"[backward {w.name}] T={w.T} d={w.d} E={w.E} k={w.k} f={w.f} local=[{w.e_lo},{w.local_hi}) "
         f"cap={w.capacity} lora={w.lora_r} dtype={w.dtype} packed={packed}")
-    inp = generate(w, seed=3)
+    inp = generate(w, seed=seed)
     dev = upload(inp)
     buf = run_forward(w, dev, prob=True, act_save=True, x_perm=False)
     g = run_backward(w, dev, buf, packed=packed)

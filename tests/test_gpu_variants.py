@@ -86,17 +86,23 @@ REMAP = {
 
 @pytest.mark.parametrize("name", sorted(REMAP))
 def test_remap_stagewise(name):
-    w = REMAP[name]
-    say(f"[remap {name}] T={w.T} d={w.d} E={w.E} k={w.k} cap={w.capacity} local=[{w.e_lo},{w.local_hi})")
-    inp = generate(w, seed=4)
-    dev = upload(inp)
-    buf, alt, moved = remap_forward(w, dev)
-    ref, R = check_remap(w, inp, dev, buf, alt, moved)
+    ref = check_remap_case(REMAP[name])
     assert ref["moved"] > 0
+
+
+def check_remap_case(w, seed=4, x_perm=True):
+    """Remapped forward: routing with alternates, the remapped dispatch against
+    the oracle, then combine over the remapped slots."""
+    say(f"[remap {w.name}] T={w.T} d={w.d} E={w.E} k={w.k} cap={w.capacity} local=[{w.e_lo},{w.local_hi})")
+    inp = generate(w, seed=seed)
+    dev = upload(inp)
+    buf, alt, moved = remap_forward(w, dev, x_perm=x_perm)
+    ref, R = check_remap(w, inp, dev, buf, alt, moved)
     # combine over the remapped slots, fed the GPU's rows
     y_ref = oracle.combine(host(buf.y_perm[:R]) if R else np.zeros((0, w.d)), host(buf.slot), host(buf.topk_gate),
                            w.T)
     assert_close(host(buf.y), y_ref, w.dtype, "combine (remapped)")
+    return ref
 
 
 def test_remap_conservation_over_all_experts_and_fused_gather():
