@@ -338,8 +338,15 @@ def test_packed_weights_need_d_multiple_of_128():
 def test_lora_forward_backward_and_aux(b_init, x_perm, r, packed, dims):
     w = W("lora_small", T=256, d=dims, E=12, k=4, f=dims, e_lo=2, e_hi=9, lora_r=r,
           lora_alpha=32.0, lora_b=b_init, aux_coef=0.01)
-    say(f"[case lora_small b={b_init} x_perm={x_perm} r={r} packed={packed} d=f={dims}]")
-    inp = generate(w, seed=6)
+    check_lora(w, x_perm, packed)
+
+
+def check_lora(w, x_perm, packed, seed=6):
+    """Forward with LoRA (rows, saved G | H | U, softmax sums, aux loss), then
+    the adapter gradients against the oracle three ways, plain and packed."""
+    b_init, r = w.lora_b, w.lora_r
+    say(f"[case {w.name} b={b_init} x_perm={x_perm} r={r} packed={packed} d={w.d} f={w.f}]")
+    inp = generate(w, seed=seed)
     dev = upload(inp)
     buf = run_forward(w, dev, prob=True, act_save=True, x_perm=x_perm, packed=packed)
     lg, idx, gate = check_route(w, inp, buf)

@@ -120,3 +120,69 @@ def test_random_shape_remap(i):
     from test_gpu_variants import check_remap_case
     w, x_perm = REMAP_CASES[i]
     check_remap_case(w, seed=300 + i, x_perm=x_perm)
+
+
+def lora_cases(n=10, seed=2027):
+    """Shapes for the adapter sweep: ranks from 1 to 64 (the matrix-core
+    forms at r <= 16, the extra K step at r = 16, the row loops above),
+    zero-initialised B on some, packed weights where d, f % 128 == 0."""
+    rng = np.random.default_rng(seed)
+    ranks = [1, 5, 8, 12, 16, 16, 24, 32, 48, 64]
+    cases = []
+    for i in range(n):
+        r = int(ranks[i % len(ranks)])
+        d = int(rng.choice([64, 128, 192, 256]))
+        f = int(rng.choice([64, 128, 192, 256]))
+        E = int(rng.integers(2, 41))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        T = int(rng.integers(1, max(2, 2500 // k)))
+        e_lo, e_hi = 0, -1
+        if rng.random() < 0.5 and E > 2:
+            e_lo = int(rng.integers(0, E - 1))
+            e_hi = int(rng.integers(e_lo + 1, E + 1))
+        cap = max(1, int(T * k / E * rng.uniform(0.5, 1.5))) if rng.random() < 0.25 else 0
+        w = Workload(f"lsweep{i}", T=T, d=d, E=E, k=k, f=f, e_lo=e_lo, e_hi=e_hi, capacity=cap,
+                     zipf_s=float(rng.choice([0.0, 1.0])), lora_r=r, lora_alpha=float(rng.choice([8.0, 32.0])),
+                     lora_b="zero" if rng.random() < 0.2 else "normal", aux_coef=0.01)
+        packed = d % 128 == 0 and f % 128 == 0 and bool(rng.random() < 0.5)
+        cases.append((w, bool(rng.random() < 0.5), packed))
+    return cases
+
+
+LORA_CASES = lora_cases()
+
+
+@pytest.mark.parametrize("i", range(len(LORA_CASES)))
+def test_random_shape_lora(i):
+    from test_gpu_parity import check_lora
+    w, x_perm, packed = LORA_CASES[i]
+    check_lora(w, x_perm, packed, seed=400 + i)
+
+
+def latent_cases(n=6, seed=2028):
+    """Shapes for the latent-router sweep: latent widths 64 to 256, model
+    widths to 512, with and without a logit bias, local ranges."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        d = int(rng.choice([64, 128, 256, 384, 512]))
+        dc = int(rng.choice([64, 128, 192, 256]))
+        E = int(rng.integers(2, 201))
+        k = int(rng.integers(1, min(E, 16) + 1))
+        T = int(rng.integers(1, max(2, 3000 // k)))
+        e_lo, e_hi = 0, -1
+        if rng.random() < 0.4 and E > 2:
+            e_lo = int(rng.integers(0, E - 1))
+            e_hi = int(rng.integers(e_lo + 1, E + 1))
+        cases.append(Workload(f"csweep{i}", T=T, d=d, E=E, k=k, f=int(rng.choice([64, 128])), e_lo=e_lo,
+                              e_hi=e_hi, zipf_s=float(rng.choice([0.0, 1.0])), latent_dc=dc))
+    return cases
+
+
+LATENT_CASES = latent_cases()
+
+
+@pytest.mark.parametrize("i", range(len(LATENT_CASES)))
+def test_random_shape_latent(i):
+    from test_gpu_variants import check_latent_case
+    check_latent_case(LATENT_CASES[i], seed=500 + i)

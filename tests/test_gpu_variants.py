@@ -195,9 +195,13 @@ LATENT = {
 
 @pytest.mark.parametrize("name", sorted(LATENT))
 def test_latent_router_stagewise(name):
-    w = LATENT[name]
-    say(f"[latent {name}] T={w.T} d={w.d} d_c={w.latent_dc} E={w.E} k={w.k}")
-    inp = generate(w, seed=6)
+    check_latent_case(LATENT[name])
+
+
+def check_latent_case(w, seed=6):
+    """Latent routing against the oracle, then the rest of the layer on it."""
+    say(f"[latent {w.name}] T={w.T} d={w.d} d_c={w.latent_dc} E={w.E} k={w.k}")
+    inp = generate(w, seed=seed)
     dev = upload(inp)
     buf, z = latent_route(w, dev)
     check_latent(w, inp, buf, z)
