@@ -155,6 +155,7 @@ __device__ __forceinline__ int64_t gathered_row(const int32_t* row_src, const Ro
 // twice (high and low parts meet the same values), zeros for gate columns.
 template <class Cfg, int LORA = 0>
 struct GateUpProb {
+  static_assert(Cfg::FN % 4 == 0, "the epilogue stores two (G, U) fragment pairs at a time");
   static constexpr int kExtra = LORA == 2 ? 1 : 0;
   const bf16_t* x;
   const int32_t* row_src;
@@ -236,7 +237,9 @@ struct GateUpProb {
   __device__ __forceinline__ void epilogue(int item, Acc<Cfg>& acc) const {
     const RowTile t = row_tile<Cfg::BM>(tiles, offsets, item / nt);
     const int ni = item % nt;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // wave-uniform, so the column tests below branch on scalars and the
+    // lane swaps of the paired stores run with every lane active
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i) {
@@ -246,32 +249,41 @@ struct GateUpProb {
       const bool ok = rin < t.valid;
       const int64_t row = t.row0 + rin;
 #pragma unroll
-      for (int jj = 0; jj < Cfg::FN; jj += 2) {
-        // fragment jg (even) holds G, jg + 1 holds U, for the same 16 FFN columns
+      for (int jj = 0; jj < Cfg::FN; jj += 4) {
+        // fragments jg + 2 h (h = 0, 1) hold G and jg + 2 h + 1 hold U, of the
+        // 16 FFN columns c0 + 16 h .. +15; f % 64 == 0, so the 32 columns are
+        // all inside f or all past it
         const int jg = wn * Cfg::FN + jj;
-        // f % 64 == 0: a 16-column fragment pair is all inside f or all past it
-        if (ni * HALF + (jg >> 1) * 16 >= f) continue;
-        const int fcol = ni * HALF + (jg >> 1) * 16 + (lane >> 4) * 4;
-        float h[4], g[4], uu[4], lt[4] = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (LORA == 1) {
-          if (ok) lora_term_rows(zu + row * r, b_up + ((int64_t)t.le * f + fcol) * r, r, lt);
-        }
+        const int c0 = ni * HALF + (jg >> 1) * 16;
+        if (c0 >= f) continue;
+        float h[2][4], g[2][4], uu[2][4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          g[q] = acc.v[i][jj][q];
-          float u = acc.v[i][jj + 1][q];
-          if constexpr (LORA == 1) u = fmaf(scale, lt[q], u);
-          uu[q] = u;
-          h[q] = silu_f(g[q]) * u;
+        for (int p = 0; p < 2; ++p) {
+          float lt[4] = {0.f, 0.f, 0.f, 0.f};
+          if constexpr (LORA == 1) {
+            const int fcol = c0 + 16 * p + (lane >> 4) * 4;
+            if (ok) lora_term_rows(zu + row * r, b_up + ((int64_t)t.le * f + fcol) * r, r, lt);
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            g[p][q] = acc.v[i][jj + 2 * p][q];
+            float u = acc.v[i][jj + 2 * p + 1][q];
+            if constexpr (LORA == 1) u = fmaf(scale, lt[q], u);
+            uu[p][q] = u;
+            h[p][q] = silu_f(g[p][q]) * u;
+          }
         }
-        if (ok) {
-          const uint2 hv = pack4_bf16(h[0], h[1], h[2], h[3]);
-          *reinterpret_cast<uint2*>(hbuf + row * f + fcol) = hv;
-          if (act_save) {
-            bf16_t* as = act_save + row * 3 * f + fcol;
-            *reinterpret_cast<uint2*>(as) = pack4_bf16(g[0], g[1], g[2], g[3]);
-            *reinterpret_cast<uint2*>(as + f) = hv;
-            *reinterpret_cast<uint2*>(as + 2 * f) = pack4_bf16(uu[0], uu[1], uu[2], uu[3]);
+        const int col = c0 + pair_col(lane);
+        const uint4 hv = pair_cols_bf16(h[0], h[1]);
+        if (ok) *reinterpret_cast<uint4*>(hbuf + row * f + col) = hv;
+        if (act_save) {  // kernel-uniform
+          const uint4 gv = pair_cols_bf16(g[0], g[1]);
+          const uint4 uv = pair_cols_bf16(uu[0], uu[1]);
+          if (ok) {
+            bf16_t* as = act_save + row * 3 * f + col;
+            *reinterpret_cast<uint4*>(as) = gv;
+            *reinterpret_cast<uint4*>(as + f) = hv;
+            *reinterpret_cast<uint4*>(as + 2 * f) = uv;
           }
         }
       }
@@ -293,6 +305,7 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::WAVES_PER_SIMD) void gate_up_bf1
 // twice (high and low parts meet the same values), zeros for gate columns.
 template <class Cfg, int LORA = 0>
 struct DownProb {
+  static_assert(Cfg::FN % 2 == 0, "the epilogue stores fragment pairs");
   static constexpr int kExtra = LORA == 2 ? 1 : 0;
   const bf16_t* hbuf;
   const int32_t* offsets;
@@ -358,7 +371,9 @@ struct DownProb {
   __device__ __forceinline__ void epilogue(int item, Acc<Cfg>& acc) const {
     const RowTile t = row_tile<Cfg::BM>(tiles, offsets, item / nt);
     const int n0 = (item % nt) * Cfg::BN;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // wave-uniform, so the column tests below branch on scalars and the
+    // lane swaps of the paired stores run with every lane active
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i) {
@@ -368,20 +383,27 @@ struct DownProb {
       const bool ok = rin < t.valid;
       const int64_t row = t.row0 + rin;
 #pragma unroll
-      for (int j = 0; j < Cfg::FN; ++j) {
-        // d % 64 == 0: a wave's 16-column fragment is all valid or all not
-        if (n0 + wn * (Cfg::BN / Cfg::WN) + j * 16 >= d) continue;
-        const int n = n0 + dma_out_col<Cfg>(wn, j, lane);
-        float o[4], lt[4] = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (LORA == 1) {
-          if (ok) lora_term_rows(zd + row * r, b_down + ((int64_t)t.le * d + n) * r, r, lt);
-        }
+      for (int j = 0; j < Cfg::FN; j += 2) {
+        // fragments j, j + 1: 32 output columns from c0; d % 64 == 0, so
+        // they are all valid or all not
+        const int c0 = n0 + wn * (Cfg::BN / Cfg::WN) + j * 16;
+        if (c0 >= d) continue;
+        float o[2][4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          o[q] = acc.v[i][j][q];
-          if constexpr (LORA == 1) o[q] = fmaf(scale, lt[q], o[q]);
+        for (int h = 0; h < 2; ++h) {
+          float lt[4] = {0.f, 0.f, 0.f, 0.f};
+          if constexpr (LORA == 1) {
+            const int n = n0 + dma_out_col<Cfg>(wn, j + h, lane);
+            if (ok) lora_term_rows(zd + row * r, b_down + ((int64_t)t.le * d + n) * r, r, lt);
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            o[h][q] = acc.v[i][j + h][q];
+            if constexpr (LORA == 1) o[h][q] = fmaf(scale, lt[q], o[h][q]);
+          }
         }
-        if (ok) *reinterpret_cast<uint2*>(y_perm + row * d + n) = pack4_bf16(o[0], o[1], o[2], o[3]);
+        const uint4 v = pair_cols_bf16(o[0], o[1]);
+        if (ok) *reinterpret_cast<uint4*>(y_perm + row * d + c0 + pair_col(lane)) = v;
       }
     }
   }
@@ -412,6 +434,7 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::WAVES_PER_SIMD) void down_bf16(D
 // scales the whole sum.
 template <class Cfg, bool LORA = false, bool DU32 = false, bool KX = false>
 struct DguPackedProb {
+  static_assert(Cfg::FN % 2 == 0, "the epilogue takes fragment pairs");
   static constexpr int kExtra = KX ? 1 : 0;
   const bf16_t* dy;
   const int32_t* row_src;
@@ -471,7 +494,9 @@ struct DguPackedProb {
   __device__ __forceinline__ void epilogue(int item, Acc<Cfg>& acc) const {
     const RowTile t = row_tile<Cfg::BM>(tiles, offsets, item / nt);
     const int n0 = (item % nt) * Cfg::BN;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // wave-uniform, so the column tests below branch on scalars and the
+    // lane swaps of the paired stores run with every lane active
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i) {
@@ -481,16 +506,16 @@ struct DguPackedProb {
       const bool ok = rin < t.valid;
       const int64_t row = t.row0 + rin;
       const float g_row = ok ? row_gate[row] : 0.f;
+      if constexpr (DU32) {
+        // fp32 dU only: a lane's four columns are one 16-byte store already
 #pragma unroll
-      for (int j = 0; j < Cfg::FN; ++j) {
-        if (n0 + wn * (Cfg::BN / Cfg::WN) + j * 16 >= f) continue;
-        const int n = n0 + dma_out_col<Cfg>(wn, j, lane);
-        if (!ok) continue;
-        const bf16_t* as = act_save + row * 3 * f + n;
-        const uint2 gv = *reinterpret_cast<const uint2*>(as);
-        float dgv[4], duv[4], lt[4] = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (LORA && !KX) lora_term_cols(wproj + row * r, a_down + (int64_t)t.le * r * f + n, f, r, lt);
-        if constexpr (DU32) {
+        for (int j = 0; j < Cfg::FN; ++j) {
+          if (n0 + wn * (Cfg::BN / Cfg::WN) + j * 16 >= f) continue;
+          const int n = n0 + dma_out_col<Cfg>(wn, j, lane);
+          if (!ok) continue;
+          const uint2 gv = *reinterpret_cast<const uint2*>(act_save + row * 3 * f + n);
+          float duv[4], lt[4] = {0.f, 0.f, 0.f, 0.f};
+          if constexpr (LORA && !KX) lora_term_cols(wproj + row * r, a_down + (int64_t)t.le * r * f + n, f, r, lt);
           const uint32_t gw[2] = {gv.x, gv.y};
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
@@ -499,21 +524,50 @@ struct DguPackedProb {
             duv[q] = dh * (g / (1.0f + expf(-g)));
           }
           *reinterpret_cast<float4*>(du32 + row * f + n) = make_float4(duv[0], duv[1], duv[2], duv[3]);
-          continue;
         }
-        const uint2 uv = *reinterpret_cast<const uint2*>(as + 2 * f);
-        const uint32_t gw[2] = {gv.x, gv.y}, uw[2] = {uv.x, uv.y};
+        continue;
+      }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float dh = fmaf(g_row, acc.v[i][j][q], scale * lt[q]);
+      for (int j = 0; j < Cfg::FN; j += 2) {
+        // fragments j, j + 1: 32 FFN columns from c0, all inside f or all
+        // past it (f % 64 == 0); lane l takes columns n .. n + 7
+        const int c0 = n0 + wn * (Cfg::BN / Cfg::WN) + j * 16;
+        if (c0 >= f) continue;
+        float a[8];
+        pair_cols_f32(acc.v[i][j], acc.v[i][j + 1], a);  // every lane, before the row test
+        const int n = c0 + pair_col(lane);
+        if (!ok) continue;
+        const bf16_t* as = act_save + row * 3 * f + n;
+        const uint4 gv = *reinterpret_cast<const uint4*>(as);
+        const uint4 uv = *reinterpret_cast<const uint4*>(as + 2 * f);
+        float lt[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if constexpr (LORA && !KX) {
+          float l0[4], l1[4];
+          lora_term_cols(wproj + row * r, a_down + (int64_t)t.le * r * f + n, f, r, l0);
+          lora_term_cols(wproj + row * r, a_down + (int64_t)t.le * r * f + n + 4, f, r, l1);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            lt[q] = l0[q];
+            lt[4 + q] = l1[q];
+          }
+        }
+        const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w}, uw[4] = {uv.x, uv.y, uv.z, uv.w};
+        float dgv[8], duv[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float dh = fmaf(g_row, a[q], scale * lt[q]);
           const float g = bf16_to_f32(static_cast<bf16_t>(gw[q >> 1] >> ((q & 1) * 16)));
           const float u = bf16_to_f32(static_cast<bf16_t>(uw[q >> 1] >> ((q & 1) * 16)));
           const float sg = 1.0f / (1.0f + expf(-g));
           dgv[q] = dh * u * (sg * (1.0f + g * (1.0f - sg)));
           duv[q] = dh * g * sg;
         }
-        *reinterpret_cast<uint2*>(dgu + row * 2 * f + n) = pack4_bf16(dgv[0], dgv[1], dgv[2], dgv[3]);
-        *reinterpret_cast<uint2*>(dgu + row * 2 * f + f + n) = pack4_bf16(duv[0], duv[1], duv[2], duv[3]);
+        *reinterpret_cast<uint4*>(dgu + row * 2 * f + n) =
+            make_uint4(f32x2_to_bf16x2(dgv[0], dgv[1]), f32x2_to_bf16x2(dgv[2], dgv[3]),
+                       f32x2_to_bf16x2(dgv[4], dgv[5]), f32x2_to_bf16x2(dgv[6], dgv[7]));
+        *reinterpret_cast<uint4*>(dgu + row * 2 * f + f + n) =
+            make_uint4(f32x2_to_bf16x2(duv[0], duv[1]), f32x2_to_bf16x2(duv[2], duv[3]),
+                       f32x2_to_bf16x2(duv[4], duv[5]), f32x2_to_bf16x2(duv[6], duv[7]));
       }
     }
   }

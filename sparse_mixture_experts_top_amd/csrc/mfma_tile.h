@@ -590,6 +590,43 @@ __device__ __forceinline__ int dma_out_col(int wn, int j, int lane) {
   return wn * (Cfg::BN / Cfg::WN) + j * 16 + (lane >> 4) * 4;
 }
 
+// Two output fragments side by side (columns c .. c+15 in `lo`, c+16 .. c+31
+// in `hi`, each lane holding its four columns 4 (l / 16) .. +3 of both) as
+// bf16, moved across the lanes of the same output row so that lane l holds
+// the eight consecutive columns c + pair_col(l) .. +7: one 16-byte store per
+// lane instead of two 8-byte ones, and every output row written in 64-byte
+// runs per store (two 32-byte runs before). The row fragment's 16 rows keep
+// their lanes (l % 16): v_permlane32_swap exchanges the upper half-wave of
+// its first operand with the lower half-wave of its second, and
+// v_permlane16_swap the odd 16-lane groups of its first operand with the
+// even groups of its second. All 64 lanes must execute it (a lane that
+// stores nothing still passes its values through).
+__device__ __forceinline__ uint4 pair_cols_bf16(const float (&lo)[4], const float (&hi)[4]) {
+  const uint2 x = pack4_bf16(lo[0], lo[1], lo[2], lo[3]);
+  const uint2 y = pack4_bf16(hi[0], hi[1], hi[2], hi[3]);
+  // lane groups (16 lanes) of x: columns 0-3 | 4-7 | 8-11 | 12-15, of y: 16-19 | ... | 28-31
+  const auto a0 = __builtin_amdgcn_permlane32_swap(x.x, y.x, false, false);
+  const auto a1 = __builtin_amdgcn_permlane32_swap(x.y, y.y, false, false);
+  // a[0]: 0-3 | 4-7 | 16-19 | 20-23, a[1]: 8-11 | 12-15 | 24-27 | 28-31
+  const auto b0 = __builtin_amdgcn_permlane16_swap(a0[0], a0[1], false, false);
+  const auto b1 = __builtin_amdgcn_permlane16_swap(a1[0], a1[1], false, false);
+  // b[0]: 0-3 | 8-11 | 16-19 | 24-27, b[1]: 4-7 | 12-15 | 20-23 | 28-31
+  return make_uint4(b0[0], b1[0], b0[1], b1[1]);
+}
+__device__ __forceinline__ int pair_col(int lane) { return (lane >> 4) * 8; }
+// The same move for fp32 values: out[k] = column c + pair_col(l) + k. (The
+// conversions go through values: __builtin_bit_cast of a vector element such
+// as lo[q] or b[1] reads element 0 with this compiler.)
+__device__ __forceinline__ void pair_cols_f32(const f32x4& lo, const f32x4& hi, float (&out)[8]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(lo[q]), __float_as_uint(hi[q]), false, false);
+    const auto b = __builtin_amdgcn_permlane16_swap(a[0], a[1], false, false);
+    out[q] = __uint_as_float(b[0]);
+    out[4 + q] = __uint_as_float(b[1]);
+  }
+}
+
 // s_waitcnt with vmcnt = n (n < 64) and the other counters left alone: vmcnt
 // lives in bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
 template <int N>
