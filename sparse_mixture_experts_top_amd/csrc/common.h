@@ -49,6 +49,13 @@ template <> __device__ __forceinline__ void store_f<bf16_t>(bf16_t* p, float v) 
 
 __device__ __forceinline__ float silu_f(float a) { return a / (1.0f + expf(-a)); }
 
+// A 16-byte store with the non-temporal hint: the L2 keeps the line only
+// until it needs the space, so rows written once and read by a later
+// kernel do not push out data the writing kernel still reuses.
+__device__ __forceinline__ void store16_nt(void* p, uint4 v) {
+  __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(p));
+}
+
 // Four floats -> four bf16 (round to nearest even) packed in 8 bytes.
 __device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) {
   return make_uint2(f32x2_to_bf16x2(a, b), f32x2_to_bf16x2(c, d));

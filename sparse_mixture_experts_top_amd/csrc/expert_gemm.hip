@@ -275,15 +275,18 @@ struct GateUpProb {
         }
         const int col = c0 + pair_col(lane);
         const uint4 hv = pair_cols_bf16(h[0], h[1]);
-        if (ok) *reinterpret_cast<uint4*>(hbuf + row * f + col) = hv;
+        // H (read by the down GEMM) and the saved rows (read by the
+        // backward) with the non-temporal hint: the token rows this launch
+        // still gathers keep the L2 (full_router gate/up 363 -> 348 us)
+        if (ok) store16_nt(hbuf + row * f + col, hv);
         if (act_save) {  // kernel-uniform
           const uint4 gv = pair_cols_bf16(g[0], g[1]);
           const uint4 uv = pair_cols_bf16(uu[0], uu[1]);
           if (ok) {
             bf16_t* as = act_save + row * 3 * f + col;
-            *reinterpret_cast<uint4*>(as) = gv;
-            *reinterpret_cast<uint4*>(as + f) = hv;
-            *reinterpret_cast<uint4*>(as + 2 * f) = uv;
+            store16_nt(as, gv);
+            store16_nt(as + f, hv);
+            store16_nt(as + 2 * f, uv);
           }
         }
       }
