@@ -65,7 +65,7 @@ Workspace carve_workspace(const moe_shape_t& s, int lora_r, void* base, bool dis
     w.rm_counts2 = static_cast<int32_t*>(take((int64_t)s.E * 4));
   }
   w.gemm_tiles = static_cast<int32_t*>(take((2 * (int64_t)gemm_max_tiles(s) + 1) * 4));
-  w.hbuf = take(rmax * s.f * elt);
+  w.hbuf = take(std::max(rmax * s.f * elt, s.dtype == MOE_BF16 ? packed_h_elems(s) * 2 : 0));
   if (lora_r > 0) {
     w.zu = static_cast<float*>(take(rmax * lora_r * 4));
     w.zd = static_cast<float*>(take(rmax * lora_r * 4));

@@ -173,7 +173,7 @@ struct Workspace {
   uint32_t* cand_key;    // [T*k]   gate bits of candidates (capacity)
   int32_t* cand_idx;     // [T*k]   assignment index t*k+j (capacity)
   int32_t* gemm_tiles;   // [max_tiles*2 + 1] (expert, row0) pairs + count at the end
-  void* hbuf;            // [Rmax, f] H in the shape's dtype
+  void* hbuf;            // H in the shape's dtype: [Rmax, f], or tile-packed (bf16 without adapters)
   float* zu;             // [Rmax, rmax] LoRA X A_up^T
   float* zd;             // [Rmax, rmax] LoRA H A_down^T
   float* wproj;          // [Rmax, rmax] LoRA dO B_down
@@ -204,6 +204,12 @@ constexpr int kGemmBM = 128;       // grouped GEMM row tile
 Workspace carve_workspace(const moe_shape_t& s, int lora_r, void* base, bool dispatch_only = false);
 int64_t max_rows(const moe_shape_t& s);
 int gemm_max_tiles(const moe_shape_t& s);
+// Row-tile height of the forward grouped GEMMs for a shape (128, or 320
+// where each expert expects a few hundred rows), and the bf16 elements of
+// H in its tile-packed layout (each 320-row tile owns BM x f elements; 0 for
+// the 128-row tiles, which keep H row-major).
+int gemm_tile_rows(const moe_shape_t& s);
+int64_t packed_h_elems(const moe_shape_t& s);
 
 // ------------------------------------------------------ kernel launchers ---
 // Each returns hipSuccess or the launch error.

@@ -61,11 +61,24 @@ using GemmCfgWide = DmaCfg<kGemmBM, 256, MOE_GEMM_STAGES, 2, 8, 4>;
 #ifndef MOE_GEMM_TALL_BSTAGES
 #define MOE_GEMM_TALL_BSTAGES 12
 #endif
-using GemmCfgTall = DmaCfg<320, 128, MOE_GEMM_TALL_STAGES, 4, 8, 4, 32, MOE_GEMM_TALL_BSTAGES>;
+constexpr int kTallBM = 320;
+using GemmCfgTall = DmaCfg<kTallBM, 128, MOE_GEMM_TALL_STAGES, 4, 8, 4, 32, MOE_GEMM_TALL_BSTAGES>;
 
 // Rows per local expert expected under uniform routing (capped by the
 // capacity) at which the tall layout is used.
 constexpr int kWideRowsPerExpert = 192;
+
+int gemm_tile_rows(const moe_shape_t& s) {
+  int64_t per_expert = (int64_t)s.T * s.k / s.E;
+  if (s.capacity > 0 && per_expert > s.capacity) per_expert = s.capacity;
+  return per_expert >= kWideRowsPerExpert ? GemmCfgTall::BM : GemmCfg::BM;
+}
+
+int64_t packed_h_elems(const moe_shape_t& s) {
+  const int64_t bm = gemm_tile_rows(s);
+  if (bm != kTallBM) return 0;  // the 128-row tiles keep H row-major
+  return ((max_rows(s) + bm - 1) / bm + (s.e_hi - s.e_lo)) * bm * s.f;
+}
 
 __global__ __launch_bounds__(1024) void build_row_tiles(const int32_t* __restrict__ offsets, int L,
                                                         int bm, int max_tiles,
@@ -157,6 +170,8 @@ template <class Cfg, int LORA = 0>
 struct GateUpProb {
   static_assert(Cfg::FN % 4 == 0, "the epilogue stores two (G, U) fragment pairs at a time");
   static constexpr int kExtra = LORA == 2 ? 1 : 0;
+  // H tile-packed on the tall tiles (see DownProb)
+  static constexpr bool kPackedH = LORA == 0 && Cfg::BM == kTallBM;
   const bf16_t* x;
   const int32_t* row_src;
   const int32_t* offsets;
@@ -278,7 +293,13 @@ struct GateUpProb {
         // H (read by the down GEMM) and the saved rows (read by the
         // backward) with the non-temporal hint: the token rows this launch
         // still gathers keep the L2 (full_router gate/up 363 -> 348 us)
-        if (ok) store16_nt(hbuf + row * f + col, hv);
+        if constexpr (kPackedH) {
+          // one 16-row x 64-byte block: the store writes 1 KB contiguously
+          bf16_t* hp = hbuf + (int64_t)(item / nt) * Cfg::BM * f + ((c0 >> 5) * Cfg::BM + rin) * 32 + pair_col(lane);
+          if (ok) store16_nt(hp, hv);
+        } else {
+          if (ok) store16_nt(hbuf + row * f + col, hv);
+        }
         if (act_save) {  // kernel-uniform
           const uint4 gv = pair_cols_bf16(g[0], g[1]);
           const uint4 uv = pair_cols_bf16(uu[0], uu[1]);
@@ -310,6 +331,16 @@ template <class Cfg, int LORA = 0>
 struct DownProb {
   static_assert(Cfg::FN % 2 == 0, "the epilogue stores fragment pairs");
   static constexpr int kExtra = LORA == 2 ? 1 : 0;
+  // On the tall tiles, without adapters, H is tile-packed: row tile t owns
+  // BM x f elements at t * BM * f, stored [K step of 32][tile row][32
+  // values], so the 16 rows of one DMA instruction are 1 KB of contiguous
+  // memory (64-byte pieces 2 f bytes apart in the row-major form), and the
+  // gate/up epilogue writes each such block with one store instruction.
+  // Measured at ep64_rank: down 59 -> 52 us, gate/up unchanged; on the
+  // 128-row tiles at full_router a wash (down -1, gate/up +3..+5 us), so
+  // those keep the row-major form, as do the adapter paths, which read H
+  // row by row.
+  static constexpr bool kPackedH = LORA == 0 && Cfg::BM == kTallBM;
   const bf16_t* hbuf;
   const int32_t* offsets;
   const int32_t* tiles;
@@ -333,9 +364,21 @@ struct DownProb {
     const int n0 = (item % nt) * Cfg::BN;
     const int ce = dma_chunk_elem<Cfg>();
     ld.b_stream = stream_b;
+    if constexpr (kPackedH) {
+      // instructions wholly past the valid rows re-read the last valid block
+      const bf16_t* hp = hbuf + (int64_t)(item / nt) * Cfg::BM * f;
+      const int last = (t.valid - 1) / Cfg::RPD;
 #pragma unroll
-    for (int q = 0; q < Cfg::A_DMA / Cfg::DW; ++q)
-      ld.a[q] = hbuf + (t.row0 + min(dma_row<Cfg>(q * Cfg::DW + part), t.valid - 1)) * f + ce;
+      for (int q = 0; q < Cfg::A_DMA / Cfg::DW; ++q) {
+        const int blk = min(q * Cfg::DW + part, last);
+        ld.a[q] = hp + (Cfg::RPD * blk + (threadIdx.x & 63) / Cfg::CPR) * Cfg::BK + ce;
+      }
+      ld.a_kstep = Cfg::BM * Cfg::BK;
+    } else {
+#pragma unroll
+      for (int q = 0; q < Cfg::A_DMA / Cfg::DW; ++q)
+        ld.a[q] = hbuf + (t.row0 + min(dma_row<Cfg>(q * Cfg::DW + part), t.valid - 1)) * f + ce;
+    }
     if (w_packed) {
       // packed tiles hold 128 output columns each; blocks past d (a partial
       // last item) re-read the last block, never stored
@@ -1058,10 +1101,7 @@ hipError_t launch_expert_gemm(const Ctx& c, const moe_shape_t& s, const Workspac
                                             lora->r, zu);
     if (err != hipSuccess) return err;
   }
-  const int64_t tk = (int64_t)s.T * s.k;
-  int64_t per_expert = tk / s.E;
-  if (s.capacity > 0 && per_expert > s.capacity) per_expert = s.capacity;
-  if (per_expert >= kWideRowsPerExpert)
+  if (gemm_tile_rows(s) == GemmCfgTall::BM)
     return launch_grouped_bf16<GemmCfgTall>(c, s, ws, xr, row_src, offsets, gu_packed, d_packed, w_gate,
                                             w_up, w_down, lora, act_save, y_perm, max_tiles, lora_mode);
   return launch_grouped_bf16<GemmCfg>(c, s, ws, xr, row_src, offsets, gu_packed, d_packed, w_gate, w_up,
