@@ -354,38 +354,43 @@ __global__ __launch_bounds__(256) void topk_softmax(const float* __restrict__ lo
     prob_part[(int64_t)blockIdx.x * E + e] = ((red[0][e] + red[1][e]) + red[2][e]) + red[3][e];
 }
 
-// prob_sum[e] = sum over blocks of prob_part[b, e]. Workgroup (e-group of
-// 64 experts, 16 waves): lane l of wave w sums blocks w, w + 16, ... of
-// expert 64 g + l in order (32 loads in flight per batch), then the waves'
-// partials are added in wave order - a fixed order, so the result does not
-// depend on scheduling.
+// prob_sum[e] = sum over blocks of prob_part[b, e]. Workgroup of 1024
+// threads for kReduceE experts: thread (j, u) (u = expert within the group,
+// j = 0 .. 1023 / kReduceE) sums blocks j, j + J, j + 2 J, ... of its expert
+// in order (kReduceNB loads in flight per batch; a block's kReduceE experts
+// are one 128-byte line), then the J partials of an expert are added
+// pairwise in a fixed tree through LDS, so the result does not depend on
+// scheduling. At the LoRA step's shape (2048 blocks x 896 experts) this
+// takes 8 us against 11 for 64 experts per workgroup summed by 16 waves
+// (8 and 16 experts per workgroup: 9.1 and 8.2 us).
+constexpr int kReduceE = 32;
+constexpr int kReduceNB = 16;
 __global__ __launch_bounds__(1024) void prob_reduce(const float* __restrict__ part, int nblk, int E,
                                                     float* __restrict__ out) {
-  constexpr int NB = 32;
-  __shared__ float red[16][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int e = blockIdx.x * 64 + lane;
+  constexpr int J = 1024 / kReduceE;
+  __shared__ float red[J][kReduceE];
+  const int u = threadIdx.x % kReduceE, j = threadIdx.x / kReduceE;
+  const int e = blockIdx.x * kReduceE + u;
   float acc = 0.f;
   if (e < E) {
-    for (int b0 = wave; b0 < nblk; b0 += 16 * NB) {
-      float v[NB];
+    for (int b0 = j; b0 < nblk; b0 += J * kReduceNB) {
+      float v[kReduceNB];
 #pragma unroll
-      for (int u = 0; u < NB; ++u) {
-        const int b = b0 + 16 * u;
-        v[u] = b < nblk ? part[(int64_t)b * E + e] : 0.f;
+      for (int q = 0; q < kReduceNB; ++q) {
+        const int b = b0 + J * q;
+        v[q] = b < nblk ? part[(int64_t)b * E + e] : 0.f;
       }
 #pragma unroll
-      for (int u = 0; u < NB; ++u) acc += v[u];
+      for (int q = 0; q < kReduceNB; ++q) acc += v[q];
     }
   }
-  red[wave][lane] = acc;
+  red[j][u] = acc;
   __syncthreads();
-  if (wave == 0 && e < E) {
-    float sum = 0.f;
-#pragma unroll
-    for (int w = 0; w < 16; ++w) sum += red[w][lane];
-    out[e] = sum;
+  for (int h = J / 2; h >= 1; h >>= 1) {
+    if (j < h) red[j][u] += red[j + h][u];
+    __syncthreads();
   }
+  if (j == 0 && e < E) out[e] = red[0][u];
 }
 
 hipError_t launch_topk(const Ctx& c, const moe_shape_t& s, const float* logits, int32_t* idx,
@@ -418,7 +423,8 @@ hipError_t launch_topk(const Ctx& c, const moe_shape_t& s, const float* logits, 
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || !prob_sum) return err;
   TimedLaunch tl(MOE_K_PROB_REDUCE, c.stream);
-  hipLaunchKernelGGL(prob_reduce, dim3((s.E + 63) / 64), dim3(1024), 0, c.stream, part, nblk, s.E, prob_sum);
+  hipLaunchKernelGGL(prob_reduce, dim3((s.E + kReduceE - 1) / kReduceE), dim3(1024), 0, c.stream, part, nblk, s.E,
+                     prob_sum);
   return hipGetLastError();
 }
 
