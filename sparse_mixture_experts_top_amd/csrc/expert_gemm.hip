@@ -700,12 +700,15 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::WAVES_PER_SIMD) void expert_dx_d
   persistent_gemm_dma<Cfg>(pb, items, 2 * pb.f / Cfg::BK);
 }
 
-template <class Cfg>
+// dG/dU on CfgH tiles, then dX on Cfg tiles; with rebuild_for_dx the row
+// tiles are rebuilt for Cfg's height in between (the list the caller built
+// is for CfgH).
+template <class CfgH, class Cfg>
 static hipError_t launch_bwd_gemms_cfg(const Ctx& c, const moe_shape_t& s, const Workspace& ws,
                                        const LoraArgs* lo, const bf16_t* dy, const int32_t* row_src,
                                        const float* row_gate, const int32_t* offsets, const bf16_t* act_save,
                                        const bf16_t* dgu_packed, const bf16_t* dx_packed, bf16_t* dgu,
-                                       float* dx_rows, int max_tiles) {
+                                       float* dx_rows, int max_tiles, bool rebuild_for_dx = false) {
   const int L = s.e_hi - s.e_lo;
   const int64_t rmax = max_rows(s);
   hipError_t err;
@@ -714,10 +717,6 @@ static hipError_t launch_bwd_gemms_cfg(const Ctx& c, const moe_shape_t& s, const
                                       lo->r, ws.wproj, ws.lora_mt);
     if (err != hipSuccess) return err;
   }
-  // dG/dU runs the two-waves-per-SIMD layout at every row count (its
-  // epilogue reads G and U and writes two outputs per element; smaller wave
-  // tiles measured faster even at 73 rows per expert: 293 -> 265 us)
-  using CfgH = GemmCfgWide;
   auto dgu_launch = [&](auto with_lora) {
     constexpr bool LO = decltype(with_lora)::value;
     DguPackedProb<CfgH, LO> pb{dy, row_src, row_gate, offsets, ws.gemm_tiles, dgu_packed, s.d, s.f,
@@ -734,6 +733,8 @@ static hipError_t launch_bwd_gemms_cfg(const Ctx& c, const moe_shape_t& s, const
                                       false, lo->r, ws.vproj, ws.lora_mt);
     if (err != hipSuccess) return err;
   }
+  if (rebuild_for_dx && (err = launch_row_tiles(c, offsets, L, max_tiles, ws.gemm_tiles, Cfg::BM)) != hipSuccess)
+    return err;
   auto dx_launch = [&](auto with_lora) {
     constexpr bool LO = decltype(with_lora)::value;
     DxPackedProb<Cfg, LO> pb{dgu, offsets, ws.gemm_tiles, dx_packed, s.d, s.f, (s.d + Cfg::BN - 1) / Cfg::BN,
@@ -790,11 +791,18 @@ hipError_t launch_bwd_gemms_packed(const Ctx& c, const moe_shape_t& s, const Wor
   if (err != hipSuccess) return err;
   int64_t per_expert = (int64_t)s.T * s.k / s.E;
   if (s.capacity > 0 && per_expert > s.capacity) per_expert = s.capacity;
+  // dG/dU runs the two-waves-per-SIMD layout at every row count (its
+  // epilogue reads G and U and writes two outputs per element; smaller wave
+  // tiles measured faster even at 73 rows per expert: 293 -> 265 us; on
+  // 320 x 64 tall tiles it measured 101 us against 86 at ep64_rank). dX
+  // (N = d) takes the tall tiles where the forward does: each packed weight
+  // tile streams once per expert instead of once per 128-row tile (ep64_rank
+  // 140 -> 119 us).
   if (per_expert >= kWideRowsPerExpert)
-    return launch_bwd_gemms_cfg<GemmCfgWide>(c, s, ws, lo, dy, row_src, row_gate, offsets, act_save, dgu_packed,
-                                             dx_packed, dgu, dx_rows, max_tiles);
-  return launch_bwd_gemms_cfg<GemmCfg>(c, s, ws, lo, dy, row_src, row_gate, offsets, act_save, dgu_packed,
-                                       dx_packed, dgu, dx_rows, max_tiles);
+    return launch_bwd_gemms_cfg<GemmCfgWide, GemmCfgTall>(c, s, ws, lo, dy, row_src, row_gate, offsets, act_save,
+                                                          dgu_packed, dx_packed, dgu, dx_rows, max_tiles, true);
+  return launch_bwd_gemms_cfg<GemmCfgWide, GemmCfg>(c, s, ws, lo, dy, row_src, row_gate, offsets, act_save,
+                                                    dgu_packed, dx_packed, dgu, dx_rows, max_tiles);
 }
 
 // Transposing pack: tile (le, n block of 128 rows, K step) of the matrix
