@@ -292,7 +292,8 @@ struct GateUpProb {
         const uint4 hv = pair_cols_bf16(h[0], h[1]);
         // H (read by the down GEMM) and the saved rows (read by the
         // backward) with the non-temporal hint: the token rows this launch
-        // still gathers keep the L2 (full_router gate/up 363 -> 348 us)
+        // still gathers keep the L2 (896 experts of ~73 rows, d = 2048: gate/up
+        // 363 -> 348 us)
         if constexpr (kPackedH) {
           // one 16-row x 64-byte block: the store writes 1 KB contiguously
           bf16_t* hp = hbuf + (int64_t)(item / nt) * Cfg::BM * f + ((c0 >> 5) * Cfg::BM + rin) * 32 + pair_col(lane);
@@ -336,8 +337,9 @@ struct DownProb {
   // values], so the 16 rows of one DMA instruction are 1 KB of contiguous
   // memory (64-byte pieces 2 f bytes apart in the row-major form), and the
   // gate/up epilogue writes each such block with one store instruction.
-  // Measured at ep64_rank: down 59 -> 52 us, gate/up unchanged; on the
-  // 128-row tiles at full_router a wash (down -1, gate/up +3..+5 us), so
+  // Measured on 14 experts of ~296 rows (d = 4096, f = 1024): down 59 -> 52
+  // us, gate/up unchanged; on the 128-row tiles (896 experts of ~73 rows) a
+  // wash (down -1, gate/up +3..+5 us), so
   // those keep the row-major form, as do the adapter paths, which read H
   // row by row.
   static constexpr bool kPackedH = LORA == 0 && Cfg::BM == kTallBM;
@@ -794,10 +796,10 @@ hipError_t launch_bwd_gemms_packed(const Ctx& c, const moe_shape_t& s, const Wor
   // dG/dU runs the two-waves-per-SIMD layout at every row count (its
   // epilogue reads G and U and writes two outputs per element; smaller wave
   // tiles measured faster even at 73 rows per expert: 293 -> 265 us; on
-  // 320 x 64 tall tiles it measured 101 us against 86 at ep64_rank). dX
-  // (N = d) takes the tall tiles where the forward does: each packed weight
-  // tile streams once per expert instead of once per 128-row tile (ep64_rank
-  // 140 -> 119 us).
+  // 320 x 64 tall tiles it measured 101 us against 86 on 14 experts of ~296
+  // rows). dX (N = d) takes the tall tiles where the forward does: each
+  // packed weight tile streams once per expert instead of once per 128-row
+  // tile (14 experts of ~296 rows, d = 4096: 140 -> 119 us).
   if (per_expert >= kWideRowsPerExpert)
     return launch_bwd_gemms_cfg<GemmCfgWide, GemmCfgTall>(c, s, ws, lo, dy, row_src, row_gate, offsets, act_save,
                                                           dgu_packed, dx_packed, dgu, dx_rows, max_tiles, true);
