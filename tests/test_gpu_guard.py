@@ -61,6 +61,9 @@ CASES = {
                             lora_r=8, lora_alpha=16.0, lora_b="normal", aux_coef=0.01),
     # fp32, rows of an odd number of elements
     "f32_odd": Workload("g_f32_odd", T=131, d=45, E=9, k=2, f=19, capacity=40, zipf_s=1.0, dtype="f32"),
+    # ~150 rows per expert: two 128-row tiles each, LoRA at r = 16
+    "mid_lora": Workload("g_mid_lora", T=600, d=128, E=16, k=4, f=128, e_lo=1, e_hi=14, lora_r=16,
+                         lora_alpha=32.0, lora_b="normal", aux_coef=0.01),
     # about 500 rows per expert: 320-row tiles (two per expert), LoRA at r = 16
     "tall_lora": Workload("g_tall_lora", T=2048, d=128, E=8, k=2, f=128, e_lo=1, e_hi=7, lora_r=16,
                           lora_alpha=32.0, lora_b="normal", aux_coef=0.01),
@@ -68,7 +71,8 @@ CASES = {
 
 
 @pytest.mark.parametrize("name,packed", [("lora_local", False), ("lora_local", True),
-                                         ("capacity_r8", True), ("f32_odd", False), ("tall_lora", True)])
+                                         ("capacity_r8", True), ("f32_odd", False), ("tall_lora", True),
+                                         ("mid_lora", True)])
 def test_no_write_outside_buffers(name, packed):
     w = CASES[name]
     say(f"[guard {name} packed={packed}] T={w.T} d={w.d} E={w.E} k={w.k} f={w.f} dtype={w.dtype}")

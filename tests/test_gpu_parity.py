@@ -37,6 +37,12 @@ SMALL = {
     "tall_shortk_bf16": W("tall_shortk_bf16", T=8192, d=64, E=64, k=2, f=512),
     # the same with four K steps (packed weights need d % 128 == 0)
     "tall_k128_bf16": W("tall_k128_bf16", T=8192, d=128, E=64, k=2, f=512),
+    # ~150 rows per expert: two 128-row tiles per expert, the second ragged,
+    # a local range, 3 gate/up column tiles
+    "mid_bf16": W("mid_bf16", T=600, d=128, E=16, k=4, f=192, e_lo=1, e_hi=14),
+    # capacity 160 under Zipf skew: the hot experts at capacity span two
+    # 128-row tiles that share each weight tile
+    "mid_capacity_bf16": W("mid_capacity_bf16", T=2000, d=128, E=64, k=4, f=128, capacity=160, zipf_s=1.2),
     # router on 256 x 224 tiles (64 x 4 = 256 of them) with a partial last
     # column tile (880 = 3 x 224 + 208)
     "router_wide_bf16": W("router_wide_bf16", T=16384, d=128, E=880, k=4, f=64),
@@ -67,7 +73,7 @@ def test_stagewise_parity(name):
 
 
 @pytest.mark.parametrize("name", ["tiny_f32", "ragged_bf16", "local_bf16", "rows_bf16", "capacity_bf16",
-                                  "wide_bf16"])
+                                  "wide_bf16", "mid_capacity_bf16"])
 def test_stagewise_parity_fused_gather(name):
     """The expert GEMM reading x through row_src (no x_perm copy)."""
     run_and_check(SMALL[name], seed=7, x_perm=False)
@@ -251,7 +257,7 @@ def test_capacity_one_everywhere():
 
 
 @pytest.mark.parametrize("name", ["ragged_bf16", "rows_bf16", "capacity_bf16", "k1_bf16", "wide_bf16",
-                                  "tall_k128_bf16"])
+                                  "tall_k128_bf16", "mid_bf16", "mid_capacity_bf16"])
 def test_stagewise_parity_packed_weights(name):
     """Expert weights streamed from their packed copies (fused gather too)."""
     run_and_check(SMALL[name], seed=8, x_perm=False, packed=True)
