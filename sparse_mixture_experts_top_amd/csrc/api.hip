@@ -73,6 +73,8 @@ Workspace carve_workspace(const moe_shape_t& s, int lora_r, void* base, bool dis
     w.vproj = static_cast<float*>(take(rmax * lora_r * 4));
     w.du = static_cast<float*>(take(rmax * s.f * 4));
     w.lora_mt = static_cast<bf16_t*>(take(L * lora_r * std::max(s.d, s.f) * 2));
+    w.lora_mt2 = static_cast<bf16_t*>(take(L * lora_r * std::max(s.d, s.f) * 2));
+    w.lora_mt3 = static_cast<bf16_t*>(take(L * lora_r * std::max(s.d, s.f) * 2));
     w.zx = static_cast<bf16_t*>(take(rmax * 2 * lora_r * 2));
   }
   w.logits = static_cast<float*>(take((int64_t)s.T * s.E * 4));

@@ -180,6 +180,8 @@ struct Workspace {
   float* vproj;          // [Rmax, rmax] LoRA dU B_up
   float* du;             // [Rmax, f]   LoRA backward dU (f32)
   bf16_t* lora_mt;       // [L, r, max(d, f)] a [K, r] adapter transposed for the rank-r projections
+  bf16_t* lora_mt2;      // [L, r, max(d, f)] the adapter backward's B_up made K-contiguous
+  bf16_t* lora_mt3;      // [L, max(d, f), r] the adapter backward's A_down as [L, f, r] rows
   bf16_t* zx;            // [Rmax, 2r] s Z as bf16 high | low parts (the extra adapter K step)
   float* logits;         // [T, E]
   float* prob_part;      // [prob_blocks, E]

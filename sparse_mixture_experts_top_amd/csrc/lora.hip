@@ -298,6 +298,30 @@ __global__ __launch_bounds__(256) void lora_transpose_kr(const bf16_t* __restric
   for (int q = 0; q < r; ++q) Mt[(le * r + q) * K + k] = M[id * r + q];
 }
 
+// The adapter backward's three re-layouts in one launch (blockIdx.y picks
+// the job, workgroups past a job's elements return): B_d [L, d, r] and B_u
+// [L, f, r] made K-contiguous ([L, r, d], [L, r, f]) for the projections
+// dO B_d and dU B_u, and, with ad_t, A_d [L, r, f] as [L, f, r] rows for the
+// dH product's extra K step.
+__global__ __launch_bounds__(256) void lora_transpose_bwd(const bf16_t* __restrict__ bd, const bf16_t* __restrict__ bu,
+                                                          const bf16_t* __restrict__ ad, int L, int d, int f, int r,
+                                                          bf16_t* __restrict__ bd_t, bf16_t* __restrict__ bu_t,
+                                                          bf16_t* __restrict__ ad_t) {
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (blockIdx.y < 2) {
+    const int K = blockIdx.y == 0 ? d : f;
+    const bf16_t* M = blockIdx.y == 0 ? bd : bu;
+    bf16_t* Mt = blockIdx.y == 0 ? bd_t : bu_t;
+    if (id >= (int64_t)L * K) return;
+    const int64_t le = id / K, k = id % K;
+    for (int q = 0; q < r; ++q) Mt[(le * r + q) * K + k] = M[id * r + q];
+    return;
+  }
+  if (!ad_t || id >= (int64_t)L * r * f) return;
+  const int64_t n = id % f, q = (id / f) % r, le = id / ((int64_t)f * r);
+  ad_t[(le * f + n) * r + q] = ad[id];
+}
+
 template <class TIn>
 hipError_t launch_lora_rowproj(const Ctx& c, int L, const int32_t* offsets, int64_t rmax_rows,
                                const TIn* in, int64_t in_stride, const int32_t* src,
@@ -884,15 +908,18 @@ hipError_t launch_lora_bwd(const Ctx& c, const moe_shape_t& sh, const Workspace&
   // packed dH product's extra K step, s dY B_d as bf16 high/low parts (the
   // row gate scales the whole dH there)
   const bool kx = dgu_packed && lo.r == 16 && ws.zx;
-  if (rmax > 0 && r <= 16 && d % 32 == 0 && f % 32 == 0 && ws.lora_mt) {
-    // the three projections are independent: one launch, B_d made K-contiguous first
-    {
-      TimedLaunch tl(MOE_K_LORA_PROJ, c.stream);
-      const int64_t n = (int64_t)L * d;
-      hipLaunchKernelGGL(lora_transpose_kr, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, c.stream, lo.b_down, L,
-                         d, r, ws.lora_mt);
-      MOE_TRY(hipGetLastError());
-    }
+  // on the matrix-core path all three adapter re-layouts (B_d and B_u
+  // K-contiguous, A_d as rows of the extra K step) go first, in one launch
+  const bool mt_all = rmax > 0 && r <= 16 && d % 32 == 0 && f % 32 == 0 && ws.lora_mt && ws.lora_mt2 && ws.lora_mt3;
+  if (mt_all) {
+    TimedLaunch tl(MOE_K_LORA_PROJ, c.stream);
+    const int64_t n = std::max<int64_t>((int64_t)L * std::max(d, f), kx ? (int64_t)L * r * f : 0);
+    hipLaunchKernelGGL(lora_transpose_bwd, dim3((unsigned)((n + 255) / 256), 3), dim3(256), 0, c.stream, lo.b_down,
+                       lo.b_up, lo.a_down, L, d, f, r, ws.lora_mt, ws.lora_mt2, kx ? ws.lora_mt3 : nullptr);
+    MOE_TRY(hipGetLastError());
+  }
+  if (mt_all) {
+    // the three projections are independent: one launch
     const ProjJob<bf16_t> j_dob{dy, d, row_src, row_gate, d, ws.lora_mt, ws.wproj, kx ? ws.zx : nullptr, lo.scale};
     const unsigned gx = (unsigned)((rmax + 16 * kProjRowGroups - 1) / (16 * kProjRowGroups));
     TimedLaunch tl(MOE_K_LORA_PROJ, c.stream);
@@ -917,9 +944,9 @@ hipError_t launch_lora_bwd(const Ctx& c, const moe_shape_t& sh, const Workspace&
                                         ws.wproj, ws.lora_mt, kx ? ws.zx : nullptr, lo.scale));
   }
   if (dgu_packed) {
-    if (kx) MOE_TRY(launch_lora_transpose_rn(c, lo.a_down, L, r, f, ws.lora_mt));
+    if (kx && !mt_all) MOE_TRY(launch_lora_transpose_rn(c, lo.a_down, L, r, f, ws.lora_mt3));
     MOE_TRY(launch_lora_dh_packed(c, sh, ws, lo, dy, row_src, row_gate, offsets, act_save, dgu_packed,
-                                  kx ? ws.lora_mt : nullptr));
+                                  kx ? ws.lora_mt3 : nullptr));
   } else {
     TimedLaunch tl(MOE_K_LORA_DH, c.stream);
     DhProb<Cfg> pb{dy, row_src, row_gate, offsets, ws.gemm_tiles, w_down, d, f, (f + Cfg::BN - 1) / Cfg::BN,
@@ -928,21 +955,25 @@ hipError_t launch_lora_bwd(const Ctx& c, const moe_shape_t& sh, const Workspace&
                        max_tiles);
     MOE_TRY(hipGetLastError());
   }
-  MOE_TRY(launch_lora_rowproj<float>(c, L, offsets, rmax, ws.du, f, nullptr, nullptr, f, lo.b_up, false, r, ws.vproj, ws.lora_mt));
-  if (seg_mfma_ok(r, dy, d, d) && seg_mfma_ok(r, H, 3 * f, f)) {
-    // db_down and da_down together (both bf16 rows)
+  MOE_TRY(launch_lora_rowproj<float>(c, L, offsets, rmax, ws.du, f, nullptr, nullptr, f, mt_all ? ws.lora_mt2 : lo.b_up,
+                                     mt_all, r, ws.vproj, ws.lora_mt));
+  if (seg_mfma_ok(r, dy, d, d) && seg_mfma_ok(r, H, 3 * f, f) && seg_mfma_ok(r, x_rows, d, d)) {
+    // db_down, da_down and da_up (bf16 rows) in one launch
     TimedLaunch tl(MOE_K_LORA_GRAD, c.stream);
-    SegJobs<2> jobs{{{zd, dy, d, row_src, row_gate, d, 0, db_down}, {ws.wproj, H, 3 * f, nullptr, nullptr, f, 1, da_down}}};
-    hipLaunchKernelGGL((lora_seg_mfma<2>), dim3(std::max(d, f) / kSmCols, L, 2), dim3(64 * kSmWaves), 0, c.stream,
+    SegJobs<3> jobs{{{zd, dy, d, row_src, row_gate, d, 0, db_down},
+                     {ws.wproj, H, 3 * f, nullptr, nullptr, f, 1, da_down},
+                     {ws.vproj, x_rows, d, x_src, nullptr, d, 1, da_up}}};
+    hipLaunchKernelGGL((lora_seg_mfma<3>), dim3(std::max(d, f) / kSmCols, L, 3), dim3(64 * kSmWaves), 0, c.stream,
                        offsets, r, lo.scale, jobs);
     MOE_TRY(hipGetLastError());
   } else {
     MOE_TRY(launch_seg_outer<bf16_t>(c, L, offsets, zd, r, dy, d, row_src, row_gate, d, lo.scale, false, db_down));
     MOE_TRY(launch_seg_outer<bf16_t>(c, L, offsets, ws.wproj, r, H, 3 * f, nullptr, nullptr, f, lo.scale, true,
                                      da_down));
+    MOE_TRY(launch_seg_outer<bf16_t>(c, L, offsets, ws.vproj, r, x_rows, d, x_src, nullptr, d, lo.scale, true,
+                                     da_up));
   }
   MOE_TRY(launch_seg_outer<float>(c, L, offsets, zu, r, ws.du, f, nullptr, nullptr, f, lo.scale, false, db_up));
-  MOE_TRY(launch_seg_outer<bf16_t>(c, L, offsets, ws.vproj, r, x_rows, d, x_src, nullptr, d, lo.scale, true, da_up));
 #undef MOE_TRY
   return hipSuccess;
 }
