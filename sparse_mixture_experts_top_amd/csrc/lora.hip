@@ -299,27 +299,47 @@ __global__ __launch_bounds__(256) void lora_transpose_kr(const bf16_t* __restric
 }
 
 // The adapter backward's three re-layouts in one launch (blockIdx.y picks
-// the job, workgroups past a job's elements return): B_d [L, d, r] and B_u
-// [L, f, r] made K-contiguous ([L, r, d], [L, r, f]) for the projections
-// dO B_d and dU B_u, and, with ad_t, A_d [L, r, f] as [L, f, r] rows for the
-// dH product's extra K step.
+// the job, threads past a job's rows return): B_d [L, d, r] and B_u [L, f, r]
+// made K-contiguous ([L, r, d], [L, r, f]) for the projections dO B_d and
+// dU B_u, and, with ad_t, A_d [L, r, f] as [L, f, r] rows for the dH
+// product's extra K step. One thread per adapter row (le, k): its r values
+// are contiguous on the [., r] side, read or written as 16-byte vectors when
+// r = 16 and the rows are 16-byte aligned, and strided by K on the other
+// side, where consecutive threads touch consecutive elements.
 __global__ __launch_bounds__(256) void lora_transpose_bwd(const bf16_t* __restrict__ bd, const bf16_t* __restrict__ bu,
                                                           const bf16_t* __restrict__ ad, int L, int d, int f, int r,
                                                           bf16_t* __restrict__ bd_t, bf16_t* __restrict__ bu_t,
                                                           bf16_t* __restrict__ ad_t) {
   const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (blockIdx.y < 2) {
-    const int K = blockIdx.y == 0 ? d : f;
+  const int K = blockIdx.y == 0 ? d : f;
+  if (id >= (int64_t)L * K) return;
+  const int64_t le = id / K, k = id % K;
+  if (blockIdx.y < 2) {  // [le][k][q] -> [le][q][k]
     const bf16_t* M = blockIdx.y == 0 ? bd : bu;
     bf16_t* Mt = blockIdx.y == 0 ? bd_t : bu_t;
-    if (id >= (int64_t)L * K) return;
-    const int64_t le = id / K, k = id % K;
-    for (int q = 0; q < r; ++q) Mt[(le * r + q) * K + k] = M[id * r + q];
+    if (r == 16 && (reinterpret_cast<uintptr_t>(M) & 15) == 0) {
+      const uint4 v0 = reinterpret_cast<const uint4*>(M + id * 16)[0];
+      const uint4 v1 = reinterpret_cast<const uint4*>(M + id * 16)[1];
+      const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        Mt[(le * 16 + q) * K + k] = static_cast<bf16_t>(w[q >> 1] >> (16 * (q & 1)));
+    } else {
+      for (int q = 0; q < r; ++q) Mt[(le * r + q) * K + k] = M[id * r + q];
+    }
     return;
   }
-  if (!ad_t || id >= (int64_t)L * r * f) return;
-  const int64_t n = id % f, q = (id / f) % r, le = id / ((int64_t)f * r);
-  ad_t[(le * f + n) * r + q] = ad[id];
+  if (!ad_t) return;  // [le][q][n] -> [le][n][q], n = k < f
+  if (r == 16 && (reinterpret_cast<uintptr_t>(ad_t) & 15) == 0) {
+    uint32_t w[8];
+#pragma unroll
+    for (int q2 = 0; q2 < 8; ++q2)
+      w[q2] = (uint32_t)ad[(le * 16 + 2 * q2) * f + k] | ((uint32_t)ad[(le * 16 + 2 * q2 + 1) * f + k] << 16);
+    reinterpret_cast<uint4*>(ad_t + id * 16)[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    reinterpret_cast<uint4*>(ad_t + id * 16)[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  } else {
+    for (int q = 0; q < r; ++q) ad_t[id * r + q] = ad[(le * r + q) * f + k];
+  }
 }
 
 template <class TIn>
@@ -913,7 +933,7 @@ hipError_t launch_lora_bwd(const Ctx& c, const moe_shape_t& sh, const Workspace&
   const bool mt_all = rmax > 0 && r <= 16 && d % 32 == 0 && f % 32 == 0 && ws.lora_mt && ws.lora_mt2 && ws.lora_mt3;
   if (mt_all) {
     TimedLaunch tl(MOE_K_LORA_PROJ, c.stream);
-    const int64_t n = std::max<int64_t>((int64_t)L * std::max(d, f), kx ? (int64_t)L * r * f : 0);
+    const int64_t n = (int64_t)L * std::max(d, f);
     hipLaunchKernelGGL(lora_transpose_bwd, dim3((unsigned)((n + 255) / 256), 3), dim3(256), 0, c.stream, lo.b_down,
                        lo.b_up, lo.a_down, L, d, f, r, ws.lora_mt, ws.lora_mt2, kx ? ws.lora_mt3 : nullptr);
     MOE_TRY(hipGetLastError());
