@@ -167,7 +167,11 @@ def check_backward(w, packed, seed=3):
                                            buf.row_gate[:R].cpu().numpy().astype(np.float64), slot, x_perm,
                                            to_f64(inp["w_gate"]), to_f64(inp["w_up"]), to_f64(inp["w_down"]),
                                            T, lora=_lora64(w, inp))
-    assert_close(host(g["dx_experts"]), dx_ref, w.dtype, "dx (experts)")
+    # dx through the experts sums products of bf16-stored inputs (G, U in
+    # act_save, dG | dU in the scratch rows): their relative rounding stays in
+    # the sum whatever its order, so with bf16 the max-abs bound scales with
+    # max(1, |dx|inf)
+    assert_close(host(g["dx_experts"]), dx_ref, w.dtype, "dx (experts)", scale_atol=w.dtype == "bf16")
     none = (slot < 0).all(axis=1)
     assert (host(g["dx_experts"])[none] == 0).all()
     # router part on the GPU's dlogits
@@ -269,6 +273,6 @@ def test_backward_full_size_sampled(name):
                                                to_f64(wg[le:le + 1]), to_f64(wu[le:le + 1]),
                                                to_f64(wd[le:le + 1]), 1)
             dx_ref[a] += dX[0]
-    assert_close(host(g["dx_experts"][ts]), dx_ref, "bf16", "dx experts (sampled)")
+    assert_close(host(g["dx_experts"][ts]), dx_ref, "bf16", "dx experts (sampled)", scale_atol=True)
     dxr_ref = oracle.router_backward(dl, to_f64(inp["w_router"]))
     assert_close(host(g["dx_router"][ts]), dxr_ref, "bf16", "dx router (sampled)")

@@ -359,7 +359,10 @@ def check_lora(w, x_perm, packed, seed=6):
     ref, R = check_dispatch(w, dev, buf, idx, gate)
     lo64 = {"scale": w.lora_alpha / w.lora_r}
     o_ref = expert_ref_rows(w, inp, buf, np.arange(R), lora=lo64)
-    assert_close(host(buf.y_perm[:R]), o_ref, "bf16", "expert rows (LoRA)", stored_bf16=True)
+    # with s = alpha / r up to 32 the adapter term can make rows large (|O| ~ 15
+    # at r = 1), and the bf16 H fed to the down product carries a relative
+    # rounding into them: the max-abs bound scales with max(1, |O|inf)
+    assert_close(host(buf.y_perm[:R]), o_ref, "bf16", "expert rows (LoRA)", stored_bf16=True, scale_atol=True)
     # the saved G | H | U rows the backward reads, against the oracle's own
     parts = check_act_save(w, inp, buf, np.arange(R), lora=lo64)
     # aux loss from the GPU counts and probabilities
