@@ -92,8 +92,9 @@ def test_lora_step_full():
         xe = rows_x(w, inp, buf, np.arange(a, b))
         args = (dy64, xe, np.array([0, b - a]), host(buf.row_src[sl]), buf.row_gate[sl].cpu().numpy())
         # fed the GPU's saved G and H, then the oracle's own: rounded to bf16
-        # where act_save stores them (plain tolerance) and unrounded (max-abs
-        # scaled by |ref|inf: the stored rows' relative rounding stays)
+        # where act_save stores them and unrounded (max-abs scaled by
+        # |ref|inf: neighbouring-bf16 roundings of G or H, and the stored
+        # rows' relative rounding, stay in the sums)
         wd = to_f64(inp["w_down"][le:le + 1])
         g_ref = oracle.lora_backward(*args, act[:, :f], act[:, f:2 * f], wd, lo)
         g_own = oracle.lora_backward(*args, bf16_round(parts["G"]), bf16_round(parts["H"]), wd, lo)
@@ -101,6 +102,7 @@ def test_lora_step_full():
         for n in grads:
             assert_close(host(grads[n][le:le + 1]), g_ref[n], "bf16", f"{n}[{le}]")
             assert_close(host(gp[n][le:le + 1]), g_ref[n], "bf16", f"{n}[{le}] (packed)")
-            assert_close(host(gp[n][le:le + 1]), g_own[n], "bf16", f"{n}[{le}] (packed, oracle G, H at bf16)")
+            assert_close(host(gp[n][le:le + 1]), g_own[n], "bf16", f"{n}[{le}] (packed, oracle G, H at bf16)",
+                         scale_atol=True)
             assert_close(host(gp[n][le:le + 1]), g_own64[n], "bf16", f"{n}[{le}] (packed, oracle G, H unrounded)",
                          scale_atol=True)
