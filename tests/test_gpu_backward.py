@@ -248,12 +248,19 @@ def test_backward_full_size_sampled(name):
     rows = np.unique(slot[slot >= 0])
     o = {int(r): v for r, v in zip(rows, host(buf.y_perm[torch.as_tensor(rows, device="cuda")]))}
     dg_ref = np.zeros((len(toks), w.k))
+    bound = np.zeros_like(dg_ref)
     for a in range(len(toks)):
         for j in range(w.k):
             if slot[a, j] >= 0:
                 dg_ref[a, j] = float(np.dot(dy[a], o[int(slot[a, j])]))
+                bound[a, j] = dot_bound(dy[a], o[int(slot[a, j])])
     dg = host(g["dgate"][ts])
-    assert_close(dg, dg_ref, "f32", "dgate (sampled)")
+    # each gate gradient is an fp32 dot product of d terms (|dgate| reaches
+    # ~85 at d = 2048): held to the same rounding bound as the small cases
+    err = np.abs(dg - dg_ref)
+    say(f"  dgate (sampled): max_abs={err.max():.3e} max(err/bound)={(err / np.maximum(bound, 1e-30)).max():.3f}")
+    assert (err <= 2 * bound + 1e-30).all()
+    assert (dg[slot < 0] == 0).all()
     dl_ref = oracle.logits_backward(dg, idx, gate, logits, counts, AUX, w.k, T_total=w.T)
     dl = host(g["dlogits"][ts])
     assert np.abs(dl - dl_ref).max() <= 1e-5 * max(1.0, float(np.abs(dl_ref).max()))
